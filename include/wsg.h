@@ -1,0 +1,216 @@
+/*
+ * wsg.h -- C ABI of the MI355X (gfx950) weight-streaming decode library.
+ *
+ * The library runs the batch-one token-to-logits decode step of a
+ * Qwen3-0.6B-shaped decoder (Megakernels, "What runs in the DSL" and
+ * "GPU-wide end-to-end generation") and the weight-streaming GEMV family it
+ * is built from (Our Kernel Benchmark Was Measuring the System Cache,
+ * "Summary" and "Why it mattered").
+ *
+ * Conventions for every entry point:
+ *   - plain C types only; pointers named d_* are HIP device pointers, all
+ *     other pointers are host pointers;
+ *   - every call validates its arguments before it enqueues any GPU work;
+ *     on an error nothing is enqueued, model state is unchanged, the call
+ *     returns a negative wsg_status and wsg_last_error() describes it;
+ *   - device memory is owned by the caller (the library borrows it); the
+ *     library owns only the opaque wsg_model host object, its HIP graphs,
+ *     events and a small pinned host staging buffer;
+ *   - "hip_stream" is a hipStream_t passed as void*; NULL selects a stream
+ *     the library creates for the model (required for graph replay when the
+ *     caller has no non-default stream).
+ */
+#ifndef WSG_H
+#define WSG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WSG_OK = 0,
+  WSG_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad enum value   */
+  WSG_ERR_OUT_OF_RANGE = -2,  /* token id or position outside its range   */
+  WSG_ERR_STATE = -3,         /* call not valid in the model's state      */
+  WSG_ERR_HIP = -4,           /* a HIP runtime call failed                */
+  WSG_ERR_UNSUPPORTED = -5    /* valid, but a shape this build does not run */
+} wsg_status;
+
+/* Storage dtype of weights, KV cache, logits and stage outputs.  Reductions
+ * always accumulate in FP32 (Megakernels, "What runs in the DSL"). */
+typedef enum { WSG_F32 = 0, WSG_F16 = 1 } wsg_dtype;
+
+/* Decoder geometry and run limits.
+ *   head_dim must be 128; hidden, intermediate and n_q_heads*head_dim must
+ *   each be one of 512, 1024, 2048, 3072 (256 is also accepted for FP32);
+ *   n_q_heads must be a multiple of n_kv_heads with a group size of 1, 2
+ *   or 4.  max_context is the KV capacity in
+ *   positions.  prefill_chunk is the largest number of prompt rows one
+ *   prefill chunk may hold (0 = tokenwise prefill only).  */
+typedef struct {
+  int32_t n_layers, hidden, intermediate, n_q_heads, n_kv_heads, head_dim, vocab;
+  int32_t max_context;
+  int32_t prefill_chunk;
+  float rms_eps;      /* RMSNorm epsilon, inside the square root */
+  float rope_theta;   /* RoPE base; pair i turns by p * theta^(-2i/head_dim) */
+  int32_t dtype;      /* wsg_dtype */
+} wsg_config;
+
+/* Host-side unpacked weights, element type = cfg.dtype (float32, or IEEE
+ * binary16 bit patterns).  All matrices are row-major [out][in].  The
+ * per-layer members point to arrays of n_layers pointers.
+ *   embed [vocab][hidden] (also the tied vocabulary head), final_norm [hidden];
+ *   per layer: in_norm [hidden], wq [n_q*hd][hidden], wk [n_kv*hd][hidden],
+ *   wv [n_kv*hd][hidden], q_norm [hd], k_norm [hd], wo [hidden][n_q*hd],
+ *   post_norm [hidden], wg [intermediate][hidden], wu [intermediate][hidden],
+ *   wd [hidden][intermediate].                                            */
+typedef struct {
+  const void* embed;
+  const void* final_norm;
+  const void* const* in_norm;
+  const void* const* wq;
+  const void* const* wk;
+  const void* const* wv;
+  const void* const* q_norm;
+  const void* const* k_norm;
+  const void* const* wo;
+  const void* const* post_norm;
+  const void* const* wg;
+  const void* const* wu;
+  const void* const* wd;
+} wsg_host_weights;
+
+typedef struct wsg_model wsg_model;   /* opaque; one model per stream and host thread */
+
+/* Size in bytes of the packed weight image for cfg (host and device copies
+ * have the same layout).  Packing happens once on the host, outside any
+ * timed region (Megakernels, "What runs in the DSL": the host packs the
+ * weights and precomputes rotary constants but runs no layer arithmetic). */
+wsg_status wsg_packed_weight_bytes(const wsg_config* cfg, size_t* bytes);
+
+/* Copy the host weights into the packed layout at host_out (out_bytes must
+ * be at least wsg_packed_weight_bytes).  Fuses Wq/Wk/Wv into one
+ * [(n_q+2 n_kv) hd][hidden] matrix and Wg/Wu into one [2 I][hidden] matrix;
+ * values are copied bit for bit. */
+wsg_status wsg_pack_weights(const wsg_config* cfg, const wsg_host_weights* w,
+                            void* host_out, size_t out_bytes);
+
+/* Size in bytes of the device workspace for cfg: KV cache
+ * [n_layers][2][n_kv][max_context][head_dim], rotary table, stage buffers,
+ * prefill chunk scratch, token history and control words. */
+wsg_status wsg_workspace_bytes(const wsg_config* cfg, size_t* bytes);
+
+/* Create a model over caller-owned device buffers: d_packed (a device copy
+ * of the packed image) and d_workspace (at least wsg_workspace_bytes,
+ * 256-byte aligned).  Both must stay allocated until wsg_model_destroy.
+ * Builds and uploads the rotary table (synchronously, on hip_stream) and
+ * clears the control words.  The cache starts empty (position 0). */
+wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t packed_bytes,
+                            void* d_workspace, size_t ws_bytes, void* hip_stream, wsg_model** out);
+
+void wsg_model_destroy(wsg_model* m);
+
+/* Empty the KV cache: valid length 0.  Stale slots are never read, since
+ * attention only reads positions 0..p (Megakernels, "Matrix-tiled
+ * attention": logical extents exclude future cache slots).  Enqueues a
+ * small device update on the model stream. */
+wsg_status wsg_reset_cache(wsg_model* m);
+
+/* Run prompt tokens host_ids[0..n) at positions pos..pos+n-1 and return the
+ * greedy token of the last row in *out_token (lowest id among maximal
+ * logits).  Only the last row reaches the final norm and vocabulary head
+ * (Benchmark methodology, "Long-document chunked prefill").  Rows go through
+ * the chunked path when cfg.prefill_chunk > 0 (chunk size set by
+ * wsg_set_prefill_chunk), else one decode forward per row.  *out_logits (if
+ * out_logits is not NULL) receives a device pointer to the last row's
+ * logits [vocab] in the storage dtype, valid until the next call.  Blocks
+ * until the token id is on the host.  Errors: n < 1, any id outside
+ * [0, vocab), pos + n > max_context. */
+wsg_status wsg_prefill(wsg_model* m, const int32_t* host_ids, int32_t n,
+                       int32_t* out_token, const void** out_logits);
+
+/* One decode step at position pos: consumes in_token (or, if in_token < 0,
+ * the previous greedy output, which never leaves the device), appends its
+ * K/V to the cache and returns the next greedy token.  The only
+ * device-to-host transfer is the 4-byte token id (Megakernels, "GPU-wide
+ * end-to-end generation").  Errors: in_token >= vocab; in_token < 0 with no
+ * previous output (WSG_ERR_STATE); pos == max_context. */
+wsg_status wsg_step(wsg_model* m, int32_t in_token, int32_t* out_token, const void** out_logits);
+
+/* Current position (number of valid KV entries). */
+int32_t wsg_position(const wsg_model* m);
+
+/* Device pointers to layer `layer`'s K and V cache blocks, each laid out
+ * [n_kv][max_context][head_dim] in the storage dtype, and the valid length.
+ * For validation; the memory belongs to the workspace. */
+wsg_status wsg_kv_view(const wsg_model* m, int32_t layer, const void** d_k, const void** d_v,
+                       int32_t* valid_len);
+
+/* Rows per prefill chunk for later wsg_prefill calls: 1 <= rows <=
+ * cfg.prefill_chunk (Benchmark methodology, "Long-document chunked
+ * prefill": candidate chunk sizes are a run-time choice). */
+wsg_status wsg_set_prefill_chunk(wsg_model* m, int32_t rows);
+
+/* Options: WSG_OPT_USE_GRAPH (1 = replay captured HIP graphs, the default;
+ * 0 = launch every kernel directly), WSG_OPT_TIMED_STAGE (record HIP events
+ * around every launch of one stage kind, see wsg_stage_time; -1 = off). */
+enum { WSG_OPT_USE_GRAPH = 1, WSG_OPT_TIMED_STAGE = 2 };
+/* Stage kinds for WSG_OPT_TIMED_STAGE. */
+enum { WSG_STAGE_QKV = 0, WSG_STAGE_ATTN = 1, WSG_STAGE_O = 2, WSG_STAGE_GATEUP = 3,
+       WSG_STAGE_DOWN = 4, WSG_STAGE_HEAD = 5, WSG_STAGE_ARGMAX = 6 };
+wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value);
+
+/* Accumulated device time (HIP events, on the model stream) of the timed
+ * stage since the option was set or last read, the number of launches it
+ * covers, and the algorithmic weight bytes those launches streamed.  Resets
+ * the accumulators. */
+wsg_status wsg_stage_time(wsg_model* m, double* total_ms, int64_t* launches, int64_t* bytes);
+
+/* Stand-alone GEMV, Y[t][m] = sum_k W[m][k] X[t][k] for t < T, with FP32
+ * accumulation (Megakernels, "GPU-wide end-to-end generation": one wave
+ * per group of output rows; Our Kernel Benchmark Was Measuring the System
+ * Cache, "Why it mattered": rows per wave and the two-token variant).
+ *   w_dtype WSG_F32: d_W float [M][K], d_X float [T][K];
+ *   w_dtype WSG_F16: d_W half [M][K],  d_X half [T][K];
+ *   d_Y float [T][M].  1 <= T <= 2; rows_per_wave in {1,2,4,8}, 0 = default.
+ *   M >= 1, K >= 1, any sizes; d_W and d_X 16-byte aligned.
+ * Asynchronous on hip_stream. */
+wsg_status wsg_gemv(int32_t w_dtype, int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,
+                    const void* d_W, const void* d_X, float* d_Y, void* hip_stream);
+
+/* wsg_gemv with an explicit launch shape: grid_blocks of 256 threads
+ * (0 = one row group per wave, no grid-stride loop) and flags
+ * (WSG_GEMV_NONTEMPORAL: weight loads bypass cache allocation). */
+enum { WSG_GEMV_NONTEMPORAL = 1 };
+wsg_status wsg_gemv_ex(int32_t w_dtype, int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,
+                       int32_t grid_blocks, int32_t flags,
+                       const void* d_W, const void* d_X, float* d_Y, void* hip_stream);
+
+/* 4-bit GEMV: symmetric int4 weights in groups of 64 along K with one FP16
+ * scale per group (the 4-bit matrix-vector kernel of Our Kernel Benchmark
+ * Was Measuring the System Cache, "Summary").
+ *   d_Wq uint32 [M][K/8]: nibble j of word w is element 8w+j, two's complement;
+ *   d_scales half [M][K/64]; d_X half [T][K]; d_Y float [T][M].
+ *   K % 64 == 0, 1 <= T <= 2, rows_per_wave in {1,2,4,8} (0 = default).  */
+wsg_status wsg_gemv_q4g64(int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,
+                          const uint32_t* d_Wq, const void* d_scales, const void* d_X,
+                          float* d_Y, void* hip_stream);
+wsg_status wsg_gemv_q4g64_ex(int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,
+                             int32_t grid_blocks, int32_t flags,
+                             const uint32_t* d_Wq, const void* d_scales, const void* d_X,
+                             float* d_Y, void* hip_stream);
+
+/* Message for the last error on this host thread ("" if none). */
+const char* wsg_last_error(void);
+
+/* Library version string. */
+const char* wsg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WSG_H */

@@ -73,7 +73,7 @@ QWEN3_0_6B = ModelShape(n_layers=28, hidden=1024, intermediate=3072, n_q_heads=1
 
 # A small geometry with ragged sizes (vocab not a multiple of any tile), used
 # by fast CPU and GPU tests.  head_dim stays 128, as in the real model.
-MINI = ModelShape(n_layers=2, hidden=256, intermediate=512, n_q_heads=4,
+MINI = ModelShape(n_layers=2, hidden=512, intermediate=1024, n_q_heads=4,
                   n_kv_heads=2, head_dim=128, vocab=1000)
 
 WEIGHT_SEED = 0

@@ -1,0 +1,201 @@
+"""MI355X (gfx950) weight-streaming decode engine: Python binding.
+
+Argument marshalling only.  Every step of the decode path runs in the HIP
+kernels of ``libwsg.so`` behind the C ABI of ``include/wsg.h``; PyTorch is
+used to allocate device memory and to provide a stream.  Importing this
+package fails if the library has not been built, and the GPU entry points
+fail if no GPU is present -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _abi
+from ._abi import (WSG_F16, WSG_F32, WSG_GEMV_NONTEMPORAL, WSG_OPT_TIMED_STAGE, WSG_OPT_USE_GRAPH,
+                   WSG_STAGE_ARGMAX, WSG_STAGE_ATTN, WSG_STAGE_DOWN, WSG_STAGE_GATEUP, WSG_STAGE_HEAD,
+                   WSG_STAGE_O, WSG_STAGE_QKV, WsgError, check, wsg_config, wsg_host_weights)
+
+__all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "WsgError", "WSG_F32", "WSG_F16",
+           "WSG_STAGE_QKV", "WSG_STAGE_ATTN", "WSG_STAGE_O", "WSG_STAGE_GATEUP", "WSG_STAGE_DOWN",
+           "WSG_STAGE_HEAD", "WSG_STAGE_ARGMAX", "WSG_GEMV_NONTEMPORAL", "lib"]
+
+lib = _abi.lib
+lib()  # fail loudly at import when libwsg.so is missing
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("weight_streaming_gemv_amd needs a ROCm GPU (torch.cuda.is_available() is False)")
+    return torch
+
+
+def _stream_handle(stream) -> int:
+    return 0 if stream is None else int(stream.cuda_stream)
+
+
+# ----------------------------------------------------------------- GEMV
+def gemv(W, X, rows_per_wave: int = 0, Y=None, stream=None, grid_blocks: int = 0, flags: int = 0):
+    """``Y[T, M] = X[T, K] @ W[M, K]^T`` on the GPU (torch tensors, FP32 or FP16 W/X, FP32 Y)."""
+    torch = _torch()
+    M, K = W.shape
+    T = X.shape[0]
+    dt = {torch.float32: WSG_F32, torch.float16: WSG_F16}[W.dtype]
+    if X.dtype != W.dtype or not (W.is_contiguous() and X.is_contiguous()):
+        raise ValueError("W and X must be contiguous and share a dtype")
+    if Y is None:
+        Y = torch.empty((T, M), dtype=torch.float32, device=W.device)
+    check(_abi.lib().wsg_gemv_ex(dt, M, K, T, rows_per_wave, grid_blocks, flags, W.data_ptr(), X.data_ptr(),
+                                 Y.data_ptr(), _stream_handle(stream)))
+    return Y
+
+
+def gemv_q4g64(Wq, S, X, rows_per_wave: int = 0, Y=None, stream=None, grid_blocks: int = 0, flags: int = 0):
+    """int4 group-64 GEMV: ``Wq`` int32/uint32 [M, K/8], ``S`` fp16 [M, K/64], ``X`` fp16 [T, K]."""
+    torch = _torch()
+    M = Wq.shape[0]
+    K = Wq.shape[1] * 8
+    T = X.shape[0]
+    if Y is None:
+        Y = torch.empty((T, M), dtype=torch.float32, device=Wq.device)
+    check(_abi.lib().wsg_gemv_q4g64_ex(M, K, T, rows_per_wave, grid_blocks, flags, Wq.data_ptr(), S.data_ptr(),
+                                       X.data_ptr(), Y.data_ptr(), _stream_handle(stream)))
+    return Y
+
+
+# ---------------------------------------------------------------- model
+def make_config(shape, max_context: int, dtype: int = WSG_F32, prefill_chunk: int = 0) -> wsg_config:
+    """C config from a ``synth.ModelShape``-like object."""
+    return wsg_config(shape.n_layers, shape.hidden, shape.intermediate, shape.n_q_heads, shape.n_kv_heads,
+                      shape.head_dim, shape.vocab, max_context, prefill_chunk, shape.rms_eps, shape.rope_theta,
+                      dtype)
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def pack_weights(cfg: wsg_config, weights: Dict[str, object]) -> np.ndarray:
+    """Host packing through ``wsg_pack_weights`` (a bit-for-bit copy into the packed layout)."""
+    want = np.float16 if cfg.dtype == WSG_F16 else np.float32
+    keep = []
+
+    def arr(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype != want:
+            raise ValueError(f"weight dtype {a.dtype} does not match the config dtype {np.dtype(want)}")
+        keep.append(a)
+        return _ptr(a)
+
+    layers = weights["layers"]
+    L = cfg.n_layers
+    if len(layers) != L:
+        raise ValueError("layer count mismatch")
+
+    def plist(name):
+        P = (C.c_void_p * L)(*[arr(lw[name]) for lw in layers])
+        keep.append(P)
+        return C.cast(P, C.POINTER(C.c_void_p))
+
+    hw = wsg_host_weights(arr(weights["embed"]), arr(weights["final_norm"]), plist("in_norm"), plist("wq"),
+                          plist("wk"), plist("wv"), plist("q_norm"), plist("k_norm"), plist("wo"),
+                          plist("post_norm"), plist("wg"), plist("wu"), plist("wd"))
+    n = C.c_size_t()
+    check(_abi.lib().wsg_packed_weight_bytes(C.byref(cfg), C.byref(n)))
+    out = np.empty(n.value, dtype=np.uint8)
+    check(_abi.lib().wsg_pack_weights(C.byref(cfg), C.byref(hw), _ptr(out), n.value))
+    return out
+
+
+class Model:
+    """A decode model on the GPU; weights and workspace are torch device tensors it owns."""
+
+    def __init__(self, shape, weights: Dict[str, object], max_context: int, dtype: int = WSG_F32,
+                 prefill_chunk: int = 0, stream=None, packed: Optional[np.ndarray] = None):
+        torch = _torch()
+        self.torch = torch
+        self.shape = shape
+        self.cfg = make_config(shape, max_context, dtype, prefill_chunk)
+        self.np_dtype = np.float16 if dtype == WSG_F16 else np.float32
+        self.t_dtype = torch.float16 if dtype == WSG_F16 else torch.float32
+        host = packed if packed is not None else pack_weights(self.cfg, weights)
+        self.d_packed = torch.from_numpy(host).to("cuda")
+        n = C.c_size_t()
+        check(_abi.lib().wsg_workspace_bytes(C.byref(self.cfg), C.byref(n)))
+        self.ws = torch.empty(n.value, dtype=torch.uint8, device="cuda")
+        self.stream = stream if stream is not None else torch.cuda.Stream()
+        torch.cuda.synchronize()
+        h = C.c_void_p()
+        check(_abi.lib().wsg_model_create(C.byref(self.cfg), self.d_packed.data_ptr(), self.d_packed.numel(),
+                                          self.ws.data_ptr(), self.ws.numel(), _stream_handle(self.stream),
+                                          C.byref(h)))
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            _abi.lib().wsg_model_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- calls
+    def reset(self) -> None:
+        check(_abi.lib().wsg_reset_cache(self.h))
+
+    def prefill(self, ids: Sequence[int]) -> int:
+        a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        tok = C.c_int32()
+        lp = C.c_void_p()
+        check(_abi.lib().wsg_prefill(self.h, a.ctypes.data_as(C.POINTER(C.c_int32)), a.size, C.byref(tok),
+                                     C.byref(lp)))
+        self._logits_ptr = lp.value
+        return tok.value
+
+    def step(self, in_token: int = -1) -> int:
+        tok = C.c_int32()
+        lp = C.c_void_p()
+        check(_abi.lib().wsg_step(self.h, int(in_token), C.byref(tok), C.byref(lp)))
+        self._logits_ptr = lp.value
+        return tok.value
+
+    @property
+    def position(self) -> int:
+        return _abi.lib().wsg_position(self.h)
+
+    def set_prefill_chunk(self, rows: int) -> None:
+        check(_abi.lib().wsg_set_prefill_chunk(self.h, rows))
+
+    def set_option(self, option: int, value: int) -> None:
+        check(_abi.lib().wsg_set_option(self.h, option, value))
+
+    def stage_time(self) -> Tuple[float, int, int]:
+        ms, n, b = C.c_double(), C.c_int64(), C.c_int64()
+        check(_abi.lib().wsg_stage_time(self.h, C.byref(ms), C.byref(n), C.byref(b)))
+        return ms.value, n.value, b.value
+
+    # -- views into the workspace (validation)
+    def _view(self, ptr: int, count: int):
+        off = ptr - self.ws.data_ptr()
+        es = 2 if self.t_dtype == self.torch.float16 else 4
+        assert 0 <= off and off + count * es <= self.ws.numel()
+        return self.ws[off:off + count * es].view(self.t_dtype)
+
+    def logits(self):
+        """Last logits [vocab] (device tensor view, storage dtype)."""
+        return self._view(self._logits_ptr, self.shape.vocab)
+
+    def kv(self, layer: int):
+        """(K, V, valid_len): device views [n_kv, max_context, head_dim]."""
+        k, v, n = C.c_void_p(), C.c_void_p(), C.c_int32()
+        check(_abi.lib().wsg_kv_view(self.h, layer, C.byref(k), C.byref(v), C.byref(n)))
+        sh = (self.shape.n_kv_heads, self.cfg.max_context, self.shape.head_dim)
+        cnt = sh[0] * sh[1] * sh[2]
+        return self._view(k.value, cnt).view(sh), self._view(v.value, cnt).view(sh), n.value

@@ -1,0 +1,70 @@
+"""Compile the HIP sources into ``libwsg.so`` (in-tree, gfx950).
+
+``python -m weight_streaming_gemv_amd.build`` or ``build()`` from Python.
+Every call recompiles every source (object files go to ``_build/``).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libwsg.so")
+ARCH = os.environ.get("WSG_OFFLOAD_ARCH", "gfx950")
+
+# -packed-fp32-ops: keep the compiler from forming packed FP32 VALU ops.
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def _hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src: str, obj: str) -> str:
+    cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in line and line.strip())
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all ``csrc/*.hip`` and link ``libwsg.so``; returns its path."""
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    objs = []
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = {}
+        for f in srcs:
+            obj = os.path.join(objdir, f[:-4] + ".o")
+            objs.append(obj)
+            futs[ex.submit(_compile, os.path.join(CSRC, f), obj)] = f
+        for fu in cf.as_completed(futs):
+            msg = fu.result()
+            if verbose and msg:
+                print(f"[{futs[fu]}]\n{msg}", file=sys.stderr)
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

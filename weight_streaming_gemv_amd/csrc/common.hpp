@@ -1,0 +1,120 @@
+// Device helpers shared by the gfx950 kernels: wave64 reductions, vector
+// loads and storage-dtype conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace wsg {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;          // 4 waves per workgroup
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// ---------------------------------------------------------------- DPP sums
+// DPP control words (GFX9 encoding).
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+constexpr int kDppBcast15 = 0x142;    // row_bcast:15
+constexpr int kDppBcast31 = 0x143;    // row_bcast:31
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 ROW_MASK, 0xF, false));
+}
+
+// Sum over each row of 16 lanes; every lane of the row receives the row sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppQuadSwap1>(v);
+  v += dpp<kDppQuadSwap2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return v;
+}
+
+// Sum over the wavefront; the result is wave-uniform (read from lane 63).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += dpp<kDppBcast15, 0xA>(v);   // rows 1, 3 += last lane of rows 0, 2
+  v += dpp<kDppBcast31, 0xC>(v);   // rows 2, 3 += lane 31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppQuadSwap1>(v));
+  v = fmaxf(v, dpp<kDppQuadSwap2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ---------------------------------------------------------------- dtypes
+template <typename T> struct Store;
+template <> struct Store<float> {
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+};
+template <> struct Store<__half> {
+  static __device__ __forceinline__ float to_f(__half v) { return __half2float(v); }
+  static __device__ __forceinline__ __half from_f(float v) { return __float2half_rn(v); }
+};
+
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte vector of storage elements, widened to floats.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  float v[4];
+  template <bool NT>
+  __device__ __forceinline__ void load(const float* p) {
+    f4_t t;
+    if constexpr (NT) t = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(p));
+    else t = *reinterpret_cast<const f4_t*>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  }
+};
+template <> struct Vec16<__half> {
+  static constexpr int N = 8;
+  float v[8];
+  template <bool NT>
+  __device__ __forceinline__ void load(const __half* p) {
+    u4_t t;
+    if constexpr (NT) t = __builtin_nontemporal_load(reinterpret_cast<const u4_t*>(p));
+    else t = *reinterpret_cast<const u4_t*>(p);
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __half2float(__ushort_as_half((unsigned short)(w[i] & 0xFFFFu)));
+      v[2 * i + 1] = __half2float(__ushort_as_half((unsigned short)(w[i] >> 16)));
+    }
+  }
+};
+
+// Raw 16-byte loads (kept packed) for the FP16 dot2 path.
+template <bool NT>
+__device__ __forceinline__ uint4 load_u4(const void* p) {
+  u4_t t;
+  if constexpr (NT) t = __builtin_nontemporal_load(reinterpret_cast<const u4_t*>(p));
+  else t = *reinterpret_cast<const u4_t*>(p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
+
+// acc + a.x*b.x + a.y*b.y with FP32 accumulation (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2(h2_t a, h2_t b, float acc) {
+  return __builtin_amdgcn_fdot2(a, b, acc, false);
+}
+
+}  // namespace wsg

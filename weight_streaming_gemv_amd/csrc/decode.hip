@@ -1,0 +1,634 @@
+// Decode-step kernels for gfx950: one token through the decoder.
+//
+// The pages split a layer into eight ordered stages connected by device
+// buffers, with no host waits and no cross-workgroup spin barriers
+// (Megakernels, "GPU-wide end-to-end generation").  Here the same order is
+// kept with fewer, fused launches per layer:
+//
+//   qkv     input RMSNorm (each wave normalises the 1024-float residual in
+//           registers) + fused Q/K/V GEMV; layer 0 also gathers the token's
+//           embedding row and writes it to the residual buffer
+//   attn    per-head Q/K RMSNorm + RoPE + K/V cache write of position p +
+//           split-K grouped-query attention; the last-arriving split block
+//           of each KV head merges the partial softmax states (an atomic
+//           arrival count, no waiting)
+//   o       output GEMV + residual add
+//   gateup  post-attention RMSNorm + gate/up GEMV + SwiGLU
+//   down    down GEMV + residual add
+//   head    final RMSNorm + tied vocabulary GEMV + per-block argmax keys
+//   argmax  one block reduces the block keys; writes the token into the
+//           token history and advances the position
+//
+// Every GEMV wave owns R consecutive output rows and streams them with
+// 16-byte loads; reductions accumulate in FP32 and are combined with DPP.
+#include <type_traits>
+
+#include "common.hpp"
+#include "decode.hpp"
+
+namespace wsg {
+
+namespace {
+
+constexpr int kD = 128;          // head_dim
+constexpr float kLog2e = 1.4426950408889634f;
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Activations of length K in the lane layout the GEMV rows use:
+// a[c*VEC + i] = x[c*64*VEC + lane*VEC + i].
+template <typename TS, int K>
+struct Act {
+  static constexpr int VEC = Vec16<TS>::N;
+  static constexpr int NV = K / (kWave * VEC);
+  static_assert(K % (kWave * VEC) == 0, "K must be a multiple of 64 vectors");
+  float a[K / kWave];
+
+  __device__ __forceinline__ void load(const TS* p) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      Vec16<TS> v;
+      v.template load<false>(p + c * kWave * VEC + lane * VEC);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) a[c * VEC + i] = v.v[i];
+    }
+  }
+  __device__ __forceinline__ void store(TS* p) const {
+    const int lane = lane_id();
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) p[c * kWave * VEC + lane * VEC + i] = Store<TS>::from_f(a[c * VEC + i]);
+  }
+  // In-register RMSNorm with gain: a = a * (mean(a^2) + eps)^-1/2 * g.
+  __device__ __forceinline__ void rms_norm(const TS* gain, float eps) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < K / kWave; ++i) ss = fmaf(a[i], a[i], ss);
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)K + eps);
+    Act<TS, K> g;
+    g.load(gain);
+#pragma unroll
+    for (int i = 0; i < K / kWave; ++i) a[i] = a[i] * inv * g.a[i];
+  }
+};
+
+// acc[r] += W[row0 + r] . act for r < R (rows clamped to M-1 for loads).
+template <typename TS, int K, int R>
+__device__ __forceinline__ void rows_dot(const TS* __restrict__ W, int row0, int M, const Act<TS, K>& x,
+                                         float (&acc)[R]) {
+  constexpr int VEC = Vec16<TS>::N;
+  constexpr int NV = K / (kWave * VEC);
+  const int lane = lane_id();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const TS* wr = W + (size_t)min(row0 + r, M - 1) * K + lane * VEC;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      Vec16<TS> w;
+      w.template load<false>(wr + c * kWave * VEC);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[r] = fmaf(w.v[i], x.a[c * VEC + i], acc[r]);
+    }
+  }
+}
+
+__device__ __forceinline__ int wave_row_groups_begin() { return blockIdx.x * kWavesPerBlock + wave_id(); }
+__device__ __forceinline__ int wave_row_groups_stride() { return gridDim.x * kWavesPerBlock; }
+
+// ------------------------------------------------------------------ qkv
+template <typename TS, int H, int R>
+__global__ __launch_bounds__(kBlock) void k_qkv(const TS* __restrict__ W, const TS* __restrict__ in_norm,
+                                                TS* __restrict__ x_res, const TS* __restrict__ embed,
+                                                const int32_t* __restrict__ ids, const int32_t* __restrict__ ctrl,
+                                                int first_layer, int vocab, float eps, TS* __restrict__ out,
+                                                int M) {
+  Act<TS, H> x;
+  if (first_layer) {
+    int tok = ids[ctrl[kCtrlPos]];
+    tok = (tok < 0 || tok >= vocab) ? 0 : tok;   // ids are validated on the host; never read outside E
+    x.load(embed + (size_t)tok * H);
+    if (blockIdx.x == 0 && wave_id() == 0) x.store(x_res);
+  } else {
+    x.load(x_res);
+  }
+  x.rms_norm(in_norm, eps);
+  const int lane = lane_id();
+  const int ngroups = ceil_div(M, R);
+  for (int g = wave_row_groups_begin(); g < ngroups; g += wave_row_groups_stride()) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    rows_dot<TS, H, R>(W, g * R, M, x, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float s = wave_sum(acc[r]);
+      if (lane == 0 && g * R + r < M) out[g * R + r] = Store<TS>::from_f(s);
+    }
+  }
+}
+
+// ------------------------------------------------------------ o / down
+// x_res[m] += W[m] . in  for m < M (M = hidden).
+template <typename TS, int K, int R>
+__global__ __launch_bounds__(kBlock) void k_gemv_residual(const TS* __restrict__ W, const TS* __restrict__ in,
+                                                          TS* __restrict__ x_res, int M, int32_t* __restrict__ ctrl,
+                                                          int advance_pos) {
+  if (advance_pos && blockIdx.x == 0 && threadIdx.x == 0) ctrl[kCtrlPos] = ctrl[kCtrlPos] + 1;
+  Act<TS, K> x;
+  x.load(in);
+  const int lane = lane_id();
+  const int ngroups = ceil_div(M, R);
+  for (int g = wave_row_groups_begin(); g < ngroups; g += wave_row_groups_stride()) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    rows_dot<TS, K, R>(W, g * R, M, x, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float s = wave_sum(acc[r]);
+      const int m = g * R + r;
+      if (lane == 0 && m < M) x_res[m] = Store<TS>::from_f(Store<TS>::to_f(x_res[m]) + s);
+    }
+  }
+}
+
+// -------------------------------------------------------------- gate/up
+// act[m] = silu(Wg[m] . b) * (Wu[m] . b), b = rms(x, post_norm); Wgu holds
+// the I gate rows followed by the I up rows.
+template <typename TS, int H, int R>
+__global__ __launch_bounds__(kBlock) void k_gateup(const TS* __restrict__ Wgu, const TS* __restrict__ post_norm,
+                                                   const TS* __restrict__ x_res, float eps, TS* __restrict__ act,
+                                                   int I) {
+  Act<TS, H> x;
+  x.load(x_res);
+  x.rms_norm(post_norm, eps);
+  const int lane = lane_id();
+  const int ngroups = ceil_div(I, R);
+  for (int g = wave_row_groups_begin(); g < ngroups; g += wave_row_groups_stride()) {
+    float ga[R], ua[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ga[r] = ua[r] = 0.f;
+    rows_dot<TS, H, R>(Wgu, g * R, I, x, ga);
+    rows_dot<TS, H, R>(Wgu + (size_t)I * H, g * R, I, x, ua);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float gs = wave_sum(ga[r]);
+      const float us = wave_sum(ua[r]);
+      const int m = g * R + r;
+      if (lane == 0 && m < I) act[m] = Store<TS>::from_f(gs / (1.0f + expf(-gs)) * us);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- head
+// Argmax keys: larger key = larger logit, then lower index.  -0.0 is folded
+// into +0.0 first, so the two zeros tie.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
+  if (v == 0.0f) v = 0.0f;
+  uint32_t b = __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(k, off);
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
+template <typename TS, int H, int R>
+__global__ __launch_bounds__(kBlock) void k_head(const TS* __restrict__ E, const TS* __restrict__ final_norm,
+                                                 const TS* __restrict__ x_res, float eps, TS* __restrict__ logits,
+                                                 int V, unsigned long long* __restrict__ am_part) {
+  __shared__ unsigned long long best_wave[kWavesPerBlock];
+  Act<TS, H> x;
+  x.load(x_res);
+  x.rms_norm(final_norm, eps);
+  const int lane = lane_id();
+  unsigned long long best = 0;   // below every real key
+  const int ngroups = ceil_div(V, R);
+  for (int g = wave_row_groups_begin(); g < ngroups; g += wave_row_groups_stride()) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    rows_dot<TS, H, R>(E, g * R, V, x, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float s = wave_sum(acc[r]);
+      const int m = g * R + r;
+      if (m < V) {
+        const TS stored = Store<TS>::from_f(s);
+        if (lane == 0) logits[m] = stored;
+        const unsigned long long k = argmax_key(Store<TS>::to_f(stored), m);
+        best = k > best ? k : best;
+      }
+    }
+  }
+  if (lane == 0) best_wave[wave_id()] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long b = best_wave[0];
+#pragma unroll
+    for (int w = 1; w < kWavesPerBlock; ++w) b = best_wave[w] > b ? best_wave[w] : b;
+    am_part[blockIdx.x] = b;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_argmax(const unsigned long long* __restrict__ am_part, int n,
+                                                 int32_t* __restrict__ ctrl, int32_t* __restrict__ ids) {
+  __shared__ unsigned long long red[1024 / kWave];
+  unsigned long long b = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) b = am_part[i] > b ? am_part[i] : b;
+  b = wave_max_u64(b);
+  if (lane_id() == 0) red[threadIdx.x >> 6] = b;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) b = red[w] > b ? red[w] : b;
+    b = red[0] > b ? red[0] : b;
+    int tok = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
+    if (b == 0) tok = 0;   // no block key at all (cannot happen with vocab >= 1)
+    const int pos = ctrl[kCtrlPos];
+    ctrl[kCtrlOutTok] = tok;
+    ids[pos + 1] = tok;
+    ctrl[kCtrlPos] = pos + 1;
+  }
+}
+
+__global__ void k_set_pos(int32_t* ctrl, int pos) {
+  if (threadIdx.x == 0) ctrl[kCtrlPos] = pos;
+}
+
+// ------------------------------------------------------------ attention
+// Lane layout for one 128-wide head row: a row of 16 lanes covers one key;
+// lane sl of the row holds dims [4sl, 4sl+4) and [64+4sl, 64+4sl+4), so both
+// members of every rotary pair (i, i+64) sit in the same lane.
+template <typename TS>
+__device__ __forceinline__ void load_head8(const TS* p, int sl, float (&v)[8]) {
+  if constexpr (sizeof(TS) == 4) {
+    const float4 lo = *reinterpret_cast<const float4*>(p + 4 * sl);
+    const float4 hi = *reinterpret_cast<const float4*>(p + 64 + 4 * sl);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  } else {
+    const uint2 lo = *reinterpret_cast<const uint2*>(p + 4 * sl);
+    const uint2 hi = *reinterpret_cast<const uint2*>(p + 64 + 4 * sl);
+    const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __half2float(__ushort_as_half((unsigned short)(w[i] & 0xFFFFu)));
+      v[2 * i + 1] = __half2float(__ushort_as_half((unsigned short)(w[i] >> 16)));
+    }
+  }
+}
+
+template <typename TS>
+__device__ __forceinline__ void store_head8(TS* p, int sl, const float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[4 * sl + i] = Store<TS>::from_f(v[i]);
+    p[64 + 4 * sl + i] = Store<TS>::from_f(v[4 + i]);
+  }
+}
+
+// Per-head RMSNorm (over the 16 lanes of a row) then rotation at position p.
+template <typename TS>
+__device__ __forceinline__ void norm_rope8(float (&v)[8], const TS* gain, const float (&c)[4], const float (&s)[4],
+                                           int sl, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+  ss = row16_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)kD + eps);
+  float g[8];
+  load_head8<TS>(gain, sl, g);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = v[i] * inv * g[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = v[i], hi = v[4 + i];
+    v[i] = lo * c[i] - hi * s[i];
+    v[4 + i] = hi * c[i] + lo * s[i];
+  }
+}
+
+template <typename TS>
+__device__ __forceinline__ void round_to_store(float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = Store<TS>::to_f(Store<TS>::from_f(v[i]));
+}
+
+template <int G>
+struct SoftState {
+  float m[G], l[G], acc[G][8];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
+    }
+  }
+  // Online softmax update with one key (scores in the log2 domain).
+  __device__ __forceinline__ void add(const float (&q)[G][8], const float (&k)[8], const float (&v)[8]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d = fmaf(q[g][i], k[i], d);
+      d = row16_sum(d);
+      const float mn = fmaxf(m[g], d);
+      const float alpha = exp2f(m[g] - mn);
+      const float p = exp2f(d - mn);
+      l[g] = fmaf(l[g], alpha, p);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(acc[g][i], alpha, p * v[i]);
+      m[g] = mn;
+    }
+  }
+};
+
+// Partial state layout: for each (kv head, split, g): [m, l, acc[128]].
+constexpr int kPartStride = 2 + kD;
+
+template <typename TS, int G>
+__global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
+                                                 TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
+                                                 const TS* __restrict__ k_norm, const float* __restrict__ rope_cos,
+                                                 const float* __restrict__ rope_sin, int32_t* __restrict__ ctrl,
+                                                 int n_q, int n_kv, int cap, float eps, int min_chunk,
+                                                 float* __restrict__ part, TS* __restrict__ o) {
+  __shared__ float sm_m[16][G], sm_l[16][G];
+  __shared__ float sm_acc[16][G][kD];
+  __shared__ int sm_last;
+
+  const int j = blockIdx.y;            // KV head
+  const int split = blockIdx.x;
+  const int pos = ctrl[kCtrlPos];
+  const int n_keys = pos + 1;
+  int chunk = max(min_chunk, ceil_div(n_keys, (int)gridDim.x));
+  chunk = (chunk + 15) & ~15;
+  const int n_splits = ceil_div(n_keys, chunk);
+  if (split >= n_splits) return;
+  const int k_begin = split * chunk;
+  const int k_end = min(n_keys, k_begin + chunk);
+  const bool has_cur = (k_end == n_keys);
+  const int k_stop = has_cur ? k_end - 1 : k_end;   // cached keys [k_begin, k_stop)
+
+  const int lane = lane_id(), wave = wave_id();
+  const int row = lane >> 4, sl = lane & 15;
+  const int Q = n_q * kD, KV = n_kv * kD;
+
+  float c[4], s[4];
+  {
+    const float4 cv = *reinterpret_cast<const float4*>(rope_cos + (size_t)pos * (kD / 2) + 4 * sl);
+    const float4 sv = *reinterpret_cast<const float4*>(rope_sin + (size_t)pos * (kD / 2) + 4 * sl);
+    c[0] = cv.x; c[1] = cv.y; c[2] = cv.z; c[3] = cv.w;
+    s[0] = sv.x; s[1] = sv.y; s[2] = sv.z; s[3] = sv.w;
+  }
+  // queries of this group: normalised, rotated, rounded as stored, then
+  // pre-scaled by log2(e)/sqrt(D) so scores are in the log2 domain
+  float q[G][8];
+  const float qscale = kLog2e / sqrtf((float)kD);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    load_head8<TS>(qkv + (size_t)(j * G + g) * kD, sl, q[g]);
+    norm_rope8<TS>(q[g], q_norm, c, s, sl, eps);
+    round_to_store<TS>(q[g]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[g][i] *= qscale;
+  }
+
+  SoftState<G> st;
+  st.init();
+  const size_t head_off = (size_t)j * cap * kD;
+  for (int key = k_begin + wave * 4 + row; key < k_stop; key += 16) {
+    float kk[8], vv[8];
+    load_head8<TS>(k_cache + head_off + (size_t)key * kD, sl, kk);
+    load_head8<TS>(v_cache + head_off + (size_t)key * kD, sl, vv);
+    st.add(q, kk, vv);
+  }
+  if (has_cur) {
+    // the current token's key and value: normalise/rotate, write slot p,
+    // and fold them in from registers (row 0 of wave 0)
+    float kk[8], vv[8];
+    load_head8<TS>(qkv + Q + (size_t)j * kD, sl, kk);
+    norm_rope8<TS>(kk, k_norm, c, s, sl, eps);
+    round_to_store<TS>(kk);
+    load_head8<TS>(qkv + Q + KV + (size_t)j * kD, sl, vv);
+    if (wave == 0 && row == 0) {
+      store_head8<TS>(k_cache + head_off + (size_t)pos * kD, sl, kk);
+      store_head8<TS>(v_cache + head_off + (size_t)pos * kD, sl, vv);
+      st.add(q, kk, vv);
+    }
+  }
+
+  // merge the 16 row states of this block
+  const int sid = wave * 4 + row;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (sl == 0) { sm_m[sid][g] = st.m[g]; sm_l[sid][g] = st.l[g]; }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sm_acc[sid][g][4 * sl + i] = st.acc[g][i];
+      sm_acc[sid][g][64 + 4 * sl + i] = st.acc[g][4 + i];
+    }
+  }
+  __syncthreads();
+  float* my_part = part + ((size_t)(j * gridDim.x + split) * G) * kPartStride;
+  for (int t = threadIdx.x; t < G * kD; t += kBlock) {
+    const int g = t / kD, d = t - g * kD;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sm_m[r][g]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float w = exp2f(sm_m[r][g] - mx);   // rows without keys: exp2(-inf) = 0
+      L = fmaf(sm_l[r][g], w, L);
+      A = fmaf(sm_acc[r][g][d], w, A);
+    }
+    if (n_splits == 1) {
+      o[(size_t)(j * G + g) * kD + d] = Store<TS>::from_f(A / L);
+    } else {
+      if (d == 0) { my_part[g * kPartStride] = mx; my_part[g * kPartStride + 1] = L; }
+      my_part[g * kPartStride + 2 + d] = A;
+    }
+  }
+  if (n_splits == 1) return;
+
+  // last-arriving split of this KV head merges all partial states
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(&ctrl[kCtrlAttnCnt + j], 1);
+    sm_last = (prev == n_splits - 1);
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  __threadfence();
+  const float* head_part = part + (size_t)j * gridDim.x * G * kPartStride;
+  for (int t = threadIdx.x; t < G * kD; t += kBlock) {
+    const int g = t / kD, d = t - g * kD;
+    float mx = -INFINITY;
+    for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, head_part[(size_t)(sp * G + g) * kPartStride]);
+    float L = 0.f, A = 0.f;
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const float* ps = head_part + (size_t)(sp * G + g) * kPartStride;
+      const float w = exp2f(ps[0] - mx);
+      L = fmaf(ps[1], w, L);
+      A = fmaf(ps[2 + d], w, A);
+    }
+    o[(size_t)(j * G + g) * kD + d] = Store<TS>::from_f(A / L);
+  }
+  if (threadIdx.x == 0) ctrl[kCtrlAttnCnt + j] = 0;
+}
+
+// --------------------------------------------------------------- dispatch
+int blocks_for(int M, int R, int grid) {
+  const int one_shot = ceil_div(ceil_div(M, R), kWavesPerBlock);
+  return (grid > 0 && grid < one_shot) ? grid : one_shot;
+}
+
+// K values compiled in; a K must also be a multiple of 64 16-byte vectors
+// of the storage type (256 floats, 512 halves).
+template <int V> using IC = std::integral_constant<int, V>;
+
+template <typename TS, int K, typename F>
+bool call_k(F& f) {
+  if constexpr (K % (kWave * Vec16<TS>::N) == 0) return f(IC<K>{});
+  else return false;
+}
+template <typename TS, typename F>
+bool with_k(int K, F&& f) {
+  switch (K) {
+    case 256: return call_k<TS, 256>(f);
+    case 512: return call_k<TS, 512>(f);
+    case 1024: return call_k<TS, 1024>(f);
+    case 2048: return call_k<TS, 2048>(f);
+    case 3072: return call_k<TS, 3072>(f);
+    default: return false;
+  }
+}
+template <typename F>
+bool with_r(int R, F&& f) {
+  switch (R) {
+    case 1: return f(IC<1>{});
+    case 2: return f(IC<2>{});
+    case 4: return f(IC<4>{});
+    default: return false;
+  }
+}
+
+template <typename TS>
+bool qkv_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, hipStream_t s) {
+  const int M = (a.n_q + 2 * a.n_kv) * a.head_dim;
+  const int grid = blocks_for(M, sh.rows_qkv, sh.grid_qkv);
+  return with_k<TS>(a.hidden, [&](auto kc) {
+    return with_r(sh.rows_qkv, [&](auto rc) {
+      hipLaunchKernelGGL((k_qkv<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock), 0, s,
+                         (const TS*)L.wqkv, (const TS*)L.in_norm, (TS*)a.x, (const TS*)a.embed, a.ids, a.ctrl,
+                         first ? 1 : 0, a.vocab, a.eps, (TS*)a.qkv, M);
+      return true;
+    });
+  });
+}
+
+template <typename TS>
+bool residual_t(const DecodeArgs& a, int K, int R, int grid_req, const void* W, const void* in, bool adv,
+                hipStream_t s) {
+  const int grid = blocks_for(a.hidden, R, grid_req);
+  return with_k<TS>(K, [&](auto kc) {
+    return with_r(R, [&](auto rc) {
+      hipLaunchKernelGGL((k_gemv_residual<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock),
+                         0, s, (const TS*)W, (const TS*)in, (TS*)a.x, a.hidden, a.ctrl, adv ? 1 : 0);
+      return true;
+    });
+  });
+}
+
+template <typename TS>
+bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+  const int grid = blocks_for(a.inter, sh.rows_gu, sh.grid_gu);
+  return with_k<TS>(a.hidden, [&](auto kc) {
+    return with_r(sh.rows_gu, [&](auto rc) {
+      hipLaunchKernelGGL((k_gateup<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock), 0, s,
+                         (const TS*)L.wgu, (const TS*)L.post_norm, (const TS*)a.x, a.eps, (TS*)a.act, a.inter);
+      return true;
+    });
+  });
+}
+
+template <typename TS>
+bool head_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
+  const int grid = blocks_for(a.vocab, sh.rows_head, sh.grid_head);
+  return with_k<TS>(a.hidden, [&](auto kc) {
+    return with_r(sh.rows_head, [&](auto rc) {
+      hipLaunchKernelGGL((k_head<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock), 0, s,
+                         (const TS*)a.embed, (const TS*)a.final_norm, (const TS*)a.x, a.eps, (TS*)a.logits, a.vocab,
+                         a.am_part);
+      return true;
+    });
+  });
+}
+
+template <typename TS>
+bool attn_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+  const int G = a.n_q / a.n_kv;
+  const dim3 grid(sh.attn_splits, a.n_kv);
+  auto go = [&](auto gc) {
+    hipLaunchKernelGGL((k_attn<TS, decltype(gc)::value>), grid, dim3(kBlock), 0, s, (const TS*)a.qkv,
+                       (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm, a.rope_cos,
+                       a.rope_sin, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, sh.attn_min_chunk, a.attn_part, (TS*)a.o);
+    return true;
+  };
+  switch (G) {
+    case 1: return go(IC<1>{});
+    case 2: return go(IC<2>{});
+    case 4: return go(IC<4>{});
+    default: return false;
+  }
+}
+
+}  // namespace
+
+int head_blocks(const DecodeArgs& a, const DecodeShape& sh) { return blocks_for(a.vocab, sh.rows_head, sh.grid_head); }
+
+bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, hipStream_t s) {
+  return a.dtype == 0 ? qkv_t<float>(a, sh, L, first, s) : qkv_t<__half>(a, sh, L, first, s);
+}
+bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+  return a.dtype == 0 ? attn_t<float>(a, sh, L, s) : attn_t<__half>(a, sh, L, s);
+}
+bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+  const int K = a.n_q * a.head_dim;
+  return a.dtype == 0 ? residual_t<float>(a, K, sh.rows_o, sh.grid_o, L.wo, a.o, false, s)
+                      : residual_t<__half>(a, K, sh.rows_o, sh.grid_o, L.wo, a.o, false, s);
+}
+bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+  return a.dtype == 0 ? gateup_t<float>(a, sh, L, s) : gateup_t<__half>(a, sh, L, s);
+}
+bool launch_down(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool adv, hipStream_t s) {
+  return a.dtype == 0 ? residual_t<float>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, a.act, adv, s)
+                      : residual_t<__half>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, a.act, adv, s);
+}
+bool launch_head(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
+  return a.dtype == 0 ? head_t<float>(a, sh, s) : head_t<__half>(a, sh, s);
+}
+bool launch_argmax(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax, dim3(1), dim3(1024), 0, s, (const unsigned long long*)a.am_part,
+                     head_blocks(a, sh), a.ctrl, a.ids);
+  return true;
+}
+bool launch_set_pos(int32_t* ctrl, int pos, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_pos, dim3(1), dim3(64), 0, s, ctrl, pos);
+  return true;
+}
+
+}  // namespace wsg

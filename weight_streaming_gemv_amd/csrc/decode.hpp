@@ -1,0 +1,72 @@
+// Launch interface of the decode-step kernels (one token through one layer,
+// and the vocabulary head).  Arguments are validated by the runtime.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wsg {
+
+// Control words in the workspace (int32 each).
+enum CtrlWord : int {
+  kCtrlPos = 0,        // current position p (tokens already in the cache)
+  kCtrlOutTok = 1,     // last greedy token
+  kCtrlAttnCnt = 16,   // [n_kv] arrival counters of the split-K attention merge
+  kCtrlWords = 64
+};
+
+struct LayerPtrs {
+  const void* wqkv;     // [(Q + 2 KV)][H]
+  const void* wo;       // [H][Q]
+  const void* wgu;      // [2 I][H]  gate rows then up rows
+  const void* wd;       // [H][I]
+  const void* in_norm;  // [H]
+  const void* post_norm;
+  const void* q_norm;   // [D]
+  const void* k_norm;
+  void* k_cache;        // [n_kv][cap][D]
+  void* v_cache;
+};
+
+struct DecodeArgs {
+  int dtype;            // 0 FP32, 1 FP16 storage
+  int hidden, inter, n_q, n_kv, head_dim, vocab, cap;
+  float eps;
+  const void* embed;    // [V][H]
+  const void* final_norm;
+  const float* rope_cos;  // [cap][D/2]
+  const float* rope_sin;
+  void* x;              // residual [H]
+  void* qkv;            // [Q + 2 KV]
+  void* o;              // [Q]
+  void* act;            // [I]
+  void* logits;         // [V]
+  float* attn_part;     // split-K partial states
+  int attn_part_splits; // capacity in splits per KV head
+  unsigned long long* am_part;  // per-block argmax keys of the head
+  int am_part_cap;
+  int32_t* ctrl;
+  int32_t* ids;         // token history [cap + 1]
+};
+
+// Grid shapes chosen by the runtime.
+struct DecodeShape {
+  int rows_qkv, rows_o, rows_gu, rows_down, rows_head;   // rows per wave
+  int grid_qkv, grid_o, grid_gu, grid_down, grid_head;   // blocks (0 = one row group per wave)
+  int attn_splits;                                       // split-K blocks per KV head (grid.x)
+  int attn_min_chunk;                                    // fewest keys per split
+};
+
+// Stage launches; each returns false if the shape is not compiled in.
+bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first_layer, hipStream_t s);
+bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
+bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
+bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
+bool launch_down(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool advance_pos, hipStream_t s);
+bool launch_head(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s);
+bool launch_argmax(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s);
+bool launch_set_pos(int32_t* ctrl, int pos, hipStream_t s);
+
+// Blocks the head launch uses for a given shape (for sizing am_part).
+int head_blocks(const DecodeArgs& a, const DecodeShape& sh);
+
+}  // namespace wsg

@@ -1,0 +1,413 @@
+// Weight-streaming GEMV family for gfx950: FP32 and FP16 weights, int4
+// group-64 weights, one or two input vectors, R output rows per wavefront.
+//
+// One wavefront owns a group of R consecutive output rows and streams those
+// rows with 16-byte loads, 64 lanes side by side, so each wave-wide load
+// instruction reads 1 KiB of contiguous weights.  Partial sums stay in
+// lanes (FP32) and are combined with DPP row operations at the end.  The
+// design follows the row-per-SIMD-group GEMV of Megakernels ("GPU-wide
+// end-to-end generation") re-shaped for 64-lane waves, with R as the tuning
+// constant of Our Kernel Benchmark Was Measuring the System Cache ("Why it
+// mattered": fewer rows per group give more loads in flight when the
+// weights come from DRAM).
+#include "common.hpp"
+#include "gemv.hpp"
+
+namespace wsg {
+
+// ------------------------------------------------------------ FP32, fixed K
+template <int K, int R, int T, bool NT>
+__global__ __launch_bounds__(kBlock) void k_gemv_f32(const float* __restrict__ W,
+                                                     const float* __restrict__ X,
+                                                     float* __restrict__ Y, int M) {
+  constexpr int NV = K / 256;  // float4 chunks per lane per row
+  static_assert(K % 256 == 0, "K must be a multiple of 256");
+  const int lane = lane_id();
+  float4 x[T][NV];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < NV; ++c) x[t][c] = *reinterpret_cast<const float4*>(X + t * K + c * 256 + lane * 4);
+
+  const int ngroups = (M + R - 1) / R;
+  for (int g = blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += gridDim.x * kWavesPerBlock) {
+    const int row0 = g * R;
+    float acc[R][T];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float* wr = W + (size_t)min(row0 + r, M - 1) * K + lane * 4;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        Vec16<float> w;
+        w.load<NT>(wr + c * 256);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          float a = acc[r][t];
+          a = fmaf(w.v[0], x[t][c].x, a);
+          a = fmaf(w.v[1], x[t][c].y, a);
+          a = fmaf(w.v[2], x[t][c].z, a);
+          a = fmaf(w.v[3], x[t][c].w, a);
+          acc[r][t] = a;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float s = wave_sum(acc[r][t]);
+        if (lane == 0 && row0 + r < M) Y[(size_t)t * M + row0 + r] = s;
+      }
+  }
+}
+
+// ------------------------------------------------------------ FP16, fixed K
+// Weights and activations stay packed as half pairs; v_dot2_f32_f16 forms
+// the exact FP16 products and adds them into an FP32 accumulator.
+template <int K, int R, int T, bool NT>
+__global__ __launch_bounds__(kBlock) void k_gemv_f16(const __half* __restrict__ W,
+                                                     const __half* __restrict__ X,
+                                                     float* __restrict__ Y, int M) {
+  constexpr int NV = K / 512;  // 8-half chunks per lane per row
+  static_assert(K % 512 == 0, "K must be a multiple of 512");
+  const int lane = lane_id();
+  uint4 x[T][NV];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < NV; ++c) x[t][c] = *reinterpret_cast<const uint4*>(X + t * K + c * 512 + lane * 8);
+
+  const int ngroups = (M + R - 1) / R;
+  for (int g = blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += gridDim.x * kWavesPerBlock) {
+    const int row0 = g * R;
+    float acc[R][T];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const __half* wr = W + (size_t)min(row0 + r, M - 1) * K + lane * 8;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        const uint4 w = load_u4<NT>(wr + c * 512);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          float a = acc[r][t];
+          a = dot2(as_h2(w.x), as_h2(x[t][c].x), a);
+          a = dot2(as_h2(w.y), as_h2(x[t][c].y), a);
+          a = dot2(as_h2(w.z), as_h2(x[t][c].z), a);
+          a = dot2(as_h2(w.w), as_h2(x[t][c].w), a);
+          acc[r][t] = a;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float s = wave_sum(acc[r][t]);
+        if (lane == 0 && row0 + r < M) Y[(size_t)t * M + row0 + r] = s;
+      }
+  }
+}
+
+// ------------------------------------------------- any K (multiple of VEC)
+// Run-time K: full 64-lane chunks plus a partial last chunk; activations are
+// read from global memory (cached) instead of registers.
+template <typename TW, int R, int T>
+__global__ __launch_bounds__(kBlock) void k_gemv_anyk(const TW* __restrict__ W, const TW* __restrict__ X,
+                                                      float* __restrict__ Y, int M, int K) {
+  constexpr int VEC = Vec16<TW>::N;
+  const int lane = lane_id();
+  const int ngroups = (M + R - 1) / R;
+  for (int g = blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += gridDim.x * kWavesPerBlock) {
+    const int row0 = g * R;
+    float acc[R][T];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
+    for (int k = lane * VEC; k < K; k += kWave * VEC) {
+      Vec16<TW> xv[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) xv[t].template load<false>(X + (size_t)t * K + k);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        Vec16<TW> w;
+        w.template load<false>(W + (size_t)min(row0 + r, M - 1) * K + k);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[r][t] = fmaf(w.v[i], xv[t].v[i], acc[r][t]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float s = wave_sum(acc[r][t]);
+        if (lane == 0 && row0 + r < M) Y[(size_t)t * M + row0 + r] = s;
+      }
+  }
+}
+
+// ------------------------------------------------- scalar fallback (any K)
+template <typename TW, int T>
+__global__ __launch_bounds__(kBlock) void k_gemv_scalar(const TW* __restrict__ W, const TW* __restrict__ X,
+                                                        float* __restrict__ Y, int M, int K) {
+  const int lane = lane_id();
+  for (int row = blockIdx.x * kWavesPerBlock + wave_id(); row < M; row += gridDim.x * kWavesPerBlock) {
+    float acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = 0.f;
+    for (int k = lane; k < K; k += kWave) {
+      const float w = Store<TW>::to_f(W[(size_t)row * K + k]);
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[t] = fmaf(w, Store<TW>::to_f(X[(size_t)t * K + k]), acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0) Y[(size_t)t * M + row] = s;
+    }
+  }
+}
+
+// ------------------------------------------------------------ int4 group-64
+// Each lane reads 16 bytes = 32 consecutive weights = half of one group, so a
+// lane needs exactly one scale per chunk.  Nibbles are decoded two at a time
+// into FP16 pairs by OR-ing them under the exponent of 1024 and subtracting
+// 1032 (after flipping bit 3, which maps two's complement onto offset
+// binary); every step is exact.  The activations are staged once per
+// workgroup in LDS, permuted so that each FP16 pair lines up with the
+// nibble pair (j, j+4) that one 32-bit word yields.
+template <int K, int R, int T, bool NT>
+__global__ __launch_bounds__(kBlock) void k_gemv_q4(const uint32_t* __restrict__ Wq,
+                                                    const __half* __restrict__ S,
+                                                    const __half* __restrict__ X,
+                                                    float* __restrict__ Y, int M) {
+  constexpr int NV = K / 2048;   // 16-byte chunks per lane per row
+  constexpr int W8 = K / 8;      // words per row
+  constexpr int G = K / 64;      // groups (scales) per row
+  static_assert(K % 2048 == 0, "fixed-K int4 kernel needs K % 2048 == 0");
+  __shared__ uint4 xs[T][W8];
+  for (int i = threadIdx.x; i < T * W8; i += kBlock) {
+    const int t = i / W8, gi = i - t * W8;
+    const uint4 h = *reinterpret_cast<const uint4*>(X + (size_t)t * K + gi * 8);
+    // halves 0..7 -> pairs (0,4) (1,5) (2,6) (3,7)
+    uint4 p;
+    p.x = (h.x & 0xFFFFu) | (h.z << 16);
+    p.y = (h.x >> 16) | (h.z & 0xFFFF0000u);
+    p.z = (h.y & 0xFFFFu) | (h.w << 16);
+    p.w = (h.y >> 16) | (h.w & 0xFFFF0000u);
+    xs[t][gi] = p;
+  }
+  __syncthreads();
+
+  const int lane = lane_id();
+  const h2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const int ngroups = (M + R - 1) / R;
+  for (int g = blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += gridDim.x * kWavesPerBlock) {
+    const int row0 = g * R;
+    float acc[R][T];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const size_t row = (size_t)min(row0 + r, M - 1);
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        const uint4 w = load_u4<NT>(Wq + row * W8 + c * 256 + lane * 4);
+        const float sc = __half2float(S[row * G + c * 32 + (lane >> 1)]);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        float inner[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) inner[t] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t v = ww[i] ^ 0x88888888u;
+          const h2_t p0 = as_h2((v & 0x000F000Fu) | 0x64006400u) - bias;
+          const h2_t p1 = as_h2(((v >> 4) & 0x000F000Fu) | 0x64006400u) - bias;
+          const h2_t p2 = as_h2(((v >> 8) & 0x000F000Fu) | 0x64006400u) - bias;
+          const h2_t p3 = as_h2(((v >> 12) & 0x000F000Fu) | 0x64006400u) - bias;
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const uint4 xv = xs[t][c * 256 + lane * 4 + i];
+            float a = inner[t];
+            a = dot2(p0, as_h2(xv.x), a);
+            a = dot2(p1, as_h2(xv.y), a);
+            a = dot2(p2, as_h2(xv.z), a);
+            a = dot2(p3, as_h2(xv.w), a);
+            inner[t] = a;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[r][t] = fmaf(sc, inner[t], acc[r][t]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float s = wave_sum(acc[r][t]);
+        if (lane == 0 && row0 + r < M) Y[(size_t)t * M + row0 + r] = s;
+      }
+  }
+}
+
+// int4, any K % 64 == 0: one 16-byte chunk per lane per step, run-time loop;
+// activations read directly from global memory.
+template <int R, int T>
+__global__ __launch_bounds__(kBlock) void k_gemv_q4_anyk(const uint32_t* __restrict__ Wq,
+                                                         const __half* __restrict__ S,
+                                                         const __half* __restrict__ X,
+                                                         float* __restrict__ Y, int M, int K) {
+  const int lane = lane_id();
+  const int W8 = K / 8, G = K / 64;
+  const int ngroups = (M + R - 1) / R;
+  for (int g = blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += gridDim.x * kWavesPerBlock) {
+    const int row0 = g * R;
+    float acc[R][T];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
+    // word index = 4*lane + 256*step; K/8 words per row, multiple of 8
+    for (int wi = lane * 4; wi < W8; wi += kWave * 4) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const size_t row = (size_t)min(row0 + r, M - 1);
+        const uint4 w = *reinterpret_cast<const uint4*>(Wq + row * W8 + wi);
+        const float sc = __half2float(S[row * G + wi / 8]);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          float inner = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t v = ww[i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int q = (int)((v >> (4 * j)) & 0xFu);
+              const float qf = (float)(q >= 8 ? q - 16 : q);
+              inner = fmaf(qf, __half2float(X[(size_t)t * K + (wi + i) * 8 + j]), inner);
+            }
+          }
+          acc[r][t] = fmaf(sc, inner, acc[r][t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float s = wave_sum(acc[r][t]);
+        if (lane == 0 && row0 + r < M) Y[(size_t)t * M + row0 + r] = s;
+      }
+  }
+}
+
+// ------------------------------------------------------------ dispatch
+namespace {
+
+int default_grid(int M, int R, int grid_blocks) {
+  const int ngroups = (M + R - 1) / R;
+  const int one_shot = (ngroups + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (grid_blocks > 0) return grid_blocks < one_shot ? grid_blocks : one_shot;
+  return one_shot;
+}
+
+#define WSG_LAUNCH_FIXED(KERNEL, KK)                                                         \
+  if (K == KK) {                                                                             \
+    if (nt) hipLaunchKernelGGL((KERNEL<KK, R, T, true>), dim3(grid), dim3(kBlock), 0, s, W, X, Y, M);  \
+    else hipLaunchKernelGGL((KERNEL<KK, R, T, false>), dim3(grid), dim3(kBlock), 0, s, W, X, Y, M);    \
+    return true;                                                                             \
+  }
+
+template <int R, int T>
+bool launch_f32_fixed(int M, int K, int grid, bool nt, const float* W, const float* X, float* Y, hipStream_t s) {
+  WSG_LAUNCH_FIXED(k_gemv_f32, 1024)
+  WSG_LAUNCH_FIXED(k_gemv_f32, 2048)
+  WSG_LAUNCH_FIXED(k_gemv_f32, 3072)
+  return false;
+}
+template <int R, int T>
+bool launch_f16_fixed(int M, int K, int grid, bool nt, const __half* W, const __half* X, float* Y, hipStream_t s) {
+  WSG_LAUNCH_FIXED(k_gemv_f16, 1024)
+  WSG_LAUNCH_FIXED(k_gemv_f16, 2048)
+  WSG_LAUNCH_FIXED(k_gemv_f16, 3072)
+  return false;
+}
+#undef WSG_LAUNCH_FIXED
+
+template <int R, int T>
+void launch_dense(int dtype, int M, int K, int grid_req, bool nt, const void* W, const void* X, float* Y,
+                  hipStream_t s) {
+  const int grid = default_grid(M, R, grid_req);
+  if (dtype == 0) {
+    const float* w = static_cast<const float*>(W);
+    const float* x = static_cast<const float*>(X);
+    if (launch_f32_fixed<R, T>(M, K, grid, nt, w, x, Y, s)) return;
+    if (K % 4 == 0) hipLaunchKernelGGL((k_gemv_anyk<float, R, T>), dim3(grid), dim3(kBlock), 0, s, w, x, Y, M, K);
+    else hipLaunchKernelGGL((k_gemv_scalar<float, T>), dim3(default_grid(M, 1, grid_req)), dim3(kBlock), 0, s, w, x, Y, M, K);
+  } else {
+    const __half* w = static_cast<const __half*>(W);
+    const __half* x = static_cast<const __half*>(X);
+    if (launch_f16_fixed<R, T>(M, K, grid, nt, w, x, Y, s)) return;
+    if (K % 8 == 0) hipLaunchKernelGGL((k_gemv_anyk<__half, R, T>), dim3(grid), dim3(kBlock), 0, s, w, x, Y, M, K);
+    else hipLaunchKernelGGL((k_gemv_scalar<__half, T>), dim3(default_grid(M, 1, grid_req)), dim3(kBlock), 0, s, w, x, Y, M, K);
+  }
+}
+
+template <int R, int T>
+void launch_q4(int M, int K, int grid_req, bool nt, const uint32_t* Wq, const __half* S, const __half* X,
+               float* Y, hipStream_t s) {
+  const int grid = default_grid(M, R, grid_req);
+#define WSG_Q4(KK)                                                                                         \
+  if (K == KK) {                                                                                           \
+    if (nt) hipLaunchKernelGGL((k_gemv_q4<KK, R, T, true>), dim3(grid), dim3(kBlock), 0, s, Wq, S, X, Y, M); \
+    else hipLaunchKernelGGL((k_gemv_q4<KK, R, T, false>), dim3(grid), dim3(kBlock), 0, s, Wq, S, X, Y, M);  \
+    return;                                                                                                \
+  }
+  WSG_Q4(4096)
+  WSG_Q4(14336)
+#undef WSG_Q4
+  hipLaunchKernelGGL((k_gemv_q4_anyk<R, T>), dim3(grid), dim3(kBlock), 0, s, Wq, S, X, Y, M, K);
+}
+
+}  // namespace
+
+void gemv_dispatch(int dtype, int M, int K, int T, int R, int grid, int flags, const void* W, const void* X,
+                   float* Y, hipStream_t s) {
+  const bool nt = (flags & 1) != 0;
+#define WSG_DR(RR)                                                             \
+  case RR:                                                                     \
+    if (T == 1) launch_dense<RR, 1>(dtype, M, K, grid, nt, W, X, Y, s);        \
+    else launch_dense<RR, 2>(dtype, M, K, grid, nt, W, X, Y, s);               \
+    break;
+  switch (R) { WSG_DR(1) WSG_DR(2) WSG_DR(4) WSG_DR(8) default: break; }
+#undef WSG_DR
+}
+
+void gemv_q4_dispatch(int M, int K, int T, int R, int grid, int flags, const uint32_t* Wq, const void* S,
+                      const void* X, float* Y, hipStream_t s) {
+  const bool nt = (flags & 1) != 0;
+  const __half* sc = static_cast<const __half*>(S);
+  const __half* x = static_cast<const __half*>(X);
+#define WSG_QR(RR)                                                             \
+  case RR:                                                                     \
+    if (T == 1) launch_q4<RR, 1>(M, K, grid, nt, Wq, sc, x, Y, s);             \
+    else launch_q4<RR, 2>(M, K, grid, nt, Wq, sc, x, Y, s);                    \
+    break;
+  switch (R) { WSG_QR(1) WSG_QR(2) WSG_QR(4) WSG_QR(8) default: break; }
+#undef WSG_QR
+}
+
+}  // namespace wsg

@@ -1,0 +1,579 @@
+// Runtime of the decode engine: packed-weight and workspace layouts, model
+// creation, the ordered stage plan per token (captured once into HIP graphs
+// and replayed), prefill and step, and the C ABI around them.
+//
+// The host packs weights and precomputes the rotary table once, outside
+// any timed region, and runs no layer arithmetic (Megakernels, "What runs
+// in the DSL").  Per token the host launches one graph and reads back the
+// 4-byte token id, the only synchronisation (Megakernels, "GPU-wide
+// end-to-end generation").
+#include <math.h>
+#include <string.h>
+
+#include <map>
+#include <vector>
+
+#include "../../include/wsg.h"
+#include "decode.hpp"
+#include "prefill.hpp"
+#include "status.hpp"
+
+namespace wsg {
+
+thread_local char g_last_error[512];
+
+namespace {
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Dims {
+  int L, H, I, nq, nkv, D, V, cap, chunk, Q, KV, G;
+  size_t es;   // storage element bytes
+};
+
+Dims dims_of(const wsg_config& c) {
+  Dims d;
+  d.L = c.n_layers; d.H = c.hidden; d.I = c.intermediate; d.nq = c.n_q_heads; d.nkv = c.n_kv_heads;
+  d.D = c.head_dim; d.V = c.vocab; d.cap = c.max_context; d.chunk = c.prefill_chunk;
+  d.Q = d.nq * d.D; d.KV = d.nkv * d.D; d.G = d.nkv > 0 ? d.nq / d.nkv : 0;
+  d.es = c.dtype == WSG_F16 ? 2 : 4;
+  return d;
+}
+
+bool dim_ok(int v, int dtype) {
+  if (dtype == WSG_F32 && v == 256) return true;
+  return v == 512 || v == 1024 || v == 2048 || v == 3072;
+}
+
+wsg_status validate_config(const wsg_config* c) {
+  if (!c) return fail(WSG_ERR_INVALID_ARG, "config is NULL");
+  if (c->dtype != WSG_F32 && c->dtype != WSG_F16) return fail(WSG_ERR_INVALID_ARG, "dtype %d", c->dtype);
+  if (c->n_layers < 1 || c->vocab < 1 || c->max_context < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1)
+    return fail(WSG_ERR_INVALID_ARG, "sizes must be positive");
+  if (c->prefill_chunk < 0 || c->prefill_chunk > 4096) return fail(WSG_ERR_INVALID_ARG, "prefill_chunk must be in [0, 4096]");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f)) return fail(WSG_ERR_INVALID_ARG, "rms_eps and rope_theta must be > 0");
+  if (c->head_dim != 128) return fail(WSG_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", c->head_dim);
+  if (c->n_q_heads % c->n_kv_heads != 0) return fail(WSG_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4) return fail(WSG_ERR_UNSUPPORTED, "query group size %d not in {1,2,4}", G);
+  if (!dim_ok(c->hidden, c->dtype) || !dim_ok(c->intermediate, c->dtype) ||
+      !dim_ok(c->n_q_heads * c->head_dim, c->dtype))
+    return fail(WSG_ERR_UNSUPPORTED, "hidden/intermediate/query width must be in {512,1024,2048,3072}%s",
+                c->dtype == WSG_F32 ? " or 256" : "");
+  if ((int64_t)c->max_context > (1 << 20)) return fail(WSG_ERR_UNSUPPORTED, "max_context too large");
+  return WSG_OK;
+}
+
+// ------------------------------------------------------------ layouts
+struct LayerOff { size_t in_norm, post_norm, q_norm, k_norm, wqkv, wo, wgu, wd; };
+struct PackedLayout {
+  size_t embed = 0, final_norm = 0, total = 0;
+  std::vector<LayerOff> layers;
+};
+
+PackedLayout packed_layout(const Dims& d) {
+  PackedLayout p;
+  size_t off = 0;
+  auto take = [&](size_t elems) { const size_t o = off; off = align256(off + elems * d.es); return o; };
+  p.embed = take((size_t)d.V * d.H);
+  p.final_norm = take(d.H);
+  for (int l = 0; l < d.L; ++l) {
+    LayerOff lo;
+    lo.in_norm = take(d.H);
+    lo.post_norm = take(d.H);
+    lo.q_norm = take(d.D);
+    lo.k_norm = take(d.D);
+    lo.wqkv = take((size_t)(d.Q + 2 * d.KV) * d.H);
+    lo.wo = take((size_t)d.H * d.Q);
+    lo.wgu = take((size_t)2 * d.I * d.H);
+    lo.wd = take((size_t)d.H * d.I);
+    p.layers.push_back(lo);
+  }
+  p.total = off;
+  return p;
+}
+
+constexpr int kAmPartCap = 65536;
+constexpr int kMinAttnChunk = 64;
+
+int attn_split_cap(const Dims& d) {
+  int s = 1;
+  while (s < 128 && (int64_t)s * kMinAttnChunk < d.cap) s <<= 1;
+  return s;
+}
+
+struct WsLayout {
+  size_t kv = 0, rope_cos = 0, rope_sin = 0, x = 0, qkv = 0, o = 0, act = 0, logits = 0;
+  size_t attn_part = 0, am_part = 0, ctrl = 0, ids = 0, total = 0;
+  PrefillLayout pf;
+  int attn_splits_cap = 1;
+};
+
+WsLayout ws_layout(const Dims& d) {
+  WsLayout w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
+  w.kv = take((size_t)d.L * 2 * d.nkv * d.cap * d.D * d.es);
+  w.rope_cos = take((size_t)d.cap * (d.D / 2) * 4);
+  w.rope_sin = take((size_t)d.cap * (d.D / 2) * 4);
+  w.x = take((size_t)d.H * d.es);
+  w.qkv = take((size_t)(d.Q + 2 * d.KV) * d.es);
+  w.o = take((size_t)d.Q * d.es);
+  w.act = take((size_t)d.I * d.es);
+  w.logits = take((size_t)d.V * d.es);
+  w.attn_splits_cap = attn_split_cap(d);
+  w.attn_part = take((size_t)d.nkv * w.attn_splits_cap * d.G * (2 + d.D) * 4);
+  w.am_part = take((size_t)kAmPartCap * 8);
+  w.ctrl = take((size_t)kCtrlWords * 4);
+  w.ids = take((size_t)(d.cap + 1) * 4);
+  const size_t pf_base = off;
+  w.pf = prefill_layout(d.chunk, d.H, d.I, d.Q, d.KV, d.es, pf_base);
+  off = align256(pf_base + w.pf.total);
+  w.total = off;
+  return w;
+}
+
+int pow2_ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
+
+}  // namespace
+}  // namespace wsg
+
+using namespace wsg;
+
+struct wsg_model {
+  wsg_config cfg;
+  Dims d;
+  hipStream_t stream = nullptr;
+  bool own_stream = false;
+  const uint8_t* packed = nullptr;
+  uint8_t* ws = nullptr;
+  PackedLayout pl;
+  WsLayout wl;
+  DecodeArgs args;
+  DecodeShape shape;
+  std::vector<LayerPtrs> layers;
+  int32_t pos = 0;
+  bool has_output = false;
+  int32_t* pin = nullptr;          // pinned staging: [0] token out, [1..] ids in
+  bool use_graph = true;
+  std::map<int, hipGraphExec_t> graphs;   // key: splits*2 + head
+  int timed_stage = -1;
+  std::vector<hipEvent_t> ev;
+  int ev_used = 0;
+  int64_t timed_bytes_per_launch_sum = 0;
+  double acc_ms = 0;
+  int64_t acc_launches = 0, acc_bytes = 0;
+  int prefill_rows = 0;
+};
+
+namespace {
+
+int64_t stage_bytes(const wsg_model* m, int stage) {
+  const Dims& d = m->d;
+  switch (stage) {
+    case WSG_STAGE_QKV: return (int64_t)(d.Q + 2 * d.KV) * d.H * d.es;
+    case WSG_STAGE_O: return (int64_t)d.H * d.Q * d.es;
+    case WSG_STAGE_GATEUP: return (int64_t)2 * d.I * d.H * d.es;
+    case WSG_STAGE_DOWN: return (int64_t)d.H * d.I * d.es;
+    case WSG_STAGE_HEAD: return (int64_t)d.V * d.H * d.es;
+    default: return 0;
+  }
+}
+
+// Launch one stage, bracketed by events when it is the timed stage kind.
+template <typename F>
+bool timed(wsg_model* m, int stage, F&& launch) {
+  const bool t = (m->timed_stage == stage) && (m->ev_used + 2 <= (int)m->ev.size());
+  if (t) (void)hipEventRecord(m->ev[m->ev_used], m->stream);
+  const bool ok = launch();
+  if (t) {
+    (void)hipEventRecord(m->ev[m->ev_used + 1], m->stream);
+    m->ev_used += 2;
+    m->timed_bytes_per_launch_sum += stage_bytes(m, stage);
+  }
+  return ok;
+}
+
+bool enqueue_forward(wsg_model* m, bool head, int splits) {
+  DecodeShape sh = m->shape;
+  sh.attn_splits = splits;
+  const hipStream_t s = m->stream;
+  const int L = m->d.L;
+  m->ev_used = 0;
+  m->timed_bytes_per_launch_sum = 0;
+  for (int l = 0; l < L; ++l) {
+    const LayerPtrs& lp = m->layers[l];
+    if (!timed(m, WSG_STAGE_QKV, [&] { return launch_qkv(m->args, sh, lp, l == 0, s); })) return false;
+    if (!timed(m, WSG_STAGE_ATTN, [&] { return launch_attn(m->args, sh, lp, s); })) return false;
+    if (!timed(m, WSG_STAGE_O, [&] { return launch_o(m->args, sh, lp, s); })) return false;
+    if (!timed(m, WSG_STAGE_GATEUP, [&] { return launch_gateup(m->args, sh, lp, s); })) return false;
+    if (!timed(m, WSG_STAGE_DOWN, [&] { return launch_down(m->args, sh, lp, !head && l == L - 1, s); })) return false;
+  }
+  if (head) {
+    if (!timed(m, WSG_STAGE_HEAD, [&] { return launch_head(m->args, sh, s); })) return false;
+    if (!timed(m, WSG_STAGE_ARGMAX, [&] { return launch_argmax(m->args, sh, s); })) return false;
+  }
+  return true;
+}
+
+int splits_for(const wsg_model* m, int n_keys) {
+  const int want = pow2_ceil((n_keys + kMinAttnChunk - 1) / kMinAttnChunk);
+  return want < m->wl.attn_splits_cap ? want : m->wl.attn_splits_cap;
+}
+
+void drop_graphs(wsg_model* m) {
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  m->graphs.clear();
+}
+
+// Enqueue one token forward at the current device position.
+wsg_status run_forward(wsg_model* m, bool head, int n_keys) {
+  const int splits = splits_for(m, n_keys);
+  if (!m->use_graph) {
+    if (!enqueue_forward(m, head, splits)) return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape");
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(WSG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return WSG_OK;
+  }
+  const int key = splits * 2 + (head ? 1 : 0);
+  auto it = m->graphs.find(key);
+  if (it == m->graphs.end()) {
+    WSG_HIP_CHECK(hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
+    const bool ok = enqueue_forward(m, head, splits);
+    hipGraph_t g = nullptr;
+    const hipError_t ec = hipStreamEndCapture(m->stream, &g);
+    if (!ok) { if (g) (void)hipGraphDestroy(g); return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape"); }
+    if (ec != hipSuccess) return fail(WSG_ERR_HIP, "graph capture: %s", hipGetErrorString(ec));
+    hipGraphExec_t ex = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (ei != hipSuccess) return fail(WSG_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ei));
+    it = m->graphs.emplace(key, ex).first;
+  } else {
+    // keep ev_used consistent with the event nodes the graph records
+    m->ev_used = 0;
+    m->timed_bytes_per_launch_sum = 0;
+    if (m->timed_stage >= 0) {
+      int launches = 0;
+      if (m->timed_stage == WSG_STAGE_HEAD || m->timed_stage == WSG_STAGE_ARGMAX) launches = head ? 1 : 0;
+      else launches = m->d.L;
+      m->ev_used = 2 * launches;
+      m->timed_bytes_per_launch_sum = launches * stage_bytes(m, m->timed_stage);
+    }
+  }
+  WSG_HIP_CHECK(hipGraphLaunch(it->second, m->stream));
+  return WSG_OK;
+}
+
+wsg_status collect_timing(wsg_model* m) {
+  if (m->timed_stage < 0 || m->ev_used == 0) return WSG_OK;
+  for (int i = 0; i + 1 < m->ev_used; i += 2) {
+    float ms = 0.f;
+    WSG_HIP_CHECK(hipEventElapsedTime(&ms, m->ev[i], m->ev[i + 1]));
+    m->acc_ms += ms;
+    m->acc_launches += 1;
+  }
+  m->acc_bytes += m->timed_bytes_per_launch_sum;
+  m->ev_used = 0;
+  return WSG_OK;
+}
+
+wsg_status read_token(wsg_model* m, int32_t* out_token) {
+  WSG_HIP_CHECK(hipMemcpyAsync(m->pin, m->args.ctrl + kCtrlOutTok, sizeof(int32_t), hipMemcpyDeviceToHost, m->stream));
+  WSG_HIP_CHECK(hipStreamSynchronize(m->stream));
+  const wsg_status st = collect_timing(m);
+  if (st != WSG_OK) return st;
+  if (out_token) *out_token = m->pin[0];
+  return WSG_OK;
+}
+
+void fill_rope(const wsg_config& c, std::vector<float>& cs, std::vector<float>& sn) {
+  const int half = c.head_dim / 2;
+  cs.resize((size_t)c.max_context * half);
+  sn.resize(cs.size());
+  for (int i = 0; i < half; ++i) {
+    const double inv_freq = pow((double)c.rope_theta, -2.0 * i / (double)c.head_dim);
+    for (int p = 0; p < c.max_context; ++p) {
+      const double a = (double)p * inv_freq;
+      cs[(size_t)p * half + i] = (float)cos(a);
+      sn[(size_t)p * half + i] = (float)sin(a);
+    }
+  }
+}
+
+}  // namespace
+
+// ======================================================================= ABI
+extern "C" {
+
+const char* wsg_last_error(void) { return g_last_error; }
+const char* wsg_version(void) { return "wsg 0.1 gfx950"; }
+
+wsg_status wsg_packed_weight_bytes(const wsg_config* cfg, size_t* bytes) {
+  clear_error();
+  const wsg_status st = validate_config(cfg);
+  if (st != WSG_OK) return st;
+  if (!bytes) return fail(WSG_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = packed_layout(dims_of(*cfg)).total;
+  return WSG_OK;
+}
+
+wsg_status wsg_workspace_bytes(const wsg_config* cfg, size_t* bytes) {
+  clear_error();
+  const wsg_status st = validate_config(cfg);
+  if (st != WSG_OK) return st;
+  if (!bytes) return fail(WSG_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ws_layout(dims_of(*cfg)).total;
+  return WSG_OK;
+}
+
+wsg_status wsg_pack_weights(const wsg_config* cfg, const wsg_host_weights* w, void* host_out, size_t out_bytes) {
+  clear_error();
+  wsg_status st = validate_config(cfg);
+  if (st != WSG_OK) return st;
+  if (!w || !host_out) return fail(WSG_ERR_INVALID_ARG, "weights or output is NULL");
+  const Dims d = dims_of(*cfg);
+  const PackedLayout p = packed_layout(d);
+  if (out_bytes < p.total) return fail(WSG_ERR_INVALID_ARG, "output has %zu bytes, need %zu", out_bytes, p.total);
+  if (!w->embed || !w->final_norm || !w->in_norm || !w->wq || !w->wk || !w->wv || !w->q_norm || !w->k_norm ||
+      !w->wo || !w->post_norm || !w->wg || !w->wu || !w->wd)
+    return fail(WSG_ERR_INVALID_ARG, "a weight pointer is NULL");
+  for (int l = 0; l < d.L; ++l)
+    if (!w->in_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->q_norm[l] || !w->k_norm[l] || !w->wo[l] ||
+        !w->post_norm[l] || !w->wg[l] || !w->wu[l] || !w->wd[l])
+      return fail(WSG_ERR_INVALID_ARG, "layer %d has a NULL weight pointer", l);
+  uint8_t* out = static_cast<uint8_t*>(host_out);
+  memset(out, 0, p.total);
+  const size_t es = d.es;
+  auto put = [&](size_t off, const void* src, size_t elems) { memcpy(out + off, src, elems * es); };
+  put(p.embed, w->embed, (size_t)d.V * d.H);
+  put(p.final_norm, w->final_norm, d.H);
+  for (int l = 0; l < d.L; ++l) {
+    const LayerOff& lo = p.layers[l];
+    put(lo.in_norm, w->in_norm[l], d.H);
+    put(lo.post_norm, w->post_norm[l], d.H);
+    put(lo.q_norm, w->q_norm[l], d.D);
+    put(lo.k_norm, w->k_norm[l], d.D);
+    put(lo.wqkv, w->wq[l], (size_t)d.Q * d.H);
+    put(lo.wqkv + (size_t)d.Q * d.H * es, w->wk[l], (size_t)d.KV * d.H);
+    put(lo.wqkv + (size_t)(d.Q + d.KV) * d.H * es, w->wv[l], (size_t)d.KV * d.H);
+    put(lo.wo, w->wo[l], (size_t)d.H * d.Q);
+    put(lo.wgu, w->wg[l], (size_t)d.I * d.H);
+    put(lo.wgu + (size_t)d.I * d.H * es, w->wu[l], (size_t)d.I * d.H);
+    put(lo.wd, w->wd[l], (size_t)d.H * d.I);
+  }
+  return WSG_OK;
+}
+
+wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t packed_bytes, void* d_workspace,
+                            size_t ws_bytes, void* hip_stream, wsg_model** out) {
+  clear_error();
+  wsg_status st = validate_config(cfg);
+  if (st != WSG_OK) return st;
+  if (!d_packed || !d_workspace || !out) return fail(WSG_ERR_INVALID_ARG, "NULL pointer");
+  if (((uintptr_t)d_packed | (uintptr_t)d_workspace) & 255)
+    return fail(WSG_ERR_INVALID_ARG, "packed weights and workspace must be 256-byte aligned");
+  const Dims d = dims_of(*cfg);
+  PackedLayout pl = packed_layout(d);
+  WsLayout wl = ws_layout(d);
+  if (packed_bytes < pl.total) return fail(WSG_ERR_INVALID_ARG, "packed buffer has %zu bytes, need %zu", packed_bytes, pl.total);
+  if (ws_bytes < wl.total) return fail(WSG_ERR_INVALID_ARG, "workspace has %zu bytes, need %zu", ws_bytes, wl.total);
+
+  wsg_model* m = new wsg_model();
+  m->cfg = *cfg;
+  m->d = d;
+  m->packed = static_cast<const uint8_t*>(d_packed);
+  m->ws = static_cast<uint8_t*>(d_workspace);
+  m->pl = pl;
+  m->wl = wl;
+  m->prefill_rows = cfg->prefill_chunk;
+  auto fail_free = [&](wsg_status code) { wsg_model_destroy(m); return code; };
+
+  if (hip_stream) {
+    m->stream = static_cast<hipStream_t>(hip_stream);
+  } else {
+    if (hipStreamCreateWithFlags(&m->stream, hipStreamNonBlocking) != hipSuccess)
+      return fail_free(fail(WSG_ERR_HIP, "hipStreamCreate failed"));
+    m->own_stream = true;
+  }
+  if (hipHostMalloc((void**)&m->pin, (size_t)(d.cap + 2) * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
+    return fail_free(fail(WSG_ERR_HIP, "hipHostMalloc failed"));
+  m->ev.resize(2 * (d.L + 1));
+  for (auto& e : m->ev)
+    if (hipEventCreate(&e) != hipSuccess) { e = nullptr; return fail_free(fail(WSG_ERR_HIP, "hipEventCreate failed")); }
+
+  DecodeArgs& a = m->args;
+  a.dtype = cfg->dtype;
+  a.hidden = d.H; a.inter = d.I; a.n_q = d.nq; a.n_kv = d.nkv; a.head_dim = d.D; a.vocab = d.V; a.cap = d.cap;
+  a.eps = cfg->rms_eps;
+  a.embed = m->packed + pl.embed;
+  a.final_norm = m->packed + pl.final_norm;
+  a.rope_cos = reinterpret_cast<const float*>(m->ws + wl.rope_cos);
+  a.rope_sin = reinterpret_cast<const float*>(m->ws + wl.rope_sin);
+  a.x = m->ws + wl.x; a.qkv = m->ws + wl.qkv; a.o = m->ws + wl.o; a.act = m->ws + wl.act;
+  a.logits = m->ws + wl.logits;
+  a.attn_part = reinterpret_cast<float*>(m->ws + wl.attn_part);
+  a.attn_part_splits = wl.attn_splits_cap;
+  a.am_part = reinterpret_cast<unsigned long long*>(m->ws + wl.am_part);
+  a.am_part_cap = kAmPartCap;
+  a.ctrl = reinterpret_cast<int32_t*>(m->ws + wl.ctrl);
+  a.ids = reinterpret_cast<int32_t*>(m->ws + wl.ids);
+  const size_t kv_layer = (size_t)2 * d.nkv * d.cap * d.D * d.es;
+  for (int l = 0; l < d.L; ++l) {
+    const LayerOff& lo = pl.layers[l];
+    LayerPtrs lp;
+    lp.wqkv = m->packed + lo.wqkv; lp.wo = m->packed + lo.wo; lp.wgu = m->packed + lo.wgu; lp.wd = m->packed + lo.wd;
+    lp.in_norm = m->packed + lo.in_norm; lp.post_norm = m->packed + lo.post_norm;
+    lp.q_norm = m->packed + lo.q_norm; lp.k_norm = m->packed + lo.k_norm;
+    lp.k_cache = m->ws + wl.kv + l * kv_layer;
+    lp.v_cache = m->ws + wl.kv + l * kv_layer + kv_layer / 2;
+    m->layers.push_back(lp);
+  }
+  DecodeShape& sh = m->shape;
+  sh.rows_qkv = sh.rows_o = sh.rows_gu = sh.rows_down = sh.rows_head = 1;
+  sh.grid_qkv = sh.grid_o = sh.grid_gu = sh.grid_down = 0;
+  sh.grid_head = 4096;
+  sh.attn_splits = 1;
+  sh.attn_min_chunk = kMinAttnChunk;
+  if (head_blocks(a, sh) > kAmPartCap) return fail_free(fail(WSG_ERR_UNSUPPORTED, "vocabulary too large"));
+
+  std::vector<float> cs, sn;
+  fill_rope(*cfg, cs, sn);
+  if (hipMemcpyAsync(m->ws + wl.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, m->stream) != hipSuccess ||
+      hipMemcpyAsync(m->ws + wl.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, m->stream) != hipSuccess ||
+      hipMemsetAsync(m->ws + wl.ctrl, 0, (size_t)kCtrlWords * 4, m->stream) != hipSuccess ||
+      hipMemsetAsync(m->ws + wl.ids, 0, (size_t)(d.cap + 1) * 4, m->stream) != hipSuccess ||
+      hipStreamSynchronize(m->stream) != hipSuccess)
+    return fail_free(fail(WSG_ERR_HIP, "uploading the rotary table failed"));
+  // graphs need a capturable (non-null) stream
+  m->use_graph = (m->stream != nullptr);
+  *out = m;
+  return WSG_OK;
+}
+
+void wsg_model_destroy(wsg_model* m) {
+  if (!m) return;
+  if (m->stream) (void)hipStreamSynchronize(m->stream);
+  drop_graphs(m);
+  for (auto e : m->ev) if (e) (void)hipEventDestroy(e);
+  if (m->pin) (void)hipHostFree(m->pin);
+  if (m->own_stream && m->stream) (void)hipStreamDestroy(m->stream);
+  delete m;
+}
+
+wsg_status wsg_reset_cache(wsg_model* m) {
+  clear_error();
+  if (!m) return fail(WSG_ERR_INVALID_ARG, "model is NULL");
+  launch_set_pos(m->args.ctrl, 0, m->stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(WSG_ERR_HIP, "reset: %s", hipGetErrorString(e));
+  m->pos = 0;
+  m->has_output = false;
+  return WSG_OK;
+}
+
+int32_t wsg_position(const wsg_model* m) { return m ? m->pos : -1; }
+
+wsg_status wsg_prefill(wsg_model* m, const int32_t* host_ids, int32_t n, int32_t* out_token, const void** out_logits) {
+  clear_error();
+  if (!m || !host_ids) return fail(WSG_ERR_INVALID_ARG, "NULL pointer");
+  if (n < 1) return fail(WSG_ERR_INVALID_ARG, "n=%d must be >= 1", n);
+  if ((int64_t)m->pos + n > m->d.cap)
+    return fail(WSG_ERR_OUT_OF_RANGE, "position %d + %d rows exceeds max_context %d", m->pos, n, m->d.cap);
+  for (int i = 0; i < n; ++i)
+    if (host_ids[i] < 0 || host_ids[i] >= m->d.V)
+      return fail(WSG_ERR_OUT_OF_RANGE, "token id %d at index %d outside [0, %d)", host_ids[i], i, m->d.V);
+  memcpy(m->pin + 1, host_ids, (size_t)n * sizeof(int32_t));
+  WSG_HIP_CHECK(hipMemcpyAsync(m->args.ids + m->pos, m->pin + 1, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice,
+                               m->stream));
+  const int p0 = m->pos;
+  int done = 0;
+  if (m->prefill_rows > 0 && n > 1) {
+    // chunked path for all rows but the last; the last row runs the decode
+    // forward so that it alone reaches the head
+    PrefillCtx pc = prefill_ctx(m->args, m->shape, m->layers.data(), m->d.L, m->ws, m->wl.pf, m->prefill_rows);
+    const wsg_status st = run_prefill_chunks(pc, p0, n - 1, m->stream);
+    if (st != WSG_OK) return st;
+    done = n - 1;
+  }
+  for (int r = done; r < n; ++r) {
+    const bool last = (r == n - 1);
+    const wsg_status st = run_forward(m, last, p0 + r + 1);
+    if (st != WSG_OK) return st;
+  }
+  const wsg_status st = read_token(m, out_token);
+  if (st != WSG_OK) return st;
+  m->pos = p0 + n;
+  m->has_output = true;
+  if (out_logits) *out_logits = m->args.logits;
+  return WSG_OK;
+}
+
+wsg_status wsg_step(wsg_model* m, int32_t in_token, int32_t* out_token, const void** out_logits) {
+  clear_error();
+  if (!m) return fail(WSG_ERR_INVALID_ARG, "model is NULL");
+  if (in_token >= m->d.V) return fail(WSG_ERR_OUT_OF_RANGE, "token id %d >= vocab %d", in_token, m->d.V);
+  if (in_token < 0 && !m->has_output) return fail(WSG_ERR_STATE, "no previous output token; pass in_token or prefill first");
+  if (m->pos >= m->d.cap) return fail(WSG_ERR_OUT_OF_RANGE, "cache full (max_context %d)", m->d.cap);
+  if (in_token >= 0) {
+    m->pin[1] = in_token;
+    WSG_HIP_CHECK(hipMemcpyAsync(m->args.ids + m->pos, m->pin + 1, sizeof(int32_t), hipMemcpyHostToDevice, m->stream));
+  }
+  wsg_status st = run_forward(m, true, m->pos + 1);
+  if (st != WSG_OK) return st;
+  st = read_token(m, out_token);
+  if (st != WSG_OK) return st;
+  m->pos += 1;
+  m->has_output = true;
+  if (out_logits) *out_logits = m->args.logits;
+  return WSG_OK;
+}
+
+wsg_status wsg_kv_view(const wsg_model* m, int32_t layer, const void** d_k, const void** d_v, int32_t* valid_len) {
+  clear_error();
+  if (!m || !d_k || !d_v || !valid_len) return fail(WSG_ERR_INVALID_ARG, "NULL pointer");
+  if (layer < 0 || layer >= m->d.L) return fail(WSG_ERR_OUT_OF_RANGE, "layer %d outside [0, %d)", layer, m->d.L);
+  *d_k = m->layers[layer].k_cache;
+  *d_v = m->layers[layer].v_cache;
+  *valid_len = m->pos;
+  return WSG_OK;
+}
+
+wsg_status wsg_set_prefill_chunk(wsg_model* m, int32_t rows) {
+  clear_error();
+  if (!m) return fail(WSG_ERR_INVALID_ARG, "model is NULL");
+  if (rows < 1 || rows > m->cfg.prefill_chunk)
+    return fail(WSG_ERR_INVALID_ARG, "chunk rows %d outside [1, %d]", rows, m->cfg.prefill_chunk);
+  m->prefill_rows = rows;
+  return WSG_OK;
+}
+
+wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value) {
+  clear_error();
+  if (!m) return fail(WSG_ERR_INVALID_ARG, "model is NULL");
+  switch (option) {
+    case WSG_OPT_USE_GRAPH:
+      if (value != 0 && value != 1) return fail(WSG_ERR_INVALID_ARG, "use_graph must be 0 or 1");
+      if (value == 1 && m->stream == nullptr) return fail(WSG_ERR_STATE, "graphs need a non-null stream");
+      m->use_graph = value == 1;
+      return WSG_OK;
+    case WSG_OPT_TIMED_STAGE:
+      if (value < -1 || value > WSG_STAGE_ARGMAX) return fail(WSG_ERR_INVALID_ARG, "stage %d", value);
+      m->timed_stage = value;
+      m->acc_ms = 0; m->acc_launches = 0; m->acc_bytes = 0;
+      drop_graphs(m);   // the captured plan changes with the event nodes
+      return WSG_OK;
+    default:
+      return fail(WSG_ERR_INVALID_ARG, "unknown option %d", option);
+  }
+}
+
+wsg_status wsg_stage_time(wsg_model* m, double* total_ms, int64_t* launches, int64_t* bytes) {
+  clear_error();
+  if (!m || !total_ms || !launches || !bytes) return fail(WSG_ERR_INVALID_ARG, "NULL pointer");
+  *total_ms = m->acc_ms; *launches = m->acc_launches; *bytes = m->acc_bytes;
+  m->acc_ms = 0; m->acc_launches = 0; m->acc_bytes = 0;
+  return WSG_OK;
+}
+
+}  // extern "C"
