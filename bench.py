@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Decode benchmark on one MI355X: 28-layer FP32 Qwen3-0.6B-shaped decoder.
+
+One step = the four short greedy generations of the pages' GPU-wide study
+(prompt/output 8/8, 8/16, 32/8, 32/16; Megakernels, "GPU-wide end-to-end
+generation"), each timed from before the cache reset to the last token id
+on the host.  ``value`` is the post-first-token decode rate: generated
+tokens after the first, divided by the time after the first token
+(Benchmark methodology, "What the measurements mean" and "Long-document
+chunked prefill").  Timings are published only after the GPU's greedy
+tokens, logits and KV matched the CPU oracle on the same inputs; every timed
+generation must reproduce the validated token ids.
+
+Also reported: the dominant decode kernel against the HBM roofline (HIP
+events around each of its launches inside the timed region), the oracle
+timed on the host cores, and (``--sweep``) the cold-cache GEMV sweep.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+COMBOS = [(8, 8), (8, 16), (32, 8), (32, 16)]
+STAGES = {"qkv": 0, "attn": 1, "o": 2, "gateup": 3, "down": 4, "head": 5}
+STAGE_KERNEL = {"qkv": "k_qkv", "attn": "k_attn", "o": "k_gemv_residual", "gateup": "k_gateup",
+                "down": "k_gemv_residual", "head": "k_head"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def generate(model, prompt, n_out):
+    """One timed greedy generation: (tokens, ttft_s, decode_s, total_s)."""
+    t0 = time.perf_counter()
+    model.reset()
+    toks = [model.prefill(prompt)]
+    t1 = time.perf_counter()
+    for _ in range(n_out - 1):
+        toks.append(model.step())
+    t2 = time.perf_counter()
+    return toks, t1 - t0, t2 - t1, t2 - t0
+
+
+def validate(model, orc, prompt, n_out):
+    """Lockstep check of logits, tokens and KV; returns (tokens, max errors, oracle decode seconds)."""
+    import oracle
+    model.reset()
+    orc.reset()
+    tok = model.prefill(prompt)
+    ref = orc.forward_rows(prompt)
+    toks, rtoks = [tok], [oracle.argmax_lowest(ref)]
+    max_l = max_kv = 0.0
+    t_dec = 0.0
+
+    def cmp(got, ref_, what):
+        g = got.float().cpu().numpy().astype(np.float64)
+        r = np.asarray(ref_, dtype=np.float64)
+        err = np.abs(g - r)
+        if np.any(err > 1e-3 + 1e-3 * np.abs(r)):
+            raise RuntimeError(f"validation failed: {what} off by {err.max():.3e}")
+        return float(err.max())
+
+    max_l = max(max_l, cmp(model.logits(), ref, "logits at the first output"))
+    for s in range(1, n_out):
+        if toks[-1] != rtoks[-1]:
+            raise RuntimeError(f"validation failed: token {toks[-1]} != oracle {rtoks[-1]} "
+                               f"(oracle margin {orc.logits_margin(ref):.3e})")
+        p = orc.pos
+        toks.append(model.step())
+        t = time.perf_counter()
+        ref = orc.forward_rows([rtoks[-1]])
+        t_dec += time.perf_counter() - t
+        rtoks.append(oracle.argmax_lowest(ref))
+        max_l = max(max_l, cmp(model.logits(), ref, f"logits at step {s}"))
+        for l in range(orc.shape.n_layers):
+            k, v, _ = model.kv(l)
+            max_kv = max(max_kv, cmp(k[:, p:p + 1], orc.k_cache[l][:, p:p + 1], f"K layer {l} step {s}"))
+            max_kv = max(max_kv, cmp(v[:, p:p + 1], orc.v_cache[l][:, p:p + 1], f"V layer {l} step {s}"))
+    if toks != rtoks:
+        raise RuntimeError(f"validation failed: tokens {toks} != oracle {rtoks}")
+    n = orc.pos
+    for l in range(orc.shape.n_layers):
+        k, v, _ = model.kv(l)
+        max_kv = max(max_kv, cmp(k[:, :n], orc.k_cache[l][:, :n], f"K prefix layer {l}"))
+        max_kv = max(max_kv, cmp(v[:, :n], orc.v_cache[l][:, :n], f"V prefix layer {l}"))
+    return toks, max_l, max_kv, t_dec
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--timed-stage", default="head", choices=sorted(STAGES),
+                    help="stage kind bracketed by HIP events (graph mode: head only)")
+    ap.add_argument("--no-graph", action="store_true", help="launch every kernel directly")
+    ap.add_argument("--no-oracle", action="store_true",
+                    help="skip validation and the CPU baseline (profiling runs only; no value is published)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import weight_streaming_gemv_amd as wsg
+    from synth import PROMPT_SEEDS, QWEN3_0_6B, model_weights, prompt_ids
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    shape = QWEN3_0_6B
+    cap = 48
+    t = time.perf_counter()
+    w = model_weights(shape, seed=0)
+    log(f"weights generated in {time.perf_counter() - t:.1f} s")
+    prompt32 = prompt_ids(PROMPT_SEEDS["short"], 32, shape.vocab)
+    prompts = {8: prompt32[:8], 32: prompt32}
+    model = wsg.Model(shape, w, max_context=cap)
+    if args.no_graph:
+        model.set_option(wsg._abi.WSG_OPT_USE_GRAPH, 0)
+
+    # ---- correctness gate and CPU baseline (oracle on the host cores)
+    expected = {}
+    cpu = None
+    errs = {}
+    if not args.no_oracle:
+        import oracle
+        t = time.perf_counter()
+        orc = oracle.OracleModel(shape, w, cap)
+        log(f"oracle set up in {time.perf_counter() - t:.1f} s")
+        for n_p in (8, 32):
+            toks, ml, mkv, t_dec = validate(model, orc, prompts[n_p], 16)
+            for n_o in (8, 16):
+                expected[(n_p, n_o)] = toks[:n_o]
+            errs[n_p] = (ml, mkv)
+            if n_p == 8:
+                cpu = {"value": round(15 / t_dec, 3), "unit": "tokens/s", "cores": cpu_threads(), "kind": "oracle",
+                       "sample": "15 post-first-token decode forwards of the 8/16 generation (28 layers, "
+                                 "float64 reductions), same weights and prompt"}
+        log(f"validation passed: max |dlogit| {max(e[0] for e in errs.values()):.2e}, "
+            f"max |dkv| {max(e[1] for e in errs.values()):.2e}")
+
+    del w
+    stage = STAGES[args.timed_stage]
+    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, stage)
+
+    def run_step(rec):
+        for (n_p, n_o) in COMBOS:
+            toks, ttft, dec, tot = generate(model, prompts[n_p], n_o)
+            if expected and toks != expected[(n_p, n_o)]:
+                raise RuntimeError(f"timed generation {n_p}/{n_o} returned {toks}, validated {expected[(n_p, n_o)]}")
+            if rec is not None:
+                rec.append((n_p, n_o, ttft, dec, tot))
+
+    for _ in range(args.warmup):
+        run_step(None)
+    model.stage_time()   # reset the event accumulators
+    rec = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(rec)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st_ms, st_n, st_bytes = model.stage_time()
+
+    dec_tokens = sum(n_o - 1 for (_, n_o, _, _, _) in rec)
+    dec_time = sum(r[3] for r in rec)
+    value = dec_tokens / dec_time
+    per_combo = {}
+    for (n_p, n_o) in COMBOS:
+        rows = [r for r in rec if r[0] == n_p and r[1] == n_o]
+        per_combo[f"{n_p}/{n_o}"] = {
+            "ttft_ms": round(statistics.median(r[2] for r in rows) * 1e3, 3),
+            "decode_tok_s": round(statistics.median((n_o - 1) / r[3] for r in rows), 1),
+            "total_ms": round(statistics.median(r[4] for r in rows) * 1e3, 3)}
+    weight_bytes = shape.weight_bytes_per_token(4)
+    avg_launch_ms = st_ms / max(st_n, 1)
+    achieved = (st_bytes / max(st_n, 1)) / (avg_launch_ms * 1e-3) / 1e9 if st_n else None
+    out = {
+        "metric": "decode tokens/s + cold-cache effective weight GB/s (% of HBM peak), 1 MI355X",
+        "value": None if args.no_oracle else round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (random-init N(0,0.02) weights, uniform-random token ids)",
+        "config": {"workload": "Qwen3-0.6B-shaped decoder, 28 layers, FP32 weights/activations/KV, batch 1, "
+                               "greedy; prompt/output 8/8, 8/16, 32/8, 32/16 per step",
+                   "global_batch": 1, "seq_len": 48, "parallelism": "single-gpu"},
+        "decode_weight_gbps": round(weight_bytes * value / 1e9, 1),
+        "decode_weight_frac_of_hbm_peak": round(weight_bytes * value / 1e9 / HBM_PEAK_GBPS, 4),
+        "per_combo_median": per_combo,
+        "roofline": {"bound": "hbm", "kernel": STAGE_KERNEL[args.timed_stage],
+                     "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None, "traffic": None,
+                     "bytes_per_launch": st_bytes // max(st_n, 1), "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+                     "launches_timed": st_n},
+        "cpu_baseline": cpu,
+        "validation": ({"status": "passed", "max_abs_logit_err": max(e[0] for e in errs.values()),
+                        "max_abs_kv_err": max(e[1] for e in errs.values()), "rtol": 1e-3, "atol": 1e-3}
+                       if errs else {"status": "skipped"}),
+        "graphs": not args.no_graph,
+    }
+    print(json.dumps(out), flush=True)
+    model.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -156,11 +156,25 @@ wsg_status wsg_set_prefill_chunk(wsg_model* m, int32_t rows);
 
 /* Options: WSG_OPT_USE_GRAPH (1 = replay captured HIP graphs, the default;
  * 0 = launch every kernel directly), WSG_OPT_TIMED_STAGE (record HIP events
- * around every launch of one stage kind, see wsg_stage_time; -1 = off). */
+ * on the model stream around every launch of one stage kind, see
+ * wsg_stage_time; -1 = off).  Event-record nodes inside HIP graphs carry no
+ * usable timestamps on this platform, so with graphs on only
+ * WSG_STAGE_HEAD can be timed (its launch is a graph of its own, bracketed
+ * by stream events); other stages need WSG_OPT_USE_GRAPH = 0, where each
+ * bracketing event adds its own overhead to short kernels.
+ * Errors: WSG_ERR_UNSUPPORTED for a per-layer stage while graphs are on. */
 enum { WSG_OPT_USE_GRAPH = 1, WSG_OPT_TIMED_STAGE = 2 };
-/* Stage kinds for WSG_OPT_TIMED_STAGE. */
+/* Launch shape of the decode GEMV stages (tuning): rows per wave (1, 2 or
+ * 4) and blocks of 256 threads (0 = one row group per wave; fewer blocks
+ * loop over row groups; the head is capped at 4096 blocks).  Defaults:
+ * 1 row per wave, one-shot grids, 4096 head blocks. */
+enum { WSG_OPT_ROWS_QKV = 10, WSG_OPT_ROWS_O = 11, WSG_OPT_ROWS_GATEUP = 12, WSG_OPT_ROWS_DOWN = 13,
+       WSG_OPT_ROWS_HEAD = 14, WSG_OPT_GRID_QKV = 20, WSG_OPT_GRID_O = 21, WSG_OPT_GRID_GATEUP = 22,
+       WSG_OPT_GRID_DOWN = 23, WSG_OPT_GRID_HEAD = 24 };
+/* Stage kinds for WSG_OPT_TIMED_STAGE.  HEAD = final RMSNorm + vocabulary
+ * GEMV + greedy argmax (one launch). */
 enum { WSG_STAGE_QKV = 0, WSG_STAGE_ATTN = 1, WSG_STAGE_O = 2, WSG_STAGE_GATEUP = 3,
-       WSG_STAGE_DOWN = 4, WSG_STAGE_HEAD = 5, WSG_STAGE_ARGMAX = 6 };
+       WSG_STAGE_DOWN = 4, WSG_STAGE_HEAD = 5 };
 wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value);
 
 /* Accumulated device time (HIP events, on the model stream) of the timed

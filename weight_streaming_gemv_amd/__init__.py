@@ -15,12 +15,12 @@ import numpy as np
 
 from . import _abi
 from ._abi import (WSG_F16, WSG_F32, WSG_GEMV_NONTEMPORAL, WSG_OPT_TIMED_STAGE, WSG_OPT_USE_GRAPH,
-                   WSG_STAGE_ARGMAX, WSG_STAGE_ATTN, WSG_STAGE_DOWN, WSG_STAGE_GATEUP, WSG_STAGE_HEAD,
-                   WSG_STAGE_O, WSG_STAGE_QKV, WsgError, check, wsg_config, wsg_host_weights)
+                   WSG_STAGE_ATTN, WSG_STAGE_DOWN, WSG_STAGE_GATEUP, WSG_STAGE_HEAD, WSG_STAGE_O,
+                   WSG_STAGE_QKV, WsgError, check, wsg_config, wsg_host_weights)
 
 __all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "WsgError", "WSG_F32", "WSG_F16",
            "WSG_STAGE_QKV", "WSG_STAGE_ATTN", "WSG_STAGE_O", "WSG_STAGE_GATEUP", "WSG_STAGE_DOWN",
-           "WSG_STAGE_HEAD", "WSG_STAGE_ARGMAX", "WSG_GEMV_NONTEMPORAL", "lib"]
+           "WSG_STAGE_HEAD", "WSG_OPT_USE_GRAPH", "WSG_OPT_TIMED_STAGE", "WSG_GEMV_NONTEMPORAL", "lib"]
 
 lib = _abi.lib
 lib()  # fail loudly at import when libwsg.so is missing

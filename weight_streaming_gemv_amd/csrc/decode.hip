@@ -75,6 +75,35 @@ struct Act {
   }
 };
 
+// R weight rows held in registers (16-byte vectors in the lane layout), so
+// a wave can put its first rows in flight before its prologue finishes.
+template <typename TS, int K, int R>
+struct WRows {
+  static constexpr int VEC = Vec16<TS>::N;
+  static constexpr int NV = K / (kWave * VEC);
+  Vec16<TS> v[R][NV];
+  __device__ __forceinline__ void load(const TS* __restrict__ W, int row0, int M) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const TS* wr = W + (size_t)min(row0 + r, M - 1) * K + lane * VEC;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) v[r][c].template load<false>(wr + c * kWave * VEC);
+    }
+  }
+  __device__ __forceinline__ void dot(const Act<TS, K>& x, float (&acc)[R]) const {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < NV; ++c)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) a = fmaf(v[r][c].v[i], x.a[c * VEC + i], a);
+      acc[r] = a;
+    }
+  }
+};
+
 // acc[r] += W[row0 + r] . act for r < R (rows clamped to M-1 for loads).
 template <typename TS, int K, int R>
 __device__ __forceinline__ void rows_dot(const TS* __restrict__ W, int row0, int M, const Act<TS, K>& x,
@@ -105,6 +134,10 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TS* __restrict__ W, const 
                                                 const int32_t* __restrict__ ids, const int32_t* __restrict__ ctrl,
                                                 int first_layer, int vocab, float eps, TS* __restrict__ out,
                                                 int M) {
+  const int ngroups = ceil_div(M, R);
+  int g = wave_row_groups_begin();
+  WRows<TS, H, R> w;
+  if (g < ngroups) w.load(W, g * R, M);   // first rows in flight before the prologue
   Act<TS, H> x;
   if (first_layer) {
     int tok = ids[ctrl[kCtrlPos]];
@@ -116,12 +149,11 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TS* __restrict__ W, const 
   }
   x.rms_norm(in_norm, eps);
   const int lane = lane_id();
-  const int ngroups = ceil_div(M, R);
-  for (int g = wave_row_groups_begin(); g < ngroups; g += wave_row_groups_stride()) {
+  for (; g < ngroups; g += wave_row_groups_stride()) {
     float acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
-    rows_dot<TS, H, R>(W, g * R, M, x, acc);
+    w.dot(x, acc);
+    const int next = g + wave_row_groups_stride();
+    if (next < ngroups) w.load(W, next * R, M);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float s = wave_sum(acc[r]);
@@ -131,26 +163,30 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TS* __restrict__ W, const 
 }
 
 // ------------------------------------------------------------ o / down
-// x_res[m] += W[m] . in  for m < M (M = hidden).
+// x_out[m] = x_in[m] + W[m] . in  for m < M (M = hidden); the residual
+// ping-pongs between two buffers, so no kernel rewrites what it reads.
 template <typename TS, int K, int R>
 __global__ __launch_bounds__(kBlock) void k_gemv_residual(const TS* __restrict__ W, const TS* __restrict__ in,
-                                                          TS* __restrict__ x_res, int M, int32_t* __restrict__ ctrl,
-                                                          int advance_pos) {
+                                                          const TS* __restrict__ x_in, TS* __restrict__ x_out, int M,
+                                                          int32_t* __restrict__ ctrl, int advance_pos) {
   if (advance_pos && blockIdx.x == 0 && threadIdx.x == 0) ctrl[kCtrlPos] = ctrl[kCtrlPos] + 1;
+  const int ngroups = ceil_div(M, R);
+  int g = wave_row_groups_begin();
+  WRows<TS, K, R> w;
+  if (g < ngroups) w.load(W, g * R, M);
   Act<TS, K> x;
   x.load(in);
   const int lane = lane_id();
-  const int ngroups = ceil_div(M, R);
-  for (int g = wave_row_groups_begin(); g < ngroups; g += wave_row_groups_stride()) {
+  for (; g < ngroups; g += wave_row_groups_stride()) {
     float acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
-    rows_dot<TS, K, R>(W, g * R, M, x, acc);
+    w.dot(x, acc);
+    const int next = g + wave_row_groups_stride();
+    if (next < ngroups) w.load(W, next * R, M);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float s = wave_sum(acc[r]);
       const int m = g * R + r;
-      if (lane == 0 && m < M) x_res[m] = Store<TS>::from_f(Store<TS>::to_f(x_res[m]) + s);
+      if (lane == 0 && m < M) x_out[m] = Store<TS>::from_f(Store<TS>::to_f(x_in[m]) + s);
     }
   }
 }
@@ -162,17 +198,21 @@ template <typename TS, int H, int R>
 __global__ __launch_bounds__(kBlock) void k_gateup(const TS* __restrict__ Wgu, const TS* __restrict__ post_norm,
                                                    const TS* __restrict__ x_res, float eps, TS* __restrict__ act,
                                                    int I) {
+  const int ngroups = ceil_div(I, R);
+  const TS* Wu = Wgu + (size_t)I * H;
+  int g = wave_row_groups_begin();
+  WRows<TS, H, R> wg, wu;
+  if (g < ngroups) { wg.load(Wgu, g * R, I); wu.load(Wu, g * R, I); }
   Act<TS, H> x;
   x.load(x_res);
   x.rms_norm(post_norm, eps);
   const int lane = lane_id();
-  const int ngroups = ceil_div(I, R);
-  for (int g = wave_row_groups_begin(); g < ngroups; g += wave_row_groups_stride()) {
+  for (; g < ngroups; g += wave_row_groups_stride()) {
     float ga[R], ua[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) ga[r] = ua[r] = 0.f;
-    rows_dot<TS, H, R>(Wgu, g * R, I, x, ga);
-    rows_dot<TS, H, R>(Wgu + (size_t)I * H, g * R, I, x, ua);
+    wg.dot(x, ga);
+    wu.dot(x, ua);
+    const int next = g + wave_row_groups_stride();
+    if (next < ngroups) { wg.load(Wgu, next * R, I); wu.load(Wu, next * R, I); }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float gs = wave_sum(ga[r]);
@@ -202,22 +242,30 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
   return k;
 }
 
+// The head writes one argmax key per block; a one-block kernel then reduces
+// them (the pages' two argmax kernels, Megakernels, "GPU-wide end-to-end
+// generation").  A single fused launch would need a device-scope release
+// fence per block, and on this multi-XCD part each such fence writes back
+// the issuing XCD's L2, which costs far more than the extra launch.
 template <typename TS, int H, int R>
 __global__ __launch_bounds__(kBlock) void k_head(const TS* __restrict__ E, const TS* __restrict__ final_norm,
                                                  const TS* __restrict__ x_res, float eps, TS* __restrict__ logits,
                                                  int V, unsigned long long* __restrict__ am_part) {
   __shared__ unsigned long long best_wave[kWavesPerBlock];
+  const int lane = lane_id();
+  const int ngroups = ceil_div(V, R);
+  int g = wave_row_groups_begin();
+  WRows<TS, H, R> w;
+  if (g < ngroups) w.load(E, g * R, V);   // first rows in flight before the norm
   Act<TS, H> x;
   x.load(x_res);
   x.rms_norm(final_norm, eps);
-  const int lane = lane_id();
   unsigned long long best = 0;   // below every real key
-  const int ngroups = ceil_div(V, R);
-  for (int g = wave_row_groups_begin(); g < ngroups; g += wave_row_groups_stride()) {
+  for (; g < ngroups; g += wave_row_groups_stride()) {
     float acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
-    rows_dot<TS, H, R>(E, g * R, V, x, acc);
+    w.dot(x, acc);
+    const int next = g + wave_row_groups_stride();
+    if (next < ngroups) w.load(E, next * R, V);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float s = wave_sum(acc[r]);
@@ -235,7 +283,7 @@ __global__ __launch_bounds__(kBlock) void k_head(const TS* __restrict__ E, const
   if (threadIdx.x == 0) {
     unsigned long long b = best_wave[0];
 #pragma unroll
-    for (int w = 1; w < kWavesPerBlock; ++w) b = best_wave[w] > b ? best_wave[w] : b;
+    for (int w2 = 1; w2 < kWavesPerBlock; ++w2) b = best_wave[w2] > b ? best_wave[w2] : b;
     am_part[blockIdx.x] = b;
   }
 }
@@ -250,7 +298,6 @@ __global__ __launch_bounds__(1024) void k_argmax(const unsigned long long* __res
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) b = red[w] > b ? red[w] : b;
-    b = red[0] > b ? red[0] : b;
     int tok = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
     if (b == 0) tok = 0;   // no block key at all (cannot happen with vocab >= 1)
     const int pos = ctrl[kCtrlPos];
@@ -296,17 +343,15 @@ __device__ __forceinline__ void store_head8(TS* p, int sl, const float (&v)[8]) 
   }
 }
 
-// Per-head RMSNorm (over the 16 lanes of a row) then rotation at position p.
-template <typename TS>
-__device__ __forceinline__ void norm_rope8(float (&v)[8], const TS* gain, const float (&c)[4], const float (&s)[4],
-                                           int sl, float eps) {
+// Per-head RMSNorm (over the 16 lanes of a row) with gain g, then rotation
+// at position p (c, s: this lane's cos/sin of its four pairs).
+__device__ __forceinline__ void norm_rope8(float (&v)[8], const float (&g)[8], const float (&c)[4],
+                                           const float (&s)[4], float eps) {
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
   ss = row16_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)kD + eps);
-  float g[8];
-  load_head8<TS>(gain, sl, g);
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = v[i] * inv * g[i];
 #pragma unroll
@@ -370,6 +415,29 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
 
   const int j = blockIdx.y;            // KV head
   const int split = blockIdx.x;
+  const int lane = lane_id(), wave = wave_id();
+  const int row = lane >> 4, sl = lane & 15;
+  const int sid = wave * 4 + row;       // this row's slot among the block's 16 keys in flight
+  const int Q = n_q * kD, KV = n_kv * kD;
+  const size_t head_off = (size_t)j * cap * kD;
+
+  // Loads that do not depend on the position go first: raw queries, the
+  // current token's key and value, the norm gains, and (split 0 always
+  // starts at key 0) this row's first cached key.
+  float q[G][8], kc[8], vc[8], gq[8], gk[8], kk[8], vv[8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) load_head8<TS>(qkv + (size_t)(j * G + g) * kD, sl, q[g]);
+  load_head8<TS>(qkv + Q + (size_t)j * kD, sl, kc);
+  load_head8<TS>(qkv + Q + KV + (size_t)j * kD, sl, vc);
+  load_head8<TS>(q_norm, sl, gq);
+  load_head8<TS>(k_norm, sl, gk);
+  const bool spec = (split == 0);
+  if (spec) {
+    const int key0 = min(sid, cap - 1);
+    load_head8<TS>(k_cache + head_off + (size_t)key0 * kD, sl, kk);
+    load_head8<TS>(v_cache + head_off + (size_t)key0 * kD, sl, vv);
+  }
+
   const int pos = ctrl[kCtrlPos];
   const int n_keys = pos + 1;
   int chunk = max(min_chunk, ceil_div(n_keys, (int)gridDim.x));
@@ -381,10 +449,6 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
   const bool has_cur = (k_end == n_keys);
   const int k_stop = has_cur ? k_end - 1 : k_end;   // cached keys [k_begin, k_stop)
 
-  const int lane = lane_id(), wave = wave_id();
-  const int row = lane >> 4, sl = lane & 15;
-  const int Q = n_q * kD, KV = n_kv * kD;
-
   float c[4], s[4];
   {
     const float4 cv = *reinterpret_cast<const float4*>(rope_cos + (size_t)pos * (kD / 2) + 4 * sl);
@@ -392,14 +456,17 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
     c[0] = cv.x; c[1] = cv.y; c[2] = cv.z; c[3] = cv.w;
     s[0] = sv.x; s[1] = sv.y; s[2] = sv.z; s[3] = sv.w;
   }
-  // queries of this group: normalised, rotated, rounded as stored, then
-  // pre-scaled by log2(e)/sqrt(D) so scores are in the log2 domain
-  float q[G][8];
+  int key = k_begin + sid;
+  if (!spec && key < k_stop) {
+    load_head8<TS>(k_cache + head_off + (size_t)key * kD, sl, kk);
+    load_head8<TS>(v_cache + head_off + (size_t)key * kD, sl, vv);
+  }
+  // queries: normalised, rotated, rounded as stored, then pre-scaled by
+  // log2(e)/sqrt(D) so that scores are in the log2 domain
   const float qscale = kLog2e / sqrtf((float)kD);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    load_head8<TS>(qkv + (size_t)(j * G + g) * kD, sl, q[g]);
-    norm_rope8<TS>(q[g], q_norm, c, s, sl, eps);
+    norm_rope8(q[g], gq, c, s, eps);
     round_to_store<TS>(q[g]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) q[g][i] *= qscale;
@@ -407,30 +474,33 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
 
   SoftState<G> st;
   st.init();
-  const size_t head_off = (size_t)j * cap * kD;
-  for (int key = k_begin + wave * 4 + row; key < k_stop; key += 16) {
-    float kk[8], vv[8];
-    load_head8<TS>(k_cache + head_off + (size_t)key * kD, sl, kk);
-    load_head8<TS>(v_cache + head_off + (size_t)key * kD, sl, vv);
+  // each row walks keys sid, sid+16, ...; the next key's loads are issued
+  // before the current key is folded in
+  while (key < k_stop) {
+    const int nkey = key + 16;
+    float nk[8], nv[8];
+    if (nkey < k_stop) {
+      load_head8<TS>(k_cache + head_off + (size_t)nkey * kD, sl, nk);
+      load_head8<TS>(v_cache + head_off + (size_t)nkey * kD, sl, nv);
+    }
     st.add(q, kk, vv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { kk[i] = nk[i]; vv[i] = nv[i]; }
+    key = nkey;
   }
   if (has_cur) {
     // the current token's key and value: normalise/rotate, write slot p,
     // and fold them in from registers (row 0 of wave 0)
-    float kk[8], vv[8];
-    load_head8<TS>(qkv + Q + (size_t)j * kD, sl, kk);
-    norm_rope8<TS>(kk, k_norm, c, s, sl, eps);
-    round_to_store<TS>(kk);
-    load_head8<TS>(qkv + Q + KV + (size_t)j * kD, sl, vv);
+    norm_rope8(kc, gk, c, s, eps);
+    round_to_store<TS>(kc);
     if (wave == 0 && row == 0) {
-      store_head8<TS>(k_cache + head_off + (size_t)pos * kD, sl, kk);
-      store_head8<TS>(v_cache + head_off + (size_t)pos * kD, sl, vv);
-      st.add(q, kk, vv);
+      store_head8<TS>(k_cache + head_off + (size_t)pos * kD, sl, kc);
+      store_head8<TS>(v_cache + head_off + (size_t)pos * kD, sl, vc);
+      st.add(q, kc, vc);
     }
   }
 
   // merge the 16 row states of this block
-  const int sid = wave * 4 + row;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (sl == 0) { sm_m[sid][g] = st.m[g]; sm_l[sid][g] = st.l[g]; }
@@ -496,6 +566,11 @@ int blocks_for(int M, int R, int grid) {
   return (grid > 0 && grid < one_shot) ? grid : one_shot;
 }
 
+int head_grid(int V, int R, int grid) {
+  const int b = blocks_for(V, R, grid);
+  return b < kHeadMaxBlocks ? b : kHeadMaxBlocks;
+}
+
 // K values compiled in; a K must also be a multiple of 64 16-byte vectors
 // of the storage type (256 floats, 512 halves).
 template <int V> using IC = std::integral_constant<int, V>;
@@ -541,13 +616,14 @@ bool qkv_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool 
 }
 
 template <typename TS>
-bool residual_t(const DecodeArgs& a, int K, int R, int grid_req, const void* W, const void* in, bool adv,
-                hipStream_t s) {
+bool residual_t(const DecodeArgs& a, int K, int R, int grid_req, const void* W, const void* in, const void* x_in,
+                void* x_out, bool adv, hipStream_t s) {
   const int grid = blocks_for(a.hidden, R, grid_req);
   return with_k<TS>(K, [&](auto kc) {
     return with_r(R, [&](auto rc) {
       hipLaunchKernelGGL((k_gemv_residual<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock),
-                         0, s, (const TS*)W, (const TS*)in, (TS*)a.x, a.hidden, a.ctrl, adv ? 1 : 0);
+                         0, s, (const TS*)W, (const TS*)in, (const TS*)x_in, (TS*)x_out, a.hidden, a.ctrl,
+                         adv ? 1 : 0);
       return true;
     });
   });
@@ -559,7 +635,7 @@ bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hi
   return with_k<TS>(a.hidden, [&](auto kc) {
     return with_r(sh.rows_gu, [&](auto rc) {
       hipLaunchKernelGGL((k_gateup<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock), 0, s,
-                         (const TS*)L.wgu, (const TS*)L.post_norm, (const TS*)a.x, a.eps, (TS*)a.act, a.inter);
+                         (const TS*)L.wgu, (const TS*)L.post_norm, (const TS*)a.x2, a.eps, (TS*)a.act, a.inter);
       return true;
     });
   });
@@ -567,7 +643,7 @@ bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hi
 
 template <typename TS>
 bool head_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
-  const int grid = blocks_for(a.vocab, sh.rows_head, sh.grid_head);
+  const int grid = head_grid(a.vocab, sh.rows_head, sh.grid_head);
   return with_k<TS>(a.hidden, [&](auto kc) {
     return with_r(sh.rows_head, [&](auto rc) {
       hipLaunchKernelGGL((k_head<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock), 0, s,
@@ -598,7 +674,7 @@ bool attn_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipS
 
 }  // namespace
 
-int head_blocks(const DecodeArgs& a, const DecodeShape& sh) { return blocks_for(a.vocab, sh.rows_head, sh.grid_head); }
+int head_blocks(const DecodeArgs& a, const DecodeShape& sh) { return head_grid(a.vocab, sh.rows_head, sh.grid_head); }
 
 bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, hipStream_t s) {
   return a.dtype == 0 ? qkv_t<float>(a, sh, L, first, s) : qkv_t<__half>(a, sh, L, first, s);
@@ -608,15 +684,15 @@ bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L,
 }
 bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   const int K = a.n_q * a.head_dim;
-  return a.dtype == 0 ? residual_t<float>(a, K, sh.rows_o, sh.grid_o, L.wo, a.o, false, s)
-                      : residual_t<__half>(a, K, sh.rows_o, sh.grid_o, L.wo, a.o, false, s);
+  return a.dtype == 0 ? residual_t<float>(a, K, sh.rows_o, sh.grid_o, L.wo, a.o, a.x, a.x2, false, s)
+                      : residual_t<__half>(a, K, sh.rows_o, sh.grid_o, L.wo, a.o, a.x, a.x2, false, s);
 }
 bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   return a.dtype == 0 ? gateup_t<float>(a, sh, L, s) : gateup_t<__half>(a, sh, L, s);
 }
 bool launch_down(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool adv, hipStream_t s) {
-  return a.dtype == 0 ? residual_t<float>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, a.act, adv, s)
-                      : residual_t<__half>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, a.act, adv, s);
+  return a.dtype == 0 ? residual_t<float>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, a.act, a.x2, a.x, adv, s)
+                      : residual_t<__half>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, a.act, a.x2, a.x, adv, s);
 }
 bool launch_head(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   return a.dtype == 0 ? head_t<float>(a, sh, s) : head_t<__half>(a, sh, s);

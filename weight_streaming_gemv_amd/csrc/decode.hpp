@@ -8,11 +8,14 @@ namespace wsg {
 
 // Control words in the workspace (int32 each).
 enum CtrlWord : int {
-  kCtrlPos = 0,        // current position p (tokens already in the cache)
-  kCtrlOutTok = 1,     // last greedy token
-  kCtrlAttnCnt = 16,   // [n_kv] arrival counters of the split-K attention merge
-  kCtrlWords = 64
+  kCtrlPos = 0,          // current position p (tokens already in the cache)
+  kCtrlOutTok = 1,       // last greedy token
+  kCtrlAttnCnt = 128,    // [n_kv <= 256] arrival counters of the split-K attention merge
+  kCtrlWords = 384
 };
+
+// The head kernel runs at most kHeadMaxBlocks blocks (one argmax key each).
+constexpr int kHeadMaxBlocks = 4096;
 
 struct LayerPtrs {
   const void* wqkv;     // [(Q + 2 KV)][H]
@@ -35,15 +38,15 @@ struct DecodeArgs {
   const void* final_norm;
   const float* rope_cos;  // [cap][D/2]
   const float* rope_sin;
-  void* x;              // residual [H]
+  void* x;              // residual [H]: layer input / down-projection output
+  void* x2;             // residual [H]: output-projection output / MLP input
   void* qkv;            // [Q + 2 KV]
   void* o;              // [Q]
   void* act;            // [I]
   void* logits;         // [V]
   float* attn_part;     // split-K partial states
   int attn_part_splits; // capacity in splits per KV head
-  unsigned long long* am_part;  // per-block argmax keys of the head
-  int am_part_cap;
+  unsigned long long* am_part;  // [kHeadMaxBlocks] per-block argmax keys of the head
   int32_t* ctrl;
   int32_t* ids;         // token history [cap + 1]
 };
@@ -62,6 +65,9 @@ bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L,
 bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
 bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
 bool launch_down(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool advance_pos, hipStream_t s);
+// Final RMSNorm + vocabulary GEMV with one argmax key per block; then the
+// one-block argmax (ties to the lowest id) writes the token into ctrl and
+// the token history and advances the position.
 bool launch_head(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s);
 bool launch_argmax(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s);
 bool launch_set_pos(int32_t* ctrl, int pos, hipStream_t s);

@@ -93,7 +93,6 @@ PackedLayout packed_layout(const Dims& d) {
   return p;
 }
 
-constexpr int kAmPartCap = 65536;
 constexpr int kMinAttnChunk = 64;
 
 int attn_split_cap(const Dims& d) {
@@ -103,7 +102,7 @@ int attn_split_cap(const Dims& d) {
 }
 
 struct WsLayout {
-  size_t kv = 0, rope_cos = 0, rope_sin = 0, x = 0, qkv = 0, o = 0, act = 0, logits = 0;
+  size_t kv = 0, rope_cos = 0, rope_sin = 0, x = 0, x2 = 0, qkv = 0, o = 0, act = 0, logits = 0;
   size_t attn_part = 0, am_part = 0, ctrl = 0, ids = 0, total = 0;
   PrefillLayout pf;
   int attn_splits_cap = 1;
@@ -117,13 +116,14 @@ WsLayout ws_layout(const Dims& d) {
   w.rope_cos = take((size_t)d.cap * (d.D / 2) * 4);
   w.rope_sin = take((size_t)d.cap * (d.D / 2) * 4);
   w.x = take((size_t)d.H * d.es);
+  w.x2 = take((size_t)d.H * d.es);
   w.qkv = take((size_t)(d.Q + 2 * d.KV) * d.es);
   w.o = take((size_t)d.Q * d.es);
   w.act = take((size_t)d.I * d.es);
   w.logits = take((size_t)d.V * d.es);
   w.attn_splits_cap = attn_split_cap(d);
   w.attn_part = take((size_t)d.nkv * w.attn_splits_cap * d.G * (2 + d.D) * 4);
-  w.am_part = take((size_t)kAmPartCap * 8);
+  w.am_part = take((size_t)kHeadMaxBlocks * 8);
   w.ctrl = take((size_t)kCtrlWords * 4);
   w.ids = take((size_t)(d.cap + 1) * 4);
   const size_t pf_base = off;
@@ -164,6 +164,9 @@ struct wsg_model {
   double acc_ms = 0;
   int64_t acc_launches = 0, acc_bytes = 0;
   int prefill_rows = 0;
+  bool event_error = false;
+  bool capturing = false;
+  char event_msg[160] = {0};
 };
 
 namespace {
@@ -180,41 +183,54 @@ int64_t stage_bytes(const wsg_model* m, int stage) {
   }
 }
 
-// Launch one stage, bracketed by events when it is the timed stage kind.
+// Events bracket launches of the timed stage kind.  Event-record nodes
+// inside HIP graphs do not carry usable timestamps, so in graph mode only the
+// head is timed, with events recorded on the stream around its own graph;
+// per-layer stages are timed in direct-launch mode.
+bool record_event(wsg_model* m, hipEvent_t e) {
+  const hipError_t r = hipEventRecord(e, m->stream);
+  if (r != hipSuccess) {
+    snprintf(m->event_msg, sizeof(m->event_msg), "hipEventRecord: %s", hipGetErrorString(r));
+    m->event_error = true;
+    return false;
+  }
+  return true;
+}
+
 template <typename F>
 bool timed(wsg_model* m, int stage, F&& launch) {
-  const bool t = (m->timed_stage == stage) && (m->ev_used + 2 <= (int)m->ev.size());
-  if (t) (void)hipEventRecord(m->ev[m->ev_used], m->stream);
+  const bool t = !m->capturing && (m->timed_stage == stage) && (m->ev_used + 2 <= (int)m->ev.size());
+  if (t) record_event(m, m->ev[m->ev_used]);
   const bool ok = launch();
   if (t) {
-    (void)hipEventRecord(m->ev[m->ev_used + 1], m->stream);
+    record_event(m, m->ev[m->ev_used + 1]);
     m->ev_used += 2;
     m->timed_bytes_per_launch_sum += stage_bytes(m, stage);
   }
   return ok;
 }
 
-bool enqueue_forward(wsg_model* m, bool head, int splits) {
+// All layers of one token; the last down projection advances the position
+// when no head follows (prompt rows before the last).
+bool enqueue_body(wsg_model* m, int splits, bool advance) {
   DecodeShape sh = m->shape;
   sh.attn_splits = splits;
   const hipStream_t s = m->stream;
   const int L = m->d.L;
-  m->ev_used = 0;
-  m->timed_bytes_per_launch_sum = 0;
   for (int l = 0; l < L; ++l) {
     const LayerPtrs& lp = m->layers[l];
     if (!timed(m, WSG_STAGE_QKV, [&] { return launch_qkv(m->args, sh, lp, l == 0, s); })) return false;
     if (!timed(m, WSG_STAGE_ATTN, [&] { return launch_attn(m->args, sh, lp, s); })) return false;
     if (!timed(m, WSG_STAGE_O, [&] { return launch_o(m->args, sh, lp, s); })) return false;
     if (!timed(m, WSG_STAGE_GATEUP, [&] { return launch_gateup(m->args, sh, lp, s); })) return false;
-    if (!timed(m, WSG_STAGE_DOWN, [&] { return launch_down(m->args, sh, lp, !head && l == L - 1, s); })) return false;
-  }
-  if (head) {
-    if (!timed(m, WSG_STAGE_HEAD, [&] { return launch_head(m->args, sh, s); })) return false;
-    if (!timed(m, WSG_STAGE_ARGMAX, [&] { return launch_argmax(m->args, sh, s); })) return false;
+    if (!timed(m, WSG_STAGE_DOWN, [&] { return launch_down(m->args, sh, lp, advance && l == L - 1, s); }))
+      return false;
   }
   return true;
 }
+
+bool enqueue_head(wsg_model* m) { return launch_head(m->args, m->shape, m->stream); }
+bool enqueue_argmax(wsg_model* m) { return launch_argmax(m->args, m->shape, m->stream); }
 
 int splits_for(const wsg_model* m, int n_keys) {
   const int want = pow2_ceil((n_keys + kMinAttnChunk - 1) / kMinAttnChunk);
@@ -226,46 +242,80 @@ void drop_graphs(wsg_model* m) {
   m->graphs.clear();
 }
 
-// Enqueue one token forward at the current device position.
+// Capture (once) and return the graph for `key`, built by `enqueue`.
+template <typename F>
+wsg_status graph_for(wsg_model* m, int key, F&& enqueue, hipGraphExec_t* out) {
+  auto it = m->graphs.find(key);
+  if (it != m->graphs.end()) { *out = it->second; return WSG_OK; }
+  WSG_HIP_CHECK(hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
+  m->capturing = true;
+  const bool ok = enqueue();
+  m->capturing = false;
+  hipGraph_t g = nullptr;
+  const hipError_t ec = hipStreamEndCapture(m->stream, &g);
+  if (!ok) { if (g) (void)hipGraphDestroy(g); return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape"); }
+  if (ec != hipSuccess) return fail(WSG_ERR_HIP, "graph capture: %s", hipGetErrorString(ec));
+  hipGraphExec_t ex = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (ei != hipSuccess) return fail(WSG_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ei));
+  m->graphs.emplace(key, ex);
+  *out = ex;
+  return WSG_OK;
+}
+
+constexpr int kHeadGraphKey = -1;
+constexpr int kArgmaxGraphKey = -2;
+
+// Enqueue one token forward at the current device position: the layer body
+// and, if `head`, the head (final norm, vocabulary GEMV, argmax).
 wsg_status run_forward(wsg_model* m, bool head, int n_keys) {
   const int splits = splits_for(m, n_keys);
+  const bool advance = !head;
+  (void)hipGetLastError();   // errors of earlier calls were reported by those calls
+  m->ev_used = 0;
+  m->timed_bytes_per_launch_sum = 0;
   if (!m->use_graph) {
-    if (!enqueue_forward(m, head, splits)) return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape");
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(WSG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
-    return WSG_OK;
-  }
-  const int key = splits * 2 + (head ? 1 : 0);
-  auto it = m->graphs.find(key);
-  if (it == m->graphs.end()) {
-    WSG_HIP_CHECK(hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
-    const bool ok = enqueue_forward(m, head, splits);
-    hipGraph_t g = nullptr;
-    const hipError_t ec = hipStreamEndCapture(m->stream, &g);
-    if (!ok) { if (g) (void)hipGraphDestroy(g); return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape"); }
-    if (ec != hipSuccess) return fail(WSG_ERR_HIP, "graph capture: %s", hipGetErrorString(ec));
-    hipGraphExec_t ex = nullptr;
-    const hipError_t ei = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(g);
-    if (ei != hipSuccess) return fail(WSG_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ei));
-    it = m->graphs.emplace(key, ex).first;
+    if (!enqueue_body(m, splits, advance)) return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape");
   } else {
-    // keep ev_used consistent with the event nodes the graph records
-    m->ev_used = 0;
-    m->timed_bytes_per_launch_sum = 0;
-    if (m->timed_stage >= 0) {
-      int launches = 0;
-      if (m->timed_stage == WSG_STAGE_HEAD || m->timed_stage == WSG_STAGE_ARGMAX) launches = head ? 1 : 0;
-      else launches = m->d.L;
-      m->ev_used = 2 * launches;
-      m->timed_bytes_per_launch_sum = launches * stage_bytes(m, m->timed_stage);
+    hipGraphExec_t body = nullptr;
+    const wsg_status st = graph_for(m, splits * 2 + (advance ? 1 : 0),
+                                    [&] { return enqueue_body(m, splits, advance); }, &body);
+    if (st != WSG_OK) return st;
+    WSG_HIP_CHECK(hipGraphLaunch(body, m->stream));
+  }
+  if (head) {
+    const bool t = m->timed_stage == WSG_STAGE_HEAD;
+    if (t) record_event(m, m->ev[0]);
+    if (!m->use_graph) {
+      if (!enqueue_head(m)) return fail(WSG_ERR_UNSUPPORTED, "no compiled head kernel for this shape");
+    } else {
+      hipGraphExec_t hg = nullptr;
+      const wsg_status st = graph_for(m, kHeadGraphKey, [&] { return enqueue_head(m); }, &hg);
+      if (st != WSG_OK) return st;
+      WSG_HIP_CHECK(hipGraphLaunch(hg, m->stream));
+    }
+    if (t) {
+      record_event(m, m->ev[1]);
+      m->ev_used = 2;
+      m->timed_bytes_per_launch_sum = stage_bytes(m, WSG_STAGE_HEAD);
+    }
+    if (!m->use_graph) {
+      if (!enqueue_argmax(m)) return fail(WSG_ERR_UNSUPPORTED, "argmax launch");
+    } else {
+      hipGraphExec_t ag = nullptr;
+      const wsg_status st = graph_for(m, kArgmaxGraphKey, [&] { return enqueue_argmax(m); }, &ag);
+      if (st != WSG_OK) return st;
+      WSG_HIP_CHECK(hipGraphLaunch(ag, m->stream));
     }
   }
-  WSG_HIP_CHECK(hipGraphLaunch(it->second, m->stream));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(WSG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return WSG_OK;
 }
 
 wsg_status collect_timing(wsg_model* m) {
+  if (m->event_error) { m->event_error = false; return fail(WSG_ERR_HIP, "recording a timing event failed: %s", m->event_msg); }
   if (m->timed_stage < 0 || m->ev_used == 0) return WSG_OK;
   for (int i = 0; i + 1 < m->ev_used; i += 2) {
     float ms = 0.f;
@@ -410,12 +460,11 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   a.final_norm = m->packed + pl.final_norm;
   a.rope_cos = reinterpret_cast<const float*>(m->ws + wl.rope_cos);
   a.rope_sin = reinterpret_cast<const float*>(m->ws + wl.rope_sin);
-  a.x = m->ws + wl.x; a.qkv = m->ws + wl.qkv; a.o = m->ws + wl.o; a.act = m->ws + wl.act;
+  a.x = m->ws + wl.x; a.x2 = m->ws + wl.x2; a.qkv = m->ws + wl.qkv; a.o = m->ws + wl.o; a.act = m->ws + wl.act;
   a.logits = m->ws + wl.logits;
   a.attn_part = reinterpret_cast<float*>(m->ws + wl.attn_part);
   a.attn_part_splits = wl.attn_splits_cap;
   a.am_part = reinterpret_cast<unsigned long long*>(m->ws + wl.am_part);
-  a.am_part_cap = kAmPartCap;
   a.ctrl = reinterpret_cast<int32_t*>(m->ws + wl.ctrl);
   a.ids = reinterpret_cast<int32_t*>(m->ws + wl.ids);
   const size_t kv_layer = (size_t)2 * d.nkv * d.cap * d.D * d.es;
@@ -435,7 +484,6 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   sh.grid_head = 4096;
   sh.attn_splits = 1;
   sh.attn_min_chunk = kMinAttnChunk;
-  if (head_blocks(a, sh) > kAmPartCap) return fail_free(fail(WSG_ERR_UNSUPPORTED, "vocabulary too large"));
 
   std::vector<float> cs, sn;
   fill_rope(*cfg, cs, sn);
@@ -464,6 +512,7 @@ void wsg_model_destroy(wsg_model* m) {
 wsg_status wsg_reset_cache(wsg_model* m) {
   clear_error();
   if (!m) return fail(WSG_ERR_INVALID_ARG, "model is NULL");
+  (void)hipGetLastError();   // errors of earlier calls were reported by those calls
   launch_set_pos(m->args.ctrl, 0, m->stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(WSG_ERR_HIP, "reset: %s", hipGetErrorString(e));
@@ -555,14 +604,35 @@ wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value) {
     case WSG_OPT_USE_GRAPH:
       if (value != 0 && value != 1) return fail(WSG_ERR_INVALID_ARG, "use_graph must be 0 or 1");
       if (value == 1 && m->stream == nullptr) return fail(WSG_ERR_STATE, "graphs need a non-null stream");
+      if (value == 1 && m->timed_stage >= 0 && m->timed_stage != WSG_STAGE_HEAD)
+        return fail(WSG_ERR_UNSUPPORTED, "in graph mode only the head stage can be timed");
       m->use_graph = value == 1;
       return WSG_OK;
     case WSG_OPT_TIMED_STAGE:
-      if (value < -1 || value > WSG_STAGE_ARGMAX) return fail(WSG_ERR_INVALID_ARG, "stage %d", value);
+      if (value < -1 || value > WSG_STAGE_HEAD) return fail(WSG_ERR_INVALID_ARG, "stage %d", value);
+      if (m->use_graph && value >= 0 && value != WSG_STAGE_HEAD)
+        return fail(WSG_ERR_UNSUPPORTED, "in graph mode only the head stage can be timed (set use_graph 0 first)");
       m->timed_stage = value;
       m->acc_ms = 0; m->acc_launches = 0; m->acc_bytes = 0;
-      drop_graphs(m);   // the captured plan changes with the event nodes
       return WSG_OK;
+    default:
+      break;
+  }
+  if (option >= WSG_OPT_ROWS_QKV && option <= WSG_OPT_ROWS_HEAD) {
+    if (value != 1 && value != 2 && value != 4) return fail(WSG_ERR_INVALID_ARG, "rows per wave must be 1, 2 or 4");
+    int* rows[] = {&m->shape.rows_qkv, &m->shape.rows_o, &m->shape.rows_gu, &m->shape.rows_down, &m->shape.rows_head};
+    *rows[option - WSG_OPT_ROWS_QKV] = value;
+    drop_graphs(m);
+    return WSG_OK;
+  }
+  if (option >= WSG_OPT_GRID_QKV && option <= WSG_OPT_GRID_HEAD) {
+    if (value < 0 || value > (1 << 20)) return fail(WSG_ERR_INVALID_ARG, "grid must be in [0, 2^20]");
+    int* grids[] = {&m->shape.grid_qkv, &m->shape.grid_o, &m->shape.grid_gu, &m->shape.grid_down, &m->shape.grid_head};
+    *grids[option - WSG_OPT_GRID_QKV] = value;
+    drop_graphs(m);
+    return WSG_OK;
+  }
+  switch (option) {
     default:
       return fail(WSG_ERR_INVALID_ARG, "unknown option %d", option);
   }
