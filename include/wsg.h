@@ -159,9 +159,10 @@ wsg_status wsg_set_prefill_chunk(wsg_model* m, int32_t rows);
  * on the model stream around every launch of one stage kind, see
  * wsg_stage_time; -1 = off).  Event-record nodes inside HIP graphs carry no
  * usable timestamps on this platform, so with graphs on only
- * WSG_STAGE_HEAD can be timed (its launch is a graph of its own, bracketed
- * by stream events); other stages need WSG_OPT_USE_GRAPH = 0, where each
- * bracketing event adds its own overhead to short kernels.
+ * WSG_STAGE_HEAD can be timed (the head is always a direct launch after the
+ * layer graph, bracketed by stream events); other stages need
+ * WSG_OPT_USE_GRAPH = 0, where each bracketing event adds its own overhead
+ * to short kernels.
  * Errors: WSG_ERR_UNSUPPORTED for a per-layer stage while graphs are on. */
 enum { WSG_OPT_USE_GRAPH = 1, WSG_OPT_TIMED_STAGE = 2 };
 /* Launch shape of the decode GEMV stages (tuning): rows per wave (1, 2 or

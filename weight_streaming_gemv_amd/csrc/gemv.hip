@@ -185,7 +185,9 @@ __global__ __launch_bounds__(kBlock) void k_gemv_scalar(const TW* __restrict__ W
 // 1032 (after flipping bit 3, which maps two's complement onto offset
 // binary); every step is exact.  The activations are staged once per
 // workgroup in LDS, permuted so that each FP16 pair lines up with the
-// nibble pair (j, j+4) that one 32-bit word yields.
+// nibble pair (j, j+4) that one 32-bit word yields, and placed so that the
+// 64 lanes of a wave read 64 consecutive 16-byte LDS slots (lane l's word i
+// of chunk c sits at c*256 + i*64 + l): no bank conflicts.
 template <int K, int R, int T, bool NT>
 __global__ __launch_bounds__(kBlock) void k_gemv_q4(const uint32_t* __restrict__ Wq,
                                                     const __half* __restrict__ S,
@@ -196,16 +198,29 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4(const uint32_t* __restrict__
   constexpr int G = K / 64;      // groups (scales) per row
   static_assert(K % 2048 == 0, "fixed-K int4 kernel needs K % 2048 == 0");
   __shared__ uint4 xs[T][W8];
-  for (int i = threadIdx.x; i < T * W8; i += kBlock) {
+  static_assert((T * W8) % kBlock == 0, "staging assumes whole rounds of the block");
+  constexpr int kStage = T * W8 / kBlock;
+  // all staging loads in flight at once, then the permuted LDS stores
+  uint4 hx[kStage];
+#pragma unroll
+  for (int it = 0; it < kStage; ++it) {
+    const int i = threadIdx.x + it * kBlock;
     const int t = i / W8, gi = i - t * W8;
-    const uint4 h = *reinterpret_cast<const uint4*>(X + (size_t)t * K + gi * 8);
+    hx[it] = *reinterpret_cast<const uint4*>(X + (size_t)t * K + gi * 8);
+  }
+#pragma unroll
+  for (int it = 0; it < kStage; ++it) {
+    const int i = threadIdx.x + it * kBlock;
+    const int t = i / W8, gi = i - t * W8;
+    const uint4 h = hx[it];
     // halves 0..7 -> pairs (0,4) (1,5) (2,6) (3,7)
     uint4 p;
     p.x = (h.x & 0xFFFFu) | (h.z << 16);
     p.y = (h.x >> 16) | (h.z & 0xFFFF0000u);
     p.z = (h.y & 0xFFFFu) | (h.w << 16);
     p.w = (h.y >> 16) | (h.w & 0xFFFF0000u);
-    xs[t][gi] = p;
+    const int c = gi >> 8, w = gi & 255;
+    xs[t][(c << 8) + ((w & 3) << 6) + (w >> 2)] = p;
   }
   __syncthreads();
 
@@ -222,7 +237,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4(const uint32_t* __restrict__
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const size_t row = (size_t)min(row0 + r, M - 1);
-#pragma unroll
+      // partial unroll keeps long rows (K = 14336) from using every VGPR
+#pragma unroll 2
       for (int c = 0; c < NV; ++c) {
         const uint4 w = load_u4<NT>(Wq + row * W8 + c * 256 + lane * 4);
         const float sc = __half2float(S[row * G + c * 32 + (lane >> 1)]);
@@ -239,7 +255,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4(const uint32_t* __restrict__
           const h2_t p3 = as_h2(((v >> 12) & 0x000F000Fu) | 0x64006400u) - bias;
 #pragma unroll
           for (int t = 0; t < T; ++t) {
-            const uint4 xv = xs[t][c * 256 + lane * 4 + i];
+            const uint4 xv = xs[t][c * 256 + i * 64 + lane];
             float a = inner[t];
             a = dot2(p0, as_h2(xv.x), a);
             a = dot2(p1, as_h2(xv.y), a);

@@ -264,8 +264,6 @@ wsg_status graph_for(wsg_model* m, int key, F&& enqueue, hipGraphExec_t* out) {
   return WSG_OK;
 }
 
-constexpr int kHeadGraphKey = -1;
-constexpr int kArgmaxGraphKey = -2;
 
 // Enqueue one token forward at the current device position: the layer body
 // and, if `head`, the head (final norm, vocabulary GEMV, argmax).
@@ -285,29 +283,17 @@ wsg_status run_forward(wsg_model* m, bool head, int n_keys) {
     WSG_HIP_CHECK(hipGraphLaunch(body, m->stream));
   }
   if (head) {
+    // The head and the argmax are single launches, issued directly (a graph
+    // saves nothing for one kernel), so stream events can bracket the head.
     const bool t = m->timed_stage == WSG_STAGE_HEAD;
     if (t) record_event(m, m->ev[0]);
-    if (!m->use_graph) {
-      if (!enqueue_head(m)) return fail(WSG_ERR_UNSUPPORTED, "no compiled head kernel for this shape");
-    } else {
-      hipGraphExec_t hg = nullptr;
-      const wsg_status st = graph_for(m, kHeadGraphKey, [&] { return enqueue_head(m); }, &hg);
-      if (st != WSG_OK) return st;
-      WSG_HIP_CHECK(hipGraphLaunch(hg, m->stream));
-    }
+    if (!enqueue_head(m)) return fail(WSG_ERR_UNSUPPORTED, "no compiled head kernel for this shape");
     if (t) {
       record_event(m, m->ev[1]);
       m->ev_used = 2;
       m->timed_bytes_per_launch_sum = stage_bytes(m, WSG_STAGE_HEAD);
     }
-    if (!m->use_graph) {
-      if (!enqueue_argmax(m)) return fail(WSG_ERR_UNSUPPORTED, "argmax launch");
-    } else {
-      hipGraphExec_t ag = nullptr;
-      const wsg_status st = graph_for(m, kArgmaxGraphKey, [&] { return enqueue_argmax(m); }, &ag);
-      if (st != WSG_OK) return st;
-      WSG_HIP_CHECK(hipGraphLaunch(ag, m->stream));
-    }
+    if (!enqueue_argmax(m)) return fail(WSG_ERR_UNSUPPORTED, "argmax launch");
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(WSG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));

@@ -1,0 +1,111 @@
+"""Summaries of rocprofv3 kernel traces for the profiles/ notes.
+
+``python -m weight_streaming_gemv_amd.profsum decode <run_kernel_trace.csv>``
+    per-kernel median durations of a decode run and the per-token sum;
+``python -m weight_streaming_gemv_amd.profsum sweep <run_kernel_trace.csv>``
+    kernel-only GB/s of every cold-sweep configuration (bench.py --sweep-only),
+    matched to its launch by kernel template arguments and grid size.
+
+Durations are the trace's begin/end timestamps (device time of each dispatch,
+no launch gaps).
+"""
+from __future__ import annotations
+
+import csv
+import re
+import statistics
+import sys
+from collections import defaultdict
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def load(path):
+    groups = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            blocks = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            groups[(r["Kernel_Name"], blocks, int(r["Grid_Size_Y"]))].append(d)
+    return groups
+
+
+def short(name):
+    m = re.match(r"(?:void )?(?:wsg::)?(?:\(anonymous namespace\)::)?([\w:]+)(<[^(]*>)?", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name[:60]
+
+
+def decode_table(path):
+    g = load(path)
+    by_name = defaultdict(list)
+    for (name, blocks, gy), ds in g.items():
+        by_name[short(name).split("<")[0]].extend(ds)
+    rows = sorted(((sum(ds), n, ds) for n, ds in by_name.items()), reverse=True)
+    print("| kernel | calls | median us | mean us | total ms | share |")
+    print("|---|---|---|---|---|---|")
+    tot = sum(r[0] for r in rows)
+    for s, n, ds in rows:
+        print(f"| {n} | {len(ds)} | {statistics.median(ds) / 1e3:.2f} | {statistics.fmean(ds) / 1e3:.2f} | "
+              f"{s / 1e6:.2f} | {100 * s / tot:.1f}% |")
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+def sweep_table(path):
+    from synth import GEMV_SHAPES, Q4_SHAPES
+    g = load(path)
+    idx = defaultdict(list)
+    for (name, blocks, gy), ds in g.items():
+        idx[(short(name), blocks)].extend(ds)
+    print("| kernel | M x K | T | R | blocks | calls | median us | GB/s | % of 8 TB/s |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    best = {}
+    for dt, es, kname in (("f32", 4, "k_gemv_f32"), ("f16", 2, "k_gemv_f16"), ("q4g64", None, "k_gemv_q4")):
+        shapes = Q4_SHAPES if dt == "q4g64" else GEMV_SHAPES
+        for (M, K) in shapes:
+            nbytes = M * K // 2 + M * (K // 64) * 2 if dt == "q4g64" else M * K * es
+            for T in (1, 2):
+                for R in (1, 2, 4, 8):
+                    seen = set()
+                    grids = (0, 256, 512) if dt == "q4g64" else ((0, 1280, 2048, 4096) if M > 100000 else (0,))
+                    for G in grids:
+                        one = _ceil(_ceil(M, R), 4)
+                        blocks = one if G == 0 or G >= one else G
+                        if blocks in seen:
+                            continue
+                        seen.add(blocks)
+                        key = (f"{kname}<{K}, {R}, {T}, false>", blocks)
+                        ds = idx.get(key)
+                        if not ds:
+                            continue
+                        us = statistics.median(ds) / 1e3
+                        gbps = nbytes / us / 1e3
+                        print(f"| {kname} | {M}x{K} | {T} | {R} | {blocks} | {len(ds)} | {us:.2f} | {gbps:.0f} | "
+                              f"{100 * gbps / HBM_PEAK_GBPS:.1f} |")
+                        k = (dt, M, K, T)
+                        if k not in best or us < best[k][0]:
+                            best[k] = (us, R, blocks, gbps)
+    print()
+    print("Best per shape (kernel-only):")
+    print()
+    print("| dtype | M x K | T | R | blocks | median us | GB/s | % of peak |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (dt, M, K, T), (us, R, b, gbps) in sorted(best.items()):
+        print(f"| {dt} | {M}x{K} | {T} | {R} | {b} | {us:.2f} | {gbps:.0f} | {100 * gbps / HBM_PEAK_GBPS:.1f} |")
+    for dt, es in (("f32", 4), ("f16", 2)):
+        names = [(4096, 1024), (1024, 2048), (6144, 1024), (1024, 3072), (151936, 1024)]
+        if all((dt, M, K, 1) in best for M, K in names):
+            w = [28, 28, 28, 28, 1]
+            b = sum(wi * M * K * es for wi, (M, K) in zip(w, names))
+            t = sum(wi * best[(dt, M, K, 1)][0] for wi, (M, K) in zip(w, names))
+            print(f"\nDecode-mix aggregate {dt} (28 x [QKV, O, gate/up, down] + vocab, T=1, best R): "
+                  f"{b / t / 1e3:.0f} GB/s = {100 * b / t / 1e3 / HBM_PEAK_GBPS:.1f}% of 8 TB/s")
+
+
+if __name__ == "__main__":
+    import os
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    mode, path = sys.argv[1], sys.argv[2]
+    {"decode": decode_table, "sweep": sweep_table}[mode](path)
