@@ -229,6 +229,130 @@ def sweep_summary(sw):
     return best, agg
 
 
+def long_context(torch, wsg, shape, w, validate_outputs=32, trials=5, warmup=2):
+    """Long-document workload (Benchmark methodology, "Long-document chunked prefill").
+
+    Chunk selection: a 2048-id prompt with 8 outputs at chunk sizes 128, 256,
+    512 and 1024; every candidate is validated first (whole-prefix KV of every
+    layer, first-output logits, greedy tokens against the oracle); 2 warm-ups
+    and 5 timed trials each; the smallest median TTFT wins, ties to the smaller
+    chunk.  Held-out: a different 4096-id prompt with 1024 outputs at the chosen
+    chunk, validated (prefix KV, first logits, the first ``validate_outputs``
+    greedy tokens, each new KV slot) against the oracle, then timed; every
+    timed run must reproduce the validated token ids (all 1024).
+    """
+    import oracle
+    from synth import PROMPT_SEEDS, prompt_ids
+    cap = 5120
+    tune = prompt_ids(PROMPT_SEEDS["tuning"], 2048, shape.vocab)
+    held = prompt_ids(PROMPT_SEEDS["heldout"], 4096, shape.vocab)
+    assert not np.array_equal(tune[:2048], held[:2048])
+    model = wsg.Model(shape, w, max_context=cap, prefill_chunk=1024)
+    orc = oracle.OracleModel(shape, w, cap)
+
+    def cmp(got, ref, what, tol=1e-3):
+        g = got.float().cpu().numpy().astype(np.float64)
+        r = np.asarray(ref, dtype=np.float64)
+        err = np.abs(g - r)
+        if np.any(err > tol + tol * np.abs(r)):
+            raise RuntimeError(f"long-context validation failed: {what} off by {err.max():.3e}")
+        return float(err.max())
+
+    def check_prefix(n, what):
+        mk = 0.0
+        for l in range(shape.n_layers):
+            k, v, _ = model.kv(l)
+            mk = max(mk, cmp(k[:, :n], orc.k_cache[l][:, :n], f"{what} K layer {l}"))
+            mk = max(mk, cmp(v[:, :n], orc.v_cache[l][:, :n], f"{what} V layer {l}"))
+        return mk
+
+    # oracle reference for the tuning prompt (chunk-independent)
+    t = time.perf_counter()
+    orc.reset()
+    ref_logits = orc.forward_rows(tune)
+    ref_toks = [oracle.argmax_lowest(ref_logits)]
+    for _ in range(7):
+        ref_toks.append(oracle.argmax_lowest(orc.forward_rows([ref_toks[-1]])))
+    log(f"long: oracle tuning reference in {time.perf_counter() - t:.1f} s")
+    # orc now holds the KV of 2048 + 7 positions
+    max_kv = max_logit = 0.0
+    sweep = {}
+    for chunk in (128, 256, 512, 1024):
+        model.set_prefill_chunk(chunk)
+        model.reset()
+        tok = model.prefill(tune)
+        max_logit = max(max_logit, cmp(model.logits(), ref_logits, f"chunk {chunk} first logits"))
+        max_kv = max(max_kv, check_prefix(2048, f"chunk {chunk} prompt"))
+        toks = [tok] + [model.step() for _ in range(7)]
+        if toks != ref_toks:
+            raise RuntimeError(f"long-context validation failed: chunk {chunk} tokens {toks} != oracle {ref_toks}")
+        rec = []
+        for i in range(warmup + trials):
+            tk, ttft, dec, tot = generate(model, tune, 8)
+            if tk != ref_toks:
+                raise RuntimeError(f"chunk {chunk}: timed tokens differ from the validated ones")
+            if i >= warmup:
+                rec.append((ttft, dec, tot))
+        sweep[chunk] = {"ttft_ms": round(statistics.median(r[0] for r in rec) * 1e3, 2),
+                        "total_ms": round(statistics.median(r[2] for r in rec) * 1e3, 2)}
+        log(f"long: chunk {chunk}: {sweep[chunk]}")
+    best = min(sweep, key=lambda c: (sweep[c]["ttft_ms"], c))
+
+    # held-out: validate then time
+    model.set_prefill_chunk(best)
+    t = time.perf_counter()
+    orc.reset()
+    ref_logits = orc.forward_rows(held)
+    log(f"long: oracle held-out prefill in {time.perf_counter() - t:.1f} s")
+    model.reset()
+    tok = model.prefill(held)
+    max_logit = max(max_logit, cmp(model.logits(), ref_logits, "held-out first logits"))
+    max_kv = max(max_kv, check_prefix(4096, "held-out prompt"))
+    toks = [tok]
+    rtok = oracle.argmax_lowest(ref_logits)
+    if tok != rtok:
+        raise RuntimeError(f"held-out first token {tok} != oracle {rtok} (margin {orc.logits_margin(ref_logits):.3e})")
+    t_or = 0.0
+    for s_ in range(1, 1024):
+        p = model.position
+        toks.append(model.step())
+        if s_ < validate_outputs:
+            t0 = time.perf_counter()
+            ref = orc.forward_rows([toks[-2]])
+            t_or += time.perf_counter() - t0
+            rtok = oracle.argmax_lowest(ref)
+            max_logit = max(max_logit, cmp(model.logits(), ref, f"held-out logits step {s_}"))
+            for l in range(shape.n_layers):
+                k, v, _ = model.kv(l)
+                max_kv = max(max_kv, cmp(k[:, p:p + 1], orc.k_cache[l][:, p:p + 1], f"held-out K step {s_}"))
+                max_kv = max(max_kv, cmp(v[:, p:p + 1], orc.v_cache[l][:, p:p + 1], f"held-out V step {s_}"))
+            if toks[-1] != rtok:
+                raise RuntimeError(f"held-out step {s_}: token {toks[-1]} != oracle {rtok} "
+                                   f"(margin {orc.logits_margin(ref):.3e})")
+    max_kv = max(max_kv, check_prefix(4096 + validate_outputs - 1, "held-out prefix"))
+    if model.position != 4096 + 1023:
+        raise RuntimeError("held-out valid length is not 5119")
+    rec = []
+    for i in range(warmup + trials):
+        tk, ttft, dec, tot = generate(model, held, 1024)
+        if tk != toks:
+            raise RuntimeError("held-out timed tokens differ from the validated sequence")
+        if i >= warmup:
+            rec.append((ttft, dec, tot))
+    model.close()
+    return {
+        "workload": "28-layer FP32; chunk selection on a 2048-id prompt / 8 outputs, held-out 4096-id prompt / "
+                    "1024 outputs (5,119 valid KV entries at the end)",
+        "chunk_sweep": sweep, "selected_chunk": best,
+        "heldout_median": {"ttft_ms": round(statistics.median(r[0] for r in rec) * 1e3, 2),
+                           "decode_tok_s": round(statistics.median(1023 / r[1] for r in rec), 1),
+                           "total_s": round(statistics.median(r[2] for r in rec), 3)},
+        "validation": {"max_abs_logit_err": max_logit, "max_abs_kv_err": max_kv,
+                       "oracle_checked_outputs": validate_outputs, "timed_runs_token_exact": True},
+        "cpu_oracle_decode_tok_s_at_4k": round((validate_outputs - 1) / t_or, 3) if t_or else None,
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +364,8 @@ def main(argv=None):
     ap.add_argument("--sweep", choices=["full", "quick", "none"], default="full",
                     help="cold-cache GEMV sweep after the decode timing")
     ap.add_argument("--sweep-only", action="store_true", help="run only the cold-cache GEMV sweep")
+    ap.add_argument("--long", choices=["on", "off", "only"], default="on",
+                    help="long-document workload (2048-id chunk selection, 4096 -> 1024 held-out)")
     ap.add_argument("--no-oracle", action="store_true",
                     help="skip validation and the CPU baseline (profiling runs only; no value is published)")
     args = ap.parse_args(argv)
@@ -269,7 +395,7 @@ def main(argv=None):
     log(f"weights generated in {time.perf_counter() - t:.1f} s")
     prompt32 = prompt_ids(PROMPT_SEEDS["short"], 32, shape.vocab)
     prompts = {8: prompt32[:8], 32: prompt32}
-    model = wsg.Model(shape, w, max_context=cap)
+    model = wsg.Model(shape, w, max_context=cap, prefill_chunk=32)
     if args.no_graph:
         model.set_option(wsg._abi.WSG_OPT_USE_GRAPH, 0)
 
@@ -294,6 +420,12 @@ def main(argv=None):
         log(f"validation passed: max |dlogit| {max(e[0] for e in errs.values()):.2e}, "
             f"max |dkv| {max(e[1] for e in errs.values()):.2e}")
 
+    long_res = None
+    if args.long != "off" and not args.no_oracle:
+        long_res = long_context(torch, wsg, shape, w)
+        if args.long == "only":
+            print(json.dumps({"long_context": long_res}), flush=True)
+            return 0
     del w
     stage = STAGES[args.timed_stage]
     model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, stage)
@@ -360,6 +492,7 @@ def main(argv=None):
                         "max_abs_kv_err": max(e[1] for e in errs.values()), "rtol": 1e-3, "atol": 1e-3}
                        if errs else {"status": "skipped"}),
         "graphs": not args.no_graph,
+        "long_context": long_res,
     }
     model.close()
     del model

@@ -218,6 +218,16 @@ wsg_status wsg_gemv_q4g64_ex(int32_t M, int32_t K, int32_t T, int32_t rows_per_w
                              const uint32_t* d_Wq, const void* d_scales, const void* d_X,
                              float* d_Y, void* hip_stream);
 
+/* FP32 GEMM on the matrix cores: C[M][N] = A[M][K] . B[N][K]^T, or C += that
+ * product when accumulate = 1.  Row-major, K-contiguous operands: the batched
+ * projection of chunked prefill, with B a packed weight matrix [out][in]
+ * (Megakernels, "Chunked prefill for long prompts": projections as ordinary
+ * tiled matrix multiplication on the matrix units, FP32 accumulation).
+ * M >= 1 (any), N % 64 == 0, K % 32 == 0; all pointers 16-byte aligned.
+ * Asynchronous on hip_stream. */
+wsg_status wsg_gemm_nt_f32(int32_t M, int32_t N, int32_t K, const float* d_A, const float* d_B, float* d_C,
+                           int32_t accumulate, void* hip_stream);
+
 /* Message for the last error on this host thread ("" if none). */
 const char* wsg_last_error(void);
 

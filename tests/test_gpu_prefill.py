@@ -1,0 +1,133 @@
+"""Chunked prefill vs the oracle, through the C ABI.
+
+The projection GEMM (FP32 MFMA) is checked on its own against the oracle's
+float64 product with a rigorous summation bound, then the chunked prefill of
+whole models in lockstep: every valid K/V entry of every layer after the
+prompt (Benchmark methodology, "Long-document chunked prefill": the whole
+prefix is checked at chunk boundaries), the first token and its logits, then
+decode steps.  Chunk sizes include 1, ragged tails and chunks larger than the
+prompt; a second prefill call must continue the same sequence.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import U32, _np, announce, close_rel, gemv_bound, gpu_available, lockstep
+import oracle
+from synth import MINI, PROMPT_SEEDS, QWEN3_0_6B, model_weights, prompt_ids
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 32), (37, 128, 64), (65, 192, 96), (130, 4096, 1024),
+                                   (1024, 4096, 1024), (500, 1024, 2048), (257, 6144, 1024),
+                                   (1024, 1024, 3072), (2048, 4096, 1024)])
+@pytest.mark.parametrize("acc", [0, 1])
+def test_gemm_nt_f32(M, N, K, acc):
+    import torch
+    import weight_streaming_gemv_amd as wsg
+    rng = np.random.default_rng(M * 7 + N + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    C0 = rng.standard_normal((M, N)).astype(np.float32)
+    announce(f"gemm_nt M={M} N={N} K={K} acc={acc}")
+    Cd = torch.from_numpy(C0.copy()).cuda()
+    wsg.gemm_nt(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), Cd, accumulate=bool(acc))
+    torch.cuda.synchronize()
+    got = Cd.cpu().numpy().astype(np.float64)
+    prod = oracle.gemv(B, A).astype(np.float64)          # A @ B^T
+    bound = gemv_bound(oracle.gemv(np.abs(B), np.abs(A)).astype(np.float64), K)
+    ref = prod + (C0 if acc else 0.0)
+    bound = bound + (U32 * np.abs(ref) if acc else 0.0) + 1e-30
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"max err {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
+
+
+def test_gemm_rejects_bad_shapes():
+    import torch
+    import weight_streaming_gemv_amd as wsg
+    a = torch.zeros((4, 48), device="cuda")
+    b = torch.zeros((64, 48), device="cuda")
+    with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+        wsg.gemm_nt(a, b)          # K % 32 != 0
+    with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+        wsg.gemm_nt(torch.zeros((4, 64), device="cuda"), torch.zeros((48, 64), device="cuda"))
+
+
+@pytest.fixture(scope="module")
+def mini_w():
+    return model_weights(MINI, seed=0)
+
+
+@pytest.mark.parametrize("n_prompt,chunk", [(2, 1), (17, 16), (64, 16), (65, 64), (130, 32), (300, 64),
+                                            (300, 7), (20, 64)])
+def test_mini_chunked_prefill(mini_w, n_prompt, chunk):
+    import weight_streaming_gemv_amd as wsg
+    cap = 320
+    m = wsg.Model(MINI, mini_w, max_context=cap, prefill_chunk=64)
+    m.set_prefill_chunk(chunk)
+    orc = oracle.OracleModel(MINI, mini_w, cap)
+    prompt = prompt_ids(11, n_prompt, MINI.vocab)
+    lockstep(m, orc, prompt, 4, label=f"mini chunked n={n_prompt} c={chunk}")
+    m.close()
+
+
+def test_mini_chunked_matches_tokenwise_and_continues(mini_w):
+    """Chunked and tokenwise prefill agree; a second prefill call continues the sequence."""
+    import weight_streaming_gemv_amd as wsg
+    cap = 200
+    prompt = prompt_ids(12, 150, MINI.vocab)
+    a = wsg.Model(MINI, mini_w, max_context=cap, prefill_chunk=32)
+    b = wsg.Model(MINI, mini_w, max_context=cap)
+    ta = a.prefill(prompt[:100])
+    ta2 = a.prefill(prompt[100:])
+    tb = b.prefill(prompt)
+    assert ta2 == tb
+    orc = oracle.OracleModel(MINI, mini_w, cap)
+    lo = orc.forward_rows(prompt[:100])
+    assert ta == oracle.argmax_lowest(lo)
+    lo = orc.forward_rows(prompt[100:])
+    ok, err, _ = close_rel(_np(a.logits()), lo, 1e-3, 1e-3)
+    assert ok, err
+    for l in range(MINI.n_layers):
+        ka, va, na = a.kv(l)
+        kb, vb, nb = b.kv(l)
+        assert na == nb == 150
+        for g, r in ((ka, orc.k_cache[l]), (va, orc.v_cache[l]), (kb, orc.k_cache[l]), (vb, orc.v_cache[l])):
+            ok, err, _ = close_rel(_np(g[:, :150]), r[:, :150], 1e-3, 1e-3)
+            assert ok, err
+    a.close()
+    b.close()
+
+
+@pytest.fixture(scope="module")
+def c1_w():
+    return model_weights(QWEN3_0_6B.with_layers(2), seed=0)
+
+
+@pytest.mark.parametrize("n_prompt,chunk", [(8, 8), (32, 8), (32, 32), (200, 64), (200, 128)])
+def test_tiny_qwen3_chunked_prefill(c1_w, n_prompt, chunk):
+    import weight_streaming_gemv_amd as wsg
+    sh = QWEN3_0_6B.with_layers(2)
+    cap = 256
+    m = wsg.Model(sh, c1_w, max_context=cap, prefill_chunk=128)
+    m.set_prefill_chunk(chunk)
+    orc = oracle.OracleModel(sh, c1_w, cap)
+    prompt = prompt_ids(PROMPT_SEEDS["short"] if n_prompt <= 32 else 13, n_prompt, sh.vocab)
+    toks, _, ck = lockstep(m, orc, prompt, 4, label=f"qwen3x2 chunked n={n_prompt} c={chunk}")
+    print(f"n={n_prompt} c={chunk}: max |dlogit| {ck.max_logit_err:.2e} max |dkv| {ck.max_kv_err:.2e}")
+    m.close()
+
+
+def test_chunked_prefill_config_checks(c1_w):
+    import weight_streaming_gemv_amd as wsg
+    sh = QWEN3_0_6B.with_layers(2)
+    m = wsg.Model(sh, c1_w, max_context=16, prefill_chunk=8)
+    with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+        m.set_prefill_chunk(9)
+    with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+        m.set_prefill_chunk(0)
+    m.close()
+    w16 = {"embed": c1_w["embed"].astype(np.float16), "final_norm": c1_w["final_norm"].astype(np.float16),
+           "layers": [{k: v.astype(np.float16) for k, v in lw.items()} for lw in c1_w["layers"]]}
+    with pytest.raises(wsg.WsgError, match="UNSUPPORTED"):
+        wsg.Model(sh, w16, max_context=16, dtype=wsg.WSG_F16, prefill_chunk=8)

@@ -18,7 +18,7 @@ from ._abi import (WSG_F16, WSG_F32, WSG_GEMV_NONTEMPORAL, WSG_OPT_TIMED_STAGE, 
                    WSG_STAGE_ATTN, WSG_STAGE_DOWN, WSG_STAGE_GATEUP, WSG_STAGE_HEAD, WSG_STAGE_O,
                    WSG_STAGE_QKV, WsgError, check, wsg_config, wsg_host_weights)
 
-__all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "WsgError", "WSG_F32", "WSG_F16",
+__all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "gemm_nt", "WsgError", "WSG_F32", "WSG_F16",
            "WSG_STAGE_QKV", "WSG_STAGE_ATTN", "WSG_STAGE_O", "WSG_STAGE_GATEUP", "WSG_STAGE_DOWN",
            "WSG_STAGE_HEAD", "WSG_OPT_USE_GRAPH", "WSG_OPT_TIMED_STAGE", "WSG_GEMV_NONTEMPORAL", "lib"]
 
@@ -64,6 +64,18 @@ def gemv_q4g64(Wq, S, X, rows_per_wave: int = 0, Y=None, stream=None, grid_block
     check(_abi.lib().wsg_gemv_q4g64_ex(M, K, T, rows_per_wave, grid_blocks, flags, Wq.data_ptr(), S.data_ptr(),
                                        X.data_ptr(), Y.data_ptr(), _stream_handle(stream)))
     return Y
+
+
+def gemm_nt(A, B, C=None, accumulate: bool = False, stream=None):
+    """``C[M, N] (+)= A[M, K] @ B[N, K]^T`` on FP32 MFMA (torch FP32 device tensors)."""
+    torch = _torch()
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    check(_abi.lib().wsg_gemm_nt_f32(M, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(), int(accumulate),
+                                     _stream_handle(stream)))
+    return C
 
 
 # ---------------------------------------------------------------- model

@@ -76,6 +76,8 @@ _SIGS = {
                                  C.c_void_p, C.c_void_p, C.c_void_p]),
     "wsg_gemv_q4g64_ex": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "wsg_gemm_nt_f32": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_int32, C.c_void_p]),
     "wsg_last_error": (C.c_char_p, []),
     "wsg_version": (C.c_char_p, []),
 }

@@ -1,7 +1,8 @@
 """Compile the HIP sources into ``libwsg.so`` (in-tree, gfx950).
 
-``python -m weight_streaming_gemv_amd.build`` or ``build()`` from Python.
-Every call recompiles every source (object files go to ``_build/``).
+``python weight_streaming_gemv_amd/build.py`` (a plain script: importing the
+package itself requires the built library).  Every call recompiles every
+source (object files go to ``_build/``).
 """
 from __future__ import annotations
 

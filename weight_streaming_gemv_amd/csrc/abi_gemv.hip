@@ -1,6 +1,7 @@
 // C ABI of the stand-alone GEMV family: argument validation, then launch.
 #include "../../include/wsg.h"
 #include "gemv.hpp"
+#include "prefill.hpp"
 #include "status.hpp"
 
 using namespace wsg;
@@ -62,4 +63,19 @@ extern "C" wsg_status wsg_gemv_q4g64(int32_t M, int32_t K, int32_t T, int32_t ro
                                      const uint32_t* d_Wq, const void* d_scales, const void* d_X, float* d_Y,
                                      void* hip_stream) {
   return wsg_gemv_q4g64_ex(M, K, T, rows_per_wave, 0, 0, d_Wq, d_scales, d_X, d_Y, hip_stream);
+}
+
+extern "C" wsg_status wsg_gemm_nt_f32(int32_t M, int32_t N, int32_t K, const float* d_A, const float* d_B, float* d_C,
+                                     int32_t accumulate, void* hip_stream) {
+  clear_error();
+  if (M < 1 || N < 64 || N % 64 != 0 || K < 32 || K % 32 != 0)
+    return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_nt_f32: need M >= 1, N % 64 == 0, K % 32 == 0 (M=%d N=%d K=%d)", M, N, K);
+  if (accumulate != 0 && accumulate != 1) return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_nt_f32: accumulate must be 0 or 1");
+  if (!d_A || !d_B || !d_C) return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_nt_f32: null pointer");
+  if (((uintptr_t)d_A | (uintptr_t)d_B | (uintptr_t)d_C) & 15)
+    return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_nt_f32: pointers must be 16-byte aligned");
+  (void)hipGetLastError();
+  if (!gemm_nt_f32(d_A, d_B, d_C, M, N, K, accumulate == 1, static_cast<hipStream_t>(hip_stream)))
+    return fail(WSG_ERR_UNSUPPORTED, "wsg_gemm_nt_f32: shape not supported");
+  return check_launch("wsg_gemm_nt_f32");
 }

@@ -9,9 +9,9 @@
 //           registers) + fused Q/K/V GEMV; layer 0 also gathers the token's
 //           embedding row and writes it to the residual buffer
 //   attn    per-head Q/K RMSNorm + RoPE + K/V cache write of position p +
-//           split-K grouped-query attention; the last-arriving split block
-//           of each KV head merges the partial softmax states (an atomic
-//           arrival count, no waiting)
+//           split-K grouped-query attention; with one split the block
+//           writes o itself, otherwise a merge launch combines the partial
+//           softmax states
 //   o       output GEMV + residual add
 //   gateup  post-attention RMSNorm + gate/up GEMV + SwiGLU
 //   down    down GEMV + residual add
@@ -411,7 +411,6 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
                                                  float* __restrict__ part, TS* __restrict__ o) {
   __shared__ float sm_m[16][G], sm_l[16][G];
   __shared__ float sm_acc[16][G][kD];
-  __shared__ int sm_last;
 
   const int j = blockIdx.y;            // KV head
   const int split = blockIdx.x;
@@ -531,33 +530,34 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
       my_part[g * kPartStride + 2 + d] = A;
     }
   }
-  if (n_splits == 1) return;
+}
 
-  // last-arriving split of this KV head merges all partial states
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&ctrl[kCtrlAttnCnt + j], 1);
-    sm_last = (prev == n_splits - 1);
+// Merge of the split-K partial states of one query head (one block per
+// head, thread d = dimension): rescale every split to the common maximum
+// and add.  A separate launch, because a last-arriving-block merge needs a
+// device-scope fence per block, and on this multi-XCD part each such fence
+// writes back the issuing XCD's L2.
+template <typename TS, int G>
+__global__ __launch_bounds__(kD) void k_attn_merge(const float* __restrict__ part, const int32_t* __restrict__ ctrl,
+                                                   int splits, int min_chunk, TS* __restrict__ o) {
+  const int h = blockIdx.x, j = h / G, g = h - j * G, d = threadIdx.x;
+  const int n_keys = ctrl[kCtrlPos] + 1;
+  int chunk = max(min_chunk, ceil_div(n_keys, splits));
+  chunk = (chunk + 15) & ~15;
+  const int n_splits = ceil_div(n_keys, chunk);
+  if (n_splits == 1) return;   // the attention block wrote o itself
+  const float* hp = part + ((size_t)j * splits * G + g) * kPartStride;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, hp[(size_t)sp * G * kPartStride]);
+  float L = 0.f, A = 0.f;
+#pragma unroll 4
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const float* ps = hp + (size_t)sp * G * kPartStride;
+    const float w = exp2f(ps[0] - mx);
+    L = fmaf(ps[1], w, L);
+    A = fmaf(ps[2 + d], w, A);
   }
-  __syncthreads();
-  if (!sm_last) return;
-  __threadfence();
-  const float* head_part = part + (size_t)j * gridDim.x * G * kPartStride;
-  for (int t = threadIdx.x; t < G * kD; t += kBlock) {
-    const int g = t / kD, d = t - g * kD;
-    float mx = -INFINITY;
-    for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, head_part[(size_t)(sp * G + g) * kPartStride]);
-    float L = 0.f, A = 0.f;
-    for (int sp = 0; sp < n_splits; ++sp) {
-      const float* ps = head_part + (size_t)(sp * G + g) * kPartStride;
-      const float w = exp2f(ps[0] - mx);
-      L = fmaf(ps[1], w, L);
-      A = fmaf(ps[2 + d], w, A);
-    }
-    o[(size_t)(j * G + g) * kD + d] = Store<TS>::from_f(A / L);
-  }
-  if (threadIdx.x == 0) ctrl[kCtrlAttnCnt + j] = 0;
+  o[(size_t)h * kD + d] = Store<TS>::from_f(A / L);
 }
 
 // --------------------------------------------------------------- dispatch
@@ -672,6 +672,22 @@ bool attn_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipS
   }
 }
 
+template <typename TS>
+bool attn_merge_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
+  const int G = a.n_q / a.n_kv;
+  auto go = [&](auto gc) {
+    hipLaunchKernelGGL((k_attn_merge<TS, decltype(gc)::value>), dim3(a.n_q), dim3(kD), 0, s, a.attn_part, a.ctrl,
+                       sh.attn_splits, sh.attn_min_chunk, (TS*)a.o);
+    return true;
+  };
+  switch (G) {
+    case 1: return go(IC<1>{});
+    case 2: return go(IC<2>{});
+    case 4: return go(IC<4>{});
+    default: return false;
+  }
+}
+
 }  // namespace
 
 int head_blocks(const DecodeArgs& a, const DecodeShape& sh) { return head_grid(a.vocab, sh.rows_head, sh.grid_head); }
@@ -681,6 +697,9 @@ bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, 
 }
 bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   return a.dtype == 0 ? attn_t<float>(a, sh, L, s) : attn_t<__half>(a, sh, L, s);
+}
+bool launch_attn_merge(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
+  return a.dtype == 0 ? attn_merge_t<float>(a, sh, s) : attn_merge_t<__half>(a, sh, s);
 }
 bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   const int K = a.n_q * a.head_dim;

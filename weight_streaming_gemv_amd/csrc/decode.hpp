@@ -10,8 +10,7 @@ namespace wsg {
 enum CtrlWord : int {
   kCtrlPos = 0,          // current position p (tokens already in the cache)
   kCtrlOutTok = 1,       // last greedy token
-  kCtrlAttnCnt = 128,    // [n_kv <= 256] arrival counters of the split-K attention merge
-  kCtrlWords = 384
+  kCtrlWords = 64
 };
 
 // The head kernel runs at most kHeadMaxBlocks blocks (one argmax key each).
@@ -62,6 +61,8 @@ struct DecodeShape {
 // Stage launches; each returns false if the shape is not compiled in.
 bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first_layer, hipStream_t s);
 bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
+// Combines the split-K partial states (needed when sh.attn_splits > 1).
+bool launch_attn_merge(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s);
 bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
 bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
 bool launch_down(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool advance_pos, hipStream_t s);

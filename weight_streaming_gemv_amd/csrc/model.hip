@@ -61,6 +61,8 @@ wsg_status validate_config(const wsg_config* c) {
     return fail(WSG_ERR_UNSUPPORTED, "hidden/intermediate/query width must be in {512,1024,2048,3072}%s",
                 c->dtype == WSG_F32 ? " or 256" : "");
   if ((int64_t)c->max_context > (1 << 20)) return fail(WSG_ERR_UNSUPPORTED, "max_context too large");
+  if (c->prefill_chunk > 0 && (c->dtype != WSG_F32 || G > 2))
+    return fail(WSG_ERR_UNSUPPORTED, "chunked prefill needs FP32 storage and a query group of 1 or 2");
   return WSG_OK;
 }
 
@@ -220,7 +222,10 @@ bool enqueue_body(wsg_model* m, int splits, bool advance) {
   for (int l = 0; l < L; ++l) {
     const LayerPtrs& lp = m->layers[l];
     if (!timed(m, WSG_STAGE_QKV, [&] { return launch_qkv(m->args, sh, lp, l == 0, s); })) return false;
-    if (!timed(m, WSG_STAGE_ATTN, [&] { return launch_attn(m->args, sh, lp, s); })) return false;
+    if (!timed(m, WSG_STAGE_ATTN, [&] {
+          return launch_attn(m->args, sh, lp, s) && (splits == 1 || launch_attn_merge(m->args, sh, s));
+        }))
+      return false;
     if (!timed(m, WSG_STAGE_O, [&] { return launch_o(m->args, sh, lp, s); })) return false;
     if (!timed(m, WSG_STAGE_GATEUP, [&] { return launch_gateup(m->args, sh, lp, s); })) return false;
     if (!timed(m, WSG_STAGE_DOWN, [&] { return launch_down(m->args, sh, lp, advance && l == L - 1, s); }))
