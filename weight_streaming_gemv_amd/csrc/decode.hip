@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
                                                  TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
                                                  const TS* __restrict__ k_norm, const float* __restrict__ rope_cos,
                                                  const float* __restrict__ rope_sin, int32_t* __restrict__ ctrl,
-                                                 int n_q, int n_kv, int cap, float eps, int min_chunk,
+                                                 int n_q, int n_kv, int cap, float eps, int chunk,
                                                  float* __restrict__ part, TS* __restrict__ o) {
   __shared__ float sm_m[16][G], sm_l[16][G];
   __shared__ float sm_acc[16][G][kD];
@@ -420,46 +420,41 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
   const int Q = n_q * kD, KV = n_kv * kD;
   const size_t head_off = (size_t)j * cap * kD;
 
-  // Loads that do not depend on the position go first: raw queries, the
-  // current token's key and value, the norm gains, and (split 0 always
-  // starts at key 0) this row's first cached key.
-  float q[G][8], kc[8], vc[8], gq[8], gk[8], kk[8], vv[8];
+  // Every split covers the fixed key range [split*chunk, split*chunk + chunk)
+  // (chunk is a per-model constant), so the loads that do not depend on the
+  // position go first: raw queries, the current token's key and value, and
+  // this row's first four cached keys (clamped into the cache; keys past the
+  // position are loaded but never used).
+  const int k_begin = split * chunk;
+  float q[G][8], kc[8], vc[8], k4[4][8], v4[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int kk = min(k_begin + sid + 16 * u, cap - 1);
+    load_head8<TS>(k_cache + head_off + (size_t)kk * kD, sl, k4[u]);
+    load_head8<TS>(v_cache + head_off + (size_t)kk * kD, sl, v4[u]);
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) load_head8<TS>(qkv + (size_t)(j * G + g) * kD, sl, q[g]);
   load_head8<TS>(qkv + Q + (size_t)j * kD, sl, kc);
   load_head8<TS>(qkv + Q + KV + (size_t)j * kD, sl, vc);
-  load_head8<TS>(q_norm, sl, gq);
-  load_head8<TS>(k_norm, sl, gk);
-  const bool spec = (split == 0);
-  if (spec) {
-    const int key0 = min(sid, cap - 1);
-    load_head8<TS>(k_cache + head_off + (size_t)key0 * kD, sl, kk);
-    load_head8<TS>(v_cache + head_off + (size_t)key0 * kD, sl, vv);
-  }
 
   const int pos = ctrl[kCtrlPos];
   const int n_keys = pos + 1;
-  int chunk = max(min_chunk, ceil_div(n_keys, (int)gridDim.x));
-  chunk = (chunk + 15) & ~15;
   const int n_splits = ceil_div(n_keys, chunk);
   if (split >= n_splits) return;
-  const int k_begin = split * chunk;
   const int k_end = min(n_keys, k_begin + chunk);
   const bool has_cur = (k_end == n_keys);
   const int k_stop = has_cur ? k_end - 1 : k_end;   // cached keys [k_begin, k_stop)
 
-  float c[4], s[4];
+  float c[4], s[4], gq[8], gk[8];
   {
     const float4 cv = *reinterpret_cast<const float4*>(rope_cos + (size_t)pos * (kD / 2) + 4 * sl);
     const float4 sv = *reinterpret_cast<const float4*>(rope_sin + (size_t)pos * (kD / 2) + 4 * sl);
     c[0] = cv.x; c[1] = cv.y; c[2] = cv.z; c[3] = cv.w;
     s[0] = sv.x; s[1] = sv.y; s[2] = sv.z; s[3] = sv.w;
   }
-  int key = k_begin + sid;
-  if (!spec && key < k_stop) {
-    load_head8<TS>(k_cache + head_off + (size_t)key * kD, sl, kk);
-    load_head8<TS>(v_cache + head_off + (size_t)key * kD, sl, vv);
-  }
+  load_head8<TS>(q_norm, sl, gq);
+  load_head8<TS>(k_norm, sl, gk);
   // queries: normalised, rotated, rounded as stored, then pre-scaled by
   // log2(e)/sqrt(D) so that scores are in the log2 domain
   const float qscale = kLog2e / sqrtf((float)kD);
@@ -473,19 +468,21 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
 
   SoftState<G> st;
   st.init();
-  // each row walks keys sid, sid+16, ...; the next key's loads are issued
-  // before the current key is folded in
-  while (key < k_stop) {
-    const int nkey = key + 16;
-    float nk[8], nv[8];
-    if (nkey < k_stop) {
-      load_head8<TS>(k_cache + head_off + (size_t)nkey * kD, sl, nk);
-      load_head8<TS>(v_cache + head_off + (size_t)nkey * kD, sl, nv);
-    }
-    st.add(q, kk, vv);
+  // row keys k_begin + sid + 16u: the first four are in registers already;
+  // longer chunks continue in groups of four with all loads in flight first
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { kk[i] = nk[i]; vv[i] = nv[i]; }
-    key = nkey;
+  for (int u = 0; u < 4; ++u)
+    if (k_begin + sid + 16 * u < k_stop) st.add(q, k4[u], v4[u]);
+  for (int key = k_begin + sid + 64; key < k_stop; key += 64) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (key + 16 * u < k_stop) {
+        load_head8<TS>(k_cache + head_off + (size_t)(key + 16 * u) * kD, sl, k4[u]);
+        load_head8<TS>(v_cache + head_off + (size_t)(key + 16 * u) * kD, sl, v4[u]);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (key + 16 * u < k_stop) st.add(q, k4[u], v4[u]);
   }
   if (has_cur) {
     // the current token's key and value: normalise/rotate, write slot p,
@@ -532,32 +529,52 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
   }
 }
 
-// Merge of the split-K partial states of one query head (one block per
-// head, thread d = dimension): rescale every split to the common maximum
-// and add.  A separate launch, because a last-arriving-block merge needs a
+// Merge of the split-K partial states of one query head (one block of 256
+// threads per head): the split maxima and sums are loaded in parallel, the
+// per-split weights exp2(m_s - max) are kept in LDS, and each output dim
+// sums its weighted partials with the loads of two halves of the splits in
+// flight.  A separate launch, because a last-arriving-block merge needs a
 // device-scope fence per block, and on this multi-XCD part each such fence
 // writes back the issuing XCD's L2.
+constexpr int kMaxSplits = 128;
+
 template <typename TS, int G>
-__global__ __launch_bounds__(kD) void k_attn_merge(const float* __restrict__ part, const int32_t* __restrict__ ctrl,
-                                                   int splits, int min_chunk, TS* __restrict__ o) {
-  const int h = blockIdx.x, j = h / G, g = h - j * G, d = threadIdx.x;
+__global__ __launch_bounds__(kBlock) void k_attn_merge(const float* __restrict__ part,
+                                                       const int32_t* __restrict__ ctrl, int splits, int chunk,
+                                                       TS* __restrict__ o) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[kWavesPerBlock];
+  __shared__ float s_a[2][kD];
+  const int h = blockIdx.x, j = h / G, g = h - j * G, tid = threadIdx.x;
   const int n_keys = ctrl[kCtrlPos] + 1;
-  int chunk = max(min_chunk, ceil_div(n_keys, splits));
-  chunk = (chunk + 15) & ~15;
   const int n_splits = ceil_div(n_keys, chunk);
   if (n_splits == 1) return;   // the attention block wrote o itself
   const float* hp = part + ((size_t)j * splits * G + g) * kPartStride;
-  float mx = -INFINITY;
-  for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, hp[(size_t)sp * G * kPartStride]);
-  float L = 0.f, A = 0.f;
-#pragma unroll 4
-  for (int sp = 0; sp < n_splits; ++sp) {
-    const float* ps = hp + (size_t)sp * G * kPartStride;
-    const float w = exp2f(ps[0] - mx);
-    L = fmaf(ps[1], w, L);
-    A = fmaf(ps[2 + d], w, A);
-  }
-  o[(size_t)h * kD + d] = Store<TS>::from_f(A / L);
+  const size_t sstride = (size_t)G * kPartStride;
+  // split statistics: thread sp < n_splits (n_splits <= kMaxSplits)
+  const float m_s = tid < n_splits ? hp[tid * sstride] : -INFINITY;
+  const float l_s = tid < n_splits ? hp[tid * sstride + 1] : 0.f;
+  float mx = m_s;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane_id() == 0) s_red[wave_id()] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float w = tid < n_splits ? exp2f(m_s - mx) : 0.f;
+  if (tid < kMaxSplits) s_w[tid] = w;
+  float L = wave_sum(l_s * w);
+  __syncthreads();
+  if (lane_id() == 0) s_red[wave_id()] = L;
+  __syncthreads();
+  L = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  // weighted partial outputs: thread (half, d) sums splits half, half+2, ...
+  const int d = tid & (kD - 1), half = tid >> 7;
+  float A = 0.f;
+#pragma unroll 8
+  for (int sp = half; sp < n_splits; sp += 2) A = fmaf(s_w[sp], hp[sp * sstride + 2 + d], A);
+  s_a[half][d] = A;
+  __syncthreads();
+  if (tid < kD) o[(size_t)h * kD + tid] = Store<TS>::from_f((s_a[0][tid] + s_a[1][tid]) / L);
 }
 
 // --------------------------------------------------------------- dispatch
@@ -661,7 +678,7 @@ bool attn_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipS
   auto go = [&](auto gc) {
     hipLaunchKernelGGL((k_attn<TS, decltype(gc)::value>), grid, dim3(kBlock), 0, s, (const TS*)a.qkv,
                        (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm, a.rope_cos,
-                       a.rope_sin, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, sh.attn_min_chunk, a.attn_part, (TS*)a.o);
+                       a.rope_sin, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, sh.attn_chunk, a.attn_part, (TS*)a.o);
     return true;
   };
   switch (G) {
@@ -676,8 +693,8 @@ template <typename TS>
 bool attn_merge_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
   auto go = [&](auto gc) {
-    hipLaunchKernelGGL((k_attn_merge<TS, decltype(gc)::value>), dim3(a.n_q), dim3(kD), 0, s, a.attn_part, a.ctrl,
-                       sh.attn_splits, sh.attn_min_chunk, (TS*)a.o);
+    hipLaunchKernelGGL((k_attn_merge<TS, decltype(gc)::value>), dim3(a.n_q), dim3(kBlock), 0, s, a.attn_part, a.ctrl,
+                       sh.attn_splits, sh.attn_chunk, (TS*)a.o);
     return true;
   };
   switch (G) {

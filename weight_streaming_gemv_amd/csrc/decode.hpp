@@ -55,7 +55,7 @@ struct DecodeShape {
   int rows_qkv, rows_o, rows_gu, rows_down, rows_head;   // rows per wave
   int grid_qkv, grid_o, grid_gu, grid_down, grid_head;   // blocks (0 = one row group per wave)
   int attn_splits;                                       // split-K blocks per KV head (grid.x)
-  int attn_min_chunk;                                    // fewest keys per split
+  int attn_chunk;                                        // keys per split (a multiple of 16, >= 64)
 };
 
 // Stage launches; each returns false if the shape is not compiled in.

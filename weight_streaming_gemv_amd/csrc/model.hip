@@ -95,11 +95,21 @@ PackedLayout packed_layout(const Dims& d) {
   return p;
 }
 
-constexpr int kMinAttnChunk = 64;
+// Decode attention splits the keys into fixed ranges of attn_chunk(d)
+// keys (at least 64, and at most 128 splits for the whole capacity), so a
+// block's key range does not depend on the position.
+constexpr int kMaxAttnSplits = 128;
+
+int attn_chunk(const Dims& d) {
+  int c = (d.cap + kMaxAttnSplits - 1) / kMaxAttnSplits;
+  c = (c + 15) & ~15;
+  return c < 64 ? 64 : c;
+}
 
 int attn_split_cap(const Dims& d) {
+  const int need = (d.cap + attn_chunk(d) - 1) / attn_chunk(d);
   int s = 1;
-  while (s < 128 && (int64_t)s * kMinAttnChunk < d.cap) s <<= 1;
+  while (s < need) s <<= 1;
   return s;
 }
 
@@ -238,7 +248,7 @@ bool enqueue_head(wsg_model* m) { return launch_head(m->args, m->shape, m->strea
 bool enqueue_argmax(wsg_model* m) { return launch_argmax(m->args, m->shape, m->stream); }
 
 int splits_for(const wsg_model* m, int n_keys) {
-  const int want = pow2_ceil((n_keys + kMinAttnChunk - 1) / kMinAttnChunk);
+  const int want = pow2_ceil((n_keys + m->shape.attn_chunk - 1) / m->shape.attn_chunk);
   return want < m->wl.attn_splits_cap ? want : m->wl.attn_splits_cap;
 }
 
@@ -474,7 +484,7 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   sh.grid_qkv = sh.grid_o = sh.grid_gu = sh.grid_down = 0;
   sh.grid_head = 4096;
   sh.attn_splits = 1;
-  sh.attn_min_chunk = kMinAttnChunk;
+  sh.attn_chunk = attn_chunk(d);
 
   std::vector<float> cs, sn;
   fill_rope(*cfg, cs, sn);
