@@ -36,6 +36,25 @@ STAGE_KERNEL = {"qkv": "k_qkv", "attn": "k_attn", "o": "k_gemv_residual", "gateu
                 "down": "k_gemv_residual", "head": "k_head"}
 
 
+# HBM bytes per launch of the roofline kernel from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs, scaled by a plain-copy calibration (FETCH x 2.0, WRITE x
+# 1.0); valid only for the kernel source they were measured on.
+HEAD_TRAFFIC = {"bytes": 624_127_000, "k_head_sha256_16": "1275e0bbece696c0"}
+
+
+def head_traffic():
+    """Recorded traffic of k_head, or None if the kernel source has changed since."""
+    import hashlib
+    import re
+    try:
+        src = open(os.path.join(ROOT, "weight_streaming_gemv_amd", "csrc", "decode.hip")).read()
+        m = re.search(r"__global__ __launch_bounds__\(kBlock\) void k_head\(.*?\n}\n", src, re.S)
+        h = hashlib.sha256(m.group(0).encode()).hexdigest()[:16] if m else None
+    except OSError:
+        h = None
+    return HEAD_TRAFFIC["bytes"] if h == HEAD_TRAFFIC["k_head_sha256_16"] else None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -364,6 +383,8 @@ def main(argv=None):
     ap.add_argument("--sweep", choices=["full", "quick", "none"], default="full",
                     help="cold-cache GEMV sweep after the decode timing")
     ap.add_argument("--sweep-only", action="store_true", help="run only the cold-cache GEMV sweep")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 512 MiB device copy (reference for the HBM traffic counters)")
     ap.add_argument("--long", choices=["on", "off", "only"], default="on",
                     help="long-document workload (2048-id chunk selection, 4096 -> 1024 held-out)")
     ap.add_argument("--no-oracle", action="store_true",
@@ -383,6 +404,17 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        # a plain device copy of known size, for scaling the FETCH_SIZE /
+        # WRITE_SIZE counters of the profiled kernels
+        n = 1 << 27                                   # 128 Mi floats = 512 MiB each way
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4}), flush=True)
+        return 0
     if args.sweep_only:
         sw = gemv_sweep(quick=args.sweep == "quick")
         best, agg = sweep_summary(sw)
@@ -484,7 +516,8 @@ def main(argv=None):
         "per_combo_median": per_combo,
         "roofline": {"bound": "hbm", "kernel": STAGE_KERNEL[args.timed_stage],
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None, "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
+                     "traffic": head_traffic() if args.timed_stage == "head" else None,
                      "bytes_per_launch": st_bytes // max(st_n, 1), "avg_launch_us": round(avg_launch_ms * 1e3, 3),
                      "launches_timed": st_n},
         "cpu_baseline": cpu,
