@@ -165,6 +165,15 @@ wsg_status wsg_set_prefill_chunk(wsg_model* m, int32_t rows);
  * to short kernels.
  * Errors: WSG_ERR_UNSUPPORTED for a per-layer stage while graphs are on. */
 enum { WSG_OPT_USE_GRAPH = 1, WSG_OPT_TIMED_STAGE = 2 };
+/* WSG_OPT_FUSE_ATTN_O: 1 (default) = while the context fits one attention
+ * split, each layer runs attention and the output projection as one launch
+ * (the projection split by KV head into FP32 partials that the gate/up
+ * launch sums in a fixed order); that launch is timed as WSG_STAGE_ATTN and
+ * counts the output-projection weight bytes.  0 = separate attention and
+ * output-projection launches at every context length.
+ * WSG_OPT_ROWS_ATTN_O: output-projection rows per wave in the fused launch
+ * (4 or 8, default 8). */
+enum { WSG_OPT_FUSE_ATTN_O = 3, WSG_OPT_ROWS_ATTN_O = 15 };
 /* Launch shape of the decode GEMV stages (tuning): rows per wave (1, 2 or
  * 4) and blocks of 256 threads (0 = one row group per wave; fewer blocks
  * loop over row groups; the head is capped at 4096 blocks).  Defaults:

@@ -11,7 +11,7 @@ import pytest
 
 from gpu_util import _np, announce, gpu_available, lockstep
 import oracle
-from synth import MINI, PROMPT_SEEDS, QWEN3_0_6B, model_weights, prompt_ids
+from synth import MINI, PROMPT_SEEDS, QWEN3_0_6B, ModelShape, model_weights, prompt_ids
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -32,6 +32,33 @@ def test_mini_fp32_generation_graph_and_direct(mini_w):
     toks2, _, _ = lockstep(m, orc, prompt, 8, label="mini direct")
     assert toks2 == toks
     assert np.array_equal(_np(m.logits()), logits_graph)   # same kernels, same bits
+    m.close()
+
+
+@pytest.mark.parametrize("fuse,rows", [(0, 8), (1, 8), (1, 4)])
+def test_mini_fused_attention_output(mini_w, fuse, rows):
+    """Attention fused with the output projection (KV-head partials summed by
+    the gate/up launch) and the separate launches both match the oracle, and
+    give the same tokens; contexts cross the one-split limit (64 keys)."""
+    import weight_streaming_gemv_amd as wsg
+    cap = 96
+    m = wsg.Model(MINI, mini_w, max_context=cap)
+    m.set_option(wsg._abi.WSG_OPT_FUSE_ATTN_O, fuse)
+    m.set_option(wsg._abi.WSG_OPT_ROWS_ATTN_O, rows)
+    orc = oracle.OracleModel(MINI, mini_w, cap)
+    prompt = prompt_ids(21, 58, MINI.vocab)
+    toks, _, ck = lockstep(m, orc, prompt, 12, label=f"mini fuse={fuse} rows={rows}")
+    print(f"fuse={fuse} rows={rows}: max |dlogit| {ck.max_logit_err:.2e}")
+    m.close()
+
+
+def test_fused_option_checks(mini_w):
+    import weight_streaming_gemv_amd as wsg
+    m = wsg.Model(MINI, mini_w, max_context=8)
+    for opt, bad in ((wsg._abi.WSG_OPT_FUSE_ATTN_O, 2), (wsg._abi.WSG_OPT_ROWS_ATTN_O, 2),
+                     (wsg._abi.WSG_OPT_ROWS_ATTN_O, 16)):
+        with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+            m.set_option(opt, bad)
     m.close()
 
 
@@ -60,6 +87,19 @@ def test_mini_split_attention_long_prompt(mini_w, n_prompt):
     orc = oracle.OracleModel(MINI, mini_w, cap)
     prompt = prompt_ids(9, n_prompt, MINI.vocab)
     lockstep(m, orc, prompt, 6, label=f"mini split n={n_prompt}")
+    m.close()
+
+
+@pytest.mark.parametrize("n_prompt", [600, 1000])
+def test_mini_many_splits(mini_w, n_prompt):
+    """More than 8 attention splits (split counts rounded to multiples of 8,
+    so some blocks find no keys), reached through chunked prefill."""
+    import weight_streaming_gemv_amd as wsg
+    cap = 1100
+    m = wsg.Model(MINI, mini_w, max_context=cap, prefill_chunk=128)
+    orc = oracle.OracleModel(MINI, mini_w, cap)
+    prompt = prompt_ids(10, n_prompt, MINI.vocab)
+    lockstep(m, orc, prompt, 5, label=f"mini splits n={n_prompt}")
     m.close()
 
 
@@ -116,4 +156,38 @@ def test_tiny_qwen3_fp16_teacher_forced(c1_w):
     prompt = prompt_ids(PROMPT_SEEDS["tiny"], 8, sh.vocab)
     _, _, ck = lockstep(m, orc, prompt, 8, rtol=2e-2, atol=2e-2, teacher=True, label="qwen3x2 fp16")
     print(f"fp16 max |dlogit| {ck.max_logit_err:.2e}; max |dkv| {ck.max_kv_err:.2e}")
+    m.close()
+
+
+# Query-group sizes 1, 2 and 4 and other widths (each fused row-slice
+# reduction shape: 16, 32, 64 and 128 lanes per output row).
+VARIANTS = {
+    "g1_h512": ModelShape(n_layers=2, hidden=512, intermediate=1024, n_q_heads=4, n_kv_heads=4,
+                          head_dim=128, vocab=777),
+    "g4_h1024": ModelShape(n_layers=2, hidden=1024, intermediate=2048, n_q_heads=8, n_kv_heads=2,
+                           head_dim=128, vocab=1500),
+    "g1_h2048": ModelShape(n_layers=1, hidden=2048, intermediate=1024, n_q_heads=16, n_kv_heads=16,
+                           head_dim=128, vocab=640),
+    "g4_h3072": ModelShape(n_layers=1, hidden=3072, intermediate=3072, n_q_heads=24, n_kv_heads=6,
+                           head_dim=128, vocab=999),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VARIANTS))
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_shape_variants(name, dtype):
+    import weight_streaming_gemv_amd as wsg
+    sh = VARIANTS[name]
+    w = model_weights(sh, seed=5)
+    if dtype == "f16":
+        w = {"embed": w["embed"].astype(np.float16), "final_norm": w["final_norm"].astype(np.float16),
+             "layers": [{k: v.astype(np.float16) for k, v in lw.items()} for lw in w["layers"]]}
+    cap = 80
+    m = wsg.Model(sh, w, max_context=cap, dtype=wsg.WSG_F32 if dtype == "f32" else wsg.WSG_F16)
+    orc = oracle.OracleModel(sh, w, cap)
+    prompt = prompt_ids(31, 60, sh.vocab)
+    tol = 1e-3 if dtype == "f32" else 2e-2
+    _, _, ck = lockstep(m, orc, prompt, 8, rtol=tol, atol=tol, teacher=(dtype == "f16"),
+                        label=f"{name} {dtype}")
+    print(f"{name} {dtype}: max |dlogit| {ck.max_logit_err:.2e} max |dkv| {ck.max_kv_err:.2e}")
     m.close()

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libwsg.so")
 WSG_OK, WSG_ERR_INVALID_ARG, WSG_ERR_OUT_OF_RANGE, WSG_ERR_STATE, WSG_ERR_HIP, WSG_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 WSG_F32, WSG_F16 = 0, 1
 WSG_OPT_USE_GRAPH, WSG_OPT_TIMED_STAGE = 1, 2
+WSG_OPT_FUSE_ATTN_O, WSG_OPT_ROWS_ATTN_O = 3, 15
 WSG_OPT_ROWS = {"qkv": 10, "o": 11, "gateup": 12, "down": 13, "head": 14}
 WSG_OPT_GRID = {"qkv": 20, "o": 21, "gateup": 22, "down": 23, "head": 24}
 WSG_STAGE_QKV, WSG_STAGE_ATTN, WSG_STAGE_O, WSG_STAGE_GATEUP, WSG_STAGE_DOWN, WSG_STAGE_HEAD = range(6)

@@ -69,7 +69,7 @@ extern "C" wsg_status wsg_gemm_nt_f32(int32_t M, int32_t N, int32_t K, const flo
                                      int32_t accumulate, void* hip_stream) {
   clear_error();
   if (M < 1 || N < 64 || N % 64 != 0 || K < 32 || K % 32 != 0)
-    return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_nt_f32: need M >= 1, N % 64 == 0, K % 32 == 0 (M=%d N=%d K=%d)", M, N, K);
+    return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_nt_f32: need M >= 1, N %% 64 == 0, K %% 32 == 0 (M=%d N=%d K=%d)", M, N, K);
   if (accumulate != 0 && accumulate != 1) return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_nt_f32: accumulate must be 0 or 1");
   if (!d_A || !d_B || !d_C) return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_nt_f32: null pointer");
   if (((uintptr_t)d_A | (uintptr_t)d_B | (uintptr_t)d_C) & 15)

@@ -8,12 +8,15 @@
 //   qkv     input RMSNorm (each wave normalises the 1024-float residual in
 //           registers) + fused Q/K/V GEMV; layer 0 also gathers the token's
 //           embedding row and writes it to the residual buffer
-//   attn    per-head Q/K RMSNorm + RoPE + K/V cache write of position p +
-//           split-K grouped-query attention; with one split the block
-//           writes o itself, otherwise a merge launch combines the partial
-//           softmax states
-//   o       output GEMV + residual add
-//   gateup  post-attention RMSNorm + gate/up GEMV + SwiGLU
+//   attn_o  (contexts that fit one attention split) per-head Q/K RMSNorm +
+//           RoPE + K/V cache write + grouped-query attention, fused with the
+//           output GEMV split by KV head: per-head partial sums, the first
+//           one carrying the residual
+//   attn    (longer contexts) the same attention, split-K over the keys;
+//           a merge launch combines the partial softmax states
+//   o       (longer contexts) output GEMV + residual add
+//   gateup  [sum of the attn_o partials +] post-attention RMSNorm + gate/up
+//           GEMV + SwiGLU
 //   down    down GEMV + residual add
 //   head    final RMSNorm + tied vocabulary GEMV + per-block argmax keys
 //   argmax  one block reduces the block keys; writes the token into the
@@ -33,7 +36,7 @@ namespace {
 constexpr int kD = 128;          // head_dim
 constexpr float kLog2e = 1.4426950408889634f;
 
-__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ __forceinline__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Activations of length K in the lane layout the GEMV rows use:
 // a[c*VEC + i] = x[c*64*VEC + lane*VEC + i].
@@ -53,6 +56,14 @@ struct Act {
 #pragma unroll
       for (int i = 0; i < VEC; ++i) a[c * VEC + i] = v.v[i];
     }
+  }
+  // From an FP32 array in the same element order (e.g. in LDS).
+  __device__ __forceinline__ void load_f32(const float* p) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) a[c * VEC + i] = p[c * kWave * VEC + lane * VEC + i];
   }
   __device__ __forceinline__ void store(TS* p) const {
     const int lane = lane_id();
@@ -127,25 +138,52 @@ __device__ __forceinline__ void rows_dot(const TS* __restrict__ W, int row0, int
 __device__ __forceinline__ int wave_row_groups_begin() { return blockIdx.x * kWavesPerBlock + wave_id(); }
 __device__ __forceinline__ int wave_row_groups_stride() { return gridDim.x * kWavesPerBlock; }
 
+// Lane r's value of v (r wave-uniform).
+__device__ __forceinline__ float lane_value(float v, int r) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), r));
+}
+
+// Lane r < R gets base[row0 + r] (rows clamped to M-1): residual values put
+// in flight with the operands instead of being loaded after the dot.
+template <typename TS, int R>
+__device__ __forceinline__ float rows_prefetch(const TS* __restrict__ base, int row0, int M) {
+  const int lane = lane_id();
+  return Store<TS>::to_f(base[min(row0 + (lane < R ? lane : R - 1), M - 1)]);
+}
+
 // ------------------------------------------------------------------ qkv
 template <typename TS, int H, int R>
 __global__ __launch_bounds__(kBlock) void k_qkv(const TS* __restrict__ W, const TS* __restrict__ in_norm,
                                                 TS* __restrict__ x_res, const TS* __restrict__ embed,
                                                 const int32_t* __restrict__ ids, const int32_t* __restrict__ ctrl,
-                                                int first_layer, int vocab, float eps, TS* __restrict__ out,
-                                                int M) {
+                                                const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
+                                                float* __restrict__ rope_cur, int first_layer, int vocab, float eps,
+                                                TS* __restrict__ out, int M) {
   const int ngroups = ceil_div(M, R);
   int g = wave_row_groups_begin();
   WRows<TS, H, R> w;
-  if (g < ngroups) w.load(W, g * R, M);   // first rows in flight before the prologue
   Act<TS, H> x;
+  // Vector loads return in issue order: the residual goes out before the
+  // first weight rows (so the norm overlaps them); at layer 0 the
+  // position -> id -> embedding chain is issued after them.
+  if (!first_layer) x.load(x_res);
+  __builtin_amdgcn_sched_barrier(0);
+  w.load(W, g * R, M);   // rows clamped into W: no branch around the loads
+  __builtin_amdgcn_sched_barrier(0);
   if (first_layer) {
-    int tok = ids[ctrl[kCtrlPos]];
+    const int pos = ctrl[kCtrlPos];
+    int tok = ids[pos];
     tok = (tok < 0 || tok >= vocab) ? 0 : tok;   // ids are validated on the host; never read outside E
     x.load(embed + (size_t)tok * H);
     if (blockIdx.x == 0 && wave_id() == 0) x.store(x_res);
-  } else {
-    x.load(x_res);
+    if (blockIdx.x == 0 && wave_id() == 1) {
+      // the rotary row of position p, for every attention launch of this
+      // token (their loads then do not wait for the position)
+      static_assert(kD / 2 == kWave, "one rotary pair per lane");
+      const int lane = lane_id();
+      rope_cur[lane] = rope_cos[(size_t)pos * (kD / 2) + lane];
+      rope_cur[kD / 2 + lane] = rope_sin[(size_t)pos * (kD / 2) + lane];
+    }
   }
   x.rms_norm(in_norm, eps);
   const int lane = lane_id();
@@ -169,42 +207,107 @@ template <typename TS, int K, int R>
 __global__ __launch_bounds__(kBlock) void k_gemv_residual(const TS* __restrict__ W, const TS* __restrict__ in,
                                                           const TS* __restrict__ x_in, TS* __restrict__ x_out, int M,
                                                           int32_t* __restrict__ ctrl, int advance_pos) {
-  if (advance_pos && blockIdx.x == 0 && threadIdx.x == 0) ctrl[kCtrlPos] = ctrl[kCtrlPos] + 1;
   const int ngroups = ceil_div(M, R);
   int g = wave_row_groups_begin();
-  WRows<TS, K, R> w;
-  if (g < ngroups) w.load(W, g * R, M);
+  // operands first, then the weight rows (vector loads return in issue order)
   Act<TS, K> x;
   x.load(in);
+  float xr = rows_prefetch<TS, R>(x_in, g * R, M);
+  __builtin_amdgcn_sched_barrier(0);
+  WRows<TS, K, R> w;
+  w.load(W, g * R, M);   // rows clamped into W: no branch around the loads
+  __builtin_amdgcn_sched_barrier(0);
   const int lane = lane_id();
   for (; g < ngroups; g += wave_row_groups_stride()) {
     float acc[R];
     w.dot(x, acc);
     const int next = g + wave_row_groups_stride();
-    if (next < ngroups) w.load(W, next * R, M);
+    float xr_next = 0.f;
+    if (next < ngroups) {
+      xr_next = rows_prefetch<TS, R>(x_in, next * R, M);
+      w.load(W, next * R, M);
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float s = wave_sum(acc[r]);
       const int m = g * R + r;
-      if (lane == 0 && m < M) x_out[m] = Store<TS>::from_f(Store<TS>::to_f(x_in[m]) + s);
+      if (lane == 0 && m < M) x_out[m] = Store<TS>::from_f(lane_value(xr, r) + s);
     }
+    xr = xr_next;
   }
+  // (no kernel of this launch reads the position)
+  if (advance_pos && blockIdx.x == 0 && threadIdx.x == 0) ctrl[kCtrlPos] = ctrl[kCtrlPos] + 1;
 }
 
 // -------------------------------------------------------------- gate/up
-// act[m] = silu(Wg[m] . b) * (Wu[m] . b), b = rms(x, post_norm); Wgu holds
-// the I gate rows followed by the I up rows.
-template <typename TS, int H, int R>
+// Partial vectors (float4 loads per thread) the gate/up prologue holds in
+// registers: ceil(H / 1024) * slots <= kMaxPartVec; other shapes use the
+// separate attention and output-projection launches.
+constexpr int kMaxPartVec = 16;
+
+// act[m] = silu(Wg[m] . b) * (Wu[m] . b), b = rms(x2, post_norm); Wgu holds
+// the I gate rows followed by the I up rows.  With NP > 0 the residual x2
+// arrives as NP FP32 partial vectors (the KV-head split of the fused
+// attention/output launch, the first carrying the residual; slots past the
+// KV head count hold zeros): every block sums them in the same order,
+// rounds as stored, and block 0 writes x2 for the down projection.
+template <typename TS, int H, int R, int NP>
 __global__ __launch_bounds__(kBlock) void k_gateup(const TS* __restrict__ Wgu, const TS* __restrict__ post_norm,
-                                                   const TS* __restrict__ x_res, float eps, TS* __restrict__ act,
-                                                   int I) {
+                                                   const TS* __restrict__ x_res, const float* __restrict__ opart,
+                                                   float eps, TS* __restrict__ act, int I, TS* __restrict__ x2_out) {
   const int ngroups = ceil_div(I, R);
   const TS* Wu = Wgu + (size_t)I * H;
+  const int tid = threadIdx.x;
   int g = wave_row_groups_begin();
-  WRows<TS, H, R> wg, wu;
-  if (g < ngroups) { wg.load(Wgu, g * R, I); wu.load(Wu, g * R, I); }
   Act<TS, H> x;
-  x.load(x_res);
+  WRows<TS, H, R> wg, wu;
+  if constexpr (NP > 0) {
+    // Vector loads return in issue order, so the partials (this thread's
+    // float4 column of every partial, for each 1024-wide slice of x2) go out
+    // before the weight rows, and their sum overlaps the weight stream.
+    constexpr int NC = ceil_div(H, 4 * kBlock);
+    static_assert(NC * NP <= kMaxPartVec, "partials held in registers");
+    __shared__ float s_x[NC * 4 * kBlock];   // padded: every thread writes its column
+    f4_t pv[NP][NC];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int i = min(4 * (c * kBlock + tid), H - 4);
+        pv[p][c] = *reinterpret_cast<const f4_t*>(opart + (size_t)p * H + i);
+      }
+    __builtin_amdgcn_sched_barrier(0);   // partials before weights
+    wg.load(Wgu, g * R, I);   // rows clamped into W: no branch around the loads
+    wu.load(Wu, g * R, I);
+    __builtin_amdgcn_sched_barrier(0);   // all loads issued in this order first
+    // (the sums are used unconditionally, so the loads are not sunk into a
+    // branch below the weight loads)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int i = 4 * (c * kBlock + tid);
+      f4_t v = pv[0][c];
+#pragma unroll
+      for (int p = 1; p < NP; ++p) v += pv[p][c];
+      TS t[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t[e] = Store<TS>::from_f(v[e]);
+        v[e] = Store<TS>::to_f(t[e]);
+      }
+      *reinterpret_cast<f4_t*>(s_x + i) = v;
+      if (blockIdx.x == 0 && i < H)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x2_out[i + e] = t[e];
+    }
+    __syncthreads();
+    x.load_f32(s_x);
+  } else {
+    x.load(x_res);
+    __builtin_amdgcn_sched_barrier(0);
+    wg.load(Wgu, g * R, I);   // rows clamped into W: no branch around the loads
+    wu.load(Wu, g * R, I);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   x.rms_norm(post_norm, eps);
   const int lane = lane_id();
   for (; g < ngroups; g += wave_row_groups_stride()) {
@@ -402,124 +505,163 @@ struct SoftState {
 // Partial state layout: for each (kv head, split, g): [m, l, acc[128]].
 constexpr int kPartStride = 2 + kD;
 
+// The attention of one KV head j (its G query heads) over the keys
+// [k_begin, k_end) of the sequence at position p, spread over the 16
+// 16-lane rows of a 256-thread block: row sid takes keys k_begin + sid +
+// 16u.  prefetch() issues every load that does not depend on p (raw
+// queries, the current token's key and value, the rotary row of p, the
+// norm gains, and each row's first four cached keys, clamped into the
+// cache: keys past p are loaded but never used), so they are in flight
+// together with the read of p.
+template <typename TS, int G>
+struct HeadAttn {
+  float q[G][8], kc[8], vc[8], k4[4][8], v4[4][8], c[4], s[4], gq[8], gk[8];
+
+  __device__ __forceinline__ void prefetch(const TS* __restrict__ qkv, const TS* __restrict__ kh,
+                                           const TS* __restrict__ vh, const TS* __restrict__ q_norm,
+                                           const TS* __restrict__ k_norm, const float* __restrict__ rope_cur,
+                                           int j, int Q, int KV, int cap, int k_begin, int sid, int sl) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kk = min(k_begin + sid + 16 * u, cap - 1);
+      load_head8<TS>(kh + (size_t)kk * kD, sl, k4[u]);
+      load_head8<TS>(vh + (size_t)kk * kD, sl, v4[u]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) load_head8<TS>(qkv + (size_t)(j * G + g) * kD, sl, q[g]);
+    load_head8<TS>(qkv + Q + (size_t)j * kD, sl, kc);
+    load_head8<TS>(qkv + Q + KV + (size_t)j * kD, sl, vc);
+    const float4 cv = *reinterpret_cast<const float4*>(rope_cur + 4 * sl);
+    const float4 sv = *reinterpret_cast<const float4*>(rope_cur + kD / 2 + 4 * sl);
+    c[0] = cv.x; c[1] = cv.y; c[2] = cv.z; c[3] = cv.w;
+    s[0] = sv.x; s[1] = sv.y; s[2] = sv.z; s[3] = sv.w;
+    load_head8<TS>(q_norm, sl, gq);
+    load_head8<TS>(k_norm, sl, gk);
+  }
+
+  // Cached keys [k_begin, k_stop); with has_cur the current token's
+  // key/value (slot p) are normalised, rotated and folded in from registers
+  // by row 0 of wave 0, which also writes slot p when write_cur is set.
+  __device__ __forceinline__ void run(TS* __restrict__ kh, TS* __restrict__ vh, int pos, int k_begin, int k_stop,
+                                      bool has_cur, bool write_cur, float eps, int sid, int sl, SoftState<G>& st) {
+    // queries: normalised, rotated, rounded as stored, then pre-scaled by
+    // log2(e)/sqrt(D) so that scores are in the log2 domain
+    const float qscale = kLog2e / sqrtf((float)kD);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      norm_rope8(q[g], gq, c, s, eps);
+      round_to_store<TS>(q[g]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[g][i] *= qscale;
+    }
+    st.init();
+    // the first four keys of the row are in registers already; longer
+    // ranges continue in groups of four with all loads in flight first
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k_begin + sid + 16 * u < k_stop) st.add(q, k4[u], v4[u]);
+    for (int key = k_begin + sid + 64; key < k_stop; key += 64) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (key + 16 * u < k_stop) {
+          load_head8<TS>(kh + (size_t)(key + 16 * u) * kD, sl, k4[u]);
+          load_head8<TS>(vh + (size_t)(key + 16 * u) * kD, sl, v4[u]);
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (key + 16 * u < k_stop) st.add(q, k4[u], v4[u]);
+    }
+    if (has_cur) {
+      norm_rope8(kc, gk, c, s, eps);
+      round_to_store<TS>(kc);
+      if (sid == 0) {
+        if (write_cur) {
+          store_head8<TS>(kh + (size_t)pos * kD, sl, kc);
+          store_head8<TS>(vh + (size_t)pos * kD, sl, vc);
+        }
+        st.add(q, kc, vc);
+      }
+    }
+  }
+};
+
+// LDS merge of the 16 row states of a block.
+template <int G>
+struct RowMerge {
+  float m[16][G], l[16][G];
+  float acc[16][G][kD];
+
+  __device__ __forceinline__ void put(const SoftState<G>& st, int sid, int sl) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (sl == 0) { m[sid][g] = st.m[g]; l[sid][g] = st.l[g]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[sid][g][4 * sl + i] = st.acc[g][i];
+        acc[sid][g][64 + 4 * sl + i] = st.acc[g][4 + i];
+      }
+    }
+  }
+  // Combined (max, sum, weighted output) of query head g, dim d.
+  __device__ __forceinline__ void get(int g, int d, float& mx, float& L, float& A) const {
+    mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, m[r][g]);
+    L = 0.f;
+    A = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float w = exp2f(m[r][g] - mx);   // rows without keys: exp2(-inf) = 0
+      L = fmaf(l[r][g], w, L);
+      A = fmaf(acc[r][g][d], w, A);
+    }
+  }
+};
+
 template <typename TS, int G>
 __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
                                                  TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
-                                                 const TS* __restrict__ k_norm, const float* __restrict__ rope_cos,
-                                                 const float* __restrict__ rope_sin, int32_t* __restrict__ ctrl,
-                                                 int n_q, int n_kv, int cap, float eps, int chunk,
-                                                 float* __restrict__ part, TS* __restrict__ o) {
-  __shared__ float sm_m[16][G], sm_l[16][G];
-  __shared__ float sm_acc[16][G][kD];
-
+                                                 const TS* __restrict__ k_norm, const float* __restrict__ rope_cur,
+                                                 const int32_t* __restrict__ ctrl, int n_q, int n_kv, int cap,
+                                                 float eps, int chunk, float* __restrict__ part,
+                                                 TS* __restrict__ o) {
+  __shared__ RowMerge<G> sm;
   const int j = blockIdx.y;            // KV head
   const int split = blockIdx.x;
   const int lane = lane_id(), wave = wave_id();
-  const int row = lane >> 4, sl = lane & 15;
-  const int sid = wave * 4 + row;       // this row's slot among the block's 16 keys in flight
-  const int Q = n_q * kD, KV = n_kv * kD;
+  const int sid = wave * 4 + (lane >> 4), sl = lane & 15;
   const size_t head_off = (size_t)j * cap * kD;
+  TS* kh = k_cache + head_off;
+  TS* vh = v_cache + head_off;
 
   // Every split covers the fixed key range [split*chunk, split*chunk + chunk)
-  // (chunk is a per-model constant), so the loads that do not depend on the
-  // position go first: raw queries, the current token's key and value, and
-  // this row's first four cached keys (clamped into the cache; keys past the
-  // position are loaded but never used).
+  // (chunk is a per-model constant), so its first keys can be loaded before p.
   const int k_begin = split * chunk;
-  float q[G][8], kc[8], vc[8], k4[4][8], v4[4][8];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int kk = min(k_begin + sid + 16 * u, cap - 1);
-    load_head8<TS>(k_cache + head_off + (size_t)kk * kD, sl, k4[u]);
-    load_head8<TS>(v_cache + head_off + (size_t)kk * kD, sl, v4[u]);
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) load_head8<TS>(qkv + (size_t)(j * G + g) * kD, sl, q[g]);
-  load_head8<TS>(qkv + Q + (size_t)j * kD, sl, kc);
-  load_head8<TS>(qkv + Q + KV + (size_t)j * kD, sl, vc);
-
+  HeadAttn<TS, G> ha;
+  ha.prefetch(qkv, kh, vh, q_norm, k_norm, rope_cur, j, n_q * kD, n_kv * kD, cap, k_begin, sid, sl);
+  // keep the scheduler from moving work that waits on the first loads
+  // (the query norm) above the later ones
+  __builtin_amdgcn_sched_barrier(0);
   const int pos = ctrl[kCtrlPos];
   const int n_keys = pos + 1;
   const int n_splits = ceil_div(n_keys, chunk);
-  if (split >= n_splits) return;
-  const int k_end = min(n_keys, k_begin + chunk);
-  const bool has_cur = (k_end == n_keys);
-  const int k_stop = has_cur ? k_end - 1 : k_end;   // cached keys [k_begin, k_stop)
-
-  float c[4], s[4], gq[8], gk[8];
-  {
-    const float4 cv = *reinterpret_cast<const float4*>(rope_cos + (size_t)pos * (kD / 2) + 4 * sl);
-    const float4 sv = *reinterpret_cast<const float4*>(rope_sin + (size_t)pos * (kD / 2) + 4 * sl);
-    c[0] = cv.x; c[1] = cv.y; c[2] = cv.z; c[3] = cv.w;
-    s[0] = sv.x; s[1] = sv.y; s[2] = sv.z; s[3] = sv.w;
-  }
-  load_head8<TS>(q_norm, sl, gq);
-  load_head8<TS>(k_norm, sl, gk);
-  // queries: normalised, rotated, rounded as stored, then pre-scaled by
-  // log2(e)/sqrt(D) so that scores are in the log2 domain
-  const float qscale = kLog2e / sqrtf((float)kD);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    norm_rope8(q[g], gq, c, s, eps);
-    round_to_store<TS>(q[g]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[g][i] *= qscale;
-  }
-
+  // Splits past the context run on an empty range and write nothing (an
+  // early return would let the compiler sink the loads above below the
+  // position read).
+  const bool active = split < n_splits;
+  const int k_end = active ? min(n_keys, k_begin + chunk) : k_begin;
+  const bool has_cur = active && k_end == n_keys;
   SoftState<G> st;
-  st.init();
-  // row keys k_begin + sid + 16u: the first four are in registers already;
-  // longer chunks continue in groups of four with all loads in flight first
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (k_begin + sid + 16 * u < k_stop) st.add(q, k4[u], v4[u]);
-  for (int key = k_begin + sid + 64; key < k_stop; key += 64) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (key + 16 * u < k_stop) {
-        load_head8<TS>(k_cache + head_off + (size_t)(key + 16 * u) * kD, sl, k4[u]);
-        load_head8<TS>(v_cache + head_off + (size_t)(key + 16 * u) * kD, sl, v4[u]);
-      }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (key + 16 * u < k_stop) st.add(q, k4[u], v4[u]);
-  }
-  if (has_cur) {
-    // the current token's key and value: normalise/rotate, write slot p,
-    // and fold them in from registers (row 0 of wave 0)
-    norm_rope8(kc, gk, c, s, eps);
-    round_to_store<TS>(kc);
-    if (wave == 0 && row == 0) {
-      store_head8<TS>(k_cache + head_off + (size_t)pos * kD, sl, kc);
-      store_head8<TS>(v_cache + head_off + (size_t)pos * kD, sl, vc);
-      st.add(q, kc, vc);
-    }
-  }
+  ha.run(kh, vh, pos, k_begin, has_cur ? k_end - 1 : k_end, has_cur, true, eps, sid, sl, st);
 
-  // merge the 16 row states of this block
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (sl == 0) { sm_m[sid][g] = st.m[g]; sm_l[sid][g] = st.l[g]; }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sm_acc[sid][g][4 * sl + i] = st.acc[g][i];
-      sm_acc[sid][g][64 + 4 * sl + i] = st.acc[g][4 + i];
-    }
-  }
+  sm.put(st, sid, sl);
   __syncthreads();
+  if (!active) return;
   float* my_part = part + ((size_t)(j * gridDim.x + split) * G) * kPartStride;
   for (int t = threadIdx.x; t < G * kD; t += kBlock) {
     const int g = t / kD, d = t - g * kD;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sm_m[r][g]);
-    float L = 0.f, A = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float w = exp2f(sm_m[r][g] - mx);   // rows without keys: exp2(-inf) = 0
-      L = fmaf(sm_l[r][g], w, L);
-      A = fmaf(sm_acc[r][g][d], w, A);
-    }
+    float mx, L, A;
+    sm.get(g, d, mx, L, A);
     if (n_splits == 1) {
       o[(size_t)(j * G + g) * kD + d] = Store<TS>::from_f(A / L);
     } else {
@@ -527,6 +669,117 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
       my_part[g * kPartStride + 2 + d] = A;
     }
   }
+}
+
+// ------------------------------------------- attention + output projection
+// Contexts that fit one attention split: the output GEMV is split by KV
+// head.  Block (b, j) recomputes the attention of KV head j over all keys
+// (a few KiB per key range, read from L2 by the blocks of that head), then
+// multiplies its 4R rows of W_o restricted to head j's G*128 columns,
+// which it put in flight first:
+//   part[j][m] = W_o[m, cols of head j] . o_j  (+ x[m] for j = 0).
+// The gate/up launch sums the partials in a fixed order.  Blocks b = 0
+// write the current token's key and value into the cache.
+template <typename TS, int G, int R>
+struct WoSlice {
+  static constexpr int VEC = Vec16<TS>::N;
+  static constexpr int LPR = G * kD / VEC;          // 16-byte vectors per row slice
+  static constexpr int NLD = R * LPR / kWave;       // vectors per lane
+  static_assert((R * LPR) % kWave == 0, "whole vectors per lane");
+  static_assert(LPR == 16 || LPR == 32 || LPR % kWave == 0, "row slice of 16, 32 or a multiple of 64 lanes");
+  Vec16<TS> v[NLD];
+
+  // vector t of this lane: row (64t + lane) / LPR, column vector (64t + lane) % LPR
+  __device__ __forceinline__ void load(const TS* __restrict__ Wo, int ld, int col0, int row0, int M) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      const int f = t * kWave + lane;
+      const int row = min(row0 + f / LPR, M - 1);
+      v[t].template load<false>(Wo + (size_t)row * ld + col0 + (f % LPR) * VEC);
+    }
+  }
+  // out[row0 + r] = (this slice's row r) . o + lane r's xb
+  __device__ __forceinline__ void apply(const float* o, int row0, int M, float xb, float* __restrict__ out) const {
+    const int lane = lane_id();
+    float d[NLD];
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      const int f = t * kWave + lane;
+      const float* oc = o + (f % LPR) * VEC;
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) a = fmaf(v[t].v[i], oc[i], a);
+      d[t] = a;
+    }
+    if constexpr (LPR % kWave == 0) {
+      constexpr int TPR = LPR / kWave;              // vectors per row per lane
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float a = 0.f;
+#pragma unroll
+        for (int u = 0; u < TPR; ++u) a += d[r * TPR + u];
+        a = wave_sum(a);
+        const int m = row0 + r;
+        if (lane == 0 && m < M) out[m] = a + lane_value(xb, r);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NLD; ++t) {
+        float a = row16_sum(d[t]);
+        if constexpr (LPR == 32) a += __shfl_xor(a, 16);
+        const int f = t * kWave + lane;
+        const int m = row0 + f / LPR;
+        const float b = __shfl(xb, f / LPR);
+        if (f % LPR == 0 && m < M) out[m] = a + b;
+      }
+    }
+  }
+};
+
+template <typename TS, int G, int R>
+__global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
+                                                   TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
+                                                   const TS* __restrict__ k_norm, const float* __restrict__ rope_cur,
+                                                   const int32_t* __restrict__ ctrl, int n_q, int n_kv, int cap,
+                                                   float eps, const TS* __restrict__ Wo, const TS* __restrict__ x_res,
+                                                   int H, float* __restrict__ opart) {
+  __shared__ RowMerge<G> sm;
+  __shared__ float s_o[G * kD];
+  const int j = blockIdx.y;            // KV head
+  const int lane = lane_id(), wave = wave_id();
+  const int sid = wave * 4 + (lane >> 4), sl = lane & 15;
+  const int row0 = (blockIdx.x * kWavesPerBlock + wave) * R;
+  const size_t head_off = (size_t)j * cap * kD;
+  TS* kh = k_cache + head_off;
+  TS* vh = v_cache + head_off;
+  // Vector loads return in issue order: the attention operands go out
+  // first, the W_o rows last, so the attention runs while the weights stream
+  // in.  The position (a scalar load) is read after them: scalar loads
+  // complete out of order, so any earlier wait on a kernel argument would
+  // also wait for it.
+  HeadAttn<TS, G> ha;
+  ha.prefetch(qkv, kh, vh, q_norm, k_norm, rope_cur, j, n_q * kD, n_kv * kD, cap, 0, sid, sl);
+  // the residual rows (carried by the partial of KV head 0)
+  const float xb = j == 0 ? rows_prefetch<TS, R>(x_res, row0, H) : 0.f;
+  __builtin_amdgcn_sched_barrier(0);   // attention operands before the weights
+  WoSlice<TS, G, R> w;
+  w.load(Wo, n_q * kD, j * G * kD, row0, H);
+  __builtin_amdgcn_sched_barrier(0);   // all loads issued in this order first
+  const int pos = ctrl[kCtrlPos];
+  SoftState<G> st;
+  ha.run(kh, vh, pos, 0, pos, true, blockIdx.x == 0, eps, sid, sl, st);
+
+  sm.put(st, sid, sl);
+  __syncthreads();
+  for (int t = threadIdx.x; t < G * kD; t += kBlock) {
+    const int g = t / kD, d = t - g * kD;
+    float mx, L, A;
+    sm.get(g, d, mx, L, A);
+    s_o[t] = Store<TS>::to_f(Store<TS>::from_f(A / L));   // o rounded as stored
+  }
+  __syncthreads();
+  w.apply(s_o, row0, H, xb, opart + (size_t)j * H);
 }
 
 // Merge of the split-K partial states of one query head (one block of 256
@@ -626,7 +879,7 @@ bool qkv_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool 
     return with_r(sh.rows_qkv, [&](auto rc) {
       hipLaunchKernelGGL((k_qkv<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock), 0, s,
                          (const TS*)L.wqkv, (const TS*)L.in_norm, (TS*)a.x, (const TS*)a.embed, a.ids, a.ctrl,
-                         first ? 1 : 0, a.vocab, a.eps, (TS*)a.qkv, M);
+                         a.rope_cos, a.rope_sin, a.rope_cur, first ? 1 : 0, a.vocab, a.eps, (TS*)a.qkv, M);
       return true;
     });
   });
@@ -646,14 +899,41 @@ bool residual_t(const DecodeArgs& a, int K, int R, int grid_req, const void* W, 
   });
 }
 
+// Partial slots the gate/up prologue sums for a model: the KV head count
+// rounded up to 2, 4 or 8 (the extra slots stay zero), or 0 when the
+// partials would not fit its registers.
+int parts_slots(int hidden, int n_kv) {
+  for (int np : {2, 4, 8})
+    if (n_kv <= np) return ceil_div(hidden, 4 * kBlock) * np <= kMaxPartVec ? np : 0;
+  return 0;
+}
+
 template <typename TS>
-bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool from_parts, hipStream_t s) {
   const int grid = blocks_for(a.inter, sh.rows_gu, sh.grid_gu);
+  const int np = from_parts ? parts_slots(a.hidden, a.n_kv) : 0;
+  if (from_parts && np == 0) return false;
   return with_k<TS>(a.hidden, [&](auto kc) {
     return with_r(sh.rows_gu, [&](auto rc) {
-      hipLaunchKernelGGL((k_gateup<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock), 0, s,
-                         (const TS*)L.wgu, (const TS*)L.post_norm, (const TS*)a.x2, a.eps, (TS*)a.act, a.inter);
-      return true;
+      constexpr int K = decltype(kc)::value, R = decltype(rc)::value;
+      auto go = [&](auto npc) {
+        constexpr int NP = decltype(npc)::value;
+        if constexpr (NP * ceil_div(K, 4 * kBlock) <= kMaxPartVec) {
+          hipLaunchKernelGGL((k_gateup<TS, K, R, NP>), dim3(grid), dim3(kBlock), 0, s, (const TS*)L.wgu,
+                             (const TS*)L.post_norm, (const TS*)a.x2, a.opart, a.eps, (TS*)a.act, a.inter,
+                             (TS*)a.x2);
+          return true;
+        } else {
+          return false;
+        }
+      };
+      switch (np) {
+        case 0: return go(IC<0>{});
+        case 2: return go(IC<2>{});
+        case 4: return go(IC<4>{});
+        case 8: return go(IC<8>{});
+        default: return false;
+      }
     });
   });
 }
@@ -677,8 +957,8 @@ bool attn_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipS
   const dim3 grid(sh.attn_splits, a.n_kv);
   auto go = [&](auto gc) {
     hipLaunchKernelGGL((k_attn<TS, decltype(gc)::value>), grid, dim3(kBlock), 0, s, (const TS*)a.qkv,
-                       (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm, a.rope_cos,
-                       a.rope_sin, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, sh.attn_chunk, a.attn_part, (TS*)a.o);
+                       (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm, a.rope_cur,
+                       a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, sh.attn_chunk, a.attn_part, (TS*)a.o);
     return true;
   };
   switch (G) {
@@ -705,7 +985,35 @@ bool attn_merge_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   }
 }
 
+template <typename TS>
+bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+  const int G = a.n_q / a.n_kv;
+  auto go = [&](auto gc, auto rc) {
+    constexpr int R = decltype(rc)::value;
+    const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R), a.n_kv);
+    hipLaunchKernelGGL((k_attn_o<TS, decltype(gc)::value, R>), grid, dim3(kBlock), 0, s, (const TS*)a.qkv,
+                       (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm, a.rope_cur, a.ctrl,
+                       a.n_q, a.n_kv, a.cap, a.eps, (const TS*)L.wo, (const TS*)a.x, a.hidden, a.opart);
+    return true;
+  };
+  auto with_g = [&](auto rc) {
+    switch (G) {
+      case 1: return go(IC<1>{}, rc);
+      case 2: return go(IC<2>{}, rc);
+      case 4: return go(IC<4>{}, rc);
+      default: return false;
+    }
+  };
+  switch (sh.rows_attn_o) {
+    case 4: return with_g(IC<4>{});
+    case 8: return with_g(IC<8>{});
+    default: return false;
+  }
+}
+
 }  // namespace
+
+int attn_o_part_slots(int hidden, int n_kv) { return parts_slots(hidden, n_kv); }
 
 int head_blocks(const DecodeArgs& a, const DecodeShape& sh) { return head_grid(a.vocab, sh.rows_head, sh.grid_head); }
 
@@ -723,8 +1031,11 @@ bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hi
   return a.dtype == 0 ? residual_t<float>(a, K, sh.rows_o, sh.grid_o, L.wo, a.o, a.x, a.x2, false, s)
                       : residual_t<__half>(a, K, sh.rows_o, sh.grid_o, L.wo, a.o, a.x, a.x2, false, s);
 }
-bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
-  return a.dtype == 0 ? gateup_t<float>(a, sh, L, s) : gateup_t<__half>(a, sh, L, s);
+bool launch_attn_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+  return a.dtype == 0 ? attn_o_t<float>(a, sh, L, s) : attn_o_t<__half>(a, sh, L, s);
+}
+bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool from_parts, hipStream_t s) {
+  return a.dtype == 0 ? gateup_t<float>(a, sh, L, from_parts, s) : gateup_t<__half>(a, sh, L, from_parts, s);
 }
 bool launch_down(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool adv, hipStream_t s) {
   return a.dtype == 0 ? residual_t<float>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, a.act, a.x2, a.x, adv, s)

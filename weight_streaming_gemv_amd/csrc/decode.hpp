@@ -37,12 +37,14 @@ struct DecodeArgs {
   const void* final_norm;
   const float* rope_cos;  // [cap][D/2]
   const float* rope_sin;
+  float* rope_cur;      // [D]: cos then sin of the current position (written by layer 0's qkv)
   void* x;              // residual [H]: layer input / down-projection output
   void* x2;             // residual [H]: output-projection output / MLP input
   void* qkv;            // [Q + 2 KV]
   void* o;              // [Q]
   void* act;            // [I]
   void* logits;         // [V]
+  float* opart;         // [slots][H] FP32 output-projection partials of the fused attention launch
   float* attn_part;     // split-K partial states
   int attn_part_splits; // capacity in splits per KV head
   unsigned long long* am_part;  // [kHeadMaxBlocks] per-block argmax keys of the head
@@ -56,6 +58,8 @@ struct DecodeShape {
   int grid_qkv, grid_o, grid_gu, grid_down, grid_head;   // blocks (0 = one row group per wave)
   int attn_splits;                                       // split-K blocks per KV head (grid.x)
   int attn_chunk;                                        // keys per split (a multiple of 16, >= 64)
+  int fuse_attn_o;                                       // one-split contexts: fused attention + output GEMV
+  int rows_attn_o;                                       // W_o rows per wave in the fused launch (4 or 8)
 };
 
 // Stage launches; each returns false if the shape is not compiled in.
@@ -64,7 +68,14 @@ bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L,
 // Combines the split-K partial states (needed when sh.attn_splits > 1).
 bool launch_attn_merge(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s);
 bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
-bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
+// Contexts within one attention split: attention fused with the output GEMV,
+// which writes per-KV-head partials into opart instead of x2.
+bool launch_attn_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
+// Partial slots (>= n_kv; slots past n_kv must hold zeros) the gate/up
+// prologue sums after a fused launch, or 0 if the shape cannot be fused.
+int attn_o_part_slots(int hidden, int n_kv);
+// from_parts: x2 is the sum of the opart partials (written back to x2).
+bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool from_parts, hipStream_t s);
 bool launch_down(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool advance_pos, hipStream_t s);
 // Final RMSNorm + vocabulary GEMV with one argmax key per block; then the
 // one-block argmax (ties to the lowest id) writes the token into ctrl and

@@ -10,6 +10,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <vector>
 
@@ -114,10 +115,11 @@ int attn_split_cap(const Dims& d) {
 }
 
 struct WsLayout {
-  size_t kv = 0, rope_cos = 0, rope_sin = 0, x = 0, x2 = 0, qkv = 0, o = 0, act = 0, logits = 0;
-  size_t attn_part = 0, am_part = 0, ctrl = 0, ids = 0, total = 0;
+  size_t kv = 0, rope_cos = 0, rope_sin = 0, rope_cur = 0, x = 0, x2 = 0, qkv = 0, o = 0, act = 0, logits = 0;
+  size_t opart = 0, attn_part = 0, am_part = 0, ctrl = 0, ids = 0, total = 0;
   PrefillLayout pf;
   int attn_splits_cap = 1;
+  int opart_slots = 0;
 };
 
 WsLayout ws_layout(const Dims& d) {
@@ -127,12 +129,15 @@ WsLayout ws_layout(const Dims& d) {
   w.kv = take((size_t)d.L * 2 * d.nkv * d.cap * d.D * d.es);
   w.rope_cos = take((size_t)d.cap * (d.D / 2) * 4);
   w.rope_sin = take((size_t)d.cap * (d.D / 2) * 4);
+  w.rope_cur = take((size_t)d.D * 4);
   w.x = take((size_t)d.H * d.es);
   w.x2 = take((size_t)d.H * d.es);
   w.qkv = take((size_t)(d.Q + 2 * d.KV) * d.es);
   w.o = take((size_t)d.Q * d.es);
   w.act = take((size_t)d.I * d.es);
   w.logits = take((size_t)d.V * d.es);
+  w.opart_slots = std::max(d.nkv, attn_o_part_slots(d.H, d.nkv));
+  w.opart = take((size_t)w.opart_slots * d.H * 4);
   w.attn_splits_cap = attn_split_cap(d);
   w.attn_part = take((size_t)d.nkv * w.attn_splits_cap * d.G * (2 + d.D) * 4);
   w.am_part = take((size_t)kHeadMaxBlocks * 8);
@@ -210,35 +215,47 @@ bool record_event(wsg_model* m, hipEvent_t e) {
 }
 
 template <typename F>
-bool timed(wsg_model* m, int stage, F&& launch) {
+bool timed(wsg_model* m, int stage, int64_t bytes, F&& launch) {
   const bool t = !m->capturing && (m->timed_stage == stage) && (m->ev_used + 2 <= (int)m->ev.size());
   if (t) record_event(m, m->ev[m->ev_used]);
   const bool ok = launch();
   if (t) {
     record_event(m, m->ev[m->ev_used + 1]);
     m->ev_used += 2;
-    m->timed_bytes_per_launch_sum += stage_bytes(m, stage);
+    m->timed_bytes_per_launch_sum += bytes;
   }
   return ok;
 }
 
 // All layers of one token; the last down projection advances the position
-// when no head follows (prompt rows before the last).
+// when no head follows (prompt rows before the last).  Contexts within one
+// attention split use the fused attention + output-projection launch.
 bool enqueue_body(wsg_model* m, int splits, bool advance) {
   DecodeShape sh = m->shape;
   sh.attn_splits = splits;
   const hipStream_t s = m->stream;
   const int L = m->d.L;
+  const bool fused = sh.fuse_attn_o && splits == 1 && attn_o_part_slots(m->d.H, m->d.nkv) > 0;
   for (int l = 0; l < L; ++l) {
     const LayerPtrs& lp = m->layers[l];
-    if (!timed(m, WSG_STAGE_QKV, [&] { return launch_qkv(m->args, sh, lp, l == 0, s); })) return false;
-    if (!timed(m, WSG_STAGE_ATTN, [&] {
-          return launch_attn(m->args, sh, lp, s) && (splits == 1 || launch_attn_merge(m->args, sh, s));
-        }))
+    const DecodeArgs& a = m->args;
+    if (!timed(m, WSG_STAGE_QKV, stage_bytes(m, WSG_STAGE_QKV), [&] { return launch_qkv(a, sh, lp, l == 0, s); }))
       return false;
-    if (!timed(m, WSG_STAGE_O, [&] { return launch_o(m->args, sh, lp, s); })) return false;
-    if (!timed(m, WSG_STAGE_GATEUP, [&] { return launch_gateup(m->args, sh, lp, s); })) return false;
-    if (!timed(m, WSG_STAGE_DOWN, [&] { return launch_down(m->args, sh, lp, advance && l == L - 1, s); }))
+    if (fused) {
+      if (!timed(m, WSG_STAGE_ATTN, stage_bytes(m, WSG_STAGE_O), [&] { return launch_attn_o(a, sh, lp, s); }))
+        return false;
+    } else {
+      if (!timed(m, WSG_STAGE_ATTN, 0, [&] {
+            return launch_attn(a, sh, lp, s) && (splits == 1 || launch_attn_merge(a, sh, s));
+          }))
+        return false;
+      if (!timed(m, WSG_STAGE_O, stage_bytes(m, WSG_STAGE_O), [&] { return launch_o(a, sh, lp, s); })) return false;
+    }
+    if (!timed(m, WSG_STAGE_GATEUP, stage_bytes(m, WSG_STAGE_GATEUP),
+               [&] { return launch_gateup(a, sh, lp, fused, s); }))
+      return false;
+    if (!timed(m, WSG_STAGE_DOWN, stage_bytes(m, WSG_STAGE_DOWN),
+               [&] { return launch_down(a, sh, lp, advance && l == L - 1, s); }))
       return false;
   }
   return true;
@@ -247,8 +264,13 @@ bool enqueue_body(wsg_model* m, int splits, bool advance) {
 bool enqueue_head(wsg_model* m) { return launch_head(m->args, m->shape, m->stream); }
 bool enqueue_argmax(wsg_model* m) { return launch_argmax(m->args, m->shape, m->stream); }
 
+// Attention blocks per KV head for n_keys: the splits the context needs,
+// rounded up to a power of two up to 8 and to a multiple of 8 beyond (one
+// captured graph per value; the rounded-up blocks find no keys and write
+// nothing, but still issue their speculative loads).
 int splits_for(const wsg_model* m, int n_keys) {
-  const int want = pow2_ceil((n_keys + m->shape.attn_chunk - 1) / m->shape.attn_chunk);
+  const int need = (n_keys + m->shape.attn_chunk - 1) / m->shape.attn_chunk;
+  const int want = need <= 8 ? pow2_ceil(need) : (need + 7) / 8 * 8;
   return want < m->wl.attn_splits_cap ? want : m->wl.attn_splits_cap;
 }
 
@@ -461,6 +483,8 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   a.final_norm = m->packed + pl.final_norm;
   a.rope_cos = reinterpret_cast<const float*>(m->ws + wl.rope_cos);
   a.rope_sin = reinterpret_cast<const float*>(m->ws + wl.rope_sin);
+  a.rope_cur = reinterpret_cast<float*>(m->ws + wl.rope_cur);
+  a.opart = reinterpret_cast<float*>(m->ws + wl.opart);
   a.x = m->ws + wl.x; a.x2 = m->ws + wl.x2; a.qkv = m->ws + wl.qkv; a.o = m->ws + wl.o; a.act = m->ws + wl.act;
   a.logits = m->ws + wl.logits;
   a.attn_part = reinterpret_cast<float*>(m->ws + wl.attn_part);
@@ -485,6 +509,8 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   sh.grid_head = 4096;
   sh.attn_splits = 1;
   sh.attn_chunk = attn_chunk(d);
+  sh.fuse_attn_o = 1;
+  sh.rows_attn_o = 8;
 
   std::vector<float> cs, sn;
   fill_rope(*cfg, cs, sn);
@@ -492,6 +518,8 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
       hipMemcpyAsync(m->ws + wl.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, m->stream) != hipSuccess ||
       hipMemsetAsync(m->ws + wl.ctrl, 0, (size_t)kCtrlWords * 4, m->stream) != hipSuccess ||
       hipMemsetAsync(m->ws + wl.ids, 0, (size_t)(d.cap + 1) * 4, m->stream) != hipSuccess ||
+      // partial slots past the KV head count are summed as zeros
+      hipMemsetAsync(m->ws + wl.opart, 0, (size_t)wl.opart_slots * d.H * 4, m->stream) != hipSuccess ||
       hipStreamSynchronize(m->stream) != hipSuccess)
     return fail_free(fail(WSG_ERR_HIP, "uploading the rotary table failed"));
   // graphs need a capturable (non-null) stream
@@ -608,6 +636,16 @@ wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value) {
       if (value == 1 && m->timed_stage >= 0 && m->timed_stage != WSG_STAGE_HEAD)
         return fail(WSG_ERR_UNSUPPORTED, "in graph mode only the head stage can be timed");
       m->use_graph = value == 1;
+      return WSG_OK;
+    case WSG_OPT_FUSE_ATTN_O:
+      if (value != 0 && value != 1) return fail(WSG_ERR_INVALID_ARG, "fuse_attn_o must be 0 or 1");
+      m->shape.fuse_attn_o = value;
+      drop_graphs(m);
+      return WSG_OK;
+    case WSG_OPT_ROWS_ATTN_O:
+      if (value != 4 && value != 8) return fail(WSG_ERR_INVALID_ARG, "attention/output rows per wave must be 4 or 8");
+      m->shape.rows_attn_o = value;
+      drop_graphs(m);
       return WSG_OK;
     case WSG_OPT_TIMED_STAGE:
       if (value < -1 || value > WSG_STAGE_HEAD) return fail(WSG_ERR_INVALID_ARG, "stage %d", value);
