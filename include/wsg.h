@@ -233,7 +233,9 @@ wsg_status wsg_gemv_q4g64_ex(int32_t M, int32_t K, int32_t T, int32_t rows_per_w
  * (Megakernels, "Chunked prefill for long prompts": projections as ordinary
  * tiled matrix multiplication on the matrix units, FP32 accumulation).
  * M >= 1 (any), N % 64 == 0, K % 32 == 0; all pointers 16-byte aligned.
- * Asynchronous on hip_stream. */
+ * M <= 32 with K in {256, 512, 1024, 2048, 3072} runs the small-M kernel
+ * (16-column tiles, K split over the waves of a block); other shapes the
+ * tiled one.  Asynchronous on hip_stream. */
 wsg_status wsg_gemm_nt_f32(int32_t M, int32_t N, int32_t K, const float* d_A, const float* d_B, float* d_C,
                            int32_t accumulate, void* hip_stream);
 

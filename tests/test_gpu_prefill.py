@@ -18,9 +18,15 @@ from synth import MINI, PROMPT_SEEDS, QWEN3_0_6B, model_weights, prompt_ids
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 
+# Tiled path: M > 32 or K outside {256, 512, 1024, 2048, 3072}.  Small-M
+# path (M <= 32): one and two 16-row tiles, ragged M, every compiled K and
+# 4, 8 and 16 waves per block.
 @pytest.mark.parametrize("M,N,K", [(1, 64, 32), (37, 128, 64), (65, 192, 96), (130, 4096, 1024),
                                    (1024, 4096, 1024), (500, 1024, 2048), (257, 6144, 1024),
-                                   (1024, 1024, 3072), (2048, 4096, 1024)])
+                                   (1024, 1024, 3072), (2048, 4096, 1024),
+                                   (1, 1024, 1024), (7, 4096, 1024), (16, 2048, 2048), (17, 64, 256),
+                                   (31, 6144, 1024), (32, 1024, 3072), (31, 1024, 2048), (8, 512, 512),
+                                   (3, 128, 3072)])
 @pytest.mark.parametrize("acc", [0, 1])
 def test_gemm_nt_f32(M, N, K, acc):
     import torch

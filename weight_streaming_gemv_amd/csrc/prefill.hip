@@ -3,21 +3,27 @@
 // (Megakernels, "Chunked prefill for long prompts").
 //
 // Per chunk and layer (the pages' 11 ordered stages, here 9 launches):
-//   rows_norm   RMSNorm of each row (one wave per row)
+//   rows_norm   [residual += pending split-K partials] + RMSNorm, one block per row
 //   gemm        QKV projection  [n x H] . W_qkv^T   (FP32 MFMA)
 //   rows_qkv    per-head Q/K RMSNorm + RoPE; K/V written to cache rows p0..p0+n-1
 //   attn        causal attention of the n rows over keys 0..p0+r (VALU, LDS tiles)
-//   gemm+res    O projection, residual added in the epilogue
+//   gemm+res    O projection: residual added in the epilogue, or (few rows)
+//               split-K partial slices that the next rows_norm adds
 //   rows_norm   post-attention RMSNorm
 //   gemm        gate/up projection [n x 2I]
 //   rows_swiglu SwiGLU
-//   gemm+res    down projection, residual added in the epilogue
-// The projections are the only dense contractions and the only MFMA users.
+//   gemm+res    down projection (as the O projection)
+// The projections are the only dense contractions and the only MFMA users:
+// a tiled kernel for many rows, a small-M kernel (weights streamed straight
+// into registers, K split over waves and blocks) for up to 32 rows.
 // The chunk runs exactly n rows: the GEMM masks its ragged last row tile, so
 // no padding rows exist.  Within one prefill call the last prompt row goes
 // through the decode forward (the only row that reaches the head), so every
 // chunk stops its last layer after the K/V write (Benchmark methodology,
 // "Long-document chunked prefill": nonterminal chunks prune the final layer).
+#include <algorithm>
+#include <type_traits>
+
 #include "common.hpp"
 #include "prefill.hpp"
 #include "status.hpp"
@@ -146,6 +152,88 @@ __global__ __launch_bounds__(256) void k_gemm_nt(const float* __restrict__ A, co
       }
 }
 
+// ------------------------------------------------------- small-M GEMM
+// Few rows (M <= 32, short prompts): the tiled kernel above leaves most
+// CUs idle and each block waits on its LDS pipeline.  Here a block owns a
+// 16-column slice of C (16 weight rows) and splits K over its W waves; each
+// wave streams its weight rows straight into registers with up to PD
+// 32-wide K tiles in flight and multiplies them on v_mfma_f32_16x16x4f32
+// (MT tiles of 16 rows of A).  The W partial tiles are summed in LDS in
+// wave order, so the result does not depend on timing.
+//
+// MFMA 16x16x4 operand layout (lane l): A element (row l%16, k slot l/16),
+// B element (k slot l/16, col l%16); accumulator register r holds row
+// 4*(l/16) + r, col l%16.  Slot q of step s is k = 8q + s of the 32-wide
+// tile, so each lane reads 8 consecutive floats of a row per tile.
+typedef float f4v_t __attribute__((ext_vector_type(4)));
+
+//
+// Block (x, y) covers columns [16x, 16x + 16) and the K range
+// [y*KB, (y+1)*KB) of the ldk-long rows; with several K ranges each writes
+// its own partial slice C + y*c_split (summed later by the consumer).
+template <int KB, int W, int MT, bool ACC>
+__global__ __launch_bounds__(64 * W) void k_gemm_skinny(const float* __restrict__ A, const float* __restrict__ B,
+                                                        float* __restrict__ C, int M, int N, int ldk,
+                                                        size_t c_split) {
+  constexpr int K = KB;
+  constexpr int KW = K / W;                       // K range of one wave
+  constexpr int NT = KW / kBK;                    // 32-wide tiles per wave
+  constexpr int PDM = W >= 16 ? 4 : 8;            // tiles in flight (register budget)
+  constexpr int PD = NT < PDM ? NT : PDM;
+  constexpr int RS = 17;                          // padded row of the reduction tile
+  static_assert(K % (W * kBK) == 0, "whole tiles per wave");
+  __shared__ float red[W][MT * 16 * RS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, lq = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int k0 = blockIdx.y * KB + wave * KW + 8 * lq;
+  C += blockIdx.y * c_split;
+  const float* bp = B + (size_t)(n0 + li) * ldk + k0;
+  const float* ap[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)   // rows past M feed only unstored outputs
+    ap[mt] = A + (size_t)min(mt * 16 + li, M - 1) * ldk + k0;
+
+  f4_t tb[PD][2], ta[PD][MT][2];
+#define WSG_SKINNY_LOAD(T)                                                                        {                                                                                                 const int buf_ = (T) % PD, k_ = (T) * kBK;                                                      tb[buf_][0] = *reinterpret_cast<const f4_t*>(bp + k_);                                          tb[buf_][1] = *reinterpret_cast<const f4_t*>(bp + k_ + 4);                                      _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                                               ta[buf_][mt][0] = *reinterpret_cast<const f4_t*>(ap[mt] + k_);                                  ta[buf_][mt][1] = *reinterpret_cast<const f4_t*>(ap[mt] + k_ + 4);                            }                                                                                             }
+#pragma unroll
+  for (int t = 0; t < PD - 1; ++t) WSG_SKINNY_LOAD(t)
+  // keep the scheduler from sinking each load next to its use
+  __builtin_amdgcn_sched_barrier(0);
+  f4v_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4v_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t + PD - 1 < NT) WSG_SKINNY_LOAD(t + PD - 1)
+    __builtin_amdgcn_sched_barrier(0);
+    const int b = t % PD;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float bv = tb[b][s >> 2][s & 3];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[b][mt][s >> 2][s & 3], bv, acc[mt], 0, 0, 0);
+    }
+  }
+#undef WSG_SKINNY_LOAD
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][(mt * 16 + 4 * lq + r) * RS + li] = acc[mt][r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < MT * 256; e += 64 * W) {
+    const int row = e >> 4, col = e & 15;
+    float sum = red[0][row * RS + col];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum += red[w][row * RS + col];
+    if (row < M) {
+      float* p = C + (size_t)row * N + n0 + col;
+      *p = ACC ? *p + sum : sum;
+    }
+  }
+}
+
 // --------------------------------------------------------------- row kernels
 // X[r] = E[ids[r]] for r < n (one block of 256 threads per row).
 __global__ __launch_bounds__(256) void k_rows_embed(const float* __restrict__ E, const int32_t* __restrict__ ids,
@@ -158,25 +246,59 @@ __global__ __launch_bounds__(256) void k_rows_embed(const float* __restrict__ E,
     *reinterpret_cast<float4*>(X + (size_t)r * H + c) = *reinterpret_cast<const float4*>(E + (size_t)tok * H + c);
 }
 
-// Y[r] = X[r] * (mean(X[r]^2) + eps)^-1/2 * g, one wave per row.
-__global__ __launch_bounds__(256) void k_rows_norm(const float* __restrict__ X, const float* __restrict__ g,
-                                                   int n, int H, float eps, float* __restrict__ Y) {
-  const int r = blockIdx.x * 4 + wave_id();
-  if (r >= n) return;
-  const int lane = lane_id();
-  const float* x = X + (size_t)r * H;
+// X[r] += P[0][r] + P[1][r] + ... (NP slices of n x H, added in order),
+// then Y[r] = X[r] * (mean(X[r]^2) + eps)^-1/2 * g.  One block of 256
+// threads per row (H <= 3072): thread t owns columns 4t + 1024i, with all
+// of its loads in flight at once.
+template <int NP>
+__global__ __launch_bounds__(256) void k_rows_norm(float* __restrict__ X, const float* __restrict__ P,
+                                                   const float* __restrict__ g, int n, int H, float eps,
+                                                   float* __restrict__ Y) {
+  constexpr int kMaxIt = 3;
+  __shared__ float s_ss[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  float* x = X + (size_t)r * H;
+  f4_t v[kMaxIt], gv[kMaxIt], pv[kMaxIt][NP > 0 ? NP : 1];
+#pragma unroll
+  for (int i = 0; i < kMaxIt; ++i) {
+    const int c = min(4 * tid + 1024 * i, H - 4);   // clamped: columns past H are loaded, never stored
+    v[i] = *reinterpret_cast<const f4_t*>(x + c);
+    gv[i] = *reinterpret_cast<const f4_t*>(g + c);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) pv[i][p] = *reinterpret_cast<const f4_t*>(P + ((size_t)p * n + r) * H + c);
+  }
   float ss = 0.f;
-  for (int c = lane * 4; c < H; c += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(x + c);
-    ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+#pragma unroll
+  for (int i = 0; i < kMaxIt; ++i) {
+    const int c = 4 * tid + 1024 * i;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) v[i] += pv[i][p];
+    if (c < H) {
+      if (NP > 0) *reinterpret_cast<f4_t*>(x + c) = v[i];
+      ss = fmaf(v[i].x, v[i].x, fmaf(v[i].y, v[i].y, fmaf(v[i].z, v[i].z, fmaf(v[i].w, v[i].w, ss))));
+    }
   }
   ss = wave_sum(ss);
+  if (lane_id() == 0) s_ss[wave_id()] = ss;
+  __syncthreads();
+  ss = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
   const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int c = lane * 4; c < H; c += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(x + c);
-    const float4 w = *reinterpret_cast<const float4*>(g + c);
-    *reinterpret_cast<float4*>(Y + (size_t)r * H + c) =
-        make_float4(v.x * inv * w.x, v.y * inv * w.y, v.z * inv * w.z, v.w * inv * w.w);
+#pragma unroll
+  for (int i = 0; i < kMaxIt; ++i) {
+    const int c = 4 * tid + 1024 * i;
+    if (c < H) *reinterpret_cast<f4_t*>(Y + (size_t)r * H + c) = v[i] * inv * gv[i];
+  }
+}
+
+bool launch_rows_norm(float* X, const float* P, int n_part, const float* g, int n, int H, float eps, float* Y,
+                      hipStream_t s) {
+  if (H > 3072 || H % 4 != 0) return false;
+  switch (n_part) {
+    case 0: hipLaunchKernelGGL((k_rows_norm<0>), dim3(n), dim3(256), 0, s, X, P, g, n, H, eps, Y); return true;
+    case 2: hipLaunchKernelGGL((k_rows_norm<2>), dim3(n), dim3(256), 0, s, X, P, g, n, H, eps, Y); return true;
+    case 4: hipLaunchKernelGGL((k_rows_norm<4>), dim3(n), dim3(256), 0, s, X, P, g, n, H, eps, Y); return true;
+    case 8: hipLaunchKernelGGL((k_rows_norm<8>), dim3(n), dim3(256), 0, s, X, P, g, n, H, eps, Y); return true;
+    default: return false;
   }
 }
 
@@ -368,9 +490,77 @@ __global__ __launch_bounds__(256) void k_prefill_attn(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------ launchers
-// Tile choice: the largest tile that still gives >= 256 blocks.
+constexpr int kSkinnyMaxM = 32;
+
+// Waves per block: the fewest that give >= 2048 waves in all, with whole
+// 32-wide K tiles per wave.
+int skinny_waves(int blocks, int KB) {
+  int w = 0;
+  for (int c : {4, 8, 16}) {
+    if (KB % (c * kBK) != 0) continue;
+    w = c;
+    if ((int64_t)blocks * c >= 2048) break;
+  }
+  return w;
+}
+
+template <int KB>
+bool launch_skinny_kb(const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split,
+                      bool acc, hipStream_t s) {
+  const int W = skinny_waves(N / 16 * S, KB);
+  const dim3 grid(N / 16, S);
+  auto go = [&](auto wc, auto mc, auto ac) {
+    constexpr int Wv = decltype(wc)::value, MTv = decltype(mc)::value;
+    constexpr bool ACCv = decltype(ac)::value;
+    if constexpr (KB % (Wv * kBK) == 0) {
+      hipLaunchKernelGGL((k_gemm_skinny<KB, Wv, MTv, ACCv>), grid, dim3(64 * Wv), 0, s, A, B, C, M, N, K, c_split);
+      return true;
+    } else {
+      return false;
+    }
+  };
+  auto with_m = [&](auto wc) {
+    auto with_acc = [&](auto mc) {
+      return acc ? go(wc, mc, std::true_type{}) : go(wc, mc, std::false_type{});
+    };
+    return M <= 16 ? with_acc(std::integral_constant<int, 1>{}) : with_acc(std::integral_constant<int, 2>{});
+  };
+  switch (W) {
+    case 4: return with_m(std::integral_constant<int, 4>{});
+    case 8: return with_m(std::integral_constant<int, 8>{});
+    case 16: return with_m(std::integral_constant<int, 16>{});
+    default: return false;
+  }
+}
+
+// K ranges compiled in for the small-M kernel.
+bool skinny_kb_ok(int kb) {
+  switch (kb) {
+    case 128: case 256: case 512: case 768: case 1024: case 2048: case 3072: return true;
+    default: return false;
+  }
+}
+
+bool launch_skinny(const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split, bool acc,
+                   hipStream_t s) {
+  if (K % S != 0 || !skinny_kb_ok(K / S)) return false;
+  switch (K / S) {
+    case 128: return launch_skinny_kb<128>(A, B, C, M, N, K, S, c_split, acc, s);
+    case 256: return launch_skinny_kb<256>(A, B, C, M, N, K, S, c_split, acc, s);
+    case 512: return launch_skinny_kb<512>(A, B, C, M, N, K, S, c_split, acc, s);
+    case 768: return launch_skinny_kb<768>(A, B, C, M, N, K, S, c_split, acc, s);
+    case 1024: return launch_skinny_kb<1024>(A, B, C, M, N, K, S, c_split, acc, s);
+    case 2048: return launch_skinny_kb<2048>(A, B, C, M, N, K, S, c_split, acc, s);
+    case 3072: return launch_skinny_kb<3072>(A, B, C, M, N, K, S, c_split, acc, s);
+    default: return false;
+  }
+}
+
+// M <= 32 with a compiled K: the small-M kernel; otherwise the tiled kernel
+// with the largest tile that still gives >= 256 blocks.
 bool launch_gemm(const float* A, const float* B, float* C, int M, int N, int K, bool acc, hipStream_t s) {
   if (M < 1 || N % 64 != 0 || K % kBK != 0) return false;
+  if (M <= kSkinnyMaxM && launch_skinny(A, B, C, M, N, K, 1, 0, acc, s)) return true;
   const bool big = (N % 128 == 0) && (int64_t)(N / 128) * cdiv(M, 128) >= 256;
   if (big) {
     const dim3 grid(N / 128, cdiv(M, 128));
@@ -382,6 +572,26 @@ bool launch_gemm(const float* A, const float* B, float* C, int M, int N, int K, 
     else hipLaunchKernelGGL((k_gemm_nt<64, 64, false>), grid, dim3(256), 0, s, A, B, C, M, N, K);
   }
   return true;
+}
+
+// X[M x N] += A . B^T for a residual stream consumed by k_rows_norm.  With
+// few rows and few column tiles the small-M kernel also splits K over up
+// to kMaxSplitK blocks per tile, writing FP32 partial slices to P (M x N
+// each) instead of X; returns the slice count (0: added into X), which the
+// following k_rows_norm adds to X.  Returns -1 for an unsupported shape.
+constexpr int kMaxSplitK = 8;
+
+int launch_gemm_residual(const float* A, const float* B, float* X, float* P, int M, int N, int K, hipStream_t s) {
+  if (M <= kSkinnyMaxM && N % 64 == 0 && N / 16 < 256) {
+    int S = 0;   // the fewest K splits (2, 4 or 8, a compiled K range) that give >= 256 blocks
+    for (int c = 2; c <= kMaxSplitK; c *= 2) {
+      if (K % c != 0 || !skinny_kb_ok(K / c)) continue;
+      S = c;
+      if ((N / 16) * c >= 256) break;
+    }
+    if (S > 1 && launch_skinny(A, B, P, M, N, K, S, (size_t)M * N, false, s)) return S;
+  }
+  return launch_gemm(A, B, X, M, N, K, true, s) ? 0 : -1;
 }
 
 }  // namespace
@@ -403,6 +613,7 @@ PrefillLayout prefill_layout(int rows, int H, int I, int Q, int KV, size_t es, s
   p.o = take((size_t)rows * Q * 4);
   p.act = take((size_t)rows * I * 4);
   p.gu = take((size_t)rows * 2 * I * 4);
+  p.part = take((size_t)kMaxSplitK * std::min(rows, kSkinnyMaxM) * H * 4);
   p.total = off;
   return p;
 }
@@ -426,17 +637,19 @@ wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, hipStream_t s)
   float* O = reinterpret_cast<float*>(c.ws + c.pf.o);
   float* ACT = reinterpret_cast<float*>(c.ws + c.pf.act);
   float* GU = reinterpret_cast<float*>(c.ws + c.pf.gu);
+  float* PART = reinterpret_cast<float*>(c.ws + c.pf.part);
   const float* E = static_cast<const float*>(a.embed);
   (void)hipGetLastError();
   for (int r0 = 0; r0 < n; r0 += c.chunk) {
     const int rows = min(c.chunk, n - r0);
     const int pc = p0 + r0;   // position of the chunk's first row
     hipLaunchKernelGGL(k_rows_embed, dim3(rows), dim3(256), 0, s, E, a.ids + pc, rows, H, a.vocab, X);
+    int n_part = 0;   // partial slices of the last residual GEMM not yet added to X
     for (int l = 0; l < c.n_layers; ++l) {
       const LayerPtrs& L = c.layers[l];
       const float* wqkv = static_cast<const float*>(L.wqkv);
-      hipLaunchKernelGGL(k_rows_norm, dim3(cdiv(rows, 4)), dim3(256), 0, s, X, (const float*)L.in_norm, rows, H,
-                         a.eps, A);
+      if (!launch_rows_norm(X, PART, n_part, (const float*)L.in_norm, rows, H, a.eps, A, s))
+        return fail(WSG_ERR_UNSUPPORTED, "row norm shape");
       if (!launch_gemm(A, wqkv, QKV, rows, Q + 2 * KV, H, false, s)) return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
       hipLaunchKernelGGL(k_rows_qkv, dim3(cdiv(nq + 2 * nkv, 4), rows), dim3(256), 0, s, QKV, rows, nq, nkv, pc,
                          a.cap, a.eps, (const float*)L.q_norm, (const float*)L.k_norm, a.rope_cos, a.rope_sin,
@@ -450,15 +663,15 @@ wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, hipStream_t s)
                                    (const float*)L.v_cache, rows, nq, nkv, pc, a.cap, O); break;
         default: return fail(WSG_ERR_UNSUPPORTED, "chunked prefill supports query groups of 1 or 2");
       }
-      if (!launch_gemm(O, static_cast<const float*>(L.wo), X, rows, H, Q, true, s))
-        return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
-      hipLaunchKernelGGL(k_rows_norm, dim3(cdiv(rows, 4)), dim3(256), 0, s, X, (const float*)L.post_norm, rows, H,
-                         a.eps, A);
+      n_part = launch_gemm_residual(O, static_cast<const float*>(L.wo), X, PART, rows, H, Q, s);
+      if (n_part < 0) return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
+      if (!launch_rows_norm(X, PART, n_part, (const float*)L.post_norm, rows, H, a.eps, A, s))
+        return fail(WSG_ERR_UNSUPPORTED, "row norm shape");
       if (!launch_gemm(A, static_cast<const float*>(L.wgu), GU, rows, 2 * I, H, false, s))
         return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
       hipLaunchKernelGGL(k_rows_swiglu, dim3(min(cdiv(rows * I, 256), 4096)), dim3(256), 0, s, GU, rows, I, ACT);
-      if (!launch_gemm(ACT, static_cast<const float*>(L.wd), X, rows, H, I, true, s))
-        return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
+      n_part = launch_gemm_residual(ACT, static_cast<const float*>(L.wd), X, PART, rows, H, I, s);
+      if (n_part < 0) return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
     }
   }
   launch_set_pos(a.ctrl, p0 + n, s);

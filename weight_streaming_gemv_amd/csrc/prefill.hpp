@@ -14,7 +14,7 @@ namespace wsg {
 // Byte offsets (inside the workspace) of the chunk scratch for C rows.
 struct PrefillLayout {
   int rows = 0;
-  size_t x = 0, a = 0, qkv = 0, o = 0, act = 0, gu = 0, total = 0;
+  size_t x = 0, a = 0, qkv = 0, o = 0, act = 0, gu = 0, part = 0, total = 0;
 };
 
 PrefillLayout prefill_layout(int rows, int H, int I, int Q, int KV, size_t es, size_t base);
