@@ -39,6 +39,7 @@ constexpr int kD = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
+typedef float f4v_t __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ GEMM
 // C[M x N] (+)= A[M x K] . B[N x K]^T, all row-major FP32, K-contiguous
@@ -357,135 +358,157 @@ __global__ __launch_bounds__(256) void k_rows_swiglu(const float* __restrict__ G
 
 // ------------------------------------------------------------ attention
 // Causal attention of chunk rows [0, n) (positions p0 + r) over cached keys
-// 0..p0+r of KV head j, for its G query heads.  Block = 16 rows x G heads
-// of queries and one KV head; keys stream through LDS in tiles of 32.  The
-// query tile shares every K/V tile across its rows (Megakernels, "Chunked
-// prefill for long prompts": query-tiled prefill attention), with an
-// online softmax per query in the log2 domain.  Thread t owns query t/8 of
-// the tile and, for scores, keys t%8 + 8i (i < 4); for the output, dims
-// [16 (t%8), 16 (t%8) + 16) of its query.
-constexpr int kQR = 16;            // query rows per block
-constexpr int kKT = 32;            // keys per tile
-constexpr int kRowPad = kD + 4;
+// 0..p0+r of KV head j, for its G query heads (Megakernels, "Chunked
+// prefill for long prompts": query-tiled prefill attention sharing each K/V
+// tile across the rows of a query tile, online softmax in the log2 domain).
+//
+// Both products run on v_mfma_f32_16x16x4f32, in transposed form so the
+// probabilities never leave registers.  A block holds 64 query vectors
+// (64/G rows x G heads); wave w owns vectors [16w, 16w + 16), vector v =
+// row * G + head.  Per tile of 32 keys (K row-major and V transposed in LDS):
+//   S^T[key][v] = sum_d K[key][d] Q[v][d]     (A = K from LDS, B = Q in registers)
+//   O^T[d][v]  += sum_key V^T[d][key] P^T[key][v]
+// MFMA 16x16x4 layout (lane l): A (row l%16, k slot l/16), B (k slot l/16,
+// col l%16), accumulator register r = (row 4(l/16) + r, col l%16).  For the
+// first product slot q of step s is d = 32q + s; for the second it is key
+// 4q + s of a 16-key half, which is exactly register s of the S^T
+// accumulator of lane l: P^T is the B operand as computed.  Every lane owns
+// one query vector (column l%16), so its softmax state is per lane; a
+// column's 16 keys of a half sit in the 4 lanes l%16 + 16q (xor 16, 32).
+constexpr int kAQV = 64;           // query vectors per block
+constexpr int kAKT = 32;           // keys per tile
+constexpr int kKsRow = kD + 4;     // K tile row (floats): conflict-free 16-byte reads
+constexpr int kVtRow = kAKT + 4;   // V^T tile row
 
 template <int G>
 __global__ __launch_bounds__(256) void k_prefill_attn(const float* __restrict__ QKV, const float* __restrict__ k_cache,
                                                       const float* __restrict__ v_cache, int n, int n_q, int n_kv,
                                                       int p0, int cap, float* __restrict__ O) {
-  constexpr int NQ = kQR * G;       // query vectors per block (32 for G = 2)
-  static_assert(NQ * 8 == 256 || NQ * 8 < 256, "one group of 8 threads per query");
-  __shared__ float Qs[NQ][kRowPad];
-  __shared__ float Ks[kKT][kRowPad];
-  __shared__ float Vs[kKT][kRowPad];
-  __shared__ float Ps[NQ][kKT + 1];
-
+  constexpr int BR = kAQV / G;       // rows per block
+  __shared__ float Ks[kAKT * kKsRow];
+  __shared__ float Vt[kD * kVtRow];
   const int j = blockIdx.y;
-  const int r0 = blockIdx.x * kQR;
-  const int tid = threadIdx.x;
+  const int r0 = blockIdx.x * BR;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lq = lane >> 4;
   const int width = (n_q + 2 * n_kv) * kD;
   const float qscale = kLog2e / sqrtf((float)kD);
 
-  // stage queries: vector qv = rr * G + g  <->  row r0 + rr, head j*G + g
-  for (int e = tid; e < NQ * kD; e += 256) {
-    const int qv = e / kD, d = e - qv * kD;
-    const int rr = qv / G, g = qv - rr * G;
-    const int r = r0 + rr;
-    Qs[qv][d] = r < n ? QKV[(size_t)r * width + (j * G + g) * kD + d] * qscale : 0.f;
-  }
-  const int qv = tid >> 3, sub = tid & 7;
-  const bool active = qv < NQ;
-  const int rr = qv / G;
-  const int my_pos = p0 + r0 + rr;                       // this query's position
-  const int last_row = min(n, r0 + kQR) - 1;
-  const int n_keys = p0 + last_row + 1;                  // keys any row of the tile needs
-
-  float m = -INFINITY, l = 0.f, acc[16];
+  // this lane's query vector
+  const int v = wave * 16 + li;
+  const int rr = v / G, g = v - rr * G;
+  const int row = r0 + rr;
+  const bool row_ok = row < n;
+  const int my_pos = p0 + row;
+  float qf[32];
+  {
+    const float* q = QKV + (size_t)min(row, n - 1) * width + (j * G + g) * kD + 32 * lq;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int t = 0; t < 8; ++t) {
+      const f4_t x = *reinterpret_cast<const f4_t*>(q + 4 * t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qf[4 * t + i] = x[i] * qscale;
+    }
+  }
+  const int last_row = min(n, r0 + BR) - 1;
+  const int n_keys = p0 + last_row + 1;   // keys any row of the block needs
+
+  f4v_t oacc[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) oacc[mt] = f4v_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
 
   const float* kh = k_cache + (size_t)j * cap * kD;
   const float* vh = v_cache + (size_t)j * cap * kD;
-  for (int k0 = 0; k0 < n_keys; k0 += kKT) {
-    __syncthreads();   // previous tile consumed (and queries staged)
-    for (int e = tid * 4; e < kKT * kD; e += 256 * 4) {
-      const int kk = e / kD, d = e - kk * kD;
-      const int key = k0 + kk;
-      float4 kv4 = make_float4(0.f, 0.f, 0.f, 0.f), vv4 = kv4;
-      if (key < n_keys) {
-        kv4 = *reinterpret_cast<const float4*>(kh + (size_t)key * kD + d);
-        vv4 = *reinterpret_cast<const float4*>(vh + (size_t)key * kD + d);
-      }
-      *reinterpret_cast<float4*>(&Ks[kk][d]) = kv4;
-      *reinterpret_cast<float4*>(&Vs[kk][d]) = vv4;
-    }
-    __syncthreads();
-    // scores of this thread's query against keys sub + 8i
-    float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = 0.f;
-    if (active) {
-      for (int d = 0; d < kD; d += 4) {
-        const float4 q4 = *reinterpret_cast<const float4*>(&Qs[qv][d]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 k4 = *reinterpret_cast<const float4*>(&Ks[sub + 8 * i][d]);
-          s[i] = fmaf(q4.x, k4.x, fmaf(q4.y, k4.y, fmaf(q4.z, k4.z, fmaf(q4.w, k4.w, s[i]))));
-        }
-      }
-    }
-    float tmax = -INFINITY;
+  // tile staging: K float4 #(tid + 256i) = (key idx/32, dims 4(idx%32)); V
+  // float4 #(tid + 256i) = (key idx%32, dims 4(idx/32)), so the transposed
+  // LDS writes of a wave hit consecutive banks.  Keys past the cache are
+  // clamped into it (loaded, masked).
+  f4_t kr[4], vr[4];
+#define WSG_ATTN_LOAD(K0)                                                                         \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
+    const int idx = tid + 256 * i;                                                                \
+    const int kk = min((K0) + (idx >> 5), cap - 1), kv = min((K0) + (idx & 31), cap - 1);         \
+    kr[i] = *reinterpret_cast<const f4_t*>(kh + (size_t)kk * kD + 4 * (idx & 31));                \
+    vr[i] = *reinterpret_cast<const f4_t*>(vh + (size_t)kv * kD + 4 * (idx >> 5));                \
+  }
+  WSG_ATTN_LOAD(0)
+  for (int k0 = 0; k0 < n_keys; k0 += kAKT) {
+    __syncthreads();   // previous tile consumed
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = k0 + sub + 8 * i;
-      if (!(active && key <= my_pos)) s[i] = -INFINITY;   // causal mask (and keys past the tile's end)
-      tmax = fmaxf(tmax, s[i]);
+      const int idx = tid + 256 * i;
+      *reinterpret_cast<f4_t*>(&Ks[(idx >> 5) * kKsRow + 4 * (idx & 31)]) = kr[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Vt[(4 * (idx >> 5) + e) * kVtRow + (idx & 31)] = vr[i][e];
     }
-    // max over the 8 threads of this query (lanes 8q..8q+7 of one wave)
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 1));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 2));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 4));
-    const float mn = fmaxf(m, tmax);
-    // a query with no key yet in this tile keeps m = -inf: guard the rescale
+    __syncthreads();
+    // next tile in flight during the MFMAs (the last iteration reloads an
+    // in-bounds tile, unused, to keep the loop free of branches)
+    WSG_ATTN_LOAD(min(k0 + kAKT, n_keys - 1))
+#undef WSG_ATTN_LOAD
+
+    // S^T for the two 16-key halves
+    f4v_t sacc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sacc[h] = f4v_t{0.f, 0.f, 0.f, 0.f};
+      const float* krow = &Ks[(16 * h + li) * kKsRow + 32 * lq];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const f4_t a4 = *reinterpret_cast<const f4_t*>(krow + 4 * t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sacc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[i], qf[4 * t + i], sacc[h], 0, 0, 0);
+      }
+    }
+    // causal mask, tile max per query vector
+    float mx = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + 16 * h + 4 * lq + r;
+        if (!(row_ok && key <= my_pos)) sacc[h][r] = -INFINITY;
+        mx = fmaxf(mx, sacc[h][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    // a vector with no key yet keeps m = -inf: guard the rescale
     const float alpha = mn == -INFINITY ? 1.f : exp2f(m - mn);
     float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = mn == -INFINITY ? 0.f : exp2f(s[i] - mn);
-      psum += p;
-      if (active) Ps[qv][sub + 8 * i] = p;
-    }
-    psum += __shfl_xor(psum, 1);
-    psum += __shfl_xor(psum, 2);
-    psum += __shfl_xor(psum, 4);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = mn == -INFINITY ? 0.f : exp2f(sacc[h][r] - mn);
+        sacc[h][r] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
     l = l * alpha + psum;
     m = mn;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] *= alpha;
-    __syncthreads();
-    if (active) {
-      for (int kk = 0; kk < kKT; ++kk) {
-        const float p = Ps[qv][kk];
+    for (int mt = 0; mt < 8; ++mt) oacc[mt] *= alpha;
+    // O^T += V^T P^T
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(&Vs[kk][16 * sub + 4 * q4]);
-          acc[4 * q4] = fmaf(p, v4.x, acc[4 * q4]);
-          acc[4 * q4 + 1] = fmaf(p, v4.y, acc[4 * q4 + 1]);
-          acc[4 * q4 + 2] = fmaf(p, v4.z, acc[4 * q4 + 2]);
-          acc[4 * q4 + 3] = fmaf(p, v4.w, acc[4 * q4 + 3]);
-        }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const f4_t a4 = *reinterpret_cast<const f4_t*>(&Vt[(16 * mt + li) * kVtRow + 16 * h + 4 * lq]);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+          oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[s2], sacc[h][s2], oacc[mt], 0, 0, 0);
       }
-    }
   }
-  if (active) {
-    const int r = r0 + rr, g = qv - rr * G;
-    if (r < n) {
-      const float inv = 1.0f / l;
-      float* o = O + (size_t)r * n_q * kD + (j * G + g) * kD + 16 * sub;
+  if (row_ok) {
+    // lane holds O^T[d = 16mt + 4lq + r][its vector]
+    const float inv = 1.0f / l;
+    float* o = O + (size_t)row * n_q * kD + (j * G + g) * kD + 4 * lq;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<float4*>(o + 4 * q4) =
-            make_float4(acc[4 * q4] * inv, acc[4 * q4 + 1] * inv, acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv);
-    }
+    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f4_t*>(o + 16 * mt) = oacc[mt] * inv;
   }
 }
 
@@ -655,7 +678,7 @@ wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, hipStream_t s)
                          a.cap, a.eps, (const float*)L.q_norm, (const float*)L.k_norm, a.rope_cos, a.rope_sin,
                          (float*)L.k_cache, (float*)L.v_cache);
       if (l == c.n_layers - 1) break;   // only the K/V of the last layer has a consumer
-      const dim3 ag(cdiv(rows, kQR), nkv);
+      const dim3 ag(cdiv(rows, kAQV / G), nkv);
       switch (G) {
         case 1: hipLaunchKernelGGL((k_prefill_attn<1>), ag, dim3(256), 0, s, QKV, (const float*)L.k_cache,
                                    (const float*)L.v_cache, rows, nq, nkv, pc, a.cap, O); break;
