@@ -39,7 +39,7 @@ STAGE_KERNEL = {"qkv": "k_qkv", "attn": "k_attn", "o": "k_gemv_residual", "gateu
 # HBM bytes per launch of the roofline kernel from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs, scaled by a plain-copy calibration (FETCH x 2.0, WRITE x
 # 1.0); valid only for the kernel source they were measured on.
-HEAD_TRAFFIC = {"bytes": 624_127_000, "k_head_sha256_16": "1275e0bbece696c0"}
+HEAD_TRAFFIC = {"bytes": 624_892_960, "k_head_sha256_16": "25a1ac90d77b159c"}
 
 
 def head_traffic():
@@ -48,7 +48,7 @@ def head_traffic():
     import re
     try:
         src = open(os.path.join(ROOT, "weight_streaming_gemv_amd", "csrc", "decode.hip")).read()
-        m = re.search(r"__global__ __launch_bounds__\(kBlock\) void k_head\(.*?\n}\n", src, re.S)
+        m = re.search(r"__global__ __launch_bounds__\([^)]*\) void k_head\(.*?\n}\n", src, re.S)
         h = hashlib.sha256(m.group(0).encode()).hexdigest()[:16] if m else None
     except OSError:
         h = None
@@ -97,7 +97,7 @@ def validate(model, orc, prompt, n_out):
         g = got.float().cpu().numpy().astype(np.float64)
         r = np.asarray(ref_, dtype=np.float64)
         err = np.abs(g - r)
-        if np.any(err > 1e-3 + 1e-3 * np.abs(r)):
+        if not np.all(err <= 1e-3 + 1e-3 * np.abs(r)):   # NaN fails
             raise RuntimeError(f"validation failed: {what} off by {err.max():.3e}")
         return float(err.max())
 
@@ -153,6 +153,12 @@ def gemv_sweep(rounds=15, quick=False):
     gen.manual_seed(100)
     out = {}
 
+    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def ceiling_read(buf):
+        # read-only streaming reference over the same copies (16-byte loads)
+        return lambda: wsg.stream_read(buf, out=sink, stream=s)
+
     def time_graph(fn_list):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
@@ -201,6 +207,7 @@ def gemv_sweep(rounds=15, quick=False):
             r = run(f"{dt_name}", bytes_per, n, make, (1, 2, 4, 8), (1, 2), GRIDS if M > 100000 else (0,))
             # warm: one matrix, reused n times
             r["warm_T1"] = run("warm", bytes_per, n, lambda c, T, R, G: make(0, T, R, G), (1,), (1,))["T1_R1_G0"]
+            r["ceiling"] = run("ceiling", bytes_per, n, lambda c, T, R, G: ceiling_read(W[c]), (1,), (1,))["T1_R1_G0"]
             out[f"{dt_name}_{M}x{K}"] = {"bytes": bytes_per, "copies": n, **r}
             del W, X, Y
             torch.cuda.empty_cache()
@@ -217,10 +224,59 @@ def gemv_sweep(rounds=15, quick=False):
         log(f"sweep q4g64 {M}x{K}: {n} copies")
         r = run("q4", bytes_per, n, make, (1, 2, 4, 8), (1, 2), (0, 256, 512))
         r["warm_T1"] = run("warm", bytes_per, n, lambda c, T, R, G: make(0, T, R, G), (1,), (1,))["T1_R1_G0"]
+        # the int4 ceiling reads the packed words (the scales add 1/32 of their bytes)
+        r["ceiling"] = run("ceiling", M * K // 2, n, lambda c, T, R, G: ceiling_read(Wq[c]), (1,), (1,))["T1_R1_G0"]
         out[f"q4g64_{M}x{K}"] = {"bytes": bytes_per, "copies": n, **r}
         del Wq, S, X, Y
         torch.cuda.empty_cache()
     return out
+
+
+def cpu_gemv_rates(copies=2):
+    """The oracle's GEMVs on the host cores: one call on each of `copies` host-generated
+    matrices (T=1), effective GB/s = weight bytes / median call time.  A bounded sample: the
+    four per-layer shapes in FP32 and FP16 and the smallest int4 shape (the vocabulary and the
+    two large int4 shapes would add minutes of CPU time at the same rates); one untimed call
+    first pages in the BLAS library."""
+    import oracle
+    from synth import GEMV_SHAPES, Q4_SHAPES, gemv_inputs, q4g64_inputs
+    W, X = gemv_inputs(256, 256, 1, seed=5)
+    oracle.gemv(W, X)
+    res = {}
+    for dt_name, dt, es in (("f32", np.float32, 4), ("f16", np.float16, 2)):
+        for (M, K) in GEMV_SHAPES[:4]:
+            ts = []
+            for c in range(copies):
+                W, X = gemv_inputs(M, K, 1, seed=5, copy=c, dtype=dt)
+                t = time.perf_counter()
+                oracle.gemv(W, X)
+                ts.append(time.perf_counter() - t)
+            res[f"{dt_name}_{M}x{K}"] = round(M * K * es / statistics.median(ts) / 1e9, 3)
+    M, K = Q4_SHAPES[0]
+    ts = []
+    for c in range(copies):
+        _, words, scales, X = q4g64_inputs(M, K, 1, seed=5, copy=c)
+        t = time.perf_counter()
+        oracle.gemv_q4g64(words, scales, X, K)
+        ts.append(time.perf_counter() - t)
+    res[f"q4g64_{M}x{K}"] = round((M * K // 2 + M * (K // 64) * 2) / statistics.median(ts) / 1e9, 4)
+    return {"gbps": res, "cores": cpu_threads(), "kind": "oracle", "copies": copies,
+            "sample": "per-layer shapes (FP32, FP16) and int4 4096x4096, T=1"}
+
+
+def host_info():
+    """The host cores the CPU figures ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"affinity_cpus": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(), "cpu_model": model,
+            "blas_threads": cpu_threads()}
 
 
 def sweep_summary(sw):
@@ -235,6 +291,8 @@ def sweep_summary(sw):
                 best[f"{key}_T{T}"] = {"R": int(k.split("_R")[1].split("_")[0]), "grid": int(k.split("_G")[1]), "us": us,
                                        "gbps": round(r["bytes"] / us / 1e3, 1),
                                        "frac": round(r["bytes"] / us / 1e3 / HBM_PEAK_GBPS, 4)}
+                if "ceiling" in r:
+                    best[f"{key}_T{T}"]["frac_of_stream_ceiling"] = round(r["bytes"] / us / 1e3 / r["ceiling"]["gbps"], 4)
     agg = {}
     for dt in ("f32", "f16"):
         names = ["4096x1024", "1024x2048", "6144x1024", "1024x3072", "151936x1024"]
@@ -245,6 +303,10 @@ def sweep_summary(sw):
             t = sum(wi * best[f"{dt}_{n}_T1"]["us"] for wi, n in zip(w, names))
             agg[dt] = {"gbps": round(b / t / 1e3, 1), "frac": round(b / t / 1e3 / HBM_PEAK_GBPS, 4),
                        "us_per_token": round(t, 1)}
+            if all("ceiling" in sw[f"{dt}_{n}"] for n in names):
+                tc = sum(wi * sw[f"{dt}_{n}"]["ceiling"]["us"] for wi, n in zip(w, names))
+                agg[dt]["stream_ceiling_gbps"] = round(b / tc / 1e3, 1)
+                agg[dt]["frac_of_stream_ceiling"] = round(tc / t, 4)
     return best, agg
 
 
@@ -273,7 +335,7 @@ def long_context(torch, wsg, shape, w, validate_outputs=32, trials=5, warmup=2):
         g = got.float().cpu().numpy().astype(np.float64)
         r = np.asarray(ref, dtype=np.float64)
         err = np.abs(g - r)
-        if np.any(err > tol + tol * np.abs(r)):
+        if not np.all(err <= tol + tol * np.abs(r)):     # NaN fails
             raise RuntimeError(f"long-context validation failed: {what} off by {err.max():.3e}")
         return float(err.max())
 
@@ -366,10 +428,37 @@ def long_context(torch, wsg, shape, w, validate_outputs=32, trials=5, warmup=2):
         "heldout_median": {"ttft_ms": round(statistics.median(r[0] for r in rec) * 1e3, 2),
                            "decode_tok_s": round(statistics.median(1023 / r[1] for r in rec), 1),
                            "total_s": round(statistics.median(r[2] for r in rec), 3)},
+        "heldout_prefill_mfma": prefill_mfma(shape, 4096, statistics.median(r[0] for r in rec)),
         "validation": {"max_abs_logit_err": max_logit, "max_abs_kv_err": max_kv,
                        "oracle_checked_outputs": validate_outputs, "timed_runs_token_exact": True},
         "cpu_oracle_decode_tok_s_at_4k": round((validate_outputs - 1) / t_or, 3) if t_or else None,
     }
+
+
+MFMA_FP32_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
+
+
+def prefill_mfma(shape, n, ttft_s):
+    """Effective FP32 matrix throughput of a timed prefill: chunked-prefill flops / TTFT (a
+    lower bound: TTFT also holds the last row's decode forward and the head)."""
+    f = prefill_flops(shape, n)
+    tf = f / ttft_s / 1e12
+    return {"flops": f, "tflops": round(tf, 1), "peak_tflops": MFMA_FP32_PEAK_TFLOPS,
+            "frac": round(tf / MFMA_FP32_PEAK_TFLOPS, 3)}
+
+
+def prefill_flops(shape, n):
+    """FP32 flops of the chunked part of a prefill of n ids (rows 0..n-2; the last row runs
+    the decode path): 2 per weight per row for the projections (the last layer runs only its
+    QKV projection, its K/V being the only output with a consumer), and 4*head_dim per
+    (query head, visible key) pair for QK^T and PV in the layers before the last."""
+    rows = n - 1
+    h, i, q, kv, nl = shape.hidden, shape.intermediate, shape.q_width, shape.kv_width, shape.n_layers
+    per_layer = (q + 2 * kv) * h + h * q + 2 * i * h + h * i
+    proj = 2 * rows * (per_layer * (nl - 1) + (q + 2 * kv) * h)
+    pairs = rows * (rows + 1) // 2
+    attn = 4 * shape.head_dim * shape.n_q_heads * pairs * (nl - 1)
+    return proj + attn
 
 
 def main(argv=None):
@@ -525,6 +614,7 @@ def main(argv=None):
                         "max_abs_kv_err": max(e[1] for e in errs.values()), "rtol": 1e-3, "atol": 1e-3}
                        if errs else {"status": "skipped"}),
         "graphs": not args.no_graph,
+        "host": host_info(),
         "long_context": long_res,
     }
     model.close()
@@ -534,7 +624,12 @@ def main(argv=None):
         sw = gemv_sweep(quick=args.sweep == "quick")
         best, agg = sweep_summary(sw)
         out["gemv_cold"] = {"best": best, "decode_mix": agg, "note": "dispatch-inclusive (graph replay) per-dispatch "
-                            "time over >= 1 GiB of distinct matrices per shape; median of 15 rounds"}
+                            "time over >= 1 GiB of distinct matrices per shape; median of 15 rounds; stream ceiling "
+                            "= a read-only 16-byte-load kernel over the same copies"}
+        if not args.no_oracle:
+            t = time.perf_counter()
+            out["gemv_cold"]["cpu_oracle"] = cpu_gemv_rates()
+            log(f"oracle GEMVs on the host in {time.perf_counter() - t:.1f} s")
         with open(os.path.join(ROOT, "gpurun_out", "gemv_sweep.json") if os.path.isdir(
                 os.path.join(ROOT, "gpurun_out")) else os.devnull, "w") as f:
             json.dump(sw, f, indent=1)

@@ -174,10 +174,14 @@ enum { WSG_OPT_USE_GRAPH = 1, WSG_OPT_TIMED_STAGE = 2 };
  * WSG_OPT_ROWS_ATTN_O: output-projection rows per wave in the fused launch
  * (4 or 8, default 8). */
 enum { WSG_OPT_FUSE_ATTN_O = 3, WSG_OPT_ROWS_ATTN_O = 15 };
+/* WSG_OPT_HEAD_WAVES: waves per workgroup of the head launch (4, 8 or 16,
+ * default 4); each workgroup writes one argmax key, so larger workgroups
+ * leave fewer keys for the final argmax launch. */
+enum { WSG_OPT_HEAD_WAVES = 16 };
 /* Launch shape of the decode GEMV stages (tuning): rows per wave (1, 2 or
  * 4) and blocks of 256 threads (0 = one row group per wave; fewer blocks
- * loop over row groups; the head is capped at 4096 blocks).  Defaults:
- * 1 row per wave, one-shot grids, 4096 head blocks. */
+ * loop over row groups; the head is capped at 40960 blocks).  Defaults:
+ * 1 row per wave, one-shot grids. */
 enum { WSG_OPT_ROWS_QKV = 10, WSG_OPT_ROWS_O = 11, WSG_OPT_ROWS_GATEUP = 12, WSG_OPT_ROWS_DOWN = 13,
        WSG_OPT_ROWS_HEAD = 14, WSG_OPT_GRID_QKV = 20, WSG_OPT_GRID_O = 21, WSG_OPT_GRID_GATEUP = 22,
        WSG_OPT_GRID_DOWN = 23, WSG_OPT_GRID_HEAD = 24 };
@@ -238,6 +242,15 @@ wsg_status wsg_gemv_q4g64_ex(int32_t M, int32_t K, int32_t T, int32_t rows_per_w
  * tiled one.  Asynchronous on hip_stream. */
 wsg_status wsg_gemm_nt_f32(int32_t M, int32_t N, int32_t K, const float* d_A, const float* d_B, float* d_C,
                            int32_t accumulate, void* hip_stream);
+
+/* Read-only streaming reference for the cold-cache GEMV measurements (Our
+ * Kernel Benchmark Was Measuring the System Cache, "The fix": the GEMV is
+ * judged against what a plain read of the same cycling buffers reaches).
+ * Reads all `bytes` of d_buf (16-byte aligned, bytes a positive multiple of
+ * 16) once with 16-byte loads, one 4 KiB segment per wave; writes nothing
+ * in practice (d_out, one float, is written only if the sum equals an
+ * improbable constant).  Asynchronous on hip_stream. */
+wsg_status wsg_stream_read(const void* d_buf, int64_t bytes, float* d_out, void* hip_stream);
 
 /* Message for the last error on this host thread ("" if none). */
 const char* wsg_last_error(void);

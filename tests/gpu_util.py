@@ -30,14 +30,17 @@ def gemv_bound(abs_prod_sum: np.ndarray, k: int, factor: float = 2.0) -> np.ndar
 
 
 def close_rel(got, ref, rtol, atol):
-    """Elementwise |got - ref| <= atol + rtol |ref|; returns (ok, max_abs_err, worst_index)."""
+    """Elementwise |got - ref| <= atol + rtol |ref|, a non-finite value never passing;
+    returns (ok, max_abs_err, worst_index)."""
     g = np.asarray(got, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     err = np.abs(g - r)
     lim = atol + rtol * np.abs(r)
-    bad = err > lim
-    worst = int(np.argmax(err - lim)) if err.size else -1
-    return (not bad.any()), float(err.max() if err.size else 0.0), worst
+    bad = ~(err <= lim)            # NaN compares false: counted as bad
+    if not err.size:
+        return True, 0.0, -1
+    worst = int(np.argmax(np.where(np.isnan(err), np.inf, err - lim)))
+    return (not bad.any()), float(np.nanmax(err) if not np.isnan(err).all() else np.nan), worst
 
 
 def _np(t):
@@ -78,7 +81,8 @@ def lockstep(model, orc, prompt, n_out, rtol=1e-3, atol=1e-3, teacher=False, lab
     ck.kv(0, orc.pos, 0)
     toks, rtoks = [tok], [rtok]
     if not teacher:
-        assert tok == rtok, f"{label}: first token {tok} != {rtok} (oracle margin {orc.logits_margin(ref):.3e})"
+        assert tok == rtok, (f"{label}: first token {tok} != {rtok} (oracle margin {orc.logits_margin(ref):.3e}; "
+                             f"argmax of the GPU logits {int(np.argmax(_np(model.logits())))})")
     for s in range(1, n_out):
         p = orc.pos
         tok = model.step(rtoks[-1] if teacher else -1)
@@ -87,7 +91,8 @@ def lockstep(model, orc, prompt, n_out, rtol=1e-3, atol=1e-3, teacher=False, lab
         ck.logits(ref, s)
         ck.kv(p, p + 1, s)
         if not teacher:
-            assert tok == rtok, f"{label}: step {s} token {tok} != {rtok} (margin {orc.logits_margin(ref):.3e})"
+            assert tok == rtok, (f"{label}: step {s} token {tok} != {rtok} (margin {orc.logits_margin(ref):.3e}; "
+                                 f"argmax of the GPU logits {int(np.argmax(_np(model.logits())))})")
         toks.append(tok)
         rtoks.append(rtok)
     ck.kv(0, orc.pos, n_out)

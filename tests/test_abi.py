@@ -45,6 +45,12 @@ def test_gemv_argument_validation(abi):
     assert b"aligned" in L.wsg_last_error()
     assert L.wsg_gemv_q4g64(8, 100, 1, 1, 16, 16, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
     assert L.wsg_gemv_q4g64(8, 128, 1, 1, 16, 17, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
+    # streaming reference: null, size not a multiple of 16, misaligned buffer
+    assert L.wsg_stream_read(None, 64, 16, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_stream_read(16, 64, None, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_stream_read(16, 60, 16, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_stream_read(16, 0, 16, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_stream_read(24, 64, 16, None) == abi.WSG_ERR_INVALID_ARG
 
 
 def _cfg(abi, shape, cap=16, dtype=0, chunk=0):

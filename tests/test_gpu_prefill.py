@@ -77,6 +77,24 @@ def test_mini_chunked_prefill(mini_w, n_prompt, chunk):
     m.close()
 
 
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_stale_cache_never_leaks(mini_w, chunk):
+    """Cache slots past the valid length hold whatever the allocator left there: a
+    masked key still enters the prefill PV product with weight 0, so it must not be
+    read as a value (0 * Inf = NaN).  Every slot is poisoned with NaN first."""
+    import weight_streaming_gemv_amd as wsg
+    cap = 160
+    m = wsg.Model(MINI, mini_w, max_context=cap, prefill_chunk=64)
+    m.set_prefill_chunk(chunk)
+    for l in range(MINI.n_layers):
+        k, v, _ = m.kv(l)
+        k.fill_(float("nan"))
+        v.fill_(float("inf"))
+    orc = oracle.OracleModel(MINI, mini_w, cap)
+    lockstep(m, orc, prompt_ids(14, 45, MINI.vocab), 3, label=f"poisoned cache c={chunk}")
+    m.close()
+
+
 def test_mini_chunked_matches_tokenwise_and_continues(mini_w):
     """Chunked and tokenwise prefill agree; a second prefill call continues the sequence."""
     import weight_streaming_gemv_amd as wsg

@@ -20,7 +20,7 @@ from ._abi import (WSG_F16, WSG_F32, WSG_GEMV_NONTEMPORAL, WSG_OPT_TIMED_STAGE, 
 
 __all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "gemm_nt", "WsgError", "WSG_F32", "WSG_F16",
            "WSG_STAGE_QKV", "WSG_STAGE_ATTN", "WSG_STAGE_O", "WSG_STAGE_GATEUP", "WSG_STAGE_DOWN",
-           "WSG_STAGE_HEAD", "WSG_OPT_USE_GRAPH", "WSG_OPT_TIMED_STAGE", "WSG_GEMV_NONTEMPORAL", "lib"]
+           "WSG_STAGE_HEAD", "WSG_OPT_USE_GRAPH", "WSG_OPT_TIMED_STAGE", "WSG_GEMV_NONTEMPORAL", "stream_read", "lib"]
 
 lib = _abi.lib
 lib()  # fail loudly at import when libwsg.so is missing
@@ -76,6 +76,16 @@ def gemm_nt(A, B, C=None, accumulate: bool = False, stream=None):
     check(_abi.lib().wsg_gemm_nt_f32(M, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(), int(accumulate),
                                      _stream_handle(stream)))
     return C
+
+
+def stream_read(buf, out=None, stream=None):
+    """Read every byte of a 16-byte-aligned device tensor once (streaming reference)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=buf.device)
+    check(_abi.lib().wsg_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(),
+                                     _stream_handle(stream)))
+    return out
 
 
 # ---------------------------------------------------------------- model

@@ -17,6 +17,7 @@ WSG_OK, WSG_ERR_INVALID_ARG, WSG_ERR_OUT_OF_RANGE, WSG_ERR_STATE, WSG_ERR_HIP, W
 WSG_F32, WSG_F16 = 0, 1
 WSG_OPT_USE_GRAPH, WSG_OPT_TIMED_STAGE = 1, 2
 WSG_OPT_FUSE_ATTN_O, WSG_OPT_ROWS_ATTN_O = 3, 15
+WSG_OPT_HEAD_WAVES = 16
 WSG_OPT_ROWS = {"qkv": 10, "o": 11, "gateup": 12, "down": 13, "head": 14}
 WSG_OPT_GRID = {"qkv": 20, "o": 21, "gateup": 22, "down": 23, "head": 24}
 WSG_STAGE_QKV, WSG_STAGE_ATTN, WSG_STAGE_O, WSG_STAGE_GATEUP, WSG_STAGE_DOWN, WSG_STAGE_HEAD = range(6)
@@ -79,6 +80,7 @@ _SIGS = {
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "wsg_gemm_nt_f32": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_int32, C.c_void_p]),
+    "wsg_stream_read": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
     "wsg_last_error": (C.c_char_p, []),
     "wsg_version": (C.c_char_p, []),
 }

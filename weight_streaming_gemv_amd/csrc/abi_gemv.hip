@@ -79,3 +79,13 @@ extern "C" wsg_status wsg_gemm_nt_f32(int32_t M, int32_t N, int32_t K, const flo
     return fail(WSG_ERR_UNSUPPORTED, "wsg_gemm_nt_f32: shape not supported");
   return check_launch("wsg_gemm_nt_f32");
 }
+
+extern "C" wsg_status wsg_stream_read(const void* d_buf, int64_t bytes, float* d_out, void* hip_stream) {
+  clear_error();
+  if (!d_buf || !d_out) return fail(WSG_ERR_INVALID_ARG, "wsg_stream_read: null pointer");
+  if (bytes < 16 || bytes % 16 != 0) return fail(WSG_ERR_INVALID_ARG, "wsg_stream_read: bytes must be a positive multiple of 16");
+  if ((uintptr_t)d_buf & 15) return fail(WSG_ERR_INVALID_ARG, "wsg_stream_read: buffer must be 16-byte aligned");
+  if (bytes / (16 * 4096) > (int64_t)0x7fffffff) return fail(WSG_ERR_UNSUPPORTED, "wsg_stream_read: buffer too large");
+  stream_read_dispatch(d_buf, bytes, d_out, static_cast<hipStream_t>(hip_stream));
+  return check_launch("wsg_stream_read");
+}

@@ -350,24 +350,25 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
 // generation").  A single fused launch would need a device-scope release
 // fence per block, and on this multi-XCD part each such fence writes back
 // the issuing XCD's L2, which costs far more than the extra launch.
-template <typename TS, int H, int R>
-__global__ __launch_bounds__(kBlock) void k_head(const TS* __restrict__ E, const TS* __restrict__ final_norm,
-                                                 const TS* __restrict__ x_res, float eps, TS* __restrict__ logits,
-                                                 int V, unsigned long long* __restrict__ am_part) {
-  __shared__ unsigned long long best_wave[kWavesPerBlock];
+template <typename TS, int H, int R, int WPB>
+__global__ __launch_bounds__(WPB * kWave) void k_head(const TS* __restrict__ E, const TS* __restrict__ final_norm,
+                                                      const TS* __restrict__ x_res, float eps, TS* __restrict__ logits,
+                                                      int V, unsigned long long* __restrict__ am_part) {
+  __shared__ unsigned long long best_wave[WPB];
   const int lane = lane_id();
   const int ngroups = ceil_div(V, R);
-  int g = wave_row_groups_begin();
+  int g = blockIdx.x * WPB + wave_id();
+  const int stride = gridDim.x * WPB;
   WRows<TS, H, R> w;
   if (g < ngroups) w.load(E, g * R, V);   // first rows in flight before the norm
   Act<TS, H> x;
   x.load(x_res);
   x.rms_norm(final_norm, eps);
   unsigned long long best = 0;   // below every real key
-  for (; g < ngroups; g += wave_row_groups_stride()) {
+  for (; g < ngroups; g += stride) {
     float acc[R];
     w.dot(x, acc);
-    const int next = g + wave_row_groups_stride();
+    const int next = g + stride;
     if (next < ngroups) w.load(E, next * R, V);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -386,16 +387,32 @@ __global__ __launch_bounds__(kBlock) void k_head(const TS* __restrict__ E, const
   if (threadIdx.x == 0) {
     unsigned long long b = best_wave[0];
 #pragma unroll
-    for (int w2 = 1; w2 < kWavesPerBlock; ++w2) b = best_wave[w2] > b ? best_wave[w2] : b;
+    for (int w2 = 1; w2 < WPB; ++w2) b = best_wave[w2] > b ? best_wave[w2] : b;
     am_part[blockIdx.x] = b;
   }
 }
 
+// One block of 1024 threads reads the n block keys (n even: the head grid
+// is rounded up to an even count, a block without rows writes key 0) as
+// 16-byte pairs: thread t takes pairs t + 1024k for k < PER, all loads
+// issued before the first compare; pair indices past the last are clamped
+// to it instead of branched on (a repeated key cannot change a maximum).
+template <int PER>
 __global__ __launch_bounds__(1024) void k_argmax(const unsigned long long* __restrict__ am_part, int n,
                                                  int32_t* __restrict__ ctrl, int32_t* __restrict__ ids) {
   __shared__ unsigned long long red[1024 / kWave];
+  typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
+  const u64x2_t* pairs = reinterpret_cast<const u64x2_t*>(am_part);
+  const int last = n / 2 - 1;
+  u64x2_t k[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) k[i] = pairs[min((int)threadIdx.x + 1024 * i, last)];
   unsigned long long b = 0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) b = am_part[i] > b ? am_part[i] : b;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    b = k[i].x > b ? k[i].x : b;
+    b = k[i].y > b ? k[i].y : b;
+  }
   b = wave_max_u64(b);
   if (lane_id() == 0) red[threadIdx.x >> 6] = b;
   __syncthreads();
@@ -836,9 +853,13 @@ int blocks_for(int M, int R, int grid) {
   return (grid > 0 && grid < one_shot) ? grid : one_shot;
 }
 
-int head_grid(int V, int R, int grid) {
-  const int b = blocks_for(V, R, grid);
-  return b < kHeadMaxBlocks ? b : kHeadMaxBlocks;
+// Head blocks: one row group per wave unless fewer are asked for, at most
+// kHeadMaxBlocks, rounded up to an even count (the argmax reads key pairs).
+int head_grid(int V, int R, int waves, int grid) {
+  const int one_shot = ceil_div(ceil_div(V, R), waves);
+  int b = (grid > 0 && grid < one_shot) ? grid : one_shot;
+  b = b < kHeadMaxBlocks ? b : kHeadMaxBlocks;
+  return (b + 1) & ~1;
 }
 
 // K values compiled in; a K must also be a multiple of 64 16-byte vectors
@@ -940,13 +961,22 @@ bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bo
 
 template <typename TS>
 bool head_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
-  const int grid = head_grid(a.vocab, sh.rows_head, sh.grid_head);
+  const int grid = head_grid(a.vocab, sh.rows_head, sh.head_waves, sh.grid_head);
   return with_k<TS>(a.hidden, [&](auto kc) {
     return with_r(sh.rows_head, [&](auto rc) {
-      hipLaunchKernelGGL((k_head<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock), 0, s,
-                         (const TS*)a.embed, (const TS*)a.final_norm, (const TS*)a.x, a.eps, (TS*)a.logits, a.vocab,
-                         a.am_part);
-      return true;
+      constexpr int K = decltype(kc)::value, R = decltype(rc)::value;
+      auto go = [&](auto wc) {
+        constexpr int WPB = decltype(wc)::value;
+        hipLaunchKernelGGL((k_head<TS, K, R, WPB>), dim3(grid), dim3(WPB * kWave), 0, s, (const TS*)a.embed,
+                           (const TS*)a.final_norm, (const TS*)a.x, a.eps, (TS*)a.logits, a.vocab, a.am_part);
+        return true;
+      };
+      switch (sh.head_waves) {
+        case 4: return go(IC<4>{});
+        case 8: return go(IC<8>{});
+        case 16: return go(IC<16>{});
+        default: return false;
+      }
     });
   });
 }
@@ -1015,7 +1045,9 @@ bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hi
 
 int attn_o_part_slots(int hidden, int n_kv) { return parts_slots(hidden, n_kv); }
 
-int head_blocks(const DecodeArgs& a, const DecodeShape& sh) { return head_grid(a.vocab, sh.rows_head, sh.grid_head); }
+int head_blocks(const DecodeArgs& a, const DecodeShape& sh) {
+  return head_grid(a.vocab, sh.rows_head, sh.head_waves, sh.grid_head);
+}
 
 bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, hipStream_t s) {
   return a.dtype == 0 ? qkv_t<float>(a, sh, L, first, s) : qkv_t<__half>(a, sh, L, first, s);
@@ -1045,9 +1077,19 @@ bool launch_head(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   return a.dtype == 0 ? head_t<float>(a, sh, s) : head_t<__half>(a, sh, s);
 }
 bool launch_argmax(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax, dim3(1), dim3(1024), 0, s, (const unsigned long long*)a.am_part,
-                     head_blocks(a, sh), a.ctrl, a.ids);
-  return true;
+  const int n = head_blocks(a, sh);
+  const int per = ceil_div(n / 2, 1024);
+  auto go = [&](auto pc) {
+    hipLaunchKernelGGL((k_argmax<decltype(pc)::value>), dim3(1), dim3(1024), 0, s,
+                       (const unsigned long long*)a.am_part, n, a.ctrl, a.ids);
+    return true;
+  };
+  if (per <= 1) return go(IC<1>{});
+  if (per <= 2) return go(IC<2>{});
+  if (per <= 4) return go(IC<4>{});
+  if (per <= 8) return go(IC<8>{});
+  static_assert(kHeadMaxBlocks / 2048 == 20, "pairs per thread at the largest head grid");
+  return go(IC<20>{});
 }
 bool launch_set_pos(int32_t* ctrl, int pos, hipStream_t s) {
   hipLaunchKernelGGL(k_set_pos, dim3(1), dim3(64), 0, s, ctrl, pos);

@@ -13,8 +13,10 @@ enum CtrlWord : int {
   kCtrlWords = 64
 };
 
-// The head kernel runs at most kHeadMaxBlocks blocks (one argmax key each).
-constexpr int kHeadMaxBlocks = 4096;
+// The head kernel runs at most kHeadMaxBlocks blocks (one argmax key each;
+// one row per wave for the 151936-row vocabulary is 37984 blocks); a
+// multiple of 2048 (the argmax block reads key pairs).
+constexpr int kHeadMaxBlocks = 40960;
 
 struct LayerPtrs {
   const void* wqkv;     // [(Q + 2 KV)][H]
@@ -58,6 +60,7 @@ struct DecodeShape {
   int grid_qkv, grid_o, grid_gu, grid_down, grid_head;   // blocks (0 = one row group per wave)
   int attn_splits;                                       // split-K blocks per KV head (grid.x)
   int attn_chunk;                                        // keys per split (a multiple of 16, >= 64)
+  int head_waves;                                        // waves per head block (4, 8 or 16)
   int fuse_attn_o;                                       // one-split contexts: fused attention + output GEMV
   int rows_attn_o;                                       // W_o rows per wave in the fused launch (4 or 8)
 };

@@ -14,4 +14,7 @@ void gemv_dispatch(int dtype, int M, int K, int T, int R, int grid, int flags, c
 void gemv_q4_dispatch(int M, int K, int T, int R, int grid, int flags, const uint32_t* Wq,
                       const void* S, const void* X, float* Y, hipStream_t s);
 
+// Read-only streaming reference: bytes % 16 == 0, bytes >= 16.
+void stream_read_dispatch(const void* buf, int64_t bytes, float* out, hipStream_t s);
+
 }  // namespace wsg

@@ -506,7 +506,8 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   DecodeShape& sh = m->shape;
   sh.rows_qkv = sh.rows_o = sh.rows_gu = sh.rows_down = sh.rows_head = 1;
   sh.grid_qkv = sh.grid_o = sh.grid_gu = sh.grid_down = 0;
-  sh.grid_head = 4096;
+  sh.grid_head = 0;   // one row per wave (the cold-cache sweep's best vocabulary shape)
+  sh.head_waves = 4;
   sh.attn_splits = 1;
   sh.attn_chunk = attn_chunk(d);
   sh.fuse_attn_o = 1;
@@ -645,6 +646,11 @@ wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value) {
     case WSG_OPT_ROWS_ATTN_O:
       if (value != 4 && value != 8) return fail(WSG_ERR_INVALID_ARG, "attention/output rows per wave must be 4 or 8");
       m->shape.rows_attn_o = value;
+      drop_graphs(m);
+      return WSG_OK;
+    case WSG_OPT_HEAD_WAVES:
+      if (value != 4 && value != 8 && value != 16) return fail(WSG_ERR_INVALID_ARG, "head waves must be 4, 8 or 16");
+      m->shape.head_waves = value;
       drop_graphs(m);
       return WSG_OK;
     case WSG_OPT_TIMED_STAGE:

@@ -422,15 +422,20 @@ __global__ __launch_bounds__(256) void k_prefill_attn(const float* __restrict__ 
   const float* vh = v_cache + (size_t)j * cap * kD;
   // tile staging: K float4 #(tid + 256i) = (key idx/32, dims 4(idx%32)); V
   // float4 #(tid + 256i) = (key idx%32, dims 4(idx/32)), so the transposed
-  // LDS writes of a wave hit consecutive banks.  Keys past the cache are
-  // clamped into it (loaded, masked).
+  // LDS writes of a wave hit consecutive banks.  Keys at or past n_keys are
+  // cache slots no row may see (stale memory): their loads are clamped into
+  // the cache and their values replaced by zeros, since a masked key still
+  // enters the PV product with weight 0 (and 0 * Inf is NaN).
   f4_t kr[4], vr[4];
 #define WSG_ATTN_LOAD(K0)                                                                         \
   _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
     const int idx = tid + 256 * i;                                                                \
-    const int kk = min((K0) + (idx >> 5), cap - 1), kv = min((K0) + (idx & 31), cap - 1);         \
+    const int k1 = (K0) + (idx >> 5), k2 = (K0) + (idx & 31);                                     \
+    const int kk = min(k1, cap - 1), kv = min(k2, cap - 1);                                       \
     kr[i] = *reinterpret_cast<const f4_t*>(kh + (size_t)kk * kD + 4 * (idx & 31));                \
     vr[i] = *reinterpret_cast<const f4_t*>(vh + (size_t)kv * kD + 4 * (idx >> 5));                \
+    if (k1 >= n_keys) kr[i] = f4_t{0.f, 0.f, 0.f, 0.f};                                           \
+    if (k2 >= n_keys) vr[i] = f4_t{0.f, 0.f, 0.f, 0.f};                                           \
   }
   WSG_ATTN_LOAD(0)
   for (int k0 = 0; k0 < n_keys; k0 += kAKT) {
