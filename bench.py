@@ -310,6 +310,51 @@ def sweep_summary(sw):
     return best, agg
 
 
+def lossless_bf16(torch, wsg, shape, steps=5, warmup=2):
+    """The short-prompt workload on BF16-representable FP32 weights (the synthetic weights
+    rounded to BF16), decode weights packed losslessly (Megakernels, "Lossless decode-weight
+    storage"): the packed model is validated against the oracle on the same weights, must
+    give the unpacked model's tokens, and both are timed the same way."""
+    import oracle
+    from synth import PROMPT_SEEDS, model_weights_bf16, prompt_ids
+    cap = 48
+    w = model_weights_bf16(shape, seed=0)
+    prompt32 = prompt_ids(PROMPT_SEEDS["short"], 32, shape.vocab)
+    prompts = {8: prompt32[:8], 32: prompt32}
+    packed = wsg.Model(shape, w, max_context=cap, prefill_chunk=32, lossless_pack=True)
+    plain = wsg.Model(shape, w, max_context=cap, prefill_chunk=32)
+    orc = oracle.OracleModel(shape, w, cap)
+    expected, errs = {}, []
+    for n_p in (8, 32):
+        toks, ml, mkv, _ = validate(packed, orc, prompts[n_p], 16)
+        errs.append((ml, mkv))
+        for n_o in (8, 16):
+            expected[(n_p, n_o)] = toks[:n_o]
+    del orc, w
+    res = {}
+    for name, model in (("packed", packed), ("unpacked", plain)):
+        rec = []
+        for i in range(warmup + steps):
+            for (n_p, n_o) in COMBOS:
+                toks, ttft, dec, tot = generate(model, prompts[n_p], n_o)
+                if toks != expected[(n_p, n_o)]:
+                    raise RuntimeError(f"lossless {name} {n_p}/{n_o}: tokens differ from the validated packed run")
+                if i >= warmup:
+                    rec.append((n_o, dec))
+        st = model.storage()
+        res[name] = {"decode_tok_s": round(sum(n - 1 for n, _ in rec) / sum(d for _, d in rec), 2),
+                     "decode_weight_bytes": st["decode_weight_bytes"],
+                     "packed_matrices": f"{st['packed_matrices']}/{st['decode_matrices']}"}
+        model.close()
+    res["speedup"] = round(res["packed"]["decode_tok_s"] / res["unpacked"]["decode_tok_s"], 3)
+    res["validation"] = {"max_abs_logit_err": max(e[0] for e in errs), "max_abs_kv_err": max(e[1] for e in errs),
+                         "unpacked_tokens_identical": True}
+    res["workload"] = ("28-layer FP32 model with BF16-representable weights (seed-0 draws rounded to BF16); "
+                       "prompt/output 8/8, 8/16, 32/8, 32/16; decode projections and the head read the "
+                       "packed copies, prefill the FP32 matrices")
+    return res
+
+
 def long_context(torch, wsg, shape, w, validate_outputs=32, trials=5, warmup=2):
     """Long-document workload (Benchmark methodology, "Long-document chunked prefill").
 
@@ -476,6 +521,8 @@ def main(argv=None):
                     help="run only a 512 MiB device copy (reference for the HBM traffic counters)")
     ap.add_argument("--long", choices=["on", "off", "only"], default="on",
                     help="long-document workload (2048-id chunk selection, 4096 -> 1024 held-out)")
+    ap.add_argument("--lossless", choices=["on", "off", "only"], default="on",
+                    help="short-prompt workload on BF16-representable weights, packed vs unpacked decode")
     ap.add_argument("--no-oracle", action="store_true",
                     help="skip validation and the CPU baseline (profiling runs only; no value is published)")
     args = ap.parse_args(argv)
@@ -541,6 +588,9 @@ def main(argv=None):
         log(f"validation passed: max |dlogit| {max(e[0] for e in errs.values()):.2e}, "
             f"max |dkv| {max(e[1] for e in errs.values()):.2e}")
 
+    if args.lossless == "only":
+        print(json.dumps({"lossless_bf16": lossless_bf16(torch, wsg, shape)}), flush=True)
+        return 0
     long_res = None
     if args.long != "off" and not args.no_oracle:
         long_res = long_context(torch, wsg, shape, w)
@@ -620,6 +670,11 @@ def main(argv=None):
     model.close()
     del model
     torch.cuda.empty_cache()
+    if args.lossless == "on" and not args.no_oracle:
+        t = time.perf_counter()
+        out["lossless_bf16"] = lossless_bf16(torch, wsg, shape)
+        log(f"lossless BF16-in-FP32 section in {time.perf_counter() - t:.1f} s")
+        torch.cuda.empty_cache()
     if args.sweep != "none":
         sw = gemv_sweep(quick=args.sweep == "quick")
         best, agg = sweep_summary(sw)

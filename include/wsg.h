@@ -57,6 +57,7 @@ typedef struct {
   float rms_eps;      /* RMSNorm epsilon, inside the square root */
   float rope_theta;   /* RoPE base; pair i turns by p * theta^(-2i/head_dim) */
   int32_t dtype;      /* wsg_dtype */
+  int32_t lossless_pack;  /* 1: lossless packed copies of the decode weights (FP32 only, see below) */
 } wsg_config;
 
 /* Host-side unpacked weights, element type = cfg.dtype (float32, or IEEE
@@ -83,6 +84,19 @@ typedef struct {
   const void* const* wd;
 } wsg_host_weights;
 
+/* Lossless decode-weight storage (Megakernels, "Lossless decode-weight
+ * storage"): with cfg.lossless_pack = 1 (FP32 models), wsg_pack_weights also
+ * writes a packed copy of each decode matrix (the embedding, read by the
+ * vocabulary head, and per layer W_qkv, W_o, W_gu, W_d) whose values are
+ * all finite with zero low 16 bits and whose element count is even: two
+ * values per 32-bit word (element 2i in the low half, its high 16 bits
+ * stored).  Each copy is verified bitwise by reconstruction; a mismatch
+ * fails the call (WSG_ERR_STATE).  Matrices that do not qualify keep FP32
+ * storage only.  The decode kernels read the packed copies and rebuild each
+ * FP32 value exactly before the same FP32 products, in the same order, so
+ * results are bit-identical to the unpacked model; prefill, activations,
+ * cache and accumulation stay FP32, and the FP32 matrices stay in the image
+ * (the packed copies are an addition). */
 typedef struct wsg_model wsg_model;   /* opaque; one model per stream and host thread */
 
 /* Size in bytes of the packed weight image for cfg (host and device copies
@@ -251,6 +265,12 @@ wsg_status wsg_gemm_nt_f32(int32_t M, int32_t N, int32_t K, const float* d_A, co
  * in practice (d_out, one float, is written only if the sum equals an
  * improbable constant).  Asynchronous on hip_stream. */
 wsg_status wsg_stream_read(const void* d_buf, int64_t bytes, float* d_out, void* hip_stream);
+
+/* Weight storage the decode path reads: matrices with a packed copy (of
+ * 1 + 4 n_layers decode matrices) and the decode weight bytes per token
+ * (packed copies count half). */
+wsg_status wsg_weight_storage(const wsg_model* m, int32_t* packed_matrices, int32_t* decode_matrices,
+                              int64_t* decode_weight_bytes);
 
 /* Message for the last error on this host thread ("" if none). */
 const char* wsg_last_error(void);

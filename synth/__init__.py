@@ -29,7 +29,7 @@ from typing import Dict, List
 import numpy as np
 
 __all__ = [
-    "ModelShape", "QWEN3_0_6B", "MINI", "model_weights", "prompt_ids",
+    "ModelShape", "QWEN3_0_6B", "MINI", "model_weights", "model_weights_bf16", "bf16_representable", "prompt_ids",
     "gemv_inputs", "q4g64_inputs", "pack_int4_rows", "GEMV_SHAPES", "Q4_SHAPES",
     "PROMPT_SEEDS", "WEIGHT_SEED",
 ]
@@ -118,6 +118,25 @@ def model_weights(shape: ModelShape, seed: int = WEIGHT_SEED, dtype=np.float32) 
         layers.append(lw)
     out["layers"] = layers
     return out
+
+
+def bf16_representable(a: np.ndarray) -> np.ndarray:
+    """FP32 copy of ``a`` rounded to the nearest BF16 value (round-to-nearest-even on the
+    high 16 bits): every result has zero low 16 bits.  Finite inputs only."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return r.astype(np.uint32).view(np.float32)
+
+
+def model_weights_bf16(shape: ModelShape, seed: int = WEIGHT_SEED) -> Dict[str, object]:
+    """``model_weights`` with every matrix rounded to BF16-representable FP32 values (the
+    weights of a checkpoint converted from BF16); gains stay 1."""
+    w = model_weights(shape, seed)
+    w["embed"] = bf16_representable(w["embed"])
+    for lw in w["layers"]:
+        for name in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+            lw[name] = bf16_representable(lw[name])
+    return w
 
 
 def prompt_ids(seed: int, n: int, vocab: int) -> np.ndarray:

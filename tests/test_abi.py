@@ -53,10 +53,10 @@ def test_gemv_argument_validation(abi):
     assert L.wsg_stream_read(24, 64, 16, None) == abi.WSG_ERR_INVALID_ARG
 
 
-def _cfg(abi, shape, cap=16, dtype=0, chunk=0):
+def _cfg(abi, shape, cap=16, dtype=0, chunk=0, pack=0):
     return abi.wsg_config(shape.n_layers, shape.hidden, shape.intermediate, shape.n_q_heads,
                           shape.n_kv_heads, shape.head_dim, shape.vocab, cap, chunk, shape.rms_eps,
-                          shape.rope_theta, dtype)
+                          shape.rope_theta, dtype, pack)
 
 
 def test_config_validation(abi):
@@ -74,6 +74,10 @@ def test_config_validation(abi):
     assert L.wsg_workspace_bytes(C.byref(bad), C.byref(n)) == abi.WSG_ERR_INVALID_ARG
     bad = _cfg(abi, MINI, chunk=5000)
     assert L.wsg_workspace_bytes(C.byref(bad), C.byref(n)) == abi.WSG_ERR_INVALID_ARG
+    bad = _cfg(abi, MINI, pack=2)
+    assert L.wsg_packed_weight_bytes(C.byref(bad), C.byref(n)) == abi.WSG_ERR_INVALID_ARG
+    bad = _cfg(abi, MINI, dtype=1, pack=1)
+    assert L.wsg_packed_weight_bytes(C.byref(bad), C.byref(n)) == abi.WSG_ERR_UNSUPPORTED
     # packed bytes of the 28-layer FP32 model: the weights plus norm gains, 256-byte aligned
     assert L.wsg_packed_weight_bytes(C.byref(_cfg(abi, QWEN3_0_6B)), C.byref(n)) == 0
     assert QWEN3_0_6B.weight_bytes_per_token(4) <= n.value < QWEN3_0_6B.weight_bytes_per_token(4) + 2 ** 20
@@ -114,3 +118,76 @@ def test_pack_weights_layout_is_bit_copy(abi):
         assert any((s * 4) % 256 == 0 and np.array_equal(f[s:s + block.size], block) for s in starts)
     with pytest.raises(Exception):
         pack_weights(cfg, model_weights(sh, seed=3, dtype=np.float16))
+
+
+def _align256(v):
+    return (v + 255) & ~255
+
+
+def _lossless_image(abi, shape, w):
+    """(packed image, offset of the lossless header) for weights w."""
+    from weight_streaming_gemv_amd import pack_weights
+    n0 = C.c_size_t()
+    assert abi.lib().wsg_packed_weight_bytes(C.byref(_cfg(abi, shape)), C.byref(n0)) == 0
+    img = pack_weights(_cfg(abi, shape, pack=1), w)
+    return img, n0.value   # the lossless region follows the FP32 image
+
+
+def _flags(img, hdr, shape):
+    magic, count = np.frombuffer(img[hdr:hdr + 8].tobytes(), dtype=np.uint32)
+    assert magic == 0x50475357 and count == 1 + 4 * shape.n_layers
+    return img[hdr + 8:hdr + 8 + count]
+
+
+def test_lossless_pack_eligible_weights(abi):
+    """BF16-representable FP32 weights: every decode matrix gets a packed copy holding the
+    high 16 bits of each value (Megakernels, "Lossless decode-weight storage")."""
+    from synth import MINI, model_weights_bf16
+    sh = MINI.with_layers(2)
+    w = model_weights_bf16(sh, seed=3)
+    img, hdr = _lossless_image(abi, sh, w)
+    assert list(_flags(img, hdr, sh)) == [1] * (1 + 4 * sh.n_layers)
+    n = C.c_size_t()
+    assert abi.lib().wsg_packed_weight_bytes(C.byref(_cfg(abi, sh, pack=1)), C.byref(n)) == 0
+    assert n.value == img.size
+    # the packed embedding follows the header: element i = high half of E's i-th FP32 value
+    e_off = _align256(hdr + 8 + 1 + 4 * sh.n_layers)
+    E = w["embed"].reshape(-1)
+    got = np.frombuffer(img[e_off:e_off + 2 * E.size].tobytes(), dtype=np.uint16)
+    assert np.array_equal(got, (E.view(np.uint32) >> 16).astype(np.uint16))
+    # reconstruction is exact
+    assert np.array_equal((got.astype(np.uint32) << 16).view(np.float32), E)
+
+
+def test_lossless_pack_ineligible_weights(abi):
+    """Plain FP32 weights (nonzero low bits), a single stray low bit, or a non-finite
+    value keep FP32 storage for that matrix only."""
+    from synth import MINI, model_weights, model_weights_bf16
+    sh = MINI.with_layers(2)
+    img, hdr = _lossless_image(abi, sh, model_weights(sh, seed=3))
+    assert list(_flags(img, hdr, sh)) == [0] * (1 + 4 * sh.n_layers)
+    w = model_weights_bf16(sh, seed=3)
+    wk = w["layers"][1]["wk"].copy()
+    wk.view(np.uint32)[3, 7] |= 1           # layer 1 W_qkv
+    w["layers"][1]["wk"] = wk
+    wd = w["layers"][0]["wd"].copy()
+    wd[5, 5] = np.inf                        # layer 0 W_d
+    w["layers"][0]["wd"] = wd
+    img, hdr = _lossless_image(abi, sh, w)
+    # order: embedding, then per layer W_qkv, W_o, W_gu, W_d
+    assert list(_flags(img, hdr, sh)) == [1, 1, 1, 1, 0, 0, 1, 1, 1]
+
+
+def test_bf16_rounding_matches_torch():
+    """The synthetic BF16-representable weights use round-to-nearest-even, as torch's
+    float32 -> bfloat16 conversion does (ties included)."""
+    import torch
+    from synth import bf16_representable
+    rng = np.random.default_rng(0)
+    a = (rng.standard_normal(100000) * 0.02).astype(np.float32)
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 1.5 * 2 ** -8], np.float32)
+    a = np.concatenate([a, ties])
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    got = bf16_representable(a)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert not np.any(got.view(np.uint32) & 0xFFFF)

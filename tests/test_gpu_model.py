@@ -11,7 +11,7 @@ import pytest
 
 from gpu_util import _np, announce, gpu_available, lockstep
 import oracle
-from synth import MINI, PROMPT_SEEDS, QWEN3_0_6B, ModelShape, model_weights, prompt_ids
+from synth import MINI, PROMPT_SEEDS, QWEN3_0_6B, ModelShape, model_weights, model_weights_bf16, prompt_ids
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -190,4 +190,50 @@ def test_shape_variants(name, dtype):
     _, _, ck = lockstep(m, orc, prompt, 8, rtol=tol, atol=tol, teacher=(dtype == "f16"),
                         label=f"{name} {dtype}")
     print(f"{name} {dtype}: max |dlogit| {ck.max_logit_err:.2e} max |dkv| {ck.max_kv_err:.2e}")
+    m.close()
+
+
+@pytest.mark.parametrize("name,n_prompt", [("mini", 20), ("mini", 90), ("qwen3x2", 30)])
+def test_lossless_packed_decode(name, n_prompt):
+    """Packed decode weights (two exact FP32 values per 32-bit word) give bit-identical
+    logits, K/V and tokens to the unpacked model, and match the oracle (Megakernels,
+    "Lossless decode-weight storage").  90-id prompts reach the split-attention path,
+    whose output projection is its own launch."""
+    import weight_streaming_gemv_amd as wsg
+    sh = MINI if name == "mini" else QWEN3_0_6B.with_layers(2)
+    w = model_weights_bf16(sh, seed=0)
+    cap = 128
+    a = wsg.Model(sh, w, max_context=cap, prefill_chunk=32, lossless_pack=True)
+    b = wsg.Model(sh, w, max_context=cap, prefill_chunk=32)
+    sa, sb = a.storage(), b.storage()
+    assert sa["packed_matrices"] == sa["decode_matrices"] == 1 + 4 * sh.n_layers
+    assert sb["packed_matrices"] == 0
+    assert sa["decode_weight_bytes"] * 2 == sb["decode_weight_bytes"] == sh.weight_bytes_per_token(4)
+    prompt = prompt_ids(33, n_prompt, sh.vocab)
+    ta, tb = [a.prefill(prompt)], [b.prefill(prompt)]
+    assert np.array_equal(_np(a.logits()), _np(b.logits()))
+    for _ in range(6):
+        ta.append(a.step())
+        tb.append(b.step())
+        assert np.array_equal(_np(a.logits()), _np(b.logits()))
+    assert ta == tb
+    for l in range(sh.n_layers):
+        ka, va, na = a.kv(l)
+        kb, vb, nb = b.kv(l)
+        assert na == nb == n_prompt + 6
+        assert np.array_equal(_np(ka[:, :na]), _np(kb[:, :nb])) and np.array_equal(_np(va[:, :na]), _np(vb[:, :nb]))
+    b.close()
+    orc = oracle.OracleModel(sh, w, cap)
+    lockstep(a, orc, prompt, 4, label=f"{name} packed n={n_prompt}")
+    a.close()
+
+
+def test_lossless_pack_ineligible_weights_decode_unpacked(mini_w):
+    """lossless_pack on plain FP32 weights: nothing qualifies, the model runs unpacked."""
+    import weight_streaming_gemv_amd as wsg
+    m = wsg.Model(MINI, mini_w, max_context=32, lossless_pack=True)
+    st = m.storage()
+    assert st["packed_matrices"] == 0 and st["decode_weight_bytes"] == MINI.weight_bytes_per_token(4)
+    orc = oracle.OracleModel(MINI, mini_w, 32)
+    lockstep(m, orc, prompt_ids(34, 9, MINI.vocab), 3, label="mini pack-ineligible")
     m.close()

@@ -89,11 +89,12 @@ def stream_read(buf, out=None, stream=None):
 
 
 # ---------------------------------------------------------------- model
-def make_config(shape, max_context: int, dtype: int = WSG_F32, prefill_chunk: int = 0) -> wsg_config:
+def make_config(shape, max_context: int, dtype: int = WSG_F32, prefill_chunk: int = 0,
+                lossless_pack: bool = False) -> wsg_config:
     """C config from a ``synth.ModelShape``-like object."""
     return wsg_config(shape.n_layers, shape.hidden, shape.intermediate, shape.n_q_heads, shape.n_kv_heads,
                       shape.head_dim, shape.vocab, max_context, prefill_chunk, shape.rms_eps, shape.rope_theta,
-                      dtype)
+                      dtype, int(lossless_pack))
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -137,11 +138,12 @@ class Model:
     """A decode model on the GPU; weights and workspace are torch device tensors it owns."""
 
     def __init__(self, shape, weights: Dict[str, object], max_context: int, dtype: int = WSG_F32,
-                 prefill_chunk: int = 0, stream=None, packed: Optional[np.ndarray] = None):
+                 prefill_chunk: int = 0, stream=None, packed: Optional[np.ndarray] = None,
+                 lossless_pack: bool = False):
         torch = _torch()
         self.torch = torch
         self.shape = shape
-        self.cfg = make_config(shape, max_context, dtype, prefill_chunk)
+        self.cfg = make_config(shape, max_context, dtype, prefill_chunk, lossless_pack)
         self.np_dtype = np.float16 if dtype == WSG_F16 else np.float32
         self.t_dtype = torch.float16 if dtype == WSG_F16 else torch.float32
         host = packed if packed is not None else pack_weights(self.cfg, weights)
@@ -209,6 +211,12 @@ class Model:
         es = 2 if self.t_dtype == self.torch.float16 else 4
         assert 0 <= off and off + count * es <= self.ws.numel()
         return self.ws[off:off + count * es].view(self.t_dtype)
+
+    def storage(self) -> Dict[str, int]:
+        """Decode weight storage: packed matrices, decode matrices, decode weight bytes per token."""
+        pk, tot, b = C.c_int32(), C.c_int32(), C.c_int64()
+        check(_abi.lib().wsg_weight_storage(self.h, C.byref(pk), C.byref(tot), C.byref(b)))
+        return {"packed_matrices": pk.value, "decode_matrices": tot.value, "decode_weight_bytes": b.value}
 
     def logits(self):
         """Last logits [vocab] (device tensor view, storage dtype)."""

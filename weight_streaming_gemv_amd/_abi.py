@@ -31,7 +31,8 @@ class wsg_config(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("intermediate", C.c_int32),
                 ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("vocab", C.c_int32), ("max_context", C.c_int32), ("prefill_chunk", C.c_int32),
-                ("rms_eps", C.c_float), ("rope_theta", C.c_float), ("dtype", C.c_int32)]
+                ("rms_eps", C.c_float), ("rope_theta", C.c_float), ("dtype", C.c_int32),
+                ("lossless_pack", C.c_int32)]
 
 
 _PP = C.POINTER(C.c_void_p)
@@ -81,6 +82,8 @@ _SIGS = {
     "wsg_gemm_nt_f32": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_int32, C.c_void_p]),
     "wsg_stream_read": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
+    "wsg_weight_storage": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                     C.POINTER(C.c_int64)]),
     "wsg_last_error": (C.c_char_p, []),
     "wsg_version": (C.c_char_p, []),
 }

@@ -108,6 +108,33 @@ __device__ __forceinline__ uint4 load_u4(const void* p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// Lossless packed FP32 weights: an FP32 value whose low 16 bits are zero is
+// stored as its high 16 bits (two values per 32-bit word, element 2i in the
+// low half; Megakernels, "Lossless decode-weight storage").  Reconstruction
+// (a shift or a mask) gives back the exact FP32 bit pattern.
+struct bf16w { uint16_t b; };
+
+// Weight vectors: four FP32 values per lane and load, in the same lane
+// layout whether they are stored as FP32 (one 16-byte load) or packed (one
+// 8-byte load), so the products and their summation order are identical.
+template <typename T> struct WVec { using type = Vec16<T>; };
+struct PackedVec4 {
+  static constexpr int N = 4;
+  float v[4];
+  template <bool NT>
+  __device__ __forceinline__ void load(const bf16w* p) {
+    typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+    u2_t t;
+    if constexpr (NT) t = __builtin_nontemporal_load(reinterpret_cast<const u2_t*>(p));
+    else t = *reinterpret_cast<const u2_t*>(p);
+    v[0] = __builtin_bit_cast(float, t.x << 16);
+    v[1] = __builtin_bit_cast(float, t.x & 0xFFFF0000u);
+    v[2] = __builtin_bit_cast(float, t.y << 16);
+    v[3] = __builtin_bit_cast(float, t.y & 0xFFFF0000u);
+  }
+};
+template <> struct WVec<bf16w> { using type = PackedVec4; };
+
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }

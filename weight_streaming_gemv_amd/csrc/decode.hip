@@ -86,23 +86,28 @@ struct Act {
   }
 };
 
-// R weight rows held in registers (16-byte vectors in the lane layout), so
-// a wave can put its first rows in flight before its prologue finishes.
-template <typename TS, int K, int R>
+// R weight rows held in registers (vectors in the lane layout of Act), so a
+// wave can put its first rows in flight before its prologue finishes.  TW is
+// the weight storage: TS itself, or packed FP32 (bf16w) with FP32
+// activations, which gives the same lane layout and products.
+template <typename TW, int K, int R>
 struct WRows {
-  static constexpr int VEC = Vec16<TS>::N;
+  using Vec = typename WVec<TW>::type;
+  static constexpr int VEC = Vec::N;
   static constexpr int NV = K / (kWave * VEC);
-  Vec16<TS> v[R][NV];
-  __device__ __forceinline__ void load(const TS* __restrict__ W, int row0, int M) {
+  Vec v[R][NV];
+  __device__ __forceinline__ void load(const TW* __restrict__ W, int row0, int M) {
     const int lane = lane_id();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const TS* wr = W + (size_t)min(row0 + r, M - 1) * K + lane * VEC;
+      const TW* wr = W + (size_t)min(row0 + r, M - 1) * K + lane * VEC;
 #pragma unroll
       for (int c = 0; c < NV; ++c) v[r][c].template load<false>(wr + c * kWave * VEC);
     }
   }
+  template <typename TS>
   __device__ __forceinline__ void dot(const Act<TS, K>& x, float (&acc)[R]) const {
+    static_assert(Act<TS, K>::VEC == VEC, "weights and activations share the lane layout");
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float a = 0.f;
@@ -114,26 +119,6 @@ struct WRows {
     }
   }
 };
-
-// acc[r] += W[row0 + r] . act for r < R (rows clamped to M-1 for loads).
-template <typename TS, int K, int R>
-__device__ __forceinline__ void rows_dot(const TS* __restrict__ W, int row0, int M, const Act<TS, K>& x,
-                                         float (&acc)[R]) {
-  constexpr int VEC = Vec16<TS>::N;
-  constexpr int NV = K / (kWave * VEC);
-  const int lane = lane_id();
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const TS* wr = W + (size_t)min(row0 + r, M - 1) * K + lane * VEC;
-#pragma unroll
-    for (int c = 0; c < NV; ++c) {
-      Vec16<TS> w;
-      w.template load<false>(wr + c * kWave * VEC);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[r] = fmaf(w.v[i], x.a[c * VEC + i], acc[r]);
-    }
-  }
-}
 
 __device__ __forceinline__ int wave_row_groups_begin() { return blockIdx.x * kWavesPerBlock + wave_id(); }
 __device__ __forceinline__ int wave_row_groups_stride() { return gridDim.x * kWavesPerBlock; }
@@ -152,8 +137,8 @@ __device__ __forceinline__ float rows_prefetch(const TS* __restrict__ base, int 
 }
 
 // ------------------------------------------------------------------ qkv
-template <typename TS, int H, int R>
-__global__ __launch_bounds__(kBlock) void k_qkv(const TS* __restrict__ W, const TS* __restrict__ in_norm,
+template <typename TS, typename TW, int H, int R>
+__global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const TS* __restrict__ in_norm,
                                                 TS* __restrict__ x_res, const TS* __restrict__ embed,
                                                 const int32_t* __restrict__ ids, const int32_t* __restrict__ ctrl,
                                                 const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
@@ -161,7 +146,7 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TS* __restrict__ W, const 
                                                 TS* __restrict__ out, int M) {
   const int ngroups = ceil_div(M, R);
   int g = wave_row_groups_begin();
-  WRows<TS, H, R> w;
+  WRows<TW, H, R> w;
   Act<TS, H> x;
   // Vector loads return in issue order: the residual goes out before the
   // first weight rows (so the norm overlaps them); at layer 0 the
@@ -203,8 +188,8 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TS* __restrict__ W, const 
 // ------------------------------------------------------------ o / down
 // x_out[m] = x_in[m] + W[m] . in  for m < M (M = hidden); the residual
 // ping-pongs between two buffers, so no kernel rewrites what it reads.
-template <typename TS, int K, int R>
-__global__ __launch_bounds__(kBlock) void k_gemv_residual(const TS* __restrict__ W, const TS* __restrict__ in,
+template <typename TS, typename TW, int K, int R>
+__global__ __launch_bounds__(kBlock) void k_gemv_residual(const TW* __restrict__ W, const TS* __restrict__ in,
                                                           const TS* __restrict__ x_in, TS* __restrict__ x_out, int M,
                                                           int32_t* __restrict__ ctrl, int advance_pos) {
   const int ngroups = ceil_div(M, R);
@@ -214,7 +199,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv_residual(const TS* __restrict__
   x.load(in);
   float xr = rows_prefetch<TS, R>(x_in, g * R, M);
   __builtin_amdgcn_sched_barrier(0);
-  WRows<TS, K, R> w;
+  WRows<TW, K, R> w;
   w.load(W, g * R, M);   // rows clamped into W: no branch around the loads
   __builtin_amdgcn_sched_barrier(0);
   const int lane = lane_id();
@@ -251,16 +236,16 @@ constexpr int kMaxPartVec = 16;
 // attention/output launch, the first carrying the residual; slots past the
 // KV head count hold zeros): every block sums them in the same order,
 // rounds as stored, and block 0 writes x2 for the down projection.
-template <typename TS, int H, int R, int NP>
-__global__ __launch_bounds__(kBlock) void k_gateup(const TS* __restrict__ Wgu, const TS* __restrict__ post_norm,
+template <typename TS, typename TW, int H, int R, int NP>
+__global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, const TS* __restrict__ post_norm,
                                                    const TS* __restrict__ x_res, const float* __restrict__ opart,
                                                    float eps, TS* __restrict__ act, int I, TS* __restrict__ x2_out) {
   const int ngroups = ceil_div(I, R);
-  const TS* Wu = Wgu + (size_t)I * H;
+  const TW* Wu = Wgu + (size_t)I * H;
   const int tid = threadIdx.x;
   int g = wave_row_groups_begin();
   Act<TS, H> x;
-  WRows<TS, H, R> wg, wu;
+  WRows<TW, H, R> wg, wu;
   if constexpr (NP > 0) {
     // Vector loads return in issue order, so the partials (this thread's
     // float4 column of every partial, for each 1024-wide slice of x2) go out
@@ -350,8 +335,8 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
 // generation").  A single fused launch would need a device-scope release
 // fence per block, and on this multi-XCD part each such fence writes back
 // the issuing XCD's L2, which costs far more than the extra launch.
-template <typename TS, int H, int R, int WPB>
-__global__ __launch_bounds__(WPB * kWave) void k_head(const TS* __restrict__ E, const TS* __restrict__ final_norm,
+template <typename TS, typename TW, int H, int R, int WPB>
+__global__ __launch_bounds__(WPB * kWave) void k_head(const TW* __restrict__ E, const TS* __restrict__ final_norm,
                                                       const TS* __restrict__ x_res, float eps, TS* __restrict__ logits,
                                                       int V, unsigned long long* __restrict__ am_part) {
   __shared__ unsigned long long best_wave[WPB];
@@ -359,7 +344,7 @@ __global__ __launch_bounds__(WPB * kWave) void k_head(const TS* __restrict__ E, 
   const int ngroups = ceil_div(V, R);
   int g = blockIdx.x * WPB + wave_id();
   const int stride = gridDim.x * WPB;
-  WRows<TS, H, R> w;
+  WRows<TW, H, R> w;
   if (g < ngroups) w.load(E, g * R, V);   // first rows in flight before the norm
   Act<TS, H> x;
   x.load(x_res);
@@ -697,17 +682,18 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
 //   part[j][m] = W_o[m, cols of head j] . o_j  (+ x[m] for j = 0).
 // The gate/up launch sums the partials in a fixed order.  Blocks b = 0
 // write the current token's key and value into the cache.
-template <typename TS, int G, int R>
+template <typename TW, int G, int R>
 struct WoSlice {
-  static constexpr int VEC = Vec16<TS>::N;
+  using Vec = typename WVec<TW>::type;
+  static constexpr int VEC = Vec::N;
   static constexpr int LPR = G * kD / VEC;          // 16-byte vectors per row slice
   static constexpr int NLD = R * LPR / kWave;       // vectors per lane
   static_assert((R * LPR) % kWave == 0, "whole vectors per lane");
   static_assert(LPR == 16 || LPR == 32 || LPR % kWave == 0, "row slice of 16, 32 or a multiple of 64 lanes");
-  Vec16<TS> v[NLD];
+  Vec v[NLD];
 
   // vector t of this lane: row (64t + lane) / LPR, column vector (64t + lane) % LPR
-  __device__ __forceinline__ void load(const TS* __restrict__ Wo, int ld, int col0, int row0, int M) {
+  __device__ __forceinline__ void load(const TW* __restrict__ Wo, int ld, int col0, int row0, int M) {
     const int lane = lane_id();
 #pragma unroll
     for (int t = 0; t < NLD; ++t) {
@@ -754,12 +740,12 @@ struct WoSlice {
   }
 };
 
-template <typename TS, int G, int R>
+template <typename TS, typename TW, int G, int R>
 __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
                                                    TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
                                                    const TS* __restrict__ k_norm, const float* __restrict__ rope_cur,
                                                    const int32_t* __restrict__ ctrl, int n_q, int n_kv, int cap,
-                                                   float eps, const TS* __restrict__ Wo, const TS* __restrict__ x_res,
+                                                   float eps, const TW* __restrict__ Wo, const TS* __restrict__ x_res,
                                                    int H, float* __restrict__ opart) {
   __shared__ RowMerge<G> sm;
   __shared__ float s_o[G * kD];
@@ -780,7 +766,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
   // the residual rows (carried by the partial of KV head 0)
   const float xb = j == 0 ? rows_prefetch<TS, R>(x_res, row0, H) : 0.f;
   __builtin_amdgcn_sched_barrier(0);   // attention operands before the weights
-  WoSlice<TS, G, R> w;
+  WoSlice<TW, G, R> w;
   w.load(Wo, n_q * kD, j * G * kD, row0, H);
   __builtin_amdgcn_sched_barrier(0);   // all loads issued in this order first
   const int pos = ctrl[kCtrlPos];
@@ -892,30 +878,44 @@ bool with_r(int R, F&& f) {
   }
 }
 
+// Weight storage of one matrix: its packed copy when there is one (FP32
+// models only), else the storage type itself.  f receives the typed pointer.
+template <typename TS, typename F>
+bool with_w(const void* w, const void* packed, F&& f) {
+  if constexpr (std::is_same<TS, float>::value)
+    if (packed) return f(static_cast<const bf16w*>(packed));
+  return f(static_cast<const TS*>(w));
+}
+template <typename P> using pointee_t = typename std::remove_cv<typename std::remove_pointer<P>::type>::type;
+
 template <typename TS>
 bool qkv_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, hipStream_t s) {
   const int M = (a.n_q + 2 * a.n_kv) * a.head_dim;
   const int grid = blocks_for(M, sh.rows_qkv, sh.grid_qkv);
-  return with_k<TS>(a.hidden, [&](auto kc) {
-    return with_r(sh.rows_qkv, [&](auto rc) {
-      hipLaunchKernelGGL((k_qkv<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock), 0, s,
-                         (const TS*)L.wqkv, (const TS*)L.in_norm, (TS*)a.x, (const TS*)a.embed, a.ids, a.ctrl,
-                         a.rope_cos, a.rope_sin, a.rope_cur, first ? 1 : 0, a.vocab, a.eps, (TS*)a.qkv, M);
-      return true;
+  return with_w<TS>(L.wqkv, L.wqkv_p, [&](auto W) {
+    return with_k<TS>(a.hidden, [&](auto kc) {
+      return with_r(sh.rows_qkv, [&](auto rc) {
+        hipLaunchKernelGGL((k_qkv<TS, pointee_t<decltype(W)>, decltype(kc)::value, decltype(rc)::value>), dim3(grid),
+                           dim3(kBlock), 0, s, W, (const TS*)L.in_norm, (TS*)a.x, (const TS*)a.embed, a.ids, a.ctrl,
+                           a.rope_cos, a.rope_sin, a.rope_cur, first ? 1 : 0, a.vocab, a.eps, (TS*)a.qkv, M);
+        return true;
+      });
     });
   });
 }
 
 template <typename TS>
-bool residual_t(const DecodeArgs& a, int K, int R, int grid_req, const void* W, const void* in, const void* x_in,
-                void* x_out, bool adv, hipStream_t s) {
+bool residual_t(const DecodeArgs& a, int K, int R, int grid_req, const void* W, const void* Wp, const void* in,
+                const void* x_in, void* x_out, bool adv, hipStream_t s) {
   const int grid = blocks_for(a.hidden, R, grid_req);
-  return with_k<TS>(K, [&](auto kc) {
-    return with_r(R, [&](auto rc) {
-      hipLaunchKernelGGL((k_gemv_residual<TS, decltype(kc)::value, decltype(rc)::value>), dim3(grid), dim3(kBlock),
-                         0, s, (const TS*)W, (const TS*)in, (const TS*)x_in, (TS*)x_out, a.hidden, a.ctrl,
-                         adv ? 1 : 0);
-      return true;
+  return with_w<TS>(W, Wp, [&](auto Wt) {
+    return with_k<TS>(K, [&](auto kc) {
+      return with_r(R, [&](auto rc) {
+        hipLaunchKernelGGL((k_gemv_residual<TS, pointee_t<decltype(Wt)>, decltype(kc)::value, decltype(rc)::value>),
+                           dim3(grid), dim3(kBlock), 0, s, Wt, (const TS*)in, (const TS*)x_in, (TS*)x_out, a.hidden,
+                           a.ctrl, adv ? 1 : 0);
+        return true;
+      });
     });
   });
 }
@@ -934,27 +934,30 @@ bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bo
   const int grid = blocks_for(a.inter, sh.rows_gu, sh.grid_gu);
   const int np = from_parts ? parts_slots(a.hidden, a.n_kv) : 0;
   if (from_parts && np == 0) return false;
-  return with_k<TS>(a.hidden, [&](auto kc) {
-    return with_r(sh.rows_gu, [&](auto rc) {
-      constexpr int K = decltype(kc)::value, R = decltype(rc)::value;
-      auto go = [&](auto npc) {
-        constexpr int NP = decltype(npc)::value;
-        if constexpr (NP * ceil_div(K, 4 * kBlock) <= kMaxPartVec) {
-          hipLaunchKernelGGL((k_gateup<TS, K, R, NP>), dim3(grid), dim3(kBlock), 0, s, (const TS*)L.wgu,
-                             (const TS*)L.post_norm, (const TS*)a.x2, a.opart, a.eps, (TS*)a.act, a.inter,
-                             (TS*)a.x2);
-          return true;
-        } else {
-          return false;
+  return with_w<TS>(L.wgu, L.wgu_p, [&](auto W) {
+    using TW = pointee_t<decltype(W)>;
+    return with_k<TS>(a.hidden, [&](auto kc) {
+      return with_r(sh.rows_gu, [&](auto rc) {
+        constexpr int K = decltype(kc)::value, R = decltype(rc)::value;
+        auto go = [&](auto npc) {
+          constexpr int NP = decltype(npc)::value;
+          if constexpr (NP * ceil_div(K, 4 * kBlock) <= kMaxPartVec) {
+            hipLaunchKernelGGL((k_gateup<TS, TW, K, R, NP>), dim3(grid), dim3(kBlock), 0, s, W,
+                               (const TS*)L.post_norm, (const TS*)a.x2, a.opart, a.eps, (TS*)a.act, a.inter,
+                               (TS*)a.x2);
+            return true;
+          } else {
+            return false;
+          }
+        };
+        switch (np) {
+          case 0: return go(IC<0>{});
+          case 2: return go(IC<2>{});
+          case 4: return go(IC<4>{});
+          case 8: return go(IC<8>{});
+          default: return false;
         }
-      };
-      switch (np) {
-        case 0: return go(IC<0>{});
-        case 2: return go(IC<2>{});
-        case 4: return go(IC<4>{});
-        case 8: return go(IC<8>{});
-        default: return false;
-      }
+      });
     });
   });
 }
@@ -962,21 +965,24 @@ bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bo
 template <typename TS>
 bool head_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   const int grid = head_grid(a.vocab, sh.rows_head, sh.head_waves, sh.grid_head);
-  return with_k<TS>(a.hidden, [&](auto kc) {
-    return with_r(sh.rows_head, [&](auto rc) {
-      constexpr int K = decltype(kc)::value, R = decltype(rc)::value;
-      auto go = [&](auto wc) {
-        constexpr int WPB = decltype(wc)::value;
-        hipLaunchKernelGGL((k_head<TS, K, R, WPB>), dim3(grid), dim3(WPB * kWave), 0, s, (const TS*)a.embed,
-                           (const TS*)a.final_norm, (const TS*)a.x, a.eps, (TS*)a.logits, a.vocab, a.am_part);
-        return true;
-      };
-      switch (sh.head_waves) {
-        case 4: return go(IC<4>{});
-        case 8: return go(IC<8>{});
-        case 16: return go(IC<16>{});
-        default: return false;
-      }
+  return with_w<TS>(a.embed, a.embed_p, [&](auto E) {
+    using TW = pointee_t<decltype(E)>;
+    return with_k<TS>(a.hidden, [&](auto kc) {
+      return with_r(sh.rows_head, [&](auto rc) {
+        constexpr int K = decltype(kc)::value, R = decltype(rc)::value;
+        auto go = [&](auto wc) {
+          constexpr int WPB = decltype(wc)::value;
+          hipLaunchKernelGGL((k_head<TS, TW, K, R, WPB>), dim3(grid), dim3(WPB * kWave), 0, s, E,
+                             (const TS*)a.final_norm, (const TS*)a.x, a.eps, (TS*)a.logits, a.vocab, a.am_part);
+          return true;
+        };
+        switch (sh.head_waves) {
+          case 4: return go(IC<4>{});
+          case 8: return go(IC<8>{});
+          case 16: return go(IC<16>{});
+          default: return false;
+        }
+      });
     });
   });
 }
@@ -1018,27 +1024,30 @@ bool attn_merge_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
 template <typename TS>
 bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
-  auto go = [&](auto gc, auto rc) {
-    constexpr int R = decltype(rc)::value;
-    const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R), a.n_kv);
-    hipLaunchKernelGGL((k_attn_o<TS, decltype(gc)::value, R>), grid, dim3(kBlock), 0, s, (const TS*)a.qkv,
-                       (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm, a.rope_cur, a.ctrl,
-                       a.n_q, a.n_kv, a.cap, a.eps, (const TS*)L.wo, (const TS*)a.x, a.hidden, a.opart);
-    return true;
-  };
-  auto with_g = [&](auto rc) {
-    switch (G) {
-      case 1: return go(IC<1>{}, rc);
-      case 2: return go(IC<2>{}, rc);
-      case 4: return go(IC<4>{}, rc);
+  return with_w<TS>(L.wo, L.wo_p, [&](auto Wo) {
+    using TW = pointee_t<decltype(Wo)>;
+    auto go = [&](auto gc, auto rc) {
+      constexpr int R = decltype(rc)::value;
+      const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R), a.n_kv);
+      hipLaunchKernelGGL((k_attn_o<TS, TW, decltype(gc)::value, R>), grid, dim3(kBlock), 0, s, (const TS*)a.qkv,
+                         (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm, a.rope_cur,
+                         a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, Wo, (const TS*)a.x, a.hidden, a.opart);
+      return true;
+    };
+    auto with_g = [&](auto rc) {
+      switch (G) {
+        case 1: return go(IC<1>{}, rc);
+        case 2: return go(IC<2>{}, rc);
+        case 4: return go(IC<4>{}, rc);
+        default: return false;
+      }
+    };
+    switch (sh.rows_attn_o) {
+      case 4: return with_g(IC<4>{});
+      case 8: return with_g(IC<8>{});
       default: return false;
     }
-  };
-  switch (sh.rows_attn_o) {
-    case 4: return with_g(IC<4>{});
-    case 8: return with_g(IC<8>{});
-    default: return false;
-  }
+  });
 }
 
 }  // namespace
@@ -1060,8 +1069,8 @@ bool launch_attn_merge(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s
 }
 bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   const int K = a.n_q * a.head_dim;
-  return a.dtype == 0 ? residual_t<float>(a, K, sh.rows_o, sh.grid_o, L.wo, a.o, a.x, a.x2, false, s)
-                      : residual_t<__half>(a, K, sh.rows_o, sh.grid_o, L.wo, a.o, a.x, a.x2, false, s);
+  return a.dtype == 0 ? residual_t<float>(a, K, sh.rows_o, sh.grid_o, L.wo, L.wo_p, a.o, a.x, a.x2, false, s)
+                      : residual_t<__half>(a, K, sh.rows_o, sh.grid_o, L.wo, nullptr, a.o, a.x, a.x2, false, s);
 }
 bool launch_attn_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   return a.dtype == 0 ? attn_o_t<float>(a, sh, L, s) : attn_o_t<__half>(a, sh, L, s);
@@ -1070,8 +1079,9 @@ bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& 
   return a.dtype == 0 ? gateup_t<float>(a, sh, L, from_parts, s) : gateup_t<__half>(a, sh, L, from_parts, s);
 }
 bool launch_down(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool adv, hipStream_t s) {
-  return a.dtype == 0 ? residual_t<float>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, a.act, a.x2, a.x, adv, s)
-                      : residual_t<__half>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, a.act, a.x2, a.x, adv, s);
+  return a.dtype == 0
+             ? residual_t<float>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, L.wd_p, a.act, a.x2, a.x, adv, s)
+             : residual_t<__half>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, nullptr, a.act, a.x2, a.x, adv, s);
 }
 bool launch_head(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   return a.dtype == 0 ? head_t<float>(a, sh, s) : head_t<__half>(a, sh, s);

@@ -29,6 +29,12 @@ struct LayerPtrs {
   const void* k_norm;
   void* k_cache;        // [n_kv][cap][D]
   void* v_cache;
+  // Lossless packed copies (two exact FP32 values with zero low halves per
+  // 32-bit word) read by the decode kernels; nullptr = read the FP32 matrix.
+  const void* wqkv_p = nullptr;
+  const void* wo_p = nullptr;
+  const void* wgu_p = nullptr;
+  const void* wd_p = nullptr;
 };
 
 struct DecodeArgs {
@@ -36,6 +42,7 @@ struct DecodeArgs {
   int hidden, inter, n_q, n_kv, head_dim, vocab, cap;
   float eps;
   const void* embed;    // [V][H]
+  const void* embed_p;  // packed copy of embed for the head, or nullptr
   const void* final_norm;
   const float* rope_cos;  // [cap][D/2]
   const float* rope_sin;

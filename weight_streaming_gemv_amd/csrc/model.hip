@@ -30,6 +30,7 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct Dims {
   int L, H, I, nq, nkv, D, V, cap, chunk, Q, KV, G;
   size_t es;   // storage element bytes
+  bool pack;   // lossless packed copies of the decode matrices
 };
 
 Dims dims_of(const wsg_config& c) {
@@ -38,6 +39,7 @@ Dims dims_of(const wsg_config& c) {
   d.D = c.head_dim; d.V = c.vocab; d.cap = c.max_context; d.chunk = c.prefill_chunk;
   d.Q = d.nq * d.D; d.KV = d.nkv * d.D; d.G = d.nkv > 0 ? d.nq / d.nkv : 0;
   d.es = c.dtype == WSG_F16 ? 2 : 4;
+  d.pack = c.lossless_pack != 0;
   return d;
 }
 
@@ -62,22 +64,36 @@ wsg_status validate_config(const wsg_config* c) {
     return fail(WSG_ERR_UNSUPPORTED, "hidden/intermediate/query width must be in {512,1024,2048,3072}%s",
                 c->dtype == WSG_F32 ? " or 256" : "");
   if ((int64_t)c->max_context > (1 << 20)) return fail(WSG_ERR_UNSUPPORTED, "max_context too large");
+  if (c->lossless_pack != 0 && c->lossless_pack != 1) return fail(WSG_ERR_INVALID_ARG, "lossless_pack must be 0 or 1");
+  if (c->lossless_pack && c->dtype != WSG_F32)
+    return fail(WSG_ERR_UNSUPPORTED, "lossless packing applies to FP32 models");
   if (c->prefill_chunk > 0 && (c->dtype != WSG_F32 || G > 2))
     return fail(WSG_ERR_UNSUPPORTED, "chunked prefill needs FP32 storage and a query group of 1 or 2");
   return WSG_OK;
 }
 
 // ------------------------------------------------------------ layouts
-struct LayerOff { size_t in_norm, post_norm, q_norm, k_norm, wqkv, wo, wgu, wd; };
+struct LayerOff {
+  size_t in_norm, post_norm, q_norm, k_norm, wqkv, wo, wgu, wd;
+  size_t wqkv_p = 0, wo_p = 0, wgu_p = 0, wd_p = 0;   // packed copies (lossless_pack)
+};
 struct PackedLayout {
   size_t embed = 0, final_norm = 0, total = 0;
+  size_t hdr = 0, embed_p = 0;   // lossless_pack: flag header, packed embedding
   std::vector<LayerOff> layers;
 };
+
+// Flag header of the packed copies: magic, count, then one byte per decode
+// matrix (embedding, then per layer W_qkv, W_o, W_gu, W_d): 1 = packed copy
+// present and verified.
+constexpr uint32_t kPackMagic = 0x50475357u;
+int pack_count(const Dims& d) { return 1 + 4 * d.L; }
 
 PackedLayout packed_layout(const Dims& d) {
   PackedLayout p;
   size_t off = 0;
   auto take = [&](size_t elems) { const size_t o = off; off = align256(off + elems * d.es); return o; };
+  auto take_bytes = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
   p.embed = take((size_t)d.V * d.H);
   p.final_norm = take(d.H);
   for (int l = 0; l < d.L; ++l) {
@@ -92,8 +108,33 @@ PackedLayout packed_layout(const Dims& d) {
     lo.wd = take((size_t)d.H * d.I);
     p.layers.push_back(lo);
   }
+  if (d.pack) {
+    p.hdr = take_bytes(8 + pack_count(d));
+    p.embed_p = take_bytes((size_t)d.V * d.H * 2);
+    for (LayerOff& lo : p.layers) {
+      lo.wqkv_p = take_bytes((size_t)(d.Q + 2 * d.KV) * d.H * 2);
+      lo.wo_p = take_bytes((size_t)d.H * d.Q * 2);
+      lo.wgu_p = take_bytes((size_t)2 * d.I * d.H * 2);
+      lo.wd_p = take_bytes((size_t)d.H * d.I * 2);
+    }
+  }
   p.total = off;
   return p;
+}
+
+// Lossless packed copy of elems FP32 values at src into dst (elems 16-bit
+// halves): 1 = written and verified, 0 = not eligible (odd count, a
+// non-finite value or nonzero low 16 bits), -1 = verification mismatch.
+int pack_lossless(const uint8_t* src_bytes, uint8_t* dst_bytes, size_t elems) {
+  if (elems % 2 != 0) return 0;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(src_bytes);
+  for (size_t i = 0; i < elems; ++i)
+    if ((src[i] & 0xFFFFu) != 0 || ((src[i] >> 23) & 0xFFu) == 0xFFu) return 0;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(dst_bytes);
+  for (size_t i = 0; i < elems; ++i) dst[i] = (uint16_t)(src[i] >> 16);
+  for (size_t i = 0; i < elems; ++i)
+    if (((uint32_t)dst[i] << 16) != src[i]) return -1;
+  return 1;
 }
 
 // Decode attention splits the keys into fixed ranges of attn_chunk(d)
@@ -178,6 +219,7 @@ struct wsg_model {
   std::vector<hipEvent_t> ev;
   int ev_used = 0;
   int64_t timed_bytes_per_launch_sum = 0;
+  int n_packed = 0;   // decode matrices with a lossless packed copy
   double acc_ms = 0;
   int64_t acc_launches = 0, acc_bytes = 0;
   int prefill_rows = 0;
@@ -188,14 +230,18 @@ struct wsg_model {
 
 namespace {
 
-int64_t stage_bytes(const wsg_model* m, int stage) {
+// Weight bytes one launch of a stage streams for layer l (the head: the
+// embedding); packed copies count half.
+int64_t stage_bytes(const wsg_model* m, int stage, int l) {
   const Dims& d = m->d;
+  const LayerPtrs* L = l >= 0 && l < (int)m->layers.size() ? &m->layers[l] : nullptr;
+  auto b = [&](int64_t elems, const void* packed) { return packed ? elems * 2 : elems * (int64_t)d.es; };
   switch (stage) {
-    case WSG_STAGE_QKV: return (int64_t)(d.Q + 2 * d.KV) * d.H * d.es;
-    case WSG_STAGE_O: return (int64_t)d.H * d.Q * d.es;
-    case WSG_STAGE_GATEUP: return (int64_t)2 * d.I * d.H * d.es;
-    case WSG_STAGE_DOWN: return (int64_t)d.H * d.I * d.es;
-    case WSG_STAGE_HEAD: return (int64_t)d.V * d.H * d.es;
+    case WSG_STAGE_QKV: return b((int64_t)(d.Q + 2 * d.KV) * d.H, L ? L->wqkv_p : nullptr);
+    case WSG_STAGE_O: return b((int64_t)d.H * d.Q, L ? L->wo_p : nullptr);
+    case WSG_STAGE_GATEUP: return b((int64_t)2 * d.I * d.H, L ? L->wgu_p : nullptr);
+    case WSG_STAGE_DOWN: return b((int64_t)d.H * d.I, L ? L->wd_p : nullptr);
+    case WSG_STAGE_HEAD: return b((int64_t)d.V * d.H, m->args.embed_p);
     default: return 0;
   }
 }
@@ -239,22 +285,22 @@ bool enqueue_body(wsg_model* m, int splits, bool advance) {
   for (int l = 0; l < L; ++l) {
     const LayerPtrs& lp = m->layers[l];
     const DecodeArgs& a = m->args;
-    if (!timed(m, WSG_STAGE_QKV, stage_bytes(m, WSG_STAGE_QKV), [&] { return launch_qkv(a, sh, lp, l == 0, s); }))
+    if (!timed(m, WSG_STAGE_QKV, stage_bytes(m, WSG_STAGE_QKV, l), [&] { return launch_qkv(a, sh, lp, l == 0, s); }))
       return false;
     if (fused) {
-      if (!timed(m, WSG_STAGE_ATTN, stage_bytes(m, WSG_STAGE_O), [&] { return launch_attn_o(a, sh, lp, s); }))
+      if (!timed(m, WSG_STAGE_ATTN, stage_bytes(m, WSG_STAGE_O, l), [&] { return launch_attn_o(a, sh, lp, s); }))
         return false;
     } else {
       if (!timed(m, WSG_STAGE_ATTN, 0, [&] {
             return launch_attn(a, sh, lp, s) && (splits == 1 || launch_attn_merge(a, sh, s));
           }))
         return false;
-      if (!timed(m, WSG_STAGE_O, stage_bytes(m, WSG_STAGE_O), [&] { return launch_o(a, sh, lp, s); })) return false;
+      if (!timed(m, WSG_STAGE_O, stage_bytes(m, WSG_STAGE_O, l), [&] { return launch_o(a, sh, lp, s); })) return false;
     }
-    if (!timed(m, WSG_STAGE_GATEUP, stage_bytes(m, WSG_STAGE_GATEUP),
+    if (!timed(m, WSG_STAGE_GATEUP, stage_bytes(m, WSG_STAGE_GATEUP, l),
                [&] { return launch_gateup(a, sh, lp, fused, s); }))
       return false;
-    if (!timed(m, WSG_STAGE_DOWN, stage_bytes(m, WSG_STAGE_DOWN),
+    if (!timed(m, WSG_STAGE_DOWN, stage_bytes(m, WSG_STAGE_DOWN, l),
                [&] { return launch_down(a, sh, lp, advance && l == L - 1, s); }))
       return false;
   }
@@ -328,7 +374,7 @@ wsg_status run_forward(wsg_model* m, bool head, int n_keys) {
     if (t) {
       record_event(m, m->ev[1]);
       m->ev_used = 2;
-      m->timed_bytes_per_launch_sum = stage_bytes(m, WSG_STAGE_HEAD);
+      m->timed_bytes_per_launch_sum = stage_bytes(m, WSG_STAGE_HEAD, -1);
     }
     if (!enqueue_argmax(m)) return fail(WSG_ERR_UNSUPPORTED, "argmax launch");
   }
@@ -435,6 +481,27 @@ wsg_status wsg_pack_weights(const wsg_config* cfg, const wsg_host_weights* w, vo
     put(lo.wgu + (size_t)d.I * d.H * es, w->wu[l], (size_t)d.I * d.H);
     put(lo.wd, w->wd[l], (size_t)d.H * d.I);
   }
+  if (d.pack) {
+    uint32_t* hdr = reinterpret_cast<uint32_t*>(out + p.hdr);
+    uint8_t* flags = out + p.hdr + 8;
+    hdr[0] = kPackMagic;
+    hdr[1] = (uint32_t)pack_count(d);
+    int idx = 0;
+    auto pack = [&](size_t src, size_t dst, size_t elems) {
+      const int r = pack_lossless(out + src, out + dst, elems);
+      if (r < 0) return false;
+      if (r == 0) memset(out + dst, 0, elems * 2);
+      flags[idx++] = (uint8_t)r;
+      return true;
+    };
+    bool ok = pack(p.embed, p.embed_p, (size_t)d.V * d.H);
+    for (int l = 0; l < d.L && ok; ++l) {
+      const LayerOff& lo = p.layers[l];
+      ok = pack(lo.wqkv, lo.wqkv_p, (size_t)(d.Q + 2 * d.KV) * d.H) && pack(lo.wo, lo.wo_p, (size_t)d.H * d.Q) &&
+           pack(lo.wgu, lo.wgu_p, (size_t)2 * d.I * d.H) && pack(lo.wd, lo.wd_p, (size_t)d.H * d.I);
+    }
+    if (!ok) return fail(WSG_ERR_STATE, "lossless packed copy failed its bitwise verification");
+  }
   return WSG_OK;
 }
 
@@ -480,6 +547,7 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   a.hidden = d.H; a.inter = d.I; a.n_q = d.nq; a.n_kv = d.nkv; a.head_dim = d.D; a.vocab = d.V; a.cap = d.cap;
   a.eps = cfg->rms_eps;
   a.embed = m->packed + pl.embed;
+  a.embed_p = nullptr;
   a.final_norm = m->packed + pl.final_norm;
   a.rope_cos = reinterpret_cast<const float*>(m->ws + wl.rope_cos);
   a.rope_sin = reinterpret_cast<const float*>(m->ws + wl.rope_sin);
@@ -502,6 +570,32 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
     lp.k_cache = m->ws + wl.kv + l * kv_layer;
     lp.v_cache = m->ws + wl.kv + l * kv_layer + kv_layer / 2;
     m->layers.push_back(lp);
+  }
+  if (d.pack) {
+    // which decode matrices have a verified packed copy (header written by
+    // wsg_pack_weights)
+    std::vector<uint8_t> hdr(8 + pack_count(d));
+    if (hipMemcpyAsync(hdr.data(), m->packed + pl.hdr, hdr.size(), hipMemcpyDeviceToHost, m->stream) != hipSuccess ||
+        hipStreamSynchronize(m->stream) != hipSuccess)
+      return fail_free(fail(WSG_ERR_HIP, "reading the packed-weight header failed"));
+    uint32_t magic, count;
+    memcpy(&magic, hdr.data(), 4);
+    memcpy(&count, hdr.data() + 4, 4);
+    if (magic != kPackMagic || (int)count != pack_count(d))
+      return fail_free(fail(WSG_ERR_INVALID_ARG, "packed weights lack the lossless-copy header (pack with lossless_pack = 1)"));
+    const uint8_t* f = hdr.data() + 8;
+    for (int i = 0; i < pack_count(d); ++i)
+      if (f[i] > 1) return fail_free(fail(WSG_ERR_INVALID_ARG, "corrupt packed-weight header"));
+    if (f[0]) a.embed_p = m->packed + pl.embed_p;
+    for (int l = 0; l < d.L; ++l) {
+      const LayerOff& lo = pl.layers[l];
+      LayerPtrs& lp = m->layers[l];
+      if (f[1 + 4 * l]) lp.wqkv_p = m->packed + lo.wqkv_p;
+      if (f[2 + 4 * l]) lp.wo_p = m->packed + lo.wo_p;
+      if (f[3 + 4 * l]) lp.wgu_p = m->packed + lo.wgu_p;
+      if (f[4 + 4 * l]) lp.wd_p = m->packed + lo.wd_p;
+    }
+    for (int i = 0; i < pack_count(d); ++i) m->n_packed += f[i];
   }
   DecodeShape& sh = m->shape;
   sh.rows_qkv = sh.rows_o = sh.rows_gu = sh.rows_down = sh.rows_head = 1;
@@ -681,6 +775,21 @@ wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value) {
     default:
       return fail(WSG_ERR_INVALID_ARG, "unknown option %d", option);
   }
+}
+
+wsg_status wsg_weight_storage(const wsg_model* m, int32_t* packed_matrices, int32_t* decode_matrices,
+                              int64_t* decode_weight_bytes) {
+  clear_error();
+  if (!m || !packed_matrices || !decode_matrices || !decode_weight_bytes)
+    return fail(WSG_ERR_INVALID_ARG, "NULL pointer");
+  *packed_matrices = m->n_packed;
+  *decode_matrices = pack_count(m->d);
+  int64_t b = stage_bytes(m, WSG_STAGE_HEAD, -1);
+  for (int l = 0; l < m->d.L; ++l)
+    b += stage_bytes(m, WSG_STAGE_QKV, l) + stage_bytes(m, WSG_STAGE_O, l) + stage_bytes(m, WSG_STAGE_GATEUP, l) +
+         stage_bytes(m, WSG_STAGE_DOWN, l);
+  *decode_weight_bytes = b;
+  return WSG_OK;
 }
 
 wsg_status wsg_stage_time(wsg_model* m, double* total_ms, int64_t* launches, int64_t* bytes) {
