@@ -310,6 +310,46 @@ def sweep_summary(sw):
     return best, agg
 
 
+def fixed_context(torch, wsg, shape, w, contexts=(0, 16, 64), trials=9, reps=50):
+    """Single-forward latency at fixed contexts (Megakernels, "Fixed-context methodology"):
+    per context c, three autoregressive forwards (slots c, c+1, c+2) are checked against the
+    oracle (full-vocabulary logits, every valid K/V entry, exact greedy tokens) before
+    timing; a trial then repeats the forward of one token at slot c `reps` times (rewind to
+    c, step, read the token id: the same token every time).  Median and minimum over trials
+    of the time per forward, including the rewind's one-word device update and the 4-byte
+    token read."""
+    import oracle
+    from synth import prompt_ids
+    cap = max(contexts) + 4
+    model = wsg.Model(shape, w, max_context=cap, prefill_chunk=64)
+    orc = oracle.OracleModel(shape, w, cap)
+    res, errs = {}, []
+    for c in contexts:
+        prefix = prompt_ids(50 + c, c + 1, shape.vocab)
+        toks, ml, mkv, _ = validate(model, orc, prefix, 3)
+        errs.append((ml, mkv))
+        model.reset()
+        tok = model.prefill(prefix)
+        per = []
+        for t in range(trials + 1):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                model.rewind(c)
+                if model.step() != toks[0]:
+                    raise RuntimeError(f"fixed context {c}: repeated forward changed its token")
+            if t > 0:                      # the first trial warms up
+                per.append((time.perf_counter() - t0) / reps * 1e6)
+        assert tok == toks[0]
+        res[str(c)] = {"us_median": round(statistics.median(per), 2), "us_min": round(min(per), 2)}
+    model.close()
+    res["validation"] = {"max_abs_logit_err": max(e[0] for e in errs), "max_abs_kv_err": max(e[1] for e in errs),
+                         "forwards_checked_per_context": 3}
+    res["workload"] = (f"28-layer FP32; contexts {list(contexts)}; {trials} trials x {reps} repeats of one "
+                       "token's forward at the fixed slot (graph replay + head + argmax + token read)")
+    return res
+
+
 def lossless_bf16(torch, wsg, shape, steps=5, warmup=2):
     """The short-prompt workload on BF16-representable FP32 weights (the synthetic weights
     rounded to BF16), decode weights packed losslessly (Megakernels, "Lossless decode-weight
@@ -521,6 +561,8 @@ def main(argv=None):
                     help="run only a 512 MiB device copy (reference for the HBM traffic counters)")
     ap.add_argument("--long", choices=["on", "off", "only"], default="on",
                     help="long-document workload (2048-id chunk selection, 4096 -> 1024 held-out)")
+    ap.add_argument("--fixed", choices=["on", "off", "only"], default="on",
+                    help="single-forward latency at contexts 0/16/64 (fixed cache slot)")
     ap.add_argument("--lossless", choices=["on", "off", "only"], default="on",
                     help="short-prompt workload on BF16-representable weights, packed vs unpacked decode")
     ap.add_argument("--no-oracle", action="store_true",
@@ -591,6 +633,12 @@ def main(argv=None):
     if args.lossless == "only":
         print(json.dumps({"lossless_bf16": lossless_bf16(torch, wsg, shape)}), flush=True)
         return 0
+    fixed_res = None
+    if args.fixed != "off" and not args.no_oracle:
+        fixed_res = fixed_context(torch, wsg, shape, w)
+        if args.fixed == "only":
+            print(json.dumps({"fixed_context": fixed_res}), flush=True)
+            return 0
     long_res = None
     if args.long != "off" and not args.no_oracle:
         long_res = long_context(torch, wsg, shape, w)
@@ -666,6 +714,7 @@ def main(argv=None):
         "graphs": not args.no_graph,
         "host": host_info(),
         "long_context": long_res,
+        "fixed_context": fixed_res,
     }
     model.close()
     del model

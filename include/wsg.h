@@ -157,6 +157,17 @@ wsg_status wsg_step(wsg_model* m, int32_t in_token, int32_t* out_token, const vo
 /* Current position (number of valid KV entries). */
 int32_t wsg_position(const wsg_model* m);
 
+/* Truncate the sequence to its first pos tokens (0 <= pos <= position):
+ * cache slots from pos on become invalid (they are rewritten before they are
+ * read again).  The token history is kept, so wsg_step(m, -1, ...) then
+ * re-processes the token recorded at slot pos; pass in_token to process
+ * another one.  Used to repeat one forward at a fixed cache slot
+ * (Megakernels, "Fixed-context methodology": each trial repeats one token at
+ * a fixed slot) and to drop rejected tokens.  Asynchronous on the model
+ * stream.  Errors: pos < 0 (WSG_ERR_INVALID_ARG), pos > position
+ * (WSG_ERR_OUT_OF_RANGE). */
+wsg_status wsg_rewind(wsg_model* m, int32_t pos);
+
 /* Device pointers to layer `layer`'s K and V cache blocks, each laid out
  * [n_kv][max_context][head_dim] in the storage dtype, and the valid length.
  * For validation; the memory belongs to the workspace. */
@@ -179,8 +190,8 @@ wsg_status wsg_set_prefill_chunk(wsg_model* m, int32_t rows);
  * to short kernels.
  * Errors: WSG_ERR_UNSUPPORTED for a per-layer stage while graphs are on. */
 enum { WSG_OPT_USE_GRAPH = 1, WSG_OPT_TIMED_STAGE = 2 };
-/* WSG_OPT_FUSE_ATTN_O: 1 (default) = while the context fits one attention
- * split, each layer runs attention and the output projection as one launch
+/* WSG_OPT_FUSE_ATTN_O: 1 (default) = for contexts of up to 128 keys, each
+ * layer runs attention and the output projection as one launch
  * (the projection split by KV head into FP32 partials that the gate/up
  * launch sums in a fixed order); that launch is timed as WSG_STAGE_ATTN and
  * counts the output-projection weight bytes.  0 = separate attention and

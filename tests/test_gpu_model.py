@@ -9,7 +9,7 @@ at the end.  FP16 storage is checked teacher-forced at rtol=atol=2e-2.
 import numpy as np
 import pytest
 
-from gpu_util import _np, announce, gpu_available, lockstep
+from gpu_util import _np, announce, close_rel, gpu_available, lockstep
 import oracle
 from synth import MINI, PROMPT_SEEDS, QWEN3_0_6B, ModelShape, model_weights, model_weights_bf16, prompt_ids
 
@@ -39,14 +39,17 @@ def test_mini_fp32_generation_graph_and_direct(mini_w):
 def test_mini_fused_attention_output(mini_w, fuse, rows):
     """Attention fused with the output projection (KV-head partials summed by
     the gate/up launch) and the separate launches both match the oracle, and
-    give the same tokens; contexts cross the one-split limit (64 keys)."""
+    give the same tokens; contexts cross one attention split (64 keys) and the
+    fused limit (128 keys)."""
     import weight_streaming_gemv_amd as wsg
-    cap = 96
-    m = wsg.Model(MINI, mini_w, max_context=cap)
+    cap = 160
+    m = wsg.Model(MINI, mini_w, max_context=cap, prefill_chunk=64)
     m.set_option(wsg._abi.WSG_OPT_FUSE_ATTN_O, fuse)
     m.set_option(wsg._abi.WSG_OPT_ROWS_ATTN_O, rows)
     orc = oracle.OracleModel(MINI, mini_w, cap)
     prompt = prompt_ids(21, 58, MINI.vocab)
+    lockstep(m, orc, prompt, 12, label=f"mini fuse={fuse} rows={rows} short")
+    prompt = prompt_ids(21, 120, MINI.vocab)
     toks, _, ck = lockstep(m, orc, prompt, 12, label=f"mini fuse={fuse} rows={rows}")
     print(f"fuse={fuse} rows={rows}: max |dlogit| {ck.max_logit_err:.2e}")
     m.close()
@@ -100,6 +103,38 @@ def test_mini_many_splits(mini_w, n_prompt):
     orc = oracle.OracleModel(MINI, mini_w, cap)
     prompt = prompt_ids(10, n_prompt, MINI.vocab)
     lockstep(m, orc, prompt, 5, label=f"mini splits n={n_prompt}")
+    m.close()
+
+
+def test_rewind_repeats_a_forward(mini_w):
+    """Rewinding to slot p and stepping re-processes the recorded token at p: the same
+    bits every time (the fixed-slot repeat of the fixed-context harness); rewinding
+    further back matches the oracle's forward of the shorter prefix."""
+    import weight_streaming_gemv_amd as wsg
+    m = wsg.Model(MINI, mini_w, max_context=64, prefill_chunk=16)
+    prompt = prompt_ids(35, 10, MINI.vocab)
+    toks = [m.prefill(prompt), m.step()]
+    t2 = m.step()
+    ref_logits = _np(m.logits())
+    k, v, _ = m.kv(1)
+    ref_k, ref_v = _np(k[:, 11]), _np(v[:, 11])
+    for _ in range(3):
+        m.rewind(11)
+        assert m.position == 11
+        assert m.step() == t2
+        assert np.array_equal(_np(m.logits()), ref_logits)
+        k, v, _ = m.kv(1)
+        assert np.array_equal(_np(k[:, 11]), ref_k) and np.array_equal(_np(v[:, 11]), ref_v)
+    m.rewind(5)
+    m.step()
+    orc = oracle.OracleModel(MINI, mini_w, 64)
+    ref = orc.forward_rows(prompt[:6])
+    ok, err, _ = close_rel(_np(m.logits()), ref, 1e-3, 1e-3)
+    assert ok, err
+    with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+        m.rewind(-1)
+    with pytest.raises(wsg.WsgError, match="OUT_OF_RANGE"):
+        m.rewind(7)
     m.close()
 
 

@@ -194,6 +194,10 @@ class Model:
     def position(self) -> int:
         return _abi.lib().wsg_position(self.h)
 
+    def rewind(self, pos: int) -> None:
+        """Keep the first ``pos`` tokens; ``step()`` then re-processes the token at slot ``pos``."""
+        check(_abi.lib().wsg_rewind(self.h, pos))
+
     def set_prefill_chunk(self, rows: int) -> None:
         check(_abi.lib().wsg_set_prefill_chunk(self.h, rows))
 

@@ -8,7 +8,7 @@
 //   qkv     input RMSNorm (each wave normalises the 1024-float residual in
 //           registers) + fused Q/K/V GEMV; layer 0 also gathers the token's
 //           embedding row and writes it to the residual buffer
-//   attn_o  (contexts that fit one attention split) per-head Q/K RMSNorm +
+//   attn_o  (short contexts) per-head Q/K RMSNorm +
 //           RoPE + K/V cache write + grouped-query attention, fused with the
 //           output GEMV split by KV head: per-head partial sums, the first
 //           one carrying the residual
@@ -674,11 +674,11 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
 }
 
 // ------------------------------------------- attention + output projection
-// Contexts that fit one attention split: the output GEMV is split by KV
-// head.  Block (b, j) recomputes the attention of KV head j over all keys
-// (a few KiB per key range, read from L2 by the blocks of that head), then
-// multiplies its 4R rows of W_o restricted to head j's G*128 columns,
-// which it put in flight first:
+// Short contexts: the output GEMV is split by KV head.  Block (b, j)
+// recomputes the attention of KV head j over all keys (a few KiB per key
+// range, read from L2 by the blocks of that head), then multiplies its 4R
+// rows of W_o restricted to head j's G*128 columns, which it put in flight
+// first:
 //   part[j][m] = W_o[m, cols of head j] . o_j  (+ x[m] for j = 0).
 // The gate/up launch sums the partials in a fixed order.  Blocks b = 0
 // write the current token's key and value into the cache.

@@ -68,7 +68,7 @@ struct DecodeShape {
   int attn_splits;                                       // split-K blocks per KV head (grid.x)
   int attn_chunk;                                        // keys per split (a multiple of 16, >= 64)
   int head_waves;                                        // waves per head block (4, 8 or 16)
-  int fuse_attn_o;                                       // one-split contexts: fused attention + output GEMV
+  int fuse_attn_o;                                       // short contexts: fused attention + output GEMV
   int rows_attn_o;                                       // W_o rows per wave in the fused launch (4 or 8)
 };
 
@@ -78,8 +78,8 @@ bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L,
 // Combines the split-K partial states (needed when sh.attn_splits > 1).
 bool launch_attn_merge(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s);
 bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
-// Contexts within one attention split: attention fused with the output GEMV,
-// which writes per-KV-head partials into opart instead of x2.
+// Short contexts: attention fused with the output GEMV, which writes
+// per-KV-head partials into opart instead of x2.
 bool launch_attn_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
 // Partial slots (>= n_kv; slots past n_kv must hold zeros) the gate/up
 // prologue sums after a fused launch, or 0 if the shape cannot be fused.

@@ -214,7 +214,7 @@ struct wsg_model {
   bool has_output = false;
   int32_t* pin = nullptr;          // pinned staging: [0] token out, [1..] ids in
   bool use_graph = true;
-  std::map<int, hipGraphExec_t> graphs;   // key: splits*2 + head
+  std::map<int, hipGraphExec_t> graphs;   // key: splits*4 + fused*2 + advance
   int timed_stage = -1;
   std::vector<hipEvent_t> ev;
   int ev_used = 0;
@@ -274,14 +274,13 @@ bool timed(wsg_model* m, int stage, int64_t bytes, F&& launch) {
 }
 
 // All layers of one token; the last down projection advances the position
-// when no head follows (prompt rows before the last).  Contexts within one
-// attention split use the fused attention + output-projection launch.
-bool enqueue_body(wsg_model* m, int splits, bool advance) {
+// when no head follows (prompt rows before the last).  Short contexts (fused)
+// use the fused attention + output-projection launch.
+bool enqueue_body(wsg_model* m, int splits, bool fused, bool advance) {
   DecodeShape sh = m->shape;
   sh.attn_splits = splits;
   const hipStream_t s = m->stream;
   const int L = m->d.L;
-  const bool fused = sh.fuse_attn_o && splits == 1 && attn_o_part_slots(m->d.H, m->d.nkv) > 0;
   for (int l = 0; l < L; ++l) {
     const LayerPtrs& lp = m->layers[l];
     const DecodeArgs& a = m->args;
@@ -314,6 +313,15 @@ bool enqueue_argmax(wsg_model* m) { return launch_argmax(m->args, m->shape, m->s
 // rounded up to a power of two up to 8 and to a multiple of 8 beyond (one
 // captured graph per value; the rounded-up blocks find no keys and write
 // nothing, but still issue their speculative loads).
+// Contexts up to kFuseMaxKeys keys run attention fused with the output
+// projection (each of a KV head's 32 blocks reads that head's K/V prefix;
+// beyond this length the split-K path's parallelism over keys wins).
+constexpr int kFuseMaxKeys = 128;
+
+bool use_fused_attn_o(const wsg_model* m, int n_keys) {
+  return m->shape.fuse_attn_o && n_keys <= kFuseMaxKeys && attn_o_part_slots(m->d.H, m->d.nkv) > 0;
+}
+
 int splits_for(const wsg_model* m, int n_keys) {
   const int need = (n_keys + m->shape.attn_chunk - 1) / m->shape.attn_chunk;
   const int want = need <= 8 ? pow2_ceil(need) : (need + 7) / 8 * 8;
@@ -352,16 +360,18 @@ wsg_status graph_for(wsg_model* m, int key, F&& enqueue, hipGraphExec_t* out) {
 // and, if `head`, the head (final norm, vocabulary GEMV, argmax).
 wsg_status run_forward(wsg_model* m, bool head, int n_keys) {
   const int splits = splits_for(m, n_keys);
+  const bool fused = use_fused_attn_o(m, n_keys);
   const bool advance = !head;
   (void)hipGetLastError();   // errors of earlier calls were reported by those calls
   m->ev_used = 0;
   m->timed_bytes_per_launch_sum = 0;
   if (!m->use_graph) {
-    if (!enqueue_body(m, splits, advance)) return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape");
+    if (!enqueue_body(m, splits, fused, advance))
+      return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape");
   } else {
     hipGraphExec_t body = nullptr;
-    const wsg_status st = graph_for(m, splits * 2 + (advance ? 1 : 0),
-                                    [&] { return enqueue_body(m, splits, advance); }, &body);
+    const wsg_status st = graph_for(m, splits * 4 + (fused ? 2 : 0) + (advance ? 1 : 0),
+                                    [&] { return enqueue_body(m, splits, fused, advance); }, &body);
     if (st != WSG_OK) return st;
     WSG_HIP_CHECK(hipGraphLaunch(body, m->stream));
   }
@@ -646,6 +656,21 @@ wsg_status wsg_reset_cache(wsg_model* m) {
 }
 
 int32_t wsg_position(const wsg_model* m) { return m ? m->pos : -1; }
+
+wsg_status wsg_rewind(wsg_model* m, int32_t pos) {
+  clear_error();
+  if (!m) return fail(WSG_ERR_INVALID_ARG, "model is NULL");
+  if (pos < 0) return fail(WSG_ERR_INVALID_ARG, "pos=%d must be >= 0", pos);
+  if (pos > m->pos) return fail(WSG_ERR_OUT_OF_RANGE, "pos=%d is past the current position %d", pos, m->pos);
+  if (pos == m->pos) return WSG_OK;
+  (void)hipGetLastError();
+  launch_set_pos(m->args.ctrl, pos, m->stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(WSG_ERR_HIP, "rewind: %s", hipGetErrorString(e));
+  m->pos = pos;
+  m->has_output = true;   // the token history holds the token of slot pos
+  return WSG_OK;
+}
 
 wsg_status wsg_prefill(wsg_model* m, const int32_t* host_ids, int32_t n, int32_t* out_token, const void** out_logits) {
   clear_error();
