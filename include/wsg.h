@@ -154,6 +154,31 @@ wsg_status wsg_prefill(wsg_model* m, const int32_t* host_ids, int32_t n,
  * previous output (WSG_ERR_STATE); pos == max_context. */
 wsg_status wsg_step(wsg_model* m, int32_t in_token, int32_t* out_token, const void** out_logits);
 
+/* Two-token step: the verify pass of greedy speculative decoding, in which
+ * each weight matrix is streamed once for two input vectors ("Our Kernel
+ * Benchmark Was Measuring the System Cache", "Why it mattered, concretely":
+ * the two-token matvec variant serving the speculative pass).  Row 0
+ * consumes in_token (or, if in_token < 0, the previous greedy output) at
+ * position pos; row 1 consumes `draft`, a guess of row 0's greedy token, at
+ * pos + 1.  Both rows' K/V are appended in the one pass, and each row's
+ * greedy token is returned: out_tokens[0] follows row 0, out_tokens[1]
+ * follows row 1.  The draft is accepted when it equals out_tokens[0]; then
+ * both tokens are emitted (*n_emitted = 2, position pos + 2), else only
+ * out_tokens[0] is (*n_emitted = 1, position pos + 1; slot pos + 1 still
+ * holds the rejected draft's K/V until the next call rewrites it, and
+ * out_tokens[1] is meaningless).  The same rule is applied on the device,
+ * so a following wsg_step or wsg_step2 with in_token < 0 continues from the
+ * last emitted token.  Every emitted token equals what the same number of
+ * wsg_step calls would produce, up to floating-point rounding.
+ * *out_logits (if not NULL) receives a device pointer to both rows' logits,
+ * [2][vocab] in the storage dtype, valid until the next call.  Blocks until
+ * the two token ids (8 bytes) are on the host.  Errors: a NULL out_tokens or
+ * n_emitted (WSG_ERR_INVALID_ARG); in_token >= vocab or draft outside
+ * [0, vocab) (WSG_ERR_OUT_OF_RANGE); in_token < 0 with no previous output
+ * (WSG_ERR_STATE); pos + 2 > max_context (WSG_ERR_OUT_OF_RANGE). */
+wsg_status wsg_step2(wsg_model* m, int32_t in_token, int32_t draft, int32_t out_tokens[2], int32_t* n_emitted,
+                     const void** out_logits);
+
 /* Current position (number of valid KV entries). */
 int32_t wsg_position(const wsg_model* m);
 

@@ -98,6 +98,18 @@ def test_model_create_rejects_bad_buffers(abi):
     assert b"aligned" in L.wsg_last_error()
 
 
+def test_model_calls_reject_null(abi):
+    """Model entry points validate their pointers before touching the device."""
+    L = abi.lib()
+    toks = (C.c_int32 * 2)()
+    n = C.c_int32()
+    lp = C.c_void_p()
+    assert L.wsg_step2(None, -1, 0, toks, C.byref(n), C.byref(lp)) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_step(None, -1, C.byref(n), C.byref(lp)) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_rewind(None, 0) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_position(None) == -1
+
+
 def test_pack_weights_layout_is_bit_copy(abi):
     """The packer concatenates Wq|Wk|Wv and Wg|Wu and copies every value bit for bit."""
     from synth import MINI, model_weights

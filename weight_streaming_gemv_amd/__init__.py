@@ -181,6 +181,7 @@ class Model:
         check(_abi.lib().wsg_prefill(self.h, a.ctypes.data_as(C.POINTER(C.c_int32)), a.size, C.byref(tok),
                                      C.byref(lp)))
         self._logits_ptr = lp.value
+        self._logits_rows = 1
         return tok.value
 
     def step(self, in_token: int = -1) -> int:
@@ -188,7 +189,22 @@ class Model:
         lp = C.c_void_p()
         check(_abi.lib().wsg_step(self.h, int(in_token), C.byref(tok), C.byref(lp)))
         self._logits_ptr = lp.value
+        self._logits_rows = 1
         return tok.value
+
+    def step2(self, draft: int, in_token: int = -1) -> Tuple[Tuple[int, int], int]:
+        """Two-token step: ``in_token`` (default: the last output) at p, ``draft`` at p + 1.
+
+        Returns ((token after row 0, token after row 1), tokens emitted): 2 when the
+        draft equals the first token, else 1 (the second token is then meaningless).
+        """
+        toks = (C.c_int32 * 2)()
+        n = C.c_int32()
+        lp = C.c_void_p()
+        check(_abi.lib().wsg_step2(self.h, int(in_token), int(draft), toks, C.byref(n), C.byref(lp)))
+        self._logits_ptr = lp.value
+        self._logits_rows = 2
+        return (toks[0], toks[1]), n.value
 
     @property
     def position(self) -> int:
@@ -223,8 +239,11 @@ class Model:
         return {"packed_matrices": pk.value, "decode_matrices": tot.value, "decode_weight_bytes": b.value}
 
     def logits(self):
-        """Last logits [vocab] (device tensor view, storage dtype)."""
-        return self._view(self._logits_ptr, self.shape.vocab)
+        """Last logits (device tensor view, storage dtype): [vocab] after prefill/step,
+        [2, vocab] after step2."""
+        rows = getattr(self, "_logits_rows", 1)
+        v = self._view(self._logits_ptr, rows * self.shape.vocab)
+        return v if rows == 1 else v.view(rows, self.shape.vocab)
 
     def kv(self, layer: int):
         """(K, V, valid_len): device views [n_kv, max_context, head_dim]."""

@@ -64,6 +64,8 @@ _SIGS = {
     "wsg_prefill": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.POINTER(C.c_int32),
                               C.POINTER(C.c_void_p)]),
     "wsg_step": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_void_p)]),
+    "wsg_step2": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                            C.POINTER(C.c_void_p)]),
     "wsg_position": (C.c_int32, [C.c_void_p]),
     "wsg_kv_view": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
                               C.POINTER(C.c_int32)]),

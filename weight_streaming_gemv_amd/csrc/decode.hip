@@ -137,7 +137,9 @@ __device__ __forceinline__ float rows_prefetch(const TS* __restrict__ base, int 
 }
 
 // ------------------------------------------------------------------ qkv
-template <typename TS, typename TW, int H, int R>
+// T query rows (a T-token step: positions p .. p+T-1) share every weight
+// row streamed: activations and outputs are [T][.] arrays.
+template <typename TS, typename TW, int H, int R, int T>
 __global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const TS* __restrict__ in_norm,
                                                 TS* __restrict__ x_res, const TS* __restrict__ embed,
                                                 const int32_t* __restrict__ ids, const int32_t* __restrict__ ctrl,
@@ -147,96 +149,120 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const 
   const int ngroups = ceil_div(M, R);
   int g = wave_row_groups_begin();
   WRows<TW, H, R> w;
-  Act<TS, H> x;
+  Act<TS, H> x[T];
   // Vector loads return in issue order: the residual goes out before the
   // first weight rows (so the norm overlaps them); at layer 0 the
   // position -> id -> embedding chain is issued after them.
-  if (!first_layer) x.load(x_res);
+  if (!first_layer)
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t].load(x_res + t * H);
   __builtin_amdgcn_sched_barrier(0);
   w.load(W, g * R, M);   // rows clamped into W: no branch around the loads
   __builtin_amdgcn_sched_barrier(0);
   if (first_layer) {
     const int pos = ctrl[kCtrlPos];
-    int tok = ids[pos];
-    tok = (tok < 0 || tok >= vocab) ? 0 : tok;   // ids are validated on the host; never read outside E
-    x.load(embed + (size_t)tok * H);
-    if (blockIdx.x == 0 && wave_id() == 0) x.store(x_res);
-    if (blockIdx.x == 0 && wave_id() == 1) {
-      // the rotary row of position p, for every attention launch of this
-      // token (their loads then do not wait for the position)
+    const int wave = wave_id();
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      int tok = ids[pos + t];
+      tok = (tok < 0 || tok >= vocab) ? 0 : tok;   // ids are validated on the host; never read outside E
+      x[t].load(embed + (size_t)tok * H);
+      if (blockIdx.x == 0 && wave == t) x[t].store(x_res + t * H);
+    }
+    static_assert(2 * T <= kWavesPerBlock, "a wave per residual row and per rotary row");
+    if (blockIdx.x == 0 && wave >= T && wave < 2 * T) {
+      // the rotary row of position p + t, for every attention launch of this
+      // step (their loads then do not wait for the position)
       static_assert(kD / 2 == kWave, "one rotary pair per lane");
-      const int lane = lane_id();
-      rope_cur[lane] = rope_cos[(size_t)pos * (kD / 2) + lane];
-      rope_cur[kD / 2 + lane] = rope_sin[(size_t)pos * (kD / 2) + lane];
+      const int lane = lane_id(), t = wave - T;
+      rope_cur[t * kD + lane] = rope_cos[(size_t)(pos + t) * (kD / 2) + lane];
+      rope_cur[t * kD + kD / 2 + lane] = rope_sin[(size_t)(pos + t) * (kD / 2) + lane];
     }
   }
-  x.rms_norm(in_norm, eps);
+#pragma unroll
+  for (int t = 0; t < T; ++t) x[t].rms_norm(in_norm, eps);
   const int lane = lane_id();
   for (; g < ngroups; g += wave_row_groups_stride()) {
-    float acc[R];
-    w.dot(x, acc);
+    float acc[T][R];
+#pragma unroll
+    for (int t = 0; t < T; ++t) w.dot(x[t], acc[t]);
     const int next = g + wave_row_groups_stride();
     if (next < ngroups) w.load(W, next * R, M);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float s = wave_sum(acc[r]);
-      if (lane == 0 && g * R + r < M) out[g * R + r] = Store<TS>::from_f(s);
-    }
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float s = wave_sum(acc[t][r]);
+        if (lane == 0 && g * R + r < M) out[(size_t)t * M + g * R + r] = Store<TS>::from_f(s);
+      }
   }
 }
 
 // ------------------------------------------------------------ o / down
-// x_out[m] = x_in[m] + W[m] . in  for m < M (M = hidden); the residual
-// ping-pongs between two buffers, so no kernel rewrites what it reads.
-template <typename TS, typename TW, int K, int R>
+// x_out[t][m] = x_in[t][m] + W[m] . in[t]  for m < M (M = hidden), t < T;
+// the residual ping-pongs between two buffers, so no kernel rewrites what
+// it reads.
+template <typename TS, typename TW, int K, int R, int T>
 __global__ __launch_bounds__(kBlock) void k_gemv_residual(const TW* __restrict__ W, const TS* __restrict__ in,
                                                           const TS* __restrict__ x_in, TS* __restrict__ x_out, int M,
                                                           int32_t* __restrict__ ctrl, int advance_pos) {
   const int ngroups = ceil_div(M, R);
   int g = wave_row_groups_begin();
   // operands first, then the weight rows (vector loads return in issue order)
-  Act<TS, K> x;
-  x.load(in);
-  float xr = rows_prefetch<TS, R>(x_in, g * R, M);
+  Act<TS, K> x[T];
+  float xr[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    x[t].load(in + t * K);
+    xr[t] = rows_prefetch<TS, R>(x_in + t * M, g * R, M);
+  }
   __builtin_amdgcn_sched_barrier(0);
   WRows<TW, K, R> w;
   w.load(W, g * R, M);   // rows clamped into W: no branch around the loads
   __builtin_amdgcn_sched_barrier(0);
   const int lane = lane_id();
   for (; g < ngroups; g += wave_row_groups_stride()) {
-    float acc[R];
-    w.dot(x, acc);
+    float acc[T][R];
+#pragma unroll
+    for (int t = 0; t < T; ++t) w.dot(x[t], acc[t]);
     const int next = g + wave_row_groups_stride();
-    float xr_next = 0.f;
+    float xr_next[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xr_next[t] = 0.f;
     if (next < ngroups) {
-      xr_next = rows_prefetch<TS, R>(x_in, next * R, M);
+#pragma unroll
+      for (int t = 0; t < T; ++t) xr_next[t] = rows_prefetch<TS, R>(x_in + t * M, next * R, M);
       w.load(W, next * R, M);
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float s = wave_sum(acc[r]);
-      const int m = g * R + r;
-      if (lane == 0 && m < M) x_out[m] = Store<TS>::from_f(lane_value(xr, r) + s);
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float s = wave_sum(acc[t][r]);
+        const int m = g * R + r;
+        if (lane == 0 && m < M) x_out[(size_t)t * M + m] = Store<TS>::from_f(lane_value(xr[t], r) + s);
+      }
+      xr[t] = xr_next[t];
     }
-    xr = xr_next;
   }
   // (no kernel of this launch reads the position)
-  if (advance_pos && blockIdx.x == 0 && threadIdx.x == 0) ctrl[kCtrlPos] = ctrl[kCtrlPos] + 1;
+  if (advance_pos && blockIdx.x == 0 && threadIdx.x == 0) ctrl[kCtrlPos] = ctrl[kCtrlPos] + T;
 }
 
 // -------------------------------------------------------------- gate/up
 // Partial vectors (float4 loads per thread) the gate/up prologue holds in
-// registers: ceil(H / 1024) * slots <= kMaxPartVec; other shapes use the
-// separate attention and output-projection launches.
+// registers: T * ceil(H / 1024) * slots <= kMaxPartVec; other shapes use
+// the separate attention and output-projection launches.
 constexpr int kMaxPartVec = 16;
 
-// act[m] = silu(Wg[m] . b) * (Wu[m] . b), b = rms(x2, post_norm); Wgu holds
-// the I gate rows followed by the I up rows.  With NP > 0 the residual x2
-// arrives as NP FP32 partial vectors (the KV-head split of the fused
-// attention/output launch, the first carrying the residual; slots past the
-// KV head count hold zeros): every block sums them in the same order,
-// rounds as stored, and block 0 writes x2 for the down projection.
-template <typename TS, typename TW, int H, int R, int NP>
+// act[t][m] = silu(Wg[m] . b_t) * (Wu[m] . b_t), b_t = rms(x2[t], post_norm);
+// Wgu holds the I gate rows followed by the I up rows.  With NP > 0 the
+// residual x2[t] arrives as NP FP32 partial vectors (the KV-head split of
+// the fused attention/output launch, the first carrying the residual;
+// slots past the KV head count hold zeros), at opart[(t*NP + slot)*H]:
+// every block sums them in the same order, rounds as stored, and block 0
+// writes x2 for the down projection.
+template <typename TS, typename TW, int H, int R, int NP, int T>
 __global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, const TS* __restrict__ post_norm,
                                                    const TS* __restrict__ x_res, const float* __restrict__ opart,
                                                    float eps, TS* __restrict__ act, int I, TS* __restrict__ x2_out) {
@@ -244,23 +270,25 @@ __global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, c
   const TW* Wu = Wgu + (size_t)I * H;
   const int tid = threadIdx.x;
   int g = wave_row_groups_begin();
-  Act<TS, H> x;
+  Act<TS, H> x[T];
   WRows<TW, H, R> wg, wu;
   if constexpr (NP > 0) {
     // Vector loads return in issue order, so the partials (this thread's
     // float4 column of every partial, for each 1024-wide slice of x2) go out
     // before the weight rows, and their sum overlaps the weight stream.
     constexpr int NC = ceil_div(H, 4 * kBlock);
-    static_assert(NC * NP <= kMaxPartVec, "partials held in registers");
-    __shared__ float s_x[NC * 4 * kBlock];   // padded: every thread writes its column
-    f4_t pv[NP][NC];
+    static_assert(T * NC * NP <= kMaxPartVec, "partials held in registers");
+    __shared__ float s_x[T][NC * 4 * kBlock];   // padded: every thread writes its column
+    f4_t pv[T][NP][NC];
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int i = min(4 * (c * kBlock + tid), H - 4);
-        pv[p][c] = *reinterpret_cast<const f4_t*>(opart + (size_t)p * H + i);
-      }
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int i = min(4 * (c * kBlock + tid), H - 4);
+          pv[t][p][c] = *reinterpret_cast<const f4_t*>(opart + (size_t)(t * NP + p) * H + i);
+        }
     __builtin_amdgcn_sched_barrier(0);   // partials before weights
     wg.load(Wgu, g * R, I);   // rows clamped into W: no branch around the loads
     wu.load(Wu, g * R, I);
@@ -268,46 +296,56 @@ __global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, c
     // (the sums are used unconditionally, so the loads are not sunk into a
     // branch below the weight loads)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int i = 4 * (c * kBlock + tid);
-      f4_t v = pv[0][c];
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int p = 1; p < NP; ++p) v += pv[p][c];
-      TS t[4];
+      for (int c = 0; c < NC; ++c) {
+        const int i = 4 * (c * kBlock + tid);
+        f4_t v = pv[t][0][c];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t[e] = Store<TS>::from_f(v[e]);
-        v[e] = Store<TS>::to_f(t[e]);
+        for (int p = 1; p < NP; ++p) v += pv[t][p][c];
+        TS s4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s4[e] = Store<TS>::from_f(v[e]);
+          v[e] = Store<TS>::to_f(s4[e]);
+        }
+        *reinterpret_cast<f4_t*>(&s_x[t][i]) = v;
+        if (blockIdx.x == 0 && i < H)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x2_out[t * H + i + e] = s4[e];
       }
-      *reinterpret_cast<f4_t*>(s_x + i) = v;
-      if (blockIdx.x == 0 && i < H)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x2_out[i + e] = t[e];
-    }
     __syncthreads();
-    x.load_f32(s_x);
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t].load_f32(s_x[t]);
   } else {
-    x.load(x_res);
+#pragma unroll
+    for (int t = 0; t < T; ++t) x[t].load(x_res + t * H);
     __builtin_amdgcn_sched_barrier(0);
     wg.load(Wgu, g * R, I);   // rows clamped into W: no branch around the loads
     wu.load(Wu, g * R, I);
     __builtin_amdgcn_sched_barrier(0);
   }
-  x.rms_norm(post_norm, eps);
+#pragma unroll
+  for (int t = 0; t < T; ++t) x[t].rms_norm(post_norm, eps);
   const int lane = lane_id();
   for (; g < ngroups; g += wave_row_groups_stride()) {
-    float ga[R], ua[R];
-    wg.dot(x, ga);
-    wu.dot(x, ua);
+    float ga[T][R], ua[T][R];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      wg.dot(x[t], ga[t]);
+      wu.dot(x[t], ua[t]);
+    }
     const int next = g + wave_row_groups_stride();
     if (next < ngroups) { wg.load(Wgu, next * R, I); wu.load(Wu, next * R, I); }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float gs = wave_sum(ga[r]);
-      const float us = wave_sum(ua[r]);
-      const int m = g * R + r;
-      if (lane == 0 && m < I) act[m] = Store<TS>::from_f(gs / (1.0f + expf(-gs)) * us);
-    }
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float gs = wave_sum(ga[t][r]);
+        const float us = wave_sum(ua[t][r]);
+        const int m = g * R + r;
+        if (lane == 0 && m < I) act[(size_t)t * I + m] = Store<TS>::from_f(gs / (1.0f + expf(-gs)) * us);
+      }
   }
 }
 
@@ -330,85 +368,129 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
   return k;
 }
 
-// The head writes one argmax key per block; a one-block kernel then reduces
-// them (the pages' two argmax kernels, Megakernels, "GPU-wide end-to-end
-// generation").  A single fused launch would need a device-scope release
-// fence per block, and on this multi-XCD part each such fence writes back
-// the issuing XCD's L2, which costs far more than the extra launch.
-template <typename TS, typename TW, int H, int R, int WPB>
+// The head writes one argmax key per block and row; a one-block kernel then
+// reduces them (the pages' two argmax kernels, Megakernels, "GPU-wide
+// end-to-end generation").  A single fused launch would need a device-scope
+// release fence per block, and on this multi-XCD part each such fence
+// writes back the issuing XCD's L2, which costs far more than the extra
+// launch.  Row t's logits go to logits[t*V], its block keys to
+// am_part[t*gridDim.x].
+template <typename TS, typename TW, int H, int R, int WPB, int T>
 __global__ __launch_bounds__(WPB * kWave) void k_head(const TW* __restrict__ E, const TS* __restrict__ final_norm,
                                                       const TS* __restrict__ x_res, float eps, TS* __restrict__ logits,
                                                       int V, unsigned long long* __restrict__ am_part) {
-  __shared__ unsigned long long best_wave[WPB];
+  __shared__ unsigned long long best_wave[T][WPB];
   const int lane = lane_id();
   const int ngroups = ceil_div(V, R);
   int g = blockIdx.x * WPB + wave_id();
   const int stride = gridDim.x * WPB;
   WRows<TW, H, R> w;
   if (g < ngroups) w.load(E, g * R, V);   // first rows in flight before the norm
-  Act<TS, H> x;
-  x.load(x_res);
-  x.rms_norm(final_norm, eps);
-  unsigned long long best = 0;   // below every real key
+  Act<TS, H> x[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    x[t].load(x_res + t * H);
+    x[t].rms_norm(final_norm, eps);
+  }
+  unsigned long long best[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) best[t] = 0;   // below every real key
   for (; g < ngroups; g += stride) {
-    float acc[R];
-    w.dot(x, acc);
+    float acc[T][R];
+#pragma unroll
+    for (int t = 0; t < T; ++t) w.dot(x[t], acc[t]);
     const int next = g + stride;
     if (next < ngroups) w.load(E, next * R, V);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float s = wave_sum(acc[r]);
-      const int m = g * R + r;
-      if (m < V) {
-        const TS stored = Store<TS>::from_f(s);
-        if (lane == 0) logits[m] = stored;
-        const unsigned long long k = argmax_key(Store<TS>::to_f(stored), m);
-        best = k > best ? k : best;
-      }
-    }
-  }
-  if (lane == 0) best_wave[wave_id()] = best;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long b = best_wave[0];
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int w2 = 1; w2 < WPB; ++w2) b = best_wave[w2] > b ? best_wave[w2] : b;
-    am_part[blockIdx.x] = b;
+      for (int r = 0; r < R; ++r) {
+        const float s = wave_sum(acc[t][r]);
+        const int m = g * R + r;
+        if (m < V) {
+          const TS stored = Store<TS>::from_f(s);
+          if (lane == 0) logits[(size_t)t * V + m] = stored;
+          const unsigned long long k = argmax_key(Store<TS>::to_f(stored), m);
+          best[t] = k > best[t] ? k : best[t];
+        }
+      }
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int t = 0; t < T; ++t) best_wave[t][wave_id()] = best[t];
+  __syncthreads();
+  if (threadIdx.x < T) {
+    const int t = threadIdx.x;
+    unsigned long long b = best_wave[t][0];
+#pragma unroll
+    for (int w2 = 1; w2 < WPB; ++w2) b = best_wave[t][w2] > b ? best_wave[t][w2] : b;
+    am_part[(size_t)t * gridDim.x + blockIdx.x] = b;
   }
 }
 
-// One block of 1024 threads reads the n block keys (n even: the head grid
-// is rounded up to an even count, a block without rows writes key 0) as
-// 16-byte pairs: thread t takes pairs t + 1024k for k < PER, all loads
-// issued before the first compare; pair indices past the last are clamped
-// to it instead of branched on (a repeated key cannot change a maximum).
-template <int PER>
+// One block of 1024 threads reads the n block keys of each of the T rows
+// (n even: the head grid is rounded up to an even count, a block without
+// rows writes key 0) as 16-byte pairs: thread i takes pairs i + 1024k for
+// k < PER, all loads issued before the first compare; pair indices past
+// the last are clamped to it instead of branched on (a repeated key cannot
+// change a maximum).
+//
+// Row t's token goes to ctrl[kCtrlRowTok + t].  One row (a decode step):
+// it is also the output token, the next history entry, and the position
+// advances by one.  Two rows (a two-token step whose second input is a
+// draft of the first row's token): the draft is accepted when it equals
+// row 0's greedy token; then both tokens are emitted and the position
+// advances by two, else only row 0's token is emitted (slot p + 1 then
+// holds the rejected draft's key and value, which the next step
+// overwrites) and the position advances by one.  The history receives the
+// emitted tokens, so a following step continues from the last one.
+template <int PER, int T>
 __global__ __launch_bounds__(1024) void k_argmax(const unsigned long long* __restrict__ am_part, int n,
                                                  int32_t* __restrict__ ctrl, int32_t* __restrict__ ids) {
-  __shared__ unsigned long long red[1024 / kWave];
+  static_assert(T == 1 || T == 2, "one- and two-token steps");
+  __shared__ unsigned long long red[T][1024 / kWave];
   typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
   const u64x2_t* pairs = reinterpret_cast<const u64x2_t*>(am_part);
-  const int last = n / 2 - 1;
-  u64x2_t k[PER];
+  const int half = n / 2, last = half - 1;
+  u64x2_t k[T][PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) k[i] = pairs[min((int)threadIdx.x + 1024 * i, last)];
-  unsigned long long b = 0;
+  for (int t = 0; t < T; ++t)
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    b = k[i].x > b ? k[i].x : b;
-    b = k[i].y > b ? k[i].y : b;
+    for (int i = 0; i < PER; ++i) k[t][i] = pairs[t * half + min((int)threadIdx.x + 1024 * i, last)];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    unsigned long long b = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      b = k[t][i].x > b ? k[t][i].x : b;
+      b = k[t][i].y > b ? k[t][i].y : b;
+    }
+    b = wave_max_u64(b);
+    if (lane_id() == 0) red[t][threadIdx.x >> 6] = b;
   }
-  b = wave_max_u64(b);
-  if (lane_id() == 0) red[threadIdx.x >> 6] = b;
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) b = red[w] > b ? red[w] : b;
-    int tok = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
-    if (b == 0) tok = 0;   // no block key at all (cannot happen with vocab >= 1)
+    int tok[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      unsigned long long b = red[t][0];
+      for (int w = 1; w < (int)(blockDim.x >> 6); ++w) b = red[t][w] > b ? red[t][w] : b;
+      tok[t] = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
+      if (b == 0) tok[t] = 0;   // no block key at all (cannot happen with vocab >= 1)
+      ctrl[kCtrlRowTok + t] = tok[t];
+    }
     const int pos = ctrl[kCtrlPos];
-    ctrl[kCtrlOutTok] = tok;
-    ids[pos + 1] = tok;
-    ctrl[kCtrlPos] = pos + 1;
+    if constexpr (T == 1) {
+      ctrl[kCtrlOutTok] = tok[0];
+      ids[pos + 1] = tok[0];
+      ctrl[kCtrlPos] = pos + 1;
+    } else {
+      const int accepted = ids[pos + 1] == tok[0] ? 1 : 0;
+      ids[pos + 1] = tok[0];
+      if (accepted) ids[pos + 2] = tok[1];
+      ctrl[kCtrlOutTok] = accepted ? tok[1] : tok[0];
+      ctrl[kCtrlPos] = pos + 1 + accepted;
+    }
   }
 }
 
@@ -504,28 +586,32 @@ struct SoftState {
   }
 };
 
-// Partial state layout: for each (kv head, split, g): [m, l, acc[128]].
+// Partial state layout: for each (row, kv head, split, g): [m, l, acc[128]].
 constexpr int kPartStride = 2 + kD;
 
-// The attention of one KV head j (its G query heads) over the keys
-// [k_begin, k_end) of the sequence at position p, spread over the 16
-// 16-lane rows of a 256-thread block: row sid takes keys k_begin + sid +
-// 16u.  prefetch() issues every load that does not depend on p (raw
-// queries, the current token's key and value, the rotary row of p, the
-// norm gains, and each row's first four cached keys, clamped into the
-// cache: keys past p are loaded but never used), so they are in flight
-// together with the read of p.
-template <typename TS, int G>
+// The attention of one KV head j (its G query heads) for one query row at
+// position p, over the keys [k_begin, k_end), spread over NR 16-lane rows
+// of the block (16 for one query row per block; 8 each when two rows share
+// a block): key-row sid takes keys k_begin + sid + NR*u.  prefetch() issues
+// every load that does not depend on p (raw queries, the row's current key
+// and value, its rotary row, the norm gains, and each key-row's first four
+// cached keys, clamped into the cache: keys past p are loaded but never
+// used), so they are in flight together with the read of p.  With PREV the
+// row is the second of a two-token step and also folds in the first row's
+// key and value (slot p - 1, written by another block of the same launch),
+// recomputed here from the first row's projections.
+template <typename TS, int G, int NR, bool PREV>
 struct HeadAttn {
   float q[G][8], kc[8], vc[8], k4[4][8], v4[4][8], c[4], s[4], gq[8], gk[8];
+  float kp[PREV ? 8 : 1], vp[PREV ? 8 : 1], cp[PREV ? 4 : 1], sp[PREV ? 4 : 1];
 
   __device__ __forceinline__ void prefetch(const TS* __restrict__ qkv, const TS* __restrict__ kh,
                                            const TS* __restrict__ vh, const TS* __restrict__ q_norm,
-                                           const TS* __restrict__ k_norm, const float* __restrict__ rope_cur,
+                                           const TS* __restrict__ k_norm, const float* __restrict__ rope,
                                            int j, int Q, int KV, int cap, int k_begin, int sid, int sl) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int kk = min(k_begin + sid + 16 * u, cap - 1);
+      const int kk = min(k_begin + sid + NR * u, cap - 1);
       load_head8<TS>(kh + (size_t)kk * kD, sl, k4[u]);
       load_head8<TS>(vh + (size_t)kk * kD, sl, v4[u]);
     }
@@ -533,19 +619,33 @@ struct HeadAttn {
     for (int g = 0; g < G; ++g) load_head8<TS>(qkv + (size_t)(j * G + g) * kD, sl, q[g]);
     load_head8<TS>(qkv + Q + (size_t)j * kD, sl, kc);
     load_head8<TS>(qkv + Q + KV + (size_t)j * kD, sl, vc);
-    const float4 cv = *reinterpret_cast<const float4*>(rope_cur + 4 * sl);
-    const float4 sv = *reinterpret_cast<const float4*>(rope_cur + kD / 2 + 4 * sl);
-    c[0] = cv.x; c[1] = cv.y; c[2] = cv.z; c[3] = cv.w;
-    s[0] = sv.x; s[1] = sv.y; s[2] = sv.z; s[3] = sv.w;
+    load_rope4(rope, sl, c, s);
     load_head8<TS>(q_norm, sl, gq);
     load_head8<TS>(k_norm, sl, gk);
   }
+  // The first row's raw key/value and rotary row (PREV only).
+  __device__ __forceinline__ void prefetch_prev(const TS* __restrict__ qkv_prev, const float* __restrict__ rope_prev,
+                                                int j, int Q, int KV, int sl) {
+    if constexpr (PREV) {
+      load_head8<TS>(qkv_prev + Q + (size_t)j * kD, sl, kp);
+      load_head8<TS>(qkv_prev + Q + KV + (size_t)j * kD, sl, vp);
+      load_rope4(rope_prev, sl, cp, sp);
+    }
+  }
+  static __device__ __forceinline__ void load_rope4(const float* rope, int sl, float (&c4)[4], float (&s4)[4]) {
+    const float4 cv = *reinterpret_cast<const float4*>(rope + 4 * sl);
+    const float4 sv = *reinterpret_cast<const float4*>(rope + kD / 2 + 4 * sl);
+    c4[0] = cv.x; c4[1] = cv.y; c4[2] = cv.z; c4[3] = cv.w;
+    s4[0] = sv.x; s4[1] = sv.y; s4[2] = sv.z; s4[3] = sv.w;
+  }
 
-  // Cached keys [k_begin, k_stop); with has_cur the current token's
-  // key/value (slot p) are normalised, rotated and folded in from registers
-  // by row 0 of wave 0, which also writes slot p when write_cur is set.
+  // Cached keys [k_begin, k_stop); then, with has_prev, the first row's key
+  // (slot p - 1); then, with has_cur, this row's key/value (slot p),
+  // normalised, rotated and folded in from registers by key-row 0, which
+  // also writes slot p when write_cur is set.
   __device__ __forceinline__ void run(TS* __restrict__ kh, TS* __restrict__ vh, int pos, int k_begin, int k_stop,
-                                      bool has_cur, bool write_cur, float eps, int sid, int sl, SoftState<G>& st) {
+                                      bool has_prev, bool has_cur, bool write_cur, float eps, int sid, int sl,
+                                      SoftState<G>& st) {
     // queries: normalised, rotated, rounded as stored, then pre-scaled by
     // log2(e)/sqrt(D) so that scores are in the log2 domain
     const float qscale = kLog2e / sqrtf((float)kD);
@@ -557,21 +657,28 @@ struct HeadAttn {
       for (int i = 0; i < 8; ++i) q[g][i] *= qscale;
     }
     st.init();
-    // the first four keys of the row are in registers already; longer
+    // the first four keys of the key-row are in registers already; longer
     // ranges continue in groups of four with all loads in flight first
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (k_begin + sid + 16 * u < k_stop) st.add(q, k4[u], v4[u]);
-    for (int key = k_begin + sid + 64; key < k_stop; key += 64) {
+      if (k_begin + sid + NR * u < k_stop) st.add(q, k4[u], v4[u]);
+    for (int key = k_begin + sid + 4 * NR; key < k_stop; key += 4 * NR) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (key + 16 * u < k_stop) {
-          load_head8<TS>(kh + (size_t)(key + 16 * u) * kD, sl, k4[u]);
-          load_head8<TS>(vh + (size_t)(key + 16 * u) * kD, sl, v4[u]);
+        if (key + NR * u < k_stop) {
+          load_head8<TS>(kh + (size_t)(key + NR * u) * kD, sl, k4[u]);
+          load_head8<TS>(vh + (size_t)(key + NR * u) * kD, sl, v4[u]);
         }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (key + 16 * u < k_stop) st.add(q, k4[u], v4[u]);
+        if (key + NR * u < k_stop) st.add(q, k4[u], v4[u]);
+    }
+    if constexpr (PREV) {
+      if (has_prev) {
+        norm_rope8(kp, gk, cp, sp, eps);
+        round_to_store<TS>(kp);
+        if (sid == 0) st.add(q, kp, vp);
+      }
     }
     if (has_cur) {
       norm_rope8(kc, gk, c, s, eps);
@@ -587,11 +694,11 @@ struct HeadAttn {
   }
 };
 
-// LDS merge of the 16 row states of a block.
-template <int G>
+// LDS merge of the NR key-row states of one query row.
+template <int G, int NR>
 struct RowMerge {
-  float m[16][G], l[16][G];
-  float acc[16][G][kD];
+  float m[NR][G], l[NR][G];
+  float acc[NR][G][kD];
 
   __device__ __forceinline__ void put(const SoftState<G>& st, int sid, int sl) {
 #pragma unroll
@@ -608,11 +715,11 @@ struct RowMerge {
   __device__ __forceinline__ void get(int g, int d, float& mx, float& L, float& A) const {
     mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, m[r][g]);
+    for (int r = 0; r < NR; ++r) mx = fmaxf(mx, m[r][g]);
     L = 0.f;
     A = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < NR; ++r) {
       const float w = exp2f(m[r][g] - mx);   // rows without keys: exp2(-inf) = 0
       L = fmaf(l[r][g], w, L);
       A = fmaf(acc[r][g][d], w, A);
@@ -620,52 +727,60 @@ struct RowMerge {
   }
 };
 
-template <typename TS, int G>
+// Split-K attention: block (split, j, t) covers the keys of split for query
+// row t (position p + t of a T-token step).
+template <typename TS, int G, int T>
 __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
                                                  TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
                                                  const TS* __restrict__ k_norm, const float* __restrict__ rope_cur,
                                                  const int32_t* __restrict__ ctrl, int n_q, int n_kv, int cap,
                                                  float eps, int chunk, float* __restrict__ part,
                                                  TS* __restrict__ o) {
-  __shared__ RowMerge<G> sm;
+  constexpr bool PREV = T > 1;
+  __shared__ RowMerge<G, 16> sm;
   const int j = blockIdx.y;            // KV head
   const int split = blockIdx.x;
+  const int t = blockIdx.z;            // query row
   const int lane = lane_id(), wave = wave_id();
   const int sid = wave * 4 + (lane >> 4), sl = lane & 15;
   const size_t head_off = (size_t)j * cap * kD;
+  const int Q = n_q * kD, KV = n_kv * kD, M = Q + 2 * KV;
   TS* kh = k_cache + head_off;
   TS* vh = v_cache + head_off;
 
   // Every split covers the fixed key range [split*chunk, split*chunk + chunk)
   // (chunk is a per-model constant), so its first keys can be loaded before p.
   const int k_begin = split * chunk;
-  HeadAttn<TS, G> ha;
-  ha.prefetch(qkv, kh, vh, q_norm, k_norm, rope_cur, j, n_q * kD, n_kv * kD, cap, k_begin, sid, sl);
+  HeadAttn<TS, G, 16, PREV> ha;
+  ha.prefetch(qkv + (size_t)t * M, kh, vh, q_norm, k_norm, rope_cur + t * kD, j, Q, KV, cap, k_begin, sid, sl);
+  ha.prefetch_prev(qkv, rope_cur, j, Q, KV, sl);   // (unused by row 0; no branch around loads)
   // keep the scheduler from moving work that waits on the first loads
   // (the query norm) above the later ones
   __builtin_amdgcn_sched_barrier(0);
-  const int pos = ctrl[kCtrlPos];
+  const int pos0 = ctrl[kCtrlPos];
+  const int pos = pos0 + t;
   const int n_keys = pos + 1;
   const int n_splits = ceil_div(n_keys, chunk);
-  // Splits past the context run on an empty range and write nothing (an
-  // early return would let the compiler sink the loads above below the
+  // Splits past this row's context run on an empty range and write nothing
+  // (an early return would let the compiler sink the loads above below the
   // position read).
   const bool active = split < n_splits;
   const int k_end = active ? min(n_keys, k_begin + chunk) : k_begin;
   const bool has_cur = active && k_end == n_keys;
+  const bool has_prev = active && t > 0 && k_begin <= pos0 && pos0 < k_end;
   SoftState<G> st;
-  ha.run(kh, vh, pos, k_begin, has_cur ? k_end - 1 : k_end, has_cur, true, eps, sid, sl, st);
+  ha.run(kh, vh, pos, k_begin, min(k_end, pos0), has_prev, has_cur, true, eps, sid, sl, st);
 
   sm.put(st, sid, sl);
   __syncthreads();
   if (!active) return;
-  float* my_part = part + ((size_t)(j * gridDim.x + split) * G) * kPartStride;
-  for (int t = threadIdx.x; t < G * kD; t += kBlock) {
-    const int g = t / kD, d = t - g * kD;
+  float* my_part = part + ((size_t)((t * n_kv + j) * gridDim.x + split) * G) * kPartStride;
+  for (int e = threadIdx.x; e < G * kD; e += kBlock) {
+    const int g = e / kD, d = e - g * kD;
     float mx, L, A;
     sm.get(g, d, mx, L, A);
     if (n_splits == 1) {
-      o[(size_t)(j * G + g) * kD + d] = Store<TS>::from_f(A / L);
+      o[(size_t)t * Q + (size_t)(j * G + g) * kD + d] = Store<TS>::from_f(A / L);
     } else {
       if (d == 0) { my_part[g * kPartStride] = mx; my_part[g * kPartStride + 1] = L; }
       my_part[g * kPartStride + 2 + d] = A;
@@ -679,9 +794,10 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
 // range, read from L2 by the blocks of that head), then multiplies its 4R
 // rows of W_o restricted to head j's G*128 columns, which it put in flight
 // first:
-//   part[j][m] = W_o[m, cols of head j] . o_j  (+ x[m] for j = 0).
+//   part[t][j][m] = W_o[m, cols of head j] . o_j(row t)  (+ x[t][m] for j = 0).
 // The gate/up launch sums the partials in a fixed order.  Blocks b = 0
-// write the current token's key and value into the cache.
+// write the current tokens' keys and values into the cache.  With T = 2
+// query rows, waves 0-1 serve row 0 and waves 2-3 row 1 (8 key-rows each).
 template <typename TW, int G, int R>
 struct WoSlice {
   using Vec = typename WVec<TW>::type;
@@ -740,20 +856,24 @@ struct WoSlice {
   }
 };
 
-template <typename TS, typename TW, int G, int R>
+template <typename TS, typename TW, int G, int R, int T>
 __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
                                                    TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
                                                    const TS* __restrict__ k_norm, const float* __restrict__ rope_cur,
                                                    const int32_t* __restrict__ ctrl, int n_q, int n_kv, int cap,
                                                    float eps, const TW* __restrict__ Wo, const TS* __restrict__ x_res,
-                                                   int H, float* __restrict__ opart) {
-  __shared__ RowMerge<G> sm;
-  __shared__ float s_o[G * kD];
+                                                   int H, float* __restrict__ opart, int part_row) {
+  constexpr int NR = 16 / T;           // key-rows per query row
+  constexpr int WPR = kWavesPerBlock / T;
+  __shared__ RowMerge<G, NR> sm[T];
+  __shared__ float s_o[T][G * kD];
   const int j = blockIdx.y;            // KV head
   const int lane = lane_id(), wave = wave_id();
-  const int sid = wave * 4 + (lane >> 4), sl = lane & 15;
+  const int t = wave / WPR;            // this wave's query row
+  const int sid = (wave % WPR) * 4 + (lane >> 4), sl = lane & 15;
   const int row0 = (blockIdx.x * kWavesPerBlock + wave) * R;
   const size_t head_off = (size_t)j * cap * kD;
+  const int Q = n_q * kD, KV = n_kv * kD, M = Q + 2 * KV;
   TS* kh = k_cache + head_off;
   TS* vh = v_cache + head_off;
   // Vector loads return in issue order: the attention operands go out
@@ -761,51 +881,56 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
   // in.  The position (a scalar load) is read after them: scalar loads
   // complete out of order, so any earlier wait on a kernel argument would
   // also wait for it.
-  HeadAttn<TS, G> ha;
-  ha.prefetch(qkv, kh, vh, q_norm, k_norm, rope_cur, j, n_q * kD, n_kv * kD, cap, 0, sid, sl);
+  HeadAttn<TS, G, NR, (T > 1)> ha;
+  ha.prefetch(qkv + (size_t)t * M, kh, vh, q_norm, k_norm, rope_cur + t * kD, j, Q, KV, cap, 0, sid, sl);
+  ha.prefetch_prev(qkv, rope_cur, j, Q, KV, sl);   // (unused by row 0; no branch around loads)
   // the residual rows (carried by the partial of KV head 0)
-  const float xb = j == 0 ? rows_prefetch<TS, R>(x_res, row0, H) : 0.f;
+  float xb[T];
+#pragma unroll
+  for (int r = 0; r < T; ++r) xb[r] = j == 0 ? rows_prefetch<TS, R>(x_res + (size_t)r * H, row0, H) : 0.f;
   __builtin_amdgcn_sched_barrier(0);   // attention operands before the weights
   WoSlice<TW, G, R> w;
-  w.load(Wo, n_q * kD, j * G * kD, row0, H);
+  w.load(Wo, Q, j * G * kD, row0, H);
   __builtin_amdgcn_sched_barrier(0);   // all loads issued in this order first
-  const int pos = ctrl[kCtrlPos];
+  const int pos0 = ctrl[kCtrlPos];
   SoftState<G> st;
-  ha.run(kh, vh, pos, 0, pos, true, blockIdx.x == 0, eps, sid, sl, st);
+  ha.run(kh, vh, pos0 + t, 0, pos0, t > 0, true, blockIdx.x == 0, eps, sid, sl, st);
 
-  sm.put(st, sid, sl);
+  sm[t].put(st, sid, sl);
   __syncthreads();
-  for (int t = threadIdx.x; t < G * kD; t += kBlock) {
-    const int g = t / kD, d = t - g * kD;
+  for (int e = threadIdx.x; e < T * G * kD; e += kBlock) {
+    const int r = e / (G * kD), f = e - r * G * kD;
+    const int g = f / kD, d = f - g * kD;
     float mx, L, A;
-    sm.get(g, d, mx, L, A);
-    s_o[t] = Store<TS>::to_f(Store<TS>::from_f(A / L));   // o rounded as stored
+    sm[r].get(g, d, mx, L, A);
+    s_o[r][f] = Store<TS>::to_f(Store<TS>::from_f(A / L));   // o rounded as stored
   }
   __syncthreads();
-  w.apply(s_o, row0, H, xb, opart + (size_t)j * H);
+#pragma unroll
+  for (int r = 0; r < T; ++r) w.apply(s_o[r], row0, H, xb[r], opart + (size_t)r * part_row + (size_t)j * H);
 }
 
-// Merge of the split-K partial states of one query head (one block of 256
-// threads per head): the split maxima and sums are loaded in parallel, the
-// per-split weights exp2(m_s - max) are kept in LDS, and each output dim
-// sums its weighted partials with the loads of two halves of the splits in
-// flight.  A separate launch, because a last-arriving-block merge needs a
-// device-scope fence per block, and on this multi-XCD part each such fence
-// writes back the issuing XCD's L2.
+// Merge of the split-K partial states of one query head of row t (one
+// block of 256 threads per head and row): the split maxima and sums are
+// loaded in parallel, the per-split weights exp2(m_s - max) are kept in LDS,
+// and each output dim sums its weighted partials with the loads of two
+// halves of the splits in flight.  A separate launch, because a
+// last-arriving-block merge needs a device-scope fence per block, and on
+// this multi-XCD part each such fence writes back the issuing XCD's L2.
 constexpr int kMaxSplits = 128;
 
 template <typename TS, int G>
 __global__ __launch_bounds__(kBlock) void k_attn_merge(const float* __restrict__ part,
-                                                       const int32_t* __restrict__ ctrl, int splits, int chunk,
-                                                       TS* __restrict__ o) {
+                                                       const int32_t* __restrict__ ctrl, int n_kv, int splits,
+                                                       int chunk, TS* __restrict__ o) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[kWavesPerBlock];
   __shared__ float s_a[2][kD];
-  const int h = blockIdx.x, j = h / G, g = h - j * G, tid = threadIdx.x;
-  const int n_keys = ctrl[kCtrlPos] + 1;
+  const int h = blockIdx.x, j = h / G, g = h - j * G, t = blockIdx.y, tid = threadIdx.x;
+  const int n_keys = ctrl[kCtrlPos] + t + 1;
   const int n_splits = ceil_div(n_keys, chunk);
   if (n_splits == 1) return;   // the attention block wrote o itself
-  const float* hp = part + ((size_t)j * splits * G + g) * kPartStride;
+  const float* hp = part + (((size_t)t * n_kv + j) * splits * G + g) * kPartStride;
   const size_t sstride = (size_t)G * kPartStride;
   // split statistics: thread sp < n_splits (n_splits <= kMaxSplits)
   const float m_s = tid < n_splits ? hp[tid * sstride] : -INFINITY;
@@ -830,7 +955,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_merge(const float* __restrict__
   for (int sp = half; sp < n_splits; sp += 2) A = fmaf(s_w[sp], hp[sp * sstride + 2 + d], A);
   s_a[half][d] = A;
   __syncthreads();
-  if (tid < kD) o[(size_t)h * kD + tid] = Store<TS>::from_f((s_a[0][tid] + s_a[1][tid]) / L);
+  if (tid < kD) o[((size_t)t * n_kv * G + h) * kD + tid] = Store<TS>::from_f((s_a[0][tid] + s_a[1][tid]) / L);
 }
 
 // --------------------------------------------------------------- dispatch
@@ -869,6 +994,14 @@ bool with_k(int K, F&& f) {
   }
 }
 template <typename F>
+bool with_t(int T, F&& f) {
+  switch (T) {
+    case 1: return f(IC<1>{});
+    case 2: return f(IC<2>{});
+    default: return false;
+  }
+}
+template <typename F>
 bool with_r(int R, F&& f) {
   switch (R) {
     case 1: return f(IC<1>{});
@@ -895,68 +1028,77 @@ bool qkv_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool 
   return with_w<TS>(L.wqkv, L.wqkv_p, [&](auto W) {
     return with_k<TS>(a.hidden, [&](auto kc) {
       return with_r(sh.rows_qkv, [&](auto rc) {
-        hipLaunchKernelGGL((k_qkv<TS, pointee_t<decltype(W)>, decltype(kc)::value, decltype(rc)::value>), dim3(grid),
-                           dim3(kBlock), 0, s, W, (const TS*)L.in_norm, (TS*)a.x, (const TS*)a.embed, a.ids, a.ctrl,
-                           a.rope_cos, a.rope_sin, a.rope_cur, first ? 1 : 0, a.vocab, a.eps, (TS*)a.qkv, M);
-        return true;
+        return with_t(sh.tokens, [&](auto tc) {
+          hipLaunchKernelGGL((k_qkv<TS, pointee_t<decltype(W)>, decltype(kc)::value, decltype(rc)::value,
+                                    decltype(tc)::value>),
+                             dim3(grid), dim3(kBlock), 0, s, W, (const TS*)L.in_norm, (TS*)a.x, (const TS*)a.embed,
+                             a.ids, a.ctrl, a.rope_cos, a.rope_sin, a.rope_cur, first ? 1 : 0, a.vocab, a.eps,
+                             (TS*)a.qkv, M);
+          return true;
+        });
       });
     });
   });
 }
 
 template <typename TS>
-bool residual_t(const DecodeArgs& a, int K, int R, int grid_req, const void* W, const void* Wp, const void* in,
-                const void* x_in, void* x_out, bool adv, hipStream_t s) {
+bool residual_t(const DecodeArgs& a, int T, int K, int R, int grid_req, const void* W, const void* Wp,
+                const void* in, const void* x_in, void* x_out, bool adv, hipStream_t s) {
   const int grid = blocks_for(a.hidden, R, grid_req);
   return with_w<TS>(W, Wp, [&](auto Wt) {
     return with_k<TS>(K, [&](auto kc) {
       return with_r(R, [&](auto rc) {
-        hipLaunchKernelGGL((k_gemv_residual<TS, pointee_t<decltype(Wt)>, decltype(kc)::value, decltype(rc)::value>),
-                           dim3(grid), dim3(kBlock), 0, s, Wt, (const TS*)in, (const TS*)x_in, (TS*)x_out, a.hidden,
-                           a.ctrl, adv ? 1 : 0);
-        return true;
+        return with_t(T, [&](auto tc) {
+          hipLaunchKernelGGL((k_gemv_residual<TS, pointee_t<decltype(Wt)>, decltype(kc)::value, decltype(rc)::value,
+                                              decltype(tc)::value>),
+                             dim3(grid), dim3(kBlock), 0, s, Wt, (const TS*)in, (const TS*)x_in, (TS*)x_out,
+                             a.hidden, a.ctrl, adv ? 1 : 0);
+          return true;
+        });
       });
     });
   });
 }
 
-// Partial slots the gate/up prologue sums for a model: the KV head count
-// rounded up to 2, 4 or 8 (the extra slots stay zero), or 0 when the
-// partials would not fit its registers.
-int parts_slots(int hidden, int n_kv) {
+// Partial slots per row the gate/up prologue sums for a model at T rows:
+// the KV head count rounded up to 2, 4 or 8 (the extra slots stay zero),
+// or 0 when the partials would not fit its registers.
+int parts_slots(int hidden, int n_kv, int T) {
   for (int np : {2, 4, 8})
-    if (n_kv <= np) return ceil_div(hidden, 4 * kBlock) * np <= kMaxPartVec ? np : 0;
+    if (n_kv <= np) return T * ceil_div(hidden, 4 * kBlock) * np <= kMaxPartVec ? np : 0;
   return 0;
 }
 
 template <typename TS>
 bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool from_parts, hipStream_t s) {
   const int grid = blocks_for(a.inter, sh.rows_gu, sh.grid_gu);
-  const int np = from_parts ? parts_slots(a.hidden, a.n_kv) : 0;
+  const int np = from_parts ? parts_slots(a.hidden, a.n_kv, sh.tokens) : 0;
   if (from_parts && np == 0) return false;
   return with_w<TS>(L.wgu, L.wgu_p, [&](auto W) {
     using TW = pointee_t<decltype(W)>;
     return with_k<TS>(a.hidden, [&](auto kc) {
       return with_r(sh.rows_gu, [&](auto rc) {
-        constexpr int K = decltype(kc)::value, R = decltype(rc)::value;
-        auto go = [&](auto npc) {
-          constexpr int NP = decltype(npc)::value;
-          if constexpr (NP * ceil_div(K, 4 * kBlock) <= kMaxPartVec) {
-            hipLaunchKernelGGL((k_gateup<TS, TW, K, R, NP>), dim3(grid), dim3(kBlock), 0, s, W,
-                               (const TS*)L.post_norm, (const TS*)a.x2, a.opart, a.eps, (TS*)a.act, a.inter,
-                               (TS*)a.x2);
-            return true;
-          } else {
-            return false;
+        return with_t(sh.tokens, [&](auto tc) {
+          constexpr int K = decltype(kc)::value, R = decltype(rc)::value, T = decltype(tc)::value;
+          auto go = [&](auto npc) {
+            constexpr int NP = decltype(npc)::value;
+            if constexpr (T * NP * ceil_div(K, 4 * kBlock) <= kMaxPartVec) {
+              hipLaunchKernelGGL((k_gateup<TS, TW, K, R, NP, T>), dim3(grid), dim3(kBlock), 0, s, W,
+                                 (const TS*)L.post_norm, (const TS*)a.x2, a.opart, a.eps, (TS*)a.act, a.inter,
+                                 (TS*)a.x2);
+              return true;
+            } else {
+              return false;
+            }
+          };
+          switch (np) {
+            case 0: return go(IC<0>{});
+            case 2: return go(IC<2>{});
+            case 4: return go(IC<4>{});
+            case 8: return go(IC<8>{});
+            default: return false;
           }
-        };
-        switch (np) {
-          case 0: return go(IC<0>{});
-          case 2: return go(IC<2>{});
-          case 4: return go(IC<4>{});
-          case 8: return go(IC<8>{});
-          default: return false;
-        }
+        });
       });
     });
   });
@@ -969,19 +1111,21 @@ bool head_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
     using TW = pointee_t<decltype(E)>;
     return with_k<TS>(a.hidden, [&](auto kc) {
       return with_r(sh.rows_head, [&](auto rc) {
-        constexpr int K = decltype(kc)::value, R = decltype(rc)::value;
-        auto go = [&](auto wc) {
-          constexpr int WPB = decltype(wc)::value;
-          hipLaunchKernelGGL((k_head<TS, TW, K, R, WPB>), dim3(grid), dim3(WPB * kWave), 0, s, E,
-                             (const TS*)a.final_norm, (const TS*)a.x, a.eps, (TS*)a.logits, a.vocab, a.am_part);
-          return true;
-        };
-        switch (sh.head_waves) {
-          case 4: return go(IC<4>{});
-          case 8: return go(IC<8>{});
-          case 16: return go(IC<16>{});
-          default: return false;
-        }
+        return with_t(sh.tokens, [&](auto tc) {
+          constexpr int K = decltype(kc)::value, R = decltype(rc)::value, T = decltype(tc)::value;
+          auto go = [&](auto wc) {
+            constexpr int WPB = decltype(wc)::value;
+            hipLaunchKernelGGL((k_head<TS, TW, K, R, WPB, T>), dim3(grid), dim3(WPB * kWave), 0, s, E,
+                               (const TS*)a.final_norm, (const TS*)a.x, a.eps, (TS*)a.logits, a.vocab, a.am_part);
+            return true;
+          };
+          switch (sh.head_waves) {
+            case 4: return go(IC<4>{});
+            case 8: return go(IC<8>{});
+            case 16: return go(IC<16>{});
+            default: return false;
+          }
+        });
       });
     });
   });
@@ -990,12 +1134,14 @@ bool head_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
 template <typename TS>
 bool attn_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
-  const dim3 grid(sh.attn_splits, a.n_kv);
+  const dim3 grid(sh.attn_splits, a.n_kv, sh.tokens);
   auto go = [&](auto gc) {
-    hipLaunchKernelGGL((k_attn<TS, decltype(gc)::value>), grid, dim3(kBlock), 0, s, (const TS*)a.qkv,
-                       (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm, a.rope_cur,
-                       a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, sh.attn_chunk, a.attn_part, (TS*)a.o);
-    return true;
+    return with_t(sh.tokens, [&](auto tc) {
+      hipLaunchKernelGGL((k_attn<TS, decltype(gc)::value, decltype(tc)::value>), grid, dim3(kBlock), 0, s,
+                         (const TS*)a.qkv, (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm,
+                         a.rope_cur, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, sh.attn_chunk, a.attn_part, (TS*)a.o);
+      return true;
+    });
   };
   switch (G) {
     case 1: return go(IC<1>{});
@@ -1009,8 +1155,8 @@ template <typename TS>
 bool attn_merge_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
   auto go = [&](auto gc) {
-    hipLaunchKernelGGL((k_attn_merge<TS, decltype(gc)::value>), dim3(a.n_q), dim3(kBlock), 0, s, a.attn_part, a.ctrl,
-                       sh.attn_splits, sh.attn_chunk, (TS*)a.o);
+    hipLaunchKernelGGL((k_attn_merge<TS, decltype(gc)::value>), dim3(a.n_q, sh.tokens), dim3(kBlock), 0, s,
+                       a.attn_part, a.ctrl, a.n_kv, sh.attn_splits, sh.attn_chunk, (TS*)a.o);
     return true;
   };
   switch (G) {
@@ -1026,13 +1172,20 @@ bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hi
   const int G = a.n_q / a.n_kv;
   return with_w<TS>(L.wo, L.wo_p, [&](auto Wo) {
     using TW = pointee_t<decltype(Wo)>;
+    // row t's partials start at opart[t * slots * H], as the gate/up
+    // prologue reads them
+    const int part_row = parts_slots(a.hidden, a.n_kv, sh.tokens) * a.hidden;
+    if (part_row == 0) return false;
     auto go = [&](auto gc, auto rc) {
       constexpr int R = decltype(rc)::value;
       const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R), a.n_kv);
-      hipLaunchKernelGGL((k_attn_o<TS, TW, decltype(gc)::value, R>), grid, dim3(kBlock), 0, s, (const TS*)a.qkv,
-                         (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm, a.rope_cur,
-                         a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, Wo, (const TS*)a.x, a.hidden, a.opart);
-      return true;
+      return with_t(sh.tokens, [&](auto tc) {
+        hipLaunchKernelGGL((k_attn_o<TS, TW, decltype(gc)::value, R, decltype(tc)::value>), grid, dim3(kBlock), 0, s,
+                           (const TS*)a.qkv, (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm,
+                           (const TS*)L.k_norm, a.rope_cur, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, Wo, (const TS*)a.x,
+                           a.hidden, a.opart, part_row);
+        return true;
+      });
     };
     auto with_g = [&](auto rc) {
       switch (G) {
@@ -1052,7 +1205,7 @@ bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hi
 
 }  // namespace
 
-int attn_o_part_slots(int hidden, int n_kv) { return parts_slots(hidden, n_kv); }
+int attn_o_part_slots(int hidden, int n_kv, int tokens) { return parts_slots(hidden, n_kv, tokens); }
 
 int head_blocks(const DecodeArgs& a, const DecodeShape& sh) {
   return head_grid(a.vocab, sh.rows_head, sh.head_waves, sh.grid_head);
@@ -1069,8 +1222,9 @@ bool launch_attn_merge(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s
 }
 bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   const int K = a.n_q * a.head_dim;
-  return a.dtype == 0 ? residual_t<float>(a, K, sh.rows_o, sh.grid_o, L.wo, L.wo_p, a.o, a.x, a.x2, false, s)
-                      : residual_t<__half>(a, K, sh.rows_o, sh.grid_o, L.wo, nullptr, a.o, a.x, a.x2, false, s);
+  return a.dtype == 0
+             ? residual_t<float>(a, sh.tokens, K, sh.rows_o, sh.grid_o, L.wo, L.wo_p, a.o, a.x, a.x2, false, s)
+             : residual_t<__half>(a, sh.tokens, K, sh.rows_o, sh.grid_o, L.wo, nullptr, a.o, a.x, a.x2, false, s);
 }
 bool launch_attn_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   return a.dtype == 0 ? attn_o_t<float>(a, sh, L, s) : attn_o_t<__half>(a, sh, L, s);
@@ -1079,9 +1233,10 @@ bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& 
   return a.dtype == 0 ? gateup_t<float>(a, sh, L, from_parts, s) : gateup_t<__half>(a, sh, L, from_parts, s);
 }
 bool launch_down(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool adv, hipStream_t s) {
-  return a.dtype == 0
-             ? residual_t<float>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, L.wd_p, a.act, a.x2, a.x, adv, s)
-             : residual_t<__half>(a, a.inter, sh.rows_down, sh.grid_down, L.wd, nullptr, a.act, a.x2, a.x, adv, s);
+  return a.dtype == 0 ? residual_t<float>(a, sh.tokens, a.inter, sh.rows_down, sh.grid_down, L.wd, L.wd_p, a.act,
+                                          a.x2, a.x, adv, s)
+                      : residual_t<__half>(a, sh.tokens, a.inter, sh.rows_down, sh.grid_down, L.wd, nullptr, a.act,
+                                           a.x2, a.x, adv, s);
 }
 bool launch_head(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   return a.dtype == 0 ? head_t<float>(a, sh, s) : head_t<__half>(a, sh, s);
@@ -1090,9 +1245,11 @@ bool launch_argmax(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   const int n = head_blocks(a, sh);
   const int per = ceil_div(n / 2, 1024);
   auto go = [&](auto pc) {
-    hipLaunchKernelGGL((k_argmax<decltype(pc)::value>), dim3(1), dim3(1024), 0, s,
-                       (const unsigned long long*)a.am_part, n, a.ctrl, a.ids);
-    return true;
+    return with_t(sh.tokens, [&](auto tc) {
+      hipLaunchKernelGGL((k_argmax<decltype(pc)::value, decltype(tc)::value>), dim3(1), dim3(1024), 0, s,
+                         (const unsigned long long*)a.am_part, n, a.ctrl, a.ids);
+      return true;
+    });
   };
   if (per <= 1) return go(IC<1>{});
   if (per <= 2) return go(IC<2>{});

@@ -9,7 +9,8 @@ namespace wsg {
 // Control words in the workspace (int32 each).
 enum CtrlWord : int {
   kCtrlPos = 0,          // current position p (tokens already in the cache)
-  kCtrlOutTok = 1,       // last greedy token
+  kCtrlOutTok = 1,       // last emitted greedy token
+  kCtrlRowTok = 2,       // [kMaxTokens] greedy token of each row of the last step
   kCtrlWords = 64
 };
 
@@ -17,6 +18,11 @@ enum CtrlWord : int {
 // one row per wave for the 151936-row vocabulary is 37984 blocks); a
 // multiple of 2048 (the argmax block reads key pairs).
 constexpr int kHeadMaxBlocks = 40960;
+
+// Query rows one decode step can carry: 1 (a decode step) or 2 (a
+// two-token step: the last token and a draft of the next).  Per-row
+// activation buffers below hold kMaxTokens rows.
+constexpr int kMaxTokens = 2;
 
 struct LayerPtrs {
   const void* wqkv;     // [(Q + 2 KV)][H]
@@ -46,17 +52,19 @@ struct DecodeArgs {
   const void* final_norm;
   const float* rope_cos;  // [cap][D/2]
   const float* rope_sin;
-  float* rope_cur;      // [D]: cos then sin of the current position (written by layer 0's qkv)
-  void* x;              // residual [H]: layer input / down-projection output
-  void* x2;             // residual [H]: output-projection output / MLP input
-  void* qkv;            // [Q + 2 KV]
-  void* o;              // [Q]
-  void* act;            // [I]
-  void* logits;         // [V]
-  float* opart;         // [slots][H] FP32 output-projection partials of the fused attention launch
-  float* attn_part;     // split-K partial states
+  // Per-row buffers hold kMaxTokens rows; row t of a step is at position p + t.
+  float* rope_cur;      // [rows][D]: cos then sin of each row's position (written by layer 0's qkv)
+  void* x;              // residual [rows][H]: layer input / down-projection output
+  void* x2;             // residual [rows][H]: output-projection output / MLP input
+  void* qkv;            // [rows][Q + 2 KV]
+  void* o;              // [rows][Q]
+  void* act;            // [rows][I]
+  void* logits;         // [rows][V]
+  float* opart;         // [rows][slots][H] FP32 output-projection partials of the fused attention launch
+  float* attn_part;     // [rows][n_kv][splits][G] split-K partial states
   int attn_part_splits; // capacity in splits per KV head
-  unsigned long long* am_part;  // [kHeadMaxBlocks] per-block argmax keys of the head
+  unsigned long long* am_part;  // per-block argmax keys of the head: row t's at [t * head blocks]
+                                //   (capacity kMaxTokens * kHeadMaxBlocks)
   int32_t* ctrl;
   int32_t* ids;         // token history [cap + 1]
 };
@@ -70,6 +78,7 @@ struct DecodeShape {
   int head_waves;                                        // waves per head block (4, 8 or 16)
   int fuse_attn_o;                                       // short contexts: fused attention + output GEMV
   int rows_attn_o;                                       // W_o rows per wave in the fused launch (4 or 8)
+  int tokens = 1;                                        // query rows of the step (1 or kMaxTokens)
 };
 
 // Stage launches; each returns false if the shape is not compiled in.
@@ -81,15 +90,19 @@ bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hi
 // Short contexts: attention fused with the output GEMV, which writes
 // per-KV-head partials into opart instead of x2.
 bool launch_attn_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
-// Partial slots (>= n_kv; slots past n_kv must hold zeros) the gate/up
-// prologue sums after a fused launch, or 0 if the shape cannot be fused.
-int attn_o_part_slots(int hidden, int n_kv);
+// Partial slots per row (>= n_kv; slots past n_kv must hold zeros) the
+// gate/up prologue sums after a fused launch of `tokens` rows, or 0 if the
+// shape cannot be fused.  The slot count is the same for every row count
+// that can be fused.
+int attn_o_part_slots(int hidden, int n_kv, int tokens);
 // from_parts: x2 is the sum of the opart partials (written back to x2).
 bool launch_gateup(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool from_parts, hipStream_t s);
 bool launch_down(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool advance_pos, hipStream_t s);
-// Final RMSNorm + vocabulary GEMV with one argmax key per block; then the
-// one-block argmax (ties to the lowest id) writes the token into ctrl and
-// the token history and advances the position.
+// Final RMSNorm + vocabulary GEMV with one argmax key per block and row;
+// then the one-block argmax (ties to the lowest id) writes each row's token
+// into ctrl, the emitted tokens into the token history, and advances the
+// position (a two-token step: by one or two, as its draft is rejected or
+// accepted).
 bool launch_head(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s);
 bool launch_argmax(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s);
 bool launch_set_pos(int32_t* ctrl, int pos, hipStream_t s);

@@ -170,18 +170,20 @@ WsLayout ws_layout(const Dims& d) {
   w.kv = take((size_t)d.L * 2 * d.nkv * d.cap * d.D * d.es);
   w.rope_cos = take((size_t)d.cap * (d.D / 2) * 4);
   w.rope_sin = take((size_t)d.cap * (d.D / 2) * 4);
-  w.rope_cur = take((size_t)d.D * 4);
-  w.x = take((size_t)d.H * d.es);
-  w.x2 = take((size_t)d.H * d.es);
-  w.qkv = take((size_t)(d.Q + 2 * d.KV) * d.es);
-  w.o = take((size_t)d.Q * d.es);
-  w.act = take((size_t)d.I * d.es);
-  w.logits = take((size_t)d.V * d.es);
-  w.opart_slots = std::max(d.nkv, attn_o_part_slots(d.H, d.nkv));
-  w.opart = take((size_t)w.opart_slots * d.H * 4);
+  // per-row buffers: kMaxTokens rows (a two-token step)
+  const size_t T = kMaxTokens;
+  w.rope_cur = take(T * d.D * 4);
+  w.x = take(T * d.H * d.es);
+  w.x2 = take(T * d.H * d.es);
+  w.qkv = take(T * (d.Q + 2 * d.KV) * d.es);
+  w.o = take(T * d.Q * d.es);
+  w.act = take(T * d.I * d.es);
+  w.logits = take(T * d.V * d.es);
+  w.opart_slots = std::max(d.nkv, attn_o_part_slots(d.H, d.nkv, 1));
+  w.opart = take(T * w.opart_slots * d.H * 4);
   w.attn_splits_cap = attn_split_cap(d);
-  w.attn_part = take((size_t)d.nkv * w.attn_splits_cap * d.G * (2 + d.D) * 4);
-  w.am_part = take((size_t)kHeadMaxBlocks * 8);
+  w.attn_part = take(T * d.nkv * w.attn_splits_cap * d.G * (2 + d.D) * 4);
+  w.am_part = take(T * kHeadMaxBlocks * 8);
   w.ctrl = take((size_t)kCtrlWords * 4);
   w.ids = take((size_t)(d.cap + 1) * 4);
   const size_t pf_base = off;
@@ -214,7 +216,7 @@ struct wsg_model {
   bool has_output = false;
   int32_t* pin = nullptr;          // pinned staging: [0] token out, [1..] ids in
   bool use_graph = true;
-  std::map<int, hipGraphExec_t> graphs;   // key: splits*4 + fused*2 + advance
+  std::map<int, hipGraphExec_t> graphs;   // key: graph_key(splits, tokens, fused, advance)
   int timed_stage = -1;
   std::vector<hipEvent_t> ev;
   int ev_used = 0;
@@ -273,12 +275,14 @@ bool timed(wsg_model* m, int stage, int64_t bytes, F&& launch) {
   return ok;
 }
 
-// All layers of one token; the last down projection advances the position
-// when no head follows (prompt rows before the last).  Short contexts (fused)
-// use the fused attention + output-projection launch.
-bool enqueue_body(wsg_model* m, int splits, bool fused, bool advance) {
+// All layers of one step of `tokens` rows; the last down projection
+// advances the position when no head follows (prompt rows before the
+// last).  Short contexts (fused) use the fused attention + output-projection
+// launch.
+bool enqueue_body(wsg_model* m, int splits, bool fused, bool advance, int tokens) {
   DecodeShape sh = m->shape;
   sh.attn_splits = splits;
+  sh.tokens = tokens;
   const hipStream_t s = m->stream;
   const int L = m->d.L;
   for (int l = 0; l < L; ++l) {
@@ -306,8 +310,13 @@ bool enqueue_body(wsg_model* m, int splits, bool fused, bool advance) {
   return true;
 }
 
-bool enqueue_head(wsg_model* m) { return launch_head(m->args, m->shape, m->stream); }
-bool enqueue_argmax(wsg_model* m) { return launch_argmax(m->args, m->shape, m->stream); }
+DecodeShape shape_for(const wsg_model* m, int tokens) {
+  DecodeShape sh = m->shape;
+  sh.tokens = tokens;
+  return sh;
+}
+bool enqueue_head(wsg_model* m, int tokens) { return launch_head(m->args, shape_for(m, tokens), m->stream); }
+bool enqueue_argmax(wsg_model* m, int tokens) { return launch_argmax(m->args, shape_for(m, tokens), m->stream); }
 
 // Attention blocks per KV head for n_keys: the splits the context needs,
 // rounded up to a power of two up to 8 and to a multiple of 8 beyond (one
@@ -318,8 +327,8 @@ bool enqueue_argmax(wsg_model* m) { return launch_argmax(m->args, m->shape, m->s
 // beyond this length the split-K path's parallelism over keys wins).
 constexpr int kFuseMaxKeys = 128;
 
-bool use_fused_attn_o(const wsg_model* m, int n_keys) {
-  return m->shape.fuse_attn_o && n_keys <= kFuseMaxKeys && attn_o_part_slots(m->d.H, m->d.nkv) > 0;
+bool use_fused_attn_o(const wsg_model* m, int n_keys, int tokens) {
+  return m->shape.fuse_attn_o && n_keys <= kFuseMaxKeys && attn_o_part_slots(m->d.H, m->d.nkv, tokens) > 0;
 }
 
 int splits_for(const wsg_model* m, int n_keys) {
@@ -356,22 +365,27 @@ wsg_status graph_for(wsg_model* m, int key, F&& enqueue, hipGraphExec_t* out) {
 }
 
 
-// Enqueue one token forward at the current device position: the layer body
-// and, if `head`, the head (final norm, vocabulary GEMV, argmax).
-wsg_status run_forward(wsg_model* m, bool head, int n_keys) {
+int graph_key(int splits, int tokens, bool fused, bool advance) {
+  return ((splits * 2 + (tokens - 1)) * 2 + (fused ? 1 : 0)) * 2 + (advance ? 1 : 0);
+}
+
+// Enqueue one step of `tokens` rows at the current device position (n_keys
+// = the last row's position + 1): the layer body and, if `head`, the head
+// (final norm, vocabulary GEMV, argmax).
+wsg_status run_forward(wsg_model* m, bool head, int n_keys, int tokens = 1) {
   const int splits = splits_for(m, n_keys);
-  const bool fused = use_fused_attn_o(m, n_keys);
+  const bool fused = use_fused_attn_o(m, n_keys, tokens);
   const bool advance = !head;
   (void)hipGetLastError();   // errors of earlier calls were reported by those calls
   m->ev_used = 0;
   m->timed_bytes_per_launch_sum = 0;
   if (!m->use_graph) {
-    if (!enqueue_body(m, splits, fused, advance))
+    if (!enqueue_body(m, splits, fused, advance, tokens))
       return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape");
   } else {
     hipGraphExec_t body = nullptr;
-    const wsg_status st = graph_for(m, splits * 4 + (fused ? 2 : 0) + (advance ? 1 : 0),
-                                    [&] { return enqueue_body(m, splits, fused, advance); }, &body);
+    const wsg_status st = graph_for(m, graph_key(splits, tokens, fused, advance),
+                                    [&] { return enqueue_body(m, splits, fused, advance, tokens); }, &body);
     if (st != WSG_OK) return st;
     WSG_HIP_CHECK(hipGraphLaunch(body, m->stream));
   }
@@ -380,13 +394,13 @@ wsg_status run_forward(wsg_model* m, bool head, int n_keys) {
     // saves nothing for one kernel), so stream events can bracket the head.
     const bool t = m->timed_stage == WSG_STAGE_HEAD;
     if (t) record_event(m, m->ev[0]);
-    if (!enqueue_head(m)) return fail(WSG_ERR_UNSUPPORTED, "no compiled head kernel for this shape");
+    if (!enqueue_head(m, tokens)) return fail(WSG_ERR_UNSUPPORTED, "no compiled head kernel for this shape");
     if (t) {
       record_event(m, m->ev[1]);
       m->ev_used = 2;
       m->timed_bytes_per_launch_sum = stage_bytes(m, WSG_STAGE_HEAD, -1);
     }
-    if (!enqueue_argmax(m)) return fail(WSG_ERR_UNSUPPORTED, "argmax launch");
+    if (!enqueue_argmax(m, tokens)) return fail(WSG_ERR_UNSUPPORTED, "argmax launch");
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(WSG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -413,6 +427,17 @@ wsg_status read_token(wsg_model* m, int32_t* out_token) {
   const wsg_status st = collect_timing(m);
   if (st != WSG_OK) return st;
   if (out_token) *out_token = m->pin[0];
+  return WSG_OK;
+}
+
+// The per-row tokens of the last step (`rows` words from kCtrlRowTok).
+wsg_status read_row_tokens(wsg_model* m, int rows, int32_t* out) {
+  WSG_HIP_CHECK(hipMemcpyAsync(m->pin, m->args.ctrl + kCtrlRowTok, rows * sizeof(int32_t), hipMemcpyDeviceToHost,
+                               m->stream));
+  WSG_HIP_CHECK(hipStreamSynchronize(m->stream));
+  const wsg_status st = collect_timing(m);
+  if (st != WSG_OK) return st;
+  for (int i = 0; i < rows; ++i) out[i] = m->pin[i];
   return WSG_OK;
 }
 
@@ -624,7 +649,7 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
       hipMemsetAsync(m->ws + wl.ctrl, 0, (size_t)kCtrlWords * 4, m->stream) != hipSuccess ||
       hipMemsetAsync(m->ws + wl.ids, 0, (size_t)(d.cap + 1) * 4, m->stream) != hipSuccess ||
       // partial slots past the KV head count are summed as zeros
-      hipMemsetAsync(m->ws + wl.opart, 0, (size_t)wl.opart_slots * d.H * 4, m->stream) != hipSuccess ||
+      hipMemsetAsync(m->ws + wl.opart, 0, (size_t)kMaxTokens * wl.opart_slots * d.H * 4, m->stream) != hipSuccess ||
       hipStreamSynchronize(m->stream) != hipSuccess)
     return fail_free(fail(WSG_ERR_HIP, "uploading the rotary table failed"));
   // graphs need a capturable (non-null) stream
@@ -722,6 +747,37 @@ wsg_status wsg_step(wsg_model* m, int32_t in_token, int32_t* out_token, const vo
   st = read_token(m, out_token);
   if (st != WSG_OK) return st;
   m->pos += 1;
+  m->has_output = true;
+  if (out_logits) *out_logits = m->args.logits;
+  return WSG_OK;
+}
+
+wsg_status wsg_step2(wsg_model* m, int32_t in_token, int32_t draft, int32_t out_tokens[2], int32_t* n_emitted,
+                     const void** out_logits) {
+  clear_error();
+  if (!m || !out_tokens || !n_emitted) return fail(WSG_ERR_INVALID_ARG, "NULL pointer");
+  if (in_token >= m->d.V) return fail(WSG_ERR_OUT_OF_RANGE, "token id %d >= vocab %d", in_token, m->d.V);
+  if (draft < 0 || draft >= m->d.V) return fail(WSG_ERR_OUT_OF_RANGE, "draft id %d outside [0, %d)", draft, m->d.V);
+  if (in_token < 0 && !m->has_output) return fail(WSG_ERR_STATE, "no previous output token; pass in_token or prefill first");
+  if ((int64_t)m->pos + 2 > m->d.cap)
+    return fail(WSG_ERR_OUT_OF_RANGE, "position %d + 2 rows exceeds max_context %d", m->pos, m->d.cap);
+  m->pin[1] = in_token;
+  m->pin[2] = draft;
+  if (in_token >= 0)
+    WSG_HIP_CHECK(hipMemcpyAsync(m->args.ids + m->pos, m->pin + 1, 2 * sizeof(int32_t), hipMemcpyHostToDevice, m->stream));
+  else
+    WSG_HIP_CHECK(hipMemcpyAsync(m->args.ids + m->pos + 1, m->pin + 2, sizeof(int32_t), hipMemcpyHostToDevice, m->stream));
+  wsg_status st = run_forward(m, true, m->pos + 2, 2);
+  if (st != WSG_OK) return st;
+  int32_t tok[2];
+  st = read_row_tokens(m, 2, tok);
+  if (st != WSG_OK) return st;
+  // the argmax kernel applied the same acceptance rule to the device position
+  const int emitted = tok[0] == draft ? 2 : 1;
+  out_tokens[0] = tok[0];
+  out_tokens[1] = tok[1];
+  *n_emitted = emitted;
+  m->pos += emitted;
   m->has_output = true;
   if (out_logits) *out_logits = m->args.logits;
   return WSG_OK;
