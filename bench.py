@@ -395,6 +395,136 @@ def lossless_bf16(torch, wsg, shape, steps=5, warmup=2):
     return res
 
 
+def two_token(torch, wsg, shape, w, context=16, trials=9, reps=50, n_prompt=32, n_out=33):
+    """Two-token step (the verify pass of greedy speculative decoding; "Our Kernel Benchmark
+    Was Measuring the System Cache", "Why it mattered, concretely"): each weight matrix is
+    streamed once for the last token and a draft of the next.  Validated first against the
+    oracle (both rows' full-vocabulary logits, exact greedy tokens, both new K/V slots of
+    every layer, one accepted and one rejected draft per pair of steps); then (a) the
+    latency of one two-token forward at a fixed slot beside one single-token forward
+    (rewind, forward, token read, as in the fixed-context harness), with HIP events around
+    the two-row head launch; (b) decode throughput of speculative generation with drafts
+    taken from a previous greedy run (all accepted: the decoder-side ceiling of speculative
+    decoding) and with every other draft corrupted, each checked to emit exactly the greedy
+    stream."""
+    import oracle
+    from synth import prompt_ids
+    cap = n_prompt + n_out + 4
+    model = wsg.Model(shape, w, max_context=cap, prefill_chunk=32)
+    orc = oracle.OracleModel(shape, w, cap)
+    prompt = prompt_ids(60, n_prompt, shape.vocab)
+
+    def cmp(got, ref_, what):
+        g = got.float().cpu().numpy().astype(np.float64)
+        r = np.asarray(ref_, dtype=np.float64)
+        err = np.abs(g - r)
+        if not np.all(err <= 1e-3 + 1e-3 * np.abs(r)):
+            raise RuntimeError(f"two-token validation failed: {what} off by {err.max():.3e}")
+        return float(err.max())
+
+    # ---- validation: 4 steps, drafts accepted / rejected alternately
+    tok = model.prefill(prompt)
+    ref = orc.forward_rows(prompt)
+    if tok != oracle.argmax_lowest(ref):
+        raise RuntimeError("two-token validation failed: first token")
+    last, max_l, max_kv = tok, 0.0, 0.0
+    for s in range(4):
+        p = orc.pos
+        ref0 = orc.forward_rows([last])
+        g0 = oracle.argmax_lowest(ref0)
+        draft = g0 if s % 2 == 0 else (g0 + 1) % shape.vocab
+        (t0, t1), n = model.step2(draft)
+        ref1 = orc.forward_rows([draft])
+        lg = model.logits()
+        max_l = max(max_l, cmp(lg[0], ref0, f"row 0 logits step {s}"), cmp(lg[1], ref1, f"row 1 logits step {s}"))
+        for l in range(shape.n_layers):
+            k, v, _ = model.kv(l)
+            max_kv = max(max_kv, cmp(k[:, p:p + 2], orc.k_cache[l][:, p:p + 2], f"K layer {l} step {s}"),
+                         cmp(v[:, p:p + 2], orc.v_cache[l][:, p:p + 2], f"V layer {l} step {s}"))
+        if t0 != g0 or (n == 2 and t1 != oracle.argmax_lowest(ref1)) or n != (2 if s % 2 == 0 else 1):
+            raise RuntimeError(f"two-token validation failed: tokens {t0},{t1} n={n} at step {s}")
+        if n == 1:
+            orc.pos = p + 1
+        last = t1 if n == 2 else t0
+        if model.position != orc.pos:
+            raise RuntimeError("two-token validation failed: position")
+    del orc
+
+    # ---- (a) fixed-slot latency: one two-token forward vs one single-token forward
+    model.reset()
+    model.prefill(prompt[:context])          # its output token sits at slot `context`
+    nxt = model.step()                       # greedy token after slot `context`
+    after = model.step()                     # greedy token after slot `context + 1`
+    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, STAGES["head"])
+    res = {}
+    for name in ("step", "step2"):
+        per = []
+        for t in range(trials + 1):
+            model.stage_time()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                model.rewind(context)
+                if name == "step":
+                    ok = model.step() == nxt
+                else:
+                    (a, b), n = model.step2(nxt)
+                    ok = (a, b, n) == (nxt, after, 2)
+                if not ok:
+                    raise RuntimeError(f"two-token fixed slot: repeated {name} changed its tokens")
+            if t > 0:
+                per.append((time.perf_counter() - t0) / reps * 1e6)
+        ms, nl, by = model.stage_time()
+        res[name] = {"us_median": round(statistics.median(per), 2), "us_min": round(min(per), 2),
+                     "head_us": round(ms / max(nl, 1) * 1e3, 2),
+                     "head_weight_gbps": round(by / max(nl, 1) / (ms / max(nl, 1) * 1e-3) / 1e9, 1)}
+    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, -1)
+    res["step2_over_step"] = round(res["step2"]["us_median"] / res["step"]["us_median"], 3)
+    res["tokens_per_s_at_slot"] = {"step": round(1e6 / res["step"]["us_median"], 1),
+                                   "step2_both_emitted": round(2e6 / res["step2"]["us_median"], 1)}
+
+    # ---- (b) speculative generation with drafts from a greedy run
+    greedy, _, _, _ = generate(model, prompt, n_out)
+    gen = {}
+    for name, bad_every in (("all_accepted", 0), ("every_other_rejected", 2)):
+        rates = []
+        for t in range(trials + 1):
+            model.reset()
+            out = [model.prefill(prompt)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            k = 0
+            while len(out) < n_out:
+                d = greedy[len(out)]
+                if bad_every and k % bad_every == 1:
+                    d = (d + 1) % shape.vocab
+                k += 1
+                (a, b), n = model.step2(d)
+                out += [a, b][:n]
+            dt = time.perf_counter() - t0
+            if out[:n_out] != greedy:
+                raise RuntimeError(f"speculative generation ({name}) differs from the greedy stream")
+            if t > 0:
+                rates.append((len(out) - 1) / dt)
+        gen[name] = {"decode_tok_s": round(statistics.median(rates), 1), "two_token_steps": k}
+    g_rates = []
+    for t in range(trials + 1):
+        toks, _, dec, _ = generate(model, prompt, n_out)
+        if toks != greedy:
+            raise RuntimeError("greedy generation not repeatable")
+        if t > 0:
+            g_rates.append((n_out - 1) / dec)
+    gen["greedy_step_only"] = {"decode_tok_s": round(statistics.median(g_rates), 1)}
+    model.close()
+    res["speculative_generation"] = gen
+    res["validation"] = {"max_abs_logit_err": max_l, "max_abs_kv_err": max_kv, "steps_checked": 4,
+                         "drafts": "accepted, rejected, accepted, rejected"}
+    res["workload"] = (f"28-layer FP32; fixed slot {context} ({trials} trials x {reps} repeats, rewind + forward "
+                       f"+ token read); generation: {n_prompt}-id prompt, {n_out} outputs, drafts from the "
+                       "greedy stream (every other one corrupted in the second run)")
+    return res
+
+
 def long_context(torch, wsg, shape, w, validate_outputs=32, trials=5, warmup=2):
     """Long-document workload (Benchmark methodology, "Long-document chunked prefill").
 
@@ -565,6 +695,8 @@ def main(argv=None):
                     help="single-forward latency at contexts 0/16/64 (fixed cache slot)")
     ap.add_argument("--lossless", choices=["on", "off", "only"], default="on",
                     help="short-prompt workload on BF16-representable weights, packed vs unpacked decode")
+    ap.add_argument("--two-token", choices=["on", "off", "only"], default="on",
+                    help="two-token step (speculative verify pass): fixed-slot latency and generation")
     ap.add_argument("--no-oracle", action="store_true",
                     help="skip validation and the CPU baseline (profiling runs only; no value is published)")
     args = ap.parse_args(argv)
@@ -638,6 +770,14 @@ def main(argv=None):
         fixed_res = fixed_context(torch, wsg, shape, w)
         if args.fixed == "only":
             print(json.dumps({"fixed_context": fixed_res}), flush=True)
+            return 0
+    two_res = None
+    if args.two_token != "off" and not args.no_oracle:
+        t = time.perf_counter()
+        two_res = two_token(torch, wsg, shape, w)
+        log(f"two-token section in {time.perf_counter() - t:.1f} s")
+        if args.two_token == "only":
+            print(json.dumps({"two_token": two_res}), flush=True)
             return 0
     long_res = None
     if args.long != "off" and not args.no_oracle:
@@ -715,6 +855,7 @@ def main(argv=None):
         "host": host_info(),
         "long_context": long_res,
         "fixed_context": fixed_res,
+        "two_token": two_res,
     }
     model.close()
     del model

@@ -235,6 +235,12 @@ enum { WSG_OPT_HEAD_WAVES = 16 };
 enum { WSG_OPT_ROWS_QKV = 10, WSG_OPT_ROWS_O = 11, WSG_OPT_ROWS_GATEUP = 12, WSG_OPT_ROWS_DOWN = 13,
        WSG_OPT_ROWS_HEAD = 14, WSG_OPT_GRID_QKV = 20, WSG_OPT_GRID_O = 21, WSG_OPT_GRID_GATEUP = 22,
        WSG_OPT_GRID_DOWN = 23, WSG_OPT_GRID_HEAD = 24 };
+/* OR WSG_OPT_FOR_TWO_TOKEN into any of the launch-shape options above
+ * (WSG_OPT_FUSE_ATTN_O, WSG_OPT_ROWS_ATTN_O, WSG_OPT_HEAD_WAVES, WSG_OPT_ROWS_*,
+ * WSG_OPT_GRID_*) to set it for two-token steps (wsg_step2) instead of
+ * single-token ones: the two kinds of step keep separate launch shapes.
+ * Two-token defaults: as above, except 4 head rows per wave. */
+enum { WSG_OPT_FOR_TWO_TOKEN = 0x100 };
 /* Stage kinds for WSG_OPT_TIMED_STAGE.  HEAD = final RMSNorm + vocabulary
  * GEMV + greedy argmax (one launch). */
 enum { WSG_STAGE_QKV = 0, WSG_STAGE_ATTN = 1, WSG_STAGE_O = 2, WSG_STAGE_GATEUP = 3,

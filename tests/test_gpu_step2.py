@@ -229,3 +229,51 @@ def test_step2_error_paths(mini_w):
     with pytest.raises(wsg.WsgError, match="OUT_OF_RANGE"):
         m.step2(3)                                   # would need slot 10
     m.close()
+
+
+def _two(opts):
+    import weight_streaming_gemv_amd as wsg
+    a = wsg._abi
+    names = {"head_rows": a.WSG_OPT_ROWS["head"], "head_waves": a.WSG_OPT_HEAD_WAVES, "qkv_rows": a.WSG_OPT_ROWS["qkv"],
+             "gu_rows": a.WSG_OPT_ROWS["gateup"], "down_rows": a.WSG_OPT_ROWS["down"], "o_rows": a.WSG_OPT_ROWS["o"],
+             "head_grid": a.WSG_OPT_GRID["head"], "gu_grid": a.WSG_OPT_GRID["gateup"],
+             "attn_o_rows": a.WSG_OPT_ROWS_ATTN_O, "fuse": a.WSG_OPT_FUSE_ATTN_O}
+    return [(a.WSG_OPT_FOR_TWO_TOKEN | names[k], v) for k, v in opts.items()]
+
+
+@pytest.mark.parametrize("opts", [
+    {"head_rows": 1}, {"head_rows": 2, "head_waves": 8}, {"head_waves": 16, "head_rows": 1},
+    {"qkv_rows": 4, "gu_rows": 2, "down_rows": 4}, {"head_grid": 64, "gu_grid": 40},
+    {"attn_o_rows": 4}, {"fuse": 0, "o_rows": 2}])
+def test_step2_launch_shapes(mini_w, opts):
+    """Two-token launch shapes (set with WSG_OPT_FOR_TWO_TOKEN) all match the oracle;
+    single-token steps keep their own shape (bit-identical before and after)."""
+    import weight_streaming_gemv_amd as wsg
+    cap = 96
+    m = wsg.Model(MINI, mini_w, max_context=cap, prefill_chunk=32)
+    prompt = prompt_ids(45, 30, MINI.vocab)
+    m.prefill(prompt)
+    m.step()
+    before = _np(m.logits())
+    for k, v in _two(opts):
+        m.set_option(k, v)
+    m.rewind(30)
+    m.step()
+    assert np.array_equal(_np(m.logits()), before)
+    orc = oracle.OracleModel(MINI, mini_w, cap)
+    spec_lockstep(m, orc, prompt, SCHEDULE[:6], label=f"mini step2 {opts}")
+    m.close()
+
+
+def test_two_token_option_checks(mini_w):
+    import weight_streaming_gemv_amd as wsg
+    a = wsg._abi
+    m = wsg.Model(MINI, mini_w, max_context=8)
+    for opt, bad in ((a.WSG_OPT_ROWS["head"], 3), (a.WSG_OPT_HEAD_WAVES, 2), (a.WSG_OPT_FUSE_ATTN_O, 2),
+                     (a.WSG_OPT_GRID["qkv"], -1)):
+        with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+            m.set_option(a.WSG_OPT_FOR_TWO_TOKEN | opt, bad)
+    for opt in (a.WSG_OPT_USE_GRAPH, a.WSG_OPT_TIMED_STAGE, 99):   # model-wide or unknown
+        with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+            m.set_option(a.WSG_OPT_FOR_TWO_TOKEN | opt, 0)
+    m.close()

@@ -18,6 +18,7 @@ WSG_F32, WSG_F16 = 0, 1
 WSG_OPT_USE_GRAPH, WSG_OPT_TIMED_STAGE = 1, 2
 WSG_OPT_FUSE_ATTN_O, WSG_OPT_ROWS_ATTN_O = 3, 15
 WSG_OPT_HEAD_WAVES = 16
+WSG_OPT_FOR_TWO_TOKEN = 0x100
 WSG_OPT_ROWS = {"qkv": 10, "o": 11, "gateup": 12, "down": 13, "head": 14}
 WSG_OPT_GRID = {"qkv": 20, "o": 21, "gateup": 22, "down": 23, "head": 24}
 WSG_STAGE_QKV, WSG_STAGE_ATTN, WSG_STAGE_O, WSG_STAGE_GATEUP, WSG_STAGE_DOWN, WSG_STAGE_HEAD = range(6)

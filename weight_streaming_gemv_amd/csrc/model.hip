@@ -210,7 +210,8 @@ struct wsg_model {
   PackedLayout pl;
   WsLayout wl;
   DecodeArgs args;
-  DecodeShape shape;
+  DecodeShape shape;    // launch shape of single-token steps
+  DecodeShape shape2;   // launch shape of two-token steps
   std::vector<LayerPtrs> layers;
   int32_t pos = 0;
   bool has_output = false;
@@ -275,14 +276,19 @@ bool timed(wsg_model* m, int stage, int64_t bytes, F&& launch) {
   return ok;
 }
 
+DecodeShape shape_for(const wsg_model* m, int tokens) {
+  DecodeShape sh = tokens == 2 ? m->shape2 : m->shape;
+  sh.tokens = tokens;
+  return sh;
+}
+
 // All layers of one step of `tokens` rows; the last down projection
 // advances the position when no head follows (prompt rows before the
 // last).  Short contexts (fused) use the fused attention + output-projection
 // launch.
 bool enqueue_body(wsg_model* m, int splits, bool fused, bool advance, int tokens) {
-  DecodeShape sh = m->shape;
+  DecodeShape sh = shape_for(m, tokens);
   sh.attn_splits = splits;
-  sh.tokens = tokens;
   const hipStream_t s = m->stream;
   const int L = m->d.L;
   for (int l = 0; l < L; ++l) {
@@ -310,11 +316,6 @@ bool enqueue_body(wsg_model* m, int splits, bool fused, bool advance, int tokens
   return true;
 }
 
-DecodeShape shape_for(const wsg_model* m, int tokens) {
-  DecodeShape sh = m->shape;
-  sh.tokens = tokens;
-  return sh;
-}
 bool enqueue_head(wsg_model* m, int tokens) { return launch_head(m->args, shape_for(m, tokens), m->stream); }
 bool enqueue_argmax(wsg_model* m, int tokens) { return launch_argmax(m->args, shape_for(m, tokens), m->stream); }
 
@@ -328,7 +329,8 @@ bool enqueue_argmax(wsg_model* m, int tokens) { return launch_argmax(m->args, sh
 constexpr int kFuseMaxKeys = 128;
 
 bool use_fused_attn_o(const wsg_model* m, int n_keys, int tokens) {
-  return m->shape.fuse_attn_o && n_keys <= kFuseMaxKeys && attn_o_part_slots(m->d.H, m->d.nkv, tokens) > 0;
+  return shape_for(m, tokens).fuse_attn_o && n_keys <= kFuseMaxKeys &&
+         attn_o_part_slots(m->d.H, m->d.nkv, tokens) > 0;
 }
 
 int splits_for(const wsg_model* m, int n_keys) {
@@ -641,6 +643,12 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   sh.attn_chunk = attn_chunk(d);
   sh.fuse_attn_o = 1;
   sh.rows_attn_o = 8;
+  // Two-token steps: four vocabulary rows per wave.  Each wave reads both
+  // activation rows once (from L2) for all of its rows; at one row per wave
+  // those reads double the L2 traffic of the weights they serve, and the
+  // argmax would reduce four times as many block keys.
+  m->shape2 = sh;
+  m->shape2.rows_head = 4;
 
   std::vector<float> cs, sn;
   fill_rope(*cfg, cs, sn);
@@ -813,21 +821,6 @@ wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value) {
         return fail(WSG_ERR_UNSUPPORTED, "in graph mode only the head stage can be timed");
       m->use_graph = value == 1;
       return WSG_OK;
-    case WSG_OPT_FUSE_ATTN_O:
-      if (value != 0 && value != 1) return fail(WSG_ERR_INVALID_ARG, "fuse_attn_o must be 0 or 1");
-      m->shape.fuse_attn_o = value;
-      drop_graphs(m);
-      return WSG_OK;
-    case WSG_OPT_ROWS_ATTN_O:
-      if (value != 4 && value != 8) return fail(WSG_ERR_INVALID_ARG, "attention/output rows per wave must be 4 or 8");
-      m->shape.rows_attn_o = value;
-      drop_graphs(m);
-      return WSG_OK;
-    case WSG_OPT_HEAD_WAVES:
-      if (value != 4 && value != 8 && value != 16) return fail(WSG_ERR_INVALID_ARG, "head waves must be 4, 8 or 16");
-      m->shape.head_waves = value;
-      drop_graphs(m);
-      return WSG_OK;
     case WSG_OPT_TIMED_STAGE:
       if (value < -1 || value > WSG_STAGE_HEAD) return fail(WSG_ERR_INVALID_ARG, "stage %d", value);
       if (m->use_graph && value >= 0 && value != WSG_STAGE_HEAD)
@@ -838,24 +831,40 @@ wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value) {
     default:
       break;
   }
-  if (option >= WSG_OPT_ROWS_QKV && option <= WSG_OPT_ROWS_HEAD) {
-    if (value != 1 && value != 2 && value != 4) return fail(WSG_ERR_INVALID_ARG, "rows per wave must be 1, 2 or 4");
-    int* rows[] = {&m->shape.rows_qkv, &m->shape.rows_o, &m->shape.rows_gu, &m->shape.rows_down, &m->shape.rows_head};
-    *rows[option - WSG_OPT_ROWS_QKV] = value;
-    drop_graphs(m);
-    return WSG_OK;
-  }
-  if (option >= WSG_OPT_GRID_QKV && option <= WSG_OPT_GRID_HEAD) {
-    if (value < 0 || value > (1 << 20)) return fail(WSG_ERR_INVALID_ARG, "grid must be in [0, 2^20]");
-    int* grids[] = {&m->shape.grid_qkv, &m->shape.grid_o, &m->shape.grid_gu, &m->shape.grid_down, &m->shape.grid_head};
-    *grids[option - WSG_OPT_GRID_QKV] = value;
-    drop_graphs(m);
-    return WSG_OK;
-  }
-  switch (option) {
+  // launch-shape options: of single-token steps, or with
+  // WSG_OPT_FOR_TWO_TOKEN of two-token steps
+  DecodeShape& sh = (option & WSG_OPT_FOR_TWO_TOKEN) ? m->shape2 : m->shape;
+  const int opt = option & ~WSG_OPT_FOR_TWO_TOKEN;
+  int* target = nullptr;
+  switch (opt) {
+    case WSG_OPT_FUSE_ATTN_O:
+      if (value != 0 && value != 1) return fail(WSG_ERR_INVALID_ARG, "fuse_attn_o must be 0 or 1");
+      target = &sh.fuse_attn_o;
+      break;
+    case WSG_OPT_ROWS_ATTN_O:
+      if (value != 4 && value != 8) return fail(WSG_ERR_INVALID_ARG, "attention/output rows per wave must be 4 or 8");
+      target = &sh.rows_attn_o;
+      break;
+    case WSG_OPT_HEAD_WAVES:
+      if (value != 4 && value != 8 && value != 16) return fail(WSG_ERR_INVALID_ARG, "head waves must be 4, 8 or 16");
+      target = &sh.head_waves;
+      break;
     default:
-      return fail(WSG_ERR_INVALID_ARG, "unknown option %d", option);
+      if (opt >= WSG_OPT_ROWS_QKV && opt <= WSG_OPT_ROWS_HEAD) {
+        if (value != 1 && value != 2 && value != 4) return fail(WSG_ERR_INVALID_ARG, "rows per wave must be 1, 2 or 4");
+        int* rows[] = {&sh.rows_qkv, &sh.rows_o, &sh.rows_gu, &sh.rows_down, &sh.rows_head};
+        target = rows[opt - WSG_OPT_ROWS_QKV];
+      } else if (opt >= WSG_OPT_GRID_QKV && opt <= WSG_OPT_GRID_HEAD) {
+        if (value < 0 || value > (1 << 20)) return fail(WSG_ERR_INVALID_ARG, "grid must be in [0, 2^20]");
+        int* grids[] = {&sh.grid_qkv, &sh.grid_o, &sh.grid_gu, &sh.grid_down, &sh.grid_head};
+        target = grids[opt - WSG_OPT_GRID_QKV];
+      }
+      break;
   }
+  if (!target) return fail(WSG_ERR_INVALID_ARG, "unknown option %d", option);
+  *target = value;
+  drop_graphs(m);
+  return WSG_OK;
 }
 
 wsg_status wsg_weight_storage(const wsg_model* m, int32_t* packed_matrices, int32_t* decode_matrices,
