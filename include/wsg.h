@@ -43,6 +43,18 @@ typedef enum {
  * always accumulate in FP32 (Megakernels, "What runs in the DSL"). */
 typedef enum { WSG_F32 = 0, WSG_F16 = 1 } wsg_dtype;
 
+/* Format of the decode matrices (W_qkv, W_o, W_gu, W_d and the tied
+ * embedding/vocabulary matrix).  WSG_W_DENSE: the storage dtype.
+ * WSG_W_Q4G64: symmetric int4 weights in groups of 64 along K with one FP16
+ * scale per group ("Our Kernel Benchmark Was Measuring the System Cache",
+ * "Summary": 4-bit decode matrix-vector products), weight = q * s; needs
+ * dtype WSG_F16 (activations, KV cache and logits in FP16, FP32
+ * accumulation), hidden, intermediate and n_q_heads*head_dim multiples of
+ * 1024, prefill_chunk 0 and lossless_pack 0.  The embedding gather
+ * dequantises its row and rounds it to FP16; the head multiplies by the
+ * exact q * s. */
+typedef enum { WSG_W_DENSE = 0, WSG_W_Q4G64 = 1 } wsg_weight_format;
+
 /* Decoder geometry and run limits.
  *   head_dim must be 128; hidden, intermediate and n_q_heads*head_dim must
  *   each be one of 512, 1024, 2048, 3072 (256 is also accepted for FP32);
@@ -58,6 +70,7 @@ typedef struct {
   float rope_theta;   /* RoPE base; pair i turns by p * theta^(-2i/head_dim) */
   int32_t dtype;      /* wsg_dtype */
   int32_t lossless_pack;  /* 1: lossless packed copies of the decode weights (FP32 only, see below) */
+  int32_t weight_format;  /* wsg_weight_format */
 } wsg_config;
 
 /* Host-side unpacked weights, element type = cfg.dtype (float32, or IEEE
@@ -84,6 +97,29 @@ typedef struct {
   const void* const* wd;
 } wsg_host_weights;
 
+/* Host-side int4 matrix [rows][K]: words [rows][K/8] (nibble j of word w
+ * holds k = 8w + j, low nibble first, two's complement in [-8, 7]) and
+ * scales [rows][K/64] (IEEE binary16 bit patterns), both row-major. */
+typedef struct {
+  const uint32_t* words;
+  const uint16_t* scales;
+} wsg_q4_matrix;
+
+/* Host-side int4 decode matrices of a WSG_W_Q4G64 model: the embedding
+ * [vocab][hidden] (also the tied head) and per layer (arrays of n_layers):
+ * wq [n_q*hd][hidden], wk and wv [n_kv*hd][hidden], wo [hidden][n_q*hd],
+ * wg and wu [intermediate][hidden], wd [hidden][intermediate]. */
+typedef struct {
+  wsg_q4_matrix embed;
+  const wsg_q4_matrix* wq;
+  const wsg_q4_matrix* wk;
+  const wsg_q4_matrix* wv;
+  const wsg_q4_matrix* wo;
+  const wsg_q4_matrix* wg;
+  const wsg_q4_matrix* wu;
+  const wsg_q4_matrix* wd;
+} wsg_host_q4_weights;
+
 /* Lossless decode-weight storage (Megakernels, "Lossless decode-weight
  * storage"): with cfg.lossless_pack = 1 (FP32 models), wsg_pack_weights also
  * writes a packed copy of each decode matrix (the embedding, read by the
@@ -108,9 +144,20 @@ wsg_status wsg_packed_weight_bytes(const wsg_config* cfg, size_t* bytes);
 /* Copy the host weights into the packed layout at host_out (out_bytes must
  * be at least wsg_packed_weight_bytes).  Fuses Wq/Wk/Wv into one
  * [(n_q+2 n_kv) hd][hidden] matrix and Wg/Wu into one [2 I][hidden] matrix;
- * values are copied bit for bit. */
+ * values are copied bit for bit.  Dense models only (WSG_W_Q4G64 configs
+ * are packed by wsg_pack_weights_q4: WSG_ERR_INVALID_ARG here). */
 wsg_status wsg_pack_weights(const wsg_config* cfg, const wsg_host_weights* w,
                             void* host_out, size_t out_bytes);
+
+/* Packed image of a WSG_W_Q4G64 model: the norm gains (FP16) come from
+ * `norms` (its embedding and matrix pointers are ignored and may be NULL),
+ * the decode matrices from `q`.  Each packed matrix row holds the row's
+ * K/8 words followed by its K/64 scales (row i of W_qkv is row i of
+ * [wq; wk; wv], of W_gu row i of [wg; wu]); values are copied bit for bit.
+ * Errors: a NULL pointer, out_bytes too small (WSG_ERR_INVALID_ARG), a
+ * config that is not WSG_W_Q4G64 (WSG_ERR_INVALID_ARG). */
+wsg_status wsg_pack_weights_q4(const wsg_config* cfg, const wsg_host_weights* norms,
+                               const wsg_host_q4_weights* q, void* host_out, size_t out_bytes);
 
 /* Size in bytes of the device workspace for cfg: KV cache
  * [n_layers][2][n_kv][max_context][head_dim], rotary table, stage buffers,

@@ -16,6 +16,14 @@ stored in the model dtype):
   8 down proj + residual     x = x + Wd act
   then h = rms(x, g_f) and logits = E h (tied head), token = lowest argmax.
 
+Int4 weights: a weight set with ``format`` "q4g64" gives each decode matrix
+(and the tied embedding) as int4 words and FP16 group scales; the oracle
+dequantises them once on the CPU to the exact values q * s (Our Kernel
+Benchmark Was Measuring the System Cache, "Summary": 4-bit weights) and
+then runs the same forward pass.  The embedding gather stores q * s in the
+model dtype, like every stage output; the head multiplies by the exact
+values.
+
 Rows: ``forward_rows`` runs a block of consecutive positions as one causal
 row matrix per layer.  Each row's arithmetic is the same as running the
 positions one at a time (the pages' chunked prefill keeps each row's full
@@ -27,6 +35,7 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
+from .gemv import dequant_q4g64
 from .prims import (argmax_lowest, gqa_attention, rms_norm, rope_angles, rope_apply,
                     silu, store)
 
@@ -44,15 +53,25 @@ class OracleModel:
     def __init__(self, shape, weights: Dict[str, object], max_context: int,
                  dtype: Optional[np.dtype] = None):
         self.shape = shape
-        self.dtype = np.dtype(dtype if dtype is not None else weights["embed"].dtype)
+        q4 = weights.get("format") == "q4g64"
+        self.dtype = np.dtype(dtype if dtype is not None else weights["final_norm" if q4 else "embed"].dtype)
         self.cap = int(max_context)
+
+        def mat(v):
+            """A stored matrix as float64: exact int4 values q * s, or the stored dense values."""
+            if q4:
+                words, scales = v
+                return dequant_q4g64(words, scales, 8 * np.asarray(words).shape[1]).astype(F64)
+            return np.asarray(v, dtype=self.dtype).astype(F64)
+
         # float64 copies of the stored weights, made once (setup, untimed)
-        self.E = np.asarray(weights["embed"], dtype=self.dtype)
-        self.E64 = self.E.astype(F64)
+        self.E64 = mat(weights["embed"])
+        self.E = store(self.E64, self.dtype)          # the gathered rows, as stored
         self.g_f = np.asarray(weights["final_norm"], dtype=self.dtype).astype(F64)
         self.layers: List[Dict[str, np.ndarray]] = []
         for lw in weights["layers"]:
-            self.layers.append({k: np.asarray(v, dtype=self.dtype).astype(F64) for k, v in lw.items()})
+            self.layers.append({k: (mat(v) if k.startswith("w") else np.asarray(v, dtype=self.dtype).astype(F64))
+                                for k, v in lw.items()})
         L, hkv, d = shape.n_layers, shape.n_kv_heads, shape.head_dim
         self.k_cache = np.zeros((L, hkv, self.cap, d), dtype=self.dtype)
         self.v_cache = np.zeros((L, hkv, self.cap, d), dtype=self.dtype)

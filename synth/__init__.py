@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "ModelShape", "QWEN3_0_6B", "MINI", "model_weights", "model_weights_bf16", "bf16_representable", "prompt_ids",
-    "gemv_inputs", "q4g64_inputs", "pack_int4_rows", "GEMV_SHAPES", "Q4_SHAPES",
+    "gemv_inputs", "q4g64_inputs", "pack_int4_rows", "model_weights_q4", "GEMV_SHAPES", "Q4_SHAPES",
     "PROMPT_SEEDS", "WEIGHT_SEED",
 ]
 
@@ -137,6 +137,37 @@ def model_weights_bf16(shape: ModelShape, seed: int = WEIGHT_SEED) -> Dict[str, 
         for name in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
             lw[name] = bf16_representable(lw[name])
     return w
+
+
+def model_weights_q4(shape: ModelShape, seed: int = WEIGHT_SEED, scale_std: float = 0.01) -> Dict[str, object]:
+    """Int4 group-64 weights of ``shape``, drawn as in the int4 GEMV workload: per
+    matrix ``q`` uniform in [-8, 7] and FP16 scales ``|N(0, scale_std)|`` per group
+    of 64 along K.  Returns the layout of ``model_weights`` with ``format`` =
+    "q4g64" and each matrix a pair ``(words uint32[rows, k/8], scales f16[rows, k/64])``
+    (``pack_int4_rows`` word format); norm gains are FP16 ones."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    h, i, q, kv, d = shape.hidden, shape.intermediate, shape.q_width, shape.kv_width, shape.head_dim
+
+    def mat(rows, k):
+        qv = rng.integers(-8, 8, (rows, k)).astype(np.int8)
+        sc = np.abs(rng.normal(0.0, scale_std, (rows, k // 64))).astype(np.float16)
+        return pack_int4_rows(qv), sc
+
+    one = np.float16
+    out: Dict[str, object] = {"format": "q4g64", "embed": mat(shape.vocab, h), "final_norm": np.ones(h, one)}
+    layers: List[Dict[str, object]] = []
+    for _ in range(shape.n_layers):
+        lw: Dict[str, object] = {}
+        for name, (rows, k) in (("wq", (q, h)), ("wk", (kv, h)), ("wv", (kv, h)), ("wo", (h, q)),
+                                ("wg", (i, h)), ("wu", (i, h)), ("wd", (h, i))):
+            lw[name] = mat(rows, k)
+        lw["in_norm"] = np.ones(h, one)
+        lw["post_norm"] = np.ones(h, one)
+        lw["q_norm"] = np.ones(d, one)
+        lw["k_norm"] = np.ones(d, one)
+        layers.append(lw)
+    out["layers"] = layers
+    return out
 
 
 def prompt_ids(seed: int, n: int, vocab: int) -> np.ndarray:

@@ -203,3 +203,63 @@ def test_bf16_rounding_matches_torch():
     got = bf16_representable(a)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
     assert not np.any(got.view(np.uint32) & 0xFFFF)
+
+
+def _q4_cfg(abi, shape, cap=16, dtype=1, chunk=0):
+    c = _cfg(abi, shape, cap=cap, dtype=dtype, chunk=chunk)
+    c.weight_format = abi.WSG_W_Q4G64
+    return c
+
+
+def test_q4_config_validation(abi):
+    from synth import MINI, ModelShape
+    L = abi.lib()
+    n = C.c_size_t()
+    sh = ModelShape(n_layers=1, hidden=1024, intermediate=2048, n_q_heads=8, n_kv_heads=4, head_dim=128, vocab=50)
+    assert L.wsg_packed_weight_bytes(C.byref(_q4_cfg(abi, sh)), C.byref(n)) == abi.WSG_OK
+    # int4 rows: k/2 bytes of words + k/32 bytes of scales
+    rb = lambda k: k // 2 + k // 32
+    al = lambda v: (v + 255) // 256 * 256
+    exp = al(50 * rb(1024)) + al(1024 * 2)
+    exp += 2 * al(1024 * 2) + 2 * al(128 * 2)
+    exp += al((1024 + 2 * 512) * rb(1024)) + al(1024 * rb(1024)) + al(2 * 2048 * rb(1024)) + al(1024 * rb(2048))
+    assert n.value == exp
+    assert L.wsg_packed_weight_bytes(C.byref(_q4_cfg(abi, sh, dtype=0)), C.byref(n)) == abi.WSG_ERR_UNSUPPORTED
+    assert b"FP16" in L.wsg_last_error()
+    assert L.wsg_packed_weight_bytes(C.byref(_q4_cfg(abi, MINI)), C.byref(n)) == abi.WSG_ERR_UNSUPPORTED
+    bad = _q4_cfg(abi, sh)
+    bad.weight_format = 7
+    assert L.wsg_packed_weight_bytes(C.byref(bad), C.byref(n)) == abi.WSG_ERR_INVALID_ARG
+
+
+def test_q4_pack_layout_is_row_interleaved_copy(abi):
+    """Each packed int4 row is the row's words followed by its scales, bit for bit;
+    W_qkv stacks wq, wk, wv and W_gu stacks wg, wu; the dense packer refuses int4."""
+    from synth import ModelShape, model_weights_q4
+    from weight_streaming_gemv_amd import pack_weights, pack_weights_q4
+    sh = ModelShape(n_layers=1, hidden=1024, intermediate=1024, n_q_heads=8, n_kv_heads=4, head_dim=128, vocab=40)
+    w = model_weights_q4(sh, seed=2)
+    cfg = _q4_cfg(abi, sh)
+    img = pack_weights_q4(cfg, w)
+    rb = 1024 // 2 + 1024 // 32
+
+    def row(off, r):
+        return img[off + r * rb: off + (r + 1) * rb]
+
+    def expect(m, r):
+        return np.concatenate([m[0][r].view(np.uint8), m[1][r].view(np.uint8)])
+
+    E = w["embed"]
+    for r in (0, 17, 39):
+        assert np.array_equal(row(0, r), expect(E, r))
+    al = lambda v: (v + 255) // 256 * 256
+    off = al(40 * rb)
+    assert np.array_equal(img[off:off + 2048].view(np.float16), w["final_norm"])
+    off += al(2048) + 2 * al(2048) + 2 * al(256)          # final_norm, in/post norm, q/k norm
+    lw = w["layers"][0]
+    for r, (m, rr) in {0: (lw["wq"], 0), 1023: (lw["wq"], 1023), 1024: (lw["wk"], 0),
+                       1536: (lw["wv"], 0), 2047: (lw["wv"], 511)}.items():
+        assert np.array_equal(row(off, r), expect(m, rr))
+    from synth import model_weights
+    with pytest.raises(Exception, match="INVALID_ARG"):
+        pack_weights(cfg, model_weights(sh, seed=2, dtype=np.float16))   # int4 config, dense packer

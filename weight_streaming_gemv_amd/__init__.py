@@ -90,11 +90,16 @@ def stream_read(buf, out=None, stream=None):
 
 # ---------------------------------------------------------------- model
 def make_config(shape, max_context: int, dtype: int = WSG_F32, prefill_chunk: int = 0,
-                lossless_pack: bool = False) -> wsg_config:
+                lossless_pack: bool = False, weight_format: int = 0) -> wsg_config:
     """C config from a ``synth.ModelShape``-like object."""
     return wsg_config(shape.n_layers, shape.hidden, shape.intermediate, shape.n_q_heads, shape.n_kv_heads,
                       shape.head_dim, shape.vocab, max_context, prefill_chunk, shape.rms_eps, shape.rope_theta,
-                      dtype, int(lossless_pack))
+                      dtype, int(lossless_pack), int(weight_format))
+
+
+def is_q4(weights: Dict[str, object]) -> bool:
+    """True for int4 weight sets: each decode matrix a (words uint32, scales float16) pair."""
+    return weights.get("format") == "q4g64"
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -134,6 +139,48 @@ def pack_weights(cfg: wsg_config, weights: Dict[str, object]) -> np.ndarray:
     return out
 
 
+def pack_weights_q4(cfg: wsg_config, weights: Dict[str, object]) -> np.ndarray:
+    """Host packing of an int4 model through ``wsg_pack_weights_q4`` (bit-for-bit copies)."""
+    keep = []
+
+    def arr(a, dt):
+        a = np.ascontiguousarray(a)
+        if a.dtype != dt:
+            raise ValueError(f"array dtype {a.dtype}, expected {np.dtype(dt)}")
+        keep.append(a)
+        return _ptr(a)
+
+    def q4(m):
+        words, scales = m
+        return _abi.wsg_q4_matrix(arr(words, np.uint32), arr(scales, np.float16))
+
+    layers = weights["layers"]
+    L = cfg.n_layers
+    if len(layers) != L:
+        raise ValueError("layer count mismatch")
+
+    def glist(name):
+        P = (C.c_void_p * L)(*[arr(lw[name], np.float16) for lw in layers])
+        keep.append(P)
+        return C.cast(P, C.POINTER(C.c_void_p))
+
+    def qlist(name):
+        P = (_abi.wsg_q4_matrix * L)(*[q4(lw[name]) for lw in layers])
+        keep.append(P)
+        return C.cast(P, C.POINTER(_abi.wsg_q4_matrix))
+
+    none = C.POINTER(C.c_void_p)()
+    norms = wsg_host_weights(None, arr(weights["final_norm"], np.float16), glist("in_norm"), none, none, none,
+                             glist("q_norm"), glist("k_norm"), none, glist("post_norm"), none, none, none)
+    qw = _abi.wsg_host_q4_weights(q4(weights["embed"]), qlist("wq"), qlist("wk"), qlist("wv"), qlist("wo"),
+                                  qlist("wg"), qlist("wu"), qlist("wd"))
+    n = C.c_size_t()
+    check(_abi.lib().wsg_packed_weight_bytes(C.byref(cfg), C.byref(n)))
+    out = np.empty(n.value, dtype=np.uint8)
+    check(_abi.lib().wsg_pack_weights_q4(C.byref(cfg), C.byref(norms), C.byref(qw), _ptr(out), n.value))
+    return out
+
+
 class Model:
     """A decode model on the GPU; weights and workspace are torch device tensors it owns."""
 
@@ -143,10 +190,15 @@ class Model:
         torch = _torch()
         self.torch = torch
         self.shape = shape
-        self.cfg = make_config(shape, max_context, dtype, prefill_chunk, lossless_pack)
+        q4 = is_q4(weights)
+        self.cfg = make_config(shape, max_context, dtype, prefill_chunk, lossless_pack,
+                               _abi.WSG_W_Q4G64 if q4 else _abi.WSG_W_DENSE)
         self.np_dtype = np.float16 if dtype == WSG_F16 else np.float32
         self.t_dtype = torch.float16 if dtype == WSG_F16 else torch.float32
-        host = packed if packed is not None else pack_weights(self.cfg, weights)
+        if packed is not None:
+            host = packed
+        else:
+            host = pack_weights_q4(self.cfg, weights) if q4 else pack_weights(self.cfg, weights)
         self.d_packed = torch.from_numpy(host).to("cuda")
         n = C.c_size_t()
         check(_abi.lib().wsg_workspace_bytes(C.byref(self.cfg), C.byref(n)))

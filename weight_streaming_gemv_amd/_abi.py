@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libwsg.so")
 
 WSG_OK, WSG_ERR_INVALID_ARG, WSG_ERR_OUT_OF_RANGE, WSG_ERR_STATE, WSG_ERR_HIP, WSG_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 WSG_F32, WSG_F16 = 0, 1
+WSG_W_DENSE, WSG_W_Q4G64 = 0, 1
 WSG_OPT_USE_GRAPH, WSG_OPT_TIMED_STAGE = 1, 2
 WSG_OPT_FUSE_ATTN_O, WSG_OPT_ROWS_ATTN_O = 3, 15
 WSG_OPT_HEAD_WAVES = 16
@@ -33,7 +34,7 @@ class wsg_config(C.Structure):
                 ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("vocab", C.c_int32), ("max_context", C.c_int32), ("prefill_chunk", C.c_int32),
                 ("rms_eps", C.c_float), ("rope_theta", C.c_float), ("dtype", C.c_int32),
-                ("lossless_pack", C.c_int32)]
+                ("lossless_pack", C.c_int32), ("weight_format", C.c_int32)]
 
 
 _PP = C.POINTER(C.c_void_p)
@@ -43,6 +44,18 @@ class wsg_host_weights(C.Structure):
     _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("in_norm", _PP), ("wq", _PP),
                 ("wk", _PP), ("wv", _PP), ("q_norm", _PP), ("k_norm", _PP), ("wo", _PP),
                 ("post_norm", _PP), ("wg", _PP), ("wu", _PP), ("wd", _PP)]
+
+
+class wsg_q4_matrix(C.Structure):
+    _fields_ = [("words", C.c_void_p), ("scales", C.c_void_p)]
+
+
+_PQ = C.POINTER(wsg_q4_matrix)
+
+
+class wsg_host_q4_weights(C.Structure):
+    _fields_ = [("embed", wsg_q4_matrix), ("wq", _PQ), ("wk", _PQ), ("wv", _PQ), ("wo", _PQ), ("wg", _PQ),
+                ("wu", _PQ), ("wd", _PQ)]
 
 
 class WsgError(RuntimeError):
@@ -57,6 +70,8 @@ _lib = None
 _SIGS = {
     "wsg_packed_weight_bytes": (C.c_int, [C.POINTER(wsg_config), C.POINTER(C.c_size_t)]),
     "wsg_pack_weights": (C.c_int, [C.POINTER(wsg_config), C.POINTER(wsg_host_weights), C.c_void_p, C.c_size_t]),
+    "wsg_pack_weights_q4": (C.c_int, [C.POINTER(wsg_config), C.POINTER(wsg_host_weights),
+                                      C.POINTER(wsg_host_q4_weights), C.c_void_p, C.c_size_t]),
     "wsg_workspace_bytes": (C.c_int, [C.POINTER(wsg_config), C.POINTER(C.c_size_t)]),
     "wsg_model_create": (C.c_int, [C.POINTER(wsg_config), C.c_void_p, C.c_size_t, C.c_void_p, C.c_size_t,
                                    C.c_void_p, C.POINTER(C.c_void_p)]),

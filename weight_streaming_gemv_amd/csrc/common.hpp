@@ -135,6 +135,23 @@ struct PackedVec4 {
 };
 template <> struct WVec<bf16w> { using type = PackedVec4; };
 
+// int4 group-64 weights (tag type for the decode kernels): each matrix row
+// holds K/8 32-bit words (nibble j of word w is k = 8w + j, low nibble
+// first, a two's-complement value in [-8, 7]) followed by the row's K/64
+// FP16 scales, one per group of 64 consecutive k; the weight is q * s.
+// Rows are 16-byte aligned for every K that is a multiple of 1024 (the
+// sizes this format supports).
+struct q4w { uint32_t w; };
+template <int K> struct Q4Row {
+  static_assert(K % 1024 == 0, "int4 rows hold a multiple of 1024 weights");
+  static constexpr int kWordBytes = K / 2;
+  static constexpr int kBytes = K / 2 + K / 32;   // words, then FP16 scales
+};
+// Lane layout of the int4 decode GEMVs: 16 consecutive k (two words, one
+// 8-byte load) per lane per 1024-wide chunk.
+struct Q4Vec { static constexpr int N = 16; };
+template <> struct WVec<q4w> { using type = Q4Vec; };
+
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }

@@ -39,23 +39,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 __host__ __device__ __forceinline__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Activations of length K in the lane layout the GEMV rows use:
-// a[c*VEC + i] = x[c*64*VEC + lane*VEC + i].
-template <typename TS, int K>
+// a[c*VEC + i] = x[c*64*VEC + lane*VEC + i] (VEC consecutive elements per
+// lane and chunk, loaded as VEC / Vec16<TS>::N 16-byte vectors).
+template <typename TS, int K, int VEC = Vec16<TS>::N>
 struct Act {
-  static constexpr int VEC = Vec16<TS>::N;
+  static constexpr int V16 = Vec16<TS>::N;
   static constexpr int NV = K / (kWave * VEC);
-  static_assert(K % (kWave * VEC) == 0, "K must be a multiple of 64 vectors");
+  static_assert(K % (kWave * VEC) == 0, "K must be a multiple of 64 lane vectors");
+  static_assert(VEC % V16 == 0, "whole 16-byte vectors per lane and chunk");
   float a[K / kWave];
 
   __device__ __forceinline__ void load(const TS* p) {
     const int lane = lane_id();
 #pragma unroll
-    for (int c = 0; c < NV; ++c) {
-      Vec16<TS> v;
-      v.template load<false>(p + c * kWave * VEC + lane * VEC);
+    for (int c = 0; c < NV; ++c)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) a[c * VEC + i] = v.v[i];
-    }
+      for (int u = 0; u < VEC / V16; ++u) {
+        Vec16<TS> v;
+        v.template load<false>(p + c * kWave * VEC + lane * VEC + u * V16);
+#pragma unroll
+        for (int i = 0; i < V16; ++i) a[c * VEC + u * V16 + i] = v.v[i];
+      }
   }
   // From an FP32 array in the same element order (e.g. in LDS).
   __device__ __forceinline__ void load_f32(const float* p) {
@@ -79,7 +83,7 @@ struct Act {
     for (int i = 0; i < K / kWave; ++i) ss = fmaf(a[i], a[i], ss);
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)K + eps);
-    Act<TS, K> g;
+    Act<TS, K, VEC> g;
     g.load(gain);
 #pragma unroll
     for (int i = 0; i < K / kWave; ++i) a[i] = a[i] * inv * g.a[i];
@@ -105,9 +109,9 @@ struct WRows {
       for (int c = 0; c < NV; ++c) v[r][c].template load<false>(wr + c * kWave * VEC);
     }
   }
-  template <typename TS>
-  __device__ __forceinline__ void dot(const Act<TS, K>& x, float (&acc)[R]) const {
-    static_assert(Act<TS, K>::VEC == VEC, "weights and activations share the lane layout");
+  template <typename A>
+  __device__ __forceinline__ void dot(const A& x, float (&acc)[R]) const {
+    static_assert(A::NV == NV && A::NV * VEC * kWave == K, "weights and activations share the lane layout");
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float a = 0.f;
@@ -119,6 +123,138 @@ struct WRows {
     }
   }
 };
+
+// ---------------------------------------------------------- int4 weights
+// Activations of an int4 GEMV: FP16 pairs in registers, ordered to meet the
+// nibble pairs (j, j+4) that one masked 32-bit word yields.  Lane layout:
+// chunk c, word i (0, 1), pair j (0..3) holds x[k0 + 8i + j] and
+// x[k0 + 8i + j + 4], k0 = c*1024 + 16*lane.  Rounding the FP32 activations
+// to FP16 here is the storage rounding of the stage input.
+template <int K>
+struct Q4Act {
+  static constexpr int NV = K / 1024;
+  h2_t h[NV][8];
+  template <typename TS>
+  __device__ __forceinline__ void from(const Act<TS, K, 16>& x) {
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h2_t p;
+          p.x = (_Float16)x.a[c * 16 + 8 * i + j];
+          p.y = (_Float16)x.a[c * 16 + 8 * i + j + 4];
+          h[c][4 * i + j] = p;
+        }
+  }
+};
+
+// Row n of an int4 matrix of width K.
+template <int K>
+__device__ __forceinline__ const uint8_t* q4_row(const q4w* W, size_t n) {
+  return reinterpret_cast<const uint8_t*>(W) + n * Q4Row<K>::kBytes;
+}
+
+// The four FP16 pairs of one word: nibbles (j, j+4) of w as exact FP16
+// values q = u - 8, from u = q ^ 8 (two's complement to offset binary)
+// OR-ed under the exponent of 1024 and reduced by 1032.
+__device__ __forceinline__ void q4_pairs(uint32_t w, h2_t (&p)[4]) {
+  const h2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const uint32_t v = w ^ 0x88888888u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = as_h2(((v >> (4 * j)) & 0x000F000Fu) | 0x64006400u) - bias;
+}
+
+template <int K, int R>
+struct WRows<q4w, K, R> {
+  static constexpr int NV = K / 1024;
+  typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+  u2_t q[R][NV];
+  uint16_t s[R][NV];
+  __device__ __forceinline__ void load(const q4w* __restrict__ W, int row0, int M) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint8_t* row = q4_row<K>(W, (size_t)min(row0 + r, M - 1));
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        q[r][c] = *reinterpret_cast<const u2_t*>(row + c * 512 + lane * 8);
+        s[r][c] = *reinterpret_cast<const uint16_t*>(row + Q4Row<K>::kWordBytes + 2 * (c * 16 + (lane >> 2)));
+      }
+    }
+  }
+  // acc[r] = sum over chunks of s * (sum of the chunk's 16 q*x products):
+  // products exact, FP32 accumulation.
+  __device__ __forceinline__ void dot(const Q4Act<K>& x, float (&acc)[R]) const {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        h2_t p[4];
+        float in = 0.f;
+        q4_pairs(q[r][c].x, p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) in = dot2(p[j], x.h[c][j], in);
+        q4_pairs(q[r][c].y, p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) in = dot2(p[j], x.h[c][4 + j], in);
+        a = fmaf(__half2float(__ushort_as_half(s[r][c])), in, a);
+      }
+      acc[r] = a;
+    }
+  }
+};
+
+// Row n of the lane's elements of an int4 matrix, dequantised (q * s,
+// exact in FP32) and rounded as stored: the embedding gather of an int4
+// model.
+template <typename TS, int K>
+__device__ __forceinline__ void q4_gather(const q4w* __restrict__ E, size_t n, Act<TS, K, 16>& x) {
+  const int lane = lane_id();
+  const uint8_t* row = q4_row<K>(E, n);
+#pragma unroll
+  for (int c = 0; c < K / 1024; ++c) {
+    typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+    const u2_t w = *reinterpret_cast<const u2_t*>(row + c * 512 + lane * 8);
+    const float s = __half2float(
+        __ushort_as_half(*reinterpret_cast<const uint16_t*>(row + Q4Row<K>::kWordBytes + 2 * (c * 16 + (lane >> 2)))));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t word = i < 8 ? w.x : w.y;
+      const int q = (int)(word << (28 - 4 * (i & 7))) >> 28;   // sign-extended nibble
+      x.a[c * 16 + i] = Store<TS>::to_f(Store<TS>::from_f((float)q * s));
+    }
+  }
+}
+
+// Activation operand of a weight storage: the FP32 lane array (plain and
+// packed FP32 storage), or FP16 pairs for int4 (built once per wave, after
+// the norm).
+template <typename TS, typename TW, int K>
+struct Operand {
+  using act = Act<TS, K, WVec<TW>::type::N>;
+  using dot_t = act;
+  static __device__ __forceinline__ dot_t prep(const act& a) { return a; }
+};
+template <typename TS, int K>
+struct Operand<TS, q4w, K> {
+  using act = Act<TS, K, 16>;
+  using dot_t = Q4Act<K>;
+  static __device__ __forceinline__ dot_t prep(const act& a) {
+    dot_t d;
+    d.from(a);
+    return d;
+  }
+};
+
+// Rows [n, ...) of a matrix of width K (the up half of the gate/up matrix).
+template <typename TW, int K>
+__device__ __forceinline__ const TW* rows_from(const TW* W, size_t n) {
+  if constexpr (std::is_same<TW, q4w>::value) return reinterpret_cast<const q4w*>(q4_row<K>(W, n));
+  else return W + n * K;
+}
 
 __device__ __forceinline__ int wave_row_groups_begin() { return blockIdx.x * kWavesPerBlock + wave_id(); }
 __device__ __forceinline__ int wave_row_groups_stride() { return gridDim.x * kWavesPerBlock; }
@@ -141,15 +277,16 @@ __device__ __forceinline__ float rows_prefetch(const TS* __restrict__ base, int 
 // row streamed: activations and outputs are [T][.] arrays.
 template <typename TS, typename TW, int H, int R, int T>
 __global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const TS* __restrict__ in_norm,
-                                                TS* __restrict__ x_res, const TS* __restrict__ embed,
+                                                TS* __restrict__ x_res, const void* __restrict__ embed,
                                                 const int32_t* __restrict__ ids, const int32_t* __restrict__ ctrl,
                                                 const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
                                                 float* __restrict__ rope_cur, int first_layer, int vocab, float eps,
                                                 TS* __restrict__ out, int M) {
+  using Op = Operand<TS, TW, H>;
   const int ngroups = ceil_div(M, R);
   int g = wave_row_groups_begin();
   WRows<TW, H, R> w;
-  Act<TS, H> x[T];
+  typename Op::act x[T];
   // Vector loads return in issue order: the residual goes out before the
   // first weight rows (so the norm overlaps them); at layer 0 the
   // position -> id -> embedding chain is issued after them.
@@ -166,7 +303,8 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const 
     for (int t = 0; t < T; ++t) {
       int tok = ids[pos + t];
       tok = (tok < 0 || tok >= vocab) ? 0 : tok;   // ids are validated on the host; never read outside E
-      x[t].load(embed + (size_t)tok * H);
+      if constexpr (std::is_same<TW, q4w>::value) q4_gather<TS, H>(static_cast<const q4w*>(embed), tok, x[t]);
+      else x[t].load(static_cast<const TS*>(embed) + (size_t)tok * H);
       if (blockIdx.x == 0 && wave == t) x[t].store(x_res + t * H);
     }
     static_assert(2 * T <= kWavesPerBlock, "a wave per residual row and per rotary row");
@@ -179,13 +317,17 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const 
       rope_cur[t * kD + kD / 2 + lane] = rope_sin[(size_t)(pos + t) * (kD / 2) + lane];
     }
   }
+  typename Op::dot_t xd[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) x[t].rms_norm(in_norm, eps);
+  for (int t = 0; t < T; ++t) {
+    x[t].rms_norm(in_norm, eps);
+    xd[t] = Op::prep(x[t]);
+  }
   const int lane = lane_id();
   for (; g < ngroups; g += wave_row_groups_stride()) {
     float acc[T][R];
 #pragma unroll
-    for (int t = 0; t < T; ++t) w.dot(x[t], acc[t]);
+    for (int t = 0; t < T; ++t) w.dot(xd[t], acc[t]);
     const int next = g + wave_row_groups_stride();
     if (next < ngroups) w.load(W, next * R, M);
 #pragma unroll
@@ -206,10 +348,11 @@ template <typename TS, typename TW, int K, int R, int T>
 __global__ __launch_bounds__(kBlock) void k_gemv_residual(const TW* __restrict__ W, const TS* __restrict__ in,
                                                           const TS* __restrict__ x_in, TS* __restrict__ x_out, int M,
                                                           int32_t* __restrict__ ctrl, int advance_pos) {
+  using Op = Operand<TS, TW, K>;
   const int ngroups = ceil_div(M, R);
   int g = wave_row_groups_begin();
   // operands first, then the weight rows (vector loads return in issue order)
-  Act<TS, K> x[T];
+  typename Op::act x[T];
   float xr[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -220,11 +363,14 @@ __global__ __launch_bounds__(kBlock) void k_gemv_residual(const TW* __restrict__
   WRows<TW, K, R> w;
   w.load(W, g * R, M);   // rows clamped into W: no branch around the loads
   __builtin_amdgcn_sched_barrier(0);
+  typename Op::dot_t xd[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) xd[t] = Op::prep(x[t]);
   const int lane = lane_id();
   for (; g < ngroups; g += wave_row_groups_stride()) {
     float acc[T][R];
 #pragma unroll
-    for (int t = 0; t < T; ++t) w.dot(x[t], acc[t]);
+    for (int t = 0; t < T; ++t) w.dot(xd[t], acc[t]);
     const int next = g + wave_row_groups_stride();
     float xr_next[T];
 #pragma unroll
@@ -266,11 +412,12 @@ template <typename TS, typename TW, int H, int R, int NP, int T>
 __global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, const TS* __restrict__ post_norm,
                                                    const TS* __restrict__ x_res, const float* __restrict__ opart,
                                                    float eps, TS* __restrict__ act, int I, TS* __restrict__ x2_out) {
+  using Op = Operand<TS, TW, H>;
   const int ngroups = ceil_div(I, R);
-  const TW* Wu = Wgu + (size_t)I * H;
+  const TW* Wu = rows_from<TW, H>(Wgu, I);
   const int tid = threadIdx.x;
   int g = wave_row_groups_begin();
-  Act<TS, H> x[T];
+  typename Op::act x[T];
   WRows<TW, H, R> wg, wu;
   if constexpr (NP > 0) {
     // Vector loads return in issue order, so the partials (this thread's
@@ -325,15 +472,19 @@ __global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, c
     wu.load(Wu, g * R, I);
     __builtin_amdgcn_sched_barrier(0);
   }
+  typename Op::dot_t xd[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) x[t].rms_norm(post_norm, eps);
+  for (int t = 0; t < T; ++t) {
+    x[t].rms_norm(post_norm, eps);
+    xd[t] = Op::prep(x[t]);
+  }
   const int lane = lane_id();
   for (; g < ngroups; g += wave_row_groups_stride()) {
     float ga[T][R], ua[T][R];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      wg.dot(x[t], ga[t]);
-      wu.dot(x[t], ua[t]);
+      wg.dot(xd[t], ga[t]);
+      wu.dot(xd[t], ua[t]);
     }
     const int next = g + wave_row_groups_stride();
     if (next < ngroups) { wg.load(Wgu, next * R, I); wu.load(Wu, next * R, I); }
@@ -384,13 +535,16 @@ __global__ __launch_bounds__(WPB * kWave) void k_head(const TW* __restrict__ E, 
   const int ngroups = ceil_div(V, R);
   int g = blockIdx.x * WPB + wave_id();
   const int stride = gridDim.x * WPB;
+  using Op = Operand<TS, TW, H>;
   WRows<TW, H, R> w;
   if (g < ngroups) w.load(E, g * R, V);   // first rows in flight before the norm
-  Act<TS, H> x[T];
+  typename Op::dot_t xd[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    x[t].load(x_res + t * H);
-    x[t].rms_norm(final_norm, eps);
+    typename Op::act x;
+    x.load(x_res + t * H);
+    x.rms_norm(final_norm, eps);
+    xd[t] = Op::prep(x);
   }
   unsigned long long best[T];
 #pragma unroll
@@ -398,7 +552,7 @@ __global__ __launch_bounds__(WPB * kWave) void k_head(const TW* __restrict__ E, 
   for (; g < ngroups; g += stride) {
     float acc[T][R];
 #pragma unroll
-    for (int t = 0; t < T; ++t) w.dot(x[t], acc[t]);
+    for (int t = 0; t < T; ++t) w.dot(xd[t], acc[t]);
     const int next = g + stride;
     if (next < ngroups) w.load(E, next * R, V);
 #pragma unroll
@@ -973,23 +1127,23 @@ int head_grid(int V, int R, int waves, int grid) {
   return (b + 1) & ~1;
 }
 
-// K values compiled in; a K must also be a multiple of 64 16-byte vectors
-// of the storage type (256 floats, 512 halves).
+// K values compiled in; a K must also be a multiple of 64 lane vectors of
+// the weight storage (256 floats, 512 halves, 1024 int4 weights).
 template <int V> using IC = std::integral_constant<int, V>;
 
-template <typename TS, int K, typename F>
+template <typename TW, int K, typename F>
 bool call_k(F& f) {
-  if constexpr (K % (kWave * Vec16<TS>::N) == 0) return f(IC<K>{});
+  if constexpr (K % (kWave * WVec<TW>::type::N) == 0) return f(IC<K>{});
   else return false;
 }
-template <typename TS, typename F>
+template <typename TW, typename F>
 bool with_k(int K, F&& f) {
   switch (K) {
-    case 256: return call_k<TS, 256>(f);
-    case 512: return call_k<TS, 512>(f);
-    case 1024: return call_k<TS, 1024>(f);
-    case 2048: return call_k<TS, 2048>(f);
-    case 3072: return call_k<TS, 3072>(f);
+    case 256: return call_k<TW, 256>(f);
+    case 512: return call_k<TW, 512>(f);
+    case 1024: return call_k<TW, 1024>(f);
+    case 2048: return call_k<TW, 2048>(f);
+    case 3072: return call_k<TW, 3072>(f);
     default: return false;
   }
 }
@@ -1011,10 +1165,17 @@ bool with_r(int R, F&& f) {
   }
 }
 
-// Weight storage of one matrix: its packed copy when there is one (FP32
-// models only), else the storage type itself.  f receives the typed pointer.
-template <typename TS, typename F>
-bool with_w(const void* w, const void* packed, F&& f) {
+// Weight storage of one matrix: int4 (FP16 models with int4 weights), its
+// lossless packed copy when there is one (FP32 models only), else the
+// storage type itself.  f receives the typed pointer.  Launches without an
+// int4 kernel pass Q4 = false (the caller never selects them for int4
+// weights).
+template <typename TS, bool Q4 = true, typename F>
+bool with_w(int wfmt, const void* w, const void* packed, F&& f) {
+  if (wfmt == kWeightsQ4) {
+    if constexpr (Q4 && std::is_same<TS, __half>::value) return f(static_cast<const q4w*>(w));
+    else return false;
+  }
   if constexpr (std::is_same<TS, float>::value)
     if (packed) return f(static_cast<const bf16w*>(packed));
   return f(static_cast<const TS*>(w));
@@ -1025,13 +1186,13 @@ template <typename TS>
 bool qkv_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, hipStream_t s) {
   const int M = (a.n_q + 2 * a.n_kv) * a.head_dim;
   const int grid = blocks_for(M, sh.rows_qkv, sh.grid_qkv);
-  return with_w<TS>(L.wqkv, L.wqkv_p, [&](auto W) {
-    return with_k<TS>(a.hidden, [&](auto kc) {
+  return with_w<TS>(a.wfmt, L.wqkv, L.wqkv_p, [&](auto W) {
+    return with_k<pointee_t<decltype(W)>>(a.hidden, [&](auto kc) {
       return with_r(sh.rows_qkv, [&](auto rc) {
         return with_t(sh.tokens, [&](auto tc) {
           hipLaunchKernelGGL((k_qkv<TS, pointee_t<decltype(W)>, decltype(kc)::value, decltype(rc)::value,
                                     decltype(tc)::value>),
-                             dim3(grid), dim3(kBlock), 0, s, W, (const TS*)L.in_norm, (TS*)a.x, (const TS*)a.embed,
+                             dim3(grid), dim3(kBlock), 0, s, W, (const TS*)L.in_norm, (TS*)a.x, a.embed,
                              a.ids, a.ctrl, a.rope_cos, a.rope_sin, a.rope_cur, first ? 1 : 0, a.vocab, a.eps,
                              (TS*)a.qkv, M);
           return true;
@@ -1045,8 +1206,8 @@ template <typename TS>
 bool residual_t(const DecodeArgs& a, int T, int K, int R, int grid_req, const void* W, const void* Wp,
                 const void* in, const void* x_in, void* x_out, bool adv, hipStream_t s) {
   const int grid = blocks_for(a.hidden, R, grid_req);
-  return with_w<TS>(W, Wp, [&](auto Wt) {
-    return with_k<TS>(K, [&](auto kc) {
+  return with_w<TS>(a.wfmt, W, Wp, [&](auto Wt) {
+    return with_k<pointee_t<decltype(Wt)>>(K, [&](auto kc) {
       return with_r(R, [&](auto rc) {
         return with_t(T, [&](auto tc) {
           hipLaunchKernelGGL((k_gemv_residual<TS, pointee_t<decltype(Wt)>, decltype(kc)::value, decltype(rc)::value,
@@ -1074,9 +1235,9 @@ bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bo
   const int grid = blocks_for(a.inter, sh.rows_gu, sh.grid_gu);
   const int np = from_parts ? parts_slots(a.hidden, a.n_kv, sh.tokens) : 0;
   if (from_parts && np == 0) return false;
-  return with_w<TS>(L.wgu, L.wgu_p, [&](auto W) {
+  return with_w<TS>(a.wfmt, L.wgu, L.wgu_p, [&](auto W) {
     using TW = pointee_t<decltype(W)>;
-    return with_k<TS>(a.hidden, [&](auto kc) {
+    return with_k<TW>(a.hidden, [&](auto kc) {
       return with_r(sh.rows_gu, [&](auto rc) {
         return with_t(sh.tokens, [&](auto tc) {
           constexpr int K = decltype(kc)::value, R = decltype(rc)::value, T = decltype(tc)::value;
@@ -1107,9 +1268,9 @@ bool gateup_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bo
 template <typename TS>
 bool head_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   const int grid = head_grid(a.vocab, sh.rows_head, sh.head_waves, sh.grid_head);
-  return with_w<TS>(a.embed, a.embed_p, [&](auto E) {
+  return with_w<TS>(a.wfmt, a.embed, a.embed_p, [&](auto E) {
     using TW = pointee_t<decltype(E)>;
-    return with_k<TS>(a.hidden, [&](auto kc) {
+    return with_k<TW>(a.hidden, [&](auto kc) {
       return with_r(sh.rows_head, [&](auto rc) {
         return with_t(sh.tokens, [&](auto tc) {
           constexpr int K = decltype(kc)::value, R = decltype(rc)::value, T = decltype(tc)::value;
@@ -1170,7 +1331,7 @@ bool attn_merge_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
 template <typename TS>
 bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
-  return with_w<TS>(L.wo, L.wo_p, [&](auto Wo) {
+  return with_w<TS, false>(a.wfmt, L.wo, L.wo_p, [&](auto Wo) {
     using TW = pointee_t<decltype(Wo)>;
     // row t's partials start at opart[t * slots * H], as the gate/up
     // prologue reads them

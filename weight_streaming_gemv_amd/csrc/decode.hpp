@@ -43,8 +43,13 @@ struct LayerPtrs {
   const void* wd_p = nullptr;
 };
 
+// Weight formats of the decode matrices.
+constexpr int kWeightsDense = 0;   // the storage dtype (plus lossless packed copies)
+constexpr int kWeightsQ4 = 1;      // int4 group-64 rows (FP16 models): words then FP16 scales per row
+
 struct DecodeArgs {
   int dtype;            // 0 FP32, 1 FP16 storage
+  int wfmt = kWeightsDense;   // weight format of every decode matrix and the embedding
   int hidden, inter, n_q, n_kv, head_dim, vocab, cap;
   float eps;
   const void* embed;    // [V][H]

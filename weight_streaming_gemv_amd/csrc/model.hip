@@ -31,6 +31,7 @@ struct Dims {
   int L, H, I, nq, nkv, D, V, cap, chunk, Q, KV, G;
   size_t es;   // storage element bytes
   bool pack;   // lossless packed copies of the decode matrices
+  bool q4;     // int4 group-64 decode matrices
 };
 
 Dims dims_of(const wsg_config& c) {
@@ -40,8 +41,12 @@ Dims dims_of(const wsg_config& c) {
   d.Q = d.nq * d.D; d.KV = d.nkv * d.D; d.G = d.nkv > 0 ? d.nq / d.nkv : 0;
   d.es = c.dtype == WSG_F16 ? 2 : 4;
   d.pack = c.lossless_pack != 0;
+  d.q4 = c.weight_format == WSG_W_Q4G64;
   return d;
 }
+
+// Bytes of one packed int4 row of width k: k/8 words, then k/64 FP16 scales.
+size_t q4_row_bytes(int k) { return (size_t)k / 2 + (size_t)k / 32; }
 
 bool dim_ok(int v, int dtype) {
   if (dtype == WSG_F32 && v == 256) return true;
@@ -69,6 +74,14 @@ wsg_status validate_config(const wsg_config* c) {
     return fail(WSG_ERR_UNSUPPORTED, "lossless packing applies to FP32 models");
   if (c->prefill_chunk > 0 && (c->dtype != WSG_F32 || G > 2))
     return fail(WSG_ERR_UNSUPPORTED, "chunked prefill needs FP32 storage and a query group of 1 or 2");
+  if (c->weight_format != WSG_W_DENSE && c->weight_format != WSG_W_Q4G64)
+    return fail(WSG_ERR_INVALID_ARG, "weight_format %d", c->weight_format);
+  if (c->weight_format == WSG_W_Q4G64) {
+    if (c->dtype != WSG_F16) return fail(WSG_ERR_UNSUPPORTED, "int4 weights need FP16 storage");
+    if (c->hidden % 1024 || c->intermediate % 1024 || (c->n_q_heads * c->head_dim) % 1024)
+      return fail(WSG_ERR_UNSUPPORTED, "int4 weights need hidden, intermediate and query widths that are multiples of 1024");
+    if (c->lossless_pack) return fail(WSG_ERR_UNSUPPORTED, "lossless packing applies to dense FP32 models");
+  }
   return WSG_OK;
 }
 
@@ -94,7 +107,9 @@ PackedLayout packed_layout(const Dims& d) {
   size_t off = 0;
   auto take = [&](size_t elems) { const size_t o = off; off = align256(off + elems * d.es); return o; };
   auto take_bytes = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
-  p.embed = take((size_t)d.V * d.H);
+  // a decode matrix [rows][k]: dense elements or int4 rows
+  auto take_mat = [&](size_t rows, int k) { return d.q4 ? take_bytes(rows * q4_row_bytes(k)) : take(rows * k); };
+  p.embed = take_mat(d.V, d.H);
   p.final_norm = take(d.H);
   for (int l = 0; l < d.L; ++l) {
     LayerOff lo;
@@ -102,10 +117,10 @@ PackedLayout packed_layout(const Dims& d) {
     lo.post_norm = take(d.H);
     lo.q_norm = take(d.D);
     lo.k_norm = take(d.D);
-    lo.wqkv = take((size_t)(d.Q + 2 * d.KV) * d.H);
-    lo.wo = take((size_t)d.H * d.Q);
-    lo.wgu = take((size_t)2 * d.I * d.H);
-    lo.wd = take((size_t)d.H * d.I);
+    lo.wqkv = take_mat(d.Q + 2 * d.KV, d.H);
+    lo.wo = take_mat(d.H, d.Q);
+    lo.wgu = take_mat(2 * d.I, d.H);
+    lo.wd = take_mat(d.H, d.I);
     p.layers.push_back(lo);
   }
   if (d.pack) {
@@ -238,13 +253,17 @@ namespace {
 int64_t stage_bytes(const wsg_model* m, int stage, int l) {
   const Dims& d = m->d;
   const LayerPtrs* L = l >= 0 && l < (int)m->layers.size() ? &m->layers[l] : nullptr;
-  auto b = [&](int64_t elems, const void* packed) { return packed ? elems * 2 : elems * (int64_t)d.es; };
+  // [rows][k]: int4 rows, the packed copy, or dense elements
+  auto b = [&](int64_t rows, int k, const void* packed) {
+    if (d.q4) return rows * (int64_t)q4_row_bytes(k);
+    return packed ? rows * k * 2 : rows * k * (int64_t)d.es;
+  };
   switch (stage) {
-    case WSG_STAGE_QKV: return b((int64_t)(d.Q + 2 * d.KV) * d.H, L ? L->wqkv_p : nullptr);
-    case WSG_STAGE_O: return b((int64_t)d.H * d.Q, L ? L->wo_p : nullptr);
-    case WSG_STAGE_GATEUP: return b((int64_t)2 * d.I * d.H, L ? L->wgu_p : nullptr);
-    case WSG_STAGE_DOWN: return b((int64_t)d.H * d.I, L ? L->wd_p : nullptr);
-    case WSG_STAGE_HEAD: return b((int64_t)d.V * d.H, m->args.embed_p);
+    case WSG_STAGE_QKV: return b(d.Q + 2 * d.KV, d.H, L ? L->wqkv_p : nullptr);
+    case WSG_STAGE_O: return b(d.H, d.Q, L ? L->wo_p : nullptr);
+    case WSG_STAGE_GATEUP: return b(2 * d.I, d.H, L ? L->wgu_p : nullptr);
+    case WSG_STAGE_DOWN: return b(d.H, d.I, L ? L->wd_p : nullptr);
+    case WSG_STAGE_HEAD: return b(d.V, d.H, m->args.embed_p);
     default: return 0;
   }
 }
@@ -329,7 +348,8 @@ bool enqueue_argmax(wsg_model* m, int tokens) { return launch_argmax(m->args, sh
 constexpr int kFuseMaxKeys = 128;
 
 bool use_fused_attn_o(const wsg_model* m, int n_keys, int tokens) {
-  return shape_for(m, tokens).fuse_attn_o && n_keys <= kFuseMaxKeys &&
+  // (int4 models run the separate attention and output-projection launches)
+  return !m->d.q4 && shape_for(m, tokens).fuse_attn_o && n_keys <= kFuseMaxKeys &&
          attn_o_part_slots(m->d.H, m->d.nkv, tokens) > 0;
 }
 
@@ -488,6 +508,8 @@ wsg_status wsg_pack_weights(const wsg_config* cfg, const wsg_host_weights* w, vo
   wsg_status st = validate_config(cfg);
   if (st != WSG_OK) return st;
   if (!w || !host_out) return fail(WSG_ERR_INVALID_ARG, "weights or output is NULL");
+  if (cfg->weight_format != WSG_W_DENSE)
+    return fail(WSG_ERR_INVALID_ARG, "int4 models are packed by wsg_pack_weights_q4");
   const Dims d = dims_of(*cfg);
   const PackedLayout p = packed_layout(d);
   if (out_bytes < p.total) return fail(WSG_ERR_INVALID_ARG, "output has %zu bytes, need %zu", out_bytes, p.total);
@@ -542,6 +564,57 @@ wsg_status wsg_pack_weights(const wsg_config* cfg, const wsg_host_weights* w, vo
   return WSG_OK;
 }
 
+wsg_status wsg_pack_weights_q4(const wsg_config* cfg, const wsg_host_weights* norms, const wsg_host_q4_weights* q,
+                               void* host_out, size_t out_bytes) {
+  clear_error();
+  wsg_status st = validate_config(cfg);
+  if (st != WSG_OK) return st;
+  if (cfg->weight_format != WSG_W_Q4G64) return fail(WSG_ERR_INVALID_ARG, "config is not an int4 model");
+  if (!norms || !q || !host_out) return fail(WSG_ERR_INVALID_ARG, "weights or output is NULL");
+  const Dims d = dims_of(*cfg);
+  const PackedLayout p = packed_layout(d);
+  if (out_bytes < p.total) return fail(WSG_ERR_INVALID_ARG, "output has %zu bytes, need %zu", out_bytes, p.total);
+  if (!norms->final_norm || !norms->in_norm || !norms->post_norm || !norms->q_norm || !norms->k_norm)
+    return fail(WSG_ERR_INVALID_ARG, "a norm gain pointer is NULL");
+  if (!q->embed.words || !q->embed.scales || !q->wq || !q->wk || !q->wv || !q->wo || !q->wg || !q->wu || !q->wd)
+    return fail(WSG_ERR_INVALID_ARG, "an int4 matrix pointer is NULL");
+  for (int l = 0; l < d.L; ++l) {
+    if (!norms->in_norm[l] || !norms->post_norm[l] || !norms->q_norm[l] || !norms->k_norm[l])
+      return fail(WSG_ERR_INVALID_ARG, "layer %d has a NULL norm gain pointer", l);
+    for (const wsg_q4_matrix* mt : {&q->wq[l], &q->wk[l], &q->wv[l], &q->wo[l], &q->wg[l], &q->wu[l], &q->wd[l]})
+      if (!mt->words || !mt->scales) return fail(WSG_ERR_INVALID_ARG, "layer %d has a NULL int4 matrix pointer", l);
+  }
+  uint8_t* out = static_cast<uint8_t*>(host_out);
+  memset(out, 0, p.total);
+  auto put = [&](size_t off, const void* src, size_t elems) { memcpy(out + off, src, elems * d.es); };
+  // rows [row0, row0 + rows) of a packed int4 matrix of width k from m
+  auto put_q4 = [&](size_t off, size_t row0, const wsg_q4_matrix& mt, size_t rows, int k) {
+    const size_t rb = q4_row_bytes(k);
+    for (size_t r = 0; r < rows; ++r) {
+      uint8_t* dst = out + off + (row0 + r) * rb;
+      memcpy(dst, mt.words + r * (k / 8), (size_t)k / 2);
+      memcpy(dst + k / 2, mt.scales + r * (k / 64), (size_t)k / 32);
+    }
+  };
+  put_q4(p.embed, 0, q->embed, d.V, d.H);
+  put(p.final_norm, norms->final_norm, d.H);
+  for (int l = 0; l < d.L; ++l) {
+    const LayerOff& lo = p.layers[l];
+    put(lo.in_norm, norms->in_norm[l], d.H);
+    put(lo.post_norm, norms->post_norm[l], d.H);
+    put(lo.q_norm, norms->q_norm[l], d.D);
+    put(lo.k_norm, norms->k_norm[l], d.D);
+    put_q4(lo.wqkv, 0, q->wq[l], d.Q, d.H);
+    put_q4(lo.wqkv, d.Q, q->wk[l], d.KV, d.H);
+    put_q4(lo.wqkv, d.Q + d.KV, q->wv[l], d.KV, d.H);
+    put_q4(lo.wo, 0, q->wo[l], d.H, d.Q);
+    put_q4(lo.wgu, 0, q->wg[l], d.I, d.H);
+    put_q4(lo.wgu, d.I, q->wu[l], d.I, d.H);
+    put_q4(lo.wd, 0, q->wd[l], d.H, d.I);
+  }
+  return WSG_OK;
+}
+
 wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t packed_bytes, void* d_workspace,
                             size_t ws_bytes, void* hip_stream, wsg_model** out) {
   clear_error();
@@ -581,6 +654,7 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
 
   DecodeArgs& a = m->args;
   a.dtype = cfg->dtype;
+  a.wfmt = d.q4 ? kWeightsQ4 : kWeightsDense;
   a.hidden = d.H; a.inter = d.I; a.n_q = d.nq; a.n_kv = d.nkv; a.head_dim = d.D; a.vocab = d.V; a.cap = d.cap;
   a.eps = cfg->rms_eps;
   a.embed = m->packed + pl.embed;
