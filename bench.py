@@ -525,6 +525,91 @@ def two_token(torch, wsg, shape, w, context=16, trials=9, reps=50, n_prompt=32, 
     return res
 
 
+def int4_decoder(torch, wsg, shape, steps=5, warmup=2, n_check=8):
+    """The short-prompt workload on an int4 model of the same shape: every decode matrix
+    and the tied embedding int4 in groups of 64 with FP16 scales (the int4 GEMV workload's
+    distributions: q uniform in [-8, 7], scales |N(0, 0.01)|), FP16 activations, KV cache
+    and logits, FP32 accumulation ("Our Kernel Benchmark Was Measuring the System Cache",
+    "Summary": 4-bit decode).  Validated first against the oracle, which dequantises the
+    same words on the CPU: teacher-forced (both sides consume the oracle's tokens), every
+    logit and new K/V slot within the FP16 tolerance rtol=atol=2e-2; the share of greedy
+    tokens that agree is reported.  Prompts run tokenwise (no chunked prefill for int4).
+    HIP events time the int4 head launches."""
+    import oracle
+    from synth import PROMPT_SEEDS, model_weights_q4, prompt_ids
+    t = time.perf_counter()
+    w = model_weights_q4(shape, seed=0)
+    log(f"int4 weights generated in {time.perf_counter() - t:.1f} s")
+    cap = 48
+    model = wsg.Model(shape, w, max_context=cap, dtype=wsg.WSG_F16)
+    orc = oracle.OracleModel(shape, w, cap)
+    del w
+    prompt32 = prompt_ids(PROMPT_SEEDS["short"], 32, shape.vocab)
+    prompts = {8: prompt32[:8], 32: prompt32}
+    tol = 2e-2
+
+    def cmp(got, ref_, what):
+        g = got.float().cpu().numpy().astype(np.float64)
+        r = np.asarray(ref_, dtype=np.float64)
+        err = np.abs(g - r)
+        if not np.all(err <= tol + tol * np.abs(r)):
+            raise RuntimeError(f"int4 validation failed: {what} off by {err.max():.3e}")
+        return float(err.max())
+
+    max_l = max_kv = 0.0
+    agree = total = 0
+    tok = model.prefill(prompts[8])
+    ref = orc.forward_rows(prompts[8])
+    max_l = max(max_l, cmp(model.logits(), ref, "prefill logits"))
+    for s in range(n_check):
+        rtok = oracle.argmax_lowest(ref)
+        agree += int(tok == rtok)
+        total += 1
+        p = orc.pos
+        tok = model.step(rtok)
+        ref = orc.forward_rows([rtok])
+        max_l = max(max_l, cmp(model.logits(), ref, f"logits step {s}"))
+        for l in range(shape.n_layers):
+            k, v, _ = model.kv(l)
+            max_kv = max(max_kv, cmp(k[:, p:p + 1], orc.k_cache[l][:, p:p + 1], f"K layer {l}"),
+                         cmp(v[:, p:p + 1], orc.v_cache[l][:, p:p + 1], f"V layer {l}"))
+    n = orc.pos
+    for l in range(shape.n_layers):
+        k, v, _ = model.kv(l)
+        max_kv = max(max_kv, cmp(k[:, :n], orc.k_cache[l][:, :n], f"K prefix {l}"),
+                     cmp(v[:, :n], orc.v_cache[l][:, :n], f"V prefix {l}"))
+    del orc
+    # timed generations (tokens must repeat exactly run to run)
+    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, STAGES["head"])
+    expected, rec = {}, []
+    for i in range(warmup + steps):
+        if i == warmup:
+            model.stage_time()
+        for (n_p, n_o) in COMBOS:
+            toks, ttft, dec, tot = generate(model, prompts[n_p], n_o)
+            if expected.setdefault((n_p, n_o), toks) != toks:
+                raise RuntimeError(f"int4 generation {n_p}/{n_o} not repeatable")
+            if i >= warmup:
+                rec.append((n_p, n_o, ttft, dec))
+    ms, nl, by = model.stage_time()
+    st = model.storage()
+    model.close()
+    value = sum(n_o - 1 for _, n_o, _, _ in rec) / sum(r[3] for r in rec)
+    head_us = ms / max(nl, 1) * 1e3
+    return {"decode_tok_s": round(value, 2),
+            "decode_weight_bytes": st["decode_weight_bytes"],
+            "decode_weight_gbps": round(st["decode_weight_bytes"] * value / 1e9, 1),
+            "ttft_ms_median": {str(n_p): round(statistics.median(r[2] for r in rec if r[0] == n_p) * 1e3, 3)
+                               for n_p in (8, 32)},
+            "head": {"us": round(head_us, 2), "bytes_per_launch": by // max(nl, 1),
+                     "gbps": round(by / max(nl, 1) / (head_us * 1e-6) / 1e9, 1) if nl else None},
+            "validation": {"max_abs_logit_err": max_l, "max_abs_kv_err": max_kv, "rtol": tol, "atol": tol,
+                           "teacher_forced_steps": n_check, "greedy_token_agreement": f"{agree}/{total}"},
+            "workload": ("28-layer Qwen3-0.6B-shaped decoder, int4 group-64 weights with FP16 scales for every "
+                         "decode matrix and the tied embedding, FP16 activations/KV/logits; prompt/output 8/8, "
+                         "8/16, 32/8, 32/16, tokenwise prompt")}
+
+
 def long_context(torch, wsg, shape, w, validate_outputs=32, trials=5, warmup=2):
     """Long-document workload (Benchmark methodology, "Long-document chunked prefill").
 
@@ -697,6 +782,8 @@ def main(argv=None):
                     help="short-prompt workload on BF16-representable weights, packed vs unpacked decode")
     ap.add_argument("--two-token", choices=["on", "off", "only"], default="on",
                     help="two-token step (speculative verify pass): fixed-slot latency and generation")
+    ap.add_argument("--int4", choices=["on", "off", "only"], default="on",
+                    help="short-prompt workload on an int4 (group-64) model of the same shape")
     ap.add_argument("--no-oracle", action="store_true",
                     help="skip validation and the CPU baseline (profiling runs only; no value is published)")
     args = ap.parse_args(argv)
@@ -764,6 +851,11 @@ def main(argv=None):
 
     if args.lossless == "only":
         print(json.dumps({"lossless_bf16": lossless_bf16(torch, wsg, shape)}), flush=True)
+        return 0
+    if args.int4 == "only":
+        del w, model
+        torch.cuda.empty_cache()
+        print(json.dumps({"int4_decoder": int4_decoder(torch, wsg, shape)}), flush=True)
         return 0
     fixed_res = None
     if args.fixed != "off" and not args.no_oracle:
@@ -864,6 +956,11 @@ def main(argv=None):
         t = time.perf_counter()
         out["lossless_bf16"] = lossless_bf16(torch, wsg, shape)
         log(f"lossless BF16-in-FP32 section in {time.perf_counter() - t:.1f} s")
+        torch.cuda.empty_cache()
+    if args.int4 == "on" and not args.no_oracle:
+        t = time.perf_counter()
+        out["int4_decoder"] = int4_decoder(torch, wsg, shape)
+        log(f"int4 decoder section in {time.perf_counter() - t:.1f} s")
         torch.cuda.empty_cache()
     if args.sweep != "none":
         sw = gemv_sweep(quick=args.sweep == "quick")

@@ -118,6 +118,34 @@ def test_q4_two_token_step(q4mini_w):
     m.close()
 
 
+Q4_VARIANTS = {
+    "g1_h1024": ModelShape(n_layers=2, hidden=1024, intermediate=1024, n_q_heads=8, n_kv_heads=8, head_dim=128,
+                           vocab=700),
+    "g4_h2048": ModelShape(n_layers=1, hidden=2048, intermediate=3072, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                           vocab=900),
+}
+
+
+@pytest.mark.parametrize("name", sorted(Q4_VARIANTS))
+@pytest.mark.parametrize("fuse,rows", [(1, 8), (1, 4), (0, 8)])
+def test_q4_variants_fused_and_split(name, fuse, rows):
+    """Query groups 1 and 4 with the fused attention + int4 output slice (8 or 4 rows
+    per wave; group 1 with 4 rows runs the separate launches) and without it; a
+    140-id prompt passes the fused limit of 128 keys."""
+    import weight_streaming_gemv_amd as wsg
+    sh = Q4_VARIANTS[name]
+    w = model_weights_q4(sh, seed=7)
+    cap = 160
+    m = _model(wsg, sh, w, cap)
+    m.set_option(wsg._abi.WSG_OPT_FUSE_ATTN_O, fuse)
+    m.set_option(wsg._abi.WSG_OPT_ROWS_ATTN_O, rows)
+    orc = oracle.OracleModel(sh, w, cap)
+    for n_p in (20, 140):
+        _, _, ck = lockstep(m, orc, prompt_ids(54 + n_p, n_p, sh.vocab), 6, rtol=TOL, atol=TOL, teacher=True,
+                            label=f"q4 {name} fuse={fuse} rows={rows} n={n_p}")
+    m.close()
+
+
 def test_q4_config_errors(q4mini_w):
     import weight_streaming_gemv_amd as wsg
     with pytest.raises(wsg.WsgError, match="UNSUPPORTED"):

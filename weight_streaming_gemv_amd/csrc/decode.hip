@@ -1010,6 +1010,71 @@ struct WoSlice {
   }
 };
 
+// Sum over each half-row of 8 lanes (every lane of the half-row gets it).
+__device__ __forceinline__ float row8_sum(float v) {
+  v += dpp<kDppQuadSwap1>(v);
+  v += dpp<kDppQuadSwap2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v;
+}
+
+// The int4 W_o slice: each lane holds 16 consecutive columns (two words and
+// their group's scale) of one row; LPR lanes cover a row's G*128 columns.
+// The attention output arrives as FP16 pairs in LDS, ordered as the nibble
+// pairs of q4_pairs meet them (8 pairs per 16-column lane chunk).
+template <int G, int R>
+struct WoSlice<q4w, G, R> {
+  static constexpr int LPR = G * kD / 16;           // lanes per row slice: 8, 16 or 32
+  static constexpr int NLD = R * LPR / kWave;       // 8-byte loads per lane
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row slice of 8, 16 or 32 lanes");
+  static_assert((R * LPR) % kWave == 0, "whole loads per lane");
+  typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+  u2_t q[NLD];
+  uint16_t s[NLD];
+
+  __device__ __forceinline__ void load(const q4w* __restrict__ Wo, int ld, int col0, int row0, int M) {
+    const int lane = lane_id();
+    const size_t rb = (size_t)ld / 2 + (size_t)ld / 32;   // int4 row bytes of width ld
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      const int f = t * kWave + lane;
+      const uint8_t* rp = reinterpret_cast<const uint8_t*>(Wo) + (size_t)min(row0 + f / LPR, M - 1) * rb;
+      const int k = col0 + (f % LPR) * 16;
+      q[t] = *reinterpret_cast<const u2_t*>(rp + k / 2);
+      s[t] = *reinterpret_cast<const uint16_t*>(rp + ld / 2 + 2 * (k / 64));
+    }
+  }
+  // out[row0 + r] = (this slice's row r) . o + lane r's xb
+  __device__ __forceinline__ void apply(const uint32_t* oh, int row0, int M, float xb, float* __restrict__ out) const {
+    const int lane = lane_id();
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      const int f = t * kWave + lane;
+      const uint4 a = *reinterpret_cast<const uint4*>(oh + (f % LPR) * 8);
+      const uint4 b = *reinterpret_cast<const uint4*>(oh + (f % LPR) * 8 + 4);
+      h2_t p[4];
+      float in = 0.f;
+      q4_pairs(q[t].x, p);
+      in = dot2(p[0], as_h2(a.x), in);
+      in = dot2(p[1], as_h2(a.y), in);
+      in = dot2(p[2], as_h2(a.z), in);
+      in = dot2(p[3], as_h2(a.w), in);
+      q4_pairs(q[t].y, p);
+      in = dot2(p[0], as_h2(b.x), in);
+      in = dot2(p[1], as_h2(b.y), in);
+      in = dot2(p[2], as_h2(b.z), in);
+      in = dot2(p[3], as_h2(b.w), in);
+      float v = __half2float(__ushort_as_half(s[t])) * in;
+      if constexpr (LPR == 8) v = row8_sum(v);
+      else v = row16_sum(v);
+      if constexpr (LPR == 32) v += __shfl_xor(v, 16);
+      const int m = row0 + f / LPR;
+      const float xv = __shfl(xb, f / LPR);
+      if (f % LPR == 0 && m < M) out[m] = v + xv;
+    }
+  }
+};
+
 template <typename TS, typename TW, int G, int R, int T>
 __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
                                                    TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
@@ -1060,8 +1125,24 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
     s_o[r][f] = Store<TS>::to_f(Store<TS>::from_f(A / L));   // o rounded as stored
   }
   __syncthreads();
+  if constexpr (std::is_same<TW, q4w>::value) {
+    // o as FP16 pairs in the int4 slice's order (exact: o is FP16-rounded)
+    __shared__ uint32_t s_oh[T][G * kD / 2];
+    for (int e = threadIdx.x; e < T * G * kD / 2; e += kBlock) {
+      const int r = e / (G * kD / 2), f = e - r * (G * kD / 2);
+      const int c = (f / 8) * 16 + 8 * ((f % 8) / 4) + (f % 4);   // chunk, word, pair
+      h2_t h;
+      h.x = (_Float16)s_o[r][c];
+      h.y = (_Float16)s_o[r][c + 4];
+      s_oh[r][f] = __builtin_bit_cast(uint32_t, h);
+    }
+    __syncthreads();
 #pragma unroll
-  for (int r = 0; r < T; ++r) w.apply(s_o[r], row0, H, xb[r], opart + (size_t)r * part_row + (size_t)j * H);
+    for (int r = 0; r < T; ++r) w.apply(s_oh[r], row0, H, xb[r], opart + (size_t)r * part_row + (size_t)j * H);
+  } else {
+#pragma unroll
+    for (int r = 0; r < T; ++r) w.apply(s_o[r], row0, H, xb[r], opart + (size_t)r * part_row + (size_t)j * H);
+  }
 }
 
 // Merge of the split-K partial states of one query head of row t (one
@@ -1331,22 +1412,27 @@ bool attn_merge_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
 template <typename TS>
 bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
-  return with_w<TS, false>(a.wfmt, L.wo, L.wo_p, [&](auto Wo) {
+  return with_w<TS>(a.wfmt, L.wo, L.wo_p, [&](auto Wo) {
     using TW = pointee_t<decltype(Wo)>;
     // row t's partials start at opart[t * slots * H], as the gate/up
     // prologue reads them
     const int part_row = parts_slots(a.hidden, a.n_kv, sh.tokens) * a.hidden;
     if (part_row == 0) return false;
     auto go = [&](auto gc, auto rc) {
-      constexpr int R = decltype(rc)::value;
-      const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R), a.n_kv);
-      return with_t(sh.tokens, [&](auto tc) {
-        hipLaunchKernelGGL((k_attn_o<TS, TW, decltype(gc)::value, R, decltype(tc)::value>), grid, dim3(kBlock), 0, s,
-                           (const TS*)a.qkv, (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm,
-                           (const TS*)L.k_norm, a.rope_cur, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, Wo, (const TS*)a.x,
-                           a.hidden, a.opart, part_row);
-        return true;
-      });
+      constexpr int R = decltype(rc)::value, GG = decltype(gc)::value;
+      // an int4 slice needs whole 8-byte loads per lane (not G = 1 with 4 rows)
+      if constexpr (std::is_same<TW, q4w>::value && (R * GG * kD / 16) % kWave != 0) {
+        return false;
+      } else {
+        const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R), a.n_kv);
+        return with_t(sh.tokens, [&](auto tc) {
+          hipLaunchKernelGGL((k_attn_o<TS, TW, GG, R, decltype(tc)::value>), grid, dim3(kBlock), 0, s,
+                             (const TS*)a.qkv, (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm,
+                             (const TS*)L.k_norm, a.rope_cur, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, Wo,
+                             (const TS*)a.x, a.hidden, a.opart, part_row);
+          return true;
+        });
+      }
     };
     auto with_g = [&](auto rc) {
       switch (G) {

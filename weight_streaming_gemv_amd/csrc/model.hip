@@ -348,8 +348,10 @@ bool enqueue_argmax(wsg_model* m, int tokens) { return launch_argmax(m->args, sh
 constexpr int kFuseMaxKeys = 128;
 
 bool use_fused_attn_o(const wsg_model* m, int n_keys, int tokens) {
-  // (int4 models run the separate attention and output-projection launches)
-  return !m->d.q4 && shape_for(m, tokens).fuse_attn_o && n_keys <= kFuseMaxKeys &&
+  const DecodeShape sh = shape_for(m, tokens);
+  // an int4 W_o slice of one KV head with 4 rows per wave leaves partial loads
+  if (m->d.q4 && m->d.G == 1 && sh.rows_attn_o == 4) return false;
+  return sh.fuse_attn_o && n_keys <= kFuseMaxKeys &&
          attn_o_part_slots(m->d.H, m->d.nkv, tokens) > 0;
 }
 
@@ -723,6 +725,20 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   // argmax would reduce four times as many block keys.
   m->shape2 = sh;
   m->shape2.rows_head = 4;
+  if (d.q4) {
+    // int4 rows are short (544 bytes at width 1024): the head loops over
+    // four rows per wave on 2048 blocks, so each wave's activation and norm
+    // prologue serves many rows (the one-shot grid reads more activation
+    // bytes from L2 than weight bytes from HBM)
+    for (DecodeShape* s : {&m->shape, &m->shape2}) {
+      s->rows_head = 4;
+      s->grid_head = 2048;
+      // likewise fewer, longer waves for gate/up (whose prologue sums the
+      // attention partials) and QKV (kernel-trace sweep of rows and grids)
+      s->rows_gu = 4;
+      s->rows_qkv = 2;
+    }
+  }
 
   std::vector<float> cs, sn;
   fill_rope(*cfg, cs, sn);
