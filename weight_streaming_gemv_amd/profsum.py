@@ -2,6 +2,9 @@
 
 ``python -m weight_streaming_gemv_amd.profsum decode <run_kernel_trace.csv>``
     per-kernel median durations of a decode run and the per-token sum;
+``python -m weight_streaming_gemv_amd.profsum instances <run_kernel_trace.csv>``
+    the same per template instance (row count, weight storage and launch
+    shape are template arguments), with workgroups per launch;
 ``python -m weight_streaming_gemv_amd.profsum sweep <run_kernel_trace.csv>``
     kernel-only GB/s of every cold-sweep configuration (bench.py --sweep-only),
     matched to its launch by kernel template arguments and grid size.
@@ -47,6 +50,19 @@ def decode_table(path):
     for s, n, ds in rows:
         print(f"| {n} | {len(ds)} | {statistics.median(ds) / 1e3:.2f} | {statistics.fmean(ds) / 1e3:.2f} | "
               f"{s / 1e6:.2f} | {100 * s / tot:.1f}% |")
+
+
+def instance_table(path):
+    g = load(path)
+    by_inst = defaultdict(list)
+    for (name, blocks, gy), ds in g.items():
+        by_inst[(short(name), blocks * gy)].extend(ds)
+    rows = sorted(((sum(ds), k, ds) for k, ds in by_inst.items()), reverse=True)
+    print("| kernel instance | workgroups | calls | median us | mean us | total ms |")
+    print("|---|---|---|---|---|---|")
+    for s, (n, wg), ds in rows:
+        print(f"| `{n}` | {wg} | {len(ds)} | {statistics.median(ds) / 1e3:.2f} | "
+              f"{statistics.fmean(ds) / 1e3:.2f} | {s / 1e6:.2f} |")
 
 
 def _ceil(a, b):
@@ -108,4 +124,4 @@ if __name__ == "__main__":
     import os
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     mode, path = sys.argv[1], sys.argv[2]
-    {"decode": decode_table, "sweep": sweep_table}[mode](path)
+    {"decode": decode_table, "instances": instance_table, "sweep": sweep_table}[mode](path)
