@@ -45,6 +45,8 @@ typedef float f4v_t __attribute__((ext_vector_type(4)));
 // C[M x N] (+)= A[M x K] . B[N x K]^T, all row-major FP32, K-contiguous
 // operands.  Block tile BM x BN x 32, 256 threads = 2 x 2 waves, each wave a
 // (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA tiles (v_mfma_f32_32x32x2f32).
+// Split K: block z covers k in [z*kspan, (z+1)*kspan) and writes its own
+// slice C + z*c_split (kspan = K, one slice, when K is not split).
 //
 // MFMA 32x32x2 operand layout (lane l): A element (row l%32, k l/32),
 // B element (k l/32, col l%32); accumulator register r holds row
@@ -57,7 +59,8 @@ constexpr int kLdsRow = kBK + kLdsPad;
 
 template <int BM, int BN, bool ACC>
 __global__ __launch_bounds__(256) void k_gemm_nt(const float* __restrict__ A, const float* __restrict__ B,
-                                                 float* __restrict__ C, int M, int N, int K) {
+                                                 float* __restrict__ C, int M, int N, int K, int kspan,
+                                                 size_t c_split) {
   constexpr int WM = BM / 2, WN = BN / 2;     // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;   // MFMA tiles per wave
   constexpr int A_LOADS = BM * kBK / 4 / 256; // float4 per thread per tile
@@ -70,6 +73,9 @@ __global__ __launch_bounds__(256) void k_gemm_nt(const float* __restrict__ A, co
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int li = lane & 31, lh = lane >> 5;
+  A += (size_t)blockIdx.z * kspan;   // this split's K range (row stride stays K)
+  B += (size_t)blockIdx.z * kspan;
+  C += blockIdx.z * c_split;
 
   f16v_t acc[TM][TN];
 #pragma unroll
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(256) void k_gemm_nt(const float* __restrict__ A, co
   }
 
   WSG_GEMM_LOAD(0)
-  for (int k0 = 0; k0 < K; k0 += kBK) {
+  for (int k0 = 0; k0 < kspan; k0 += kBK) {
     __syncthreads();          // previous tile fully consumed
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256) void k_gemm_nt(const float* __restrict__ A, co
     __syncthreads();
     // next tile in flight during the MFMAs (the last iteration reloads the
     // final tile, in bounds and unused, to keep the loop free of branches)
-    WSG_GEMM_LOAD(min(k0 + kBK, K - kBK))
+    WSG_GEMM_LOAD(min(k0 + kBK, kspan - kBK))
 #undef WSG_GEMM_LOAD
     float af[TM][16], bf[TN][16];
 #pragma unroll
@@ -364,8 +370,11 @@ __global__ __launch_bounds__(256) void k_rows_swiglu(const float* __restrict__ G
 //
 // Both products run on v_mfma_f32_16x16x4f32, in transposed form so the
 // probabilities never leave registers.  A block holds 64 query vectors
-// (64/G rows x G heads); wave w owns vectors [16w, 16w + 16), vector v =
-// row * G + head.  Per tile of 32 keys (K row-major and V transposed in LDS):
+// (64/G rows x G heads) and 8 waves in two groups of four: wave w of group
+// c owns vectors [16w, 16w + 16) (vector v = row * G + head) and the key
+// tiles 2i + c, so two waves share each SIMD and each K/V tile pair is read
+// from memory once per block.  Per tile of 32 keys (K row-major and V
+// transposed in LDS):
 //   S^T[key][v] = sum_d K[key][d] Q[v][d]     (A = K from LDS, B = Q in registers)
 //   O^T[d][v]  += sum_key V^T[d][key] P^T[key][v]
 // MFMA 16x16x4 layout (lane l): A (row l%16, k slot l/16), B (k slot l/16,
@@ -375,27 +384,34 @@ __global__ __launch_bounds__(256) void k_rows_swiglu(const float* __restrict__ G
 // accumulator of lane l: P^T is the B operand as computed.  Every lane owns
 // one query vector (column l%16), so its softmax state is per lane; a
 // column's 16 keys of a half sit in the 4 lanes l%16 + 16q (xor 16, 32).
+// At the end group 1 hands its (max, sum, O^T) states to group 0 through
+// LDS, which merges them and writes O.
 constexpr int kAQV = 64;           // query vectors per block
 constexpr int kAKT = 32;           // keys per tile
 constexpr int kKsRow = kD + 4;     // K tile row (floats): conflict-free 16-byte reads
 constexpr int kVtRow = kAKT + 4;   // V^T tile row
+constexpr int kAttnThreads = 512;
+constexpr int kStateRow = 34;      // merge record per lane: m, l, O^T[32]
 
 template <int G>
-__global__ __launch_bounds__(256) void k_prefill_attn(const float* __restrict__ QKV, const float* __restrict__ k_cache,
-                                                      const float* __restrict__ v_cache, int n, int n_q, int n_kv,
-                                                      int p0, int cap, float* __restrict__ O) {
+__global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __restrict__ QKV,
+                                                               const float* __restrict__ k_cache,
+                                                               const float* __restrict__ v_cache, int n, int n_q,
+                                                               int n_kv, int p0, int cap, float* __restrict__ O) {
   constexpr int BR = kAQV / G;       // rows per block
-  __shared__ float Ks[kAKT * kKsRow];
-  __shared__ float Vt[kD * kVtRow];
+  __shared__ float Ks[2][kAKT * kKsRow];
+  __shared__ float Vt[2][kD * kVtRow];
+  static_assert(4 * kWave * kStateRow <= 2 * kD * kVtRow, "merge records fit in the V tiles");
   const int j = blockIdx.y;
   const int r0 = blockIdx.x * BR;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2, wv = wave & 3;
   const int li = lane & 15, lq = lane >> 4;
   const int width = (n_q + 2 * n_kv) * kD;
   const float qscale = kLog2e / sqrtf((float)kD);
 
   // this lane's query vector
-  const int v = wave * 16 + li;
+  const int v = wv * 16 + li;
   const int rr = v / G, g = v - rr * G;
   const int row = r0 + rr;
   const bool row_ok = row < n;
@@ -420,100 +436,127 @@ __global__ __launch_bounds__(256) void k_prefill_attn(const float* __restrict__ 
 
   const float* kh = k_cache + (size_t)j * cap * kD;
   const float* vh = v_cache + (size_t)j * cap * kD;
-  // tile staging: K float4 #(tid + 256i) = (key idx/32, dims 4(idx%32)); V
-  // float4 #(tid + 256i) = (key idx%32, dims 4(idx/32)), so the transposed
-  // LDS writes of a wave hit consecutive banks.  Keys at or past n_keys are
-  // cache slots no row may see (stale memory): their loads are clamped into
-  // the cache and their values replaced by zeros, since a masked key still
-  // enters the PV product with weight 0 (and 0 * Inf is NaN).
+  // tile-pair staging: float4 #idx = tid + 512i of the pair, tile idx/1024;
+  // within a tile, K float4 f = (key f/32, dims 4(f%32)) and V float4 f =
+  // (key f%32, dims 4(f/32)), so the transposed LDS writes of a wave hit
+  // consecutive banks.  Keys at or past n_keys are cache slots no row may
+  // see (stale memory): their loads are clamped into the cache and their
+  // values replaced by zeros, since a masked key still enters the PV product
+  // with weight 0 (and 0 * Inf is NaN).
   f4_t kr[4], vr[4];
 #define WSG_ATTN_LOAD(K0)                                                                         \
   _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
-    const int idx = tid + 256 * i;                                                                \
-    const int k1 = (K0) + (idx >> 5), k2 = (K0) + (idx & 31);                                     \
+    const int idx = tid + kAttnThreads * i, f = idx & 1023;                                       \
+    const int kt = (K0) + kAKT * (idx >> 10);                                                     \
+    const int k1 = kt + (f >> 5), k2 = kt + (f & 31);                                             \
     const int kk = min(k1, cap - 1), kv = min(k2, cap - 1);                                       \
-    kr[i] = *reinterpret_cast<const f4_t*>(kh + (size_t)kk * kD + 4 * (idx & 31));                \
-    vr[i] = *reinterpret_cast<const f4_t*>(vh + (size_t)kv * kD + 4 * (idx >> 5));                \
+    kr[i] = *reinterpret_cast<const f4_t*>(kh + (size_t)kk * kD + 4 * (f & 31));                  \
+    vr[i] = *reinterpret_cast<const f4_t*>(vh + (size_t)kv * kD + 4 * (f >> 5));                  \
     if (k1 >= n_keys) kr[i] = f4_t{0.f, 0.f, 0.f, 0.f};                                           \
     if (k2 >= n_keys) vr[i] = f4_t{0.f, 0.f, 0.f, 0.f};                                           \
   }
   WSG_ATTN_LOAD(0)
-  for (int k0 = 0; k0 < n_keys; k0 += kAKT) {
-    __syncthreads();   // previous tile consumed
+  for (int k0 = 0; k0 < n_keys; k0 += 2 * kAKT) {
+    __syncthreads();   // previous tile pair consumed
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      *reinterpret_cast<f4_t*>(&Ks[(idx >> 5) * kKsRow + 4 * (idx & 31)]) = kr[i];
+      const int idx = tid + kAttnThreads * i, f = idx & 1023, t = idx >> 10;
+      *reinterpret_cast<f4_t*>(&Ks[t][(f >> 5) * kKsRow + 4 * (f & 31)]) = kr[i];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Vt[(4 * (idx >> 5) + e) * kVtRow + (idx & 31)] = vr[i][e];
+      for (int e = 0; e < 4; ++e) Vt[t][(4 * (f >> 5) + e) * kVtRow + (f & 31)] = vr[i][e];
     }
     __syncthreads();
-    // next tile in flight during the MFMAs (the last iteration reloads an
-    // in-bounds tile, unused, to keep the loop free of branches)
-    WSG_ATTN_LOAD(min(k0 + kAKT, n_keys - 1))
+    // next pair in flight during the MFMAs (the last iteration reloads an
+    // in-bounds pair, unused, to keep the loop free of branches)
+    WSG_ATTN_LOAD(min(k0 + 2 * kAKT, n_keys - 1))
 #undef WSG_ATTN_LOAD
-
-    // S^T for the two 16-key halves
-    f4v_t sacc[2];
+    const int kt = k0 + kAKT * grp;   // this group's tile
+    if (kt < n_keys) {                // wave-uniform
+      const float* ks = Ks[grp];
+      const float* vt = Vt[grp];
+      // S^T for the two 16-key halves
+      f4v_t sacc[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      sacc[h] = f4v_t{0.f, 0.f, 0.f, 0.f};
-      const float* krow = &Ks[(16 * h + li) * kKsRow + 32 * lq];
+      for (int h = 0; h < 2; ++h) {
+        sacc[h] = f4v_t{0.f, 0.f, 0.f, 0.f};
+        const float* krow = &ks[(16 * h + li) * kKsRow + 32 * lq];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const f4_t a4 = *reinterpret_cast<const f4_t*>(krow + 4 * t);
+        for (int t = 0; t < 8; ++t) {
+          const f4_t a4 = *reinterpret_cast<const f4_t*>(krow + 4 * t);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sacc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[i], qf[4 * t + i], sacc[h], 0, 0, 0);
+          for (int i = 0; i < 4; ++i)
+            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[i], qf[4 * t + i], sacc[h], 0, 0, 0);
+        }
       }
+      // causal mask, tile max per query vector
+      float mx = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kt + 16 * h + 4 * lq + r;
+          if (!(row_ok && key <= my_pos)) sacc[h][r] = -INFINITY;
+          mx = fmaxf(mx, sacc[h][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      // a vector with no key yet keeps m = -inf: guard the rescale
+      const float alpha = mn == -INFINITY ? 1.f : exp2f(m - mn);
+      float psum = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = mn == -INFINITY ? 0.f : exp2f(sacc[h][r] - mn);
+          sacc[h][r] = p;
+          psum += p;
+        }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      l = l * alpha + psum;
+      m = mn;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) oacc[mt] *= alpha;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const f4_t a4 = *reinterpret_cast<const f4_t*>(&vt[(16 * mt + li) * kVtRow + 16 * h + 4 * lq]);
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[s2], sacc[h][s2], oacc[mt], 0, 0, 0);
+        }
     }
-    // causal mask, tile max per query vector
-    float mx = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 16 * h + 4 * lq + r;
-        if (!(row_ok && key <= my_pos)) sacc[h][r] = -INFINITY;
-        mx = fmaxf(mx, sacc[h][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    // a vector with no key yet keeps m = -inf: guard the rescale
-    const float alpha = mn == -INFINITY ? 1.f : exp2f(m - mn);
-    float psum = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = mn == -INFINITY ? 0.f : exp2f(sacc[h][r] - mn);
-        sacc[h][r] = p;
-        psum += p;
-      }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l = l * alpha + psum;
-    m = mn;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) oacc[mt] *= alpha;
-    // O^T += V^T P^T
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const f4_t a4 = *reinterpret_cast<const f4_t*>(&Vt[(16 * mt + li) * kVtRow + 16 * h + 4 * lq]);
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2)
-          oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[s2], sacc[h][s2], oacc[mt], 0, 0, 0);
-      }
   }
-  if (row_ok) {
+  // merge: group 1's states -> group 0 (records in the V tile memory)
+  __syncthreads();
+  float* rec = &Vt[0][0] + (wv * kWave + lane) * kStateRow;
+  if (grp == 1) {
+    rec[0] = m;
+    rec[1] = l;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rec[2 + 4 * mt + r] = oacc[mt][r];
+  }
+  __syncthreads();
+  if (grp == 0 && row_ok) {
+    const float m2 = rec[0], l2 = rec[1];
+    const float mn = fmaxf(m, m2);   // finite: every valid row sees key 0
+    const float a1 = m == -INFINITY ? 0.f : exp2f(m - mn);
+    const float a2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mn);
+    const float inv = 1.0f / (l * a1 + l2 * a2);
     // lane holds O^T[d = 16mt + 4lq + r][its vector]
-    const float inv = 1.0f / l;
     float* o = O + (size_t)row * n_q * kD + (j * G + g) * kD + 4 * lq;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f4_t*>(o + 16 * mt) = oacc[mt] * inv;
+    for (int mt = 0; mt < 8; ++mt) {
+      f4_t out;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[r] = (oacc[mt][r] * a1 + rec[2 + 4 * mt + r] * a2) * inv;
+      *reinterpret_cast<f4_t*>(o + 16 * mt) = out;
+    }
   }
 }
 
@@ -586,27 +629,31 @@ bool launch_skinny(const float* A, const float* B, float* C, int M, int N, int K
 
 // M <= 32 with a compiled K: the small-M kernel; otherwise the tiled kernel
 // with the largest tile that still gives >= 256 blocks.
+// Tiled launch of BM x BN tiles with K split S ways (S slices c_split apart).
+template <int BM, int BN>
+void launch_tiled(const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split, bool acc,
+                  hipStream_t s) {
+  const dim3 grid(N / BN, cdiv(M, BM), S);
+  if (acc) hipLaunchKernelGGL((k_gemm_nt<BM, BN, true>), grid, dim3(256), 0, s, A, B, C, M, N, K, K / S, c_split);
+  else hipLaunchKernelGGL((k_gemm_nt<BM, BN, false>), grid, dim3(256), 0, s, A, B, C, M, N, K, K / S, c_split);
+}
+
 bool launch_gemm(const float* A, const float* B, float* C, int M, int N, int K, bool acc, hipStream_t s) {
   if (M < 1 || N % 64 != 0 || K % kBK != 0) return false;
   if (M <= kSkinnyMaxM && launch_skinny(A, B, C, M, N, K, 1, 0, acc, s)) return true;
   const bool big = (N % 128 == 0) && (int64_t)(N / 128) * cdiv(M, 128) >= 256;
-  if (big) {
-    const dim3 grid(N / 128, cdiv(M, 128));
-    if (acc) hipLaunchKernelGGL((k_gemm_nt<128, 128, true>), grid, dim3(256), 0, s, A, B, C, M, N, K);
-    else hipLaunchKernelGGL((k_gemm_nt<128, 128, false>), grid, dim3(256), 0, s, A, B, C, M, N, K);
-  } else {
-    const dim3 grid(N / 64, cdiv(M, 64));
-    if (acc) hipLaunchKernelGGL((k_gemm_nt<64, 64, true>), grid, dim3(256), 0, s, A, B, C, M, N, K);
-    else hipLaunchKernelGGL((k_gemm_nt<64, 64, false>), grid, dim3(256), 0, s, A, B, C, M, N, K);
-  }
+  if (big) launch_tiled<128, 128>(A, B, C, M, N, K, 1, 0, acc, s);
+  else launch_tiled<64, 64>(A, B, C, M, N, K, 1, 0, acc, s);
   return true;
 }
 
-// X[M x N] += A . B^T for a residual stream consumed by k_rows_norm.  With
-// few rows and few column tiles the small-M kernel also splits K over up
-// to kMaxSplitK blocks per tile, writing FP32 partial slices to P (M x N
-// each) instead of X; returns the slice count (0: added into X), which the
-// following k_rows_norm adds to X.  Returns -1 for an unsupported shape.
+// X[M x N] += A . B^T for a residual stream consumed by k_rows_norm.  A
+// residual projection has few column tiles (N = hidden), so K is split over
+// up to kMaxSplitK blocks per tile (the small-M kernel for up to 32 rows;
+// otherwise the larger tiles whose count times the split reaches 256
+// blocks), writing FP32 partial slices to P (M x N each) instead of X;
+// returns the slice count (0: added into X), which the following
+// k_rows_norm adds to X in slice order.  Returns -1 for an unsupported shape.
 constexpr int kMaxSplitK = 8;
 
 int launch_gemm_residual(const float* A, const float* B, float* X, float* P, int M, int N, int K, hipStream_t s) {
@@ -618,6 +665,27 @@ int launch_gemm_residual(const float* A, const float* B, float* X, float* P, int
       if ((N / 16) * c >= 256) break;
     }
     if (S > 1 && launch_skinny(A, B, P, M, N, K, S, (size_t)M * N, false, s)) return S;
+  }
+  if (M > kSkinnyMaxM && N % 64 == 0 && K % kBK == 0) {
+    // the fewest splits reaching 256 blocks, 128 x 128 tiles first
+    int bm = 0, S = 0;
+    for (int t : {128, 64}) {
+      if (N % t != 0) continue;
+      const int64_t tiles = (int64_t)(N / t) * cdiv(M, t);
+      for (int c = 1; c <= kMaxSplitK && K % (c * kBK) == 0; c *= 2)
+        if (tiles * c >= 256) { bm = t; S = c; break; }
+      if (bm) break;
+    }
+    if (bm == 0) {   // too few tiles for 256 blocks: small tiles, the most splits
+      bm = 64;
+      S = 1;
+      while (S < kMaxSplitK && K % (2 * S * kBK) == 0) S *= 2;
+    }
+    if (S > 1) {
+      if (bm == 128) launch_tiled<128, 128>(A, B, P, M, N, K, S, (size_t)M * N, false, s);
+      else launch_tiled<64, 64>(A, B, P, M, N, K, S, (size_t)M * N, false, s);
+      return S;
+    }
   }
   return launch_gemm(A, B, X, M, N, K, true, s) ? 0 : -1;
 }
@@ -641,7 +709,7 @@ PrefillLayout prefill_layout(int rows, int H, int I, int Q, int KV, size_t es, s
   p.o = take((size_t)rows * Q * 4);
   p.act = take((size_t)rows * I * 4);
   p.gu = take((size_t)rows * 2 * I * 4);
-  p.part = take((size_t)kMaxSplitK * std::min(rows, kSkinnyMaxM) * H * 4);
+  p.part = take((size_t)kMaxSplitK * rows * H * 4);   // split-K partial slices of a residual GEMM
   p.total = off;
   return p;
 }
@@ -685,9 +753,9 @@ wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, hipStream_t s)
       if (l == c.n_layers - 1) break;   // only the K/V of the last layer has a consumer
       const dim3 ag(cdiv(rows, kAQV / G), nkv);
       switch (G) {
-        case 1: hipLaunchKernelGGL((k_prefill_attn<1>), ag, dim3(256), 0, s, QKV, (const float*)L.k_cache,
+        case 1: hipLaunchKernelGGL((k_prefill_attn<1>), ag, dim3(kAttnThreads), 0, s, QKV, (const float*)L.k_cache,
                                    (const float*)L.v_cache, rows, nq, nkv, pc, a.cap, O); break;
-        case 2: hipLaunchKernelGGL((k_prefill_attn<2>), ag, dim3(256), 0, s, QKV, (const float*)L.k_cache,
+        case 2: hipLaunchKernelGGL((k_prefill_attn<2>), ag, dim3(kAttnThreads), 0, s, QKV, (const float*)L.k_cache,
                                    (const float*)L.v_cache, rows, nq, nkv, pc, a.cap, O); break;
         default: return fail(WSG_ERR_UNSUPPORTED, "chunked prefill supports query groups of 1 or 2");
       }
