@@ -18,12 +18,14 @@ from synth import MINI, PROMPT_SEEDS, QWEN3_0_6B, model_weights, prompt_ids
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 
-# Tiled path: M > 32 or K outside {256, 512, 1024, 2048, 3072}.  Small-M
+# Tiled path: M > 32 or K outside {256, 512, 1024, 2048, 3072}; 128x192,
+# 128x128 and 64x64 tiles with 64- or 32-wide K tiles.  Small-M
 # path (M <= 32): one and two 16-row tiles, ragged M, every compiled K and
 # 4, 8 and 16 waves per block.
 @pytest.mark.parametrize("M,N,K", [(1, 64, 32), (37, 128, 64), (65, 192, 96), (130, 4096, 1024),
                                    (1024, 4096, 1024), (500, 1024, 2048), (257, 6144, 1024),
-                                   (1024, 1024, 3072), (2048, 4096, 1024),
+                                   (1024, 1024, 3072), (2048, 4096, 1024), (1024, 6144, 1024), (300, 768, 192),
+                                   (256, 384, 160),
                                    (1, 1024, 1024), (7, 4096, 1024), (16, 2048, 2048), (17, 64, 256),
                                    (31, 6144, 1024), (32, 1024, 3072), (31, 1024, 2048), (8, 512, 512),
                                    (3, 128, 3072)])

@@ -22,6 +22,14 @@ __all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "gemm_nt", "WsgError", 
            "WSG_STAGE_QKV", "WSG_STAGE_ATTN", "WSG_STAGE_O", "WSG_STAGE_GATEUP", "WSG_STAGE_DOWN",
            "WSG_STAGE_HEAD", "WSG_OPT_USE_GRAPH", "WSG_OPT_TIMED_STAGE", "WSG_GEMV_NONTEMPORAL", "stream_read", "lib"]
 
+try:
+    # torch first: libwsg.so then binds to the HIP runtime torch already
+    # loaded (loading the library first would bring in a second runtime,
+    # under which its launches find no device)
+    import torch as _torch_module  # noqa: F401
+except ImportError:
+    pass
+
 lib = _abi.lib
 lib()  # fail loudly at import when libwsg.so is missing
 

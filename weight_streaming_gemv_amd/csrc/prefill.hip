@@ -43,7 +43,7 @@ typedef float f4v_t __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ GEMM
 // C[M x N] (+)= A[M x K] . B[N x K]^T, all row-major FP32, K-contiguous
-// operands.  Block tile BM x BN x 32, 256 threads = 2 x 2 waves, each wave a
+// operands.  Block tile BM x BN x BK, 256 threads = 2 x 2 waves, each wave a
 // (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA tiles (v_mfma_f32_32x32x2f32).
 // Split K: block z covers k in [z*kspan, (z+1)*kspan) and writes its own
 // slice C + z*c_split (kspan = K, one slice, when K is not split).
@@ -51,20 +51,26 @@ typedef float f4v_t __attribute__((ext_vector_type(4)));
 // MFMA 32x32x2 operand layout (lane l): A element (row l%32, k l/32),
 // B element (k l/32, col l%32); accumulator register r holds row
 // 8*(r/4) + 4*(l/32) + r%4, col l%32.  The two k slots of every MFMA are
-// mapped to k = h*16 + s (h = l/32, s = step 0..15) of the 32-wide K tile,
-// so each lane reads 16 consecutive floats of one LDS row per tile.
-constexpr int kBK = 32;
+// mapped to k = 32u + h*16 + s (u = 32-wide part of the K tile, h = l/32,
+// s = step 0..15), so each lane reads 16 consecutive floats of one LDS row
+// per part.  A 64-wide K tile (K ranges that are multiples of 64) gives
+// each wave 32*TM*TN MFMAs (8192 cycles for a 64 x 64 wave tile) between
+// barriers, which covers the latency of the next tile's global loads.
+constexpr int kBK = 32;                   // K granularity of the shapes accepted (and of the small-M kernel)
 constexpr int kLdsPad = 4;                // floats of padding per LDS row
-constexpr int kLdsRow = kBK + kLdsPad;
 
-template <int BM, int BN, bool ACC>
+template <int BM, int BN, int BK, bool ACC>
 __global__ __launch_bounds__(256) void k_gemm_nt(const float* __restrict__ A, const float* __restrict__ B,
                                                  float* __restrict__ C, int M, int N, int K, int kspan,
                                                  size_t c_split) {
-  constexpr int WM = BM / 2, WN = BN / 2;     // wave tile
-  constexpr int TM = WM / 32, TN = WN / 32;   // MFMA tiles per wave
-  constexpr int A_LOADS = BM * kBK / 4 / 256; // float4 per thread per tile
-  constexpr int B_LOADS = BN * kBK / 4 / 256;
+  constexpr int kLdsRow = BK + kLdsPad;
+  constexpr int NU = BK / 32;                  // 32-wide parts per K tile
+  constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
+  constexpr int TM = WM / 32, TN = WN / 32;    // MFMA tiles per wave
+  constexpr int F4_ROW = BK / 4;               // float4 per tile row
+  constexpr int A_LOADS = BM * F4_ROW / 256;   // float4 per thread per tile
+  constexpr int B_LOADS = BN * F4_ROW / 256;
+  static_assert(BM * F4_ROW % 256 == 0 && BN * F4_ROW % 256 == 0, "whole float4 per thread");
   __shared__ float As[BM * kLdsRow];
   __shared__ float Bs[BN * kLdsRow];
 
@@ -86,63 +92,72 @@ __global__ __launch_bounds__(256) void k_gemm_nt(const float* __restrict__ A, co
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   // global -> register staging: thread loads float4 #(tid + 256 i) of the
-  // tile: row = idx / 8, col4 = idx % 8 (plain loops: arrays captured by a
-  // lambda would be forced into scratch memory)
+  // tile: row = idx / F4_ROW, col4 = idx % F4_ROW (plain loops: arrays
+  // captured by a lambda would be forced into scratch memory)
   f4_t ra[A_LOADS], rb[B_LOADS];   // native vectors: HIP's float4 struct arrays end up in scratch
 #define WSG_GEMM_LOAD(K0)                                                                           \
   {                                                                                                \
     _Pragma("unroll") for (int i = 0; i < A_LOADS; ++i) {                                          \
-      const int idx = tid + 256 * i, row = idx >> 3, c4 = idx & 7;                                 \
+      const int idx = tid + 256 * i, row = idx / F4_ROW, c4 = idx % F4_ROW;                        \
       const int gm = min(m0 + row, M - 1);   /* rows past M feed only unstored outputs */        \
       ra[i] = *reinterpret_cast<const f4_t*>(A + (size_t)gm * K + (K0) + 4 * c4);                  \
     }                                                                                              \
     _Pragma("unroll") for (int i = 0; i < B_LOADS; ++i) {                                          \
-      const int idx = tid + 256 * i, row = idx >> 3, c4 = idx & 7;                                 \
+      const int idx = tid + 256 * i, row = idx / F4_ROW, c4 = idx % F4_ROW;                        \
       rb[i] = *reinterpret_cast<const f4_t*>(B + (size_t)(n0 + row) * K + (K0) + 4 * c4);          \
     }                                                                                              \
   }
 
+  // the operands of one 32-wide part u of the LDS tile
+  float af[NU][TM][16], bf[NU][TN][16];
+#define WSG_GEMM_FRAGS(U)                                                                          \
+  {                                                                                                \
+    _Pragma("unroll") for (int a = 0; a < TM; ++a)                                                 \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                              \
+        const f4_t v = *reinterpret_cast<const f4_t*>(                                             \
+            &As[(wm + a * 32 + li) * kLdsRow + 32 * (U) + lh * 16 + 4 * q]);                       \
+        af[U][a][4 * q] = v.x; af[U][a][4 * q + 1] = v.y; af[U][a][4 * q + 2] = v.z;              \
+        af[U][a][4 * q + 3] = v.w;                                                                 \
+      }                                                                                            \
+    _Pragma("unroll") for (int b = 0; b < TN; ++b)                                                 \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                              \
+        const f4_t v = *reinterpret_cast<const f4_t*>(                                             \
+            &Bs[(wn + b * 32 + li) * kLdsRow + 32 * (U) + lh * 16 + 4 * q]);                       \
+        bf[U][b][4 * q] = v.x; bf[U][b][4 * q + 1] = v.y; bf[U][b][4 * q + 2] = v.z;              \
+        bf[U][b][4 * q + 3] = v.w;                                                                 \
+      }                                                                                            \
+  }
+#define WSG_GEMM_MFMA(U)                                                                           \
+  _Pragma("unroll") for (int s = 0; s < 16; ++s)                                                   \
+    _Pragma("unroll") for (int a = 0; a < TM; ++a)                                                 \
+      _Pragma("unroll") for (int b = 0; b < TN; ++b)                                               \
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[U][a][s], bf[U][b][s], acc[a][b], 0, 0, 0);
+
   WSG_GEMM_LOAD(0)
-  for (int k0 = 0; k0 < kspan; k0 += kBK) {
+  for (int k0 = 0; k0 < kspan; k0 += BK) {
     __syncthreads();          // previous tile fully consumed
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
-      const int idx = tid + 256 * i, row = idx >> 3, c4 = idx & 7;
+      const int idx = tid + 256 * i, row = idx / F4_ROW, c4 = idx % F4_ROW;
       *reinterpret_cast<f4_t*>(&As[row * kLdsRow + 4 * c4]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
-      const int idx = tid + 256 * i, row = idx >> 3, c4 = idx & 7;
+      const int idx = tid + 256 * i, row = idx / F4_ROW, c4 = idx % F4_ROW;
       *reinterpret_cast<f4_t*>(&Bs[row * kLdsRow + 4 * c4]) = rb[i];
     }
     __syncthreads();
     // next tile in flight during the MFMAs (the last iteration reloads the
     // final tile, in bounds and unused, to keep the loop free of branches)
-    WSG_GEMM_LOAD(min(k0 + kBK, kspan - kBK))
-#undef WSG_GEMM_LOAD
-    float af[TM][16], bf[TN][16];
+    WSG_GEMM_LOAD(min(k0 + BK, kspan - BK))
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+    for (int u = 0; u < NU; ++u) WSG_GEMM_FRAGS(u)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4_t v = *reinterpret_cast<const f4_t*>(&As[(wm + a * 32 + li) * kLdsRow + lh * 16 + 4 * q]);
-        af[a][4 * q] = v.x; af[a][4 * q + 1] = v.y; af[a][4 * q + 2] = v.z; af[a][4 * q + 3] = v.w;
-      }
-#pragma unroll
-    for (int b = 0; b < TN; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4_t v = *reinterpret_cast<const f4_t*>(&Bs[(wn + b * 32 + li) * kLdsRow + lh * 16 + 4 * q]);
-        bf[b][4 * q] = v.x; bf[b][4 * q + 1] = v.y; bf[b][4 * q + 2] = v.z; bf[b][4 * q + 3] = v.w;
-      }
-#pragma unroll
-    for (int s = 0; s < 16; ++s)
-#pragma unroll
-      for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a][s], bf[b][s], acc[a][b], 0, 0, 0);
+    for (int u = 0; u < NU; ++u) { WSG_GEMM_MFMA(u) }
   }
+#undef WSG_GEMM_LOAD
+#undef WSG_GEMM_FRAGS
+#undef WSG_GEMM_MFMA
 
 #pragma unroll
   for (int a = 0; a < TM; ++a)
@@ -627,23 +642,50 @@ bool launch_skinny(const float* A, const float* B, float* C, int M, int N, int K
   }
 }
 
-// M <= 32 with a compiled K: the small-M kernel; otherwise the tiled kernel
-// with the largest tile that still gives >= 256 blocks.
-// Tiled launch of BM x BN tiles with K split S ways (S slices c_split apart).
+// Tiled launch of BM x BN tiles with K split S ways (S slices c_split
+// apart): 64-wide K tiles when the split's K range allows, else 32-wide.
 template <int BM, int BN>
 void launch_tiled(const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split, bool acc,
                   hipStream_t s) {
   const dim3 grid(N / BN, cdiv(M, BM), S);
-  if (acc) hipLaunchKernelGGL((k_gemm_nt<BM, BN, true>), grid, dim3(256), 0, s, A, B, C, M, N, K, K / S, c_split);
-  else hipLaunchKernelGGL((k_gemm_nt<BM, BN, false>), grid, dim3(256), 0, s, A, B, C, M, N, K, K / S, c_split);
+  const int kspan = K / S;
+  auto go = [&](auto bk) {
+    constexpr int BK = decltype(bk)::value;
+    if (acc) hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, true>), grid, dim3(256), 0, s, A, B, C, M, N, K, kspan, c_split);
+    else hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, false>), grid, dim3(256), 0, s, A, B, C, M, N, K, kspan, c_split);
+  };
+  if (kspan % 64 == 0) go(std::integral_constant<int, 64>{});
+  else go(std::integral_constant<int, 32>{});
 }
 
+// Tile of the tiled kernel for an M x N product: the one with the fewest
+// rounds of 256 blocks times tile area (the time of the busiest CU), the
+// larger tile on ties; 128 x 192 serves N = 6144-like widths in one round.
+struct Tile { int bm, bn; };
+Tile pick_tile(int M, int N) {
+  Tile best{64, 64};
+  int64_t best_cost = -1;
+  for (Tile t : {Tile{128, 192}, Tile{128, 128}, Tile{64, 64}}) {
+    if (N % t.bn != 0) continue;
+    const int64_t blocks = (int64_t)(N / t.bn) * cdiv(M, t.bm);
+    const int64_t cost = (blocks + 255) / 256 * t.bm * t.bn;
+    if (best_cost < 0 || cost < best_cost) { best = t; best_cost = cost; }
+  }
+  return best;
+}
+
+void launch_tile(Tile t, const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split,
+                 bool acc, hipStream_t s) {
+  if (t.bm == 128 && t.bn == 192) launch_tiled<128, 192>(A, B, C, M, N, K, S, c_split, acc, s);
+  else if (t.bm == 128) launch_tiled<128, 128>(A, B, C, M, N, K, S, c_split, acc, s);
+  else launch_tiled<64, 64>(A, B, C, M, N, K, S, c_split, acc, s);
+}
+
+// M <= 32 with a compiled K: the small-M kernel; otherwise the tiled kernel.
 bool launch_gemm(const float* A, const float* B, float* C, int M, int N, int K, bool acc, hipStream_t s) {
   if (M < 1 || N % 64 != 0 || K % kBK != 0) return false;
   if (M <= kSkinnyMaxM && launch_skinny(A, B, C, M, N, K, 1, 0, acc, s)) return true;
-  const bool big = (N % 128 == 0) && (int64_t)(N / 128) * cdiv(M, 128) >= 256;
-  if (big) launch_tiled<128, 128>(A, B, C, M, N, K, 1, 0, acc, s);
-  else launch_tiled<64, 64>(A, B, C, M, N, K, 1, 0, acc, s);
+  launch_tile(pick_tile(M, N), A, B, C, M, N, K, 1, 0, acc, s);
   return true;
 }
 
@@ -667,23 +709,22 @@ int launch_gemm_residual(const float* A, const float* B, float* X, float* P, int
     if (S > 1 && launch_skinny(A, B, P, M, N, K, S, (size_t)M * N, false, s)) return S;
   }
   if (M > kSkinnyMaxM && N % 64 == 0 && K % kBK == 0) {
-    // the fewest splits reaching 256 blocks, 128 x 128 tiles first
+    // the fewest splits (64-wide K tiles each) reaching 256 blocks, 128 x 128 tiles first
     int bm = 0, S = 0;
     for (int t : {128, 64}) {
       if (N % t != 0) continue;
       const int64_t tiles = (int64_t)(N / t) * cdiv(M, t);
-      for (int c = 1; c <= kMaxSplitK && K % (c * kBK) == 0; c *= 2)
+      for (int c = 1; c <= kMaxSplitK && K % (c * 64) == 0; c *= 2)
         if (tiles * c >= 256) { bm = t; S = c; break; }
       if (bm) break;
     }
     if (bm == 0) {   // too few tiles for 256 blocks: small tiles, the most splits
       bm = 64;
       S = 1;
-      while (S < kMaxSplitK && K % (2 * S * kBK) == 0) S *= 2;
+      while (S < kMaxSplitK && K % (2 * S * 64) == 0) S *= 2;
     }
     if (S > 1) {
-      if (bm == 128) launch_tiled<128, 128>(A, B, P, M, N, K, S, (size_t)M * N, false, s);
-      else launch_tiled<64, 64>(A, B, P, M, N, K, S, (size_t)M * N, false, s);
+      launch_tile(Tile{bm, bm}, A, B, P, M, N, K, S, (size_t)M * N, false, s);
       return S;
     }
   }
