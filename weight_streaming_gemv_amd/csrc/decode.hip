@@ -740,8 +740,11 @@ struct SoftState {
   }
 };
 
-// Partial state layout: for each (row, kv head, split, g): [m, l, acc[128]].
-constexpr int kPartStride = 2 + kD;
+// Partial state layout: for each (row, kv head, split, g): [m, l, -, -,
+// acc[128]] (kAttnPartStride floats; the accumulators 16-byte aligned).
+constexpr int kPartStride = kAttnPartStride;
+constexpr int kPartAcc = 4;
+static_assert(kPartStride == kPartAcc + kD && kPartStride % 4 == 0, "partial state layout");
 
 // The attention of one KV head j (its G query heads) for one query row at
 // position p, over the keys [k_begin, k_end), spread over NR 16-lane rows
@@ -882,14 +885,16 @@ struct RowMerge {
 };
 
 // Split-K attention: block (split, j, t) covers the keys of split for query
-// row t (position p + t of a T-token step).
+// row t (position p + t of a T-token step).  With direct set, a context
+// within one split writes o itself; otherwise every split writes its
+// partial state (for the merge, or the merging output projection).
 template <typename TS, int G, int T>
 __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
                                                  TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
                                                  const TS* __restrict__ k_norm, const float* __restrict__ rope_cur,
                                                  const int32_t* __restrict__ ctrl, int n_q, int n_kv, int cap,
                                                  float eps, int chunk, float* __restrict__ part,
-                                                 TS* __restrict__ o) {
+                                                 TS* __restrict__ o, int direct) {
   constexpr bool PREV = T > 1;
   __shared__ RowMerge<G, 16> sm;
   const int j = blockIdx.y;            // KV head
@@ -933,11 +938,11 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
     const int g = e / kD, d = e - g * kD;
     float mx, L, A;
     sm.get(g, d, mx, L, A);
-    if (n_splits == 1) {
+    if (n_splits == 1 && direct) {
       o[(size_t)t * Q + (size_t)(j * G + g) * kD + d] = Store<TS>::from_f(A / L);
     } else {
       if (d == 0) { my_part[g * kPartStride] = mx; my_part[g * kPartStride + 1] = L; }
-      my_part[g * kPartStride + 2 + d] = A;
+      my_part[g * kPartStride + kPartAcc + d] = A;
     }
   }
 }
@@ -1075,6 +1080,33 @@ struct WoSlice<q4w, G, R> {
   }
 };
 
+// The W_o slice of KV head j times the head's attention output o (T rows,
+// in LDS, already rounded as stored), plus the residual rows for j = 0:
+// part[t][j][row0 + r] for the wave's rows.  Called by every thread after
+// o is complete in LDS.
+template <typename TW, int G, int R, int T>
+__device__ __forceinline__ void wo_apply(const WoSlice<TW, G, R>& w, const float (&s_o)[T][G * kD], int row0, int H,
+                                         const float (&xb)[T], float* __restrict__ opart, int part_row, int j) {
+  if constexpr (std::is_same<TW, q4w>::value) {
+    // o as FP16 pairs in the int4 slice's order (exact: o is FP16-rounded)
+    __shared__ uint32_t s_oh[T][G * kD / 2];
+    for (int e = threadIdx.x; e < T * G * kD / 2; e += kBlock) {
+      const int r = e / (G * kD / 2), f = e - r * (G * kD / 2);
+      const int c = (f / 8) * 16 + 8 * ((f % 8) / 4) + (f % 4);   // chunk, word, pair
+      h2_t h;
+      h.x = (_Float16)s_o[r][c];
+      h.y = (_Float16)s_o[r][c + 4];
+      s_oh[r][f] = __builtin_bit_cast(uint32_t, h);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < T; ++r) w.apply(s_oh[r], row0, H, xb[r], opart + (size_t)r * part_row + (size_t)j * H);
+  } else {
+#pragma unroll
+    for (int r = 0; r < T; ++r) w.apply(s_o[r], row0, H, xb[r], opart + (size_t)r * part_row + (size_t)j * H);
+  }
+}
+
 template <typename TS, typename TW, int G, int R, int T>
 __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
                                                    TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
@@ -1125,24 +1157,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
     s_o[r][f] = Store<TS>::to_f(Store<TS>::from_f(A / L));   // o rounded as stored
   }
   __syncthreads();
-  if constexpr (std::is_same<TW, q4w>::value) {
-    // o as FP16 pairs in the int4 slice's order (exact: o is FP16-rounded)
-    __shared__ uint32_t s_oh[T][G * kD / 2];
-    for (int e = threadIdx.x; e < T * G * kD / 2; e += kBlock) {
-      const int r = e / (G * kD / 2), f = e - r * (G * kD / 2);
-      const int c = (f / 8) * 16 + 8 * ((f % 8) / 4) + (f % 4);   // chunk, word, pair
-      h2_t h;
-      h.x = (_Float16)s_o[r][c];
-      h.y = (_Float16)s_o[r][c + 4];
-      s_oh[r][f] = __builtin_bit_cast(uint32_t, h);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < T; ++r) w.apply(s_oh[r], row0, H, xb[r], opart + (size_t)r * part_row + (size_t)j * H);
-  } else {
-#pragma unroll
-    for (int r = 0; r < T; ++r) w.apply(s_o[r], row0, H, xb[r], opart + (size_t)r * part_row + (size_t)j * H);
-  }
+  wo_apply<TW, G, R, T>(w, s_o, row0, H, xb, opart, part_row, j);
 }
 
 // Merge of the split-K partial states of one query head of row t (one
@@ -1187,10 +1202,148 @@ __global__ __launch_bounds__(kBlock) void k_attn_merge(const float* __restrict__
   const int d = tid & (kD - 1), half = tid >> 7;
   float A = 0.f;
 #pragma unroll 8
-  for (int sp = half; sp < n_splits; sp += 2) A = fmaf(s_w[sp], hp[sp * sstride + 2 + d], A);
+  for (int sp = half; sp < n_splits; sp += 2) A = fmaf(s_w[sp], hp[sp * sstride + kPartAcc + d], A);
   s_a[half][d] = A;
   __syncthreads();
   if (tid < kD) o[((size_t)t * n_kv * G + h) * kD + tid] = Store<TS>::from_f((s_a[0][tid] + s_a[1][tid]) / L);
+}
+
+// Longer contexts: the split-K merge fused with the output projection.
+// Block (b, j) merges KV head j's split states (all its T*G query vectors)
+// into o_j in LDS, then multiplies its 4R rows of W_o restricted to head j's
+// columns, writing the same per-KV-head partials as the fused short-context
+// launch:
+//   part[t][j][m] = W_o[m, cols of head j] . o_j(row t)  (+ x[t][m] for j = 0).
+// Each of the 32 blocks of a head reads the head's states (a few KiB per
+// split, from L2).  Vector loads return in issue order, so the split maxima
+// and sums and the first kMergeBatch splits' accumulators of every wave are
+// issued before the W_o rows (their latency overlaps the weight stream);
+// the loads cover the launch's split count (a kernel argument), clamped,
+// and splits past a row's context are dropped by selection, never by a
+// multiply (stale memory may hold Inf or NaN).  Wave w sums splits w, w+4,
+// ... for every float4 of o_j with the weights exp2(m_s - max); the four
+// wave sums are added in LDS in wave order and divided by the weighted sum.
+constexpr int kMergeBatch = 16;   // accumulator loads in flight per lane and float4
+
+template <typename TS, typename TW, int G, int R, int T>
+__global__ __launch_bounds__(kBlock) void k_merge_o(const float* __restrict__ part, const int32_t* __restrict__ ctrl,
+                                                    int n_q, int n_kv, int splits, int chunk,
+                                                    const TW* __restrict__ Wo, const TS* __restrict__ x_res, int H,
+                                                    float* __restrict__ opart, int part_row) {
+  constexpr int TG = T * G;               // query vectors of the head
+  constexpr int NE = TG * kD / 4;         // float4 groups of o_j
+  constexpr int PL = ceil_div(NE, kWave); // per lane
+  constexpr int NST = ceil_div(TG * kMaxSplits, kBlock);   // stat entries per thread
+  __shared__ float s_w[TG][kMaxSplits];   // split maxima, then merge weights
+  __shared__ float s_l[TG][kMaxSplits];
+  __shared__ float s_inv[TG];
+  __shared__ f4_t s_acc[kWavesPerBlock][PL * kWave];
+  __shared__ float s_o[T][G * kD];
+  const int j = blockIdx.y;
+  const int lane = lane_id(), wave = wave_id(), tid = threadIdx.x;
+  const int row0 = (blockIdx.x * kWavesPerBlock + wave) * R;
+  const int Q = n_q * kD;
+  const float* hp = part + (size_t)j * splits * G * kPartStride;   // row t adds t * trow
+  const size_t trow = (size_t)n_kv * splits * G * kPartStride;
+  const size_t sstride = (size_t)G * kPartStride;                  // between splits
+
+  // 1. split statistics (entry e = tg * kMaxSplits + sp), clamped to the launch's splits
+  float mv[NST], lv[NST];
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int e = min(tid + kBlock * i, TG * kMaxSplits - 1);
+    const int tg = e / kMaxSplits, sp = min(e - tg * kMaxSplits, splits - 1), t = tg / G, g = tg - t * G;
+    const float* st = hp + t * trow + (size_t)sp * sstride + (size_t)g * kPartStride;
+    mv[i] = st[0];
+    lv[i] = st[1];
+  }
+  // 2. the first batch of accumulators: lane float4 e = lane + 64k of o_j
+  // (vector e / 32, dims 4(e % 32)), splits wave + 4b for b < kMergeBatch
+  const float* ep[PL];
+#pragma unroll
+  for (int k = 0; k < PL; ++k) {
+    const int e = min(lane + kWave * k, NE - 1);
+    const int tg = e / (kD / 4), d4 = e - tg * (kD / 4), t = tg / G, g = tg - t * G;
+    ep[k] = hp + t * trow + (size_t)g * kPartStride + kPartAcc + 4 * d4;
+  }
+  f4_t av[PL][kMergeBatch];
+#pragma unroll
+  for (int k = 0; k < PL; ++k)
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b)
+      av[k][b] = *reinterpret_cast<const f4_t*>(ep[k] + (size_t)min(wave + kWavesPerBlock * b, splits - 1) * sstride);
+  // 3. the residual rows and the W_o rows, then the position
+  float xb[T];
+#pragma unroll
+  for (int r = 0; r < T; ++r) xb[r] = j == 0 ? rows_prefetch<TS, R>(x_res + (size_t)r * H, row0, H) : 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+  WoSlice<TW, G, R> w;
+  w.load(Wo, Q, j * G * kD, row0, H);
+  __builtin_amdgcn_sched_barrier(0);
+  const int pos0 = ctrl[kCtrlPos];
+
+  // weights: per query vector the maximum over its splits, exp2(m_s - max), 1 / sum
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int e = tid + kBlock * i;
+    if (e < TG * kMaxSplits) {
+      const int tg = e / kMaxSplits, sp = e - tg * kMaxSplits, t = tg / G;
+      const bool in = sp < ceil_div(pos0 + t + 1, chunk);
+      s_w[tg][sp] = in ? mv[i] : -INFINITY;
+      s_l[tg][sp] = in ? lv[i] : 0.f;
+    }
+  }
+  __syncthreads();
+  for (int tg = wave; tg < TG; tg += kWavesPerBlock) {
+    float mx = -INFINITY;
+    for (int sp = lane; sp < kMaxSplits; sp += kWave) mx = fmaxf(mx, s_w[tg][sp]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float L = 0.f;
+    for (int sp = lane; sp < kMaxSplits; sp += kWave) {
+      const float wgt = s_w[tg][sp] == -INFINITY ? 0.f : exp2f(s_w[tg][sp] - mx);
+      L = fmaf(s_l[tg][sp], wgt, L);
+      s_w[tg][sp] = wgt;
+    }
+    L = wave_sum(L);
+    if (lane == 0) s_inv[tg] = 1.0f / L;
+  }
+  __syncthreads();
+  // weighted sums, batch by batch (later batches only for very long contexts)
+  f4_t acc[PL];
+#pragma unroll
+  for (int k = 0; k < PL; ++k) acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
+  for (int base = 0;; base += kMergeBatch * kWavesPerBlock) {
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      const int tg = min(lane + kWave * k, NE - 1) / (kD / 4);
+#pragma unroll
+      for (int b = 0; b < kMergeBatch; ++b) {
+        const int sp = base + wave + kWavesPerBlock * b;
+        const float wgt = sp < kMaxSplits ? s_w[tg][sp] : 0.f;   // 0 past the row's context
+        acc[k] += wgt == 0.f ? f4_t{0.f, 0.f, 0.f, 0.f} : wgt * av[k][b];
+      }
+    }
+    const int next = base + kMergeBatch * kWavesPerBlock;
+    if (next >= splits) break;   // uniform: launch argument
+#pragma unroll
+    for (int k = 0; k < PL; ++k)
+#pragma unroll
+      for (int b = 0; b < kMergeBatch; ++b)
+        av[k][b] = *reinterpret_cast<const f4_t*>(
+            ep[k] + (size_t)min(next + wave + kWavesPerBlock * b, splits - 1) * sstride);
+  }
+#pragma unroll
+  for (int k = 0; k < PL; ++k) s_acc[wave][lane + kWave * k] = acc[k];
+  __syncthreads();
+  for (int e = tid; e < NE; e += kBlock) {
+    const int tg = e / (kD / 4), d4 = e - tg * (kD / 4), t = tg / G, g = tg - t * G;
+    const f4_t a = ((s_acc[0][e] + s_acc[1][e]) + (s_acc[2][e] + s_acc[3][e])) * s_inv[tg];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[t][g * kD + 4 * d4 + i] = Store<TS>::to_f(Store<TS>::from_f(a[i]));
+  }
+  __syncthreads();
+  wo_apply<TW, G, R, T>(w, s_o, row0, H, xb, opart, part_row, j);
 }
 
 // --------------------------------------------------------------- dispatch
@@ -1374,14 +1527,15 @@ bool head_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
 }
 
 template <typename TS>
-bool attn_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+bool attn_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool direct, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
   const dim3 grid(sh.attn_splits, a.n_kv, sh.tokens);
   auto go = [&](auto gc) {
     return with_t(sh.tokens, [&](auto tc) {
       hipLaunchKernelGGL((k_attn<TS, decltype(gc)::value, decltype(tc)::value>), grid, dim3(kBlock), 0, s,
                          (const TS*)a.qkv, (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm,
-                         a.rope_cur, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, sh.attn_chunk, a.attn_part, (TS*)a.o);
+                         a.rope_cur, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, sh.attn_chunk, a.attn_part, (TS*)a.o,
+                         direct ? 1 : 0);
       return true;
     });
   };
@@ -1450,6 +1604,43 @@ bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hi
   });
 }
 
+template <typename TS>
+bool merge_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+  const int G = a.n_q / a.n_kv;
+  return with_w<TS>(a.wfmt, L.wo, L.wo_p, [&](auto Wo) {
+    using TW = pointee_t<decltype(Wo)>;
+    const int part_row = parts_slots(a.hidden, a.n_kv, sh.tokens) * a.hidden;
+    if (part_row == 0) return false;
+    auto go = [&](auto gc, auto rc) {
+      constexpr int R = decltype(rc)::value, GG = decltype(gc)::value;
+      if constexpr (std::is_same<TW, q4w>::value && (R * GG * kD / 16) % kWave != 0) {
+        return false;
+      } else {
+        const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R), a.n_kv);
+        return with_t(sh.tokens, [&](auto tc) {
+          hipLaunchKernelGGL((k_merge_o<TS, TW, GG, R, decltype(tc)::value>), grid, dim3(kBlock), 0, s, a.attn_part,
+                             a.ctrl, a.n_q, a.n_kv, sh.attn_splits, sh.attn_chunk, Wo, (const TS*)a.x, a.hidden,
+                             a.opart, part_row);
+          return true;
+        });
+      }
+    };
+    auto with_g = [&](auto rc) {
+      switch (G) {
+        case 1: return go(IC<1>{}, rc);
+        case 2: return go(IC<2>{}, rc);
+        case 4: return go(IC<4>{}, rc);
+        default: return false;
+      }
+    };
+    switch (sh.rows_attn_o) {
+      case 4: return with_g(IC<4>{});
+      case 8: return with_g(IC<8>{});
+      default: return false;
+    }
+  });
+}
+
 }  // namespace
 
 int attn_o_part_slots(int hidden, int n_kv, int tokens) { return parts_slots(hidden, n_kv, tokens); }
@@ -1461,8 +1652,11 @@ int head_blocks(const DecodeArgs& a, const DecodeShape& sh) {
 bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, hipStream_t s) {
   return a.dtype == 0 ? qkv_t<float>(a, sh, L, first, s) : qkv_t<__half>(a, sh, L, first, s);
 }
-bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
-  return a.dtype == 0 ? attn_t<float>(a, sh, L, s) : attn_t<__half>(a, sh, L, s);
+bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool direct, hipStream_t s) {
+  return a.dtype == 0 ? attn_t<float>(a, sh, L, direct, s) : attn_t<__half>(a, sh, L, direct, s);
+}
+bool launch_merge_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
+  return a.dtype == 0 ? merge_o_t<float>(a, sh, L, s) : merge_o_t<__half>(a, sh, L, s);
 }
 bool launch_attn_merge(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   return a.dtype == 0 ? attn_merge_t<float>(a, sh, s) : attn_merge_t<__half>(a, sh, s);

@@ -19,6 +19,10 @@ enum CtrlWord : int {
 // multiple of 2048 (the argmax block reads key pairs).
 constexpr int kHeadMaxBlocks = 40960;
 
+// Floats per split-K attention partial state (per row, KV head, split and
+// query head of the group): max, sum, two pad words, 128 accumulators.
+constexpr int kAttnPartStride = 132;
+
 // Query rows one decode step can carry: 1 (a decode step) or 2 (a
 // two-token step: the last token and a draft of the next).  Per-row
 // activation buffers below hold kMaxTokens rows.
@@ -81,20 +85,27 @@ struct DecodeShape {
   int attn_splits;                                       // split-K blocks per KV head (grid.x)
   int attn_chunk;                                        // keys per split (a multiple of 16, >= 64)
   int head_waves;                                        // waves per head block (4, 8 or 16)
-  int fuse_attn_o;                                       // short contexts: fused attention + output GEMV
+  int fuse_attn_o;                                       // short contexts: fused attention + output GEMV;
+                                                         // longer ones: merge fused with the output GEMV
   int rows_attn_o;                                       // W_o rows per wave in the fused launch (4 or 8)
   int tokens = 1;                                        // query rows of the step (1 or kMaxTokens)
 };
 
 // Stage launches; each returns false if the shape is not compiled in.
 bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first_layer, hipStream_t s);
-bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
+// direct: a context within one split writes o itself (else every split
+// writes its partial state).
+bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool direct, hipStream_t s);
 // Combines the split-K partial states (needed when sh.attn_splits > 1).
 bool launch_attn_merge(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s);
 bool launch_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
 // Short contexts: attention fused with the output GEMV, which writes
 // per-KV-head partials into opart instead of x2.
 bool launch_attn_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
+// Longer contexts: the split-K merge fused with the output GEMV split by KV
+// head, writing opart like launch_attn_o (after launch_attn with direct =
+// false); same shapes as launch_attn_o.
+bool launch_merge_o(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s);
 // Partial slots per row (>= n_kv; slots past n_kv must hold zeros) the
 // gate/up prologue sums after a fused launch of `tokens` rows, or 0 if the
 // shape cannot be fused.  The slot count is the same for every row count

@@ -197,7 +197,7 @@ WsLayout ws_layout(const Dims& d) {
   w.opart_slots = std::max(d.nkv, attn_o_part_slots(d.H, d.nkv, 1));
   w.opart = take(T * w.opart_slots * d.H * 4);
   w.attn_splits_cap = attn_split_cap(d);
-  w.attn_part = take(T * d.nkv * w.attn_splits_cap * d.G * (2 + d.D) * 4);
+  w.attn_part = take(T * d.nkv * w.attn_splits_cap * d.G * kAttnPartStride * 4);
   w.am_part = take(T * kHeadMaxBlocks * 8);
   w.ctrl = take((size_t)kCtrlWords * 4);
   w.ids = take((size_t)(d.cap + 1) * 4);
@@ -232,7 +232,7 @@ struct wsg_model {
   bool has_output = false;
   int32_t* pin = nullptr;          // pinned staging: [0] token out, [1..] ids in
   bool use_graph = true;
-  std::map<int, hipGraphExec_t> graphs;   // key: graph_key(splits, tokens, fused, advance)
+  std::map<int, hipGraphExec_t> graphs;   // key: graph_key(splits, tokens, mode, advance)
   int timed_stage = -1;
   std::vector<hipEvent_t> ev;
   int ev_used = 0;
@@ -301,11 +301,17 @@ DecodeShape shape_for(const wsg_model* m, int tokens) {
   return sh;
 }
 
+// How a layer runs attention and the output projection.
+enum AttnMode : int {
+  kAttnSeparate = 0,   // split-K attention, merge launch, output GEMV
+  kAttnFused = 1,      // short contexts: attention fused with the KV-head-split output GEMV
+  kAttnMergeO = 2,     // longer contexts: split-K attention, then the merge fused with that GEMV
+};
+
 // All layers of one step of `tokens` rows; the last down projection
 // advances the position when no head follows (prompt rows before the
-// last).  Short contexts (fused) use the fused attention + output-projection
-// launch.
-bool enqueue_body(wsg_model* m, int splits, bool fused, bool advance, int tokens) {
+// last).
+bool enqueue_body(wsg_model* m, int splits, int mode, bool advance, int tokens) {
   DecodeShape sh = shape_for(m, tokens);
   sh.attn_splits = splits;
   const hipStream_t s = m->stream;
@@ -315,18 +321,22 @@ bool enqueue_body(wsg_model* m, int splits, bool fused, bool advance, int tokens
     const DecodeArgs& a = m->args;
     if (!timed(m, WSG_STAGE_QKV, stage_bytes(m, WSG_STAGE_QKV, l), [&] { return launch_qkv(a, sh, lp, l == 0, s); }))
       return false;
-    if (fused) {
+    if (mode == kAttnFused) {
       if (!timed(m, WSG_STAGE_ATTN, stage_bytes(m, WSG_STAGE_O, l), [&] { return launch_attn_o(a, sh, lp, s); }))
+        return false;
+    } else if (mode == kAttnMergeO) {
+      if (!timed(m, WSG_STAGE_ATTN, 0, [&] { return launch_attn(a, sh, lp, false, s); })) return false;
+      if (!timed(m, WSG_STAGE_O, stage_bytes(m, WSG_STAGE_O, l), [&] { return launch_merge_o(a, sh, lp, s); }))
         return false;
     } else {
       if (!timed(m, WSG_STAGE_ATTN, 0, [&] {
-            return launch_attn(a, sh, lp, s) && (splits == 1 || launch_attn_merge(a, sh, s));
+            return launch_attn(a, sh, lp, true, s) && (splits == 1 || launch_attn_merge(a, sh, s));
           }))
         return false;
       if (!timed(m, WSG_STAGE_O, stage_bytes(m, WSG_STAGE_O, l), [&] { return launch_o(a, sh, lp, s); })) return false;
     }
     if (!timed(m, WSG_STAGE_GATEUP, stage_bytes(m, WSG_STAGE_GATEUP, l),
-               [&] { return launch_gateup(a, sh, lp, fused, s); }))
+               [&] { return launch_gateup(a, sh, lp, mode != kAttnSeparate, s); }))
       return false;
     if (!timed(m, WSG_STAGE_DOWN, stage_bytes(m, WSG_STAGE_DOWN, l),
                [&] { return launch_down(a, sh, lp, advance && l == L - 1, s); }))
@@ -347,12 +357,14 @@ bool enqueue_argmax(wsg_model* m, int tokens) { return launch_argmax(m->args, sh
 // beyond this length the split-K path's parallelism over keys wins).
 constexpr int kFuseMaxKeys = 128;
 
-bool use_fused_attn_o(const wsg_model* m, int n_keys, int tokens) {
+int attn_mode(const wsg_model* m, int n_keys, int tokens) {
   const DecodeShape sh = shape_for(m, tokens);
-  // an int4 W_o slice of one KV head with 4 rows per wave leaves partial loads
-  if (m->d.q4 && m->d.G == 1 && sh.rows_attn_o == 4) return false;
-  return sh.fuse_attn_o && n_keys <= kFuseMaxKeys &&
-         attn_o_part_slots(m->d.H, m->d.nkv, tokens) > 0;
+  // the KV-head-split output GEMV: enabled, its partials fit the gate/up
+  // prologue, and (int4) whole 8-byte loads per lane
+  const bool split_o = sh.fuse_attn_o && attn_o_part_slots(m->d.H, m->d.nkv, tokens) > 0 &&
+                       !(m->d.q4 && m->d.G == 1 && sh.rows_attn_o == 4);
+  if (!split_o) return kAttnSeparate;
+  return n_keys <= kFuseMaxKeys ? kAttnFused : kAttnMergeO;
 }
 
 int splits_for(const wsg_model* m, int n_keys) {
@@ -389,8 +401,8 @@ wsg_status graph_for(wsg_model* m, int key, F&& enqueue, hipGraphExec_t* out) {
 }
 
 
-int graph_key(int splits, int tokens, bool fused, bool advance) {
-  return ((splits * 2 + (tokens - 1)) * 2 + (fused ? 1 : 0)) * 2 + (advance ? 1 : 0);
+int graph_key(int splits, int tokens, int mode, bool advance) {
+  return ((splits * 2 + (tokens - 1)) * 3 + mode) * 2 + (advance ? 1 : 0);
 }
 
 // Enqueue one step of `tokens` rows at the current device position (n_keys
@@ -398,18 +410,18 @@ int graph_key(int splits, int tokens, bool fused, bool advance) {
 // (final norm, vocabulary GEMV, argmax).
 wsg_status run_forward(wsg_model* m, bool head, int n_keys, int tokens = 1) {
   const int splits = splits_for(m, n_keys);
-  const bool fused = use_fused_attn_o(m, n_keys, tokens);
+  const int mode = attn_mode(m, n_keys, tokens);
   const bool advance = !head;
   (void)hipGetLastError();   // errors of earlier calls were reported by those calls
   m->ev_used = 0;
   m->timed_bytes_per_launch_sum = 0;
   if (!m->use_graph) {
-    if (!enqueue_body(m, splits, fused, advance, tokens))
+    if (!enqueue_body(m, splits, mode, advance, tokens))
       return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape");
   } else {
     hipGraphExec_t body = nullptr;
-    const wsg_status st = graph_for(m, graph_key(splits, tokens, fused, advance),
-                                    [&] { return enqueue_body(m, splits, fused, advance, tokens); }, &body);
+    const wsg_status st = graph_for(m, graph_key(splits, tokens, mode, advance),
+                                    [&] { return enqueue_body(m, splits, mode, advance, tokens); }, &body);
     if (st != WSG_OK) return st;
     WSG_HIP_CHECK(hipGraphLaunch(body, m->stream));
   }
