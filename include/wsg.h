@@ -350,7 +350,8 @@ wsg_status wsg_gemm_nt_f32(int32_t M, int32_t N, int32_t K, const float* d_A, co
  * Kernel Benchmark Was Measuring the System Cache, "The fix": the GEMV is
  * judged against what a plain read of the same cycling buffers reaches).
  * Reads all `bytes` of d_buf (16-byte aligned, bytes a positive multiple of
- * 16) once with 16-byte loads, one 4 KiB segment per wave; writes nothing
+ * 16) once with 16-byte non-temporal loads (the load form of the decode
+ * weight streams), one 4 KiB segment per wave; writes nothing
  * in practice (d_out, one float, is written only if the sum equals an
  * improbable constant).  Asynchronous on hip_stream. */
 wsg_status wsg_stream_read(const void* d_buf, int64_t bytes, float* d_out, void* hip_stream);

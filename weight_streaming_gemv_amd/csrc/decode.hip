@@ -90,6 +90,18 @@ struct Act {
   }
 };
 
+// Weight streams are read once per step and never reused within it, so
+// they are loaded non-temporally: on this part a read-only stream of the
+// vocabulary matrix runs at 6.8 TB/s with non-temporal loads against 6.2
+// TB/s with ordinary ones.  Activations, the K/V cache and partials (reused
+// from L2 by many blocks) keep ordinary loads.
+constexpr bool kWeightsNT = true;
+template <typename V>
+__device__ __forceinline__ V weight_load(const V* p) {
+  if constexpr (kWeightsNT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 // R weight rows held in registers (vectors in the lane layout of Act), so a
 // wave can put its first rows in flight before its prologue finishes.  TW is
 // the weight storage: TS itself, or packed FP32 (bf16w) with FP32
@@ -106,7 +118,7 @@ struct WRows {
     for (int r = 0; r < R; ++r) {
       const TW* wr = W + (size_t)min(row0 + r, M - 1) * K + lane * VEC;
 #pragma unroll
-      for (int c = 0; c < NV; ++c) v[r][c].template load<false>(wr + c * kWave * VEC);
+      for (int c = 0; c < NV; ++c) v[r][c].template load<kWeightsNT>(wr + c * kWave * VEC);
     }
   }
   template <typename A>
@@ -179,8 +191,8 @@ struct WRows<q4w, K, R> {
       const uint8_t* row = q4_row<K>(W, (size_t)min(row0 + r, M - 1));
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
-        q[r][c] = *reinterpret_cast<const u2_t*>(row + c * 512 + lane * 8);
-        s[r][c] = *reinterpret_cast<const uint16_t*>(row + Q4Row<K>::kWordBytes + 2 * (c * 16 + (lane >> 2)));
+        q[r][c] = weight_load(reinterpret_cast<const u2_t*>(row + c * 512 + lane * 8));
+        s[r][c] = weight_load(reinterpret_cast<const uint16_t*>(row + Q4Row<K>::kWordBytes + 2 * (c * 16 + (lane >> 2))));
       }
     }
   }
@@ -974,7 +986,7 @@ struct WoSlice {
     for (int t = 0; t < NLD; ++t) {
       const int f = t * kWave + lane;
       const int row = min(row0 + f / LPR, M - 1);
-      v[t].template load<false>(Wo + (size_t)row * ld + col0 + (f % LPR) * VEC);
+      v[t].template load<kWeightsNT>(Wo + (size_t)row * ld + col0 + (f % LPR) * VEC);
     }
   }
   // out[row0 + r] = (this slice's row r) . o + lane r's xb
@@ -1045,8 +1057,8 @@ struct WoSlice<q4w, G, R> {
       const int f = t * kWave + lane;
       const uint8_t* rp = reinterpret_cast<const uint8_t*>(Wo) + (size_t)min(row0 + f / LPR, M - 1) * rb;
       const int k = col0 + (f % LPR) * 16;
-      q[t] = *reinterpret_cast<const u2_t*>(rp + k / 2);
-      s[t] = *reinterpret_cast<const uint16_t*>(rp + ld / 2 + 2 * (k / 64));
+      q[t] = weight_load(reinterpret_cast<const u2_t*>(rp + k / 2));
+      s[t] = weight_load(reinterpret_cast<const uint16_t*>(rp + ld / 2 + 2 * (k / 64)));
     }
   }
   // out[row0 + r] = (this slice's row r) . o + lane r's xb

@@ -428,9 +428,9 @@ void gemv_q4_dispatch(int M, int K, int T, int R, int grid, int flags, const uin
 
 // ------------------------------------------------------ streaming ceiling
 // Read-only streaming reference for the cold-cache sweep: each wave sums
-// one contiguous 4 KiB segment of the buffer with 16-byte loads (the same
-// access size and per-wave footprint as a 1024-float GEMV row), all loads in
-// flight at once.  The sum is stored only if it equals an improbable value,
+// one contiguous 4 KiB segment of the buffer with 16-byte non-temporal
+// loads (the same access size, per-wave footprint and load form as a
+// 1024-float decode GEMV row), all loads in flight at once.  The sum is stored only if it equals an improbable value,
 // which keeps every load live without writing anything in practice.
 namespace {
 constexpr int kStreamSeg = 4096;            // bytes per wave
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(256) void k_stream_read(const f4_t* __restrict__ bu
   const int64_t base = wave * (kStreamSeg / 16) + lane;
   f4_t v[kStreamVec];
 #pragma unroll
-  for (int i = 0; i < kStreamVec; ++i) v[i] = buf[min(base + 64 * i, n_vec - 1)];
+  for (int i = 0; i < kStreamVec; ++i) v[i] = __builtin_nontemporal_load(buf + min(base + 64 * i, n_vec - 1));
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < kStreamVec; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);

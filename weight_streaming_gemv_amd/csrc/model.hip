@@ -723,9 +723,14 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
     for (int i = 0; i < pack_count(d); ++i) m->n_packed += f[i];
   }
   DecodeShape& sh = m->shape;
-  sh.rows_qkv = sh.rows_o = sh.rows_gu = sh.rows_down = sh.rows_head = 1;
+  sh.rows_qkv = sh.rows_o = sh.rows_gu = sh.rows_down = 1;
   sh.grid_qkv = sh.grid_o = sh.grid_gu = sh.grid_down = 0;
-  sh.grid_head = 0;   // one row per wave (the cold-cache sweep's best vocabulary shape)
+  // head: two rows per wave on the one-shot grid (18992 workgroups for the
+  // 151936-row vocabulary): with non-temporal weight loads the best of rows
+  // 1/2/4 x 4/8 waves x grids 4096..one-shot; each wave's activation and
+  // norm prologue then serves 8 KiB of weights
+  sh.rows_head = 2;
+  sh.grid_head = 0;
   sh.head_waves = 4;
   sh.attn_splits = 1;
   sh.attn_chunk = attn_chunk(d);

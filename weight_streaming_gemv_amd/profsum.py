@@ -75,8 +75,8 @@ def sweep_table(path):
     idx = defaultdict(list)
     for (name, blocks, gy), ds in g.items():
         idx[(short(name), blocks)].extend(ds)
-    print("| kernel | M x K | T | R | blocks | calls | median us | GB/s | % of 8 TB/s |")
-    print("|---|---|---|---|---|---|---|---|---|")
+    print("| kernel | M x K | T | R | NT | blocks | calls | median us | GB/s | % of 8 TB/s |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
     best = {}
     for dt, es, kname in (("f32", 4, "k_gemv_f32"), ("f16", 2, "k_gemv_f16"), ("q4g64", None, "k_gemv_q4")):
         shapes = Q4_SHAPES if dt == "q4g64" else GEMV_SHAPES
@@ -84,25 +84,26 @@ def sweep_table(path):
             nbytes = M * K // 2 + M * (K // 64) * 2 if dt == "q4g64" else M * K * es
             for T in (1, 2):
                 for R in (1, 2, 4, 8):
-                    seen = set()
-                    grids = (0, 256, 512) if dt == "q4g64" else ((0, 1280, 2048, 4096) if M > 100000 else (0,))
-                    for G in grids:
-                        one = _ceil(_ceil(M, R), 4)
-                        blocks = one if G == 0 or G >= one else G
-                        if blocks in seen:
-                            continue
-                        seen.add(blocks)
-                        key = (f"{kname}<{K}, {R}, {T}, false>", blocks)
-                        ds = idx.get(key)
-                        if not ds:
-                            continue
-                        us = statistics.median(ds) / 1e3
-                        gbps = nbytes / us / 1e3
-                        print(f"| {kname} | {M}x{K} | {T} | {R} | {blocks} | {len(ds)} | {us:.2f} | {gbps:.0f} | "
-                              f"{100 * gbps / HBM_PEAK_GBPS:.1f} |")
-                        k = (dt, M, K, T)
-                        if k not in best or us < best[k][0]:
-                            best[k] = (us, R, blocks, gbps)
+                    for nt in ("false", "true"):   # ordinary / non-temporal weight loads
+                        seen = set()
+                        grids = (0, 256, 512) if dt == "q4g64" else ((0, 1280, 2048, 4096) if M > 100000 else (0,))
+                        for G in grids:
+                            one = _ceil(_ceil(M, R), 4)
+                            blocks = one if G == 0 or G >= one else G
+                            if blocks in seen:
+                                continue
+                            seen.add(blocks)
+                            key = (f"{kname}<{K}, {R}, {T}, {nt}>", blocks)
+                            ds = idx.get(key)
+                            if not ds:
+                                continue
+                            us = statistics.median(ds) / 1e3
+                            gbps = nbytes / us / 1e3
+                            print(f"| {kname} | {M}x{K} | {T} | {R} | {'y' if nt == 'true' else 'n'} | {blocks} | "
+                                  f"{len(ds)} | {us:.2f} | {gbps:.0f} | {100 * gbps / HBM_PEAK_GBPS:.1f} |")
+                            k = (dt, M, K, T)
+                            if k not in best or us < best[k][0]:
+                                best[k] = (us, R, blocks, gbps)
     print()
     print("Best per shape (kernel-only):")
     print()
