@@ -15,8 +15,9 @@ enum CtrlWord : int {
 };
 
 // The head kernel runs at most kHeadMaxBlocks blocks (one argmax key each;
-// one row per wave for the 151936-row vocabulary is 37984 blocks); a
-// multiple of 2048 (the argmax block reads key pairs).
+// one row per wave for the 151936-row vocabulary would be 37984 blocks, the
+// default two rows per wave 18992); a multiple of 2048 (the argmax block
+// reads key pairs).
 constexpr int kHeadMaxBlocks = 40960;
 
 // Floats per split-K attention partial state (per row, KV head, split and
