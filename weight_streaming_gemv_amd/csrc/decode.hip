@@ -668,16 +668,22 @@ __global__ void k_set_pos(int32_t* ctrl, int pos) {
 // Lane layout for one 128-wide head row: a row of 16 lanes covers one key;
 // lane sl of the row holds dims [4sl, 4sl+4) and [64+4sl, 64+4sl+4), so both
 // members of every rotary pair (i, i+64) sit in the same lane.
-template <typename TS>
+// NT: non-temporal loads (cached keys that no other block of the launch reads).
+template <typename TS, bool NT = false>
 __device__ __forceinline__ void load_head8(const TS* p, int sl, float (&v)[8]) {
+  auto ld = [](const auto* q) {
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
+  };
   if constexpr (sizeof(TS) == 4) {
-    const float4 lo = *reinterpret_cast<const float4*>(p + 4 * sl);
-    const float4 hi = *reinterpret_cast<const float4*>(p + 64 + 4 * sl);
+    const f4_t lo = ld(reinterpret_cast<const f4_t*>(p + 4 * sl));
+    const f4_t hi = ld(reinterpret_cast<const f4_t*>(p + 64 + 4 * sl));
     v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
     v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
   } else {
-    const uint2 lo = *reinterpret_cast<const uint2*>(p + 4 * sl);
-    const uint2 hi = *reinterpret_cast<const uint2*>(p + 64 + 4 * sl);
+    typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+    const u2_t lo = ld(reinterpret_cast<const u2_t*>(p + 4 * sl));
+    const u2_t hi = ld(reinterpret_cast<const u2_t*>(p + 64 + 4 * sl));
     const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -769,7 +775,7 @@ static_assert(kPartStride == kPartAcc + kD && kPartStride % 4 == 0, "partial sta
 // row is the second of a two-token step and also folds in the first row's
 // key and value (slot p - 1, written by another block of the same launch),
 // recomputed here from the first row's projections.
-template <typename TS, int G, int NR, bool PREV>
+template <typename TS, int G, int NR, bool PREV, bool NTKV = false>
 struct HeadAttn {
   float q[G][8], kc[8], vc[8], k4[4][8], v4[4][8], c[4], s[4], gq[8], gk[8];
   float kp[PREV ? 8 : 1], vp[PREV ? 8 : 1], cp[PREV ? 4 : 1], sp[PREV ? 4 : 1];
@@ -781,8 +787,8 @@ struct HeadAttn {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kk = min(k_begin + sid + NR * u, cap - 1);
-      load_head8<TS>(kh + (size_t)kk * kD, sl, k4[u]);
-      load_head8<TS>(vh + (size_t)kk * kD, sl, v4[u]);
+      load_head8<TS, NTKV>(kh + (size_t)kk * kD, sl, k4[u]);
+      load_head8<TS, NTKV>(vh + (size_t)kk * kD, sl, v4[u]);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) load_head8<TS>(qkv + (size_t)(j * G + g) * kD, sl, q[g]);
@@ -835,8 +841,8 @@ struct HeadAttn {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (key + NR * u < k_stop) {
-          load_head8<TS>(kh + (size_t)(key + NR * u) * kD, sl, k4[u]);
-          load_head8<TS>(vh + (size_t)(key + NR * u) * kD, sl, v4[u]);
+          load_head8<TS, NTKV>(kh + (size_t)(key + NR * u) * kD, sl, k4[u]);
+          load_head8<TS, NTKV>(vh + (size_t)(key + NR * u) * kD, sl, v4[u]);
         }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -922,7 +928,9 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
   // Every split covers the fixed key range [split*chunk, split*chunk + chunk)
   // (chunk is a per-model constant), so its first keys can be loaded before p.
   const int k_begin = split * chunk;
-  HeadAttn<TS, G, 16, PREV> ha;
+  // one query row: each cached key is read by exactly one block of this
+  // launch (two rows read it twice: ordinary loads, so the second may hit L2)
+  HeadAttn<TS, G, 16, PREV, (T == 1)> ha;
   ha.prefetch(qkv + (size_t)t * M, kh, vh, q_norm, k_norm, rope_cur + t * kD, j, Q, KV, cap, k_begin, sid, sl);
   ha.prefetch_prev(qkv, rope_cur, j, Q, KV, sl);   // (unused by row 0; no branch around loads)
   // keep the scheduler from moving work that waits on the first loads
