@@ -742,6 +742,12 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   // argmax would reduce four times as many block keys.
   m->shape2 = sh;
   m->shape2.rows_head = 4;
+  // Gate/up and QKV loop on 256 and 512 blocks: a wave that serves two
+  // activation rows streams its weights long enough to cover the per-wave
+  // prologue (28-layer kernel-trace sweep: 858 against 881 us per step at
+  // the one-shot grids; one-token steps keep the one-shot grids)
+  m->shape2.grid_gu = 256;
+  m->shape2.grid_qkv = 512;
   if (d.q4) {
     // int4 rows are short (544 bytes at width 1024): the head loops over
     // four rows per wave on 2048 blocks, so each wave's activation and norm
