@@ -629,6 +629,34 @@ def int4_decoder(torch, wsg, shape, steps=5, warmup=2, n_check=8):
                          "8/16, 32/8, 32/16, tokenwise prompt")}
 
 
+def prefill_only(torch, wsg, shape, w, chunk=1024, trials=3):
+    """The held-out 4096-id prompt's chunked prefill alone (the prefill half of the
+    long-document workload, Benchmark methodology, "Long-document chunked prefill"),
+    for counter runs: one warm-up and ``trials`` timed prefills, no decode.  The
+    matrix work per prefill is the four projections' 2*rows*N*K flops per chunk
+    plus the causal attention's score and value products."""
+    from synth import PROMPT_SEEDS, prompt_ids
+    held = prompt_ids(PROMPT_SEEDS["heldout"], 4096, shape.vocab)
+    model = wsg.Model(shape, w, max_context=len(held) + 1, prefill_chunk=chunk)
+    times = []
+    for i in range(1 + trials):
+        model.reset()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        model.prefill(held)
+        torch.cuda.synchronize()
+        if i:
+            times.append(time.perf_counter() - t)
+    H, I, D = shape.hidden, shape.intermediate, shape.head_dim
+    M = (shape.n_q_heads + 2 * shape.n_kv_heads) * D
+    n = len(held)
+    proj = 2 * n * shape.n_layers * (M * H + H * shape.n_q_heads * D + 2 * I * H + H * I)
+    attn = 2 * 2 * shape.n_layers * shape.n_q_heads * D * (n * (n + 1) // 2)
+    model.close()
+    return {"prompt": n, "chunk": chunk, "prefill_ms_median": round(statistics.median(times) * 1e3, 2),
+            "projection_flop": proj, "attention_flop": attn}
+
+
 def long_context(torch, wsg, shape, w, validate_outputs=32, trials=5, warmup=2):
     """Long-document workload (Benchmark methodology, "Long-document chunked prefill").
 
@@ -803,6 +831,9 @@ def main(argv=None):
                     help="two-token step (speculative verify pass): fixed-slot latency and generation")
     ap.add_argument("--int4", choices=["on", "off", "only"], default="on",
                     help="short-prompt workload on an int4 (group-64) model of the same shape")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the held-out 4096-id prompt's chunk-1024 prefill, 1 warm-up + 3 timed "
+                         "(profiling runs: MFMA counters; no value is published)")
     ap.add_argument("--no-oracle", action="store_true",
                     help="skip validation and the CPU baseline (profiling runs only; no value is published)")
     args = ap.parse_args(argv)
@@ -841,6 +872,9 @@ def main(argv=None):
     t = time.perf_counter()
     w = model_weights(shape, seed=0)
     log(f"weights generated in {time.perf_counter() - t:.1f} s")
+    if args.prefill_only:
+        print(json.dumps({"prefill_only": prefill_only(torch, wsg, shape, w)}), flush=True)
+        return 0
     prompt32 = prompt_ids(PROMPT_SEEDS["short"], 32, shape.vocab)
     prompts = {8: prompt32[:8], 32: prompt32}
     model = wsg.Model(shape, w, max_context=cap, prefill_chunk=32)

@@ -7,7 +7,11 @@
     shape are template arguments), with workgroups per launch;
 ``python -m weight_streaming_gemv_amd.profsum sweep <run_kernel_trace.csv>``
     kernel-only GB/s of every cold-sweep configuration (bench.py --sweep-only),
-    matched to its launch by kernel template arguments and grid size.
+    matched to its launch by kernel template arguments and grid size;
+``python -m weight_streaming_gemv_amd.profsum counters <run_counter_collection.csv>``
+    per template instance and grid size (threads): dispatches, then the median
+    per dispatch and the total over all dispatches of every collected counter
+    (a ``rocprofv3 --pmc`` run).
 
 Durations are the trace's begin/end timestamps (device time of each dispatch,
 no launch gaps).
@@ -63,6 +67,24 @@ def instance_table(path):
     for s, (n, wg), ds in rows:
         print(f"| `{n}` | {wg} | {len(ds)} | {statistics.median(ds) / 1e3:.2f} | "
               f"{statistics.fmean(ds) / 1e3:.2f} | {s / 1e6:.2f} |")
+
+
+def counter_table(path):
+    vals = defaultdict(lambda: defaultdict(list))
+    names = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            c = r["Counter_Name"]
+            if c not in names:
+                names.append(c)
+            vals[(short(r["Kernel_Name"]), int(r["Grid_Size"]))][c].append(float(r["Counter_Value"]))
+    rows = sorted(vals.items(), key=lambda kv: -sum(kv[1][names[0]]))
+    print("| kernel instance | grid | dispatches | " + " | ".join(f"{c} median | {c} total" for c in names) + " |")
+    print("|---|---|---|" + "---|---|" * len(names))
+    for (n, grid), cs in rows:
+        cells = " | ".join(f"{statistics.median(cs[c]):.6g} | {sum(cs[c]):.6g}" if cs[c] else "- | -"
+                           for c in names)
+        print(f"| `{n}` | {grid} | {len(cs[names[0]])} | {cells} |")
 
 
 def _ceil(a, b):
@@ -125,4 +147,5 @@ if __name__ == "__main__":
     import os
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     mode, path = sys.argv[1], sys.argv[2]
-    {"decode": decode_table, "instances": instance_table, "sweep": sweep_table}[mode](path)
+    {"decode": decode_table, "instances": instance_table, "sweep": sweep_table,
+     "counters": counter_table}[mode](path)
