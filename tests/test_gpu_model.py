@@ -95,14 +95,61 @@ def test_mini_split_attention_long_prompt(mini_w, n_prompt):
 
 @pytest.mark.parametrize("n_prompt", [600, 1000])
 def test_mini_many_splits(mini_w, n_prompt):
-    """More than 8 attention splits (split counts rounded to multiples of 8,
-    so some blocks find no keys), reached through chunked prefill."""
+    """Many attention splits (16 and 16 to 17 per KV head at 64 keys each),
+    reached through chunked prefill."""
     import weight_streaming_gemv_amd as wsg
     cap = 1100
     m = wsg.Model(MINI, mini_w, max_context=cap, prefill_chunk=128)
     orc = oracle.OracleModel(MINI, mini_w, cap)
     prompt = prompt_ids(10, n_prompt, MINI.vocab)
     lockstep(m, orc, prompt, 5, label=f"mini splits n={n_prompt}")
+    m.close()
+
+
+# Eight KV heads (one query head each) on a narrow residual: the attention
+# split size grows with the context once 24 splits per KV head would not
+# cover it (more than 1536 keys), at a cost the oracle finishes in seconds.
+WIDE_KV = ModelShape(n_layers=1, hidden=256, intermediate=512, n_q_heads=8, n_kv_heads=8, head_dim=128, vocab=500)
+
+
+@pytest.mark.parametrize("n_prompt", [1600, 3300])
+def test_long_context_split_sizes(n_prompt):
+    """Contexts whose split-K attention blocks take 80 keys (1600: each key-row
+    folds a second group of keys, the last one partial) and 144 keys (3300:
+    three groups per key-row); greedy steps in lockstep, then two-token steps
+    (an accepted and a rejected draft) at the same context."""
+    import weight_streaming_gemv_amd as wsg
+    sh = WIDE_KV
+    w = model_weights(sh, seed=3)
+    cap = 3328
+    m = wsg.Model(sh, w, max_context=cap, prefill_chunk=512)
+    orc = oracle.OracleModel(sh, w, cap)
+    prompt = prompt_ids(11, n_prompt, sh.vocab)
+    toks, _, _ = lockstep(m, orc, prompt, 4, label=f"wide-kv n={n_prompt}")
+    last = toks[-1]
+    for s, accept in enumerate((True, False)):
+        p = orc.pos
+        ref0 = orc.forward_rows([last])
+        g0 = oracle.argmax_lowest(ref0)
+        draft = g0 if accept else (g0 + 1) % sh.vocab
+        announce(f"wide-kv n={n_prompt} step2 {s} p={p}")
+        (t0, t1), n = m.step2(draft)
+        ref1 = orc.forward_rows([draft])
+        got = _np(m.logits())
+        for row, r in ((0, ref0), (1, ref1)):
+            ok, err, worst = close_rel(got[row], r, 1e-3, 1e-3)
+            assert ok, f"step2 {s} row {row}: logits off by {err:.3e} at {worst}"
+        k, v, _ = m.kv(0)
+        for g_, r_ in ((k, orc.k_cache[0]), (v, orc.v_cache[0])):
+            ok, err, _ = close_rel(_np(g_[:, p:p + 2]), r_[:, p:p + 2], 1e-3, 1e-3)
+            assert ok, f"step2 {s}: K/V off by {err:.3e}"
+        assert t0 == g0 and n == (2 if accept else 1)
+        if accept:
+            assert t1 == oracle.argmax_lowest(ref1)
+            last = t1
+        else:
+            orc.pos = p + 1
+            last = t0
     m.close()
 
 

@@ -832,21 +832,36 @@ struct HeadAttn {
       for (int i = 0; i < 8; ++i) q[g][i] *= qscale;
     }
     st.init();
-    // the first four keys of the key-row are in registers already; longer
-    // ranges continue in groups of four with all loads in flight first
+    // Keys in groups of 4*NR (four per key-row); the first group is in
+    // registers already.  While a group is folded in, the next one's loads
+    // are in flight: the test for a next group is uniform over the block, so
+    // both branches issue a fixed number of loads and the wait before the
+    // fold covers only the older group.  Keys of the next group past the range
+    // are read at its last key (in bounds, from cache) and not used.
+    for (int base = k_begin;; base += 4 * NR) {
+      if (base + 4 * NR < k_stop) {
+        float kn[4][8], vn[4][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (k_begin + sid + NR * u < k_stop) st.add(q, k4[u], v4[u]);
-    for (int key = k_begin + sid + 4 * NR; key < k_stop; key += 4 * NR) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (key + NR * u < k_stop) {
-          load_head8<TS, NTKV>(kh + (size_t)(key + NR * u) * kD, sl, k4[u]);
-          load_head8<TS, NTKV>(vh + (size_t)(key + NR * u) * kD, sl, v4[u]);
+        for (int u = 0; u < 4; ++u) {
+          const int key = min(base + 4 * NR + sid + NR * u, k_stop - 1);
+          load_head8<TS, NTKV>(kh + (size_t)key * kD, sl, kn[u]);
+          load_head8<TS, NTKV>(vh + (size_t)key * kD, sl, vn[u]);
         }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (key + NR * u < k_stop) st.add(q, k4[u], v4[u]);
+        for (int u = 0; u < 4; ++u) st.add(q, k4[u], v4[u]);   // a whole group: base + 4*NR < k_stop
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            k4[u][i] = kn[u][i];
+            v4[u][i] = vn[u][i];
+          }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (base + sid + NR * u < k_stop) st.add(q, k4[u], v4[u]);
+        break;
+      }
     }
     if constexpr (PREV) {
       if (has_prev) {

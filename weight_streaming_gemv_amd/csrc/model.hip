@@ -152,9 +152,11 @@ int pack_lossless(const uint8_t* src_bytes, uint8_t* dst_bytes, size_t elems) {
   return 1;
 }
 
-// Decode attention splits the keys into fixed ranges of attn_chunk(d)
-// keys (at least 64, and at most 128 splits for the whole capacity), so a
-// block's key range does not depend on the position.
+// Decode attention splits the keys into ranges of a fixed size per captured
+// graph (so a block's key range does not depend on the position read on
+// the device): at least attn_chunk(d) keys (64, or more so that the whole
+// capacity needs at most 128 splits), and longer ranges for longer contexts
+// (attn_chunk_for).
 constexpr int kMaxAttnSplits = 128;
 
 int attn_chunk(const Dims& d) {
@@ -208,7 +210,7 @@ WsLayout ws_layout(const Dims& d) {
   return w;
 }
 
-int pow2_ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace
 }  // namespace wsg
@@ -232,7 +234,7 @@ struct wsg_model {
   bool has_output = false;
   int32_t* pin = nullptr;          // pinned staging: [0] token out, [1..] ids in
   bool use_graph = true;
-  std::map<int, hipGraphExec_t> graphs;   // key: graph_key(splits, tokens, mode, advance)
+  std::map<uint64_t, hipGraphExec_t> graphs;   // key: graph_key(splits, chunk, tokens, mode, advance)
   int timed_stage = -1;
   std::vector<hipEvent_t> ev;
   int ev_used = 0;
@@ -311,9 +313,10 @@ enum AttnMode : int {
 // All layers of one step of `tokens` rows; the last down projection
 // advances the position when no head follows (prompt rows before the
 // last).
-bool enqueue_body(wsg_model* m, int splits, int mode, bool advance, int tokens) {
+bool enqueue_body(wsg_model* m, int splits, int chunk, int mode, bool advance, int tokens) {
   DecodeShape sh = shape_for(m, tokens);
   sh.attn_splits = splits;
+  sh.attn_chunk = chunk;
   const hipStream_t s = m->stream;
   const int L = m->d.L;
   for (int l = 0; l < L; ++l) {
@@ -348,10 +351,6 @@ bool enqueue_body(wsg_model* m, int splits, int mode, bool advance, int tokens) 
 bool enqueue_head(wsg_model* m, int tokens) { return launch_head(m->args, shape_for(m, tokens), m->stream); }
 bool enqueue_argmax(wsg_model* m, int tokens) { return launch_argmax(m->args, shape_for(m, tokens), m->stream); }
 
-// Attention blocks per KV head for n_keys: the splits the context needs,
-// rounded up to a power of two up to 8 and to a multiple of 8 beyond (one
-// captured graph per value; the rounded-up blocks find no keys and write
-// nothing, but still issue their speculative loads).
 // Contexts up to kFuseMaxKeys keys run attention fused with the output
 // projection (each of a KV head's 32 blocks reads that head's K/V prefix;
 // beyond this length the split-K path's parallelism over keys wins).
@@ -367,11 +366,26 @@ int attn_mode(const wsg_model* m, int n_keys, int tokens) {
   return n_keys <= kFuseMaxKeys ? kAttnFused : kAttnMergeO;
 }
 
-int splits_for(const wsg_model* m, int n_keys) {
-  const int need = (n_keys + m->shape.attn_chunk - 1) / m->shape.attn_chunk;
-  const int want = need <= 8 ? pow2_ceil(need) : (need + 7) / 8 * 8;
-  return want < m->wl.attn_splits_cap ? want : m->wl.attn_splits_cap;
+// Keys per split-K attention block for n_keys: the model's minimum, or more
+// so that about kAttnTargetBlocks blocks (over all KV heads) cover the
+// context, in multiples of 16 keys.  Every block has a fixed overhead (its
+// query, the merge of its 16 key-rows, its partial state, and one more
+// state for the merge launch to read), so fewer, longer blocks win once
+// there are enough of them to keep the memory system busy; a sweep of
+// fixed sizes on the 8-KV-head model at 1.1k / 2.1k / 4.2k keys was best
+// at 64 / 96 / 192 keys, i.e. 20-24 splits per head.
+constexpr int kAttnTargetBlocks = 192;
+
+int attn_chunk_for(const wsg_model* m, int n_keys) {
+  const int per_head = std::max(1, kAttnTargetBlocks / m->d.nkv);
+  const int c = (ceil_div(n_keys, per_head) + 15) & ~15;
+  return std::max(m->shape.attn_chunk, c);
 }
+
+// Attention blocks per KV head: exactly the splits the context needs (one
+// captured graph per (splits, chunk) pair).  With chunk >= attn_chunk(d)
+// this is at most attn_split_cap(d).
+int splits_for(int n_keys, int chunk) { return ceil_div(n_keys, chunk); }
 
 void drop_graphs(wsg_model* m) {
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
@@ -380,7 +394,7 @@ void drop_graphs(wsg_model* m) {
 
 // Capture (once) and return the graph for `key`, built by `enqueue`.
 template <typename F>
-wsg_status graph_for(wsg_model* m, int key, F&& enqueue, hipGraphExec_t* out) {
+wsg_status graph_for(wsg_model* m, uint64_t key, F&& enqueue, hipGraphExec_t* out) {
   auto it = m->graphs.find(key);
   if (it != m->graphs.end()) { *out = it->second; return WSG_OK; }
   WSG_HIP_CHECK(hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
@@ -401,27 +415,28 @@ wsg_status graph_for(wsg_model* m, int key, F&& enqueue, hipGraphExec_t* out) {
 }
 
 
-int graph_key(int splits, int tokens, int mode, bool advance) {
-  return ((splits * 2 + (tokens - 1)) * 3 + mode) * 2 + (advance ? 1 : 0);
+uint64_t graph_key(int splits, int chunk, int tokens, int mode, bool advance) {
+  return ((((uint64_t)chunk << 20 | (uint64_t)splits) * 2 + (tokens - 1)) * 3 + mode) * 2 + (advance ? 1 : 0);
 }
 
 // Enqueue one step of `tokens` rows at the current device position (n_keys
 // = the last row's position + 1): the layer body and, if `head`, the head
 // (final norm, vocabulary GEMV, argmax).
 wsg_status run_forward(wsg_model* m, bool head, int n_keys, int tokens = 1) {
-  const int splits = splits_for(m, n_keys);
+  const int chunk = attn_chunk_for(m, n_keys);
+  const int splits = splits_for(n_keys, chunk);
   const int mode = attn_mode(m, n_keys, tokens);
   const bool advance = !head;
   (void)hipGetLastError();   // errors of earlier calls were reported by those calls
   m->ev_used = 0;
   m->timed_bytes_per_launch_sum = 0;
   if (!m->use_graph) {
-    if (!enqueue_body(m, splits, mode, advance, tokens))
+    if (!enqueue_body(m, splits, chunk, mode, advance, tokens))
       return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape");
   } else {
     hipGraphExec_t body = nullptr;
-    const wsg_status st = graph_for(m, graph_key(splits, tokens, mode, advance),
-                                    [&] { return enqueue_body(m, splits, mode, advance, tokens); }, &body);
+    const wsg_status st = graph_for(m, graph_key(splits, chunk, tokens, mode, advance),
+                                    [&] { return enqueue_body(m, splits, chunk, mode, advance, tokens); }, &body);
     if (st != WSG_OK) return st;
     WSG_HIP_CHECK(hipGraphLaunch(body, m->stream));
   }
