@@ -775,7 +775,7 @@ static_assert(kPartStride == kPartAcc + kD && kPartStride % 4 == 0, "partial sta
 // row is the second of a two-token step and also folds in the first row's
 // key and value (slot p - 1, written by another block of the same launch),
 // recomputed here from the first row's projections.
-template <typename TS, int G, int NR, bool PREV, bool NTKV = false>
+template <typename TS, int G, int NR, bool PREV, bool NTKV = false, bool PIPE = false>
 struct HeadAttn {
   float q[G][8], kc[8], vc[8], k4[4][8], v4[4][8], c[4], s[4], gq[8], gk[8];
   float kp[PREV ? 8 : 1], vp[PREV ? 8 : 1], cp[PREV ? 4 : 1], sp[PREV ? 4 : 1];
@@ -833,34 +833,54 @@ struct HeadAttn {
     }
     st.init();
     // Keys in groups of 4*NR (four per key-row); the first group is in
-    // registers already.  While a group is folded in, the next one's loads
-    // are in flight: the test for a next group is uniform over the block, so
-    // both branches issue a fixed number of loads and the wait before the
-    // fold covers only the older group.  Keys of the next group past the range
-    // are read at its last key (in bounds, from cache) and not used.
-    for (int base = k_begin;; base += 4 * NR) {
-      if (base + 4 * NR < k_stop) {
-        float kn[4][8], vn[4][8];
+    // registers already.
+    if constexpr (!PIPE) {
+      // Short ranges (the fused launch): each further group's loads are all
+      // issued, then folded in.
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int key = min(base + 4 * NR + sid + NR * u, k_stop - 1);
-          load_head8<TS, NTKV>(kh + (size_t)key * kD, sl, kn[u]);
-          load_head8<TS, NTKV>(vh + (size_t)key * kD, sl, vn[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) st.add(q, k4[u], v4[u]);   // a whole group: base + 4*NR < k_stop
+      for (int u = 0; u < 4; ++u)
+        if (k_begin + sid + NR * u < k_stop) st.add(q, k4[u], v4[u]);
+      for (int key = k_begin + sid + 4 * NR; key < k_stop; key += 4 * NR) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            k4[u][i] = kn[u][i];
-            v4[u][i] = vn[u][i];
+          if (key + NR * u < k_stop) {
+            load_head8<TS, NTKV>(kh + (size_t)(key + NR * u) * kD, sl, k4[u]);
+            load_head8<TS, NTKV>(vh + (size_t)(key + NR * u) * kD, sl, v4[u]);
           }
-      } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (base + sid + NR * u < k_stop) st.add(q, k4[u], v4[u]);
-        break;
+          if (key + NR * u < k_stop) st.add(q, k4[u], v4[u]);
+      }
+    } else {
+      // Split-K ranges: while a group is folded in, the next one's loads are
+      // in flight.  The test for a next group is uniform over the block, so
+      // both branches issue a fixed number of loads and the wait before the
+      // fold covers only the older group.  Keys of the next group past the
+      // range are read at its last key (in bounds, from cache) and not used.
+      for (int base = k_begin;; base += 4 * NR) {
+        if (base + 4 * NR < k_stop) {
+          float kn[4][8], vn[4][8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int key = min(base + 4 * NR + sid + NR * u, k_stop - 1);
+            load_head8<TS, NTKV>(kh + (size_t)key * kD, sl, kn[u]);
+            load_head8<TS, NTKV>(vh + (size_t)key * kD, sl, vn[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) st.add(q, k4[u], v4[u]);   // a whole group: base + 4*NR < k_stop
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              k4[u][i] = kn[u][i];
+              v4[u][i] = vn[u][i];
+            }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (base + sid + NR * u < k_stop) st.add(q, k4[u], v4[u]);
+          break;
+        }
       }
     }
     if constexpr (PREV) {
@@ -945,7 +965,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
   const int k_begin = split * chunk;
   // one query row: each cached key is read by exactly one block of this
   // launch (two rows read it twice: ordinary loads, so the second may hit L2)
-  HeadAttn<TS, G, 16, PREV, (T == 1)> ha;
+  HeadAttn<TS, G, 16, PREV, (T == 1), true> ha;
   ha.prefetch(qkv + (size_t)t * M, kh, vh, q_norm, k_norm, rope_cur + t * kD, j, Q, KV, cap, k_begin, sid, sl);
   ha.prefetch_prev(qkv, rope_cur, j, Q, KV, sl);   // (unused by row 0; no branch around loads)
   // keep the scheduler from moving work that waits on the first loads
