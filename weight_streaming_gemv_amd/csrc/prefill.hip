@@ -384,12 +384,17 @@ __global__ __launch_bounds__(256) void k_rows_swiglu(const float* __restrict__ G
 // tile across the rows of a query tile, online softmax in the log2 domain).
 //
 // Both products run on v_mfma_f32_16x16x4f32, in transposed form so the
-// probabilities never leave registers.  A block holds 64 query vectors
-// (64/G rows x G heads) and 8 waves in two groups of four: wave w of group
-// c owns vectors [16w, 16w + 16) (vector v = row * G + head) and the key
-// tiles 2i + c, so two waves share each SIMD and each K/V tile pair is read
-// from memory once per block.  Per tile of 32 keys (K row-major and V
-// transposed in LDS):
+// probabilities never leave registers.  The chunk's query vectors (vector
+// v = row * G + head) are cut into tiles of 32 (32/G rows), and block b
+// takes tiles b and n_tiles - 1 - b: under the causal mask a tile's work
+// grows with its last row, so every block gets the same total and no CU
+// waits for the longest tile (all blocks run at once, one per CU).  The 8
+// waves: wave w serves tile w >> 2 (waves w and w + 4 share a SIMD, so
+// the later tile's keys past the earlier tile's range keep every SIMD
+// busy), key group c = (w >> 1) & 1 (the key tiles 2i + c), and vectors
+// [16h, 16h + 16) of its tile, h = w & 1.  Each K/V tile pair is staged once
+// per block and serves both query tiles.  Per tile of 32 keys (K row-major
+// and V transposed in LDS):
 //   S^T[key][v] = sum_d K[key][d] Q[v][d]     (A = K from LDS, B = Q in registers)
 //   O^T[d][v]  += sum_key V^T[d][key] P^T[key][v]
 // MFMA 16x16x4 layout (lane l): A (row l%16, k slot l/16), B (k slot l/16,
@@ -399,9 +404,9 @@ __global__ __launch_bounds__(256) void k_rows_swiglu(const float* __restrict__ G
 // accumulator of lane l: P^T is the B operand as computed.  Every lane owns
 // one query vector (column l%16), so its softmax state is per lane; a
 // column's 16 keys of a half sit in the 4 lanes l%16 + 16q (xor 16, 32).
-// At the end group 1 hands its (max, sum, O^T) states to group 0 through
-// LDS, which merges them and writes O.
-constexpr int kAQV = 64;           // query vectors per block
+// At the end key group 1 hands its (max, sum, O^T) states to key group 0
+// through LDS, which merges them and writes O.
+constexpr int kAQV = 32;           // query vectors per tile (two tiles per block)
 constexpr int kAKT = 32;           // keys per tile
 constexpr int kKsRow = kD + 4;     // K tile row (floats): conflict-free 16-byte reads
 constexpr int kVtRow = kAKT + 4;   // V^T tile row
@@ -413,23 +418,31 @@ __global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __re
                                                                const float* __restrict__ k_cache,
                                                                const float* __restrict__ v_cache, int n, int n_q,
                                                                int n_kv, int p0, int cap, float* __restrict__ O) {
-  constexpr int BR = kAQV / G;       // rows per block
+  constexpr int BR = kAQV / G;       // rows per tile
   __shared__ float Ks[2][kAKT * kKsRow];
   __shared__ float Vt[2][kD * kVtRow];
   static_assert(4 * kWave * kStateRow <= 2 * kD * kVtRow, "merge records fit in the V tiles");
   const int j = blockIdx.y;
-  const int r0 = blockIdx.x * BR;
+  const int n_tiles = (n + BR - 1) / BR;
+  const int tile_a = blockIdx.x, tile_b = n_tiles - 1 - blockIdx.x;   // tile_a <= tile_b
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = wave >> 2, wv = wave & 3;
+  const int ts = wave >> 2, grp = (wave >> 1) & 1, wh = wave & 1;
   const int li = lane & 15, lq = lane >> 4;
   const int width = (n_q + 2 * n_kv) * kD;
   const float qscale = kLog2e / sqrtf((float)kD);
+  // an odd tile count leaves the middle tile to the first half of the block
+  const bool tile_on = ts == 0 || tile_b > tile_a;
+  const int tile = ts == 0 ? tile_a : tile_b;
+  // keys a tile needs: through its last valid row's position
+  const int keys_a = p0 + min(n, (tile_a + 1) * BR);
+  const int keys_b = p0 + min(n, (tile_b + 1) * BR);
+  const int my_keys = tile_on ? (ts == 0 ? keys_a : keys_b) : 0;
 
   // this lane's query vector
-  const int v = wv * 16 + li;
+  const int v = wh * 16 + li;
   const int rr = v / G, g = v - rr * G;
-  const int row = r0 + rr;
-  const bool row_ok = row < n;
+  const int row = tile * BR + rr;
+  const bool row_ok = tile_on && row < n;
   const int my_pos = p0 + row;
   float qf[32];
   {
@@ -441,8 +454,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __re
       for (int i = 0; i < 4; ++i) qf[4 * t + i] = x[i] * qscale;
     }
   }
-  const int last_row = min(n, r0 + BR) - 1;
-  const int n_keys = p0 + last_row + 1;   // keys any row of the block needs
+  const int n_keys = keys_b;   // keys any row of the block needs (tile b ends last)
 
   f4v_t oacc[8];
 #pragma unroll
@@ -485,22 +497,31 @@ __global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __re
     // in-bounds pair, unused, to keep the loop free of branches)
     WSG_ATTN_LOAD(min(k0 + 2 * kAKT, n_keys - 1))
 #undef WSG_ATTN_LOAD
-    const int kt = k0 + kAKT * grp;   // this group's tile
-    if (kt < n_keys) {                // wave-uniform
+    const int kt = k0 + kAKT * grp;   // this group's key tile
+    if (kt < my_keys) {               // wave-uniform
       const float* ks = Ks[grp];
       const float* vt = Vt[grp];
-      // S^T for the two 16-key halves
+      // S^T for the two 16-key halves.  Each product reads all of its A
+      // operands from LDS first (16 reads in flight), then runs its 64
+      // MFMAs, so the waits for the reads overlap the matrix pipe instead of
+      // preceding every four MFMAs.
       f4v_t sacc[2];
+      {
+        f4_t ka[2][8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        sacc[h] = f4v_t{0.f, 0.f, 0.f, 0.f};
-        const float* krow = &ks[(16 * h + li) * kKsRow + 32 * lq];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const f4_t a4 = *reinterpret_cast<const f4_t*>(krow + 4 * t);
+          for (int t = 0; t < 8; ++t)
+            ka[h][t] = *reinterpret_cast<const f4_t*>(&ks[(16 * h + li) * kKsRow + 32 * lq + 4 * t]);
+        __builtin_amdgcn_sched_barrier(0);   // (the scheduler would pair each read with its MFMAs)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[i], qf[4 * t + i], sacc[h], 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+          sacc[h] = f4v_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sacc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[h][t][i], qf[4 * t + i], sacc[h], 0, 0, 0);
         }
       }
       // causal mask, tile max per query vector
@@ -533,21 +554,26 @@ __global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __re
       m = mn;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) oacc[mt] *= alpha;
-      // O^T += V^T P^T
+      // O^T += V^T P^T (operands read first, as above)
+      f4_t va[2][8];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const f4_t a4 = *reinterpret_cast<const f4_t*>(&vt[(16 * mt + li) * kVtRow + 16 * h + 4 * lq]);
+        for (int mt = 0; mt < 8; ++mt)
+          va[h][mt] = *reinterpret_cast<const f4_t*>(&vt[(16 * mt + li) * kVtRow + 16 * h + 4 * lq]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2)
-            oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[s2], sacc[h][s2], oacc[mt], 0, 0, 0);
-        }
+            oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[h][mt][s2], sacc[h][s2], oacc[mt], 0, 0, 0);
     }
   }
   // merge: group 1's states -> group 0 (records in the V tile memory)
   __syncthreads();
-  float* rec = &Vt[0][0] + (wv * kWave + lane) * kStateRow;
+  float* rec = &Vt[0][0] + ((ts * 2 + wh) * kWave + lane) * kStateRow;
   if (grp == 1) {
     rec[0] = m;
     rec[1] = l;
@@ -792,7 +818,7 @@ wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, hipStream_t s)
                          a.cap, a.eps, (const float*)L.q_norm, (const float*)L.k_norm, a.rope_cos, a.rope_sin,
                          (float*)L.k_cache, (float*)L.v_cache);
       if (l == c.n_layers - 1) break;   // only the K/V of the last layer has a consumer
-      const dim3 ag(cdiv(rows, kAQV / G), nkv);
+      const dim3 ag(cdiv(cdiv(rows, kAQV / G), 2), nkv);   // pairs of query tiles
       switch (G) {
         case 1: hipLaunchKernelGGL((k_prefill_attn<1>), ag, dim3(kAttnThreads), 0, s, QKV, (const float*)L.k_cache,
                                    (const float*)L.v_cache, rows, nq, nkv, pc, a.cap, O); break;
