@@ -444,6 +444,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __re
   const int row = tile * BR + rr;
   const bool row_ok = tile_on && row < n;
   const int my_pos = p0 + row;
+  // the wave's rows: all inside the chunk, and the first one's position
+  // (tiles with no key past it need no causal mask)
+  const bool wave_rows_ok = tile_on && tile * BR + (wh * 16 + 15) / G < n;
+  const int wave_first_pos = p0 + tile * BR + (wh * 16) / G;
   float qf[32];
   {
     const float* q = QKV + (size_t)min(row, n - 1) * width + (j * G + g) * kD + 32 * lq;
@@ -524,27 +528,37 @@ __global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __re
               sacc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[h][t][i], qf[4 * t + i], sacc[h], 0, 0, 0);
         }
       }
-      // causal mask, tile max per query vector
+      // causal mask (only tiles that reach past the wave's first row, or
+      // hold rows past the chunk), tile max per query vector
+      if (!wave_rows_ok || kt + kAKT - 1 > wave_first_pos) {   // wave-uniform
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kt + 16 * h + 4 * lq + r;
+            if (!(row_ok && key <= my_pos)) sacc[h][r] = -INFINITY;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kt + 16 * h + 4 * lq + r;
-          if (!(row_ok && key <= my_pos)) sacc[h][r] = -INFINITY;
-          mx = fmaxf(mx, sacc[h][r]);
-        }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[h][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mn = fmaxf(m, mx);
-      // a vector with no key yet keeps m = -inf: guard the rescale
-      const float alpha = mn == -INFINITY ? 1.f : exp2f(m - mn);
+      // exponents relative to the new max (0 while a vector has no key yet,
+      // so masked scores give exp2(-inf) = 0); alpha = 1 when the max is
+      // unchanged.  The hardware exp2: arguments are <= 0, and results below
+      // the normal range (weights under 2^-126 against a sum >= 1) may flush.
+      const float base = mn == -INFINITY ? 0.f : mn;
+      const float alpha = m == mn ? 1.f : __builtin_amdgcn_exp2f(m - base);
       float psum = 0.f;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = mn == -INFINITY ? 0.f : exp2f(sacc[h][r] - mn);
+          const float p = __builtin_amdgcn_exp2f(sacc[h][r] - base);
           sacc[h][r] = p;
           psum += p;
         }
@@ -552,8 +566,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __re
       psum += __shfl_xor(psum, 32);
       l = l * alpha + psum;
       m = mn;
+      if (__any(alpha != 1.f)) {   // wave-uniform: rescale only when a max moved
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) oacc[mt] *= alpha;
+        for (int mt = 0; mt < 8; ++mt) oacc[mt] *= alpha;
+      }
       // O^T += V^T P^T (operands read first, as above)
       f4_t va[2][8];
 #pragma unroll
