@@ -8,6 +8,10 @@
 ``python -m weight_streaming_gemv_amd.profsum sweep <run_kernel_trace.csv>``
     kernel-only GB/s of every cold-sweep configuration (bench.py --sweep-only),
     matched to its launch by kernel template arguments and grid size;
+``python -m weight_streaming_gemv_amd.profsum phases <run_kernel_trace.csv> <kernel> <run> <phases>``
+    the dispatches of one kernel (name containing <kernel>) in start order,
+    dispatch i counted in phase (i // run) % phases: median duration per phase
+    (e.g. the prefill attention of each chunk: 27 launches per chunk, 4 chunks);
 ``python -m weight_streaming_gemv_amd.profsum counters <run_counter_collection.csv>``
     per template instance and grid size (threads): dispatches, then the median
     per dispatch and the total over all dispatches of every collected counter
@@ -67,6 +71,24 @@ def instance_table(path):
     for s, (n, wg), ds in rows:
         print(f"| `{n}` | {wg} | {len(ds)} | {statistics.median(ds) / 1e3:.2f} | "
               f"{statistics.fmean(ds) / 1e3:.2f} | {s / 1e6:.2f} |")
+
+
+def phase_table(path, kernel, run, phases):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"]:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    by = defaultdict(list)
+    for i, (_, d) in enumerate(rows):
+        by[(i // run) % phases].append(d)
+    print(f"| phase | dispatches | median us | mean us |")
+    print("|---|---|---|---|")
+    for ph in range(phases):
+        ds = by[ph]
+        if ds:
+            print(f"| {ph} | {len(ds)} | {statistics.median(ds) / 1e3:.2f} | {statistics.fmean(ds) / 1e3:.2f} |")
 
 
 def counter_table(path):
@@ -147,5 +169,8 @@ if __name__ == "__main__":
     import os
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     mode, path = sys.argv[1], sys.argv[2]
-    {"decode": decode_table, "instances": instance_table, "sweep": sweep_table,
-     "counters": counter_table}[mode](path)
+    if mode == "phases":
+        phase_table(path, sys.argv[3], int(sys.argv[4]), int(sys.argv[5]))
+    else:
+        {"decode": decode_table, "instances": instance_table, "sweep": sweep_table,
+         "counters": counter_table}[mode](path)
