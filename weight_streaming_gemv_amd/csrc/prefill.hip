@@ -59,18 +59,20 @@ typedef float f4v_t __attribute__((ext_vector_type(4)));
 constexpr int kBK = 32;                   // K granularity of the shapes accepted (and of the small-M kernel)
 constexpr int kLdsPad = 4;                // floats of padding per LDS row
 
-template <int BM, int BN, int BK, bool ACC>
-__global__ __launch_bounds__(256) void k_gemm_nt(const float* __restrict__ A, const float* __restrict__ B,
-                                                 float* __restrict__ C, int M, int N, int K, int kspan,
-                                                 size_t c_split) {
+template <int BM, int BN, int BK, bool ACC, int WV>
+__global__ __launch_bounds__(64 * WV) void k_gemm_nt(const float* __restrict__ A, const float* __restrict__ B,
+                                                     float* __restrict__ C, int M, int N, int K, int kspan,
+                                                     size_t c_split) {
+  constexpr int kThreads = 64 * WV;
   constexpr int kLdsRow = BK + kLdsPad;
   constexpr int NU = BK / 32;                  // 32-wide parts per K tile
-  constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
+  constexpr int WM = BM / (WV / 2), WN = BN / 2;   // wave tile: a (WV/2) x 2 grid of waves
   constexpr int TM = WM / 32, TN = WN / 32;    // MFMA tiles per wave
   constexpr int F4_ROW = BK / 4;               // float4 per tile row
-  constexpr int A_LOADS = BM * F4_ROW / 256;   // float4 per thread per tile
-  constexpr int B_LOADS = BN * F4_ROW / 256;
-  static_assert(BM * F4_ROW % 256 == 0 && BN * F4_ROW % 256 == 0, "whole float4 per thread");
+  constexpr int A_LOADS = BM * F4_ROW / kThreads;   // float4 per thread per tile
+  constexpr int B_LOADS = BN * F4_ROW / kThreads;
+  static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "whole 32 x 32 MFMA tiles per wave");
+  static_assert(BM * F4_ROW % kThreads == 0 && BN * F4_ROW % kThreads == 0, "whole float4 per thread");
   __shared__ float As[BM * kLdsRow];
   __shared__ float Bs[BN * kLdsRow];
 
@@ -91,19 +93,19 @@ __global__ __launch_bounds__(256) void k_gemm_nt(const float* __restrict__ A, co
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // global -> register staging: thread loads float4 #(tid + 256 i) of the
+  // global -> register staging: thread loads float4 #(tid + kThreads i) of the
   // tile: row = idx / F4_ROW, col4 = idx % F4_ROW (plain loops: arrays
   // captured by a lambda would be forced into scratch memory)
   f4_t ra[A_LOADS], rb[B_LOADS];   // native vectors: HIP's float4 struct arrays end up in scratch
 #define WSG_GEMM_LOAD(K0)                                                                           \
   {                                                                                                \
     _Pragma("unroll") for (int i = 0; i < A_LOADS; ++i) {                                          \
-      const int idx = tid + 256 * i, row = idx / F4_ROW, c4 = idx % F4_ROW;                        \
+      const int idx = tid + kThreads * i, row = idx / F4_ROW, c4 = idx % F4_ROW;                        \
       const int gm = min(m0 + row, M - 1);   /* rows past M feed only unstored outputs */        \
       ra[i] = *reinterpret_cast<const f4_t*>(A + (size_t)gm * K + (K0) + 4 * c4);                  \
     }                                                                                              \
     _Pragma("unroll") for (int i = 0; i < B_LOADS; ++i) {                                          \
-      const int idx = tid + 256 * i, row = idx / F4_ROW, c4 = idx % F4_ROW;                        \
+      const int idx = tid + kThreads * i, row = idx / F4_ROW, c4 = idx % F4_ROW;                        \
       rb[i] = *reinterpret_cast<const f4_t*>(B + (size_t)(n0 + row) * K + (K0) + 4 * c4);          \
     }                                                                                              \
   }
@@ -138,12 +140,12 @@ __global__ __launch_bounds__(256) void k_gemm_nt(const float* __restrict__ A, co
     __syncthreads();          // previous tile fully consumed
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
-      const int idx = tid + 256 * i, row = idx / F4_ROW, c4 = idx % F4_ROW;
+      const int idx = tid + kThreads * i, row = idx / F4_ROW, c4 = idx % F4_ROW;
       *reinterpret_cast<f4_t*>(&As[row * kLdsRow + 4 * c4]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
-      const int idx = tid + 256 * i, row = idx / F4_ROW, c4 = idx % F4_ROW;
+      const int idx = tid + kThreads * i, row = idx / F4_ROW, c4 = idx % F4_ROW;
       *reinterpret_cast<f4_t*>(&Bs[row * kLdsRow + 4 * c4]) = rb[i];
     }
     __syncthreads();
@@ -693,8 +695,13 @@ void launch_tiled(const float* A, const float* B, float* C, int M, int N, int K,
   const int kspan = K / S;
   auto go = [&](auto bk) {
     constexpr int BK = decltype(bk)::value;
-    if (acc) hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, true>), grid, dim3(256), 0, s, A, B, C, M, N, K, kspan, c_split);
-    else hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, false>), grid, dim3(256), 0, s, A, B, C, M, N, K, kspan, c_split);
+    // 128-row tiles: 8 waves, two per SIMD (one computes while the other
+    // reads its operands from LDS); 64 x 64 tiles: 4 waves
+    constexpr int WV = BM == 128 ? 8 : 4;
+    if (acc)
+      hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, true, WV>), grid, dim3(64 * WV), 0, s, A, B, C, M, N, K, kspan, c_split);
+    else
+      hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, false, WV>), grid, dim3(64 * WV), 0, s, A, B, C, M, N, K, kspan, c_split);
   };
   if (kspan % 64 == 0) go(std::integral_constant<int, 64>{});
   else go(std::integral_constant<int, 32>{});
