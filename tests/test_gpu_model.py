@@ -115,7 +115,7 @@ WIDE_KV = ModelShape(n_layers=1, hidden=256, intermediate=512, n_q_heads=8, n_kv
 @pytest.mark.parametrize("n_prompt", [1600, 3300])
 def test_long_context_split_sizes(n_prompt):
     """Contexts whose split-K attention blocks take 80 keys (1600: each key-row
-    folds a second group of keys, the last one partial) and 144 keys (3300:
+    folds a second group of keys, the last one partial) and 160 keys (3300:
     three groups per key-row); greedy steps in lockstep, then two-token steps
     (an accepted and a rejected draft) at the same context."""
     import weight_streaming_gemv_amd as wsg
@@ -150,6 +150,33 @@ def test_long_context_split_sizes(n_prompt):
         else:
             orc.pos = p + 1
             last = t0
+    m.close()
+
+
+def test_graph_cache_eviction(mini_w):
+    """More step graphs than the cache keeps (64): 68 positions whose contexts need
+    68 different split counts; steps replayed after their graphs were evicted and
+    captured again return the same bits."""
+    import weight_streaming_gemv_amd as wsg
+    cap = 4608
+    m = wsg.Model(MINI, mini_w, max_context=cap, prefill_chunk=512)
+    prompt = prompt_ids(12, 4500, MINI.vocab)
+    m.prefill(prompt)
+    # rewinding only goes back: visit from the longest context down (70 .. 3
+    # splits of 64 keys); each step reads prefill-written keys below its slot
+    positions = [130 + 64 * i for i in range(67, -1, -1)]
+    first = {}
+    for p in positions:
+        m.rewind(p)
+        m.step()
+        first[p] = _np(m.logits()).copy()
+    # the first four graphs were evicted; the last two are still cached
+    m.reset()
+    m.prefill(prompt)
+    for p in positions[:4] + positions[-2:]:
+        m.rewind(p)
+        m.step()
+        assert np.array_equal(_np(m.logits()), first[p]), f"position {p}"
     m.close()
 
 

@@ -234,7 +234,9 @@ struct wsg_model {
   bool has_output = false;
   int32_t* pin = nullptr;          // pinned staging: [0] token out, [1..] ids in
   bool use_graph = true;
-  std::map<uint64_t, hipGraphExec_t> graphs;   // key: graph_key(splits, chunk, tokens, mode, advance)
+  struct CachedGraph { hipGraphExec_t exec; uint64_t last_use; };
+  std::map<uint64_t, CachedGraph> graphs;   // key: graph_key(splits, chunk, tokens, mode, advance)
+  uint64_t graph_uses = 0;
   int timed_stage = -1;
   std::vector<hipEvent_t> ev;
   int ev_used = 0;
@@ -376,10 +378,18 @@ int attn_mode(const wsg_model* m, int n_keys, int tokens) {
 // at 64 / 96 / 192 keys, i.e. 20-24 splits per head.
 constexpr int kAttnTargetBlocks = 192;
 
+// The size is taken from a ladder with four steps per doubling (64, 80, 96,
+// 112, 128, 160, ...: 16 * {4,5,6,7} * 2^e), so a long generation passes
+// through few (splits, chunk) graphs.
 int attn_chunk_for(const wsg_model* m, int n_keys) {
   const int per_head = std::max(1, kAttnTargetBlocks / m->d.nkv);
-  const int c = (ceil_div(n_keys, per_head) + 15) & ~15;
-  return std::max(m->shape.attn_chunk, c);
+  const int need = std::max(m->shape.attn_chunk, ceil_div(n_keys, per_head));
+  int c = 64;
+  for (int e = 0; c < need; ++e) {
+    const int base = 64 << (e / 4);            // 64 * 2^(e/4) ...
+    c = base + (base / 4) * (e % 4 + 1);       // ... times 5/4, 6/4, 7/4, 8/4
+  }
+  return c;
 }
 
 // Attention blocks per KV head: exactly the splits the context needs (one
@@ -387,16 +397,36 @@ int attn_chunk_for(const wsg_model* m, int n_keys) {
 // this is at most attn_split_cap(d).
 int splits_for(int n_keys, int chunk) { return ceil_div(n_keys, chunk); }
 
+// Graphs are destroyed only once the stream has finished any replay of them.
 void drop_graphs(wsg_model* m) {
-  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (m->graphs.empty()) return;
+  if (m->stream) (void)hipStreamSynchronize(m->stream);
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second.exec);
   m->graphs.clear();
 }
+
+// At most kMaxGraphs captured step graphs are kept; the least recently used
+// one makes room (a generation moves through a few (splits, chunk) pairs at
+// a time).
+constexpr size_t kMaxGraphs = 64;
 
 // Capture (once) and return the graph for `key`, built by `enqueue`.
 template <typename F>
 wsg_status graph_for(wsg_model* m, uint64_t key, F&& enqueue, hipGraphExec_t* out) {
   auto it = m->graphs.find(key);
-  if (it != m->graphs.end()) { *out = it->second; return WSG_OK; }
+  if (it != m->graphs.end()) {
+    it->second.last_use = ++m->graph_uses;
+    *out = it->second.exec;
+    return WSG_OK;
+  }
+  if (m->graphs.size() >= kMaxGraphs) {
+    auto lru = m->graphs.begin();
+    for (auto i = m->graphs.begin(); i != m->graphs.end(); ++i)
+      if (i->second.last_use < lru->second.last_use) lru = i;
+    WSG_HIP_CHECK(hipStreamSynchronize(m->stream));   // it may still be replaying
+    (void)hipGraphExecDestroy(lru->second.exec);
+    m->graphs.erase(lru);
+  }
   WSG_HIP_CHECK(hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
   m->capturing = true;
   const bool ok = enqueue();
@@ -409,7 +439,7 @@ wsg_status graph_for(wsg_model* m, uint64_t key, F&& enqueue, hipGraphExec_t* ou
   const hipError_t ei = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
   (void)hipGraphDestroy(g);
   if (ei != hipSuccess) return fail(WSG_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ei));
-  m->graphs.emplace(key, ex);
+  m->graphs.emplace(key, wsg_model::CachedGraph{ex, ++m->graph_uses});
   *out = ex;
   return WSG_OK;
 }
