@@ -14,7 +14,8 @@
  *     on an error nothing is enqueued, model state is unchanged, the call
  *     returns a negative wsg_status and wsg_last_error() describes it;
  *   - device memory is owned by the caller (the library borrows it); the
- *     library owns only the opaque wsg_model host object, its HIP graphs,
+ *     library owns only the opaque wsg_model host object, its HIP graphs
+ *     (one per attention split shape a step has needed, at most 64 kept),
  *     events and a small pinned host staging buffer;
  *   - "hip_stream" is a hipStream_t passed as void*; NULL selects a stream
  *     the library creates for the model (required for graph replay when the

@@ -961,7 +961,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
   TS* vh = v_cache + head_off;
 
   // Every split covers the fixed key range [split*chunk, split*chunk + chunk)
-  // (chunk is a per-model constant), so its first keys can be loaded before p.
+  // (chunk is fixed per captured graph), so its first keys can be loaded before p.
   const int k_begin = split * chunk;
   // one query row: each cached key is read by exactly one block of this
   // launch (two rows read it twice: ordinary loads, so the second may hit L2)
