@@ -544,21 +544,23 @@ def two_token(torch, wsg, shape, w, context=16, trials=9, reps=50, n_prompt=32, 
     return res
 
 
-def int4_decoder(torch, wsg, shape, steps=5, warmup=2, n_check=8):
-    """The short-prompt workload on an int4 model of the same shape: every decode matrix
-    and the tied embedding int4 in groups of 64 with FP16 scales (the int4 GEMV workload's
-    distributions: q uniform in [-8, 7], scales |N(0, 0.01)|), FP16 activations, KV cache
-    and logits, FP32 accumulation ("Our Kernel Benchmark Was Measuring the System Cache",
-    "Summary": 4-bit decode).  Validated first against the oracle, which dequantises the
-    same words on the CPU: teacher-forced (both sides consume the oracle's tokens), every
-    logit and new K/V slot within the FP16 tolerance rtol=atol=2e-2; the share of greedy
-    tokens that agree is reported.  Prompts run tokenwise (no chunked prefill for int4).
-    HIP events time the int4 head launches."""
+def f16_storage_decoder(torch, wsg, shape, fmt, steps=5, warmup=2, n_check=8):
+    """The short-prompt workload on a model of the same shape with 16-bit storage:
+    ``fmt`` "int4": every decode matrix and the tied embedding int4 in groups of 64 with
+    FP16 scales (the int4 GEMV workload's distributions: q uniform in [-8, 7], scales
+    |N(0, 0.01)|; "Our Kernel Benchmark Was Measuring the System Cache", "Summary": 4-bit
+    decode); "fp16": the FP32 model's weights rounded to FP16 (the FP16 storage
+    configuration whose validation Megakernels, "GPU-wide end-to-end generation", reports).  FP16 activations, KV cache and logits, FP32
+    accumulation.  Validated first against the oracle, which computes from the same stored
+    values on the CPU: teacher-forced (both sides consume the oracle's tokens), every logit
+    and new K/V slot within the FP16 tolerance rtol=atol=2e-2; the share of greedy tokens
+    that agree is reported.  Prompts run tokenwise (chunked prefill needs FP32 storage).
+    HIP events time the head launches."""
     import oracle
-    from synth import PROMPT_SEEDS, model_weights_q4, prompt_ids
+    from synth import PROMPT_SEEDS, model_weights, model_weights_q4, prompt_ids
     t = time.perf_counter()
-    w = model_weights_q4(shape, seed=0)
-    log(f"int4 weights generated in {time.perf_counter() - t:.1f} s")
+    w = model_weights_q4(shape, seed=0) if fmt == "int4" else model_weights(shape, seed=0, dtype=np.float16)
+    log(f"{fmt} weights generated in {time.perf_counter() - t:.1f} s")
     cap = 48
     model = wsg.Model(shape, w, max_context=cap, dtype=wsg.WSG_F16)
     orc = oracle.OracleModel(shape, w, cap)
@@ -572,7 +574,7 @@ def int4_decoder(torch, wsg, shape, steps=5, warmup=2, n_check=8):
         r = np.asarray(ref_, dtype=np.float64)
         err = np.abs(g - r)
         if not np.all(err <= tol + tol * np.abs(r)):
-            raise RuntimeError(f"int4 validation failed: {what} off by {err.max():.3e}")
+            raise RuntimeError(f"{fmt} validation failed: {what} off by {err.max():.3e}")
         return float(err.max())
 
     max_l = max_kv = 0.0
@@ -607,7 +609,7 @@ def int4_decoder(torch, wsg, shape, steps=5, warmup=2, n_check=8):
         for (n_p, n_o) in COMBOS:
             toks, ttft, dec, tot = generate(model, prompts[n_p], n_o)
             if expected.setdefault((n_p, n_o), toks) != toks:
-                raise RuntimeError(f"int4 generation {n_p}/{n_o} not repeatable")
+                raise RuntimeError(f"{fmt} generation {n_p}/{n_o} not repeatable")
             if i >= warmup:
                 rec.append((n_p, n_o, ttft, dec))
     ms, nl, by = model.stage_time()
@@ -624,9 +626,10 @@ def int4_decoder(torch, wsg, shape, steps=5, warmup=2, n_check=8):
                      "gbps": round(by / max(nl, 1) / (head_us * 1e-6) / 1e9, 1) if nl else None},
             "validation": {"max_abs_logit_err": max_l, "max_abs_kv_err": max_kv, "rtol": tol, "atol": tol,
                            "teacher_forced_steps": n_check, "greedy_token_agreement": f"{agree}/{total}"},
-            "workload": ("28-layer Qwen3-0.6B-shaped decoder, int4 group-64 weights with FP16 scales for every "
-                         "decode matrix and the tied embedding, FP16 activations/KV/logits; prompt/output 8/8, "
-                         "8/16, 32/8, 32/16, tokenwise prompt")}
+            "workload": ("28-layer Qwen3-0.6B-shaped decoder, " +
+                         ("int4 group-64 weights with FP16 scales for every decode matrix and the tied embedding"
+                          if fmt == "int4" else "FP16 weights (the FP32 draws rounded to nearest)") +
+                         ", FP16 activations/KV/logits; prompt/output 8/8, 8/16, 32/8, 32/16, tokenwise prompt")}
 
 
 def prefill_only(torch, wsg, shape, w, chunk=1024, trials=3):
@@ -831,6 +834,8 @@ def main(argv=None):
                     help="two-token step (speculative verify pass): fixed-slot latency and generation")
     ap.add_argument("--int4", choices=["on", "off", "only"], default="on",
                     help="short-prompt workload on an int4 (group-64) model of the same shape")
+    ap.add_argument("--fp16", choices=["on", "off", "only"], default="on",
+                    help="short-prompt workload on the same model with FP16 storage")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the held-out 4096-id prompt's chunk-1024 prefill, 1 warm-up + 3 timed "
                          "(profiling runs: MFMA counters; no value is published)")
@@ -908,7 +913,12 @@ def main(argv=None):
     if args.int4 == "only":
         del w, model
         torch.cuda.empty_cache()
-        print(json.dumps({"int4_decoder": int4_decoder(torch, wsg, shape)}), flush=True)
+        print(json.dumps({"int4_decoder": f16_storage_decoder(torch, wsg, shape, "int4")}), flush=True)
+        return 0
+    if args.fp16 == "only":
+        del w, model
+        torch.cuda.empty_cache()
+        print(json.dumps({"fp16_decoder": f16_storage_decoder(torch, wsg, shape, "fp16")}), flush=True)
         return 0
     fixed_res = None
     if args.fixed != "off" and not args.no_oracle:
@@ -1012,8 +1022,13 @@ def main(argv=None):
         torch.cuda.empty_cache()
     if args.int4 == "on" and not args.no_oracle:
         t = time.perf_counter()
-        out["int4_decoder"] = int4_decoder(torch, wsg, shape)
+        out["int4_decoder"] = f16_storage_decoder(torch, wsg, shape, "int4")
         log(f"int4 decoder section in {time.perf_counter() - t:.1f} s")
+        torch.cuda.empty_cache()
+    if args.fp16 == "on" and not args.no_oracle:
+        t = time.perf_counter()
+        out["fp16_decoder"] = f16_storage_decoder(torch, wsg, shape, "fp16")
+        log(f"fp16 decoder section in {time.perf_counter() - t:.1f} s")
         torch.cuda.empty_cache()
     if args.sweep != "none":
         sw = gemv_sweep(quick=args.sweep == "quick")

@@ -793,6 +793,13 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   // the one-shot grids; one-token steps keep the one-shot grids)
   m->shape2.grid_gu = 256;
   m->shape2.grid_qkv = 512;
+  if (d.es == 2 && !d.q4) {
+    // FP16 rows are 2 KiB: the head loops its two rows per wave over 8192
+    // workgroups, so each wave's activation and norm prologue serves more
+    // than one row pair (kernel-trace sweep of rows 1/2/4 x 4/8 waves x
+    // grids 2048..one-shot: 49 against 62 us on the one-shot grid)
+    for (DecodeShape* s : {&m->shape, &m->shape2}) s->grid_head = 8192;
+  }
   if (d.q4) {
     // int4 rows are short (544 bytes at width 1024): the head loops over
     // four rows per wave on 2048 blocks, so each wave's activation and norm
