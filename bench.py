@@ -554,7 +554,8 @@ def f16_storage_decoder(torch, wsg, shape, fmt, steps=5, warmup=2, n_check=8):
     accumulation.  Validated first against the oracle, which computes from the same stored
     values on the CPU: teacher-forced (both sides consume the oracle's tokens), every logit
     and new K/V slot within the FP16 tolerance rtol=atol=2e-2; the share of greedy tokens
-    that agree is reported.  Prompts run tokenwise (chunked prefill needs FP32 storage).
+    that agree is reported.  Prompt rows run through the decode forward, two per forward
+    (chunked prefill needs FP32 storage).
     HIP events time the head launches."""
     import oracle
     from synth import PROMPT_SEEDS, model_weights, model_weights_q4, prompt_ids
@@ -629,7 +630,8 @@ def f16_storage_decoder(torch, wsg, shape, fmt, steps=5, warmup=2, n_check=8):
             "workload": ("28-layer Qwen3-0.6B-shaped decoder, " +
                          ("int4 group-64 weights with FP16 scales for every decode matrix and the tied embedding"
                           if fmt == "int4" else "FP16 weights (the FP32 draws rounded to nearest)") +
-                         ", FP16 activations/KV/logits; prompt/output 8/8, 8/16, 32/8, 32/16, tokenwise prompt")}
+                         ", FP16 activations/KV/logits; prompt/output 8/8, 8/16, 32/8, 32/16, prompt rows two "
+                         "per decode forward")}
 
 
 def prefill_only(torch, wsg, shape, w, chunk=1024, trials=3):

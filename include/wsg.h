@@ -62,7 +62,7 @@ typedef enum { WSG_W_DENSE = 0, WSG_W_Q4G64 = 1 } wsg_weight_format;
  *   n_q_heads must be a multiple of n_kv_heads with a group size of 1, 2
  *   or 4.  max_context is the KV capacity in
  *   positions.  prefill_chunk is the largest number of prompt rows one
- *   prefill chunk may hold (0 = tokenwise prefill only).  */
+ *   prefill chunk may hold (0 = prompt rows through the decode forward).  */
 typedef struct {
   int32_t n_layers, hidden, intermediate, n_q_heads, n_kv_heads, head_dim, vocab;
   int32_t max_context;
@@ -186,7 +186,9 @@ wsg_status wsg_reset_cache(wsg_model* m);
  * logits).  Only the last row reaches the final norm and vocabulary head
  * (Benchmark methodology, "Long-document chunked prefill").  Rows go through
  * the chunked path when cfg.prefill_chunk > 0 (chunk size set by
- * wsg_set_prefill_chunk), else one decode forward per row.  *out_logits (if
+ * wsg_set_prefill_chunk), else through the decode forward, two rows per
+ * forward before the last (the two-row forward of wsg_step2, without its
+ * head) and the last row alone.  *out_logits (if
  * out_logits is not NULL) receives a device pointer to the last row's
  * logits [vocab] in the storage dtype, valid until the next call.  Blocks
  * until the token id is on the host.  Errors: n < 1, any id outside

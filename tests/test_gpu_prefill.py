@@ -98,7 +98,8 @@ def test_stale_cache_never_leaks(mini_w, chunk):
 
 
 def test_mini_chunked_matches_tokenwise_and_continues(mini_w):
-    """Chunked and tokenwise prefill agree; a second prefill call continues the sequence."""
+    """Chunked prefill and prefill through the decode forward (rows two per forward) agree;
+    a second prefill call continues the sequence."""
     import weight_streaming_gemv_amd as wsg
     cap = 200
     prompt = prompt_ids(12, 150, MINI.vocab)

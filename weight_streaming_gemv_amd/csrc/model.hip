@@ -892,7 +892,15 @@ wsg_status wsg_prefill(wsg_model* m, const int32_t* host_ids, int32_t n, int32_t
     if (st != WSG_OK) return st;
     done = n - 1;
   }
-  for (int r = done; r < n; ++r) {
+  // Rows without the chunked path: two at a time through the two-row
+  // body (each weight vector read once for both rows), the last row alone
+  // so that it reaches the head.
+  int r = done;
+  for (; r + 2 <= n - 1; r += 2) {
+    const wsg_status st = run_forward(m, false, p0 + r + 2, 2);
+    if (st != WSG_OK) return st;
+  }
+  for (; r < n; ++r) {
     const bool last = (r == n - 1);
     const wsg_status st = run_forward(m, last, p0 + r + 1);
     if (st != WSG_OK) return st;
