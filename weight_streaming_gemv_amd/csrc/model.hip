@@ -449,6 +449,22 @@ uint64_t graph_key(int splits, int chunk, int tokens, int mode, bool advance) {
   return ((((uint64_t)chunk << 20 | (uint64_t)splits) * 2 + (tokens - 1)) * 3 + mode) * 2 + (advance ? 1 : 0);
 }
 
+// The final norm + vocabulary head and the argmax over the residual rows in
+// args.x.  They are single launches, issued directly (a graph saves nothing
+// for one kernel), so stream events can bracket the head.
+wsg_status run_head(wsg_model* m, int tokens) {
+  const bool t = m->timed_stage == WSG_STAGE_HEAD;
+  if (t) record_event(m, m->ev[0]);
+  if (!enqueue_head(m, tokens)) return fail(WSG_ERR_UNSUPPORTED, "no compiled head kernel for this shape");
+  if (t) {
+    record_event(m, m->ev[1]);
+    m->ev_used = 2;
+    m->timed_bytes_per_launch_sum = stage_bytes(m, WSG_STAGE_HEAD, -1);
+  }
+  if (!enqueue_argmax(m, tokens)) return fail(WSG_ERR_UNSUPPORTED, "argmax launch");
+  return WSG_OK;
+}
+
 // Enqueue one step of `tokens` rows at the current device position (n_keys
 // = the last row's position + 1): the layer body and, if `head`, the head
 // (final norm, vocabulary GEMV, argmax).
@@ -471,17 +487,8 @@ wsg_status run_forward(wsg_model* m, bool head, int n_keys, int tokens = 1) {
     WSG_HIP_CHECK(hipGraphLaunch(body, m->stream));
   }
   if (head) {
-    // The head and the argmax are single launches, issued directly (a graph
-    // saves nothing for one kernel), so stream events can bracket the head.
-    const bool t = m->timed_stage == WSG_STAGE_HEAD;
-    if (t) record_event(m, m->ev[0]);
-    if (!enqueue_head(m, tokens)) return fail(WSG_ERR_UNSUPPORTED, "no compiled head kernel for this shape");
-    if (t) {
-      record_event(m, m->ev[1]);
-      m->ev_used = 2;
-      m->timed_bytes_per_launch_sum = stage_bytes(m, WSG_STAGE_HEAD, -1);
-    }
-    if (!enqueue_argmax(m, tokens)) return fail(WSG_ERR_UNSUPPORTED, "argmax launch");
+    const wsg_status st = run_head(m, tokens);
+    if (st != WSG_OK) return st;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(WSG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -885,12 +892,18 @@ wsg_status wsg_prefill(wsg_model* m, const int32_t* host_ids, int32_t n, int32_t
   const int p0 = m->pos;
   int done = 0;
   if (m->prefill_rows > 0 && n > 1) {
-    // chunked path for all rows but the last; the last row runs the decode
-    // forward so that it alone reaches the head
+    // chunked path for every row; the last row alone completes the last
+    // layer and reaches the head
     PrefillCtx pc = prefill_ctx(m->args, m->shape, m->layers.data(), m->d.L, m->ws, m->wl.pf, m->prefill_rows);
-    const wsg_status st = run_prefill_chunks(pc, p0, n - 1, m->stream);
+    (void)hipGetLastError();   // errors of earlier calls were reported by those calls
+    m->ev_used = 0;
+    m->timed_bytes_per_launch_sum = 0;
+    wsg_status st = run_prefill_chunks(pc, p0, n, true, m->stream);
+    if (st == WSG_OK) st = run_head(m, 1);
     if (st != WSG_OK) return st;
-    done = n - 1;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(WSG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    done = n;
   }
   // Rows without the chunked path: two at a time through the two-row
   // body (each weight vector read once for both rows), the last row alone

@@ -326,6 +326,18 @@ bool launch_rows_norm(float* X, const float* P, int n_part, const float* g, int 
   }
 }
 
+// The residual of row r after its last pending split-K slices (added in
+// slice order, as k_rows_norm adds them), written to x_out: the input of the
+// decode head for a prompt's last row.
+__global__ __launch_bounds__(256) void k_row_residual(const float* __restrict__ X, const float* __restrict__ P,
+                                                      int n_part, int n, int H, int r, float* __restrict__ x_out) {
+  for (int c = 4 * threadIdx.x; c < H; c += 1024) {
+    f4_t v = *reinterpret_cast<const f4_t*>(X + (size_t)r * H + c);
+    for (int p = 0; p < n_part; ++p) v += *reinterpret_cast<const f4_t*>(P + ((size_t)p * n + r) * H + c);
+    *reinterpret_cast<f4_t*>(x_out + c) = v;
+  }
+}
+
 // Per (row, head) wave: Q heads normalised + rotated in place; K heads
 // normalised + rotated into the K cache at position p0 + r; V heads copied
 // into the V cache.  Lane l holds dims l and l + 64 (one rotary pair).
@@ -811,7 +823,7 @@ PrefillCtx prefill_ctx(const DecodeArgs& a, const DecodeShape& sh, const LayerPt
   return c;
 }
 
-wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, hipStream_t s) {
+wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, bool to_head, hipStream_t s) {
   const DecodeArgs& a = c.args;
   if (a.dtype != 0) return fail(WSG_ERR_UNSUPPORTED, "chunked prefill runs FP32 models only");
   if (c.chunk < 1 || c.pf.rows < c.chunk) return fail(WSG_ERR_STATE, "prefill chunk scratch too small");
@@ -840,27 +852,38 @@ wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, hipStream_t s)
       hipLaunchKernelGGL(k_rows_qkv, dim3(cdiv(nq + 2 * nkv, 4), rows), dim3(256), 0, s, QKV, rows, nq, nkv, pc,
                          a.cap, a.eps, (const float*)L.q_norm, (const float*)L.k_norm, a.rope_cos, a.rope_sin,
                          (float*)L.k_cache, (float*)L.v_cache);
-      if (l == c.n_layers - 1) break;   // only the K/V of the last layer has a consumer
-      const dim3 ag(cdiv(cdiv(rows, kAQV / G), 2), nkv);   // pairs of query tiles
+      // The last layer: its K/V is all that later rows need; with to_head
+      // the prompt's last row alone also completes it, for the head.
+      const bool last_layer = l == c.n_layers - 1;
+      if (last_layer && !(to_head && r0 + rows == n)) break;
+      const int r_first = last_layer ? rows - 1 : 0, nr = rows - r_first;
+      float* Xr = X + (size_t)r_first * H;
+      const float* QKVr = QKV + (size_t)r_first * (Q + 2 * KV);
+      const dim3 ag(cdiv(cdiv(nr, kAQV / G), 2), nkv);   // pairs of query tiles
       switch (G) {
-        case 1: hipLaunchKernelGGL((k_prefill_attn<1>), ag, dim3(kAttnThreads), 0, s, QKV, (const float*)L.k_cache,
-                                   (const float*)L.v_cache, rows, nq, nkv, pc, a.cap, O); break;
-        case 2: hipLaunchKernelGGL((k_prefill_attn<2>), ag, dim3(kAttnThreads), 0, s, QKV, (const float*)L.k_cache,
-                                   (const float*)L.v_cache, rows, nq, nkv, pc, a.cap, O); break;
+        case 1: hipLaunchKernelGGL((k_prefill_attn<1>), ag, dim3(kAttnThreads), 0, s, QKVr, (const float*)L.k_cache,
+                                   (const float*)L.v_cache, nr, nq, nkv, pc + r_first, a.cap, O); break;
+        case 2: hipLaunchKernelGGL((k_prefill_attn<2>), ag, dim3(kAttnThreads), 0, s, QKVr, (const float*)L.k_cache,
+                                   (const float*)L.v_cache, nr, nq, nkv, pc + r_first, a.cap, O); break;
         default: return fail(WSG_ERR_UNSUPPORTED, "chunked prefill supports query groups of 1 or 2");
       }
-      n_part = launch_gemm_residual(O, static_cast<const float*>(L.wo), X, PART, rows, H, Q, s);
+      n_part = launch_gemm_residual(O, static_cast<const float*>(L.wo), Xr, PART, nr, H, Q, s);
       if (n_part < 0) return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
-      if (!launch_rows_norm(X, PART, n_part, (const float*)L.post_norm, rows, H, a.eps, A, s))
+      if (!launch_rows_norm(Xr, PART, n_part, (const float*)L.post_norm, nr, H, a.eps, A, s))
         return fail(WSG_ERR_UNSUPPORTED, "row norm shape");
-      if (!launch_gemm(A, static_cast<const float*>(L.wgu), GU, rows, 2 * I, H, false, s))
+      if (!launch_gemm(A, static_cast<const float*>(L.wgu), GU, nr, 2 * I, H, false, s))
         return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
-      hipLaunchKernelGGL(k_rows_swiglu, dim3(min(cdiv(rows * I, 256), 4096)), dim3(256), 0, s, GU, rows, I, ACT);
-      n_part = launch_gemm_residual(ACT, static_cast<const float*>(L.wd), X, PART, rows, H, I, s);
+      hipLaunchKernelGGL(k_rows_swiglu, dim3(min(cdiv(nr * I, 256), 4096)), dim3(256), 0, s, GU, nr, I, ACT);
+      n_part = launch_gemm_residual(ACT, static_cast<const float*>(L.wd), Xr, PART, nr, H, I, s);
       if (n_part < 0) return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
+      if (last_layer)   // the last row's final residual, for the head
+        hipLaunchKernelGGL(k_row_residual, dim3(1), dim3(256), 0, s, Xr, PART, n_part, 1, H, 0,
+                           static_cast<float*>(a.x));
     }
   }
-  launch_set_pos(a.ctrl, p0 + n, s);
+  // the head and argmax that follow a to_head run advance the position past
+  // the last row
+  launch_set_pos(a.ctrl, to_head ? p0 + n - 1 : p0 + n, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(WSG_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return WSG_OK;

@@ -33,9 +33,12 @@ PrefillCtx prefill_ctx(const DecodeArgs& a, const DecodeShape& sh, const LayerPt
                        uint8_t* ws, const PrefillLayout& pf, int chunk);
 
 // Run rows [p0, p0 + n) through every layer in chunks of c.chunk rows (K/V
-// written to the cache; the last layer stops after its K/V write; no head).
-// Asynchronous on s.  Sets the device position to p0 + n.
-wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, hipStream_t s);
+// written to the cache; the last layer stops after its K/V write).  With
+// to_head the last row alone also completes the last layer and its final
+// residual goes to the decode residual buffer c.args.x, and the device
+// position is set to p0 + n - 1 for the head and argmax that follow;
+// otherwise it is set to p0 + n.  Asynchronous on s.
+wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, bool to_head, hipStream_t s);
 
 // C[M x N] (+)= A[M x K] . B[N x K]^T on FP32 MFMA (N % 64 == 0, K % 32 == 0).
 bool gemm_nt_f32(const float* A, const float* B, float* C, int M, int N, int K, bool accumulate, hipStream_t s);
