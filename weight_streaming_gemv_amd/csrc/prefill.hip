@@ -195,7 +195,11 @@ typedef float f4v_t __attribute__((ext_vector_type(4)));
 // Block (x, y) covers columns [16x, 16x + 16) and the K range
 // [y*KB, (y+1)*KB) of the ldk-long rows; with several K ranges each writes
 // its own partial slice C + y*c_split (summed later by the consumer).
-template <int KB, int W, int MT, bool ACC>
+// With SWI, B is a packed gate/up matrix (N/2 gate rows, then N/2 up rows):
+// workgroup b takes gate rows [8b, 8b + 8) and the matching up rows, and
+// writes C[M x N/2] = silu(gate) * up (the SwiGLU of the MLP) instead of
+// the product; the per-element sums are the same as without SWI.
+template <int KB, int W, int MT, bool ACC, bool SWI>
 __global__ __launch_bounds__(64 * W) void k_gemm_skinny(const float* __restrict__ A, const float* __restrict__ B,
                                                         float* __restrict__ C, int M, int N, int ldk,
                                                         size_t c_split) {
@@ -212,7 +216,8 @@ __global__ __launch_bounds__(64 * W) void k_gemm_skinny(const float* __restrict_
   const int n0 = blockIdx.x * 16;
   const int k0 = blockIdx.y * KB + wave * KW + 8 * lq;
   C += blockIdx.y * c_split;
-  const float* bp = B + (size_t)(n0 + li) * ldk + k0;
+  const int nrow = SWI ? blockIdx.x * 8 + (li & 7) + (li >= 8 ? N / 2 : 0) : n0 + li;
+  const float* bp = B + (size_t)nrow * ldk + k0;
   const float* ap[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)   // rows past M feed only unstored outputs
@@ -246,14 +251,28 @@ __global__ __launch_bounds__(64 * W) void k_gemm_skinny(const float* __restrict_
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave][(mt * 16 + 4 * lq + r) * RS + li] = acc[mt][r];
   __syncthreads();
-  for (int e = threadIdx.x; e < MT * 256; e += 64 * W) {
-    const int row = e >> 4, col = e & 15;
-    float sum = red[0][row * RS + col];
+  if constexpr (SWI) {
+    // columns 0-7 of the tile are gate rows, 8-15 the matching up rows
+    for (int e = threadIdx.x; e < MT * 128; e += 64 * W) {
+      const int row = e >> 3, col = e & 7;
+      float g = red[0][row * RS + col], u = red[0][row * RS + col + 8];
 #pragma unroll
-    for (int w = 1; w < W; ++w) sum += red[w][row * RS + col];
-    if (row < M) {
-      float* p = C + (size_t)row * N + n0 + col;
-      *p = ACC ? *p + sum : sum;
+      for (int w = 1; w < W; ++w) {
+        g += red[w][row * RS + col];
+        u += red[w][row * RS + col + 8];
+      }
+      if (row < M) C[(size_t)row * (N / 2) + blockIdx.x * 8 + col] = g / (1.0f + expf(-g)) * u;
+    }
+  } else {
+    for (int e = threadIdx.x; e < MT * 256; e += 64 * W) {
+      const int row = e >> 4, col = e & 15;
+      float sum = red[0][row * RS + col];
+#pragma unroll
+      for (int w = 1; w < W; ++w) sum += red[w][row * RS + col];
+      if (row < M) {
+        float* p = C + (size_t)row * N + n0 + col;
+        *p = ACC ? *p + sum : sum;
+      }
     }
   }
 }
@@ -648,14 +667,15 @@ int skinny_waves(int blocks, int KB) {
 
 template <int KB>
 bool launch_skinny_kb(const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split,
-                      bool acc, hipStream_t s) {
+                      bool acc, bool swiglu, hipStream_t s) {
   const int W = skinny_waves(N / 16 * S, KB);
   const dim3 grid(N / 16, S);
-  auto go = [&](auto wc, auto mc, auto ac) {
+  auto go = [&](auto wc, auto mc, auto ac, auto sc) {
     constexpr int Wv = decltype(wc)::value, MTv = decltype(mc)::value;
-    constexpr bool ACCv = decltype(ac)::value;
-    if constexpr (KB % (Wv * kBK) == 0) {
-      hipLaunchKernelGGL((k_gemm_skinny<KB, Wv, MTv, ACCv>), grid, dim3(64 * Wv), 0, s, A, B, C, M, N, K, c_split);
+    constexpr bool ACCv = decltype(ac)::value, SWIv = decltype(sc)::value;
+    if constexpr (KB % (Wv * kBK) == 0 && !(ACCv && SWIv)) {
+      hipLaunchKernelGGL((k_gemm_skinny<KB, Wv, MTv, ACCv, SWIv>), grid, dim3(64 * Wv), 0, s, A, B, C, M, N, K,
+                         c_split);
       return true;
     } else {
       return false;
@@ -663,7 +683,8 @@ bool launch_skinny_kb(const float* A, const float* B, float* C, int M, int N, in
   };
   auto with_m = [&](auto wc) {
     auto with_acc = [&](auto mc) {
-      return acc ? go(wc, mc, std::true_type{}) : go(wc, mc, std::false_type{});
+      if (swiglu) return go(wc, mc, std::false_type{}, std::true_type{});
+      return acc ? go(wc, mc, std::true_type{}, std::false_type{}) : go(wc, mc, std::false_type{}, std::false_type{});
     };
     return M <= 16 ? with_acc(std::integral_constant<int, 1>{}) : with_acc(std::integral_constant<int, 2>{});
   };
@@ -684,16 +705,17 @@ bool skinny_kb_ok(int kb) {
 }
 
 bool launch_skinny(const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split, bool acc,
-                   hipStream_t s) {
+                   hipStream_t s, bool swiglu = false) {
   if (K % S != 0 || !skinny_kb_ok(K / S)) return false;
+  if (swiglu && (S != 1 || acc || N % 16 != 0)) return false;
   switch (K / S) {
-    case 128: return launch_skinny_kb<128>(A, B, C, M, N, K, S, c_split, acc, s);
-    case 256: return launch_skinny_kb<256>(A, B, C, M, N, K, S, c_split, acc, s);
-    case 512: return launch_skinny_kb<512>(A, B, C, M, N, K, S, c_split, acc, s);
-    case 768: return launch_skinny_kb<768>(A, B, C, M, N, K, S, c_split, acc, s);
-    case 1024: return launch_skinny_kb<1024>(A, B, C, M, N, K, S, c_split, acc, s);
-    case 2048: return launch_skinny_kb<2048>(A, B, C, M, N, K, S, c_split, acc, s);
-    case 3072: return launch_skinny_kb<3072>(A, B, C, M, N, K, S, c_split, acc, s);
+    case 128: return launch_skinny_kb<128>(A, B, C, M, N, K, S, c_split, acc, swiglu, s);
+    case 256: return launch_skinny_kb<256>(A, B, C, M, N, K, S, c_split, acc, swiglu, s);
+    case 512: return launch_skinny_kb<512>(A, B, C, M, N, K, S, c_split, acc, swiglu, s);
+    case 768: return launch_skinny_kb<768>(A, B, C, M, N, K, S, c_split, acc, swiglu, s);
+    case 1024: return launch_skinny_kb<1024>(A, B, C, M, N, K, S, c_split, acc, swiglu, s);
+    case 2048: return launch_skinny_kb<2048>(A, B, C, M, N, K, S, c_split, acc, swiglu, s);
+    case 3072: return launch_skinny_kb<3072>(A, B, C, M, N, K, S, c_split, acc, swiglu, s);
     default: return false;
   }
 }
@@ -747,6 +769,18 @@ bool launch_gemm(const float* A, const float* B, float* C, int M, int N, int K, 
   if (M < 1 || N % 64 != 0 || K % kBK != 0) return false;
   if (M <= kSkinnyMaxM && launch_skinny(A, B, C, M, N, K, 1, 0, acc, s)) return true;
   launch_tile(pick_tile(M, N), A, B, C, M, N, K, 1, 0, acc, s);
+  return true;
+}
+
+// ACT[M x I] = silu(A . Wg^T) * (A . Wu^T) for the packed gate/up matrix Wgu
+// (I gate rows, then I up rows): up to 32 rows in the small-M kernel's
+// epilogue, otherwise the tiled product into GU followed by k_rows_swiglu.
+bool launch_gemm_swiglu(const float* A, const float* Wgu, float* GU, float* ACT, int M, int I, int K,
+                        hipStream_t s) {
+  if (M <= kSkinnyMaxM && (2 * I) % 64 == 0 && launch_skinny(A, Wgu, ACT, M, 2 * I, K, 1, 0, false, s, true))
+    return true;
+  if (!launch_gemm(A, Wgu, GU, M, 2 * I, K, false, s)) return false;
+  hipLaunchKernelGGL(k_rows_swiglu, dim3(min(cdiv(M * I, 256), 4096)), dim3(256), 0, s, GU, M, I, ACT);
   return true;
 }
 
@@ -871,9 +905,8 @@ wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, bool to_head, 
       if (n_part < 0) return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
       if (!launch_rows_norm(Xr, PART, n_part, (const float*)L.post_norm, nr, H, a.eps, A, s))
         return fail(WSG_ERR_UNSUPPORTED, "row norm shape");
-      if (!launch_gemm(A, static_cast<const float*>(L.wgu), GU, nr, 2 * I, H, false, s))
+      if (!launch_gemm_swiglu(A, static_cast<const float*>(L.wgu), GU, ACT, nr, I, H, s))
         return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
-      hipLaunchKernelGGL(k_rows_swiglu, dim3(min(cdiv(nr * I, 256), 4096)), dim3(256), 0, s, GU, nr, I, ACT);
       n_part = launch_gemm_residual(ACT, static_cast<const float*>(L.wd), Xr, PART, nr, H, I, s);
       if (n_part < 0) return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
       if (last_layer)   // the last row's final residual, for the head
