@@ -824,6 +824,7 @@ def main(argv=None):
     ap.add_argument("--sweep", choices=["full", "quick", "none"], default="full",
                     help="cold-cache GEMV sweep after the decode timing")
     ap.add_argument("--sweep-only", action="store_true", help="run only the cold-cache GEMV sweep")
+    ap.add_argument("--sweep-json", default=None, help="also write every sweep configuration's row to this file")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (reference for the HBM traffic counters)")
     ap.add_argument("--long", choices=["on", "off", "only"], default="on",
@@ -872,6 +873,9 @@ def main(argv=None):
     if args.sweep_only:
         sw = gemv_sweep(quick=args.sweep == "quick")
         best, agg = sweep_summary(sw)
+        if args.sweep_json:
+            with open(args.sweep_json, "w") as f:
+                json.dump(sw, f, indent=1)
         print(json.dumps({"gemv_cold": {"best": best, "decode_mix": agg}}), flush=True)
         return 0
     shape = QWEN3_0_6B
@@ -1042,9 +1046,9 @@ def main(argv=None):
             t = time.perf_counter()
             out["gemv_cold"]["cpu_oracle"] = cpu_gemv_rates()
             log(f"oracle GEMVs on the host in {time.perf_counter() - t:.1f} s")
-        with open(os.path.join(ROOT, "gpurun_out", "gemv_sweep.json") if os.path.isdir(
-                os.path.join(ROOT, "gpurun_out")) else os.devnull, "w") as f:
-            json.dump(sw, f, indent=1)
+        if args.sweep_json:
+            with open(args.sweep_json, "w") as f:
+                json.dump(sw, f, indent=1)
     print(json.dumps(out), flush=True)
     return 0
 
