@@ -142,7 +142,7 @@ def validate(model, orc, prompt, n_out):
     return toks, max_l, max_kv, t_dec
 
 
-def gemv_sweep(rounds=15, quick=False):
+def gemv_sweep(rounds=15, kind="full"):
     """Cold-cache GEMV sweep: each shape cycles >= 1 GiB of distinct matrices.
 
     Our Kernel Benchmark Was Measuring the System Cache ("The fix"): one reused
@@ -153,6 +153,8 @@ def gemv_sweep(rounds=15, quick=False):
     wave interleaved within each round (A/B/A, "Two neighboring traps").
     Effective GB/s = weight bytes / that time (Benchmark methodology, "What the
     measurements mean").  A warm figure (one matrix reused) is given for T=1.
+    ``kind``: "full" (every shape), "quick" (the first FP32/FP16 shape), "int4" (the int4
+    shapes only, e.g. for counter runs).
     """
     import torch
     import weight_streaming_gemv_amd as wsg
@@ -210,7 +212,7 @@ def gemv_sweep(rounds=15, quick=False):
         del graphs
         return res
 
-    shapes = GEMV_SHAPES if not quick else GEMV_SHAPES[:1]
+    shapes = {"full": GEMV_SHAPES, "quick": GEMV_SHAPES[:1], "int4": []}[kind]
     for dt_name, tdt, es in (("f32", torch.float32, 4), ("f16", torch.float16, 2)):
         for (M, K) in shapes:
             bytes_per = M * K * es
@@ -229,7 +231,7 @@ def gemv_sweep(rounds=15, quick=False):
             out[f"{dt_name}_{M}x{K}"] = {"bytes": bytes_per, "copies": n, **r}
             del W, X, Y
             torch.cuda.empty_cache()
-    for (M, K) in (Q4_SHAPES if not quick else []):
+    for (M, K) in (Q4_SHAPES if kind in ("full", "int4") else []):
         bytes_per = M * K // 2 + M * (K // 64) * 2
         n = -(-GiB // bytes_per)
         Wq = torch.randint(-2 ** 31, 2 ** 31 - 1, (n, M, K // 8), device="cuda", generator=gen, dtype=torch.int32)
@@ -821,10 +823,11 @@ def main(argv=None):
     ap.add_argument("--timed-stage", default="head", choices=sorted(STAGES),
                     help="stage kind bracketed by HIP events (graph mode: head only)")
     ap.add_argument("--no-graph", action="store_true", help="launch every kernel directly")
-    ap.add_argument("--sweep", choices=["full", "quick", "none"], default="full",
+    ap.add_argument("--sweep", choices=["full", "quick", "int4", "none"], default="full",
                     help="cold-cache GEMV sweep after the decode timing")
     ap.add_argument("--sweep-only", action="store_true", help="run only the cold-cache GEMV sweep")
     ap.add_argument("--sweep-json", default=None, help="also write every sweep configuration's row to this file")
+    ap.add_argument("--sweep-rounds", type=int, default=15, help="timed rounds per sweep configuration")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (reference for the HBM traffic counters)")
     ap.add_argument("--long", choices=["on", "off", "only"], default="on",
@@ -871,7 +874,7 @@ def main(argv=None):
         print(json.dumps({"copy_calibration_bytes_each_way": n * 4}), flush=True)
         return 0
     if args.sweep_only:
-        sw = gemv_sweep(quick=args.sweep == "quick")
+        sw = gemv_sweep(rounds=args.sweep_rounds, kind=args.sweep)
         best, agg = sweep_summary(sw)
         if args.sweep_json:
             with open(args.sweep_json, "w") as f:
@@ -1037,7 +1040,7 @@ def main(argv=None):
         log(f"fp16 decoder section in {time.perf_counter() - t:.1f} s")
         torch.cuda.empty_cache()
     if args.sweep != "none":
-        sw = gemv_sweep(quick=args.sweep == "quick")
+        sw = gemv_sweep(rounds=args.sweep_rounds, kind=args.sweep)
         best, agg = sweep_summary(sw)
         out["gemv_cold"] = {"best": best, "decode_mix": agg, "note": "dispatch-inclusive (graph replay) per-dispatch "
                             "time over >= 1 GiB of distinct matrices per shape; median of 15 rounds; stream ceiling "
