@@ -236,6 +236,29 @@ def test_mini_error_paths(mini_w):
     m.close()
 
 
+@pytest.mark.parametrize("fuse", [1, 0])
+def test_fills_cache_to_capacity(mini_w, fuse):
+    """A ragged chunked prefill (33 = 16 + 16 + 1 rows), then steps until the
+    last one writes and attends over the final slot (cap - 1): logits, tokens
+    and every K/V slot match the oracle; the next step is refused and leaves
+    the position and the logits as they were.  Fused attention + output
+    projection and the split-K launches."""
+    import weight_streaming_gemv_amd as wsg
+    cap, n_prompt = 40, 33
+    m = wsg.Model(MINI, mini_w, max_context=cap, prefill_chunk=16)
+    m.set_option(wsg._abi.WSG_OPT_FUSE_ATTN_O, fuse)
+    orc = oracle.OracleModel(MINI, mini_w, cap)
+    prompt = prompt_ids(77, n_prompt, MINI.vocab)
+    lockstep(m, orc, prompt, cap - n_prompt + 1, label=f"mini to capacity fuse={fuse}")
+    assert m.position == cap
+    logits = _np(m.logits()).copy()
+    with pytest.raises(wsg.WsgError, match="OUT_OF_RANGE"):
+        m.step()
+    assert m.position == cap
+    assert np.array_equal(_np(m.logits()), logits)
+    m.close()
+
+
 @pytest.fixture(scope="module")
 def c1_w():
     return model_weights(QWEN3_0_6B.with_layers(2), seed=0)
