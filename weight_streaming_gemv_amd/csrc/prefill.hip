@@ -787,7 +787,7 @@ bool launch_gemm_swiglu(const float* A, const float* Wgu, float* GU, float* ACT,
 // X[M x N] += A . B^T for a residual stream consumed by k_rows_norm.  A
 // residual projection has few column tiles (N = hidden), so K is split over
 // up to kMaxSplitK blocks per tile (the small-M kernel for up to 32 rows;
-// otherwise the larger tiles whose count times the split reaches 256
+// otherwise the larger tiles whose count times the split reaches 1024
 // blocks), writing FP32 partial slices to P (M x N each) instead of X;
 // returns the slice count (0: added into X), which the following
 // k_rows_norm adds to X in slice order.  Returns -1 for an unsupported shape.
@@ -804,13 +804,19 @@ int launch_gemm_residual(const float* A, const float* B, float* X, float* P, int
     if (S > 1 && launch_skinny(A, B, P, M, N, K, S, (size_t)M * N, false, s)) return S;
   }
   if (M > kSkinnyMaxM && N % 64 == 0 && K % kBK == 0) {
-    // the fewest splits (64-wide K tiles each) reaching 256 blocks, 128 x 128 tiles first
+    // the fewest splits (64-wide K tiles each) reaching 1024 blocks, 128 x 128
+    // tiles first.  Several workgroups share a CU (registers and LDS allow two
+    // of 128 x 128, four of 64 x 64), and with more of them resident each
+    // hides the others' barriers and operand loads: for 1024-row chunks the
+    // 64 x 64 tiles split 4 ways beat 128 x 128 split 4 ways (256 blocks) by
+    // 2.7 % of the whole prefill, and 128 x 128 split 8 ways by 1.2 %; a 2048-block
+    // target (64 x 64 split 8 ways) measured slower again.
     int bm = 0, S = 0;
     for (int t : {128, 64}) {
       if (N % t != 0) continue;
       const int64_t tiles = (int64_t)(N / t) * cdiv(M, t);
       for (int c = 1; c <= kMaxSplitK && K % (c * 64) == 0; c *= 2)
-        if (tiles * c >= 256) { bm = t; S = c; break; }
+        if (tiles * c >= 1024) { bm = t; S = c; break; }
       if (bm) break;
     }
     if (bm == 0) {   // too few tiles for 256 blocks: small tiles, the most splits
