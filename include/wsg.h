@@ -349,6 +349,20 @@ wsg_status wsg_gemv_q4g64_ex(int32_t M, int32_t K, int32_t T, int32_t rows_per_w
 wsg_status wsg_gemm_nt_f32(int32_t M, int32_t N, int32_t K, const float* d_A, const float* d_B, float* d_C,
                            int32_t accumulate, void* hip_stream);
 
+/* The gate/up projection of chunked prefill with its SwiGLU:
+ * ACT[M][I] = silu(A . Wg^T) * (A . Wu^T), silu(g) = g / (1 + exp(-g)), for
+ * d_Wgu = [Wg; Wu], a packed [2I][K] weight (I gate rows, then I up rows),
+ * row-major like wsg_gemm_nt_f32's B (Megakernels, "Chunked prefill for long
+ * prompts": the MLP's gate and up products as one tiled matrix product; the
+ * model's SwiGLU block for the activation).  The activation is applied in the
+ * product's epilogue, so the 2I-wide product is never stored.  M >= 1,
+ * I % 32 == 0, K % 32 == 0; A is [M][K], ACT [M][I] (caller-owned, not
+ * overlapping A or Wgu); all pointers 16-byte aligned.  Asynchronous on
+ * hip_stream.  Errors: WSG_ERR_INVALID_ARG for a bad shape, null or misaligned
+ * pointer; WSG_ERR_UNSUPPORTED for a shape no compiled kernel takes. */
+wsg_status wsg_gemm_swiglu_f32(int32_t M, int32_t I, int32_t K, const float* d_A, const float* d_Wgu, float* d_ACT,
+                               void* hip_stream);
+
 /* Read-only streaming reference for the cold-cache GEMV measurements (Our
  * Kernel Benchmark Was Measuring the System Cache, "The fix": the GEMV is
  * judged against what a plain read of the same cycling buffers reaches).

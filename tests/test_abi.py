@@ -51,6 +51,16 @@ def test_gemv_argument_validation(abi):
     assert L.wsg_stream_read(16, 60, 16, None) == abi.WSG_ERR_INVALID_ARG
     assert L.wsg_stream_read(16, 0, 16, None) == abi.WSG_ERR_INVALID_ARG
     assert L.wsg_stream_read(24, 64, 16, None) == abi.WSG_ERR_INVALID_ARG
+    # matrix-core products: bad shapes, null and misaligned pointers
+    assert L.wsg_gemm_nt_f32(4, 48, 64, 16, 16, 16, 0, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_gemm_nt_f32(4, 64, 64, 16, 16, 16, 2, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_gemm_nt_f32(4, 64, 64, 16, None, 16, 0, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_gemm_swiglu_f32(0, 64, 64, 16, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_gemm_swiglu_f32(4, 48, 64, 16, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_gemm_swiglu_f32(4, 64, 48, 16, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_gemm_swiglu_f32(4, 64, 64, 16, 16, None, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_gemm_swiglu_f32(4, 64, 64, 16, 20, 16, None) == abi.WSG_ERR_INVALID_ARG
+    assert b"aligned" in L.wsg_last_error()
 
 
 def _cfg(abi, shape, cap=16, dtype=0, chunk=0, pack=0):

@@ -50,6 +50,45 @@ def test_gemm_nt_f32(M, N, K, acc):
     assert np.all(err <= bound), f"max err {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
 
 
+# SwiGLU in the product's epilogue: small-M kernel (M <= 32), 64x64 tiles
+# with 32- and 64-wide K tiles, 128x192 tiles (the gate/up shape at 1024
+# rows), and a 128-row tile picked for a K that needs 32-wide K tiles, which
+# falls back to 64x64 tiles.
+@pytest.mark.parametrize("M,I,K", [(5, 96, 256), (32, 3072, 1024), (40, 96, 96), (97, 64, 128), (300, 3072, 1024),
+                                   (1024, 3072, 1024), (1024, 384, 160)])
+def test_gemm_swiglu_f32(M, I, K):
+    """ACT = silu(A Wg^T) * (A Wu^T) against the oracle in float64: each of the
+    two products within its FP32 summation bound, carried through the SwiGLU
+    (|silu'| <= 1.1), plus a few float ulps for exp, divide and multiply."""
+    import torch
+    import weight_streaming_gemv_amd as wsg
+    rng = np.random.default_rng(M * 31 + I + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    Wgu = (rng.standard_normal((2 * I, K)) * 0.05).astype(np.float32)
+    announce(f"gemm_swiglu M={M} I={I} K={K}")
+    got = _np(wsg.gemm_swiglu(torch.from_numpy(A).cuda(), torch.from_numpy(Wgu).cuda())).astype(np.float64)
+    assert got.shape == (M, I)
+    gu = oracle.gemv(Wgu, A).astype(np.float64)             # A @ Wgu^T, [M, 2I]
+    b = gemv_bound(oracle.gemv(np.abs(Wgu), np.abs(A)).astype(np.float64), K)
+    g, u, bg, bu = gu[:, :I], gu[:, I:], b[:, :I], b[:, I:]
+    ref = oracle.silu(g) * u
+    sg = np.abs(oracle.silu(g))
+    bound = 1.1 * bg * (np.abs(u) + bu) + (sg + 1.1 * bg) * bu + 8 * U32 * np.abs(ref) + 1e-30
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= bound), f"max err {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
+
+
+def test_gemm_swiglu_rejects_bad_shapes():
+    import torch
+    import weight_streaming_gemv_amd as wsg
+    a = torch.zeros((4, 64), device="cuda")
+    with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+        wsg.gemm_swiglu(a, torch.zeros((2 * 48, 64), device="cuda"))     # I % 32 != 0
+    with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+        wsg.gemm_swiglu(torch.zeros((4, 48), device="cuda"), torch.zeros((64, 48), device="cuda"))   # K % 32
+
+
 def test_gemm_rejects_bad_shapes():
     import torch
     import weight_streaming_gemv_amd as wsg

@@ -18,7 +18,7 @@ from ._abi import (WSG_F16, WSG_F32, WSG_GEMV_NONTEMPORAL, WSG_OPT_TIMED_STAGE, 
                    WSG_STAGE_ATTN, WSG_STAGE_DOWN, WSG_STAGE_GATEUP, WSG_STAGE_HEAD, WSG_STAGE_O,
                    WSG_STAGE_QKV, WsgError, check, wsg_config, wsg_host_weights)
 
-__all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "gemm_nt", "WsgError", "WSG_F32", "WSG_F16",
+__all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "gemm_nt", "gemm_swiglu", "WsgError", "WSG_F32", "WSG_F16",
            "WSG_STAGE_QKV", "WSG_STAGE_ATTN", "WSG_STAGE_O", "WSG_STAGE_GATEUP", "WSG_STAGE_DOWN",
            "WSG_STAGE_HEAD", "WSG_OPT_USE_GRAPH", "WSG_OPT_TIMED_STAGE", "WSG_GEMV_NONTEMPORAL", "stream_read", "lib"]
 
@@ -84,6 +84,17 @@ def gemm_nt(A, B, C=None, accumulate: bool = False, stream=None):
     check(_abi.lib().wsg_gemm_nt_f32(M, N, K, A.data_ptr(), B.data_ptr(), C.data_ptr(), int(accumulate),
                                      _stream_handle(stream)))
     return C
+
+
+def gemm_swiglu(A, Wgu, ACT=None, stream=None):
+    """``ACT[M, I] = silu(A @ Wg^T) * (A @ Wu^T)`` for ``Wgu = [Wg; Wu]`` ([2I, K]) on FP32 MFMA."""
+    torch = _torch()
+    M, K = A.shape
+    I = Wgu.shape[0] // 2
+    if ACT is None:
+        ACT = torch.empty((M, I), dtype=torch.float32, device=A.device)
+    check(_abi.lib().wsg_gemm_swiglu_f32(M, I, K, A.data_ptr(), Wgu.data_ptr(), ACT.data_ptr(), _stream_handle(stream)))
+    return ACT
 
 
 def stream_read(buf, out=None, stream=None):

@@ -80,6 +80,21 @@ extern "C" wsg_status wsg_gemm_nt_f32(int32_t M, int32_t N, int32_t K, const flo
   return check_launch("wsg_gemm_nt_f32");
 }
 
+extern "C" wsg_status wsg_gemm_swiglu_f32(int32_t M, int32_t I, int32_t K, const float* d_A, const float* d_Wgu,
+                                         float* d_ACT, void* hip_stream) {
+  clear_error();
+  if (M < 1 || I < 32 || I % 32 != 0 || K < 32 || K % 32 != 0)
+    return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_swiglu_f32: need M >= 1, I %% 32 == 0, K %% 32 == 0 (M=%d I=%d K=%d)", M, I,
+                K);
+  if (!d_A || !d_Wgu || !d_ACT) return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_swiglu_f32: null pointer");
+  if (((uintptr_t)d_A | (uintptr_t)d_Wgu | (uintptr_t)d_ACT) & 15)
+    return fail(WSG_ERR_INVALID_ARG, "wsg_gemm_swiglu_f32: pointers must be 16-byte aligned");
+  (void)hipGetLastError();
+  if (!gemm_swiglu_f32(d_A, d_Wgu, d_ACT, M, I, K, static_cast<hipStream_t>(hip_stream)))
+    return fail(WSG_ERR_UNSUPPORTED, "wsg_gemm_swiglu_f32: shape not supported");
+  return check_launch("wsg_gemm_swiglu_f32");
+}
+
 extern "C" wsg_status wsg_stream_read(const void* d_buf, int64_t bytes, float* d_out, void* hip_stream) {
   clear_error();
   if (!d_buf || !d_out) return fail(WSG_ERR_INVALID_ARG, "wsg_stream_read: null pointer");

@@ -2,25 +2,27 @@
 // per chunk, every row attending to its whole causal prefix across chunks
 // (Megakernels, "Chunked prefill for long prompts").
 //
-// Per chunk and layer (the pages' 11 ordered stages, here 9 launches):
+// Per chunk and layer (the pages' 11 ordered stages, here 8 launches):
 //   rows_norm   [residual += pending split-K partials] + RMSNorm, one block per row
 //   gemm        QKV projection  [n x H] . W_qkv^T   (FP32 MFMA)
 //   rows_qkv    per-head Q/K RMSNorm + RoPE; K/V written to cache rows p0..p0+n-1
-//   attn        causal attention of the n rows over keys 0..p0+r (VALU, LDS tiles)
-//   gemm+res    O projection: residual added in the epilogue, or (few rows)
-//               split-K partial slices that the next rows_norm adds
+//   attn        causal attention of the n rows over keys 0..p0+r (FP32 MFMA)
+//   gemm+res    O projection: residual added in the epilogue, or split-K
+//               partial slices that the next rows_norm adds
 //   rows_norm   post-attention RMSNorm
-//   gemm        gate/up projection [n x 2I]
-//   rows_swiglu SwiGLU
+//   gemm+swiglu gate/up projection [n x 2I] with the SwiGLU in its epilogue
+//               (only the [n x I] activation is stored)
 //   gemm+res    down projection (as the O projection)
-// The projections are the only dense contractions and the only MFMA users:
-// a tiled kernel for many rows, a small-M kernel (weights streamed straight
-// into registers, K split over waves and blocks) for up to 32 rows.
-// The chunk runs exactly n rows: the GEMM masks its ragged last row tile, so
-// no padding rows exist.  Within one prefill call the last prompt row goes
-// through the decode forward (the only row that reaches the head), so every
-// chunk stops its last layer after the K/V write (Benchmark methodology,
-// "Long-document chunked prefill": nonterminal chunks prune the final layer).
+// The projections and attention's two products are the dense contractions
+// and the MFMA users: a tiled kernel for many rows, a small-M kernel
+// (weights streamed straight into registers, K split over waves and blocks)
+// for up to 32 rows.  The chunk runs exactly n rows: the GEMM masks its
+// ragged last row tile, so no padding rows exist.  Every chunk stops its last
+// layer after the K/V write (Benchmark methodology, "Long-document chunked
+// prefill": nonterminal chunks prune the final layer), except that the
+// prompt's last row completes it alone (one-row launches of the same
+// kernels) and hands its residual to the decode head: the only row that
+// reaches the head.
 #include <algorithm>
 #include <type_traits>
 
@@ -56,10 +58,16 @@ typedef float f4v_t __attribute__((ext_vector_type(4)));
 // per part.  A 64-wide K tile (K ranges that are multiples of 64) gives
 // each wave 32*TM*TN MFMAs (8192 cycles for a 64 x 64 wave tile) between
 // barriers, which covers the latency of the next tile's global loads.
+// With SWI, B is a packed gate/up matrix (N/2 gate rows, then N/2 up rows):
+// tile x takes gate rows [x*BN/2, (x+1)*BN/2) as its first BN/2 columns and
+// the matching up rows as the rest, so each gate wave's up partner is the
+// wave beside it; the up waves stage their sums in LDS and the gate waves
+// write C[M x N/2] = silu(gate) * up (the same per-element sums as without
+// SWI).
 constexpr int kBK = 32;                   // K granularity of the shapes accepted (and of the small-M kernel)
 constexpr int kLdsPad = 4;                // floats of padding per LDS row
 
-template <int BM, int BN, int BK, bool ACC, int WV>
+template <int BM, int BN, int BK, bool ACC, int WV, bool SWI = false>
 __global__ __launch_bounds__(64 * WV) void k_gemm_nt(const float* __restrict__ A, const float* __restrict__ B,
                                                      float* __restrict__ C, int M, int N, int K, int kspan,
                                                      size_t c_split) {
@@ -73,6 +81,7 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_nt(const float* __restrict__ A
   constexpr int B_LOADS = BN * F4_ROW / kThreads;
   static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "whole 32 x 32 MFMA tiles per wave");
   static_assert(BM * F4_ROW % kThreads == 0 && BN * F4_ROW % kThreads == 0, "whole float4 per thread");
+  static_assert(!SWI || (!ACC && BM * (BN / 2) <= BN * kLdsRow), "SwiGLU: no accumulation, up sums fit in Bs");
   __shared__ float As[BM * kLdsRow];
   __shared__ float Bs[BN * kLdsRow];
 
@@ -80,6 +89,7 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_nt(const float* __restrict__ A
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int nb = blockIdx.x * (BN / 2);   // SWI: the tile's first gate row (output column)
   const int li = lane & 31, lh = lane >> 5;
   A += (size_t)blockIdx.z * kspan;   // this split's K range (row stride stays K)
   B += (size_t)blockIdx.z * kspan;
@@ -106,7 +116,8 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_nt(const float* __restrict__ A
     }                                                                                              \
     _Pragma("unroll") for (int i = 0; i < B_LOADS; ++i) {                                          \
       const int idx = tid + kThreads * i, row = idx / F4_ROW, c4 = idx % F4_ROW;                        \
-      rb[i] = *reinterpret_cast<const f4_t*>(B + (size_t)(n0 + row) * K + (K0) + 4 * c4);          \
+      const int brow = !SWI ? n0 + row : row < BN / 2 ? nb + row : N / 2 + nb + row - BN / 2;        \
+      rb[i] = *reinterpret_cast<const f4_t*>(B + (size_t)brow * K + (K0) + 4 * c4);                \
     }                                                                                              \
   }
 
@@ -161,19 +172,47 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_nt(const float* __restrict__ A
 #undef WSG_GEMM_FRAGS
 #undef WSG_GEMM_MFMA
 
+  if constexpr (SWI) {
+    constexpr int US = BN / 2;   // row of the staged up sums
+    float* s_up = Bs;
+    __syncthreads();             // every wave has read its last operands from Bs
+    if (wn != 0) {
 #pragma unroll
-  for (int a = 0; a < TM; ++a)
+      for (int a = 0; a < TM; ++a)
 #pragma unroll
-    for (int b = 0; b < TN; ++b)
+        for (int b = 0; b < TN; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm + a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const int col = n0 + wn + b * 32 + li;
-        if (row < M) {
-          float* p = C + (size_t)row * N + col;
-          *p = ACC ? *p + acc[a][b][r] : acc[a][b][r];
+          for (int r = 0; r < 16; ++r)
+            s_up[(wm + a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)) * US + b * 32 + li] = acc[a][b][r];
+    }
+    __syncthreads();
+    if (wn == 0) {
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rl = wm + a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3), cl = b * 32 + li;
+            const float g = acc[a][b][r], u = s_up[rl * US + cl];
+            if (m0 + rl < M) C[(size_t)(m0 + rl) * (N / 2) + nb + cl] = g / (1.0f + expf(-g)) * u;
+          }
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm + a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int col = n0 + wn + b * 32 + li;
+          if (row < M) {
+            float* p = C + (size_t)row * N + col;
+            *p = ACC ? *p + acc[a][b][r] : acc[a][b][r];
+          }
         }
-      }
+  }
 }
 
 // ------------------------------------------------------- small-M GEMM
@@ -396,17 +435,6 @@ __global__ __launch_bounds__(256) void k_rows_qkv(float* __restrict__ QKV, int n
     float* dst = k_cache + ((size_t)(hh - n_q) * cap + pos) * kD;
     dst[lane] = o_lo;
     dst[lane + 64] = o_hi;
-  }
-}
-
-// ACT[r][i] = silu(GU[r][i]) * GU[r][I + i]
-__global__ __launch_bounds__(256) void k_rows_swiglu(const float* __restrict__ GU, int n, int I,
-                                                     float* __restrict__ ACT) {
-  const size_t total = (size_t)n * I;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
-    const size_t r = e / I, i = e - r * I;
-    const float g = GU[r * 2 * I + i], u = GU[r * 2 * I + I + i];
-    ACT[e] = g / (1.0f + expf(-g)) * u;
   }
 }
 
@@ -722,9 +750,11 @@ bool launch_skinny(const float* A, const float* B, float* C, int M, int N, int K
 
 // Tiled launch of BM x BN tiles with K split S ways (S slices c_split
 // apart): 64-wide K tiles when the split's K range allows, else 32-wide.
+// With swi (one slice, no accumulation): the SwiGLU epilogue, C being
+// M x N/2; false when the tile cannot stage its up sums in LDS.
 template <int BM, int BN>
-void launch_tiled(const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split, bool acc,
-                  hipStream_t s) {
+bool launch_tiled(const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split, bool acc,
+                  hipStream_t s, bool swi = false) {
   const dim3 grid(N / BN, cdiv(M, BM), S);
   const int kspan = K / S;
   auto go = [&](auto bk) {
@@ -732,13 +762,23 @@ void launch_tiled(const float* A, const float* B, float* C, int M, int N, int K,
     // 128-row tiles: 8 waves, two per SIMD (one computes while the other
     // reads its operands from LDS); 64 x 64 tiles: 4 waves
     constexpr int WV = BM == 128 ? 8 : 4;
+    if (swi) {
+      if constexpr (BM / 2 <= BK + kLdsPad) {
+        if (S != 1 || acc) return false;
+        hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, false, WV, true>), grid, dim3(64 * WV), 0, s, A, B, C, M, N, K,
+                           kspan, c_split);
+        return true;
+      }
+      return false;
+    }
     if (acc)
       hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, true, WV>), grid, dim3(64 * WV), 0, s, A, B, C, M, N, K, kspan, c_split);
     else
       hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, false, WV>), grid, dim3(64 * WV), 0, s, A, B, C, M, N, K, kspan, c_split);
+    return true;
   };
-  if (kspan % 64 == 0) go(std::integral_constant<int, 64>{});
-  else go(std::integral_constant<int, 32>{});
+  if (kspan % 64 == 0) return go(std::integral_constant<int, 64>{});
+  return go(std::integral_constant<int, 32>{});
 }
 
 // Tile of the tiled kernel for an M x N product: the one with the fewest
@@ -757,31 +797,30 @@ Tile pick_tile(int M, int N) {
   return best;
 }
 
-void launch_tile(Tile t, const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split,
-                 bool acc, hipStream_t s) {
-  if (t.bm == 128 && t.bn == 192) launch_tiled<128, 192>(A, B, C, M, N, K, S, c_split, acc, s);
-  else if (t.bm == 128) launch_tiled<128, 128>(A, B, C, M, N, K, S, c_split, acc, s);
-  else launch_tiled<64, 64>(A, B, C, M, N, K, S, c_split, acc, s);
+bool launch_tile(Tile t, const float* A, const float* B, float* C, int M, int N, int K, int S, size_t c_split,
+                 bool acc, hipStream_t s, bool swi = false) {
+  if (t.bm == 128 && t.bn == 192) return launch_tiled<128, 192>(A, B, C, M, N, K, S, c_split, acc, s, swi);
+  if (t.bm == 128) return launch_tiled<128, 128>(A, B, C, M, N, K, S, c_split, acc, s, swi);
+  return launch_tiled<64, 64>(A, B, C, M, N, K, S, c_split, acc, s, swi);
 }
 
 // M <= 32 with a compiled K: the small-M kernel; otherwise the tiled kernel.
 bool launch_gemm(const float* A, const float* B, float* C, int M, int N, int K, bool acc, hipStream_t s) {
   if (M < 1 || N % 64 != 0 || K % kBK != 0) return false;
   if (M <= kSkinnyMaxM && launch_skinny(A, B, C, M, N, K, 1, 0, acc, s)) return true;
-  launch_tile(pick_tile(M, N), A, B, C, M, N, K, 1, 0, acc, s);
-  return true;
+  return launch_tile(pick_tile(M, N), A, B, C, M, N, K, 1, 0, acc, s);
 }
 
 // ACT[M x I] = silu(A . Wg^T) * (A . Wu^T) for the packed gate/up matrix Wgu
-// (I gate rows, then I up rows): up to 32 rows in the small-M kernel's
-// epilogue, otherwise the tiled product into GU followed by k_rows_swiglu.
-bool launch_gemm_swiglu(const float* A, const float* Wgu, float* GU, float* ACT, int M, int I, int K,
-                        hipStream_t s) {
-  if (M <= kSkinnyMaxM && (2 * I) % 64 == 0 && launch_skinny(A, Wgu, ACT, M, 2 * I, K, 1, 0, false, s, true))
-    return true;
-  if (!launch_gemm(A, Wgu, GU, M, 2 * I, K, false, s)) return false;
-  hipLaunchKernelGGL(k_rows_swiglu, dim3(min(cdiv(M * I, 256), 4096)), dim3(256), 0, s, GU, M, I, ACT);
-  return true;
+// (I gate rows, then I up rows), the SwiGLU computed in the epilogue of the
+// product: up to 32 rows in the small-M kernel, otherwise in the tiled one
+// (on the tile the plain product would take, or on 64 x 64 tiles where that
+// one cannot stage its up sums).  Same shape rules as launch_gemm for N = 2I.
+bool launch_gemm_swiglu(const float* A, const float* Wgu, float* ACT, int M, int I, int K, hipStream_t s) {
+  if (M < 1 || I < 1 || (2 * I) % 64 != 0 || K % kBK != 0) return false;
+  if (M <= kSkinnyMaxM && launch_skinny(A, Wgu, ACT, M, 2 * I, K, 1, 0, false, s, true)) return true;
+  return launch_tile(pick_tile(M, 2 * I), A, Wgu, ACT, M, 2 * I, K, 1, 0, false, s, true) ||
+         launch_tile(Tile{64, 64}, A, Wgu, ACT, M, 2 * I, K, 1, 0, false, s, true);
 }
 
 // X[M x N] += A . B^T for a residual stream consumed by k_rows_norm.  A
@@ -824,10 +863,7 @@ int launch_gemm_residual(const float* A, const float* B, float* X, float* P, int
       S = 1;
       while (S < kMaxSplitK && K % (2 * S * 64) == 0) S *= 2;
     }
-    if (S > 1) {
-      launch_tile(Tile{bm, bm}, A, B, P, M, N, K, S, (size_t)M * N, false, s);
-      return S;
-    }
+    if (S > 1 && launch_tile(Tile{bm, bm}, A, B, P, M, N, K, S, (size_t)M * N, false, s)) return S;
   }
   return launch_gemm(A, B, X, M, N, K, true, s) ? 0 : -1;
 }
@@ -836,6 +872,10 @@ int launch_gemm_residual(const float* A, const float* B, float* X, float* P, int
 
 bool gemm_nt_f32(const float* A, const float* B, float* C, int M, int N, int K, bool accumulate, hipStream_t s) {
   return launch_gemm(A, B, C, M, N, K, accumulate, s);
+}
+
+bool gemm_swiglu_f32(const float* A, const float* Wgu, float* ACT, int M, int I, int K, hipStream_t s) {
+  return launch_gemm_swiglu(A, Wgu, ACT, M, I, K, s);
 }
 
 PrefillLayout prefill_layout(int rows, int H, int I, int Q, int KV, size_t es, size_t base) {
@@ -850,7 +890,6 @@ PrefillLayout prefill_layout(int rows, int H, int I, int Q, int KV, size_t es, s
   p.qkv = take((size_t)rows * (Q + 2 * KV) * 4);
   p.o = take((size_t)rows * Q * 4);
   p.act = take((size_t)rows * I * 4);
-  p.gu = take((size_t)rows * 2 * I * 4);
   p.part = take((size_t)kMaxSplitK * rows * H * 4);   // split-K partial slices of a residual GEMM
   p.total = off;
   return p;
@@ -874,7 +913,6 @@ wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, bool to_head, 
   float* QKV = reinterpret_cast<float*>(c.ws + c.pf.qkv);
   float* O = reinterpret_cast<float*>(c.ws + c.pf.o);
   float* ACT = reinterpret_cast<float*>(c.ws + c.pf.act);
-  float* GU = reinterpret_cast<float*>(c.ws + c.pf.gu);
   float* PART = reinterpret_cast<float*>(c.ws + c.pf.part);
   const float* E = static_cast<const float*>(a.embed);
   (void)hipGetLastError();
@@ -911,7 +949,7 @@ wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, bool to_head, 
       if (n_part < 0) return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
       if (!launch_rows_norm(Xr, PART, n_part, (const float*)L.post_norm, nr, H, a.eps, A, s))
         return fail(WSG_ERR_UNSUPPORTED, "row norm shape");
-      if (!launch_gemm_swiglu(A, static_cast<const float*>(L.wgu), GU, ACT, nr, I, H, s))
+      if (!launch_gemm_swiglu(A, static_cast<const float*>(L.wgu), ACT, nr, I, H, s))
         return fail(WSG_ERR_UNSUPPORTED, "gemm shape");
       n_part = launch_gemm_residual(ACT, static_cast<const float*>(L.wd), Xr, PART, nr, H, I, s);
       if (n_part < 0) return fail(WSG_ERR_UNSUPPORTED, "gemm shape");

@@ -14,7 +14,7 @@ namespace wsg {
 // Byte offsets (inside the workspace) of the chunk scratch for C rows.
 struct PrefillLayout {
   int rows = 0;
-  size_t x = 0, a = 0, qkv = 0, o = 0, act = 0, gu = 0, part = 0, total = 0;
+  size_t x = 0, a = 0, qkv = 0, o = 0, act = 0, part = 0, total = 0;
 };
 
 PrefillLayout prefill_layout(int rows, int H, int I, int Q, int KV, size_t es, size_t base);
@@ -42,5 +42,7 @@ wsg_status run_prefill_chunks(const PrefillCtx& c, int p0, int n, bool to_head, 
 
 // C[M x N] (+)= A[M x K] . B[N x K]^T on FP32 MFMA (N % 64 == 0, K % 32 == 0).
 bool gemm_nt_f32(const float* A, const float* B, float* C, int M, int N, int K, bool accumulate, hipStream_t s);
+// ACT[M x I] = silu(A . Wg^T) * (A . Wu^T), Wgu = [Wg; Wu] packed [2I x K].
+bool gemm_swiglu_f32(const float* A, const float* Wgu, float* ACT, int M, int I, int K, hipStream_t s);
 
 }  // namespace wsg
