@@ -375,7 +375,8 @@ int attn_mode(const wsg_model* m, int n_keys, int tokens) {
 // state for the merge launch to read), so fewer, longer blocks win once
 // there are enough of them to keep the memory system busy; a sweep of
 // fixed sizes on the 8-KV-head model at 1.1k / 2.1k / 4.2k keys was best
-// at 64 / 96 / 192 keys, i.e. 20-24 splits per head.
+// at 64 / 96 / 192 keys, i.e. 20-24 splits per head.  Targets of 384 or 512
+// blocks (two per CU fit) measured 4 % slower per token at 2k-4k keys.
 constexpr int kAttnTargetBlocks = 192;
 
 // The size is taken from a ladder with four steps per doubling (64, 80, 96,
