@@ -332,6 +332,10 @@ wsg_status wsg_gemv_ex(int32_t w_dtype, int32_t M, int32_t K, int32_t T, int32_t
 wsg_status wsg_gemv_q4g64(int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,
                           const uint32_t* d_Wq, const void* d_scales, const void* d_X,
                           float* d_Y, void* hip_stream);
+/* wsg_gemv_q4g64 with an explicit launch shape (grid_blocks and flags as
+ * for wsg_gemv_ex).  A block is 4 waves, except at K = 14336, where the
+ * activations staged per block are 28 KiB per row of X and a block is 16
+ * waves (one staged copy serves four times the rows). */
 wsg_status wsg_gemv_q4g64_ex(int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,
                              int32_t grid_blocks, int32_t flags,
                              const uint32_t* d_Wq, const void* d_scales, const void* d_X,

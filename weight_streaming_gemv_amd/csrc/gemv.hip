@@ -188,8 +188,19 @@ __global__ __launch_bounds__(kBlock) void k_gemv_scalar(const TW* __restrict__ W
 // nibble pair (j, j+4) that one 32-bit word yields, and placed so that the
 // 64 lanes of a wave read 64 consecutive 16-byte LDS slots (lane l's word i
 // of chunk c sits at c*256 + i*64 + l): no bank conflicts.
-template <int K, int R, int T, bool NT>
-__global__ __launch_bounds__(kBlock) void k_gemv_q4(const uint32_t* __restrict__ Wq,
+// Eight FP16 activations (halves 0..7 of one 16-byte word) as the pairs
+// (0,4) (1,5) (2,6) (3,7) that the nibble pairs of one weight word meet.
+__device__ __forceinline__ uint4 nibble_pair_order(uint4 h) {
+  uint4 p;
+  p.x = (h.x & 0xFFFFu) | (h.z << 16);
+  p.y = (h.x >> 16) | (h.z & 0xFFFF0000u);
+  p.z = (h.y & 0xFFFFu) | (h.w << 16);
+  p.w = (h.y >> 16) | (h.w & 0xFFFF0000u);
+  return p;
+}
+
+template <int K, int R, int T, bool NT, int WV = kWavesPerBlock>
+__global__ __launch_bounds__(64 * WV) void k_gemv_q4(const uint32_t* __restrict__ Wq,
                                                     const __half* __restrict__ S,
                                                     const __half* __restrict__ X,
                                                     float* __restrict__ Y, int M) {
@@ -198,36 +209,32 @@ __global__ __launch_bounds__(kBlock) void k_gemv_q4(const uint32_t* __restrict__
   constexpr int G = K / 64;      // groups (scales) per row
   static_assert(K % 2048 == 0, "fixed-K int4 kernel needs K % 2048 == 0");
   __shared__ uint4 xs[T][W8];
-  static_assert((T * W8) % kBlock == 0, "staging assumes whole rounds of the block");
-  constexpr int kStage = T * W8 / kBlock;
+  constexpr int kThreads = 64 * WV;
+  constexpr int kStage = (T * W8 + kThreads - 1) / kThreads;
+  constexpr bool kRagged = (T * W8) % kThreads != 0;   // the last round is partial
   // all staging loads in flight at once, then the permuted LDS stores
   uint4 hx[kStage];
 #pragma unroll
   for (int it = 0; it < kStage; ++it) {
-    const int i = threadIdx.x + it * kBlock;
+    int i = threadIdx.x + it * kThreads;
+    if constexpr (kRagged) i = min(i, T * W8 - 1);   // a partial round re-reads the last word
     const int t = i / W8, gi = i - t * W8;
     hx[it] = *reinterpret_cast<const uint4*>(X + (size_t)t * K + gi * 8);
   }
 #pragma unroll
   for (int it = 0; it < kStage; ++it) {
-    const int i = threadIdx.x + it * kBlock;
+    const int i = threadIdx.x + it * kThreads;
+    if (kRagged && i >= T * W8) break;
     const int t = i / W8, gi = i - t * W8;
-    const uint4 h = hx[it];
-    // halves 0..7 -> pairs (0,4) (1,5) (2,6) (3,7)
-    uint4 p;
-    p.x = (h.x & 0xFFFFu) | (h.z << 16);
-    p.y = (h.x >> 16) | (h.z & 0xFFFF0000u);
-    p.z = (h.y & 0xFFFFu) | (h.w << 16);
-    p.w = (h.y >> 16) | (h.w & 0xFFFF0000u);
     const int c = gi >> 8, w = gi & 255;
-    xs[t][(c << 8) + ((w & 3) << 6) + (w >> 2)] = p;
+    xs[t][(c << 8) + ((w & 3) << 6) + (w >> 2)] = nibble_pair_order(hx[it]);
   }
   __syncthreads();
 
   const int lane = lane_id();
   const h2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
   const int ngroups = (M + R - 1) / R;
-  for (int g = blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += gridDim.x * kWavesPerBlock) {
+  for (int g = blockIdx.x * WV + wave_id(); g < ngroups; g += gridDim.x * WV) {
     const int row0 = g * R;
     float acc[R][T];
 #pragma unroll
@@ -393,8 +400,19 @@ void launch_q4(int M, int K, int grid_req, bool nt, const uint32_t* Wq, const __
     return;                                                                                                \
   }
   WSG_Q4(4096)
-  WSG_Q4(14336)
 #undef WSG_Q4
+  if (K == 14336) {
+    // long rows: 16-wave workgroups, so one LDS copy of the 28 KiB (per row
+    // of X) activations serves four times the waves (cold sweep of
+    // 4096 x 14336: 10.5 -> 9.4 us for one row of X, 15.3 -> 11.0 us for two)
+    constexpr int WV = 16;
+    const int ngroups = (M + R - 1) / R;
+    const int one_shot = (ngroups + WV - 1) / WV;
+    const int g16 = grid_req > 0 && grid_req < one_shot ? grid_req : one_shot;
+    if (nt) hipLaunchKernelGGL((k_gemv_q4<14336, R, T, true, WV>), dim3(g16), dim3(64 * WV), 0, s, Wq, S, X, Y, M);
+    else hipLaunchKernelGGL((k_gemv_q4<14336, R, T, false, WV>), dim3(g16), dim3(64 * WV), 0, s, Wq, S, X, Y, M);
+    return;
+  }
   hipLaunchKernelGGL((k_gemv_q4_anyk<R, T>), dim3(grid), dim3(kBlock), 0, s, Wq, S, X, Y, M, K);
 }
 

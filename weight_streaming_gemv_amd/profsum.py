@@ -131,13 +131,16 @@ def sweep_table(path):
                     for nt in ("false", "true"):   # ordinary / non-temporal weight loads
                         seen = set()
                         grids = (0, 256, 512) if dt == "q4g64" else ((0, 1280, 2048, 4096) if M > 100000 else (0,))
+                        # int4 rows of 14336 run 16-wave workgroups, every other shape 4-wave ones
+                        wv = 16 if dt == "q4g64" and K == 14336 else 4
                         for G in grids:
-                            one = _ceil(_ceil(M, R), 4)
+                            one = _ceil(_ceil(M, R), wv)
                             blocks = one if G == 0 or G >= one else G
                             if blocks in seen:
                                 continue
                             seen.add(blocks)
-                            key = (f"{kname}<{K}, {R}, {T}, {nt}>", blocks)
+                            tmpl = f"{K}, {R}, {T}, {nt}, {wv}" if dt == "q4g64" else f"{K}, {R}, {T}, {nt}"
+                            key = (f"{kname}<{tmpl}>", blocks)
                             ds = idx.get(key)
                             if not ds:
                                 continue
