@@ -52,10 +52,10 @@ def test_gemm_nt_f32(M, N, K, acc):
 
 # SwiGLU in the product's epilogue: small-M kernel (M <= 32), 64x64 tiles
 # with 32- and 64-wide K tiles, 128x192 tiles (the gate/up shape at 1024
-# rows), and a 128-row tile picked for a K that needs 32-wide K tiles, which
-# falls back to 64x64 tiles.
+# rows), and 128x192 picked for a K that needs 32-wide K tiles (1056), where
+# the up sums do not fit the LDS B tile and 64x64 tiles take over.
 @pytest.mark.parametrize("M,I,K", [(5, 96, 256), (32, 3072, 1024), (40, 96, 96), (97, 64, 128), (300, 3072, 1024),
-                                   (1024, 3072, 1024), (1024, 384, 160)])
+                                   (1024, 3072, 1024), (1024, 384, 160), (1024, 3072, 1056)])
 def test_gemm_swiglu_f32(M, I, K):
     """ACT = silu(A Wg^T) * (A Wu^T) against the oracle in float64: each of the
     two products within its FP32 summation bound, carried through the SwiGLU
