@@ -92,6 +92,16 @@ def test_q4_ragged(M, K, T):
     _run_q4(M, K, T, (2,), seed=22, grid=3, flags=1)
 
 
+@pytest.mark.parametrize("M,K", [(1000, 14336), (999, 4096)])
+@pytest.mark.parametrize("T", [1, 2])
+def test_q4_fixed_k_ragged_and_looping(M, K, T):
+    """The fixed-K int4 kernels (16-wave workgroups with a partial last round of
+    activation staging at K = 14336, 4-wave ones at K = 4096) on a ragged row
+    count: one-shot grids, and a grid-stride loop over three workgroups."""
+    _run_q4(M, K, T, (1, 4), seed=23)
+    _run_q4(M, K, T, (2,), seed=23, grid=3, flags=1)
+
+
 def test_gemv_determinism():
     import torch
     import weight_streaming_gemv_amd as wsg
