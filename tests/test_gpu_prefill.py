@@ -184,6 +184,23 @@ def test_tiny_qwen3_chunked_prefill(c1_w, n_prompt, chunk):
     m.close()
 
 
+def test_qwen3x2_chunk_2048_crosses_a_chunk(c1_w):
+    """A 2100-id prompt at 2048-row chunks (Qwen3 layer widths, 2 layers): the
+    residual projections of the full chunk take 128 x 128 tiles with K split
+    8 ways, the gate/up product its SwiGLU epilogue on 128 x 192 tiles, and a
+    52-row second chunk attends across the boundary; every K/V entry, the
+    first token and its logits, then decode steps, against the oracle."""
+    import weight_streaming_gemv_amd as wsg
+    sh = QWEN3_0_6B.with_layers(2)
+    cap = 2112
+    m = wsg.Model(sh, c1_w, max_context=cap, prefill_chunk=2048)
+    orc = oracle.OracleModel(sh, c1_w, cap)
+    prompt = prompt_ids(PROMPT_SEEDS["heldout"], 2100, sh.vocab)
+    toks, _, ck = lockstep(m, orc, prompt, 3, label="qwen3x2 chunk 2048")
+    print(f"chunk 2048: max |dlogit| {ck.max_logit_err:.2e} max |dkv| {ck.max_kv_err:.2e}")
+    m.close()
+
+
 def test_chunked_prefill_config_checks(c1_w):
     import weight_streaming_gemv_amd as wsg
     sh = QWEN3_0_6B.with_layers(2)
