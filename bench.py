@@ -850,7 +850,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one MI355X: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         return 2
 

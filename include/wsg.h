@@ -37,7 +37,7 @@ typedef enum {
   WSG_ERR_OUT_OF_RANGE = -2,  /* token id or position outside its range   */
   WSG_ERR_STATE = -3,         /* call not valid in the model's state      */
   WSG_ERR_HIP = -4,           /* a HIP runtime call failed                */
-  WSG_ERR_UNSUPPORTED = -5    /* valid, but a shape this build does not run */
+  WSG_ERR_UNSUPPORTED = -5    /* valid, but a shape no compiled kernel takes */
 } wsg_status;
 
 /* Storage dtype of weights, KV cache, logits and stage outputs.  Reductions
