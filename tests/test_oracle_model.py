@@ -164,9 +164,10 @@ def test_rejects_bad_ids_and_capacity():
 
 # ---------------------------------------------------------------- brute force
 def _rms(v, g, eps):
-    ms = math.fsum(a * a for a in v) / len(v)
+    # float(): a NumPy scalar gain would pull the product down to its own precision
+    ms = math.fsum(float(a) * float(a) for a in v) / len(v)
     r = 1.0 / math.sqrt(ms + eps)
-    return [a * r * b for a, b in zip(v, g)]
+    return [float(a) * r * float(b) for a, b in zip(v, g)]
 
 
 def _mv(wm, v):
@@ -177,11 +178,29 @@ def _f32(v):
     return [float(np.float32(a)) for a in v]
 
 
-def brute_generate(sh, w, prompt, n_out):
-    """Token-at-a-time forward written with Python lists and math.fsum."""
+def _f16(v):
+    return [float(np.float16(a)) for a in v]
+
+
+# Stored values of the brute force, by stage: the embedding gather, the eight
+# stage outputs of a layer (Megakernels, "GPU-wide end-to-end generation"),
+# the final norm and the logits.
+BRUTE_STAGES = ("gather", "norm_in", "qkv", "qk_rope", "attn", "o_res", "norm_post", "act", "down_res",
+                "norm_final", "logits")
+
+
+def brute_generate(sh, w, prompt, n_out, store=_f32, skip=None):
+    """Token-at-a-time forward written with Python lists and math.fsum.
+
+    ``store`` rounds a stored vector to the storage dtype (``_f32`` or ``_f16``);
+    ``skip`` names one entry of ``BRUTE_STAGES`` whose rounding is left out (a
+    planted slip, to show that the comparison sees that stage's rounding)."""
     d, hq, hkv, eps = sh.head_dim, sh.n_q_heads, sh.n_kv_heads, sh.rms_eps
     K = [[[] for _ in range(hkv)] for _ in range(sh.n_layers)]
     V = [[[] for _ in range(hkv)] for _ in range(sh.n_layers)]
+
+    def rd(stage, v):
+        return list(v) if stage == skip else store(v)
 
     def rot(u, p):
         half = d // 2
@@ -193,13 +212,13 @@ def brute_generate(sh, w, prompt, n_out):
         return out
 
     def step(tok, p):
-        x = [float(a) for a in w["embed"][tok]]
+        x = rd("gather", [float(a) for a in w["embed"][tok]])
         for l, lw in enumerate(w["layers"]):
-            a = _f32(_rms(x, lw["in_norm"], eps))
-            q, k, v = _f32(_mv(lw["wq"], a)), _f32(_mv(lw["wk"], a)), _f32(_mv(lw["wv"], a))
-            qs = [_f32(rot(_rms(q[h * d:(h + 1) * d], lw["q_norm"], eps), p)) for h in range(hq)]
+            a = rd("norm_in", _rms(x, lw["in_norm"], eps))
+            q, k, v = rd("qkv", _mv(lw["wq"], a)), rd("qkv", _mv(lw["wk"], a)), rd("qkv", _mv(lw["wv"], a))
+            qs = [rd("qk_rope", rot(_rms(q[h * d:(h + 1) * d], lw["q_norm"], eps), p)) for h in range(hq)]
             for j in range(hkv):
-                K[l][j].append(_f32(rot(_rms(k[j * d:(j + 1) * d], lw["k_norm"], eps), p)))
+                K[l][j].append(rd("qk_rope", rot(_rms(k[j * d:(j + 1) * d], lw["k_norm"], eps), p)))
                 V[l][j].append(v[j * d:(j + 1) * d])
             o = []
             for h in range(hq):
@@ -209,14 +228,14 @@ def brute_generate(sh, w, prompt, n_out):
                 e = [math.exp(t - mx) for t in s]
                 den = math.fsum(e)
                 o += [math.fsum(e[i] * V[l][j][i][c] for i in range(len(e))) / den for c in range(d)]
-            o = _f32(o)
-            x = _f32([a + b for a, b in zip(x, _mv(lw["wo"], o))])
-            b = _f32(_rms(x, lw["post_norm"], eps))
+            o = rd("attn", o)
+            x = rd("o_res", [a + b for a, b in zip(x, _mv(lw["wo"], o))])
+            b = rd("norm_post", _rms(x, lw["post_norm"], eps))
             g, u = _mv(lw["wg"], b), _mv(lw["wu"], b)
-            act = _f32([gi / (1.0 + math.exp(-gi)) * ui for gi, ui in zip(g, u)])
-            x = _f32([a + c for a, c in zip(x, _mv(lw["wd"], act))])
-        hvec = _f32(_rms(x, w["final_norm"], eps))
-        return _f32(_mv(w["embed"], hvec))
+            act = rd("act", [gi / (1.0 + math.exp(-gi)) * ui for gi, ui in zip(g, u)])
+            x = rd("down_res", [a + c for a, c in zip(x, _mv(lw["wd"], act))])
+        hvec = rd("norm_final", _rms(x, w["final_norm"], eps))
+        return rd("logits", _mv(w["embed"], hvec))
 
     out, logits = [], None
     for p, t in enumerate(prompt):
@@ -247,3 +266,66 @@ def test_tiny_model_brute_force():
     ot, orec = m.generate(prompt, 4, record=True)
     assert ot == bt
     assert np.allclose(orec[-1], np.array(bl, np.float32), rtol=1e-6, atol=1e-6)
+
+
+def _tiny_weights(dtype):
+    """TINY weights scaled so attention and the MLP matter at this width, with
+    non-unit gains so the order of norm, gain and rotation matters; stored in
+    ``dtype``."""
+    w = model_weights(TINY, seed=0)
+    for lw in w["layers"]:
+        for k in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+            lw[k] = (lw[k] * np.float32(25.0)).astype(dtype)
+    rng = np.random.default_rng(8)
+    for lw in w["layers"]:
+        for k in ("in_norm", "post_norm", "q_norm", "k_norm"):
+            lw[k] = rng.uniform(0.5, 1.5, lw[k].shape).astype(dtype)
+    w["final_norm"] = rng.uniform(0.5, 1.5, w["final_norm"].shape).astype(dtype)
+    w["embed"] = w["embed"].astype(dtype)
+    return w
+
+
+def _fp16_ulps(a, b):
+    """Largest distance between two FP16 vectors in units of FP16 spacing at b."""
+    a = np.asarray(a, dtype=np.float16).astype(np.float64)
+    b = np.asarray(b, dtype=np.float16)
+    return float(np.max(np.abs(a - b.astype(np.float64)) / np.spacing(np.abs(b)).astype(np.float64)))
+
+
+def test_tiny_model_brute_force_fp16_storage():
+    """FP16 storage mode: every stored value (each of the eight stage outputs per layer,
+    the final norm and the logits) rounded to FP16, every reduction exact (math.fsum).
+    The oracle in FP16 mode gives the same greedy tokens and the same FP16 logits, bit
+    for bit.  (Float64 BLAS sums and math.fsum could round a value that sits on an FP16
+    rounding boundary to neighbouring FP16 values; no value of this input does, so the
+    comparison is exact rather than one ulp wide.)"""
+    w = _tiny_weights(np.float16)
+    prompt = prompt_ids(1, 4, TINY.vocab)
+    bt, bl = brute_generate(TINY, w, prompt, 4, store=_f16)
+    m = OracleModel(TINY, w, 8)
+    assert m.dtype == np.float16
+    ot, orec = m.generate(prompt, 4, record=True)
+    assert orec[-1].dtype == np.float16
+    assert ot == bt
+    assert _fp16_ulps(bl, orec[-1]) == 0.0
+
+
+# The gathered embedding row of a dense FP16 model is a stored value already, so its
+# rounding is the identity here; the gather rounding of int4 models (q * s rounded once)
+# is pinned in test_oracle_q4_model.py.
+@pytest.mark.parametrize("stage", BRUTE_STAGES[1:])
+def test_fp16_brute_force_sees_each_stage_rounding(stage):
+    """The FP16 comparison above has teeth: leaving out the FP16 rounding of any one
+    stored stage in the brute force changes its tokens or logits against the oracle's
+    (so a dropped storage rounding in the oracle would fail that comparison too)."""
+    w = _tiny_weights(np.float16)
+    prompt = prompt_ids(1, 4, TINY.vocab)
+    m = OracleModel(TINY, w, 8)
+    ot, orec = m.generate(prompt, 4, record=True)
+    bt, bl = brute_generate(TINY, w, prompt, 4, store=_f16, skip=stage)
+    if stage == "logits":
+        # unrounded logits: compare before any rounding
+        dist = float(np.max(np.abs(np.asarray(bl) - orec[-1].astype(np.float64))))
+        assert dist > 0.0
+    else:
+        assert bt != ot or _fp16_ulps(bl, orec[-1]) > 0.0, f"skipping the {stage} rounding went unnoticed"
