@@ -377,6 +377,24 @@ wsg_status wsg_gemm_swiglu_f32(int32_t M, int32_t I, int32_t K, const float* d_A
  * improbable constant).  Asynchronous on hip_stream. */
 wsg_status wsg_stream_read(const void* d_buf, int64_t bytes, float* d_out, void* hip_stream);
 
+/* Greedy selection over stand-alone logit vectors: d_out[r] = the lowest
+ * index i whose logit d_logits[r][i] is maximal, for r < rows (Megakernels,
+ * "GPU-wide end-to-end generation": the next token is chosen on the GPU,
+ * ties going to the lowest token id; -0.0 and +0.0 tie).  The same ordering
+ * as the decode head's argmax, as two ordered launches: one key per 4096
+ * logits into d_workspace, then one block per row.
+ *   dtype WSG_F32: d_logits float [rows][n]; WSG_F16: half [rows][n];
+ *   d_out int32 [rows] (device memory, written by the second launch);
+ *   d_workspace at least wsg_argmax_workspace_bytes(rows, n) bytes, 8-byte
+ *   aligned, caller-owned scratch (its contents on entry do not matter).
+ * Logits must be finite (a NaN is ordered by its bit pattern).  1 <= rows
+ * <= 65535, 1 <= n <= 2^30.  Asynchronous on hip_stream.  Errors: a bad dtype or
+ * size, a NULL or misaligned pointer, a workspace that is too small
+ * (WSG_ERR_INVALID_ARG). */
+wsg_status wsg_argmax_workspace_bytes(int32_t rows, int32_t n, size_t* bytes);
+wsg_status wsg_argmax(int32_t dtype, int32_t rows, int32_t n, const void* d_logits, int32_t* d_out,
+                      void* d_workspace, size_t ws_bytes, void* hip_stream);
+
 /* Weight storage the decode path reads: matrices with a packed copy (of
  * 1 + 4 n_layers decode matrices) and the decode weight bytes per token
  * (packed copies count half). */

@@ -63,6 +63,29 @@ def test_gemv_argument_validation(abi):
     assert b"aligned" in L.wsg_last_error()
 
 
+def test_argmax_argument_validation(abi):
+    L = abi.lib()
+    n = C.c_size_t()
+    assert L.wsg_argmax_workspace_bytes(2, 151936, C.byref(n)) == 0
+    assert n.value == 2 * 38 * 8                       # one key per 4096 logits and row
+    assert L.wsg_argmax_workspace_bytes(1, 1, C.byref(n)) == 0 and n.value == 8
+    assert L.wsg_argmax_workspace_bytes(0, 8, C.byref(n)) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax_workspace_bytes(1, 0, C.byref(n)) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax_workspace_bytes(1, (1 << 30) + 1, C.byref(n)) == abi.WSG_ERR_INVALID_ARG
+    # bad dtype, sizes, null / misaligned pointers, small workspace: rejected before any launch
+    assert L.wsg_argmax(2, 1, 8, 16, 16, 16, 8, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax(0, 0, 8, 16, 16, 16, 8, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax(0, 1, 0, 16, 16, 16, 8, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax(0, 1, 8, None, 16, 16, 8, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax(0, 1, 8, 16, None, 16, 8, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax(0, 1, 8, 18, 16, 16, 8, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax(1, 1, 8, 17, 16, 16, 8, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax(0, 1, 8, 16, 16, None, 8, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax(0, 1, 8, 16, 16, 20, 8, None) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_argmax(0, 2, 8, 16, 16, 16, 8, None) == abi.WSG_ERR_INVALID_ARG
+    assert b"workspace" in L.wsg_last_error()
+
+
 def _cfg(abi, shape, cap=16, dtype=0, chunk=0, pack=0):
     return abi.wsg_config(shape.n_layers, shape.hidden, shape.intermediate, shape.n_q_heads,
                           shape.n_kv_heads, shape.head_dim, shape.vocab, cap, chunk, shape.rms_eps,

@@ -112,37 +112,48 @@ def test_mini_many_splits(mini_w, n_prompt):
 WIDE_KV = ModelShape(n_layers=1, hidden=256, intermediate=512, n_q_heads=8, n_kv_heads=8, head_dim=128, vocab=500)
 
 
-@pytest.mark.parametrize("n_prompt", [1600, 3300])
-def test_long_context_split_sizes(n_prompt):
-    """Contexts whose split-K attention blocks take 80 keys (1600: each key-row
-    folds a second group of keys, the last one partial) and 160 keys (3300:
-    three groups per key-row); greedy steps in lockstep, then two-token steps
-    (an accepted and a rejected draft) at the same context."""
+def _split_keys(n_keys, n_kv, cap):
+    """Keys per split-K attention block the runtime picks for a context of n_keys (its
+    documented rule: about 192 blocks over all KV heads, at least 64 keys and enough that
+    the capacity needs at most 128 splits, rounded up a ladder of four sizes per doubling),
+    so each case below states which block size it reaches."""
+    least = max(64, (-(-cap // 128) + 15) // 16 * 16)
+    need = max(least, -(-n_keys // max(1, 192 // n_kv)))
+    c, e = 64, 0
+    while c < need:
+        base = 64 << (e // 4)
+        c = base + (base // 4) * (e % 4 + 1)
+        e += 1
+    return c
+
+
+def _split_lockstep(sh, w, cap, chunk, n_prompt, label):
+    """Greedy steps in lockstep after a chunked prefill, then two two-token steps (an
+    accepted and a rejected draft), each row's logits and both new K/V slots of every
+    layer against the oracle."""
     import weight_streaming_gemv_amd as wsg
-    sh = WIDE_KV
-    w = model_weights(sh, seed=3)
-    cap = 3328
-    m = wsg.Model(sh, w, max_context=cap, prefill_chunk=512)
+    m = wsg.Model(sh, w, max_context=cap, prefill_chunk=chunk)
     orc = oracle.OracleModel(sh, w, cap)
     prompt = prompt_ids(11, n_prompt, sh.vocab)
-    toks, _, _ = lockstep(m, orc, prompt, 4, label=f"wide-kv n={n_prompt}")
+    toks, _, _ = lockstep(m, orc, prompt, 4, label=label)
     last = toks[-1]
     for s, accept in enumerate((True, False)):
         p = orc.pos
         ref0 = orc.forward_rows([last])
         g0 = oracle.argmax_lowest(ref0)
         draft = g0 if accept else (g0 + 1) % sh.vocab
-        announce(f"wide-kv n={n_prompt} step2 {s} p={p}")
+        announce(f"{label} step2 {s} p={p}")
         (t0, t1), n = m.step2(draft)
         ref1 = orc.forward_rows([draft])
         got = _np(m.logits())
         for row, r in ((0, ref0), (1, ref1)):
             ok, err, worst = close_rel(got[row], r, 1e-3, 1e-3)
-            assert ok, f"step2 {s} row {row}: logits off by {err:.3e} at {worst}"
-        k, v, _ = m.kv(0)
-        for g_, r_ in ((k, orc.k_cache[0]), (v, orc.v_cache[0])):
-            ok, err, _ = close_rel(_np(g_[:, p:p + 2]), r_[:, p:p + 2], 1e-3, 1e-3)
-            assert ok, f"step2 {s}: K/V off by {err:.3e}"
+            assert ok, f"{label} step2 {s} row {row}: logits off by {err:.3e} at {worst}"
+        for l in range(sh.n_layers):
+            k, v, _ = m.kv(l)
+            for g_, r_ in ((k, orc.k_cache[l]), (v, orc.v_cache[l])):
+                ok, err, _ = close_rel(_np(g_[:, p:p + 2]), r_[:, p:p + 2], 1e-3, 1e-3)
+                assert ok, f"{label} step2 {s}: layer {l} K/V off by {err:.3e}"
         assert t0 == g0 and n == (2 if accept else 1)
         if accept:
             assert t1 == oracle.argmax_lowest(ref1)
@@ -151,6 +162,30 @@ def test_long_context_split_sizes(n_prompt):
             orc.pos = p + 1
             last = t0
     m.close()
+
+
+@pytest.mark.parametrize("n_prompt,keys", [(1600, 80), (3300, 160), (4200, 192), (4700, 224), (5100, 224)])
+def test_long_context_split_sizes(n_prompt, keys):
+    """Contexts whose split-K attention blocks take 80 keys (1600: each key-row
+    folds a second group of keys, the last one partial), 160 keys (3300: three
+    groups per key-row), 192 keys (4200: three whole groups) and 224 keys (4700
+    and 5100, the sizes of the long-document generation past 4608 keys: four
+    groups per key-row, the last one partial); greedy steps in lockstep, then
+    two-token steps (an accepted and a rejected draft) at the same context."""
+    cap = 5120
+    assert _split_keys(n_prompt + 1, WIDE_KV.n_kv_heads, cap) == keys
+    assert _split_keys(n_prompt + 7, WIDE_KV.n_kv_heads, cap) == keys
+    _split_lockstep(WIDE_KV, model_weights(WIDE_KV, seed=3), cap, 512, n_prompt, f"wide-kv n={n_prompt}")
+
+
+def test_long_context_224_key_splits_qwen3_2layer():
+    """The real head geometry (16 query heads on 8 KV heads, two query heads per split
+    block) at 4.7k keys, where the attention blocks take 224 keys, through a chunk-1024
+    prefill (five chunks, the last one partial)."""
+    sh = QWEN3_0_6B.with_layers(2)
+    cap, n_prompt = 4736, 4700
+    assert _split_keys(n_prompt + 1, sh.n_kv_heads, cap) == 224
+    _split_lockstep(sh, model_weights(sh, seed=0), cap, 1024, n_prompt, "qwen3-2L n=4700")
 
 
 def test_graph_cache_eviction(mini_w):

@@ -18,7 +18,7 @@ from ._abi import (WSG_F16, WSG_F32, WSG_GEMV_NONTEMPORAL, WSG_OPT_TIMED_STAGE, 
                    WSG_STAGE_ATTN, WSG_STAGE_DOWN, WSG_STAGE_GATEUP, WSG_STAGE_HEAD, WSG_STAGE_O,
                    WSG_STAGE_QKV, WsgError, check, wsg_config, wsg_host_weights)
 
-__all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "gemm_nt", "gemm_swiglu", "WsgError", "WSG_F32", "WSG_F16",
+__all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "gemm_nt", "gemm_swiglu", "argmax", "WsgError", "WSG_F32", "WSG_F16",
            "WSG_STAGE_QKV", "WSG_STAGE_ATTN", "WSG_STAGE_O", "WSG_STAGE_GATEUP", "WSG_STAGE_DOWN",
            "WSG_STAGE_HEAD", "WSG_OPT_USE_GRAPH", "WSG_OPT_TIMED_STAGE", "WSG_GEMV_NONTEMPORAL", "stream_read", "lib"]
 
@@ -95,6 +95,25 @@ def gemm_swiglu(A, Wgu, ACT=None, stream=None):
         ACT = torch.empty((M, I), dtype=torch.float32, device=A.device)
     check(_abi.lib().wsg_gemm_swiglu_f32(M, I, K, A.data_ptr(), Wgu.data_ptr(), ACT.data_ptr(), _stream_handle(stream)))
     return ACT
+
+
+def argmax(logits, out=None, stream=None):
+    """Lowest-index argmax of each row of ``logits`` ([rows, n] or [n], FP32 or FP16 device
+    tensor) on the GPU; returns an int32 device tensor [rows] (scratch from torch)."""
+    torch = _torch()
+    lg = logits if logits.dim() == 2 else logits.view(1, -1)
+    if not lg.is_contiguous():
+        raise ValueError("logits must be contiguous")
+    dt = {torch.float32: WSG_F32, torch.float16: WSG_F16}[lg.dtype]
+    rows, n = lg.shape
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int32, device=lg.device)
+    nb = C.c_size_t()
+    check(_abi.lib().wsg_argmax_workspace_bytes(rows, n, C.byref(nb)))
+    ws = torch.empty(nb.value, dtype=torch.uint8, device=lg.device)
+    check(_abi.lib().wsg_argmax(dt, rows, n, lg.data_ptr(), out.data_ptr(), ws.data_ptr(), nb.value,
+                                _stream_handle(stream)))
+    return out
 
 
 def stream_read(buf, out=None, stream=None):

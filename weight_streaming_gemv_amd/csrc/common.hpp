@@ -152,6 +152,35 @@ template <int K> struct Q4Row {
 struct Q4Vec { static constexpr int N = 16; };
 template <> struct WVec<q4w> { using type = Q4Vec; };
 
+// ---------------------------------------------------------------- argmax
+// Greedy selection with ties to the lowest token id (Megakernels, "GPU-wide
+// end-to-end generation") as a maximum of 64-bit keys: the logit's bits in an
+// order-preserving form (negative values complemented, non-negative ones with
+// the sign bit set) above the complemented index, so a larger key is a larger
+// logit, then a lower index.  -0.0 is folded into +0.0 first, so the two
+// zeros tie.  Every key of an index below 2^31 is nonzero, so 0 is below all
+// of them.  (A NaN orders by its bit pattern: logits are taken to be finite.)
+__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
+  if (v == 0.0f) v = 0.0f;
+  uint32_t b = __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+// The index a key encodes.
+__device__ __forceinline__ int argmax_key_index(unsigned long long k) {
+  return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(k, off);
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }

@@ -513,23 +513,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, c
 }
 
 // ---------------------------------------------------------------- head
-// Argmax keys: larger key = larger logit, then lower index.  -0.0 is folded
-// into +0.0 first, so the two zeros tie.
-__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
-  if (v == 0.0f) v = 0.0f;
-  uint32_t b = __float_as_uint(v);
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((unsigned long long)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const unsigned long long o = __shfl_xor(k, off);
-    k = o > k ? o : k;
-  }
-  return k;
-}
+// (argmax keys: argmax_key / wave_max_u64 in common.hpp)
 
 // The head writes one argmax key per block and row; a one-block kernel then
 // reduces them (the pages' two argmax kernels, Megakernels, "GPU-wide
@@ -641,7 +625,7 @@ __global__ __launch_bounds__(1024) void k_argmax(const unsigned long long* __res
     for (int t = 0; t < T; ++t) {
       unsigned long long b = red[t][0];
       for (int w = 1; w < (int)(blockDim.x >> 6); ++w) b = red[t][w] > b ? red[t][w] : b;
-      tok[t] = (int)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
+      tok[t] = argmax_key_index(b);
       if (b == 0) tok[t] = 0;   // no block key at all (cannot happen with vocab >= 1)
       ctrl[kCtrlRowTok + t] = tok[t];
     }
