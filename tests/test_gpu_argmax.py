@@ -77,9 +77,9 @@ def _planted_cases(n):
     v = -np.abs(base()) - 1.0
     v[4097] = -0.0
     cases.append(("only -0.0", v, 4097))
-    v = np.full(n, -np.inf)
-    v[55_555] = -1e30
-    cases.append(("-inf everywhere but one", v, 55_555))
+    v = np.full(n, -60000.0)
+    v[55_555] = -59968.0
+    cases.append(("large negative values, one a step above", v, 55_555))
     return cases
 
 
