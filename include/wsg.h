@@ -395,6 +395,21 @@ wsg_status wsg_argmax_workspace_bytes(int32_t rows, int32_t n, size_t* bytes);
 wsg_status wsg_argmax(int32_t dtype, int32_t rows, int32_t n, const void* d_logits, int32_t* d_out,
                       void* d_workspace, size_t ws_bytes, void* hip_stream);
 
+/* wsg_argmax for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same result and kernels, with the span keys in a library-owned device
+ * array of 16384 keys (128 KiB; each GPU the library runs on holds its own
+ * copy until the process ends) instead of a caller workspace.  Allocates
+ * nothing; the caller passes the logits and the output.  At most
+ * rows * ceil(n / 4096) <= 16384 (WSG_ERR_INVALID_ARG beyond, before any
+ * launch).  The current device must be the stream's; the first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress), so
+ * make one call outside any graph capture first.  All calls on one GPU share
+ * its array: calls that overlap on one GPU (other streams, other host
+ * threads) race.  Other arguments and errors as for wsg_argmax. */
+wsg_status wsg_argmax_noalloc(int32_t dtype, int32_t rows, int32_t n, const void* d_logits, int32_t* d_out,
+                              void* hip_stream);
+
 /* Weight storage the decode path reads: matrices with a packed copy (of
  * 1 + 4 n_layers decode matrices) and the decode weight bytes per token
  * (packed copies count half). */

@@ -113,6 +113,8 @@ def argmax(logits, out=None, stream=None):
     ws = torch.empty(nb.value, dtype=torch.uint8, device=lg.device)
     check(_abi.lib().wsg_argmax(dt, rows, n, lg.data_ptr(), out.data_ptr(), ws.data_ptr(), nb.value,
                                 _stream_handle(stream)))
+    if stream is not None:
+        ws.record_stream(stream)   # the scratch stays reserved until the stream's work is done
     return out
 
 
