@@ -416,6 +416,15 @@ wsg_status wsg_argmax_noalloc(int32_t dtype, int32_t rows, int32_t n, const void
 wsg_status wsg_weight_storage(const wsg_model* m, int32_t* packed_matrices, int32_t* decode_matrices,
                               int64_t* decode_weight_bytes);
 
+/* A JSON text describing the model's launch shapes, for reports (the pages
+ * record kernel fingerprints beside their figures: Benchmark methodology,
+ * "Long-document chunked prefill"): rows per wave and grids of every decode
+ * stage for one- and two-token steps, the attention mode, split count and
+ * keys per split at sample context lengths, the prefill chunk, graph use and
+ * the library version.  Writes at most n bytes (NUL-terminated) to buf (may be
+ * NULL) and the full length + 1 to *needed.  Errors: NULL model or needed. */
+wsg_status wsg_describe(const wsg_model* m, char* buf, size_t n, size_t* needed);
+
 /* Message for the last error on this host thread ("" if none). */
 const char* wsg_last_error(void);
 

@@ -75,6 +75,10 @@ class OracleModel:
         L, hkv, d = shape.n_layers, shape.n_kv_heads, shape.head_dim
         self.k_cache = np.zeros((L, hkv, self.cap, d), dtype=self.dtype)
         self.v_cache = np.zeros((L, hkv, self.cap, d), dtype=self.dtype)
+        # float64 copies of the stored cache entries (exact), written with them, so
+        # attention does not widen the whole prefix again at every step
+        self._k64 = np.zeros((L, hkv, self.cap, d), dtype=F64)
+        self._v64 = np.zeros((L, hkv, self.cap, d), dtype=F64)
         self.pos = 0
 
     def reset(self) -> None:
@@ -114,7 +118,9 @@ class OracleModel:
             k = store(rope_apply(rms_norm(k, w["k_norm"], eps), ang), dt)
             self.k_cache[l, :, p0:p0 + n] = np.transpose(k, (1, 0, 2))
             self.v_cache[l, :, p0:p0 + n] = np.transpose(v, (1, 0, 2))
-            o = store(gqa_attention(q, self.k_cache[l], self.v_cache[l], positions), dt)  # stage 4
+            self._k64[l, :, p0:p0 + n] = self.k_cache[l, :, p0:p0 + n]
+            self._v64[l, :, p0:p0 + n] = self.v_cache[l, :, p0:p0 + n]
+            o = store(gqa_attention(q, self._k64[l], self._v64[l], positions), dt)  # stage 4
             o64 = o.reshape(n, hq * d).astype(F64)
             x = store(x.astype(F64) + o64 @ w["wo"].T, dt)              # stage 5
             b = store(rms_norm(x, w["post_norm"], eps), dt)             # stage 6

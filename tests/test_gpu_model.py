@@ -178,6 +178,22 @@ def test_long_context_split_sizes(n_prompt, keys):
     _split_lockstep(WIDE_KV, model_weights(WIDE_KV, seed=3), cap, 512, n_prompt, f"wide-kv n={n_prompt}")
 
 
+def test_describe_reports_launch_shapes(mini_w):
+    """wsg_describe: the launch shapes a report records, consistent with the split rule the
+    long-context tests rely on."""
+    import weight_streaming_gemv_amd as wsg
+    m = wsg.Model(WIDE_KV, model_weights(WIDE_KV, seed=3), max_context=5120, prefill_chunk=512)
+    d = m.describe()
+    assert d["one_token"]["rows_per_wave"]["head"] == 2 and d["two_token"]["rows_per_wave"]["head"] == 4
+    assert d["prefill_chunk"] == 512 and d["graphs"] is True
+    for e in d["attention"]["at_keys"]:
+        assert e["mode"] == ("fused" if e["keys"] <= 128 else "split+merge_o"), e
+        if e["keys"] > 128:
+            assert e["keys_per_split"] == _split_keys(e["keys"], WIDE_KV.n_kv_heads, 5120), e
+            assert e["splits"] == -(-e["keys"] // e["keys_per_split"]), e
+    m.close()
+
+
 def test_long_context_224_key_splits_qwen3_2layer():
     """The real head geometry (16 query heads on 8 KV heads, two query heads per split
     block) at 4.7k keys, where the attention blocks take 224 keys, through a chunk-1024

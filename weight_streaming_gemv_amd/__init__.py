@@ -330,6 +330,15 @@ class Model:
         check(_abi.lib().wsg_weight_storage(self.h, C.byref(pk), C.byref(tot), C.byref(b)))
         return {"packed_matrices": pk.value, "decode_matrices": tot.value, "decode_weight_bytes": b.value}
 
+    def describe(self) -> dict:
+        """The model's launch shapes (``wsg_describe``) as a dict."""
+        import json
+        need = C.c_size_t()
+        check(_abi.lib().wsg_describe(self.h, None, 0, C.byref(need)))
+        buf = C.create_string_buffer(need.value)
+        check(_abi.lib().wsg_describe(self.h, buf, need.value, C.byref(need)))
+        return json.loads(buf.value.decode())
+
     def logits(self):
         """Last logits (device tensor view, storage dtype): [vocab] after prefill/step,
         [2, vocab] after step2."""

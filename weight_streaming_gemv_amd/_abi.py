@@ -109,6 +109,7 @@ _SIGS = {
     "wsg_rewind": (C.c_int, [C.c_void_p, C.c_int32]),
     "wsg_weight_storage": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                      C.POINTER(C.c_int64)]),
+    "wsg_describe": (C.c_int, [C.c_void_p, C.c_char_p, C.c_size_t, C.POINTER(C.c_size_t)]),
     "wsg_last_error": (C.c_char_p, []),
     "wsg_version": (C.c_char_p, []),
 }

@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <map>
+#include <string>
 #include <vector>
 
 #include "../../include/wsg.h"
@@ -530,6 +531,18 @@ wsg_status read_row_tokens(wsg_model* m, int rows, int32_t* out) {
   return WSG_OK;
 }
 
+// A call that fails after it enqueued work may have moved the device
+// position (prefill chunks and the argmax launch advance it); put it back to
+// the host's value, which the failed call leaves unchanged (best effort: after
+// a HIP error the stream may refuse this launch too).  Returns st.
+wsg_status restore_pos(wsg_model* m, wsg_status st) {
+  if (st != WSG_OK) {
+    launch_set_pos(m->args.ctrl, m->pos, m->stream);
+    (void)hipGetLastError();
+  }
+  return st;
+}
+
 void fill_rope(const wsg_config& c, std::vector<float>& cs, std::vector<float>& sn) {
   const int half = c.head_dim / 2;
   cs.resize((size_t)c.max_context * half);
@@ -901,9 +914,9 @@ wsg_status wsg_prefill(wsg_model* m, const int32_t* host_ids, int32_t n, int32_t
     m->timed_bytes_per_launch_sum = 0;
     wsg_status st = run_prefill_chunks(pc, p0, n, true, m->stream);
     if (st == WSG_OK) st = run_head(m, 1);
-    if (st != WSG_OK) return st;
+    if (st != WSG_OK) return restore_pos(m, st);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(WSG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return restore_pos(m, fail(WSG_ERR_HIP, "kernel launch: %s", hipGetErrorString(e)));
     done = n;
   }
   // Rows without the chunked path: two at a time through the two-row
@@ -912,15 +925,15 @@ wsg_status wsg_prefill(wsg_model* m, const int32_t* host_ids, int32_t n, int32_t
   int r = done;
   for (; r + 2 <= n - 1; r += 2) {
     const wsg_status st = run_forward(m, false, p0 + r + 2, 2);
-    if (st != WSG_OK) return st;
+    if (st != WSG_OK) return restore_pos(m, st);
   }
   for (; r < n; ++r) {
     const bool last = (r == n - 1);
     const wsg_status st = run_forward(m, last, p0 + r + 1);
-    if (st != WSG_OK) return st;
+    if (st != WSG_OK) return restore_pos(m, st);
   }
   const wsg_status st = read_token(m, out_token);
-  if (st != WSG_OK) return st;
+  if (st != WSG_OK) return restore_pos(m, st);
   m->pos = p0 + n;
   m->has_output = true;
   if (out_logits) *out_logits = m->args.logits;
@@ -938,9 +951,9 @@ wsg_status wsg_step(wsg_model* m, int32_t in_token, int32_t* out_token, const vo
     WSG_HIP_CHECK(hipMemcpyAsync(m->args.ids + m->pos, m->pin + 1, sizeof(int32_t), hipMemcpyHostToDevice, m->stream));
   }
   wsg_status st = run_forward(m, true, m->pos + 1);
-  if (st != WSG_OK) return st;
+  if (st != WSG_OK) return restore_pos(m, st);
   st = read_token(m, out_token);
-  if (st != WSG_OK) return st;
+  if (st != WSG_OK) return restore_pos(m, st);
   m->pos += 1;
   m->has_output = true;
   if (out_logits) *out_logits = m->args.logits;
@@ -963,10 +976,10 @@ wsg_status wsg_step2(wsg_model* m, int32_t in_token, int32_t draft, int32_t out_
   else
     WSG_HIP_CHECK(hipMemcpyAsync(m->args.ids + m->pos + 1, m->pin + 2, sizeof(int32_t), hipMemcpyHostToDevice, m->stream));
   wsg_status st = run_forward(m, true, m->pos + 2, 2);
-  if (st != WSG_OK) return st;
+  if (st != WSG_OK) return restore_pos(m, st);
   int32_t tok[2];
   st = read_row_tokens(m, 2, tok);
-  if (st != WSG_OK) return st;
+  if (st != WSG_OK) return restore_pos(m, st);
   // the argmax kernel applied the same acceptance rule to the device position
   const int emitted = tok[0] == draft ? 2 : 1;
   out_tokens[0] = tok[0];
@@ -1066,6 +1079,54 @@ wsg_status wsg_weight_storage(const wsg_model* m, int32_t* packed_matrices, int3
     b += stage_bytes(m, WSG_STAGE_QKV, l) + stage_bytes(m, WSG_STAGE_O, l) + stage_bytes(m, WSG_STAGE_GATEUP, l) +
          stage_bytes(m, WSG_STAGE_DOWN, l);
   *decode_weight_bytes = b;
+  return WSG_OK;
+}
+
+wsg_status wsg_describe(const wsg_model* m, char* buf, size_t n, size_t* needed) {
+  clear_error();
+  if (!m || !needed) return fail(WSG_ERR_INVALID_ARG, "NULL pointer");
+  std::string j = "{";
+  char t[256];
+  auto shape_json = [&](const char* name, const DecodeShape& sh) {
+    snprintf(t, sizeof(t),
+             "\"%s\": {\"rows_per_wave\": {\"qkv\": %d, \"o\": %d, \"gateup\": %d, \"down\": %d, \"head\": %d}, ",
+             name, sh.rows_qkv, sh.rows_o, sh.rows_gu, sh.rows_down, sh.rows_head);
+    j += t;
+    snprintf(t, sizeof(t),
+             "\"grid_blocks\": {\"qkv\": %d, \"o\": %d, \"gateup\": %d, \"down\": %d, \"head\": %d}, ",
+             sh.grid_qkv, sh.grid_o, sh.grid_gu, sh.grid_down, head_blocks(m->args, sh));
+    j += t;
+    snprintf(t, sizeof(t), "\"head_waves\": %d, \"fuse_attn_o\": %d, \"rows_attn_o\": %d}, ", sh.head_waves,
+             sh.fuse_attn_o, sh.rows_attn_o);
+    j += t;
+  };
+  shape_json("one_token", shape_for(m, 1));
+  shape_json("two_token", shape_for(m, 2));
+  snprintf(t, sizeof(t), "\"attention\": {\"fused_max_keys\": %d, \"target_blocks\": %d, \"min_split_keys\": %d, ",
+           kFuseMaxKeys, kAttnTargetBlocks, attn_chunk(m->d));
+  j += t;
+  j += "\"at_keys\": [";
+  const int probes[] = {1, 48, 129, 1100, 2100, 4200, 4700, 5119};
+  bool first = true;
+  for (int k : probes) {
+    if (k > m->d.cap) continue;
+    const int c = attn_chunk_for(m, k);
+    snprintf(t, sizeof(t), "%s{\"keys\": %d, \"mode\": \"%s\", \"splits\": %d, \"keys_per_split\": %d}",
+             first ? "" : ", ", k, attn_mode(m, k, 1) == kAttnFused ? "fused" : (attn_mode(m, k, 1) == kAttnMergeO ? "split+merge_o" : "separate"),
+             splits_for(k, c), c);
+    j += t;
+    first = false;
+  }
+  j += "]}, ";
+  snprintf(t, sizeof(t), "\"prefill_chunk\": %d, \"graphs\": %s, \"weights_packed\": %d, \"version\": \"%s\"}",
+           m->prefill_rows, m->use_graph ? "true" : "false", m->n_packed, wsg_version());
+  j += t;
+  *needed = j.size() + 1;
+  if (buf && n > 0) {
+    const size_t c = std::min(n - 1, j.size());
+    memcpy(buf, j.data(), c);
+    buf[c] = 0;
+  }
   return WSG_OK;
 }
 
