@@ -12,9 +12,9 @@ tokens, logits and KV matched the CPU oracle on the same inputs; every timed
 generation must reproduce the validated token ids.
 
 Also reported: every decode stage against the HBM roofline, the one with
-the largest share of per-token stage time as ``roofline`` (HIP events around
-each of its launches in a direct-launch pass of the same generations after
-the timed region), the whole step's weight bytes per token times tokens/s
+the largest share of per-token stage time as ``roofline`` (its launches for
+all layers replayed as one graph between HIP events, after the timed
+region), the whole step's weight bytes per token times tokens/s
 (``step_roofline``), the head timed inside the timed region, the oracle timed
 on the host cores, provenance (hashes, versions, device, launch shapes), and
 (``--sweep``) the cold-cache GEMV sweep.  A validation failure anywhere
@@ -914,39 +914,29 @@ def long_context(torch, wsg, shape, w, trials=5, warmup=2, tune_len=2048, held_l
     }
 
 
-def stage_pass(torch, wsg, model, run_step, steps=2):
-    """Per-stage HBM rooflines of the decode step.  For each stage kind the timed region's
-    generations run ``steps`` more times with direct launches and HIP events on the model
-    stream around every launch of that kind (event nodes inside replayed graphs carry no
-    timestamps here, so the timed region itself can only bracket the head).  Per stage:
-    mean launch time, algorithmic weight bytes per launch (the fused attention launch counts
-    its output-projection weights; the few KiB of K/V are left out), achieved GB/s, and the
-    stage's share of the per-token time of all stages (28 launches per token for the layer
-    stages, one for the head)."""
-    A = wsg._abi
+def stage_pass(wsg, model, head, reps=20):
+    """Per-stage HBM rooflines of the decode step.  Each per-layer stage is timed with
+    ``wsg_time_stage``: a graph of that stage's launches for all layers (each layer's own
+    weights, so the stream stays cold), replayed ``reps`` times between two HIP events on
+    the model stream, at the context of the next step.  One event pair around each single
+    launch would add its own dispatch cost (several microseconds on kernels of 4-9 us), so
+    the events bracket whole replays.  The head comes from the timed region (``head``: HIP
+    events around each of its launches, a single 90-us kernel).  Per stage: mean launch
+    time, algorithmic bytes per launch (weights; the attention launch's cached keys and
+    values plus, fused, its output-projection weights), achieved GB/s, and the
+    stage's share of the per-token time of all stages (n_layers launches per token for the
+    layer stages, one for the head)."""
     L = model.shape.n_layers
     res = {}
-    model.set_option(A.WSG_OPT_TIMED_STAGE, -1)
-    model.set_option(A.WSG_OPT_USE_GRAPH, 0)
-    try:
-        for name in ("qkv", "attn", "gateup", "down", "head"):
-            model.set_option(A.WSG_OPT_TIMED_STAGE, STAGES[name])
-            run_step(None)
-            model.stage_time()
-            for _ in range(steps):
-                run_step(None)
-            torch.cuda.synchronize()
-            ms, n, b = model.stage_time()
-            model.set_option(A.WSG_OPT_TIMED_STAGE, -1)
-            if not n:
-                continue
-            us = ms * 1e3 / n
-            res[name] = {"kernel": STAGE_KERNEL[name], "launches": n, "us_per_launch": round(us, 3),
-                         "bytes_per_launch": b // n, "gbps": round(b / n / (us * 1e-6) / 1e9, 1),
-                         "ms_per_token": round(us * (1 if name == "head" else L) / 1e3, 4)}
-    finally:
-        model.set_option(A.WSG_OPT_TIMED_STAGE, -1)
-        model.set_option(A.WSG_OPT_USE_GRAPH, 1)
+    for name in ("qkv", "attn", "gateup", "down"):
+        us, b = model.time_stage(STAGES[name], reps)
+        res[name] = {"kernel": STAGE_KERNEL[name], "launches": reps * (L - 1 if name == "qkv" else L),
+                     "us_per_launch": round(us, 3), "bytes_per_launch": b, "gbps": round(b / (us * 1e-6) / 1e9, 1),
+                     "ms_per_token": round(us * L / 1e3, 4)}
+    if head:
+        res["head"] = {"kernel": head["kernel"], "launches": head["launches_timed"],
+                       "us_per_launch": head["avg_launch_us"], "bytes_per_launch": head["bytes_per_launch"],
+                       "gbps": head["achieved"], "ms_per_token": round(head["avg_launch_us"] / 1e3, 4)}
     tot = sum(r["ms_per_token"] for r in res.values())
     for r in res.values():
         r["share"] = round(r["ms_per_token"] / tot, 4) if tot else None
@@ -998,8 +988,8 @@ def _main(argv=None):
     ap.add_argument("--timed-stage", default="head", choices=sorted(STAGES),
                     help="stage kind bracketed by HIP events (graph mode: head only)")
     ap.add_argument("--no-graph", action="store_true", help="launch every kernel directly")
-    ap.add_argument("--roofline-steps", type=int, default=2,
-                    help="steps per stage kind of the per-stage roofline pass after the timed region (0: none)")
+    ap.add_argument("--roofline-reps", type=int, default=20,
+                    help="replays of each per-layer stage's graph for the stage rooflines (0: none)")
     ap.add_argument("--sweep", choices=["full", "quick", "int4", "none"], default="full",
                     help="cold-cache GEMV sweep after the decode timing")
     ap.add_argument("--sweep-only", action="store_true", help="run only the cold-cache GEMV sweep")
@@ -1172,7 +1162,13 @@ def _main(argv=None):
                    "launches_timed": st_n, "timing": "HIP events on the model stream around each launch, "
                                                     "in the timed region (graph replay; the head is a direct launch)"}
     model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, -1)
-    stages = stage_pass(torch, wsg, model, run_step, steps=args.roofline_steps) if args.roofline_steps else {}
+    stages = {}
+    if args.roofline_reps:
+        # at the context of the first short prompt's first step (its prefill done)
+        model.reset()
+        model.prefill(prompts[8])
+        stages = stage_pass(wsg, model, timed_stage if args.timed_stage == "head" else None,
+                            reps=args.roofline_reps)
     if stages:
         dom = max(stages, key=lambda k: stages[k]["ms_per_token"])
         d = stages[dom]
@@ -1181,10 +1177,10 @@ def _main(argv=None):
                     "traffic": recorded_traffic(d["kernel"]), "bytes_per_launch": d["bytes_per_launch"],
                     "avg_launch_us": d["us_per_launch"], "launches_timed": d["launches"],
                     "share_of_stage_time": d["share"],
-                    "timing": "HIP events on the model stream around each launch of the stage with the largest "
-                              "share of per-token stage time, in a pass of the same generations with direct "
-                              "launches after the timed region (event nodes inside replayed HIP graphs carry "
-                              "no timestamps here)"}
+                    "timing": "stage with the largest share of per-token stage time; its launches for all "
+                              "layers captured as one HIP graph (each layer's weights) and replayed between "
+                              "two HIP events on the model stream, after the timed region, at the context of "
+                              "the short prompt's first step"}
     else:
         roofline = timed_stage
     out = {

@@ -257,13 +257,13 @@ wsg_status wsg_set_prefill_chunk(wsg_model* m, int32_t rows);
 /* Options: WSG_OPT_USE_GRAPH (1 = replay captured HIP graphs, the default;
  * 0 = launch every kernel directly), WSG_OPT_TIMED_STAGE (record HIP events
  * on the model stream around every launch of one stage kind, see
- * wsg_stage_time; -1 = off).  Event-record nodes inside HIP graphs carry no
- * usable timestamps on this platform, so with graphs on only
- * WSG_STAGE_HEAD can be timed (the head is always a direct launch after the
- * layer graph, bracketed by stream events); other stages need
- * WSG_OPT_USE_GRAPH = 0, where each bracketing event adds its own overhead
- * to short kernels.
- * Errors: WSG_ERR_UNSUPPORTED for a per-layer stage while graphs are on. */
+ * wsg_stage_time; -1 = off).  The head is a direct launch after the layer
+ * graph, bracketed by stream events.  A per-layer stage in graph mode is
+ * timed by step graphs captured with explicit event-record nodes around that
+ * stage's launches (kept apart from the untimed graphs); each such node
+ * lengthens the step by several microseconds on this platform, but the time
+ * between the two nodes of a pair is the launch's own.  In direct-launch mode
+ * each bracketing event adds its own overhead to short kernels. */
 enum { WSG_OPT_USE_GRAPH = 1, WSG_OPT_TIMED_STAGE = 2 };
 /* WSG_OPT_FUSE_ATTN_O: 1 (default) = for contexts of up to 128 keys, each
  * layer runs attention and the output projection as one launch
@@ -278,6 +278,14 @@ enum { WSG_OPT_FUSE_ATTN_O = 3, WSG_OPT_ROWS_ATTN_O = 15 };
  * default 4); each workgroup writes one argmax key, so larger workgroups
  * leave fewer keys for the final argmax launch. */
 enum { WSG_OPT_HEAD_WAVES = 16 };
+/* WSG_OPT_SPLIT_DOWN: K slices of the down projection (1, 2 or 4).  With 2
+ * or 4, every layer but the last writes that many FP32 slices of
+ * W_d . act (the first plus the residual), which the next layer's QKV
+ * launch adds up in slice order before its norm (more, shorter waves for
+ * the 1024-row projection); it applies to dense weights whose slice width
+ * holds whole lane vectors (256 FP32 / 512 FP16 elements) with 1 or 2 rows
+ * per wave, else the projection runs whole. */
+enum { WSG_OPT_SPLIT_DOWN = 17 };
 /* Launch shape of the decode GEMV stages (tuning): rows per wave (1, 2 or
  * 4) and blocks of 256 threads (0 = one row group per wave; fewer blocks
  * loop over row groups; the head is capped at 40960 blocks).  Defaults:
@@ -286,8 +294,8 @@ enum { WSG_OPT_ROWS_QKV = 10, WSG_OPT_ROWS_O = 11, WSG_OPT_ROWS_GATEUP = 12, WSG
        WSG_OPT_ROWS_HEAD = 14, WSG_OPT_GRID_QKV = 20, WSG_OPT_GRID_O = 21, WSG_OPT_GRID_GATEUP = 22,
        WSG_OPT_GRID_DOWN = 23, WSG_OPT_GRID_HEAD = 24 };
 /* OR WSG_OPT_FOR_TWO_TOKEN into any of the launch-shape options above
- * (WSG_OPT_FUSE_ATTN_O, WSG_OPT_ROWS_ATTN_O, WSG_OPT_HEAD_WAVES, WSG_OPT_ROWS_*,
- * WSG_OPT_GRID_*) to set it for two-token steps (wsg_step2) instead of
+ * (WSG_OPT_FUSE_ATTN_O, WSG_OPT_ROWS_ATTN_O, WSG_OPT_HEAD_WAVES, WSG_OPT_SPLIT_DOWN,
+ * WSG_OPT_ROWS_*, WSG_OPT_GRID_*) to set it for two-token steps (wsg_step2) instead of
  * single-token ones: the two kinds of step keep separate launch shapes.
  * Two-token defaults: as above, except 4 head rows per wave. */
 enum { WSG_OPT_FOR_TWO_TOKEN = 0x100 };
@@ -302,6 +310,26 @@ wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value);
  * covers, and the algorithmic weight bytes those launches streamed.  Resets
  * the accumulators. */
 wsg_status wsg_stage_time(wsg_model* m, double* total_ms, int64_t* launches, int64_t* bytes);
+
+/* Average device time of one launch of a per-layer decode stage
+ * (WSG_STAGE_QKV, _ATTN, _O, _GATEUP or _DOWN) at the model's shapes and the
+ * context of its next one-token step: a HIP graph of that stage's launches
+ * for every layer in turn (each with its own layer's weights; QKV skips the
+ * first layer, whose launch also gathers the embedding) is replayed `reps`
+ * times back to back between two events on the model stream, so the
+ * events' own cost is spread over reps * n_layers launches.  *bytes_per_launch
+ * receives the algorithmic bytes of one launch: its weights, and for the
+ * attention stage the keys and values of the context (plus the output-
+ * projection weights when it is fused with attention).  For the roofline of a stage
+ * (Megakernels, "GPU-wide end-to-end generation": the stages of a forward
+ * are ordered launches).  What the launches leave in the stage buffers and in
+ * the next cache slot is rewritten by the next step before it is read; the
+ * valid cache prefix, the position and the last logits are untouched.
+ * Blocks until done.  Errors:
+ * WSG_ERR_INVALID_ARG (stage, reps outside [1, 10000], NULL), WSG_ERR_STATE
+ * (no prefill yet or a full cache), WSG_ERR_UNSUPPORTED (WSG_STAGE_O at a
+ * context where it is fused into the attention launch). */
+wsg_status wsg_time_stage(wsg_model* m, int32_t stage, int32_t reps, double* us_per_launch, int64_t* bytes_per_launch);
 
 /* Stand-alone GEMV, Y[t][m] = sum_k W[m][k] X[t][k] for t < T, with FP32
  * accumulation (Megakernels, "GPU-wide end-to-end generation": one wave

@@ -55,11 +55,93 @@ def test_mini_fused_attention_output(mini_w, fuse, rows):
     m.close()
 
 
+@pytest.mark.parametrize("split", [2, 4])
+@pytest.mark.parametrize("graph", [1, 0])
+def test_mini_split_down(mini_w, split, graph):
+    """The down projection in K slices summed by the next layer's QKV launch: lockstep
+    against the oracle (contexts within and past the fused attention limit), and the same
+    tokens as the whole projection."""
+    import weight_streaming_gemv_amd as wsg
+    cap = 160
+    m = wsg.Model(MINI, mini_w, max_context=cap, prefill_chunk=64)
+    m.set_option(wsg._abi.WSG_OPT_USE_GRAPH, graph)
+    orc = oracle.OracleModel(MINI, mini_w, cap)
+    prompt = prompt_ids(23, 120, MINI.vocab)
+    ref_toks, _, _ = lockstep(m, orc, prompt, 12, label="mini split=1")
+    m.set_option(wsg._abi.WSG_OPT_SPLIT_DOWN, split)
+    assert m.describe()["one_token"]["down_k_slices"] == split
+    toks, _, ck = lockstep(m, orc, prompt, 12, label=f"mini split={split} graph={graph}")
+    assert toks == ref_toks
+    m.close()
+
+
+@pytest.mark.parametrize("split", [2, 4])
+def test_qwen3_2layer_split_down(split):
+    """The Qwen3-shaped down projection (K = 3072) in 2 and 4 slices: one- and two-token
+    steps in lockstep."""
+    import weight_streaming_gemv_amd as wsg
+    from gpu_util import Checker
+    sh = QWEN3_0_6B.with_layers(2)
+    w = model_weights(sh, seed=0)
+    cap = 64
+    m = wsg.Model(sh, w, max_context=cap, prefill_chunk=32)
+    for opt in (wsg._abi.WSG_OPT_SPLIT_DOWN, wsg._abi.WSG_OPT_SPLIT_DOWN | wsg._abi.WSG_OPT_FOR_TWO_TOKEN):
+        m.set_option(opt, split)
+    orc = oracle.OracleModel(sh, w, cap)
+    prompt = prompt_ids(PROMPT_SEEDS["short"], 32, sh.vocab)
+    toks, _, _ = lockstep(m, orc, prompt, 6, label=f"qwen3-2L split={split}")
+    ck = Checker(m, orc, 1e-3, 1e-3, f"qwen3-2L split={split} step2")
+    last = toks[-1]
+    for s_, accept in enumerate((True, False)):
+        p = orc.pos
+        ref0 = orc.forward_rows([last])
+        g0 = oracle.argmax_lowest(ref0)
+        draft = g0 if accept else (g0 + 1) % sh.vocab
+        announce(f"qwen3-2L split={split} step2 {s_}")
+        (t0, t1), n = m.step2(draft)
+        ref1 = orc.forward_rows([draft])
+        got = _np(m.logits())
+        for row, r in ((0, ref0), (1, ref1)):
+            ok, err, worst = close_rel(got[row], r, 1e-3, 1e-3)
+            assert ok, f"step2 {s_} row {row}: logits off by {err:.3e}"
+        assert t0 == g0 and n == (2 if accept else 1)
+        if accept:
+            assert t1 == oracle.argmax_lowest(ref1)
+            ck.kv(p, p + 2, s_)
+            last = t1
+        else:
+            orc.pos = p + 1
+            ck.kv(p, p + 1, s_)
+            last = t0
+    m.close()
+
+
+@pytest.mark.parametrize("shape_name", ["mini", "qwen3-2L"])
+def test_fp16_split_down(shape_name, mini_w):
+    """FP16 storage with the down projection in 2 slices: teacher-forced within the FP16
+    tolerance (4 slices do not hold whole 512-element FP16 lane vectors at these widths,
+    so the projection then runs whole)."""
+    import weight_streaming_gemv_amd as wsg
+    sh = MINI if shape_name == "mini" else QWEN3_0_6B.with_layers(2)
+    w = mini_w if shape_name == "mini" else model_weights(sh, seed=0)
+    w16 = {"embed": w["embed"].astype(np.float16), "final_norm": w["final_norm"].astype(np.float16),
+           "layers": [{k: v.astype(np.float16) for k, v in lw.items()} for lw in w["layers"]]}
+    m = wsg.Model(sh, w16, max_context=32, dtype=wsg.WSG_F16)
+    m.set_option(wsg._abi.WSG_OPT_SPLIT_DOWN, 2)
+    assert m.describe()["one_token"]["down_k_slices"] == 2
+    orc = oracle.OracleModel(sh, w16, 32)
+    lockstep(m, orc, prompt_ids(PROMPT_SEEDS["tiny"], 8, sh.vocab), 6, rtol=2e-2, atol=2e-2, teacher=True,
+             label=f"{shape_name} fp16 split=2")
+    m.set_option(wsg._abi.WSG_OPT_SPLIT_DOWN, 4)
+    assert m.describe()["one_token"]["down_k_slices"] == 1
+    m.close()
+
+
 def test_fused_option_checks(mini_w):
     import weight_streaming_gemv_amd as wsg
     m = wsg.Model(MINI, mini_w, max_context=8)
     for opt, bad in ((wsg._abi.WSG_OPT_FUSE_ATTN_O, 2), (wsg._abi.WSG_OPT_ROWS_ATTN_O, 2),
-                     (wsg._abi.WSG_OPT_ROWS_ATTN_O, 16)):
+                     (wsg._abi.WSG_OPT_ROWS_ATTN_O, 16), (wsg._abi.WSG_OPT_SPLIT_DOWN, 3)):
         with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
             m.set_option(opt, bad)
     m.close()
@@ -176,6 +258,60 @@ def test_long_context_split_sizes(n_prompt, keys):
     assert _split_keys(n_prompt + 1, WIDE_KV.n_kv_heads, cap) == keys
     assert _split_keys(n_prompt + 7, WIDE_KV.n_kv_heads, cap) == keys
     _split_lockstep(WIDE_KV, model_weights(WIDE_KV, seed=3), cap, 512, n_prompt, f"wide-kv n={n_prompt}")
+
+
+def test_stage_timing_inside_graphs(mini_w):
+    """A per-layer stage timed in graph mode: step graphs carry event-record nodes around
+    that stage's launches (one pair per layer), the accumulated time covers one launch per
+    layer and step, and the results are the untimed graphs' bit for bit."""
+    import weight_streaming_gemv_amd as wsg
+    A = wsg._abi
+    m = wsg.Model(MINI, mini_w, max_context=64, prefill_chunk=16)
+    prompt = prompt_ids(41, 10, MINI.vocab)
+    ref = [m.prefill(prompt)] + [m.step() for _ in range(5)]
+    ref_logits = _np(m.logits()).copy()
+    for stage in (A.WSG_STAGE_QKV, A.WSG_STAGE_ATTN, A.WSG_STAGE_GATEUP, A.WSG_STAGE_DOWN):
+        m.set_option(A.WSG_OPT_TIMED_STAGE, stage)
+        m.reset()
+        toks = [m.prefill(prompt)] + [m.step() for _ in range(5)]
+        ms, n, b = m.stage_time()
+        assert toks == ref and np.array_equal(_np(m.logits()), ref_logits)
+        assert n == 5 * MINI.n_layers and ms > 0 and b > 0, (stage, ms, n, b)
+        assert 0.5 < ms * 1e3 / n < 1000, (stage, ms, n)       # microseconds per launch
+    m.set_option(A.WSG_OPT_TIMED_STAGE, -1)
+    m.close()
+
+
+@pytest.mark.parametrize("n_prompt", [10, 150])
+def test_time_stage_leaves_the_sequence_alone(mini_w, n_prompt):
+    """wsg_time_stage between steps: positive times and weight bytes for every per-layer
+    stage at the next step's context (fused attention at 11 keys, split attention with a
+    merging output projection at 151), and the generation continues bit for bit as if no
+    stage had been timed."""
+    import weight_streaming_gemv_amd as wsg
+    A = wsg._abi
+    m = wsg.Model(MINI, mini_w, max_context=192, prefill_chunk=64)
+    with pytest.raises(wsg.WsgError, match="STATE"):
+        m.time_stage(A.WSG_STAGE_GATEUP)
+    prompt = prompt_ids(42, n_prompt, MINI.vocab)
+    ref = [m.prefill(prompt)] + [m.step() for _ in range(4)]
+    ref_logits = _np(m.logits()).copy()
+    m.reset()
+    toks = [m.prefill(prompt)]
+    for stage in (A.WSG_STAGE_QKV, A.WSG_STAGE_ATTN, A.WSG_STAGE_GATEUP, A.WSG_STAGE_DOWN):
+        us, b = m.time_stage(stage, reps=3)
+        assert 0.5 < us < 1000 and b > 0, (stage, us, b)
+    if n_prompt < 128:
+        with pytest.raises(wsg.WsgError, match="UNSUPPORTED"):   # fused into the attention launch
+            m.time_stage(A.WSG_STAGE_O)
+    else:
+        us, b = m.time_stage(A.WSG_STAGE_O, reps=3)
+        assert b == MINI.hidden * MINI.q_width * 4
+    with pytest.raises(wsg.WsgError, match="INVALID_ARG"):
+        m.time_stage(A.WSG_STAGE_HEAD)
+    toks += [m.step() for _ in range(4)]
+    assert toks == ref and np.array_equal(_np(m.logits()), ref_logits)
+    m.close()
 
 
 def test_describe_reports_launch_shapes(mini_w):

@@ -330,6 +330,13 @@ class Model:
         check(_abi.lib().wsg_weight_storage(self.h, C.byref(pk), C.byref(tot), C.byref(b)))
         return {"packed_matrices": pk.value, "decode_matrices": tot.value, "decode_weight_bytes": b.value}
 
+    def time_stage(self, stage: int, reps: int = 10) -> Tuple[float, int]:
+        """(microseconds per launch, weight bytes per launch) of a per-layer stage, from
+        ``wsg_time_stage`` (a graph of the stage's launches over all layers, replayed)."""
+        us, b = C.c_double(), C.c_int64()
+        check(_abi.lib().wsg_time_stage(self.h, stage, reps, C.byref(us), C.byref(b)))
+        return us.value, b.value
+
     def describe(self) -> dict:
         """The model's launch shapes (``wsg_describe``) as a dict."""
         import json

@@ -19,6 +19,7 @@ WSG_W_DENSE, WSG_W_Q4G64 = 0, 1
 WSG_OPT_USE_GRAPH, WSG_OPT_TIMED_STAGE = 1, 2
 WSG_OPT_FUSE_ATTN_O, WSG_OPT_ROWS_ATTN_O = 3, 15
 WSG_OPT_HEAD_WAVES = 16
+WSG_OPT_SPLIT_DOWN = 17
 WSG_OPT_FOR_TWO_TOKEN = 0x100
 WSG_OPT_ROWS = {"qkv": 10, "o": 11, "gateup": 12, "down": 13, "head": 14}
 WSG_OPT_GRID = {"qkv": 20, "o": 21, "gateup": 22, "down": 23, "head": 24}
@@ -110,6 +111,7 @@ _SIGS = {
     "wsg_weight_storage": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                      C.POINTER(C.c_int64)]),
     "wsg_describe": (C.c_int, [C.c_void_p, C.c_char_p, C.c_size_t, C.POINTER(C.c_size_t)]),
+    "wsg_time_stage": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
     "wsg_last_error": (C.c_char_p, []),
     "wsg_version": (C.c_char_p, []),
 }

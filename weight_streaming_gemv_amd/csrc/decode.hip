@@ -61,6 +61,30 @@ struct Act {
         for (int i = 0; i < V16; ++i) a[c * VEC + u * V16 + i] = v.v[i];
       }
   }
+  // Sum of NP FP32 vectors (n-th at p + n * stride) in the same element order,
+  // added in order n = 0, 1, ... and rounded as stored: a residual that
+  // arrives as partial slices.  16-byte loads (VEC is a multiple of 4).
+  template <int NP>
+  __device__ __forceinline__ void load_sum_f32(const float* __restrict__ p, size_t stride) {
+    static_assert(VEC % 4 == 0, "whole float4 per lane and chunk");
+    const int lane = lane_id();
+    f4_t v[NP][NV * VEC / 4];
+#pragma unroll
+    for (int n = 0; n < NP; ++n)
+#pragma unroll
+      for (int c = 0; c < NV; ++c)
+#pragma unroll
+        for (int u = 0; u < VEC / 4; ++u)
+          v[n][c * VEC / 4 + u] = *reinterpret_cast<const f4_t*>(p + n * stride + c * kWave * VEC + lane * VEC + 4 * u);
+#pragma unroll
+    for (int i = 0; i < NV * VEC / 4; ++i) {
+      f4_t acc = v[0][i];
+#pragma unroll
+      for (int n = 1; n < NP; ++n) acc += v[n][i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[4 * i + e] = Store<TS>::to_f(Store<TS>::from_f(acc[e]));
+    }
+  }
   // From an FP32 array in the same element order (e.g. in LDS).
   __device__ __forceinline__ void load_f32(const float* p) {
     const int lane = lane_id();
@@ -112,11 +136,13 @@ struct WRows {
   static constexpr int VEC = Vec::N;
   static constexpr int NV = K / (kWave * VEC);
   Vec v[R][NV];
-  __device__ __forceinline__ void load(const TW* __restrict__ W, int row0, int M) {
+  // rows row0 .. row0+R-1 (clamped to M-1) of a matrix whose rows are ld
+  // elements apart (ld = K for whole rows; a K-slice of wider rows otherwise)
+  __device__ __forceinline__ void load(const TW* __restrict__ W, int row0, int M, size_t ld = K) {
     const int lane = lane_id();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const TW* wr = W + (size_t)min(row0 + r, M - 1) * K + lane * VEC;
+      const TW* wr = W + (size_t)min(row0 + r, M - 1) * ld + lane * VEC;
 #pragma unroll
       for (int c = 0; c < NV; ++c) v[r][c].template load<kWeightsNT>(wr + c * kWave * VEC);
     }
@@ -287,13 +313,17 @@ __device__ __forceinline__ float rows_prefetch(const TS* __restrict__ base, int 
 // ------------------------------------------------------------------ qkv
 // T query rows (a T-token step: positions p .. p+T-1) share every weight
 // row streamed: activations and outputs are [T][.] arrays.
-template <typename TS, typename TW, int H, int R, int T>
+// NPD > 0: the residual arrives as the previous layer's NPD split-K slices
+// of the down projection (FP32, the first carrying that layer's residual) at
+// dpart[(t*NPD + s)*H]: every wave sums them in slice order and rounds as
+// stored, and block 0 writes the residual x_res for the attention launch.
+template <typename TS, typename TW, int H, int R, int T, int NPD>
 __global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const TS* __restrict__ in_norm,
                                                 TS* __restrict__ x_res, const void* __restrict__ embed,
                                                 const int32_t* __restrict__ ids, const int32_t* __restrict__ ctrl,
                                                 const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
                                                 float* __restrict__ rope_cur, int first_layer, int vocab, float eps,
-                                                TS* __restrict__ out, int M) {
+                                                TS* __restrict__ out, int M, const float* __restrict__ dpart) {
   using Op = Operand<TS, TW, H>;
   const int ngroups = ceil_div(M, R);
   int g = wave_row_groups_begin();
@@ -302,12 +332,24 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const 
   // Vector loads return in issue order: the residual goes out before the
   // first weight rows (so the norm overlaps them); at layer 0 the
   // position -> id -> embedding chain is issued after them.
-  if (!first_layer)
+  if (!first_layer) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) x[t].load(x_res + t * H);
+    for (int t = 0; t < T; ++t) {
+      if constexpr (NPD > 0) x[t].template load_sum_f32<NPD>(dpart + (size_t)t * NPD * H, H);
+      else x[t].load(x_res + t * H);
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
   w.load(W, g * R, M);   // rows clamped into W: no branch around the loads
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NPD > 0) {
+    // the summed residual, for the attention launch (a constant index into x:
+    // a run-time one would move the array out of registers)
+    if (!first_layer && blockIdx.x == 0)
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        if (wave_id() == t) x[t].store(x_res + t * H);
+  }
   if (first_layer) {
     const int pos = ctrl[kCtrlPos];
     const int wave = wave_id();
@@ -405,6 +447,48 @@ __global__ __launch_bounds__(kBlock) void k_gemv_residual(const TW* __restrict__
   }
   // (no kernel of this launch reads the position)
   if (advance_pos && blockIdx.x == 0 && threadIdx.x == 0) ctrl[kCtrlPos] = ctrl[kCtrlPos] + T;
+}
+
+// --------------------------------------------------- down, split over K
+// The down projection in S slices of K (more, shorter waves: each streams
+// K/S of a row).  Block (b, s): row groups of block b, columns
+// [s*K/S, (s+1)*K/S); it writes FP32 slices
+//   dpart[(t*S + s)*M + m] = W[m, slice s] . in[t][slice s]  (+ x_in[t][m] for s = 0),
+// which the next layer's QKV launch adds up in slice order (rounding once,
+// as stored).  One-shot grid: gridDim.x blocks of 4 waves cover every row.
+template <typename TS, typename TW, int K, int S, int R, int T>
+__global__ __launch_bounds__(kBlock) void k_down_split(const TW* __restrict__ W, const TS* __restrict__ in,
+                                                       const TS* __restrict__ x_in, float* __restrict__ dpart, int M) {
+  constexpr int KS = K / S;
+  using Op = Operand<TS, TW, KS>;
+  const int sl = blockIdx.y;
+  const int g = wave_row_groups_begin();
+  typename Op::act x[T];
+  float xr[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    x[t].load(in + (size_t)t * K + sl * KS);
+    xr[t] = sl == 0 ? rows_prefetch<TS, R>(x_in + t * M, g * R, M) : 0.f;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  WRows<TW, KS, R> w;
+  w.load(W + (size_t)sl * KS, g * R, M, K);   // rows clamped into W: no branch around the loads
+  __builtin_amdgcn_sched_barrier(0);
+  typename Op::dot_t xd[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) xd[t] = Op::prep(x[t]);
+  const int lane = lane_id();
+  float acc[T][R];
+#pragma unroll
+  for (int t = 0; t < T; ++t) w.dot(xd[t], acc[t]);
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = wave_sum(acc[t][r]);
+      const int m = g * R + r;
+      if (lane == 0 && m < M) dpart[((size_t)t * S + sl) * M + m] = lane_value(xr[t], r) + v;
+    }
 }
 
 // -------------------------------------------------------------- gate/up
@@ -987,6 +1071,14 @@ __global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS*
 }
 
 // ------------------------------------------- attention + output projection
+// Blocks of the KV-head-split launches: one linear grid of (row blocks) x
+// n_kv, block i serving KV head i % n_kv and row block i / n_kv.  Workgroups
+// go to the XCDs round-robin by linear index, so with 8 KV heads all blocks
+// of a head run on one XCD and share its L2: the head's K/V prefix (or its
+// split states) comes from HBM once instead of once per XCD.
+__device__ __forceinline__ int kv_head_of_block(int n_kv) { return (int)blockIdx.x % n_kv; }
+__device__ __forceinline__ int row_block_of_block(int n_kv) { return (int)blockIdx.x / n_kv; }
+
 // Short contexts: the output GEMV is split by KV head.  Block (b, j)
 // recomputes the attention of KV head j over all keys (a few KiB per key
 // range, read from L2 by the blocks of that head), then multiplies its 4R
@@ -1157,11 +1249,11 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
   constexpr int WPR = kWavesPerBlock / T;
   __shared__ RowMerge<G, NR> sm[T];
   __shared__ float s_o[T][G * kD];
-  const int j = blockIdx.y;            // KV head
+  const int j = kv_head_of_block(n_kv);   // KV head
   const int lane = lane_id(), wave = wave_id();
   const int t = wave / WPR;            // this wave's query row
   const int sid = (wave % WPR) * 4 + (lane >> 4), sl = lane & 15;
-  const int row0 = (blockIdx.x * kWavesPerBlock + wave) * R;
+  const int row0 = (row_block_of_block(n_kv) * kWavesPerBlock + wave) * R;
   const size_t head_off = (size_t)j * cap * kD;
   const int Q = n_q * kD, KV = n_kv * kD, M = Q + 2 * KV;
   TS* kh = k_cache + head_off;
@@ -1184,7 +1276,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
   __builtin_amdgcn_sched_barrier(0);   // all loads issued in this order first
   const int pos0 = ctrl[kCtrlPos];
   SoftState<G> st;
-  ha.run(kh, vh, pos0 + t, 0, pos0, t > 0, true, blockIdx.x == 0, eps, sid, sl, st);
+  ha.run(kh, vh, pos0 + t, 0, pos0, t > 0, true, row_block_of_block(n_kv) == 0, eps, sid, sl, st);
 
   sm[t].put(st, sid, sl);
   __syncthreads();
@@ -1278,9 +1370,9 @@ __global__ __launch_bounds__(kBlock) void k_merge_o(const float* __restrict__ pa
   __shared__ float s_inv[TG];
   __shared__ f4_t s_acc[kWavesPerBlock][PL * kWave];
   __shared__ float s_o[T][G * kD];
-  const int j = blockIdx.y;
+  const int j = kv_head_of_block(n_kv);
   const int lane = lane_id(), wave = wave_id(), tid = threadIdx.x;
-  const int row0 = (blockIdx.x * kWavesPerBlock + wave) * R;
+  const int row0 = (row_block_of_block(n_kv) * kWavesPerBlock + wave) * R;
   const int Q = n_q * kD;
   const float* hp = part + (size_t)j * splits * G * kPartStride;   // row t adds t * trow
   const size_t trow = (size_t)n_kv * splits * G * kPartStride;
@@ -1454,22 +1546,70 @@ bool with_w(int wfmt, const void* w, const void* packed, F&& f) {
   return f(static_cast<const TS*>(w));
 }
 template <typename P> using pointee_t = typename std::remove_cv<typename std::remove_pointer<P>::type>::type;
+// The lossless packed copy applies to FP32 storage only.
+template <typename TS> const void* TS_packed(const void* p) { return std::is_same<TS, float>::value ? p : nullptr; }
 
 template <typename TS>
-bool qkv_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, hipStream_t s) {
+bool qkv_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, int npd, hipStream_t s) {
   const int M = (a.n_q + 2 * a.n_kv) * a.head_dim;
   const int grid = blocks_for(M, sh.rows_qkv, sh.grid_qkv);
   return with_w<TS>(a.wfmt, L.wqkv, L.wqkv_p, [&](auto W) {
     return with_k<pointee_t<decltype(W)>>(a.hidden, [&](auto kc) {
       return with_r(sh.rows_qkv, [&](auto rc) {
         return with_t(sh.tokens, [&](auto tc) {
-          hipLaunchKernelGGL((k_qkv<TS, pointee_t<decltype(W)>, decltype(kc)::value, decltype(rc)::value,
-                                    decltype(tc)::value>),
-                             dim3(grid), dim3(kBlock), 0, s, W, (const TS*)L.in_norm, (TS*)a.x, a.embed,
-                             a.ids, a.ctrl, a.rope_cos, a.rope_sin, a.rope_cur, first ? 1 : 0, a.vocab, a.eps,
-                             (TS*)a.qkv, M);
-          return true;
+          auto go = [&](auto nc) {
+            hipLaunchKernelGGL((k_qkv<TS, pointee_t<decltype(W)>, decltype(kc)::value, decltype(rc)::value,
+                                      decltype(tc)::value, decltype(nc)::value>),
+                               dim3(grid), dim3(kBlock), 0, s, W, (const TS*)L.in_norm, (TS*)a.x, a.embed,
+                               a.ids, a.ctrl, a.rope_cos, a.rope_sin, a.rope_cur, first ? 1 : 0, a.vocab, a.eps,
+                               (TS*)a.qkv, M, (const float*)a.dpart);
+            return true;
+          };
+          switch (first ? 0 : npd) {
+            case 0: return go(IC<0>{});
+            case 2: return go(IC<2>{});
+            case 4: return go(IC<4>{});
+            default: return false;
+          }
         });
+      });
+    });
+  });
+}
+
+// The down projection split over K into S FP32 slices (dense weights; the
+// slice width must hold whole lane vectors).
+template <typename TS>
+bool down_split_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, int S, hipStream_t s) {
+  if (a.wfmt != kWeightsDense) return false;
+  const int grid = blocks_for(a.hidden, sh.rows_down, 0);
+  return with_w<TS, false>(a.wfmt, L.wd, TS_packed<TS>(L.wd_p), [&](auto W) {
+    using TW = pointee_t<decltype(W)>;
+    return with_k<TW>(a.inter, [&](auto kc) {
+      return with_t(sh.tokens, [&](auto tc) {
+        constexpr int K = decltype(kc)::value, T = decltype(tc)::value;
+        auto go = [&](auto sc, auto rc) {
+          constexpr int SS = decltype(sc)::value, R = decltype(rc)::value;
+          if constexpr (K % SS == 0 && (K / SS) % (kWave * WVec<TW>::type::N) == 0) {
+            hipLaunchKernelGGL((k_down_split<TS, TW, K, SS, R, T>), dim3(grid, SS), dim3(kBlock), 0, s, W,
+                               (const TS*)a.act, (const TS*)a.x2, a.dpart, a.hidden);
+            return true;
+          } else {
+            return false;
+          }
+        };
+        auto with_s = [&](auto rc) {
+          switch (S) {
+            case 2: return go(IC<2>{}, rc);
+            case 4: return go(IC<4>{}, rc);
+            default: return false;
+          }
+        };
+        switch (sh.rows_down) {
+          case 1: return with_s(IC<1>{});
+          case 2: return with_s(IC<2>{});
+          default: return false;
+        }
       });
     });
   });
@@ -1617,7 +1757,7 @@ bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hi
       if constexpr (std::is_same<TW, q4w>::value && (R * GG * kD / 16) % kWave != 0) {
         return false;
       } else {
-        const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R), a.n_kv);
+        const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R) * a.n_kv);   // KV head = block % n_kv
         return with_t(sh.tokens, [&](auto tc) {
           hipLaunchKernelGGL((k_attn_o<TS, TW, GG, R, decltype(tc)::value>), grid, dim3(kBlock), 0, s,
                              (const TS*)a.qkv, (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm,
@@ -1655,7 +1795,7 @@ bool merge_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, h
       if constexpr (std::is_same<TW, q4w>::value && (R * GG * kD / 16) % kWave != 0) {
         return false;
       } else {
-        const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R), a.n_kv);
+        const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R) * a.n_kv);   // KV head = block % n_kv
         return with_t(sh.tokens, [&](auto tc) {
           hipLaunchKernelGGL((k_merge_o<TS, TW, GG, R, decltype(tc)::value>), grid, dim3(kBlock), 0, s, a.attn_part,
                              a.ctrl, a.n_q, a.n_kv, sh.attn_splits, sh.attn_chunk, Wo, (const TS*)a.x, a.hidden,
@@ -1688,8 +1828,11 @@ int head_blocks(const DecodeArgs& a, const DecodeShape& sh) {
   return head_grid(a.vocab, sh.rows_head, sh.head_waves, sh.grid_head);
 }
 
-bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, hipStream_t s) {
-  return a.dtype == 0 ? qkv_t<float>(a, sh, L, first, s) : qkv_t<__half>(a, sh, L, first, s);
+bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first, int npd, hipStream_t s) {
+  return a.dtype == 0 ? qkv_t<float>(a, sh, L, first, npd, s) : qkv_t<__half>(a, sh, L, first, npd, s);
+}
+bool launch_down_split(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, int S, hipStream_t s) {
+  return a.dtype == 0 ? down_split_t<float>(a, sh, L, S, s) : down_split_t<__half>(a, sh, L, S, s);
 }
 bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool direct, hipStream_t s) {
   return a.dtype == 0 ? attn_t<float>(a, sh, L, direct, s) : attn_t<__half>(a, sh, L, direct, s);

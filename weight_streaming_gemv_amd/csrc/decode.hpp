@@ -29,6 +29,9 @@ constexpr int kAttnPartStride = 132;
 // activation buffers below hold kMaxTokens rows.
 constexpr int kMaxTokens = 2;
 
+// Largest number of K slices of the split down projection.
+constexpr int kMaxDownSplit = 4;
+
 struct LayerPtrs {
   const void* wqkv;     // [(Q + 2 KV)][H]
   const void* wo;       // [H][Q]
@@ -71,6 +74,7 @@ struct DecodeArgs {
   void* act;            // [rows][I]
   void* logits;         // [rows][V]
   float* opart;         // [rows][slots][H] FP32 output-projection partials of the fused attention launch
+  float* dpart;         // [rows][kMaxDownSplit][H] FP32 split-K slices of the down projection
   float* attn_part;     // [rows][n_kv][splits][G] split-K partial states
   int attn_part_splits; // capacity in splits per KV head
   unsigned long long* am_part;  // per-block argmax keys of the head: row t's at [t * head blocks]
@@ -89,11 +93,19 @@ struct DecodeShape {
   int fuse_attn_o;                                       // short contexts: fused attention + output GEMV;
                                                          // longer ones: merge fused with the output GEMV
   int rows_attn_o;                                       // W_o rows per wave in the fused launch (4 or 8)
+  int split_down = 1;                                    // K slices of the down projection of every layer
+                                                         // but the last (1: one launch writes x)
   int tokens = 1;                                        // query rows of the step (1 or kMaxTokens)
 };
 
 // Stage launches; each returns false if the shape is not compiled in.
-bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first_layer, hipStream_t s);
+// npd > 0: the residual is the sum of the previous layer's npd split-K down
+// slices in a.dpart (written back to a.x by the launch); 0: read a.x.
+bool launch_qkv(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool first_layer, int npd,
+                hipStream_t s);
+// The down projection split over K into S (2 or 4) FP32 slices in a.dpart
+// (the first carrying the residual a.x2), for the next layer's QKV launch.
+bool launch_down_split(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, int S, hipStream_t s);
 // direct: a context within one split writes o itself (else every split
 // writes its partial state).
 bool launch_attn(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool direct, hipStream_t s);

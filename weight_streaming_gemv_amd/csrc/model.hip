@@ -175,7 +175,7 @@ int attn_split_cap(const Dims& d) {
 
 struct WsLayout {
   size_t kv = 0, rope_cos = 0, rope_sin = 0, rope_cur = 0, x = 0, x2 = 0, qkv = 0, o = 0, act = 0, logits = 0;
-  size_t opart = 0, attn_part = 0, am_part = 0, ctrl = 0, ids = 0, total = 0;
+  size_t opart = 0, dpart = 0, attn_part = 0, am_part = 0, ctrl = 0, ids = 0, total = 0;
   PrefillLayout pf;
   int attn_splits_cap = 1;
   int opart_slots = 0;
@@ -199,6 +199,7 @@ WsLayout ws_layout(const Dims& d) {
   w.logits = take(T * d.V * d.es);
   w.opart_slots = std::max(d.nkv, attn_o_part_slots(d.H, d.nkv, 1));
   w.opart = take(T * w.opart_slots * d.H * 4);
+  w.dpart = take(T * kMaxDownSplit * d.H * 4);
   w.attn_splits_cap = attn_split_cap(d);
   w.attn_part = take(T * d.nkv * w.attn_splits_cap * d.G * kAttnPartStride * 4);
   w.am_part = take(T * kHeadMaxBlocks * 8);
@@ -235,7 +236,10 @@ struct wsg_model {
   bool has_output = false;
   int32_t* pin = nullptr;          // pinned staging: [0] token out, [1..] ids in
   bool use_graph = true;
-  struct CachedGraph { hipGraphExec_t exec; uint64_t last_use; };
+  // a captured step graph; a graph captured while a per-layer stage was timed
+  // holds event-record nodes around that stage's launches (n_events events of
+  // ev, bracketing launches that stream `bytes` weight bytes in all)
+  struct CachedGraph { hipGraphExec_t exec; uint64_t last_use; int n_events; int64_t bytes; };
   std::map<uint64_t, CachedGraph> graphs;   // key: graph_key(splits, chunk, tokens, mode, advance)
   uint64_t graph_uses = 0;
   int timed_stage = -1;
@@ -273,14 +277,33 @@ int64_t stage_bytes(const wsg_model* m, int stage, int l) {
   }
 }
 
-// Events bracket launches of the timed stage kind.  Event-record nodes
-// inside HIP graphs do not carry usable timestamps, so in graph mode only the
-// head is timed, with events recorded on the stream around its own graph;
-// per-layer stages are timed in direct-launch mode.
+// Events bracket launches of the timed stage kind.  While a step graph is
+// captured, an event recorded on the stream becomes a node whose event has no
+// usable timestamps on this platform, so the event is added as an explicit
+// event-record node after the capture's current leaves instead, and the
+// captured work continues from that node; such nodes time correctly on replay.
 bool record_event(wsg_model* m, hipEvent_t e) {
-  const hipError_t r = hipEventRecord(e, m->stream);
+  hipError_t r;
+  const char* what = "hipEventRecord";
+  if (m->capturing) {
+    hipStreamCaptureStatus cs;
+    unsigned long long id = 0;
+    hipGraph_t g = nullptr;
+    const hipGraphNode_t* deps = nullptr;
+    size_t nd = 0;
+    hipGraphNode_t node = nullptr;
+    r = hipStreamGetCaptureInfo_v2(m->stream, &cs, &id, &g, &deps, &nd);
+    what = "hipStreamGetCaptureInfo_v2";
+    if (r == hipSuccess) { r = hipGraphAddEventRecordNode(&node, g, deps, nd, e); what = "hipGraphAddEventRecordNode"; }
+    if (r == hipSuccess) {
+      r = hipStreamUpdateCaptureDependencies(m->stream, &node, 1, hipStreamSetCaptureDependencies);
+      what = "hipStreamUpdateCaptureDependencies";
+    }
+  } else {
+    r = hipEventRecord(e, m->stream);
+  }
   if (r != hipSuccess) {
-    snprintf(m->event_msg, sizeof(m->event_msg), "hipEventRecord: %s", hipGetErrorString(r));
+    snprintf(m->event_msg, sizeof(m->event_msg), "%s: %s", what, hipGetErrorString(r));
     m->event_error = true;
     return false;
   }
@@ -289,7 +312,7 @@ bool record_event(wsg_model* m, hipEvent_t e) {
 
 template <typename F>
 bool timed(wsg_model* m, int stage, int64_t bytes, F&& launch) {
-  const bool t = !m->capturing && (m->timed_stage == stage) && (m->ev_used + 2 <= (int)m->ev.size());
+  const bool t = (m->timed_stage == stage) && (m->ev_used + 2 <= (int)m->ev.size());
   if (t) record_event(m, m->ev[m->ev_used]);
   const bool ok = launch();
   if (t) {
@@ -313,19 +336,35 @@ enum AttnMode : int {
   kAttnMergeO = 2,     // longer contexts: split-K attention, then the merge fused with that GEMV
 };
 
+// K slices of the down projection for a step of `tokens` rows: the launch
+// shape's, where the weights are dense, the slice width holds whole lane
+// vectors (256 FP32 or 512 FP16 elements) and a row group is 1 or 2 rows;
+// else 1.
+int down_split(const wsg_model* m, const DecodeShape& sh) {
+  const int S = sh.split_down;
+  if (S <= 1 || m->d.q4 || m->d.I % S || (sh.rows_down != 1 && sh.rows_down != 2)) return 1;
+  const int vec = m->d.es == 2 ? 512 : 256;
+  return (m->d.I / S) % vec == 0 ? S : 1;
+}
+
 // All layers of one step of `tokens` rows; the last down projection
 // advances the position when no head follows (prompt rows before the
-// last).
+// last).  With a split down projection, every layer but the last writes K
+// slices that the next layer's QKV launch sums; the last writes x itself,
+// for the head.
 bool enqueue_body(wsg_model* m, int splits, int chunk, int mode, bool advance, int tokens) {
   DecodeShape sh = shape_for(m, tokens);
   sh.attn_splits = splits;
   sh.attn_chunk = chunk;
   const hipStream_t s = m->stream;
   const int L = m->d.L;
+  const int S = down_split(m, sh);
   for (int l = 0; l < L; ++l) {
     const LayerPtrs& lp = m->layers[l];
     const DecodeArgs& a = m->args;
-    if (!timed(m, WSG_STAGE_QKV, stage_bytes(m, WSG_STAGE_QKV, l), [&] { return launch_qkv(a, sh, lp, l == 0, s); }))
+    const int npd = (l > 0 && S > 1) ? S : 0;
+    if (!timed(m, WSG_STAGE_QKV, stage_bytes(m, WSG_STAGE_QKV, l),
+               [&] { return launch_qkv(a, sh, lp, l == 0, npd, s); }))
       return false;
     if (mode == kAttnFused) {
       if (!timed(m, WSG_STAGE_ATTN, stage_bytes(m, WSG_STAGE_O, l), [&] { return launch_attn_o(a, sh, lp, s); }))
@@ -344,8 +383,10 @@ bool enqueue_body(wsg_model* m, int splits, int chunk, int mode, bool advance, i
     if (!timed(m, WSG_STAGE_GATEUP, stage_bytes(m, WSG_STAGE_GATEUP, l),
                [&] { return launch_gateup(a, sh, lp, mode != kAttnSeparate, s); }))
       return false;
-    if (!timed(m, WSG_STAGE_DOWN, stage_bytes(m, WSG_STAGE_DOWN, l),
-               [&] { return launch_down(a, sh, lp, advance && l == L - 1, s); }))
+    if (!timed(m, WSG_STAGE_DOWN, stage_bytes(m, WSG_STAGE_DOWN, l), [&] {
+          return (S > 1 && l < L - 1) ? launch_down_split(a, sh, lp, S, s)
+                                      : launch_down(a, sh, lp, advance && l == L - 1, s);
+        }))
       return false;
   }
   return true;
@@ -419,6 +460,8 @@ wsg_status graph_for(wsg_model* m, uint64_t key, F&& enqueue, hipGraphExec_t* ou
   if (it != m->graphs.end()) {
     it->second.last_use = ++m->graph_uses;
     *out = it->second.exec;
+    m->ev_used = it->second.n_events;
+    m->timed_bytes_per_launch_sum = it->second.bytes;
     return WSG_OK;
   }
   if (m->graphs.size() >= kMaxGraphs) {
@@ -431,6 +474,8 @@ wsg_status graph_for(wsg_model* m, uint64_t key, F&& enqueue, hipGraphExec_t* ou
   }
   WSG_HIP_CHECK(hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
   m->capturing = true;
+  m->ev_used = 0;
+  m->timed_bytes_per_launch_sum = 0;
   const bool ok = enqueue();
   m->capturing = false;
   hipGraph_t g = nullptr;
@@ -441,14 +486,22 @@ wsg_status graph_for(wsg_model* m, uint64_t key, F&& enqueue, hipGraphExec_t* ou
   const hipError_t ei = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
   (void)hipGraphDestroy(g);
   if (ei != hipSuccess) return fail(WSG_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ei));
-  m->graphs.emplace(key, wsg_model::CachedGraph{ex, ++m->graph_uses});
+  if (m->event_error) {
+    (void)hipGraphExecDestroy(ex);
+    m->event_error = false;
+    return fail(WSG_ERR_HIP, "timing event in a captured graph: %s", m->event_msg);
+  }
+  m->graphs.emplace(key, wsg_model::CachedGraph{ex, ++m->graph_uses, m->ev_used, m->timed_bytes_per_launch_sum});
   *out = ex;
   return WSG_OK;
 }
 
 
-uint64_t graph_key(int splits, int chunk, int tokens, int mode, bool advance) {
-  return ((((uint64_t)chunk << 20 | (uint64_t)splits) * 2 + (tokens - 1)) * 3 + mode) * 2 + (advance ? 1 : 0);
+// timed: the per-layer stage whose launches the graph brackets with event
+// nodes (-1: none).
+uint64_t graph_key(int splits, int chunk, int tokens, int mode, bool advance, int timed) {
+  const uint64_t k = ((((uint64_t)chunk << 20 | (uint64_t)splits) * 2 + (tokens - 1)) * 3 + mode) * 2 + (advance ? 1 : 0);
+  return k * 8 + (uint64_t)(timed + 1);
 }
 
 // The final norm + vocabulary head and the argmax over the residual rows in
@@ -483,7 +536,8 @@ wsg_status run_forward(wsg_model* m, bool head, int n_keys, int tokens = 1) {
       return fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape");
   } else {
     hipGraphExec_t body = nullptr;
-    const wsg_status st = graph_for(m, graph_key(splits, chunk, tokens, mode, advance),
+    const int tstage = m->timed_stage == WSG_STAGE_HEAD ? -1 : m->timed_stage;
+    const wsg_status st = graph_for(m, graph_key(splits, chunk, tokens, mode, advance, tstage),
                                     [&] { return enqueue_body(m, splits, chunk, mode, advance, tokens); }, &body);
     if (st != WSG_OK) return st;
     WSG_HIP_CHECK(hipGraphLaunch(body, m->stream));
@@ -744,6 +798,7 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   a.rope_sin = reinterpret_cast<const float*>(m->ws + wl.rope_sin);
   a.rope_cur = reinterpret_cast<float*>(m->ws + wl.rope_cur);
   a.opart = reinterpret_cast<float*>(m->ws + wl.opart);
+  a.dpart = reinterpret_cast<float*>(m->ws + wl.dpart);
   a.x = m->ws + wl.x; a.x2 = m->ws + wl.x2; a.qkv = m->ws + wl.qkv; a.o = m->ws + wl.o; a.act = m->ws + wl.act;
   a.logits = m->ws + wl.logits;
   a.attn_part = reinterpret_cast<float*>(m->ws + wl.attn_part);
@@ -791,6 +846,23 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   DecodeShape& sh = m->shape;
   sh.rows_qkv = sh.rows_o = sh.rows_gu = sh.rows_down = 1;
   sh.grid_qkv = sh.grid_o = sh.grid_gu = sh.grid_down = 0;
+  int cus = 0;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 0;
+  }
+  if (cus > 0 && d.es == 4 && !d.pack && !d.q4) {
+    // FP32 weights: QKV on 3 blocks per CU and gate/up on 2, looping over
+    // their row groups, instead of one-shot grids (4 and 3 per CU at the
+    // 0.6B shape): fewer waves repeat the norm prologue (the residual, the
+    // attention partials and the gain, read from L2 by every wave), and the
+    // second row group's weights are loaded while the first is reduced
+    // (28-layer sweep of 640..896 / 448..768 blocks, interleaved rounds:
+    // 1415 against 1384 tokens/s; neighbouring sizes were slower)
+    sh.grid_qkv = 3 * cus;
+    sh.grid_gu = 2 * cus;
+  }
   // head: two rows per wave on the one-shot grid (18992 workgroups for the
   // 151936-row vocabulary): with non-temporal weight loads the best of rows
   // 1/2/4 x 4/8 waves x grids 4096..one-shot; each wave's activation and
@@ -1017,14 +1089,10 @@ wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value) {
     case WSG_OPT_USE_GRAPH:
       if (value != 0 && value != 1) return fail(WSG_ERR_INVALID_ARG, "use_graph must be 0 or 1");
       if (value == 1 && m->stream == nullptr) return fail(WSG_ERR_STATE, "graphs need a non-null stream");
-      if (value == 1 && m->timed_stage >= 0 && m->timed_stage != WSG_STAGE_HEAD)
-        return fail(WSG_ERR_UNSUPPORTED, "in graph mode only the head stage can be timed");
       m->use_graph = value == 1;
       return WSG_OK;
     case WSG_OPT_TIMED_STAGE:
       if (value < -1 || value > WSG_STAGE_HEAD) return fail(WSG_ERR_INVALID_ARG, "stage %d", value);
-      if (m->use_graph && value >= 0 && value != WSG_STAGE_HEAD)
-        return fail(WSG_ERR_UNSUPPORTED, "in graph mode only the head stage can be timed (set use_graph 0 first)");
       m->timed_stage = value;
       m->acc_ms = 0; m->acc_launches = 0; m->acc_bytes = 0;
       return WSG_OK;
@@ -1048,6 +1116,10 @@ wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value) {
     case WSG_OPT_HEAD_WAVES:
       if (value != 4 && value != 8 && value != 16) return fail(WSG_ERR_INVALID_ARG, "head waves must be 4, 8 or 16");
       target = &sh.head_waves;
+      break;
+    case WSG_OPT_SPLIT_DOWN:
+      if (value != 1 && value != 2 && value != 4) return fail(WSG_ERR_INVALID_ARG, "down K slices must be 1, 2 or 4");
+      target = &sh.split_down;
       break;
     default:
       if (opt >= WSG_OPT_ROWS_QKV && opt <= WSG_OPT_ROWS_HEAD) {
@@ -1082,6 +1154,84 @@ wsg_status wsg_weight_storage(const wsg_model* m, int32_t* packed_matrices, int3
   return WSG_OK;
 }
 
+wsg_status wsg_time_stage(wsg_model* m, int32_t stage, int32_t reps, double* us_per_launch, int64_t* bytes_per_launch) {
+  clear_error();
+  if (!m || !us_per_launch || !bytes_per_launch) return fail(WSG_ERR_INVALID_ARG, "NULL pointer");
+  if (stage < WSG_STAGE_QKV || stage > WSG_STAGE_DOWN)
+    return fail(WSG_ERR_INVALID_ARG, "stage %d is not a per-layer stage", stage);
+  if (reps < 1 || reps > 10000) return fail(WSG_ERR_INVALID_ARG, "reps=%d outside [1, 10000]", reps);
+  if (!m->has_output || m->pos >= m->d.cap)
+    return fail(WSG_ERR_STATE, "time a stage between steps: after a prefill, with a free cache slot");
+  if (m->stream == nullptr) return fail(WSG_ERR_STATE, "stage timing needs a non-null stream");
+  // the launches the next one-token step would make, at its context
+  const int n_keys = m->pos + 1;
+  DecodeShape sh = shape_for(m, 1);
+  sh.attn_chunk = attn_chunk_for(m, n_keys);
+  sh.attn_splits = splits_for(n_keys, sh.attn_chunk);
+  const int mode = attn_mode(m, n_keys, 1);
+  const int S = down_split(m, sh);
+  const int L = m->d.L;
+  const DecodeArgs& a = m->args;
+  const hipStream_t s = m->stream;
+  (void)hipGetLastError();
+  WSG_HIP_CHECK(hipStreamSynchronize(s));
+  WSG_HIP_CHECK(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+  bool ok = true;
+  int64_t bytes = 0;
+  int launches = 0;
+  for (int l = 0; l < L && ok; ++l) {
+    const LayerPtrs& lp = m->layers[l];
+    switch (stage) {
+      case WSG_STAGE_QKV:   // layers after the first (the first also gathers the embedding)
+        if (l == 0) continue;
+        ok = launch_qkv(a, sh, lp, false, S > 1 ? S : 0, s);
+        break;
+      case WSG_STAGE_ATTN:
+        ok = mode == kAttnFused ? launch_attn_o(a, sh, lp, s) : launch_attn(a, sh, lp, mode == kAttnSeparate, s);
+        break;
+      case WSG_STAGE_O:
+        if (mode == kAttnFused) { ok = false; break; }
+        ok = mode == kAttnMergeO ? launch_merge_o(a, sh, lp, s) : launch_o(a, sh, lp, s);
+        break;
+      case WSG_STAGE_GATEUP:
+        ok = launch_gateup(a, sh, lp, mode != kAttnSeparate, s);
+        break;
+      case WSG_STAGE_DOWN:
+        ok = (S > 1 && l < L - 1) ? launch_down_split(a, sh, lp, S, s) : launch_down(a, sh, lp, false, s);
+        break;
+    }
+    if (stage == WSG_STAGE_ATTN)   // the cached keys and values it reads (+ W_o when fused)
+      bytes += (int64_t)2 * m->d.nkv * n_keys * m->d.D * (int64_t)m->d.es +
+               (mode == kAttnFused ? stage_bytes(m, WSG_STAGE_O, l) : 0);
+    else
+      bytes += stage_bytes(m, stage, l);
+    ++launches;
+  }
+  hipGraph_t g = nullptr;
+  const hipError_t ec = hipStreamEndCapture(s, &g);
+  if (!ok) {
+    if (g) (void)hipGraphDestroy(g);
+    return fail(WSG_ERR_UNSUPPORTED, "stage %d has no launch of its own at this context or shape", stage);
+  }
+  if (ec != hipSuccess) return fail(WSG_ERR_HIP, "graph capture: %s", hipGetErrorString(ec));
+  hipGraphExec_t ex = nullptr;
+  hipError_t e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return fail(WSG_ERR_HIP, "graph instantiate: %s", hipGetErrorString(e));
+  float ms = 0.f;
+  e = hipGraphLaunch(ex, s);   // warm-up replay
+  if (e == hipSuccess) e = hipEventRecord(m->ev[0], s);
+  for (int r = 0; r < reps && e == hipSuccess; ++r) e = hipGraphLaunch(ex, s);
+  if (e == hipSuccess) e = hipEventRecord(m->ev[1], s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, m->ev[0], m->ev[1]);
+  (void)hipGraphExecDestroy(ex);
+  if (e != hipSuccess) return fail(WSG_ERR_HIP, "stage timing: %s", hipGetErrorString(e));
+  *us_per_launch = (double)ms * 1e3 / ((double)reps * launches);
+  *bytes_per_launch = bytes / launches;
+  return WSG_OK;
+}
+
 wsg_status wsg_describe(const wsg_model* m, char* buf, size_t n, size_t* needed) {
   clear_error();
   if (!m || !needed) return fail(WSG_ERR_INVALID_ARG, "NULL pointer");
@@ -1096,8 +1246,8 @@ wsg_status wsg_describe(const wsg_model* m, char* buf, size_t n, size_t* needed)
              "\"grid_blocks\": {\"qkv\": %d, \"o\": %d, \"gateup\": %d, \"down\": %d, \"head\": %d}, ",
              sh.grid_qkv, sh.grid_o, sh.grid_gu, sh.grid_down, head_blocks(m->args, sh));
     j += t;
-    snprintf(t, sizeof(t), "\"head_waves\": %d, \"fuse_attn_o\": %d, \"rows_attn_o\": %d}, ", sh.head_waves,
-             sh.fuse_attn_o, sh.rows_attn_o);
+    snprintf(t, sizeof(t), "\"head_waves\": %d, \"fuse_attn_o\": %d, \"rows_attn_o\": %d, \"down_k_slices\": %d}, ",
+             sh.head_waves, sh.fuse_attn_o, sh.rows_attn_o, down_split(m, sh));
     j += t;
   };
   shape_json("one_token", shape_for(m, 1));
