@@ -12,9 +12,10 @@ tokens, logits and KV matched the CPU oracle on the same inputs; every timed
 generation must reproduce the validated token ids.
 
 Also reported: every decode stage against the HBM roofline, the one with
-the largest share of per-token stage time as ``roofline`` (its launches for
-all layers replayed as one graph between HIP events, after the timed
-region), the whole step's weight bytes per token times tokens/s
+the largest share of per-token stage time as ``roofline`` (its time per
+launch inside the step: the step's layer graph with and without the stage,
+replayed between HIP events after the timed region), the whole step's weight
+bytes per token times tokens/s
 (``step_roofline``), the head timed inside the timed region, the oracle timed
 on the host cores, provenance (hashes, versions, device, launch shapes), and
 (``--sweep``) the cold-cache GEMV sweep.  A validation failure anywhere
@@ -47,7 +48,9 @@ STAGE_KERNEL = {"qkv": "k_qkv", "attn": "k_attn_o", "o": "k_gemv_residual", "gat
 # runs, each scaled by what the same counter reads for a plain copy of known size
 # (FETCH x 2.0, WRITE x 1.0); valid only for the decode kernel sources they were
 # measured on (their hash below), else reported as null.
-DECODE_TRAFFIC = {"sha256_16": None, "bytes": {}}
+DECODE_TRAFFIC = {"sha256_16": "b0a220f5f0f543f3",
+                  "bytes": {"k_gateup": 25_541_488, "k_attn_o": 9_027_173, "k_qkv": 16_921_851,
+                            "k_gemv_residual": 12_759_480, "k_head": 623_635_636}}
 
 
 def decode_source_hash():
@@ -916,21 +919,22 @@ def long_context(torch, wsg, shape, w, trials=5, warmup=2, tune_len=2048, held_l
 
 def stage_pass(wsg, model, head, reps=20):
     """Per-stage HBM rooflines of the decode step.  Each per-layer stage is timed with
-    ``wsg_time_stage``: a graph of that stage's launches for all layers (each layer's own
-    weights, so the stream stays cold), replayed ``reps`` times between two HIP events on
-    the model stream, at the context of the next step.  One event pair around each single
-    launch would add its own dispatch cost (several microseconds on kernels of 4-9 us), so
-    the events bracket whole replays.  The head comes from the timed region (``head``: HIP
-    events around each of its launches, a single 90-us kernel).  Per stage: mean launch
-    time, algorithmic bytes per launch (weights; the attention launch's cached keys and
-    values plus, fused, its output-projection weights), achieved GB/s, and the
-    stage's share of the per-token time of all stages (n_layers launches per token for the
-    layer stages, one for the head)."""
+    ``wsg_time_stage``: the next step's layer body (one graph of all stages of all layers)
+    and the same body without that stage are replayed alternately ``reps`` times, each
+    replay between two HIP events on the model stream; the difference of the mean replay
+    times over the layer count is the stage's time per launch inside the step.  (An event
+    pair around one launch would add its own dispatch cost to kernels of 4-7 us, so the
+    events bracket whole replays.)  The head comes from the timed region (``head``: HIP
+    events around each of its launches, a single 90-us kernel).  Per stage: time per
+    launch, algorithmic bytes per launch (weights; the attention launch's cached keys and
+    values plus, fused, its output-projection weights), achieved GB/s, and the stage's
+    share of the per-token time of all stages (n_layers launches per token for the layer
+    stages, one for the head)."""
     L = model.shape.n_layers
     res = {}
     for name in ("qkv", "attn", "gateup", "down"):
         us, b = model.time_stage(STAGES[name], reps)
-        res[name] = {"kernel": STAGE_KERNEL[name], "launches": reps * (L - 1 if name == "qkv" else L),
+        res[name] = {"kernel": STAGE_KERNEL[name], "launches": reps * L,
                      "us_per_launch": round(us, 3), "bytes_per_launch": b, "gbps": round(b / (us * 1e-6) / 1e9, 1),
                      "ms_per_token": round(us * L / 1e3, 4)}
     if head:
@@ -1177,10 +1181,10 @@ def _main(argv=None):
                     "traffic": recorded_traffic(d["kernel"]), "bytes_per_launch": d["bytes_per_launch"],
                     "avg_launch_us": d["us_per_launch"], "launches_timed": d["launches"],
                     "share_of_stage_time": d["share"],
-                    "timing": "stage with the largest share of per-token stage time; its launches for all "
-                              "layers captured as one HIP graph (each layer's weights) and replayed between "
-                              "two HIP events on the model stream, after the timed region, at the context of "
-                              "the short prompt's first step"}
+                    "timing": "stage with the largest share of per-token stage time; time per launch = "
+                              "(step body graph - the same graph without the stage) / layers, HIP events around "
+                              "whole replays on the model stream, alternated 20 times each, after the timed "
+                              "region, at the context of the short prompt's first step"}
     else:
         roofline = timed_stage
     out = {
