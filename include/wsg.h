@@ -162,17 +162,28 @@ wsg_status wsg_pack_weights_q4(const wsg_config* cfg, const wsg_host_weights* no
 
 /* Size in bytes of the device workspace for cfg: KV cache
  * [n_layers][2][n_kv][max_context][head_dim], rotary table, stage buffers,
- * prefill chunk scratch, token history and control words. */
+ * prefill chunk scratch, token history and control words.  (Library
+ * plumbing: no passage of the pages defines it.)  Errors: an invalid config,
+ * a NULL bytes (WSG_ERR_INVALID_ARG / WSG_ERR_UNSUPPORTED). */
 wsg_status wsg_workspace_bytes(const wsg_config* cfg, size_t* bytes);
 
 /* Create a model over caller-owned device buffers: d_packed (a device copy
  * of the packed image) and d_workspace (at least wsg_workspace_bytes,
  * 256-byte aligned).  Both must stay allocated until wsg_model_destroy.
- * Builds and uploads the rotary table (synchronously, on hip_stream) and
- * clears the control words.  The cache starts empty (position 0). */
+ * Builds and uploads the rotary table (synchronously, on hip_stream; the
+ * host precomputes the rotary constants, Megakernels, "What runs in the
+ * DSL") and clears the control words.  The cache starts empty (position 0).
+ * The model object itself is library plumbing (no defining passage).
+ * Errors: an invalid config, NULL or misaligned buffers, buffers smaller
+ * than required (WSG_ERR_INVALID_ARG), a HIP failure (WSG_ERR_HIP; nothing
+ * is left allocated). */
 wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t packed_bytes,
                             void* d_workspace, size_t ws_bytes, void* hip_stream, wsg_model** out);
 
+/* Wait for the model stream, then release the library-owned host objects
+ * (graphs, events, pinned staging, an own stream); the caller's device
+ * buffers are untouched.  NULL is ignored.  (Library plumbing: no defining
+ * passage.) */
 void wsg_model_destroy(wsg_model* m);
 
 /* Empty the KV cache: valid length 0.  Stale slots are never read, since
@@ -229,7 +240,9 @@ wsg_status wsg_step(wsg_model* m, int32_t in_token, int32_t* out_token, const vo
 wsg_status wsg_step2(wsg_model* m, int32_t in_token, int32_t draft, int32_t out_tokens[2], int32_t* n_emitted,
                      const void** out_logits);
 
-/* Current position (number of valid KV entries). */
+/* Current position (number of valid KV entries; Benchmark methodology,
+ * "Long-document chunked prefill": a 4096-token prompt and 1024 outputs
+ * leave 5119).  -1 for a NULL model. */
 int32_t wsg_position(const wsg_model* m);
 
 /* Truncate the sequence to its first pos tokens (0 <= pos <= position):
@@ -244,10 +257,14 @@ int32_t wsg_position(const wsg_model* m);
 wsg_status wsg_rewind(wsg_model* m, int32_t pos);
 
 /* Device pointers to layer `layer`'s K and V cache blocks, each laid out
- * [n_kv][max_context][head_dim] in the storage dtype, and the valid length.
- * For validation; the memory belongs to the workspace. */
+ * [n_kv][max_context][head_dim] in the storage dtype, the valid length, and
+ * (if strides is not NULL) the element strides of those three axes.  For
+ * validation (Benchmark methodology, "Long-document chunked prefill": every
+ * valid KV entry is checked); the memory belongs to the workspace.  Errors:
+ * NULL arguments (WSG_ERR_INVALID_ARG), a layer outside [0, n_layers)
+ * (WSG_ERR_OUT_OF_RANGE). */
 wsg_status wsg_kv_view(const wsg_model* m, int32_t layer, const void** d_k, const void** d_v,
-                       int32_t* valid_len);
+                       int32_t* valid_len, int64_t strides[3]);
 
 /* Rows per prefill chunk for later wsg_prefill calls: 1 <= rows <=
  * cfg.prefill_chunk (Benchmark methodology, "Long-document chunked
@@ -311,24 +328,25 @@ wsg_status wsg_set_option(wsg_model* m, int32_t option, int32_t value);
  * the accumulators. */
 wsg_status wsg_stage_time(wsg_model* m, double* total_ms, int64_t* launches, int64_t* bytes);
 
-/* Average device time of one launch of a per-layer decode stage
- * (WSG_STAGE_QKV, _ATTN, _O, _GATEUP or _DOWN) at the model's shapes and the
- * context of its next one-token step: a HIP graph of that stage's launches
- * for every layer in turn (each with its own layer's weights; QKV skips the
- * first layer, whose launch also gathers the embedding) is replayed `reps`
- * times back to back between two events on the model stream, so the
- * events' own cost is spread over reps * n_layers launches.  *bytes_per_launch
- * receives the algorithmic bytes of one launch: its weights, and for the
- * attention stage the keys and values of the context (plus the output-
- * projection weights when it is fused with attention).  For the roofline of a stage
- * (Megakernels, "GPU-wide end-to-end generation": the stages of a forward
- * are ordered launches).  What the launches leave in the stage buffers and in
- * the next cache slot is rewritten by the next step before it is read; the
- * valid cache prefix, the position and the last logits are untouched.
- * Blocks until done.  Errors:
- * WSG_ERR_INVALID_ARG (stage, reps outside [1, 10000], NULL), WSG_ERR_STATE
- * (no prefill yet or a full cache), WSG_ERR_UNSUPPORTED (WSG_STAGE_O at a
- * context where it is fused into the attention launch). */
+/* Device time one launch of a per-layer decode stage (WSG_STAGE_QKV, _ATTN,
+ * _O, _GATEUP or _DOWN) adds to a step, at the model's shapes and the context
+ * of its next one-token step: the layer body of that step (all stages of all
+ * layers, as one HIP graph) and the same body without the stage's launches
+ * are replayed alternately `reps` times each, every replay between two events
+ * on the model stream, and the difference of the mean replay times is divided
+ * by n_layers.  An event pair around a single launch would add its own
+ * dispatch cost to kernels of a few microseconds; whole replays spread it.
+ * *bytes_per_launch receives the algorithmic bytes of one launch: its
+ * weights, and for the attention stage the keys and values of the context
+ * (plus the output-projection weights when it is fused with attention).  For
+ * the roofline of a stage (Megakernels, "GPU-wide end-to-end generation": the
+ * stages of a forward are ordered launches).  What the replays leave in the
+ * stage buffers and in the next cache slot is rewritten by the next step
+ * before it is read; the valid cache prefix, the position and the last
+ * logits are untouched.  Blocks until done.  Errors: WSG_ERR_INVALID_ARG
+ * (stage, reps outside [1, 10000], NULL), WSG_ERR_STATE (no prefill yet or a
+ * full cache), WSG_ERR_UNSUPPORTED (WSG_STAGE_O at a context where it runs
+ * inside the attention launch). */
 wsg_status wsg_time_stage(wsg_model* m, int32_t stage, int32_t reps, double* us_per_launch, int64_t* bytes_per_launch);
 
 /* Stand-alone GEMV, Y[t][m] = sum_k W[m][k] X[t][k] for t < T, with FP32
@@ -453,10 +471,11 @@ wsg_status wsg_weight_storage(const wsg_model* m, int32_t* packed_matrices, int3
  * NULL) and the full length + 1 to *needed.  Errors: NULL model or needed. */
 wsg_status wsg_describe(const wsg_model* m, char* buf, size_t n, size_t* needed);
 
-/* Message for the last error on this host thread ("" if none). */
+/* Message for the last error on this host thread ("" if none).  (Library
+ * plumbing: no defining passage.) */
 const char* wsg_last_error(void);
 
-/* Library version string. */
+/* Library version string.  (Library plumbing: no defining passage.) */
 const char* wsg_version(void);
 
 #ifdef __cplusplus

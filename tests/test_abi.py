@@ -141,6 +141,13 @@ def test_model_calls_reject_null(abi):
     assert L.wsg_step(None, -1, C.byref(n), C.byref(lp)) == abi.WSG_ERR_INVALID_ARG
     assert L.wsg_rewind(None, 0) == abi.WSG_ERR_INVALID_ARG
     assert L.wsg_position(None) == -1
+    k, v = C.c_void_p(), C.c_void_p()
+    st = (C.c_int64 * 3)()
+    assert L.wsg_kv_view(None, 0, C.byref(k), C.byref(v), C.byref(n), st) == abi.WSG_ERR_INVALID_ARG
+    need = C.c_size_t()
+    assert L.wsg_describe(None, None, 0, C.byref(need)) == abi.WSG_ERR_INVALID_ARG
+    us, b = C.c_double(), C.c_int64()
+    assert L.wsg_time_stage(None, 3, 1, C.byref(us), C.byref(b)) == abi.WSG_ERR_INVALID_ARG
 
 
 def test_pack_weights_layout_is_bit_copy(abi):

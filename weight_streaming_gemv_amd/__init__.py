@@ -354,9 +354,13 @@ class Model:
         return v if rows == 1 else v.view(rows, self.shape.vocab)
 
     def kv(self, layer: int):
-        """(K, V, valid_len): device views [n_kv, max_context, head_dim]."""
+        """(K, V, valid_len): device views [n_kv, max_context, head_dim] with the strides
+        the library reports."""
         k, v, n = C.c_void_p(), C.c_void_p(), C.c_int32()
-        check(_abi.lib().wsg_kv_view(self.h, layer, C.byref(k), C.byref(v), C.byref(n)))
+        st = (C.c_int64 * 3)()
+        check(_abi.lib().wsg_kv_view(self.h, layer, C.byref(k), C.byref(v), C.byref(n), st))
         sh = (self.shape.n_kv_heads, self.cfg.max_context, self.shape.head_dim)
-        cnt = sh[0] * sh[1] * sh[2]
-        return self._view(k.value, cnt).view(sh), self._view(v.value, cnt).view(sh), n.value
+        strides = tuple(st)
+        cnt = (sh[0] - 1) * strides[0] + (sh[1] - 1) * strides[1] + (sh[2] - 1) * strides[2] + 1
+        return (self._view(k.value, cnt).as_strided(sh, strides), self._view(v.value, cnt).as_strided(sh, strides),
+                n.value)

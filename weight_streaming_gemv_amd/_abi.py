@@ -85,7 +85,7 @@ _SIGS = {
                             C.POINTER(C.c_void_p)]),
     "wsg_position": (C.c_int32, [C.c_void_p]),
     "wsg_kv_view": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
-                              C.POINTER(C.c_int32)]),
+                              C.POINTER(C.c_int32), C.POINTER(C.c_int64)]),
     "wsg_set_prefill_chunk": (C.c_int, [C.c_void_p, C.c_int32]),
     "wsg_set_option": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32]),
     "wsg_stage_time": (C.c_int, [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_int64),

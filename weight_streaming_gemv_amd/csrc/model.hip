@@ -252,6 +252,7 @@ struct wsg_model {
   int prefill_rows = 0;
   bool event_error = false;
   bool capturing = false;
+  int skip_stage = -1;   // a stage kind enqueue_body leaves out (stage timing by difference)
   char event_msg[160] = {0};
 };
 
@@ -312,6 +313,7 @@ bool record_event(wsg_model* m, hipEvent_t e) {
 
 template <typename F>
 bool timed(wsg_model* m, int stage, int64_t bytes, F&& launch) {
+  if (stage == m->skip_stage) return true;
   const bool t = (m->timed_stage == stage) && (m->ev_used + 2 <= (int)m->ev.size());
   if (t) record_event(m, m->ev[m->ev_used]);
   const bool ok = launch();
@@ -1063,13 +1065,19 @@ wsg_status wsg_step2(wsg_model* m, int32_t in_token, int32_t draft, int32_t out_
   return WSG_OK;
 }
 
-wsg_status wsg_kv_view(const wsg_model* m, int32_t layer, const void** d_k, const void** d_v, int32_t* valid_len) {
+wsg_status wsg_kv_view(const wsg_model* m, int32_t layer, const void** d_k, const void** d_v, int32_t* valid_len,
+                       int64_t strides[3]) {
   clear_error();
   if (!m || !d_k || !d_v || !valid_len) return fail(WSG_ERR_INVALID_ARG, "NULL pointer");
   if (layer < 0 || layer >= m->d.L) return fail(WSG_ERR_OUT_OF_RANGE, "layer %d outside [0, %d)", layer, m->d.L);
   *d_k = m->layers[layer].k_cache;
   *d_v = m->layers[layer].v_cache;
   *valid_len = m->pos;
+  if (strides) {
+    strides[0] = (int64_t)m->d.cap * m->d.D;   // KV head
+    strides[1] = m->d.D;                       // position
+    strides[2] = 1;                            // dim
+  }
   return WSG_OK;
 }
 
@@ -1163,72 +1171,69 @@ wsg_status wsg_time_stage(wsg_model* m, int32_t stage, int32_t reps, double* us_
   if (!m->has_output || m->pos >= m->d.cap)
     return fail(WSG_ERR_STATE, "time a stage between steps: after a prefill, with a free cache slot");
   if (m->stream == nullptr) return fail(WSG_ERR_STATE, "stage timing needs a non-null stream");
-  // the launches the next one-token step would make, at its context
+  // the layer body the next one-token step would run, at its context
   const int n_keys = m->pos + 1;
-  DecodeShape sh = shape_for(m, 1);
-  sh.attn_chunk = attn_chunk_for(m, n_keys);
-  sh.attn_splits = splits_for(n_keys, sh.attn_chunk);
+  const int chunk = attn_chunk_for(m, n_keys);
+  const int splits = splits_for(n_keys, chunk);
   const int mode = attn_mode(m, n_keys, 1);
-  const int S = down_split(m, sh);
-  const int L = m->d.L;
-  const DecodeArgs& a = m->args;
+  if (stage == WSG_STAGE_O && mode == kAttnFused)
+    return fail(WSG_ERR_UNSUPPORTED, "the output projection runs inside the attention launch at this context");
   const hipStream_t s = m->stream;
+  const int saved_timed = m->timed_stage;
+  m->timed_stage = -1;
+  hipGraphExec_t ex[2] = {nullptr, nullptr};
+  wsg_status st = WSG_OK;
   (void)hipGetLastError();
-  WSG_HIP_CHECK(hipStreamSynchronize(s));
-  WSG_HIP_CHECK(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-  bool ok = true;
+  for (int k = 0; k < 2 && st == WSG_OK; ++k) {   // 0: every stage, 1: all but `stage`
+    m->skip_stage = k == 0 ? -1 : stage;
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) { st = fail(WSG_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e)); break; }
+    m->capturing = true;
+    const bool ok = enqueue_body(m, splits, chunk, mode, false, 1);
+    m->capturing = false;
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(s, &g);
+    if (!ok) st = fail(WSG_ERR_UNSUPPORTED, "no compiled kernel for this shape");
+    else if (e != hipSuccess) st = fail(WSG_ERR_HIP, "graph capture: %s", hipGetErrorString(e));
+    else if ((e = hipGraphInstantiate(&ex[k], g, nullptr, nullptr, 0)) != hipSuccess)
+      st = fail(WSG_ERR_HIP, "graph instantiate: %s", hipGetErrorString(e));
+    if (g) (void)hipGraphDestroy(g);
+  }
+  m->skip_stage = -1;
+  m->timed_stage = saved_timed;
+  m->ev_used = 0;
+  // alternate the two graphs; each replay between its own pair of events
+  double t[2] = {0.0, 0.0};
+  hipError_t e = hipSuccess;
+  if (st == WSG_OK) {
+    e = hipGraphLaunch(ex[0], s);   // warm-up
+    if (e == hipSuccess) e = hipGraphLaunch(ex[1], s);
+    for (int r = 0; r < reps && e == hipSuccess; ++r)
+      for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+        e = hipEventRecord(m->ev[0], s);
+        if (e == hipSuccess) e = hipGraphLaunch(ex[k], s);
+        if (e == hipSuccess) e = hipEventRecord(m->ev[1], s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, m->ev[0], m->ev[1]);
+        t[k] += ms;
+      }
+    if (e != hipSuccess) st = fail(WSG_ERR_HIP, "stage timing: %s", hipGetErrorString(e));
+  }
+  for (auto x : ex)
+    if (x) (void)hipGraphExecDestroy(x);
+  if (st != WSG_OK) return st;
+  const int L = m->d.L;
+  *us_per_launch = (t[0] - t[1]) * 1e3 / ((double)reps * L);
   int64_t bytes = 0;
-  int launches = 0;
-  for (int l = 0; l < L && ok; ++l) {
-    const LayerPtrs& lp = m->layers[l];
-    switch (stage) {
-      case WSG_STAGE_QKV:   // layers after the first (the first also gathers the embedding)
-        if (l == 0) continue;
-        ok = launch_qkv(a, sh, lp, false, S > 1 ? S : 0, s);
-        break;
-      case WSG_STAGE_ATTN:
-        ok = mode == kAttnFused ? launch_attn_o(a, sh, lp, s) : launch_attn(a, sh, lp, mode == kAttnSeparate, s);
-        break;
-      case WSG_STAGE_O:
-        if (mode == kAttnFused) { ok = false; break; }
-        ok = mode == kAttnMergeO ? launch_merge_o(a, sh, lp, s) : launch_o(a, sh, lp, s);
-        break;
-      case WSG_STAGE_GATEUP:
-        ok = launch_gateup(a, sh, lp, mode != kAttnSeparate, s);
-        break;
-      case WSG_STAGE_DOWN:
-        ok = (S > 1 && l < L - 1) ? launch_down_split(a, sh, lp, S, s) : launch_down(a, sh, lp, false, s);
-        break;
-    }
+  for (int l = 0; l < L; ++l) {
     if (stage == WSG_STAGE_ATTN)   // the cached keys and values it reads (+ W_o when fused)
       bytes += (int64_t)2 * m->d.nkv * n_keys * m->d.D * (int64_t)m->d.es +
                (mode == kAttnFused ? stage_bytes(m, WSG_STAGE_O, l) : 0);
     else
       bytes += stage_bytes(m, stage, l);
-    ++launches;
   }
-  hipGraph_t g = nullptr;
-  const hipError_t ec = hipStreamEndCapture(s, &g);
-  if (!ok) {
-    if (g) (void)hipGraphDestroy(g);
-    return fail(WSG_ERR_UNSUPPORTED, "stage %d has no launch of its own at this context or shape", stage);
-  }
-  if (ec != hipSuccess) return fail(WSG_ERR_HIP, "graph capture: %s", hipGetErrorString(ec));
-  hipGraphExec_t ex = nullptr;
-  hipError_t e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-  (void)hipGraphDestroy(g);
-  if (e != hipSuccess) return fail(WSG_ERR_HIP, "graph instantiate: %s", hipGetErrorString(e));
-  float ms = 0.f;
-  e = hipGraphLaunch(ex, s);   // warm-up replay
-  if (e == hipSuccess) e = hipEventRecord(m->ev[0], s);
-  for (int r = 0; r < reps && e == hipSuccess; ++r) e = hipGraphLaunch(ex, s);
-  if (e == hipSuccess) e = hipEventRecord(m->ev[1], s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e == hipSuccess) e = hipEventElapsedTime(&ms, m->ev[0], m->ev[1]);
-  (void)hipGraphExecDestroy(ex);
-  if (e != hipSuccess) return fail(WSG_ERR_HIP, "stage timing: %s", hipGetErrorString(e));
-  *us_per_launch = (double)ms * 1e3 / ((double)reps * launches);
-  *bytes_per_launch = bytes / launches;
+  *bytes_per_launch = bytes / L;
   return WSG_OK;
 }
 
