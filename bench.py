@@ -4,7 +4,11 @@
 One step = the four short greedy generations of the pages' GPU-wide study
 (prompt/output 8/8, 8/16, 32/8, 32/16; Megakernels, "GPU-wide end-to-end
 generation"), each timed from before the cache reset to the last token id
-on the host.  ``value`` is the post-first-token decode rate: generated
+on the host.  The decode steps of a generation go through ``wsg_generate``
+(enqueued back to back, one wait at the end: the token is chosen on the GPU
+and the history stays there); the same generations with one waiting
+``wsg_step`` per token are reported as ``step_loop``.  ``value`` is the
+post-first-token decode rate: generated
 tokens after the first, divided by the time after the first token
 (Benchmark methodology, "What the measurements mean" and "Long-document
 chunked prefill").  Timings are published only after the GPU's greedy
@@ -16,7 +20,8 @@ the largest share of per-token stage time as ``roofline`` (its time per
 launch inside the step: the step's layer graph with and without the stage,
 replayed between HIP events after the timed region), the whole step's weight
 bytes per token times tokens/s
-(``step_roofline``), the head timed inside the timed region, the oracle timed
+(``step_roofline``), the head timed with HIP events in the step-loop pass
+after the timed region, the oracle timed
 on the host cores, provenance (hashes, versions, device, launch shapes), and
 (``--sweep``) the cold-cache GEMV sweep.  A validation failure anywhere
 publishes nothing (exit status 3).
@@ -93,14 +98,19 @@ def cpu_threads():
     return len(os.sched_getaffinity(0))
 
 
-def generate(model, prompt, n_out):
-    """One timed greedy generation: (tokens, ttft_s, decode_s, total_s)."""
+def generate(model, prompt, n_out, pipelined=True):
+    """One timed greedy generation: (tokens, ttft_s, decode_s, total_s).  Pipelined: the
+    decode steps through ``wsg_generate`` (enqueued back to back, one wait); else one
+    ``wsg_step`` per token, each waiting for its token."""
     t0 = time.perf_counter()
     model.reset()
     toks = [model.prefill(prompt)]
     t1 = time.perf_counter()
-    for _ in range(n_out - 1):
-        toks.append(model.step())
+    if pipelined:
+        toks += model.generate(n_out - 1)
+    else:
+        for _ in range(n_out - 1):
+            toks.append(model.step())
     t2 = time.perf_counter()
     return toks, t1 - t0, t2 - t1, t2 - t0
 
@@ -629,14 +639,15 @@ def two_token(torch, wsg, shape, w, context=16, trials=9, reps=50, n_prompt=32, 
             if t > 0:
                 rates.append((len(out) - 1) / dt)
         gen[name] = {"decode_tok_s": round(statistics.median(rates), 1), "two_token_steps": k}
-    g_rates = []
-    for t in range(trials + 1):
-        toks, _, dec, _ = generate(model, prompt, n_out)
-        if toks != greedy:
-            raise ValidationError("greedy generation not repeatable")
-        if t > 0:
-            g_rates.append((n_out - 1) / dec)
-    gen["greedy_step_only"] = {"decode_tok_s": round(statistics.median(g_rates), 1)}
+    for name, pipelined in (("greedy_step_only", False), ("greedy_generate", True)):
+        g_rates = []
+        for t in range(trials + 1):
+            toks, _, dec, _ = generate(model, prompt, n_out, pipelined)
+            if toks != greedy:
+                raise ValidationError(f"greedy generation ({name}) not repeatable")
+            if t > 0:
+                g_rates.append((n_out - 1) / dec)
+        gen[name] = {"decode_tok_s": round(statistics.median(g_rates), 1)}
     model.close()
     res["speculative_generation"] = gen
     res["validation"] = {"max_abs_logit_err": max_l, "max_abs_kv_err": max_kv, "steps_checked": 4,
@@ -704,19 +715,23 @@ def f16_storage_decoder(torch, wsg, shape, fmt, steps=5, warmup=2, n_check=8):
         max_kv = max(max_kv, cmp(k[:, :n], orc.k_cache[l][:, :n], f"K prefix {l}"),
                      cmp(v[:, :n], orc.v_cache[l][:, :n], f"V prefix {l}"))
     del orc
-    # timed generations (tokens must repeat exactly run to run)
-    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, STAGES["head"])
+    # timed generations (tokens must repeat exactly run to run), then one pass of
+    # step-by-step generations with HIP events around the head
     expected, rec = {}, []
     for i in range(warmup + steps):
-        if i == warmup:
-            model.stage_time()
         for (n_p, n_o) in COMBOS:
             toks, ttft, dec, tot = generate(model, prompts[n_p], n_o)
             if expected.setdefault((n_p, n_o), toks) != toks:
                 raise ValidationError(f"{fmt} generation {n_p}/{n_o} not repeatable")
             if i >= warmup:
                 rec.append((n_p, n_o, ttft, dec))
+    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, STAGES["head"])
+    model.stage_time()
+    for (n_p, n_o) in COMBOS:
+        if generate(model, prompts[n_p], n_o, pipelined=False)[0] != expected[(n_p, n_o)]:
+            raise ValidationError(f"{fmt} step-by-step generation {n_p}/{n_o} differs")
     ms, nl, by = model.stage_time()
+    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, -1)
     st = model.storage()
     model.close()
     value = sum(n_o - 1 for _, n_o, _, _ in rec) / sum(r[3] for r in rec)
@@ -1122,11 +1137,11 @@ def _main(argv=None):
             return 0
     del w
     stage = STAGES[args.timed_stage]
-    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, stage)
+    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, -1)
 
-    def run_step(rec):
+    def run_step(rec, pipelined=True):
         for (n_p, n_o) in COMBOS:
-            toks, ttft, dec, tot = generate(model, prompts[n_p], n_o)
+            toks, ttft, dec, tot = generate(model, prompts[n_p], n_o, pipelined)
             if expected and toks != expected[(n_p, n_o)]:
                 raise ValidationError(f"timed generation {n_p}/{n_o} returned {toks}, validated "
                                       f"{expected[(n_p, n_o)]}")
@@ -1135,7 +1150,6 @@ def _main(argv=None):
 
     for _ in range(args.warmup):
         run_step(None)
-    model.stage_time()   # reset the event accumulators
     rec = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -1143,7 +1157,19 @@ def _main(argv=None):
         run_step(rec)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # After the timed region: the same generations one wsg_step per token, with HIP
+    # events around the timed stage's launches (no events inside the timed region).
+    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, stage)
+    run_step(None, pipelined=False)
+    model.stage_time()   # reset the event accumulators
+    step_rec = []
+    for _ in range(args.steps):
+        run_step(step_rec, pipelined=False)
     st_ms, st_n, st_bytes = model.stage_time()
+    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, -1)
+    step_loop = {"decode_tok_s": round(sum(n_o - 1 for (_, n_o, _, _, _) in step_rec) / sum(r[3] for r in step_rec), 2),
+                 "note": "the same generations with one wsg_step call per token (each waits for its token), "
+                         "HIP events around the timed stage's launches; after the timed region"}
 
     dec_tokens = sum(n_o - 1 for (_, n_o, _, _, _) in rec)
     dec_time = sum(r[3] for r in rec)
@@ -1164,8 +1190,8 @@ def _main(argv=None):
                    "traffic": recorded_traffic(STAGE_KERNEL[args.timed_stage]),
                    "bytes_per_launch": st_bytes // max(st_n, 1), "avg_launch_us": round(avg_launch_ms * 1e3, 3),
                    "launches_timed": st_n, "timing": "HIP events on the model stream around each launch, "
-                                                    "in the timed region (graph replay; the head is a direct launch)"}
-    model.set_option(wsg._abi.WSG_OPT_TIMED_STAGE, -1)
+                                                    "in the step-loop pass after the timed region (graph replay; "
+                                                    "the head is a direct launch)"}
     stages = {}
     if args.roofline_reps:
         # at the context of the first short prompt's first step (its prefill done)
@@ -1210,6 +1236,8 @@ def _main(argv=None):
                           "frac": round(weight_bytes * value / 1e9 / HBM_PEAK_GBPS, 4),
                           "note": "decode weight bytes per token x post-first-token tokens/s"},
         "per_combo_median": per_combo,
+        "decode_loop": "wsg_generate: the decode steps of a generation enqueued back to back, one wait",
+        "step_loop": step_loop,
         "roofline": roofline,
         "stage_rooflines": stages,
         ("roofline_" + args.timed_stage): timed_stage,

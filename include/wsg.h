@@ -209,11 +209,27 @@ wsg_status wsg_prefill(wsg_model* m, const int32_t* host_ids, int32_t n,
 
 /* One decode step at position pos: consumes in_token (or, if in_token < 0,
  * the previous greedy output, which never leaves the device), appends its
- * K/V to the cache and returns the next greedy token.  The only
- * device-to-host transfer is the 4-byte token id (Megakernels, "GPU-wide
- * end-to-end generation").  Errors: in_token >= vocab; in_token < 0 with no
- * previous output (WSG_ERR_STATE); pos == max_context. */
+ * K/V to the cache and returns the next greedy token.  The 4-byte token id
+ * is the only data that reaches the host (Megakernels, "GPU-wide end-to-end
+ * generation"): the argmax launch stores it in pinned host memory and the
+ * call waits for the model stream.  Errors: in_token >= vocab; in_token < 0
+ * with no previous output (WSG_ERR_STATE); pos == max_context. */
 wsg_status wsg_step(wsg_model* m, int32_t in_token, int32_t* out_token, const void** out_logits);
+
+/* n greedy decode steps in a row, each consuming the previous one's token
+ * (the first: the last greedy output), with one wait at the end: the token
+ * is chosen on the GPU and the device keeps the token history, so no step
+ * waits for the host (Megakernels, "GPU-wide end-to-end generation": the
+ * loop needs no host round trip per token).  Writes the n tokens to
+ * out_tokens[0..n) (host memory) and leaves the position at pos + n; the
+ * result equals n calls of wsg_step(m, -1, ...).  There is no stop token:
+ * callers that stop early (an end-of-sequence id) use wsg_step, or rewind
+ * past the tokens they drop.  n = 0 does nothing.  Errors: n < 0 or a NULL
+ * out_tokens with n > 0 (WSG_ERR_INVALID_ARG); no previous output
+ * (WSG_ERR_STATE); pos + n > max_context (WSG_ERR_OUT_OF_RANGE); stage
+ * timing enabled (WSG_OPT_TIMED_STAGE >= 0, WSG_ERR_STATE: it brackets
+ * single steps).  A failure part-way leaves the position at pos. */
+wsg_status wsg_generate(wsg_model* m, int32_t n, int32_t* out_tokens);
 
 /* Two-token step: the verify pass of greedy speculative decoding, in which
  * each weight matrix is streamed once for two input vectors ("Our Kernel
@@ -233,7 +249,8 @@ wsg_status wsg_step(wsg_model* m, int32_t in_token, int32_t* out_token, const vo
  * wsg_step calls would produce, up to floating-point rounding.
  * *out_logits (if not NULL) receives a device pointer to both rows' logits,
  * [2][vocab] in the storage dtype, valid until the next call.  Blocks until
- * the two token ids (8 bytes) are on the host.  Errors: a NULL out_tokens or
+ * the two token ids (8 bytes, stored by the argmax launch in pinned host
+ * memory) are on the host.  Errors: a NULL out_tokens or
  * n_emitted (WSG_ERR_INVALID_ARG); in_token >= vocab or draft outside
  * [0, vocab) (WSG_ERR_OUT_OF_RANGE); in_token < 0 with no previous output
  * (WSG_ERR_STATE); pos + 2 > max_context (WSG_ERR_OUT_OF_RANGE). */

@@ -139,6 +139,7 @@ def test_model_calls_reject_null(abi):
     lp = C.c_void_p()
     assert L.wsg_step2(None, -1, 0, toks, C.byref(n), C.byref(lp)) == abi.WSG_ERR_INVALID_ARG
     assert L.wsg_step(None, -1, C.byref(n), C.byref(lp)) == abi.WSG_ERR_INVALID_ARG
+    assert L.wsg_generate(None, 4, toks) == abi.WSG_ERR_INVALID_ARG
     assert L.wsg_rewind(None, 0) == abi.WSG_ERR_INVALID_ARG
     assert L.wsg_position(None) == -1
     k, v = C.c_void_p(), C.c_void_p()

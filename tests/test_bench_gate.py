@@ -57,6 +57,9 @@ class OracleStub:
     def step(self, in_token=-1):
         return self._emit(self.o.forward_rows([self._last if in_token < 0 else in_token]))
 
+    def generate(self, n):
+        return [self.step() for _ in range(n)]
+
     def _emit(self, lg):
         lg = lg.copy()
         tok = argmax_lowest(lg)

@@ -9,7 +9,7 @@ fail if no GPU is present -- there is no CPU fallback.
 from __future__ import annotations
 
 import ctypes as C
-from typing import Dict, Optional, Sequence, Tuple
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -283,6 +283,15 @@ class Model:
         self._logits_ptr = lp.value
         self._logits_rows = 1
         return tok.value
+
+    def generate(self, n: int) -> List[int]:
+        """``n`` greedy steps from the last output, enqueued back to back with one wait
+        at the end; the same tokens as ``n`` calls of ``step()``."""
+        toks = (C.c_int32 * max(int(n), 1))()
+        check(_abi.lib().wsg_generate(self.h, int(n), toks))
+        if n > 0:
+            self._logits_rows = 1
+        return list(toks[:max(int(n), 0)])
 
     def step2(self, draft: int, in_token: int = -1) -> Tuple[Tuple[int, int], int]:
         """Two-token step: ``in_token`` (default: the last output) at p, ``draft`` at p + 1.

@@ -81,6 +81,7 @@ _SIGS = {
     "wsg_prefill": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.POINTER(C.c_int32),
                               C.POINTER(C.c_void_p)]),
     "wsg_step": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_void_p)]),
+    "wsg_generate": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_int32)]),
     "wsg_step2": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                             C.POINTER(C.c_void_p)]),
     "wsg_position": (C.c_int32, [C.c_void_p]),

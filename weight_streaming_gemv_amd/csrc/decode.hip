@@ -669,6 +669,9 @@ __global__ __launch_bounds__(WPB * kWave) void k_head(const TW* __restrict__ E, 
 // the last are clamped to it instead of branched on (a repeated key cannot
 // change a maximum).
 //
+// Every token word written below is also written to the pinned host
+// mailbox (MailWord layout), which the host reads after synchronising.
+//
 // Row t's token goes to ctrl[kCtrlRowTok + t].  One row (a decode step):
 // it is also the output token, the next history entry, and the position
 // advances by one.  Two rows (a two-token step whose second input is a
@@ -680,7 +683,8 @@ __global__ __launch_bounds__(WPB * kWave) void k_head(const TW* __restrict__ E, 
 // emitted tokens, so a following step continues from the last one.
 template <int PER, int T>
 __global__ __launch_bounds__(1024) void k_argmax(const unsigned long long* __restrict__ am_part, int n,
-                                                 int32_t* __restrict__ ctrl, int32_t* __restrict__ ids) {
+                                                 int32_t* __restrict__ ctrl, int32_t* __restrict__ ids,
+                                                 int32_t* __restrict__ mail) {
   static_assert(T == 1 || T == 2, "one- and two-token steps");
   __shared__ unsigned long long red[T][1024 / kWave];
   typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
@@ -712,17 +716,25 @@ __global__ __launch_bounds__(1024) void k_argmax(const unsigned long long* __res
       tok[t] = argmax_key_index(b);
       if (b == 0) tok[t] = 0;   // no block key at all (cannot happen with vocab >= 1)
       ctrl[kCtrlRowTok + t] = tok[t];
+      mail[kMailRowTok + t] = tok[t];
     }
     const int pos = ctrl[kCtrlPos];
     if constexpr (T == 1) {
       ctrl[kCtrlOutTok] = tok[0];
+      mail[kMailOutTok] = tok[0];
       ids[pos + 1] = tok[0];
+      mail[kMailHist + pos + 1] = tok[0];
       ctrl[kCtrlPos] = pos + 1;
     } else {
       const int accepted = ids[pos + 1] == tok[0] ? 1 : 0;
       ids[pos + 1] = tok[0];
-      if (accepted) ids[pos + 2] = tok[1];
+      mail[kMailHist + pos + 1] = tok[0];
+      if (accepted) {
+        ids[pos + 2] = tok[1];
+        mail[kMailHist + pos + 2] = tok[1];
+      }
       ctrl[kCtrlOutTok] = accepted ? tok[1] : tok[0];
+      mail[kMailOutTok] = accepted ? tok[1] : tok[0];
       ctrl[kCtrlPos] = pos + 1 + accepted;
     }
   }
@@ -1870,7 +1882,7 @@ bool launch_argmax(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   auto go = [&](auto pc) {
     return with_t(sh.tokens, [&](auto tc) {
       hipLaunchKernelGGL((k_argmax<decltype(pc)::value, decltype(tc)::value>), dim3(1), dim3(1024), 0, s,
-                         (const unsigned long long*)a.am_part, n, a.ctrl, a.ids);
+                         (const unsigned long long*)a.am_part, n, a.ctrl, a.ids, a.mail);
       return true;
     });
   };

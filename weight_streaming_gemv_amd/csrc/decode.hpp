@@ -14,6 +14,15 @@ enum CtrlWord : int {
   kCtrlWords = 64
 };
 
+// Words of the pinned host mailbox the argmax launch writes besides the
+// control words, so that the host reads a step's tokens straight from host
+// memory once the stream has synchronised (no device-to-host copy launch).
+enum MailWord : int {
+  kMailOutTok = 0,       // last emitted greedy token
+  kMailRowTok = 1,       // [kMaxTokens] greedy token of each row of the last step
+  kMailHist = 4,         // [cap + 1] host copy of every history entry the argmax writes
+};
+
 // The head kernel runs at most kHeadMaxBlocks blocks (one argmax key each;
 // one row per wave for the 151936-row vocabulary would be 37984 blocks, the
 // default two rows per wave 18992); a multiple of 2048 (the argmax block
@@ -81,6 +90,7 @@ struct DecodeArgs {
                                 //   (capacity kMaxTokens * kHeadMaxBlocks)
   int32_t* ctrl;
   int32_t* ids;         // token history [cap + 1]
+  int32_t* mail;        // pinned host mailbox (device-visible address): MailWord layout
 };
 
 // Grid shapes chosen by the runtime.

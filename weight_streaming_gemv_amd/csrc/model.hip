@@ -234,7 +234,8 @@ struct wsg_model {
   std::vector<LayerPtrs> layers;
   int32_t pos = 0;
   bool has_output = false;
-  int32_t* pin = nullptr;          // pinned staging: [0] token out, [1..] ids in
+  int32_t* pin = nullptr;          // pinned staging of ids copied in: [1..]
+  int32_t* mail = nullptr;         // pinned mailbox the argmax launch writes (MailWord layout)
   bool use_graph = true;
   // a captured step graph; a graph captured while a per-layer stage was timed
   // holds event-record nodes around that stage's launches (n_events events of
@@ -567,23 +568,22 @@ wsg_status collect_timing(wsg_model* m) {
   return WSG_OK;
 }
 
+// The argmax launch writes its tokens straight into the pinned mailbox, so
+// reading a step's token is a wait for the stream and a host load.
 wsg_status read_token(wsg_model* m, int32_t* out_token) {
-  WSG_HIP_CHECK(hipMemcpyAsync(m->pin, m->args.ctrl + kCtrlOutTok, sizeof(int32_t), hipMemcpyDeviceToHost, m->stream));
   WSG_HIP_CHECK(hipStreamSynchronize(m->stream));
   const wsg_status st = collect_timing(m);
   if (st != WSG_OK) return st;
-  if (out_token) *out_token = m->pin[0];
+  if (out_token) *out_token = reinterpret_cast<volatile int32_t*>(m->mail)[kMailOutTok];
   return WSG_OK;
 }
 
-// The per-row tokens of the last step (`rows` words from kCtrlRowTok).
+// The per-row tokens of the last step (`rows` words from kMailRowTok).
 wsg_status read_row_tokens(wsg_model* m, int rows, int32_t* out) {
-  WSG_HIP_CHECK(hipMemcpyAsync(m->pin, m->args.ctrl + kCtrlRowTok, rows * sizeof(int32_t), hipMemcpyDeviceToHost,
-                               m->stream));
   WSG_HIP_CHECK(hipStreamSynchronize(m->stream));
   const wsg_status st = collect_timing(m);
   if (st != WSG_OK) return st;
-  for (int i = 0; i < rows; ++i) out[i] = m->pin[i];
+  for (int i = 0; i < rows; ++i) out[i] = reinterpret_cast<volatile int32_t*>(m->mail)[kMailRowTok + i];
   return WSG_OK;
 }
 
@@ -784,6 +784,12 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   }
   if (hipHostMalloc((void**)&m->pin, (size_t)(d.cap + 2) * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
     return fail_free(fail(WSG_ERR_HIP, "hipHostMalloc failed"));
+  void* mail_dev = nullptr;
+  if (hipHostMalloc((void**)&m->mail, (size_t)(kMailHist + d.cap + 1) * sizeof(int32_t), hipHostMallocMapped) !=
+          hipSuccess ||
+      hipHostGetDevicePointer(&mail_dev, m->mail, 0) != hipSuccess)
+    return fail_free(fail(WSG_ERR_HIP, "hipHostMalloc / hipHostGetDevicePointer (token mailbox) failed"));
+  memset(m->mail, 0, (size_t)(kMailHist + d.cap + 1) * sizeof(int32_t));
   m->ev.resize(2 * (d.L + 1));
   for (auto& e : m->ev)
     if (hipEventCreate(&e) != hipSuccess) { e = nullptr; return fail_free(fail(WSG_ERR_HIP, "hipEventCreate failed")); }
@@ -808,6 +814,7 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
   a.am_part = reinterpret_cast<unsigned long long*>(m->ws + wl.am_part);
   a.ctrl = reinterpret_cast<int32_t*>(m->ws + wl.ctrl);
   a.ids = reinterpret_cast<int32_t*>(m->ws + wl.ids);
+  a.mail = static_cast<int32_t*>(mail_dev);
   const size_t kv_layer = (size_t)2 * d.nkv * d.cap * d.D * d.es;
   for (int l = 0; l < d.L; ++l) {
     const LayerOff& lo = pl.layers[l];
@@ -932,6 +939,7 @@ void wsg_model_destroy(wsg_model* m) {
   drop_graphs(m);
   for (auto e : m->ev) if (e) (void)hipEventDestroy(e);
   if (m->pin) (void)hipHostFree(m->pin);
+  if (m->mail) (void)hipHostFree(m->mail);
   if (m->own_stream && m->stream) (void)hipStreamDestroy(m->stream);
   delete m;
 }
@@ -1031,6 +1039,32 @@ wsg_status wsg_step(wsg_model* m, int32_t in_token, int32_t* out_token, const vo
   m->pos += 1;
   m->has_output = true;
   if (out_logits) *out_logits = m->args.logits;
+  return WSG_OK;
+}
+
+wsg_status wsg_generate(wsg_model* m, int32_t n, int32_t* out_tokens) {
+  clear_error();
+  if (!m) return fail(WSG_ERR_INVALID_ARG, "model is NULL");
+  if (n < 0) return fail(WSG_ERR_INVALID_ARG, "n=%d must be >= 0", n);
+  if (n == 0) return WSG_OK;
+  if (!out_tokens) return fail(WSG_ERR_INVALID_ARG, "out_tokens is NULL");
+  if (!m->has_output) return fail(WSG_ERR_STATE, "no previous output token; prefill first");
+  if ((int64_t)m->pos + n > m->d.cap)
+    return fail(WSG_ERR_OUT_OF_RANGE, "position %d + %d steps exceeds max_context %d", m->pos, n, m->d.cap);
+  if (m->timed_stage >= 0)
+    return fail(WSG_ERR_STATE, "stage timing brackets single steps: use wsg_step while WSG_OPT_TIMED_STAGE is set");
+  // Every step reads its input token from the device history and writes
+  // the next one there (and to the mailbox), so the steps are enqueued
+  // back to back and the host waits once.
+  for (int t = 0; t < n; ++t) {
+    const wsg_status st = run_forward(m, true, m->pos + t + 1);
+    if (st != WSG_OK) return restore_pos(m, st);
+  }
+  const wsg_status st = read_token(m, nullptr);
+  if (st != WSG_OK) return restore_pos(m, st);
+  const volatile int32_t* hist = m->mail + kMailHist;
+  for (int t = 0; t < n; ++t) out_tokens[t] = hist[m->pos + 1 + t];
+  m->pos += n;
   return WSG_OK;
 }
 
