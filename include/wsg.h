@@ -350,9 +350,12 @@ wsg_status wsg_stage_time(wsg_model* m, double* total_ms, int64_t* launches, int
  * of its next one-token step: the layer body of that step (all stages of all
  * layers, as one HIP graph) and the same body without the stage's launches
  * are replayed alternately `reps` times each, every replay between two events
- * on the model stream, and the difference of the mean replay times is divided
- * by n_layers.  An event pair around a single launch would add its own
- * dispatch cost to kernels of a few microseconds; whole replays spread it.
+ * on the model stream, and the median over the repetitions of (replay with
+ * the stage - replay without it) is divided by n_layers.  An event pair
+ * around a single launch would add its own dispatch cost to kernels of a few
+ * microseconds; whole replays spread it.  For a stage of a few microseconds
+ * in a model of few layers the result is noisy (it can come out negative at
+ * small reps).
  * *bytes_per_launch receives the algorithmic bytes of one launch: its
  * weights, and for the attention stage the keys and values of the context
  * (plus the output-projection weights when it is fused with attention).  For

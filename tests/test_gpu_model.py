@@ -299,8 +299,10 @@ def test_time_stage_leaves_the_sequence_alone(mini_w, n_prompt):
     m.reset()
     toks = [m.prefill(prompt)]
     for stage in (A.WSG_STAGE_QKV, A.WSG_STAGE_ATTN, A.WSG_STAGE_GATEUP, A.WSG_STAGE_DOWN):
-        us, b = m.time_stage(stage, reps=3)
-        assert 0.5 < us < 1000 and b > 0, (stage, us, b)
+        # a difference of whole replays: a few-microsecond stage of a 2-layer model is
+        # within the replay noise, so only its magnitude is checked
+        us, b = m.time_stage(stage, reps=5)
+        assert np.isfinite(us) and abs(us) < 1000 and b > 0, (stage, us, b)
     if n_prompt < 128:
         with pytest.raises(wsg.WsgError, match="UNSUPPORTED"):   # fused into the attention launch
             m.time_stage(A.WSG_STAGE_O)

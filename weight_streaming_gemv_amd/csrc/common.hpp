@@ -36,6 +36,14 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Sum over each half-row of 8 lanes (every lane of the half-row gets it).
+__device__ __forceinline__ float row8_sum(float v) {
+  v += dpp<kDppQuadSwap1>(v);
+  v += dpp<kDppQuadSwap2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v;
+}
+
 // Sum over the wavefront; the result is wave-uniform (read from lane 63).
 __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);

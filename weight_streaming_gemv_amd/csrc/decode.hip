@@ -836,6 +836,68 @@ struct SoftState {
       m[g] = mn;
     }
   }
+  // Up to four keys at once (key u where use[u]): their scores are
+  // independent, so the dot-product reductions and exponentials overlap
+  // instead of forming one chain per key.  Same online-softmax state.
+  __device__ __forceinline__ void add4(const float (&q)[G][8], const float (&k)[4][8], const float (&v)[4][8],
+                                       const bool (&use)[4]) {
+    float d[G][4];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaf(q[g][i], k[u][i], a);
+        d[g][u] = a;
+      }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) d[g][u] = row16_sum(d[g][u]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mn = m[g];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mn = use[u] ? fmaxf(mn, d[g][u]) : mn;
+      if (mn == -INFINITY) continue;            // no key yet, none added (this lane's key-row)
+      const float alpha = exp2f(m[g] - mn);     // exp2(-inf) = 0 before the first key
+      float p[4], ls = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        p[u] = use[u] ? exp2f(d[g][u] - mn) : 0.f;
+        ls += p[u];
+      }
+      l[g] = fmaf(l[g], alpha, ls);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float a = acc[g][i] * alpha;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a = use[u] ? fmaf(p[u], v[u][i], a) : a;   // an unused value may be NaN
+        acc[g][i] = a;
+      }
+      m[g] = mn;
+    }
+  }
+  // Fold in the state of the lane `mask` lanes away (another key-row of the
+  // wave: mask 16 or 32), so that after masks 16 and 32 every key-row of
+  // the wave holds the merge of its four.
+  __device__ __forceinline__ void combine_xor(int mask) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mo = __shfl_xor(m[g], mask), lo = __shfl_xor(l[g], mask);
+      float ao[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ao[i] = __shfl_xor(acc[g][i], mask);
+      const float mn = fmaxf(m[g], mo);
+      const float a = mn == -INFINITY ? 0.f : exp2f(m[g] - mn);
+      const float b = mn == -INFINITY ? 0.f : exp2f(mo - mn);
+      l[g] = fmaf(l[g], a, lo * b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(acc[g][i], a, ao[i] * b);
+      m[g] = mn;
+    }
+  }
 };
 
 // Partial state layout: for each (row, kv head, split, g): [m, l, -, -,
@@ -917,6 +979,8 @@ struct HeadAttn {
     if constexpr (!PIPE) {
       // Short ranges (the fused launch): each further group's loads are all
       // issued, then folded in.
+      // (few keys per key-row: a key slot without a key is skipped, not
+      // computed and discarded)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (k_begin + sid + NR * u < k_stop) st.add(q, k4[u], v4[u]);
@@ -946,8 +1010,8 @@ struct HeadAttn {
             load_head8<TS, NTKV>(kh + (size_t)key * kD, sl, kn[u]);
             load_head8<TS, NTKV>(vh + (size_t)key * kD, sl, vn[u]);
           }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) st.add(q, k4[u], v4[u]);   // a whole group: base + 4*NR < k_stop
+          const bool all[4] = {true, true, true, true};   // a whole group: base + 4*NR < k_stop
+          st.add4(q, k4, v4, all);
 #pragma unroll
           for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -1014,6 +1078,51 @@ struct RowMerge {
       L = fmaf(l[r][g], w, L);
       A = fmaf(acc[r][g][d], w, A);
     }
+  }
+};
+
+// The fused launch's per-wave attention states, after each wave merged its
+// four key-rows (SoftState::combine_xor): maxima and sums per [row][wave of
+// the row][g], accumulators as float4 [hi][sl] = dims 64 hi + 4 sl .. +3.
+template <int G, int T, int WPR>
+struct WaveStates {
+  float m[T][WPR][G], l[T][WPR][G];
+  f4_t acc[T][WPR][G][2][16];
+
+  // key-row 0 of wave wi of row t writes the wave's state
+  __device__ __forceinline__ void put(const SoftState<G>& st, int t, int wi, int lane) {
+    if (lane < 16) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        acc[t][wi][g][0][lane] = f4_t{st.acc[g][0], st.acc[g][1], st.acc[g][2], st.acc[g][3]};
+        acc[t][wi][g][1][lane] = f4_t{st.acc[g][4], st.acc[g][5], st.acc[g][6], st.acc[g][7]};
+        if (lane == 0) {
+          m[t][wi][g] = st.m[g];
+          l[t][wi][g] = st.l[g];
+        }
+      }
+    }
+  }
+  // The attention output of query head g of row t, dims 64 hi + 4 sl .. +3:
+  // the waves' states merged (a wave without keys has m = -inf, weight 0).
+  __device__ __forceinline__ f4_t get4(int t, int g, int hi, int sl) const {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) mx = fmaxf(mx, m[t][w][g]);
+    float L = 0.f;
+    f4_t A = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) {
+      const float e = exp2f(m[t][w][g] - mx);
+      L = fmaf(l[t][w][g], e, L);
+      const f4_t a = acc[t][w][g][hi][sl];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) A[i] = fmaf(a[i], e, A[i]);
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[i] *= inv;
+    return A;
   }
 };
 
@@ -1120,6 +1229,46 @@ struct WoSlice {
       v[t].template load<kWeightsNT>(Wo + (size_t)row * ld + col0 + (f % LPR) * VEC);
     }
   }
+  // apply() for R = 8 with the operand in registers: lane l holds
+  // o[VEC l .. VEC l + VEC), the columns of its vector in every row (slices
+  // of one vector per lane).  The eight row sums share one transposed
+  // butterfly: across lane halves (xor 32), quarters (xor 16) and rows of
+  // 16 (mirror) each lane keeps half of its values and adds its partner's
+  // other half, so lane l ends with a partial of row l / 8 over 8 lanes,
+  // which the 8-lane sum completes.  xb8: row (lane / 8)'s residual.
+  __device__ __forceinline__ void apply_regs8(const float (&o)[VEC], int row0, int M, float xb8,
+                                              float* __restrict__ out) const {
+    static_assert(LPR == kWave && NLD == R && R == 8, "one vector per lane and row, eight rows");
+    const int lane = lane_id();
+    float d[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) a = fmaf(v[r].v[i], o[i], a);
+      d[r] = a;
+    }
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+    float e[4], f[2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float give = b5 ? d[k] : d[k + 4];
+      e[k] = (b5 ? d[k + 4] : d[k]) + __shfl_xor(give, 32);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float give = b4 ? e[k] : e[k + 2];
+      f[k] = (b4 ? e[k + 2] : e[k]) + __shfl_xor(give, 16);
+    }
+    // lanes i and 15 - i of a row of 16 differ in bit 3: the partner's
+    // other row, then the sum over the 8 lanes of this half-row (quad swaps
+    // and the half-row mirror reach all of them)
+    const float give = b3 ? f[0] : f[1];
+    float a = (b3 ? f[1] : f[0]) + dpp<kDppMirror>(give);
+    a = row8_sum(a);
+    const int m = row0 + (lane >> 3);
+    if ((lane & 7) == 0 && m < M) out[m] = a + xb8;
+  }
   // out[row0 + r] = (this slice's row r) . o + lane r's xb
   __device__ __forceinline__ void apply(const float* o, int row0, int M, float xb, float* __restrict__ out) const {
     const int lane = lane_id();
@@ -1157,14 +1306,6 @@ struct WoSlice {
     }
   }
 };
-
-// Sum over each half-row of 8 lanes (every lane of the half-row gets it).
-__device__ __forceinline__ float row8_sum(float v) {
-  v += dpp<kDppQuadSwap1>(v);
-  v += dpp<kDppQuadSwap2>(v);
-  v += dpp<kDppHalfMirror>(v);
-  return v;
-}
 
 // The int4 W_o slice: each lane holds 16 consecutive columns (two words and
 // their group's scale) of one row; LPR lanes cover a row's G*128 columns.
@@ -1259,8 +1400,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
                                                    int H, float* __restrict__ opart, int part_row) {
   constexpr int NR = 16 / T;           // key-rows per query row
   constexpr int WPR = kWavesPerBlock / T;
-  __shared__ RowMerge<G, NR> sm[T];
-  __shared__ float s_o[T][G * kD];
+  __shared__ WaveStates<G, T, WPR> sw;
   const int j = kv_head_of_block(n_kv);   // KV head
   const int lane = lane_id(), wave = wave_id();
   const int t = wave / WPR;            // this wave's query row
@@ -1278,10 +1418,18 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
   HeadAttn<TS, G, NR, (T > 1)> ha;
   ha.prefetch(qkv + (size_t)t * M, kh, vh, q_norm, k_norm, rope_cur + t * kD, j, Q, KV, cap, 0, sid, sl);
   ha.prefetch_prev(qkv, rope_cur, j, Q, KV, sl);   // (unused by row 0; no branch around loads)
-  // the residual rows (carried by the partial of KV head 0)
+  // the residual rows (carried by the partial of KV head 0): lane r holds
+  // row r, or with the register operand path below lane l holds row l / 8
+  constexpr bool kRegs = T == 1 && G == 2 && R == 8 &&
+                        (std::is_same<TW, float>::value || std::is_same<TW, bf16w>::value);   // 4 values per lane vector
   float xb[T];
 #pragma unroll
-  for (int r = 0; r < T; ++r) xb[r] = j == 0 ? rows_prefetch<TS, R>(x_res + (size_t)r * H, row0, H) : 0.f;
+  for (int r = 0; r < T; ++r) {
+    if constexpr (kRegs)
+      xb[r] = j == 0 ? Store<TS>::to_f(x_res[min(row0 + (lane >> 3), H - 1)]) : 0.f;
+    else
+      xb[r] = j == 0 ? rows_prefetch<TS, R>(x_res + (size_t)r * H, row0, H) : 0.f;
+  }
   __builtin_amdgcn_sched_barrier(0);   // attention operands before the weights
   WoSlice<TW, G, R> w;
   w.load(Wo, Q, j * G * kD, row0, H);
@@ -1289,18 +1437,33 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
   const int pos0 = ctrl[kCtrlPos];
   SoftState<G> st;
   ha.run(kh, vh, pos0 + t, 0, pos0, t > 0, true, row_block_of_block(n_kv) == 0, eps, sid, sl, st);
-
-  sm[t].put(st, sid, sl);
+  // the wave's four key-rows merged in registers, then the waves of the row
+  // through LDS (one barrier)
+  st.combine_xor(16);
+  st.combine_xor(32);
+  sw.put(st, t, wave % WPR, lane);
   __syncthreads();
-  for (int e = threadIdx.x; e < T * G * kD; e += kBlock) {
-    const int r = e / (G * kD), f = e - r * G * kD;
-    const int g = f / kD, d = f - g * kD;
-    float mx, L, A;
-    sm[r].get(g, d, mx, L, A);
-    s_o[r][f] = Store<TS>::to_f(Store<TS>::from_f(A / L));   // o rounded as stored
+  if constexpr (kRegs) {
+    // FP32 (or packed FP32) slices: lane l's W_o columns (4l .. 4l+3 of the head's 256) are
+    // dims 64 hi + 4 sl .. +3 of query head l / 32, hi = l / 16 % 2, sl = l % 16
+    const f4_t o = sw.get4(0, lane >> 5, (lane >> 4) & 1, lane & 15);
+    float o4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o4[i] = Store<TS>::to_f(Store<TS>::from_f(o[i]));   // o rounded as stored
+    w.apply_regs8(o4, row0, H, xb[0], opart + (size_t)j * H);
+  } else {
+    __shared__ float s_o[T][G * kD];
+    for (int e = threadIdx.x; e < T * G * 32; e += kBlock) {
+      const int r = e / (G * 32), f = e - r * (G * 32);
+      const int g = f >> 5, hi = (f >> 4) & 1, sl4 = f & 15;
+      const f4_t o = sw.get4(r, g, hi, sl4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s_o[r][g * kD + 64 * hi + 4 * sl4 + i] = Store<TS>::to_f(Store<TS>::from_f(o[i]));   // o rounded as stored
+    }
+    __syncthreads();
+    wo_apply<TW, G, R, T>(w, s_o, row0, H, xb, opart, part_row, j);
   }
-  __syncthreads();
-  wo_apply<TW, G, R, T>(w, s_o, row0, H, xb, opart, part_row, j);
 }
 
 // Merge of the split-K partial states of one query head of row t (one

@@ -1236,13 +1236,16 @@ wsg_status wsg_time_stage(wsg_model* m, int32_t stage, int32_t reps, double* us_
   m->skip_stage = -1;
   m->timed_stage = saved_timed;
   m->ev_used = 0;
-  // alternate the two graphs; each replay between its own pair of events
-  double t[2] = {0.0, 0.0};
+  // alternate the two graphs, each replay between its own pair of events;
+  // the median over the repetitions of (with - without) resists a stray
+  // slow replay
+  std::vector<double> diff;
   hipError_t e = hipSuccess;
   if (st == WSG_OK) {
     e = hipGraphLaunch(ex[0], s);   // warm-up
     if (e == hipSuccess) e = hipGraphLaunch(ex[1], s);
-    for (int r = 0; r < reps && e == hipSuccess; ++r)
+    for (int r = 0; r < reps && e == hipSuccess; ++r) {
+      double t[2] = {0.0, 0.0};
       for (int k = 0; k < 2 && e == hipSuccess; ++k) {
         e = hipEventRecord(m->ev[0], s);
         if (e == hipSuccess) e = hipGraphLaunch(ex[k], s);
@@ -1250,15 +1253,20 @@ wsg_status wsg_time_stage(wsg_model* m, int32_t stage, int32_t reps, double* us_
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         float ms = 0.f;
         if (e == hipSuccess) e = hipEventElapsedTime(&ms, m->ev[0], m->ev[1]);
-        t[k] += ms;
+        t[k] = ms;
       }
+      diff.push_back(t[0] - t[1]);
+    }
     if (e != hipSuccess) st = fail(WSG_ERR_HIP, "stage timing: %s", hipGetErrorString(e));
   }
   for (auto x : ex)
     if (x) (void)hipGraphExecDestroy(x);
   if (st != WSG_OK) return st;
   const int L = m->d.L;
-  *us_per_launch = (t[0] - t[1]) * 1e3 / ((double)reps * L);
+  std::sort(diff.begin(), diff.end());
+  const size_t n = diff.size();
+  const double med = n % 2 ? diff[n / 2] : 0.5 * (diff[n / 2 - 1] + diff[n / 2]);
+  *us_per_launch = med * 1e3 / L;
   int64_t bytes = 0;
   for (int l = 0; l < L; ++l) {
     if (stage == WSG_STAGE_ATTN)   // the cached keys and values it reads (+ W_o when fused)
