@@ -1400,7 +1400,6 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
                                                    int H, float* __restrict__ opart, int part_row) {
   constexpr int NR = 16 / T;           // key-rows per query row
   constexpr int WPR = kWavesPerBlock / T;
-  __shared__ WaveStates<G, T, WPR> sw;
   const int j = kv_head_of_block(n_kv);   // KV head
   const int lane = lane_id(), wave = wave_id();
   const int t = wave / WPR;            // this wave's query row
@@ -1437,13 +1436,14 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
   const int pos0 = ctrl[kCtrlPos];
   SoftState<G> st;
   ha.run(kh, vh, pos0 + t, 0, pos0, t > 0, true, row_block_of_block(n_kv) == 0, eps, sid, sl, st);
-  // the wave's four key-rows merged in registers, then the waves of the row
-  // through LDS (one barrier)
-  st.combine_xor(16);
-  st.combine_xor(32);
-  sw.put(st, t, wave % WPR, lane);
-  __syncthreads();
   if constexpr (kRegs) {
+    // the wave's four key-rows merged in registers, then the waves of the
+    // row through LDS (one barrier)
+    __shared__ WaveStates<G, T, WPR> sw;
+    st.combine_xor(16);
+    st.combine_xor(32);
+    sw.put(st, t, wave % WPR, lane);
+    __syncthreads();
     // FP32 (or packed FP32) slices: lane l's W_o columns (4l .. 4l+3 of the head's 256) are
     // dims 64 hi + 4 sl .. +3 of query head l / 32, hi = l / 16 % 2, sl = l % 16
     const f4_t o = sw.get4(0, lane >> 5, (lane >> 4) & 1, lane & 15);
@@ -1452,14 +1452,19 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, T
     for (int i = 0; i < 4; ++i) o4[i] = Store<TS>::to_f(Store<TS>::from_f(o[i]));   // o rounded as stored
     w.apply_regs8(o4, row0, H, xb[0], opart + (size_t)j * H);
   } else {
+    // the other W_o formats and two-token steps: every key-row's state
+    // through LDS, one output dim per thread (measured faster here than the
+    // register merge followed by a second pass for the LDS operand)
+    __shared__ RowMerge<G, NR> sm[T];
     __shared__ float s_o[T][G * kD];
-    for (int e = threadIdx.x; e < T * G * 32; e += kBlock) {
-      const int r = e / (G * 32), f = e - r * (G * 32);
-      const int g = f >> 5, hi = (f >> 4) & 1, sl4 = f & 15;
-      const f4_t o = sw.get4(r, g, hi, sl4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s_o[r][g * kD + 64 * hi + 4 * sl4 + i] = Store<TS>::to_f(Store<TS>::from_f(o[i]));   // o rounded as stored
+    sm[t].put(st, sid, sl);
+    __syncthreads();
+    for (int e = threadIdx.x; e < T * G * kD; e += kBlock) {
+      const int r = e / (G * kD), f = e - r * G * kD;
+      const int g = f / kD, d = f - g * kD;
+      float mx, L, A;
+      sm[r].get(g, d, mx, L, A);
+      s_o[r][f] = Store<TS>::to_f(Store<TS>::from_f(A / L));   // o rounded as stored
     }
     __syncthreads();
     wo_apply<TW, G, R, T>(w, s_o, row0, H, xb, opart, part_row, j);
