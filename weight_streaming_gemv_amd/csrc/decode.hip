@@ -102,13 +102,19 @@ struct Act {
   }
   // In-register RMSNorm with gain: a = a * (mean(a^2) + eps)^-1/2 * g.
   __device__ __forceinline__ void rms_norm(const TS* gain, float eps) {
+    Act<TS, K, VEC> g;
+    g.load(gain);
+    rms_norm(g, eps);
+  }
+  // The same with the gain already loaded (its load issued ahead of the
+  // weight rows, so that the norm does not wait for them: vector loads
+  // return in issue order).
+  __device__ __forceinline__ void rms_norm(const Act& g, float eps) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < K / kWave; ++i) ss = fmaf(a[i], a[i], ss);
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)K + eps);
-    Act<TS, K, VEC> g;
-    g.load(gain);
 #pragma unroll
     for (int i = 0; i < K / kWave; ++i) a[i] = a[i] * inv * g.a[i];
   }
@@ -287,6 +293,13 @@ struct Operand<TS, q4w, K> {
   }
 };
 
+// Whether the QKV and gate/up launches issue their norm gain ahead of the
+// weight rows (so that the norm need not wait for the rows: vector loads
+// return in issue order).  Measured: 16-bit storage +2-3 % decode tokens/s;
+// FP32 -0.9 % (its weight rows take the registers), so there the gain
+// follows the rows.
+template <typename TS> constexpr bool kGainAhead = !std::is_same<TS, float>::value;
+
 // Rows [n, ...) of a matrix of width K (the up half of the gate/up matrix).
 template <typename TW, int K>
 __device__ __forceinline__ const TW* rows_from(const TW* W, size_t n) {
@@ -339,6 +352,8 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const 
       else x[t].load(x_res + t * H);
     }
   }
+  typename Op::act gain;
+  if constexpr (kGainAhead<TS>) gain.load(in_norm);
   __builtin_amdgcn_sched_barrier(0);
   w.load(W, g * R, M);   // rows clamped into W: no branch around the loads
   __builtin_amdgcn_sched_barrier(0);
@@ -374,7 +389,8 @@ __global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const 
   typename Op::dot_t xd[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    x[t].rms_norm(in_norm, eps);
+    if constexpr (kGainAhead<TS>) x[t].rms_norm(gain, eps);
+    else x[t].rms_norm(in_norm, eps);   // the gain loaded here, after the weight rows
     xd[t] = Op::prep(x[t]);
   }
   const int lane = lane_id();
@@ -513,7 +529,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, c
   const TW* Wu = rows_from<TW, H>(Wgu, I);
   const int tid = threadIdx.x;
   int g = wave_row_groups_begin();
-  typename Op::act x[T];
+  typename Op::act x[T], gain;
   WRows<TW, H, R> wg, wu;
   if constexpr (NP > 0) {
     // Vector loads return in issue order, so the partials (this thread's
@@ -532,7 +548,8 @@ __global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, c
           const int i = min(4 * (c * kBlock + tid), H - 4);
           pv[t][p][c] = *reinterpret_cast<const f4_t*>(opart + (size_t)(t * NP + p) * H + i);
         }
-    __builtin_amdgcn_sched_barrier(0);   // partials before weights
+    if constexpr (kGainAhead<TS>) gain.load(post_norm);
+    __builtin_amdgcn_sched_barrier(0);   // partials (and gain) before weights
     wg.load(Wgu, g * R, I);   // rows clamped into W: no branch around the loads
     wu.load(Wu, g * R, I);
     __builtin_amdgcn_sched_barrier(0);   // all loads issued in this order first
@@ -563,6 +580,7 @@ __global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, c
   } else {
 #pragma unroll
     for (int t = 0; t < T; ++t) x[t].load(x_res + t * H);
+    if constexpr (kGainAhead<TS>) gain.load(post_norm);
     __builtin_amdgcn_sched_barrier(0);
     wg.load(Wgu, g * R, I);   // rows clamped into W: no branch around the loads
     wu.load(Wu, g * R, I);
@@ -571,7 +589,8 @@ __global__ __launch_bounds__(kBlock) void k_gateup(const TW* __restrict__ Wgu, c
   typename Op::dot_t xd[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    x[t].rms_norm(post_norm, eps);
+    if constexpr (kGainAhead<TS>) x[t].rms_norm(gain, eps);
+    else x[t].rms_norm(post_norm, eps);   // the gain loaded here, after the weight rows
     xd[t] = Op::prep(x[t]);
   }
   const int lane = lane_id();
