@@ -330,13 +330,16 @@ __device__ __forceinline__ float rows_prefetch(const TS* __restrict__ base, int 
 // of the down projection (FP32, the first carrying that layer's residual) at
 // dpart[(t*NPD + s)*H]: every wave sums them in slice order and rounds as
 // stored, and block 0 writes the residual x_res for the attention launch.
+// Arguments are ordered so that the ones the first loads need fill the 14
+// dwords preloaded into SGPRs at wave launch (the rest arrive by a scalar
+// load that the first loads then need not wait for).
 template <typename TS, typename TW, int H, int R, int T, int NPD>
-__global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, const TS* __restrict__ in_norm,
-                                                TS* __restrict__ x_res, const void* __restrict__ embed,
-                                                const int32_t* __restrict__ ids, const int32_t* __restrict__ ctrl,
-                                                const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
-                                                float* __restrict__ rope_cur, int first_layer, int vocab, float eps,
-                                                TS* __restrict__ out, int M, const float* __restrict__ dpart) {
+__global__ __launch_bounds__(kBlock) void k_qkv(const TW* __restrict__ W, TS* __restrict__ x_res,
+                                                const TS* __restrict__ in_norm, const float* __restrict__ dpart,
+                                                int M, int first_layer, TS* __restrict__ out, float eps, int vocab,
+                                                const void* __restrict__ embed, const int32_t* __restrict__ ids,
+                                                const int32_t* __restrict__ ctrl, const float* __restrict__ rope_cos,
+                                                const float* __restrict__ rope_sin, float* __restrict__ rope_cur) {
   using Op = Operand<TS, TW, H>;
   const int ngroups = ceil_div(M, R);
   int g = wave_row_groups_begin();
@@ -1759,9 +1762,9 @@ bool qkv_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool 
           auto go = [&](auto nc) {
             hipLaunchKernelGGL((k_qkv<TS, pointee_t<decltype(W)>, decltype(kc)::value, decltype(rc)::value,
                                       decltype(tc)::value, decltype(nc)::value>),
-                               dim3(grid), dim3(kBlock), 0, s, W, (const TS*)L.in_norm, (TS*)a.x, a.embed,
-                               a.ids, a.ctrl, a.rope_cos, a.rope_sin, a.rope_cur, first ? 1 : 0, a.vocab, a.eps,
-                               (TS*)a.qkv, M, (const float*)a.dpart);
+                               dim3(grid), dim3(kBlock), 0, s, W, (TS*)a.x, (const TS*)L.in_norm,
+                               (const float*)a.dpart, M, first ? 1 : 0, (TS*)a.qkv, a.eps, a.vocab, a.embed, a.ids,
+                               a.ctrl, a.rope_cos, a.rope_sin, a.rope_cur);
             return true;
           };
           switch (first ? 0 : npd) {
