@@ -1413,13 +1413,24 @@ __device__ __forceinline__ void wo_apply(const WoSlice<TW, G, R>& w, const float
   }
 }
 
+// Arguments: the first 14 dwords (preloaded into SGPRs at wave launch) hold
+// every address the loads and the position read need, so no scalar load
+// precedes them.  dims = n_kv | hidden << 8.  Derived from neighbours (the
+// runtime checks these layouts before the launch): the residual x and the
+// projections qkv from rope_cur (row_block_* offsets), the V cache block of
+// a layer from its K block (n_kv * cap * 128 elements on) and the K-norm gain
+// from the Q-norm gain (128 elements on).
 template <typename TS, typename TW, int G, int R, int T>
-__global__ __launch_bounds__(kBlock) void k_attn_o(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
-                                                   TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
-                                                   const TS* __restrict__ k_norm, const float* __restrict__ rope_cur,
-                                                   const int32_t* __restrict__ ctrl, int n_q, int n_kv, int cap,
-                                                   float eps, const TW* __restrict__ Wo, const TS* __restrict__ x_res,
-                                                   int H, float* __restrict__ opart, int part_row) {
+__global__ __launch_bounds__(kBlock) void k_attn_o(const float* __restrict__ rope_cur, TS* __restrict__ k_cache,
+                                                   const TS* __restrict__ q_norm, const int32_t* __restrict__ ctrl,
+                                                   const TW* __restrict__ Wo, int dims, int cap, float eps,
+                                                   int part_row, float* __restrict__ opart) {
+  const int n_kv = dims & 0xFF, H = dims >> 8, n_q = G * n_kv;
+  const char* rb = reinterpret_cast<const char*>(rope_cur);
+  const TS* x_res = reinterpret_cast<const TS*>(rb + row_block_x_offset());
+  const TS* qkv = reinterpret_cast<const TS*>(rb + row_block_qkv_offset(H, sizeof(TS)));
+  TS* v_cache = k_cache + (size_t)n_kv * cap * kD;
+  const TS* k_norm = q_norm + kD;
   constexpr int NR = 16 / T;           // key-rows per query row
   constexpr int WPR = kWavesPerBlock / T;
   const int j = kv_head_of_block(n_kv);   // KV head
@@ -1947,6 +1958,15 @@ bool attn_merge_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
 template <typename TS>
 bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
+  // the layouts the launch derives its other addresses from
+  const char* rb = reinterpret_cast<const char*>(a.rope_cur);
+  if (a.n_kv > 0xFF || a.hidden >= (1 << 23) ||
+      static_cast<const char*>(a.x) != rb + row_block_x_offset() ||
+      static_cast<const char*>(a.qkv) != rb + row_block_qkv_offset(a.hidden, sizeof(TS)) ||
+      static_cast<const char*>(L.v_cache) !=
+          static_cast<const char*>(L.k_cache) + (size_t)a.n_kv * a.cap * kD * sizeof(TS) ||
+      static_cast<const char*>(L.k_norm) != static_cast<const char*>(L.q_norm) + kD * sizeof(TS))
+    return false;
   return with_w<TS>(a.wfmt, L.wo, L.wo_p, [&](auto Wo) {
     using TW = pointee_t<decltype(Wo)>;
     // row t's partials start at opart[t * slots * H], as the gate/up
@@ -1962,9 +1982,8 @@ bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hi
         const dim3 grid(ceil_div(a.hidden, kWavesPerBlock * R) * a.n_kv);   // KV head = block % n_kv
         return with_t(sh.tokens, [&](auto tc) {
           hipLaunchKernelGGL((k_attn_o<TS, TW, GG, R, decltype(tc)::value>), grid, dim3(kBlock), 0, s,
-                             (const TS*)a.qkv, (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm,
-                             (const TS*)L.k_norm, a.rope_cur, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, Wo,
-                             (const TS*)a.x, a.hidden, a.opart, part_row);
+                             a.rope_cur, (TS*)L.k_cache, (const TS*)L.q_norm, a.ctrl, Wo,
+                             a.n_kv | (a.hidden << 8), a.cap, a.eps, part_row, a.opart);
           return true;
         });
       }

@@ -41,6 +41,17 @@ constexpr int kMaxTokens = 2;
 // Largest number of K slices of the split down projection.
 constexpr int kMaxDownSplit = 4;
 
+// The per-row buffers rope_cur [kMaxTokens][128] FP32, x and x2
+// [kMaxTokens][hidden] and qkv follow each other in the workspace, each
+// starting on a 256-byte boundary; the fused attention launch finds x and
+// qkv from rope_cur with these offsets (the runtime checks its layout
+// against them before that launch).
+__host__ __device__ constexpr size_t row_buffer_bytes(size_t bytes) { return (bytes + 255) & ~size_t(255); }
+__host__ __device__ constexpr size_t row_block_x_offset() { return row_buffer_bytes(kMaxTokens * 128 * 4); }
+__host__ __device__ constexpr size_t row_block_qkv_offset(int hidden, int elem_bytes) {
+  return row_block_x_offset() + 2 * row_buffer_bytes((size_t)kMaxTokens * hidden * elem_bytes);
+}
+
 struct LayerPtrs {
   const void* wqkv;     // [(Q + 2 KV)][H]
   const void* wo;       // [H][Q]
