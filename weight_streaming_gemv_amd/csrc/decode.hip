@@ -2099,6 +2099,7 @@ bool launch_argmax(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   if (per <= 2) return go(IC<2>{});
   if (per <= 4) return go(IC<4>{});
   if (per <= 8) return go(IC<8>{});
+  if (per <= 10) return go(IC<10>{});   // the 18992-block FP32 head: 9496 pairs
   static_assert(kHeadMaxBlocks / 2048 == 20, "pairs per thread at the largest head grid");
   return go(IC<20>{});
 }
