@@ -1616,10 +1616,21 @@ __global__ __launch_bounds__(kBlock) void k_merge_o(const float* __restrict__ pa
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b)
       av[k][b] = *reinterpret_cast<const f4_t*>(ep[k] + (size_t)min(wave + kWavesPerBlock * b, splits - 1) * sstride);
-  // 3. the residual rows and the W_o rows, then the position
+  // 3. the residual rows and the W_o rows, then the position.  With FP32
+  // (or packed) slices of one query row, lane l's W_o columns are exactly
+  // o_j's float4 e = l, so each wave finishes o_j in registers and lane l
+  // holds row l / 8's residual for the eight-row butterfly; else lane r holds
+  // row r.
+  constexpr bool kRegs = T == 1 && G == 2 && R == 8 &&
+                        (std::is_same<TW, float>::value || std::is_same<TW, bf16w>::value);
   float xb[T];
 #pragma unroll
-  for (int r = 0; r < T; ++r) xb[r] = j == 0 ? rows_prefetch<TS, R>(x_res + (size_t)r * H, row0, H) : 0.f;
+  for (int r = 0; r < T; ++r) {
+    if constexpr (kRegs)
+      xb[r] = j == 0 ? Store<TS>::to_f(x_res[min(row0 + (lane >> 3), H - 1)]) : 0.f;
+    else
+      xb[r] = j == 0 ? rows_prefetch<TS, R>(x_res + (size_t)r * H, row0, H) : 0.f;
+  }
   __builtin_amdgcn_sched_barrier(0);
   WoSlice<TW, G, R> w;
   w.load(Wo, Q, j * G * kD, row0, H);
@@ -1680,14 +1691,23 @@ __global__ __launch_bounds__(kBlock) void k_merge_o(const float* __restrict__ pa
 #pragma unroll
   for (int k = 0; k < PL; ++k) s_acc[wave][lane + kWave * k] = acc[k];
   __syncthreads();
-  for (int e = tid; e < NE; e += kBlock) {
-    const int tg = e / (kD / 4), d4 = e - tg * (kD / 4), t = tg / G, g = tg - t * G;
-    const f4_t a = ((s_acc[0][e] + s_acc[1][e]) + (s_acc[2][e] + s_acc[3][e])) * s_inv[tg];
+  if constexpr (kRegs) {
+    static_assert(NE == kWave, "one float4 of o_j per lane");
+    const f4_t a = ((s_acc[0][lane] + s_acc[1][lane]) + (s_acc[2][lane] + s_acc[3][lane])) * s_inv[lane / (kD / 4)];
+    float o4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_o[t][g * kD + 4 * d4 + i] = Store<TS>::to_f(Store<TS>::from_f(a[i]));
+    for (int i = 0; i < 4; ++i) o4[i] = Store<TS>::to_f(Store<TS>::from_f(a[i]));
+    w.apply_regs8(o4, row0, H, xb[0], opart + (size_t)j * H);
+  } else {
+    for (int e = tid; e < NE; e += kBlock) {
+      const int tg = e / (kD / 4), d4 = e - tg * (kD / 4), t = tg / G, g = tg - t * G;
+      const f4_t a = ((s_acc[0][e] + s_acc[1][e]) + (s_acc[2][e] + s_acc[3][e])) * s_inv[tg];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[t][g * kD + 4 * d4 + i] = Store<TS>::to_f(Store<TS>::from_f(a[i]));
+    }
+    __syncthreads();
+    wo_apply<TW, G, R, T>(w, s_o, row0, H, xb, opart, part_row, j);
   }
-  __syncthreads();
-  wo_apply<TW, G, R, T>(w, s_o, row0, H, xb, opart, part_row, j);
 }
 
 // --------------------------------------------------------------- dispatch
