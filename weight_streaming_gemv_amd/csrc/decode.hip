@@ -1153,13 +1153,19 @@ struct WaveStates {
 // within one split writes o itself; otherwise every split writes its
 // partial state (for the merge, or the merging output projection).
 template <typename TS, int G, int T>
-__global__ __launch_bounds__(kBlock) void k_attn(const TS* __restrict__ qkv, TS* __restrict__ k_cache,
-                                                 TS* __restrict__ v_cache, const TS* __restrict__ q_norm,
-                                                 const TS* __restrict__ k_norm, const float* __restrict__ rope_cur,
-                                                 const int32_t* __restrict__ ctrl, int n_q, int n_kv, int cap,
-                                                 float eps, int chunk, float* __restrict__ part,
-                                                 TS* __restrict__ o, int direct) {
+// Arguments as the fused launch's: the first 14 dwords (preloaded into
+// SGPRs) hold every address the loads and the position read need (dims =
+// n_kv | hidden << 8; qkv from rope_cur, V after K, K-norm after Q-norm).
+__global__ __launch_bounds__(kBlock) void k_attn(const float* __restrict__ rope_cur, TS* __restrict__ k_cache,
+                                                 const TS* __restrict__ q_norm, const int32_t* __restrict__ ctrl,
+                                                 int dims, int cap, int chunk, float eps, int direct,
+                                                 float* __restrict__ part, TS* __restrict__ o) {
   constexpr bool PREV = T > 1;
+  const int n_kv = dims & 0xFF, n_q = G * n_kv;
+  const TS* qkv = reinterpret_cast<const TS*>(reinterpret_cast<const char*>(rope_cur) +
+                                              row_block_qkv_offset(dims >> 8, sizeof(TS)));
+  TS* v_cache = k_cache + (size_t)n_kv * cap * kD;
+  const TS* k_norm = q_norm + kD;
   __shared__ RowMerge<G, 16> sm;
   const int j = blockIdx.y;            // KV head
   const int split = blockIdx.x;
@@ -1938,16 +1944,28 @@ bool head_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
   });
 }
 
+// The layouts the attention launches derive their other addresses from
+// (their arguments hold rope_cur, the K block and the Q-norm gain only).
+template <typename TS>
+bool attn_layout_ok(const DecodeArgs& a, const LayerPtrs& L) {
+  const char* rb = reinterpret_cast<const char*>(a.rope_cur);
+  return a.n_kv <= 0xFF && a.hidden < (1 << 23) && static_cast<const char*>(a.x) == rb + row_block_x_offset() &&
+         static_cast<const char*>(a.qkv) == rb + row_block_qkv_offset(a.hidden, sizeof(TS)) &&
+         static_cast<const char*>(L.v_cache) ==
+             static_cast<const char*>(L.k_cache) + (size_t)a.n_kv * a.cap * kD * sizeof(TS) &&
+         static_cast<const char*>(L.k_norm) == static_cast<const char*>(L.q_norm) + kD * sizeof(TS);
+}
+
 template <typename TS>
 bool attn_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, bool direct, hipStream_t s) {
+  if (!attn_layout_ok<TS>(a, L)) return false;
   const int G = a.n_q / a.n_kv;
   const dim3 grid(sh.attn_splits, a.n_kv, sh.tokens);
   auto go = [&](auto gc) {
     return with_t(sh.tokens, [&](auto tc) {
       hipLaunchKernelGGL((k_attn<TS, decltype(gc)::value, decltype(tc)::value>), grid, dim3(kBlock), 0, s,
-                         (const TS*)a.qkv, (TS*)L.k_cache, (TS*)L.v_cache, (const TS*)L.q_norm, (const TS*)L.k_norm,
-                         a.rope_cur, a.ctrl, a.n_q, a.n_kv, a.cap, a.eps, sh.attn_chunk, a.attn_part, (TS*)a.o,
-                         direct ? 1 : 0);
+                         a.rope_cur, (TS*)L.k_cache, (const TS*)L.q_norm, a.ctrl, a.n_kv | (a.hidden << 8), a.cap,
+                         sh.attn_chunk, a.eps, direct ? 1 : 0, a.attn_part, (TS*)a.o);
       return true;
     });
   };
@@ -1978,15 +1996,7 @@ bool attn_merge_t(const DecodeArgs& a, const DecodeShape& sh, hipStream_t s) {
 template <typename TS>
 bool attn_o_t(const DecodeArgs& a, const DecodeShape& sh, const LayerPtrs& L, hipStream_t s) {
   const int G = a.n_q / a.n_kv;
-  // the layouts the launch derives its other addresses from
-  const char* rb = reinterpret_cast<const char*>(a.rope_cur);
-  if (a.n_kv > 0xFF || a.hidden >= (1 << 23) ||
-      static_cast<const char*>(a.x) != rb + row_block_x_offset() ||
-      static_cast<const char*>(a.qkv) != rb + row_block_qkv_offset(a.hidden, sizeof(TS)) ||
-      static_cast<const char*>(L.v_cache) !=
-          static_cast<const char*>(L.k_cache) + (size_t)a.n_kv * a.cap * kD * sizeof(TS) ||
-      static_cast<const char*>(L.k_norm) != static_cast<const char*>(L.q_norm) + kD * sizeof(TS))
-    return false;
+  if (!attn_layout_ok<TS>(a, L)) return false;
   return with_w<TS>(a.wfmt, L.wo, L.wo_p, [&](auto Wo) {
     using TW = pointee_t<decltype(Wo)>;
     // row t's partials start at opart[t * slots * H], as the gate/up
