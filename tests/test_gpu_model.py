@@ -196,11 +196,11 @@ WIDE_KV = ModelShape(n_layers=1, hidden=256, intermediate=512, n_q_heads=8, n_kv
 
 def _split_keys(n_keys, n_kv, cap):
     """Keys per split-K attention block the runtime picks for a context of n_keys (its
-    documented rule: about 192 blocks over all KV heads, at least 64 keys and enough that
+    documented rule: about 256 blocks over all KV heads, at least 64 keys and enough that
     the capacity needs at most 128 splits, rounded up a ladder of four sizes per doubling),
     so each case below states which block size it reaches."""
     least = max(64, (-(-cap // 128) + 15) // 16 * 16)
-    need = max(least, -(-n_keys // max(1, 192 // n_kv)))
+    need = max(least, -(-n_keys // max(1, 256 // n_kv)))
     c, e = 64, 0
     while c < need:
         base = 64 << (e // 4)
@@ -246,14 +246,15 @@ def _split_lockstep(sh, w, cap, chunk, n_prompt, label):
     m.close()
 
 
-@pytest.mark.parametrize("n_prompt,keys", [(1600, 80), (3300, 160), (4200, 192), (4700, 224), (5100, 224)])
+@pytest.mark.parametrize("n_prompt,keys", [(2100, 80), (3300, 112), (3600, 128), (4700, 160), (5100, 160)])
 def test_long_context_split_sizes(n_prompt, keys):
-    """Contexts whose split-K attention blocks take 80 keys (1600: each key-row
-    folds a second group of keys, the last one partial), 160 keys (3300: three
-    groups per key-row), 192 keys (4200: three whole groups) and 224 keys (4700
-    and 5100, the sizes of the long-document generation past 4608 keys: four
-    groups per key-row, the last one partial); greedy steps in lockstep, then
-    two-token steps (an accepted and a rejected draft) at the same context."""
+    """Contexts whose split-K attention blocks take 80 keys (2100: each key-row
+    folds a whole group of four keys, then a partial one), 112 keys (3300: a
+    whole group and three keys), 128 keys (3600: two whole groups) and 160 keys
+    (4700 and 5100, the size of the long-document generation past 4096 keys: two
+    whole groups and a partial one; 5100 keys take 32 splits per head, 256
+    blocks); greedy steps in lockstep, then two-token steps (an accepted and a
+    rejected draft) at the same context."""
     cap = 5120
     assert _split_keys(n_prompt + 1, WIDE_KV.n_kv_heads, cap) == keys
     assert _split_keys(n_prompt + 7, WIDE_KV.n_kv_heads, cap) == keys
@@ -332,13 +333,13 @@ def test_describe_reports_launch_shapes(mini_w):
     m.close()
 
 
-def test_long_context_224_key_splits_qwen3_2layer():
+def test_long_context_160_key_splits_qwen3_2layer():
     """The real head geometry (16 query heads on 8 KV heads, two query heads per split
-    block) at 4.7k keys, where the attention blocks take 224 keys, through a chunk-1024
-    prefill (five chunks, the last one partial)."""
+    block) at 4.7k keys, where the attention blocks take 160 keys (30 splits per head),
+    through a chunk-1024 prefill (five chunks, the last one partial)."""
     sh = QWEN3_0_6B.with_layers(2)
     cap, n_prompt = 4736, 4700
-    assert _split_keys(n_prompt + 1, sh.n_kv_heads, cap) == 224
+    assert _split_keys(n_prompt + 1, sh.n_kv_heads, cap) == 160
     _split_lockstep(sh, model_weights(sh, seed=0), cap, 1024, n_prompt, "qwen3-2L n=4700")
 
 

@@ -420,9 +420,11 @@ int attn_mode(const wsg_model* m, int n_keys, int tokens) {
 // state for the merge launch to read), so fewer, longer blocks win once
 // there are enough of them to keep the memory system busy; a sweep of
 // fixed sizes on the 8-KV-head model at 1.1k / 2.1k / 4.2k keys was best
-// at 64 / 96 / 192 keys, i.e. 20-24 splits per head.  Targets of 384 or 512
-// blocks (two per CU fit) measured 4 % slower per token at 2k-4k keys.
-constexpr int kAttnTargetBlocks = 192;
+// at 64 / 96 / 192 keys, i.e. 20-24 splits per head.  Since the merge launch
+// got cheaper, a target of one block per CU (256: 27-32 splits per head)
+// measured 0.6 % faster per token than 192 at 4.1-4.4k keys; 160 was slower,
+// and 320 (more blocks than CUs) 5 % slower, as were 384 or 512 before.
+constexpr int kAttnTargetBlocks = 256;
 
 // The size is taken from a ladder with four steps per doubling (64, 80, 96,
 // 112, 128, 160, ...: 16 * {4,5,6,7} * 2^e), so a long generation passes
