@@ -60,6 +60,41 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// Cross-lane pairs from the gfx950 lane-swap instructions (VALU only, no
+// LDS round trip).  Measured lane layout: swap32(x, y) gives a lane l of the
+// lower half of the wave (x(l), x(l + 32)) and a lane of the upper half
+// (y(l - 32), y(l)); swap16(x, y) likewise for lanes l and l ^ 16, with x
+// paired in the even rows of 16 lanes and y in the odd ones.  Each lane so
+// holds one value and its xor partner's, the lower lane's first; with x = y
+// that is the plain xor-32 (xor-16) exchange, and with x != y the
+// transposed step of a butterfly that halves the values a lane carries.
+// Both results are read through one 64-bit value: subscripting the
+// builtin's two-element result reads element 0 twice with this compiler.
+struct LanePair { float lo, hi; };
+__device__ __forceinline__ LanePair swap32(float x, float y) {
+  const unsigned long long w = __builtin_bit_cast(
+      unsigned long long, __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                           __builtin_bit_cast(unsigned, y), false, false));
+  return {__builtin_bit_cast(float, (unsigned)w), __builtin_bit_cast(float, (unsigned)(w >> 32))};
+}
+__device__ __forceinline__ LanePair swap16(float x, float y) {
+  const unsigned long long w = __builtin_bit_cast(
+      unsigned long long, __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                           __builtin_bit_cast(unsigned, y), false, false));
+  return {__builtin_bit_cast(float, (unsigned)w), __builtin_bit_cast(float, (unsigned)(w >> 32))};
+}
+__device__ __forceinline__ LanePair lanes_xor32(float x) { return swap32(x, x); }
+__device__ __forceinline__ LanePair lanes_xor16(float x) { return swap16(x, x); }
+
+// Maximum over the wavefront, in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  LanePair p = lanes_xor16(v);
+  v = fmaxf(p.lo, p.hi);
+  p = lanes_xor32(v);
+  return fmaxf(p.lo, p.hi);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
@@ -180,13 +215,34 @@ __device__ __forceinline__ int argmax_key_index(unsigned long long k) {
   return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
 }
 
+// Maximum key over the wavefront, in every lane: within rows of 16 by DPP
+// (quad swaps, half-row and row mirrors), then across rows by the lane swaps.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long k) {
+  const unsigned lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+  const unsigned hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+template <bool X32>
+__device__ __forceinline__ unsigned long long max_xor_u64(unsigned long long k) {
+  const float lo = __uint_as_float((uint32_t)k), hi = __uint_as_float((uint32_t)(k >> 32));
+  const LanePair a = X32 ? lanes_xor32(lo) : lanes_xor16(lo);
+  const LanePair b = X32 ? lanes_xor32(hi) : lanes_xor16(hi);
+  const unsigned long long k0 = ((unsigned long long)__float_as_uint(b.lo) << 32) | __float_as_uint(a.lo);
+  const unsigned long long k1 = ((unsigned long long)__float_as_uint(b.hi) << 32) | __float_as_uint(a.hi);
+  return k1 > k0 ? k1 : k0;
+}
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const unsigned long long o = __shfl_xor(k, off);
-    k = o > k ? o : k;
-  }
-  return k;
+  unsigned long long o = dpp_u64<kDppQuadSwap1>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<kDppQuadSwap2>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<kDppHalfMirror>(k);
+  k = o > k ? o : k;
+  o = dpp_u64<kDppMirror>(k);
+  k = o > k ? o : k;
+  k = max_xor_u64<false>(k);
+  return max_xor_u64<true>(k);
 }
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));

@@ -901,22 +901,27 @@ struct SoftState {
       m[g] = mn;
     }
   }
-  // Fold in the state of the lane `mask` lanes away (another key-row of the
-  // wave: mask 16 or 32), so that after masks 16 and 32 every key-row of
-  // the wave holds the merge of its four.
-  __device__ __forceinline__ void combine_xor(int mask) {
+  // Merge with the state of the lane MASK lanes away (another key-row of
+  // the wave: MASK 16 or 32), so that after masks 16 and 32 every key-row of
+  // the wave holds the merge of its four.  Both lanes of a pair compute the
+  // merge from the same (lower lane, upper lane) operands, so they hold the
+  // same bits.
+  template <int MASK>
+  __device__ __forceinline__ void combine_xor() {
+    static_assert(MASK == 16 || MASK == 32, "key-rows of a wave");
+    auto pair = [](float v) { return MASK == 32 ? lanes_xor32(v) : lanes_xor16(v); };
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], mask), lo = __shfl_xor(l[g], mask);
-      float ao[8];
+      const LanePair pm = pair(m[g]), pl = pair(l[g]);
+      const float mn = fmaxf(pm.lo, pm.hi);
+      const float a = mn == -INFINITY ? 0.f : exp2f(pm.lo - mn);
+      const float b = mn == -INFINITY ? 0.f : exp2f(pm.hi - mn);
+      l[g] = fmaf(pl.lo, a, pl.hi * b);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ao[i] = __shfl_xor(acc[g][i], mask);
-      const float mn = fmaxf(m[g], mo);
-      const float a = mn == -INFINITY ? 0.f : exp2f(m[g] - mn);
-      const float b = mn == -INFINITY ? 0.f : exp2f(mo - mn);
-      l[g] = fmaf(l[g], a, lo * b);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(acc[g][i], a, ao[i] * b);
+      for (int i = 0; i < 8; ++i) {
+        const LanePair pa = pair(acc[g][i]);
+        acc[g][i] = fmaf(pa.lo, a, pa.hi * b);
+      }
       m[g] = mn;
     }
   }
@@ -1276,17 +1281,17 @@ struct WoSlice {
       for (int i = 0; i < VEC; ++i) a = fmaf(v[r].v[i], o[i], a);
       d[r] = a;
     }
-    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+    const bool b3 = lane & 8;
     float e[4], f[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float give = b5 ? d[k] : d[k + 4];
-      e[k] = (b5 ? d[k + 4] : d[k]) + __shfl_xor(give, 32);
+    for (int k = 0; k < 4; ++k) {   // lower half keeps rows k, upper half rows k + 4
+      const LanePair p = swap32(d[k], d[k + 4]);
+      e[k] = p.lo + p.hi;
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const float give = b4 ? e[k] : e[k + 2];
-      f[k] = (b4 ? e[k + 2] : e[k]) + __shfl_xor(give, 16);
+    for (int k = 0; k < 2; ++k) {   // even rows of 16 keep e[k], odd rows e[k + 2]
+      const LanePair p = swap16(e[k], e[k + 2]);
+      f[k] = p.lo + p.hi;
     }
     // lanes i and 15 - i of a row of 16 differ in bit 3: the partner's
     // other row, then the sum over the 8 lanes of this half-row (quad swaps
@@ -1325,7 +1330,10 @@ struct WoSlice {
 #pragma unroll
       for (int t = 0; t < NLD; ++t) {
         float a = row16_sum(d[t]);
-        if constexpr (LPR == 32) a += __shfl_xor(a, 16);
+        if constexpr (LPR == 32) {
+          const LanePair p = lanes_xor16(a);
+          a = p.lo + p.hi;
+        }
         const int f = t * kWave + lane;
         const int m = row0 + f / LPR;
         const float b = __shfl(xb, f / LPR);
@@ -1384,7 +1392,10 @@ struct WoSlice<q4w, G, R> {
       float v = __half2float(__ushort_as_half(s[t])) * in;
       if constexpr (LPR == 8) v = row8_sum(v);
       else v = row16_sum(v);
-      if constexpr (LPR == 32) v += __shfl_xor(v, 16);
+      if constexpr (LPR == 32) {
+        const LanePair p = lanes_xor16(v);
+        v = p.lo + p.hi;
+      }
       const int m = row0 + f / LPR;
       const float xv = __shfl(xb, f / LPR);
       if (f % LPR == 0 && m < M) out[m] = v + xv;
@@ -1479,8 +1490,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const float* __restrict__ rop
     // the wave's four key-rows merged in registers, then the waves of the
     // row through LDS (one barrier)
     __shared__ WaveStates<G, T, WPR> sw;
-    st.combine_xor(16);
-    st.combine_xor(32);
+    st.template combine_xor<16>();
+    st.template combine_xor<32>();
     sw.put(st, t, wave % WPR, lane);
     __syncthreads();
     // FP32 (or packed FP32) slices: lane l's W_o columns (4l .. 4l+3 of the head's 256) are
@@ -1535,9 +1546,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_merge(const float* __restrict__
   // split statistics: thread sp < n_splits (n_splits <= kMaxSplits)
   const float m_s = tid < n_splits ? hp[tid * sstride] : -INFINITY;
   const float l_s = tid < n_splits ? hp[tid * sstride + 1] : 0.f;
-  float mx = m_s;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float mx = wave_max(m_s);
   if (lane_id() == 0) s_red[wave_id()] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
@@ -1658,8 +1667,7 @@ __global__ __launch_bounds__(kBlock) void k_merge_o(const float* __restrict__ pa
   for (int tg = wave; tg < TG; tg += kWavesPerBlock) {
     float mx = -INFINITY;
     for (int sp = lane; sp < kMaxSplits; sp += kWave) mx = fmaxf(mx, s_w[tg][sp]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = wave_max(mx);
     float L = 0.f;
     for (int sp = lane; sp < kMaxSplits; sp += kWave) {
       const float wgt = s_w[tg][sp] == -INFINITY ? 0.f : exp2f(s_w[tg][sp] - mx);
