@@ -480,10 +480,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __re
                                                                const float* __restrict__ v_cache, int n, int n_q,
                                                                int n_kv, int p0, int cap, float* __restrict__ O) {
   constexpr int BR = kAQV / G;       // rows per tile
-  // two stages each of the K and V tiles of a tile pair
-  __shared__ float Ks[2][2][kAKT * kKsRow];
-  __shared__ float Vt[2][2][kD * kVtRow];
-  static_assert(4 * kWave * kStateRow <= 2 * kD * kVtRow, "merge records fit in one stage's V tiles");
+  __shared__ float Ks[2][kAKT * kKsRow];
+  __shared__ float Vt[2][kD * kVtRow];
+  static_assert(4 * kWave * kStateRow <= 2 * kD * kVtRow, "merge records fit in the V tiles");
   const int j = blockIdx.y;
   const int n_tiles = (n + BR - 1) / BR;
   const int tile_a = blockIdx.x, tile_b = n_tiles - 1 - blockIdx.x;   // tile_a <= tile_b
@@ -537,94 +536,68 @@ __global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __re
   // values replaced by zeros, since a masked key still enters the PV product
   // with weight 0 (and 0 * Inf is NaN).
   f4_t kr[4], vr[4];
-  // K of pair kp into kr, V of pair vp into vr (pair p = keys [64p, 64p + 64))
-#define WSG_ATTN_LOAD(KP, VP)                                                                     \
+#define WSG_ATTN_LOAD(K0)                                                                         \
   _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
-    const int idx = tid + kAttnThreads * i, f = idx & 1023, t = idx >> 10;                        \
-    const int k1 = 2 * kAKT * (KP) + kAKT * t + (f >> 5), k2 = 2 * kAKT * (VP) + kAKT * t + (f & 31); \
+    const int idx = tid + kAttnThreads * i, f = idx & 1023;                                       \
+    const int kt = (K0) + kAKT * (idx >> 10);                                                     \
+    const int k1 = kt + (f >> 5), k2 = kt + (f & 31);                                             \
     const int kk = min(k1, cap - 1), kv = min(k2, cap - 1);                                       \
     kr[i] = *reinterpret_cast<const f4_t*>(kh + (size_t)kk * kD + 4 * (f & 31));                  \
     vr[i] = *reinterpret_cast<const f4_t*>(vh + (size_t)kv * kD + 4 * (f >> 5));                  \
     if (k1 >= n_keys) kr[i] = f4_t{0.f, 0.f, 0.f, 0.f};                                           \
     if (k2 >= n_keys) vr[i] = f4_t{0.f, 0.f, 0.f, 0.f};                                           \
   }
-#define WSG_ATTN_STAGE_K(S)                                                                       \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
-    const int idx = tid + kAttnThreads * i, f = idx & 1023, t = idx >> 10;                        \
-    *reinterpret_cast<f4_t*>(&Ks[S][t][(f >> 5) * kKsRow + 4 * (f & 31)]) = kr[i];               \
-  }
-#define WSG_ATTN_STAGE_V(S)                                                                       \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
-    const int idx = tid + kAttnThreads * i, f = idx & 1023, t = idx >> 10;                        \
-    _Pragma("unroll") for (int e = 0; e < 4; ++e) Vt[S][t][(4 * (f >> 5) + e) * kVtRow + (f & 31)] = vr[i][e]; \
-  }
-  // this wave's K operands of its tile of a pair staged in K stage S: rows
-  // 16h + li, dims 32lq + 4t .. + 3
-  f4_t ka[2][8];
-#define WSG_ATTN_READ_K(S)                                                                        \
-  _Pragma("unroll") for (int h = 0; h < 2; ++h)                                                   \
-    _Pragma("unroll") for (int t = 0; t < 8; ++t)                                                 \
-      ka[h][t] = *reinterpret_cast<const f4_t*>(&Ks[S][grp][(16 * h + li) * kKsRow + 32 * lq + 4 * t]);
-  // Software pipeline over tile pairs, two LDS stages each for K and V: K
-  // is staged two pairs ahead and V one, so a wave reads the K operands of
-  // its next tile while its value product still runs, and the V operands
-  // while its scores are computed, and no operand read waits at the start
-  // of a product.  In iteration p: scores of pair p (K operands already in
-  // registers), V operands of pair p; K of pair p + 2 and V of pair p + 1
-  // written from registers into the stages pair p's K (read in the previous
-  // iteration) and pair p - 1's V (read before the previous barrier) left,
-  // and the loads for K of p + 3 and V of p + 2 issued; softmax and value
-  // product of pair p; K operands of pair p + 1; one barrier.  Loads past
-  // the last pair reload an in-bounds one, unused, to keep them free of
-  // branches.
-  const int n_pairs = (n_keys + 2 * kAKT - 1) / (2 * kAKT);
-  WSG_ATTN_LOAD(0, 0)
-  WSG_ATTN_STAGE_K(0)
-  WSG_ATTN_STAGE_V(0)
-  WSG_ATTN_LOAD(min(1, n_pairs - 1), min(1, n_pairs - 1))
-  WSG_ATTN_STAGE_K(1)
-  WSG_ATTN_LOAD(min(2, n_pairs - 1), min(1, n_pairs - 1))
-  __syncthreads();
-  if (kAKT * grp < my_keys) {   // wave-uniform
-    WSG_ATTN_READ_K(0)
-  }
-  __syncthreads();   // K stage 0 read by every wave before pair 2 overwrites it
-  for (int pi = 0; pi < n_pairs; ++pi) {
-    const int stg = pi & 1;
-    const int kt = 2 * kAKT * pi + kAKT * grp;   // this group's key tile
-    const bool on = kt < my_keys;                // wave-uniform
-    f4v_t sacc[2];
-    f4_t va[2][8];
-    if (on) {
-      // S^T for the two 16-key halves
+  WSG_ATTN_LOAD(0)
+  for (int k0 = 0; k0 < n_keys; k0 += 2 * kAKT) {
+    __syncthreads();   // previous tile pair consumed
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        sacc[h] = f4v_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + kAttnThreads * i, f = idx & 1023, t = idx >> 10;
+      *reinterpret_cast<f4_t*>(&Ks[t][(f >> 5) * kKsRow + 4 * (f & 31)]) = kr[i];
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+      for (int e = 0; e < 4; ++e) Vt[t][(4 * (f >> 5) + e) * kVtRow + (f & 31)] = vr[i][e];
+    }
+    __syncthreads();
+    // next pair in flight during the MFMAs (the last iteration reloads an
+    // in-bounds pair, unused, to keep the loop free of branches)
+    WSG_ATTN_LOAD(min(k0 + 2 * kAKT, n_keys - 1))
+#undef WSG_ATTN_LOAD
+    const int kt = k0 + kAKT * grp;   // this group's key tile
+    if (kt < my_keys) {               // wave-uniform
+      const float* ks = Ks[grp];
+      const float* vt = Vt[grp];
+      // S^T for the two 16-key halves.  Each product reads all of its A
+      // operands from LDS first (16 reads in flight), then runs its 64
+      // MFMAs, so the waits for the reads overlap the matrix pipe instead of
+      // preceding every four MFMAs.
+      f4v_t sacc[2];
+      {
+        f4_t ka[2][8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sacc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[h][t][i], qf[4 * t + i], sacc[h], 0, 0, 0);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            ka[h][t] = *reinterpret_cast<const f4_t*>(&ks[(16 * h + li) * kKsRow + 32 * lq + 4 * t]);
+        __builtin_amdgcn_sched_barrier(0);   // (the scheduler would pair each read with its MFMAs)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          sacc[h] = f4v_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sacc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[h][t][i], qf[4 * t + i], sacc[h], 0, 0, 0);
+        }
       }
       // the V^T operands of O^T += V^T P^T, read while the score MFMAs run
-      // (after them: the K operands' registers are free by then)
-      __builtin_amdgcn_sched_barrier(0);
-      const float* vt = Vt[stg][grp];
+      // and the softmax is computed
+      f4_t va[2][8];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
           va[h][mt] = *reinterpret_cast<const f4_t*>(&vt[(16 * mt + li) * kVtRow + 16 * h + 4 * lq]);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (pi + 2 < n_pairs) {   // uniform
-      WSG_ATTN_STAGE_K(stg)
-    }
-    if (pi + 1 < n_pairs) {   // uniform
-      WSG_ATTN_STAGE_V(stg ^ 1)
-    }
-    WSG_ATTN_LOAD(min(pi + 3, n_pairs - 1), min(pi + 2, n_pairs - 1))
-    if (on) {
       // causal mask (only tiles that reach past the wave's first row, or
       // hold rows past the chunk), tile max per query vector
       if (!wave_rows_ok || kt + kAKT - 1 > wave_first_pos) {   // wave-uniform
@@ -682,20 +655,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_prefill_attn(const float* __re
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2)
             oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[h][mt][s2], sacc[h][s2], oacc[mt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 2 * kAKT < my_keys) {   // wave-uniform: this wave's next tile
-      WSG_ATTN_READ_K(stg ^ 1)
-    }
-    __syncthreads();
   }
-#undef WSG_ATTN_LOAD
-#undef WSG_ATTN_STAGE_K
-#undef WSG_ATTN_STAGE_V
-#undef WSG_ATTN_READ_K
-  // merge: group 1's states -> group 0 (records in the V tile memory; every
-  // wave's reads of it ended before the loop's last barrier)
-  float* rec = &Vt[0][0][0] + ((ts * 2 + wh) * kWave + lane) * kStateRow;
+  // merge: group 1's states -> group 0 (records in the V tile memory)
+  __syncthreads();
+  float* rec = &Vt[0][0] + ((ts * 2 + wh) * kWave + lane) * kStateRow;
   if (grp == 1) {
     rec[0] = m;
     rec[1] = l;
