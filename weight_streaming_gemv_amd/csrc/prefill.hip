@@ -67,7 +67,7 @@ typedef float f4v_t __attribute__((ext_vector_type(4)));
 constexpr int kBK = 32;                   // K granularity of the shapes accepted (and of the small-M kernel)
 constexpr int kLdsPad = 4;                // floats of padding per LDS row
 
-template <int BM, int BN, int BK, bool ACC, int WV, bool SWI = false>
+template <int BM, int BN, int BK, bool ACC, int WV, bool SWI = false, bool EARLY = false>
 __global__ __launch_bounds__(64 * WV) void k_gemm_nt(const float* __restrict__ A, const float* __restrict__ B,
                                                      float* __restrict__ C, int M, int N, int K, int kspan,
                                                      size_t c_split) {
@@ -161,8 +161,13 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_nt(const float* __restrict__ A
     }
     __syncthreads();
     // next tile in flight during the MFMAs (the last iteration reloads the
-    // final tile, in bounds and unused, to keep the loop free of branches)
+    // final tile, in bounds and unused, to keep the loop free of branches).
+    // The scheduler sinks these loads to the end of the loop body; with at
+    // most one workgroup per CU (EARLY) nothing else covers their latency
+    // there, so they are pinned here, ahead of the MFMAs (with two or more
+    // workgroups per CU the sunk placement measured faster)
     WSG_GEMM_LOAD(min(k0 + BK, kspan - BK))
+    if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NU; ++u) WSG_GEMM_FRAGS(u)
 #pragma unroll
@@ -757,6 +762,8 @@ bool launch_skinny(const float* A, const float* B, float* C, int M, int N, int K
   }
 }
 
+constexpr int kCUs = 256;   // compute units: workgroups of one round at one per CU
+
 // Tiled launch of BM x BN tiles with K split S ways (S slices c_split
 // apart): 64-wide K tiles when the split's K range allows, else 32-wide.
 // With swi (one slice, no accumulation): the SwiGLU epilogue, C being
@@ -771,14 +778,26 @@ bool launch_tiled(const float* A, const float* B, float* C, int M, int N, int K,
     // 128-row tiles: 8 waves, two per SIMD (one computes while the other
     // reads its operands from LDS); 64 x 64 tiles: 4 waves
     constexpr int WV = BM == 128 ? 8 : 4;
+    // one round of workgroups (at most one per CU): next-tile loads pinned early
+    const bool early = (int64_t)grid.x * grid.y * grid.z <= kCUs;
     if (swi) {
       if constexpr (BM / 2 <= BK + kLdsPad) {
         if (S != 1 || acc) return false;
+        if (early) {
+          hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, false, WV, true, true>), grid, dim3(64 * WV), 0, s, A, B, C, M,
+                             N, K, kspan, c_split);
+          return true;
+        }
         hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, false, WV, true>), grid, dim3(64 * WV), 0, s, A, B, C, M, N, K,
                            kspan, c_split);
         return true;
       }
       return false;
+    }
+    if (early && !acc) {
+      hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, false, WV, false, true>), grid, dim3(64 * WV), 0, s, A, B, C, M, N,
+                         K, kspan, c_split);
+      return true;
     }
     if (acc)
       hipLaunchKernelGGL((k_gemm_nt<BM, BN, BK, true, WV>), grid, dim3(64 * WV), 0, s, A, B, C, M, N, K, kspan, c_split);
