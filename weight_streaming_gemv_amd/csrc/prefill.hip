@@ -475,7 +475,7 @@ __global__ __launch_bounds__(256) void k_rows_qkv(float* __restrict__ QKV, int n
 constexpr int kAQV = 32;           // query vectors per tile (two tiles per block)
 constexpr int kAKT = 32;           // keys per tile
 constexpr int kKsRow = kD + 4;     // K tile row (floats): conflict-free 16-byte reads
-constexpr int kVtRow = kAKT + 4;   // V^T tile row
+constexpr int kVtRow = kAKT + 8;   // V^T tile row (+4 measured twice the LDS bank-conflict cycles)
 constexpr int kAttnThreads = 512;
 constexpr int kStateRow = 34;      // merge record per lane: m, l, O^T[32]
 
