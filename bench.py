@@ -963,6 +963,37 @@ def stage_pass(wsg, model, head, reps=20):
     return res
 
 
+def launch_floor(torch, launches, reps=20):
+    """Cost per node of a chain of ``launches`` dependent one-element kernels (torch's
+    in-place add) replayed as one HIP graph, median over ``reps`` replays between HIP
+    events: the dispatch floor that each of the decode step's launches pays besides its own
+    kernel time (completion, the cache write-back and invalidation between dependent
+    launches, the next dispatch).  An upper bound: the add itself runs well under 1 us."""
+    t = torch.zeros(1, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            t.add_(1.0)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            t.add_(1.0)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per_node = []
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        per_node.append(e0.elapsed_time(e1) * 1e3 / launches)
+    del g
+    return statistics.median(per_node)
+
+
 MFMA_FP32_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
 
 
@@ -1213,6 +1244,14 @@ def _main(argv=None):
                               "region, at the context of the short prompt's first step"}
     else:
         roofline = timed_stage
+    # the dispatch floor of the step's launches: 4 per layer, the head and the argmax
+    n_launch = 4 * shape.n_layers + 2
+    floor_us = launch_floor(torch, n_launch)
+    floor = {"us_per_dependent_launch": round(floor_us, 3), "launches_per_token": n_launch,
+             "us_per_token": round(floor_us * n_launch, 1),
+             "share_of_token_time": round(floor_us * n_launch * value / 1e6, 4) if value else None,
+             "note": "a chain of dependent one-element kernels replayed as one HIP graph (median per node of "
+                     "20 replays): the cost each launch pays besides its kernel time, an upper bound"}
     out = {
         "metric": "decode tokens/s + cold-cache effective weight GB/s (% of HBM peak), 1 MI355X",
         "value": None if args.no_oracle else round(value, 2),
@@ -1240,6 +1279,7 @@ def _main(argv=None):
         "step_loop": step_loop,
         "roofline": roofline,
         "stage_rooflines": stages,
+        "launch_floor": floor,
         ("roofline_" + args.timed_stage): timed_stage,
         "cpu_baseline": cpu,
         "validation": ({"status": "passed", "max_abs_logit_err": max(e[0] for e in errs.values()),
