@@ -178,6 +178,25 @@ struct PackedVec4 {
 };
 template <> struct WVec<bf16w> { using type = PackedVec4; };
 
+// Four FP16 weights per 8-byte load, widened to FP32: the W_o slice vector
+// of FP16 models, so that a lane covers four columns like the FP32 and
+// packed slices (the layout the attention's register merge leaves in a lane).
+struct Half4Vec {
+  static constexpr int N = 4;
+  float v[4];
+  template <bool NT>
+  __device__ __forceinline__ void load(const __half* p) {
+    typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+    u2_t t;
+    if constexpr (NT) t = __builtin_nontemporal_load(reinterpret_cast<const u2_t*>(p));
+    else t = *reinterpret_cast<const u2_t*>(p);
+    v[0] = __half2float(__ushort_as_half((unsigned short)(t.x & 0xFFFFu)));
+    v[1] = __half2float(__ushort_as_half((unsigned short)(t.x >> 16)));
+    v[2] = __half2float(__ushort_as_half((unsigned short)(t.y & 0xFFFFu)));
+    v[3] = __half2float(__ushort_as_half((unsigned short)(t.y >> 16)));
+  }
+};
+
 // int4 group-64 weights (tag type for the decode kernels): each matrix row
 // holds K/8 32-bit words (nibble j of word w is k = 8w + j, low nibble
 // first, a two's-complement value in [-8, 7]) followed by the row's K/64

@@ -1242,9 +1242,15 @@ __device__ __forceinline__ int row_block_of_block(int n_kv) { return (int)blockI
 // The gate/up launch sums the partials in a fixed order.  Blocks b = 0
 // write the current tokens' keys and values into the cache.  With T = 2
 // query rows, waves 0-1 serve row 0 and waves 2-3 row 1 (8 key-rows each).
+// Vector type of the W_o slices: the weight format's, except FP16 slices,
+// which load four values per lane (Half4Vec) so that every format with a
+// 256-wide KV-head slice has four columns per lane.
+template <typename TW> struct WoVec { using type = typename WVec<TW>::type; };
+template <> struct WoVec<__half> { using type = Half4Vec; };
+
 template <typename TW, int G, int R>
 struct WoSlice {
-  using Vec = typename WVec<TW>::type;
+  using Vec = typename WoVec<TW>::type;
   static constexpr int VEC = Vec::N;
   static constexpr int LPR = G * kD / VEC;          // 16-byte vectors per row slice
   static constexpr int NLD = R * LPR / kWave;       // vectors per lane
@@ -1470,7 +1476,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const float* __restrict__ rop
   // the residual rows (carried by the partial of KV head 0): lane r holds
   // row r, or with the register operand path below lane l holds row l / 8
   constexpr bool kRegs = T == 1 && G == 2 && R == 8 &&
-                        (std::is_same<TW, float>::value || std::is_same<TW, bf16w>::value);   // 4 values per lane vector
+                        (std::is_same<TW, float>::value || std::is_same<TW, bf16w>::value ||
+                         std::is_same<TW, __half>::value);   // 4 values per lane vector
   float xb[T];
 #pragma unroll
   for (int r = 0; r < T; ++r) {
@@ -1494,7 +1501,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const float* __restrict__ rop
     st.template combine_xor<32>();
     sw.put(st, t, wave % WPR, lane);
     __syncthreads();
-    // FP32 (or packed FP32) slices: lane l's W_o columns (4l .. 4l+3 of the head's 256) are
+    // FP32, packed FP32 and FP16 slices: lane l's W_o columns (4l .. 4l+3 of the head's 256) are
     // dims 64 hi + 4 sl .. +3 of query head l / 32, hi = l / 16 % 2, sl = l % 16
     const f4_t o = sw.get4(0, lane >> 5, (lane >> 4) & 1, lane & 15);
     float o4[4];
@@ -1637,7 +1644,8 @@ __global__ __launch_bounds__(kBlock) void k_merge_o(const float* __restrict__ pa
   // holds row l / 8's residual for the eight-row butterfly; else lane r holds
   // row r.
   constexpr bool kRegs = T == 1 && G == 2 && R == 8 &&
-                        (std::is_same<TW, float>::value || std::is_same<TW, bf16w>::value);
+                        (std::is_same<TW, float>::value || std::is_same<TW, bf16w>::value ||
+                         std::is_same<TW, __half>::value);
   float xb[T];
 #pragma unroll
   for (int r = 0; r < T; ++r) {
