@@ -1475,14 +1475,14 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const float* __restrict__ rop
   ha.prefetch_prev(qkv, rope_cur, j, Q, KV, sl);   // (unused by row 0; no branch around loads)
   // the residual rows (carried by the partial of KV head 0): lane r holds
   // row r, or with the register operand path below lane l holds row l / 8
-  constexpr bool kRegs = T == 1 && G == 2 && R == 8 &&
+  constexpr bool kRegs = G == 2 && R == 8 &&
                         (std::is_same<TW, float>::value || std::is_same<TW, bf16w>::value ||
                          std::is_same<TW, __half>::value);   // 4 values per lane vector
   float xb[T];
 #pragma unroll
   for (int r = 0; r < T; ++r) {
     if constexpr (kRegs)
-      xb[r] = j == 0 ? Store<TS>::to_f(x_res[min(row0 + (lane >> 3), H - 1)]) : 0.f;
+      xb[r] = j == 0 ? Store<TS>::to_f(x_res[(size_t)r * H + min(row0 + (lane >> 3), H - 1)]) : 0.f;
     else
       xb[r] = j == 0 ? rows_prefetch<TS, R>(x_res + (size_t)r * H, row0, H) : 0.f;
   }
@@ -1502,12 +1502,16 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const float* __restrict__ rop
     sw.put(st, t, wave % WPR, lane);
     __syncthreads();
     // FP32, packed FP32 and FP16 slices: lane l's W_o columns (4l .. 4l+3 of the head's 256) are
-    // dims 64 hi + 4 sl .. +3 of query head l / 32, hi = l / 16 % 2, sl = l % 16
-    const f4_t o = sw.get4(0, lane >> 5, (lane >> 4) & 1, lane & 15);
-    float o4[4];
+    // dims 64 hi + 4 sl .. +3 of query head l / 32, hi = l / 16 % 2, sl = l % 16; every wave
+    // applies its rows to each query row (two-token steps: the weights loaded once)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o4[i] = Store<TS>::to_f(Store<TS>::from_f(o[i]));   // o rounded as stored
-    w.apply_regs8(o4, row0, H, xb[0], opart + (size_t)j * H);
+    for (int r = 0; r < T; ++r) {
+      const f4_t o = sw.get4(r, lane >> 5, (lane >> 4) & 1, lane & 15);
+      float o4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = Store<TS>::to_f(Store<TS>::from_f(o[i]));   // o rounded as stored
+      w.apply_regs8(o4, row0, H, xb[r], opart + (size_t)r * part_row + (size_t)j * H);
+    }
   } else {
     // the other W_o formats and two-token steps: every key-row's state
     // through LDS, one output dim per thread (measured faster here than the
