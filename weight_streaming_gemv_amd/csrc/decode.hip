@@ -1513,9 +1513,10 @@ __global__ __launch_bounds__(kBlock) void k_attn_o(const float* __restrict__ rop
       w.apply_regs8(o4, row0, H, xb[r], opart + (size_t)r * part_row + (size_t)j * H);
     }
   } else {
-    // the other W_o formats and two-token steps: every key-row's state
-    // through LDS, one output dim per thread (measured faster here than the
-    // register merge followed by a second pass for the LDS operand)
+    // int4 slices and the other shapes: every key-row's state through LDS,
+    // one output dim per thread (measured faster for int4 than the register
+    // merge with four columns per lane or with a second pass for the LDS
+    // operand)
     __shared__ RowMerge<G, NR> sm[T];
     __shared__ float s_o[T][G * kD];
     sm[t].put(st, sid, sl);
