@@ -863,14 +863,15 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 0;
   }
-  if (cus > 0 && d.es == 4 && !d.pack && !d.q4) {
-    // FP32 weights: QKV on 3 blocks per CU and gate/up on 2, looping over
-    // their row groups, instead of one-shot grids (4 and 3 per CU at the
-    // 0.6B shape): fewer waves repeat the norm prologue (the residual, the
-    // attention partials and the gain, read from L2 by every wave), and the
-    // second row group's weights are loaded while the first is reduced
-    // (28-layer sweep of 640..896 / 448..768 blocks, interleaved rounds:
-    // 1415 against 1384 tokens/s; neighbouring sizes were slower)
+  if (cus > 0 && !d.q4) {
+    // FP32, packed and FP16 weights: QKV on 3 blocks per CU and gate/up on
+    // 2, looping over their row groups, instead of one-shot grids (4 and 3
+    // per CU at the 0.6B shape): fewer waves repeat the norm prologue (the
+    // residual, the attention partials and the gain, read from L2 by every
+    // wave), and the second row group's weights are loaded while the first
+    // is reduced (28-layer sweeps, interleaved rounds: FP32 1415 against
+    // 1384 tokens/s over 640..896 / 448..768 blocks, neighbouring sizes
+    // slower; FP16 1918 against 1877)
     sh.grid_qkv = 3 * cus;
     sh.grid_gu = 2 * cus;
   }
