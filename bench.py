@@ -53,7 +53,7 @@ STAGE_KERNEL = {"qkv": "k_qkv", "attn": "k_attn_o", "o": "k_gemv_residual", "gat
 # runs, each scaled by what the same counter reads for a plain copy of known size
 # (FETCH x 2.0, WRITE x 1.0); valid only for the decode kernel sources they were
 # measured on (their hash below), else reported as null.
-DECODE_TRAFFIC = {"sha256_16": "562957e27dd4da36",
+DECODE_TRAFFIC = {"sha256_16": "247485dc258d7d4a",
                   "bytes": {"k_gateup": 25_539_434, "k_attn_o": 9_014_883, "k_qkv": 16_915_703,
                             "k_gemv_residual": 12_763_573, "k_head": 623_631_400}}
 

@@ -905,6 +905,12 @@ wsg_status wsg_model_create(const wsg_config* cfg, const void* d_packed, size_t 
     // grids 2048..one-shot: 49 against 62 us on the one-shot grid)
     for (DecodeShape* s : {&m->shape, &m->shape2}) s->grid_head = 8192;
   }
+  if (d.pack) {
+    // packed rows are 2 KiB like FP16 rows: the one-token head loops its two
+    // rows per wave over 4096 workgroups (28-layer sweep of 4096 / 8192 /
+    // 12288 / one-shot: 1875 / 1865 / 1847 / 1816 tokens/s)
+    m->shape.grid_head = 4096;
+  }
   if (d.q4) {
     // int4 rows are short (544 bytes at width 1024): the head loops over
     // four rows per wave on 2048 blocks, so each wave's activation and norm
