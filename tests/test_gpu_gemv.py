@@ -97,9 +97,12 @@ def test_q4_ragged(M, K, T):
 def test_q4_fixed_k_ragged_and_looping(M, K, T):
     """The fixed-K int4 kernels (16-wave workgroups with a partial last round of
     activation staging at K = 14336, 4-wave ones at K = 4096) on a ragged row
-    count: one-shot grids, and a grid-stride loop over three workgroups."""
+    count: one-shot grids, and grid-stride loops over three workgroups (at
+    K = 4096 one row per wave issues each next row before reducing the
+    current one; waves past the last row read it and discard it)."""
     _run_q4(M, K, T, (1, 4), seed=23)
     _run_q4(M, K, T, (2,), seed=23, grid=3, flags=1)
+    _run_q4(M, K, T, (1,), seed=23, grid=3)
 
 
 def test_gemv_determinism():

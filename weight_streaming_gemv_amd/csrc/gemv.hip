@@ -221,6 +221,31 @@ __global__ __launch_bounds__(64 * WV) void k_gemv_q4(const uint32_t* __restrict_
     const int t = i / W8, gi = i - t * W8;
     hx[it] = *reinterpret_cast<const uint4*>(X + (size_t)t * K + gi * 8);
   }
+  const int lane = lane_id();
+  const int ngroups = (M + R - 1) / R;
+  // One row per wave in 4-wave workgroups (two 16-byte chunks per lane at
+  // most): the wave's first row is issued before the staging barrier, right
+  // after the activation loads, so its latency overlaps the staging instead
+  // of following it, and each next row is issued before the current one is
+  // reduced.  Larger groups keep chunk-by-chunk loads: holding them costs
+  // registers (occupancy) that the measured sweep valued more.
+  constexpr bool kPre = R == 1 && WV == kWavesPerBlock && NV <= 2;
+  constexpr int PN = kPre ? NV : 1;
+  uint4 wq[PN];
+  __half ws[PN];
+  auto load_row = [&](int row) {
+#pragma unroll
+    for (int c = 0; c < PN; ++c) {
+      wq[c] = load_u4<NT>(Wq + (size_t)row * W8 + c * 256 + lane * 4);
+      ws[c] = S[(size_t)row * G + c * 32 + (lane >> 1)];
+    }
+  };
+  int g = blockIdx.x * WV + wave_id();
+  // (a wave with no row reads the last row and discards it)
+  if constexpr (kPre) {
+    load_row(min(g, M - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int it = 0; it < kStage; ++it) {
     const int i = threadIdx.x + it * kThreads;
@@ -231,10 +256,51 @@ __global__ __launch_bounds__(64 * WV) void k_gemv_q4(const uint32_t* __restrict_
   }
   __syncthreads();
 
-  const int lane = lane_id();
   const h2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const int ngroups = (M + R - 1) / R;
-  for (int g = blockIdx.x * WV + wave_id(); g < ngroups; g += gridDim.x * WV) {
+  if constexpr (kPre) {
+    for (; g < M; g += gridDim.x * WV) {
+      float acc[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[t] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        const uint32_t ww[4] = {wq[c].x, wq[c].y, wq[c].z, wq[c].w};
+        float inner[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) inner[t] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t v = ww[i] ^ 0x88888888u;
+          const h2_t p0 = as_h2((v & 0x000F000Fu) | 0x64006400u) - bias;
+          const h2_t p1 = as_h2(((v >> 4) & 0x000F000Fu) | 0x64006400u) - bias;
+          const h2_t p2 = as_h2(((v >> 8) & 0x000F000Fu) | 0x64006400u) - bias;
+          const h2_t p3 = as_h2(((v >> 12) & 0x000F000Fu) | 0x64006400u) - bias;
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const uint4 xv = xs[t][c * 256 + i * 64 + lane];
+            float a = inner[t];
+            a = dot2(p0, as_h2(xv.x), a);
+            a = dot2(p1, as_h2(xv.y), a);
+            a = dot2(p2, as_h2(xv.z), a);
+            a = dot2(p3, as_h2(xv.w), a);
+            inner[t] = a;
+          }
+        }
+        const float sc = __half2float(ws[c]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[t] = fmaf(sc, inner[t], acc[t]);
+      }
+      const int next = g + gridDim.x * WV;
+      if (next < M) load_row(next);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float s = wave_sum(acc[t]);
+        if (lane == 0) Y[(size_t)t * M + g] = s;
+      }
+    }
+    return;
+  }
+  for (; g < ngroups; g += gridDim.x * WV) {
     const int row0 = g * R;
     float acc[R][T];
 #pragma unroll
