@@ -282,9 +282,13 @@ def gemv_sweep(rounds=15, kind="full"):
             Y = torch.empty((2, M), device="cuda", dtype=torch.float32)
 
             def make(c, T, R, G, W=W, X=X, Y=Y):
+                if R == "1s":   # each row over two waves of a workgroup
+                    return lambda: wsg.gemv(W[c], X[:T], rows_per_wave=1, Y=Y, stream=s, grid_blocks=G,
+                                            flags=NT | wsg.WSG_GEMV_SPLIT2)
                 return lambda: wsg.gemv(W[c], X[:T], rows_per_wave=R, Y=Y, stream=s, grid_blocks=G, flags=NT)
             log(f"sweep {dt_name} {M}x{K}: {n} copies")
-            r = run(f"{dt_name}", bytes_per, n, make, (1, 2, 4, 8), (1, 2), GRIDS if M > 100000 else (0,))
+            Rs = (1, 2, 4, 8) + (("1s",) if dt_name == "f32" and K in (1024, 2048, 3072) else ())
+            r = run(f"{dt_name}", bytes_per, n, make, Rs, (1, 2), GRIDS if M > 100000 else (0,))
             # warm: one matrix, reused n times
             r["warm_T1"] = run("warm", bytes_per, n, lambda c, T, R, G: make(0, T, R, G), (1,), (1,))["T1_R1_G0"]
             r["ceiling"] = run("ceiling", bytes_per, n, lambda c, T, R, G: ceiling_read(W[c]), (1,), (1,))["T1_R1_G0"]
@@ -420,7 +424,9 @@ def sweep_summary(sw):
             cands = [(v["us"], k) for k, v in r.items() if k.startswith(f"T{T}_")]
             if cands:
                 us, k = min(cands)
-                best[f"{key}_T{T}"] = {"R": int(k.split("_R")[1].split("_")[0]), "grid": int(k.split("_G")[1]), "us": us,
+                rk = k.split("_R")[1].split("_")[0]   # "1s": one row per two waves (WSG_GEMV_SPLIT2)
+                best[f"{key}_T{T}"] = {"R": int(rk.rstrip("s")), "waves_per_row": 2 if rk.endswith("s") else 1,
+                                       "grid": int(k.split("_G")[1]), "us": us,
                                        "gbps": round(r["bytes"] / us / 1e3, 1),
                                        "frac": round(r["bytes"] / us / 1e3 / HBM_PEAK_GBPS, 4)}
                 if "ceiling" in r:

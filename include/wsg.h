@@ -382,9 +382,17 @@ wsg_status wsg_gemv(int32_t w_dtype, int32_t M, int32_t K, int32_t T, int32_t ro
                     const void* d_W, const void* d_X, float* d_Y, void* hip_stream);
 
 /* wsg_gemv with an explicit launch shape: grid_blocks of 256 threads
- * (0 = one row group per wave, no grid-stride loop) and flags
- * (WSG_GEMV_NONTEMPORAL: weight loads bypass cache allocation). */
-enum { WSG_GEMV_NONTEMPORAL = 1 };
+ * (0 = one row group per wave, no grid-stride loop) and flags, OR-ed:
+ *   WSG_GEMV_NONTEMPORAL: weight loads bypass cache allocation;
+ *   WSG_GEMV_SPLIT2: each output row is computed by two waves of a
+ *     workgroup, each streaming one half of the row, and their two FP32
+ *     sums are added once (half 0 first); for long rows, whose single wave
+ *     cannot keep a whole row's loads in registers.  FP32 weights,
+ *     rows_per_wave 1 (or 0), K of 1024, 2048 or 3072; grid_blocks counts
+ *     workgroups of two rows (0 = one per row pair).
+ * Other flag bits, or WSG_GEMV_SPLIT2 outside those shapes, return
+ * WSG_ERR_INVALID_ARG. */
+enum { WSG_GEMV_NONTEMPORAL = 1, WSG_GEMV_SPLIT2 = 2 };
 wsg_status wsg_gemv_ex(int32_t w_dtype, int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,
                        int32_t grid_blocks, int32_t flags,
                        const void* d_W, const void* d_X, float* d_Y, void* hip_stream);
@@ -398,8 +406,8 @@ wsg_status wsg_gemv_ex(int32_t w_dtype, int32_t M, int32_t K, int32_t T, int32_t
 wsg_status wsg_gemv_q4g64(int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,
                           const uint32_t* d_Wq, const void* d_scales, const void* d_X,
                           float* d_Y, void* hip_stream);
-/* wsg_gemv_q4g64 with an explicit launch shape (grid_blocks and flags as
- * for wsg_gemv_ex).  A block is 4 waves, except at K = 14336, where the
+/* wsg_gemv_q4g64 with an explicit launch shape (grid_blocks as for
+ * wsg_gemv_ex; flags: WSG_GEMV_NONTEMPORAL only).  A block is 4 waves, except at K = 14336, where the
  * activations staged per block are 28 KiB per row of X and a block is 16
  * waves (one staged copy serves four times the rows). */
 wsg_status wsg_gemv_q4g64_ex(int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,

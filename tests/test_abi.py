@@ -45,6 +45,18 @@ def test_gemv_argument_validation(abi):
     assert b"aligned" in L.wsg_last_error()
     assert L.wsg_gemv_q4g64(8, 100, 1, 1, 16, 16, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
     assert L.wsg_gemv_q4g64(8, 128, 1, 1, 16, 17, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
+    # launch flags: unknown bits, and the two-waves-per-row form outside FP32, one row per wave,
+    # K in {1024, 2048, 3072}; a valid split request gets past the flag checks (to the null pointer)
+    split = abi.WSG_GEMV_SPLIT2
+    assert L.wsg_gemv_ex(0, 8, 1024, 1, 1, 0, 4, 16, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
+    assert b"unknown flags" in L.wsg_last_error()
+    for dt, R, K in ((1, 1, 1024), (0, 2, 1024), (0, 1, 4096), (0, 1, 512)):
+        assert L.wsg_gemv_ex(dt, 8, K, 1, R, 0, split, 16, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
+        assert b"WSG_GEMV_SPLIT2" in L.wsg_last_error()
+    assert L.wsg_gemv_ex(0, 8, 3072, 2, 0, 0, split | 1, None, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
+    assert b"null pointer" in L.wsg_last_error()
+    assert L.wsg_gemv_q4g64_ex(8, 128, 1, 1, 0, 2, 16, 16, 16, 16, None) == abi.WSG_ERR_INVALID_ARG
+    assert b"unknown flags" in L.wsg_last_error()
     # streaming reference: null, size not a multiple of 16, misaligned buffer
     assert L.wsg_stream_read(None, 64, 16, None) == abi.WSG_ERR_INVALID_ARG
     assert L.wsg_stream_read(16, 64, None, None) == abi.WSG_ERR_INVALID_ARG

@@ -54,6 +54,19 @@ def test_gemv_ragged(M, K, dtype, T):
     _run_dense(M, K, T, (1, 4), dtype, seed=12)
 
 
+@pytest.mark.parametrize("M,K", [(1024, 3072), (1024, 2048), (4096, 1024), (1001, 3072), (7, 2048), (1, 1024)])
+@pytest.mark.parametrize("T", [1, 2])
+def test_gemv_f32_two_waves_per_row(M, K, T):
+    """FP32 rows split over two waves (WSG_GEMV_SPLIT2): one workgroup per row pair, odd row
+    counts (the last pair's second row is read clamped and not written), and grid-stride loops
+    over one and three workgroups (their LDS half sums are reused pair after pair)."""
+    import weight_streaming_gemv_amd as wsg
+    split = wsg.WSG_GEMV_SPLIT2
+    _run_dense(M, K, T, (1,), "f32", seed=14, flags=split | wsg.WSG_GEMV_NONTEMPORAL)
+    _run_dense(M, K, T, (1,), "f32", seed=14, grid=3, flags=split)
+    _run_dense(M, K, T, (1,), "f32", seed=14, grid=1, flags=split)
+
+
 @pytest.mark.parametrize("grid,flags", [(1, 0), (7, 1), (256, 0), (512, 1)])
 def test_gemv_launch_shapes(grid, flags):
     _run_dense(6144, 1024, 2, (2,), "f32", grid=grid, flags=flags)

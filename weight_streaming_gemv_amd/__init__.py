@@ -14,13 +14,13 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 from . import _abi
-from ._abi import (WSG_F16, WSG_F32, WSG_GEMV_NONTEMPORAL, WSG_OPT_TIMED_STAGE, WSG_OPT_USE_GRAPH,
+from ._abi import (WSG_F16, WSG_F32, WSG_GEMV_NONTEMPORAL, WSG_GEMV_SPLIT2, WSG_OPT_TIMED_STAGE, WSG_OPT_USE_GRAPH,
                    WSG_STAGE_ATTN, WSG_STAGE_DOWN, WSG_STAGE_GATEUP, WSG_STAGE_HEAD, WSG_STAGE_O,
                    WSG_STAGE_QKV, WsgError, check, wsg_config, wsg_host_weights)
 
 __all__ = ["Model", "make_config", "gemv", "gemv_q4g64", "gemm_nt", "gemm_swiglu", "argmax", "WsgError", "WSG_F32", "WSG_F16",
            "WSG_STAGE_QKV", "WSG_STAGE_ATTN", "WSG_STAGE_O", "WSG_STAGE_GATEUP", "WSG_STAGE_DOWN",
-           "WSG_STAGE_HEAD", "WSG_OPT_USE_GRAPH", "WSG_OPT_TIMED_STAGE", "WSG_GEMV_NONTEMPORAL", "stream_read", "lib"]
+           "WSG_STAGE_HEAD", "WSG_OPT_USE_GRAPH", "WSG_OPT_TIMED_STAGE", "WSG_GEMV_NONTEMPORAL", "WSG_GEMV_SPLIT2", "stream_read", "lib"]
 
 try:
     # torch first: libwsg.so then binds to the HIP runtime torch already

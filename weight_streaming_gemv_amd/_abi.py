@@ -25,6 +25,7 @@ WSG_OPT_ROWS = {"qkv": 10, "o": 11, "gateup": 12, "down": 13, "head": 14}
 WSG_OPT_GRID = {"qkv": 20, "o": 21, "gateup": 22, "down": 23, "head": 24}
 WSG_STAGE_QKV, WSG_STAGE_ATTN, WSG_STAGE_O, WSG_STAGE_GATEUP, WSG_STAGE_DOWN, WSG_STAGE_HEAD = range(6)
 WSG_GEMV_NONTEMPORAL = 1
+WSG_GEMV_SPLIT2 = 2
 
 STATUS_NAMES = {0: "WSG_OK", -1: "WSG_ERR_INVALID_ARG", -2: "WSG_ERR_OUT_OF_RANGE", -3: "WSG_ERR_STATE",
                 -4: "WSG_ERR_HIP", -5: "WSG_ERR_UNSUPPORTED"}

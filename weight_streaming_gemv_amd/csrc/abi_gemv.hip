@@ -30,6 +30,12 @@ extern "C" wsg_status wsg_gemv_ex(int32_t w_dtype, int32_t M, int32_t K, int32_t
   if (T < 1 || T > 2) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: T=%d must be 1 or 2", T);
   if (!valid_rows(rows_per_wave)) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: rows_per_wave must be 1, 2, 4 or 8");
   if (grid_blocks < 0) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: grid_blocks < 0");
+  if (flags & ~(WSG_GEMV_NONTEMPORAL | WSG_GEMV_SPLIT2)) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: unknown flags 0x%x", flags);
+  if ((flags & WSG_GEMV_SPLIT2) &&
+      (w_dtype != WSG_F32 || rows_per_wave != 1 || (K != 1024 && K != 2048 && K != 3072)))
+    return fail(WSG_ERR_INVALID_ARG,
+                "wsg_gemv: WSG_GEMV_SPLIT2 needs FP32 weights, one row per wave and K of 1024, 2048 or 3072 "
+                "(dtype=%d rows_per_wave=%d K=%d)", w_dtype, rows_per_wave, K);
   if (!d_W || !d_X || !d_Y) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: null pointer");
   if (((uintptr_t)d_W | (uintptr_t)d_X) & 15) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: W and X must be 16-byte aligned");
   if ((int64_t)M * K > (int64_t)1 << 40) return fail(WSG_ERR_UNSUPPORTED, "wsg_gemv: matrix too large");
@@ -51,6 +57,7 @@ extern "C" wsg_status wsg_gemv_q4g64_ex(int32_t M, int32_t K, int32_t T, int32_t
   if (T < 1 || T > 2) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv_q4g64: T=%d must be 1 or 2", T);
   if (!valid_rows(rows_per_wave)) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv_q4g64: rows_per_wave must be 1, 2, 4 or 8");
   if (grid_blocks < 0) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv_q4g64: grid_blocks < 0");
+  if (flags & ~WSG_GEMV_NONTEMPORAL) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv_q4g64: unknown flags 0x%x", flags);
   if (!d_Wq || !d_scales || !d_X || !d_Y) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv_q4g64: null pointer");
   if (((uintptr_t)d_Wq | (uintptr_t)d_X) & 15) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv_q4g64: Wq and X must be 16-byte aligned");
   if (((uintptr_t)d_scales) & 1) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv_q4g64: scales must be 2-byte aligned");

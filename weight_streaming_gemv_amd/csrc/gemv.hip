@@ -65,6 +65,67 @@ __global__ __launch_bounds__(kBlock) void k_gemv_f32(const float* __restrict__ W
   }
 }
 
+// ------------------------------------------- FP32, two waves per row
+// One wave per row holds the lane's K/64 activations and, to keep the row's
+// loads in flight, as many weights: at K = 3072 that is 96 registers, and
+// the compiler instead held the weight loads back (60 registers, loads
+// issued a few at a time).  Here two waves of a workgroup share each row,
+// each streaming one half of it (and holding that half of the activations):
+// half the registers per wave and twice the waves for the same rows.  The
+// two wave sums meet in LDS and are added once, half 0 first.  Workgroup b
+// serves rows 2b and 2b + 1 (waves 0, 1 and 2, 3), then b + gridDim.x, ...
+template <int K, int T, bool NT>
+__global__ __launch_bounds__(kBlock) void k_gemv_f32_split2(const float* __restrict__ W,
+                                                            const float* __restrict__ X,
+                                                            float* __restrict__ Y, int M) {
+  constexpr int KH = K / 2;
+  constexpr int NV = KH / 256;  // float4 chunks per lane per half row
+  static_assert(KH % 256 == 0, "K must be a multiple of 512");
+  const int lane = lane_id();
+  const int wv = wave_id();
+  const int h = wv & 1;
+  float4 x[T][NV];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+      x[t][c] = *reinterpret_cast<const float4*>(X + (size_t)t * K + h * KH + c * 256 + lane * 4);
+  __shared__ float half_sum[kWavesPerBlock][T];
+  const int npairs = (M + 1) / 2;
+  // the loop bound depends on the workgroup only, so its barriers are uniform
+  for (int b = blockIdx.x; b < npairs; b += gridDim.x) {
+    const int row = 2 * b + (wv >> 1);
+    const float* wr = W + (size_t)min(row, M - 1) * K + h * KH + lane * 4;
+    float acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      Vec16<float> w;
+      w.load<NT>(wr + c * 256);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        float a = acc[t];
+        a = fmaf(w.v[0], x[t][c].x, a);
+        a = fmaf(w.v[1], x[t][c].y, a);
+        a = fmaf(w.v[2], x[t][c].z, a);
+        a = fmaf(w.v[3], x[t][c].w, a);
+        acc[t] = a;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float sum = wave_sum(acc[t]);
+      if (lane == 0) half_sum[wv][t] = sum;
+    }
+    __syncthreads();
+    if (h == 0 && lane == 0 && row < M)
+#pragma unroll
+      for (int t = 0; t < T; ++t) Y[(size_t)t * M + row] = half_sum[wv][t] + half_sum[wv + 1][t];
+    __syncthreads();  // the next pair rewrites half_sum
+  }
+}
+
 // ------------------------------------------------------------ FP16, fixed K
 // Weights and activations stay packed as half pairs; v_dot2_f32_f16 forms
 // the exact FP16 products and adds them into an FP32 accumulator.
@@ -436,6 +497,25 @@ bool launch_f16_fixed(int M, int K, int grid, bool nt, const __half* W, const __
 }
 #undef WSG_LAUNCH_FIXED
 
+// FP32, K = 1024, 2048 or 3072 (checked by the entry point), one row per
+// two waves: one workgroup per row pair unless fewer are asked for.
+template <int T>
+void launch_f32_split2(int M, int K, int grid_req, bool nt, const float* W, const float* X, float* Y,
+                       hipStream_t s) {
+  const int npairs = (M + 1) / 2;
+  const int grid = grid_req > 0 && grid_req < npairs ? grid_req : npairs;
+#define WSG_SPLIT2(KK)                                                                                        \
+  if (K == KK) {                                                                                              \
+    if (nt) hipLaunchKernelGGL((k_gemv_f32_split2<KK, T, true>), dim3(grid), dim3(kBlock), 0, s, W, X, Y, M);  \
+    else hipLaunchKernelGGL((k_gemv_f32_split2<KK, T, false>), dim3(grid), dim3(kBlock), 0, s, W, X, Y, M);    \
+    return;                                                                                                   \
+  }
+  WSG_SPLIT2(1024)
+  WSG_SPLIT2(2048)
+  WSG_SPLIT2(3072)
+#undef WSG_SPLIT2
+}
+
 template <int R, int T>
 void launch_dense(int dtype, int M, int K, int grid_req, bool nt, const void* W, const void* X, float* Y,
                   hipStream_t s) {
@@ -487,6 +567,13 @@ void launch_q4(int M, int K, int grid_req, bool nt, const uint32_t* Wq, const __
 void gemv_dispatch(int dtype, int M, int K, int T, int R, int grid, int flags, const void* W, const void* X,
                    float* Y, hipStream_t s) {
   const bool nt = (flags & 1) != 0;
+  if (flags & 2) {
+    const float* w = static_cast<const float*>(W);
+    const float* x = static_cast<const float*>(X);
+    if (T == 1) launch_f32_split2<1>(M, K, grid, nt, w, x, Y, s);
+    else launch_f32_split2<2>(M, K, grid, nt, w, x, Y, s);
+    return;
+  }
 #define WSG_DR(RR)                                                             \
   case RR:                                                                     \
     if (T == 1) launch_dense<RR, 1>(dtype, M, K, grid, nt, W, X, Y, s);        \

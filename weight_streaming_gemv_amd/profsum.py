@@ -122,27 +122,41 @@ def sweep_table(path):
     print("| kernel | M x K | T | R | NT | blocks | calls | median us | GB/s | % of 8 TB/s |")
     print("|---|---|---|---|---|---|---|---|---|---|")
     best = {}
+    # A (kernel instance, grid) pair that two shapes both launch pools their
+    # dispatches in the trace: it is shown for the first shape only (whose
+    # dispatches dominate it) and left out for the later ones.
+    owner = {}
+    pooled = []
     for dt, es, kname in (("f32", 4, "k_gemv_f32"), ("f16", 2, "k_gemv_f16"), ("q4g64", None, "k_gemv_q4")):
         shapes = Q4_SHAPES if dt == "q4g64" else GEMV_SHAPES
         for (M, K) in shapes:
             nbytes = M * K // 2 + M * (K // 64) * 2 if dt == "q4g64" else M * K * es
             for T in (1, 2):
-                for R in (1, 2, 4, 8):
+                # "1s": one FP32 row over two waves (k_gemv_f32_split2, one workgroup per row pair)
+                split_ok = dt == "f32" and K in (1024, 2048, 3072)
+                for R in (1, 2, 4, 8) + (("1s",) if split_ok else ()):
                     for nt in ("false", "true"):   # ordinary / non-temporal weight loads
                         seen = set()
                         grids = (0, 256, 512) if dt == "q4g64" else ((0, 1280, 2048, 4096) if M > 100000 else (0,))
                         # int4 rows of 14336 run 16-wave workgroups, every other shape 4-wave ones
                         wv = 16 if dt == "q4g64" and K == 14336 else 4
                         for G in grids:
-                            one = _ceil(_ceil(M, R), wv)
+                            one = _ceil(M, 2) if R == "1s" else _ceil(_ceil(M, R), wv)
                             blocks = one if G == 0 or G >= one else G
                             if blocks in seen:
                                 continue
                             seen.add(blocks)
-                            tmpl = f"{K}, {R}, {T}, {nt}, {wv}" if dt == "q4g64" else f"{K}, {R}, {T}, {nt}"
-                            key = (f"{kname}<{tmpl}>", blocks)
+                            if R == "1s":
+                                key = (f"k_gemv_f32_split2<{K}, {T}, {nt}>", blocks)
+                            else:
+                                tmpl = f"{K}, {R}, {T}, {nt}, {wv}" if dt == "q4g64" else f"{K}, {R}, {T}, {nt}"
+                                key = (f"{kname}<{tmpl}>", blocks)
                             ds = idx.get(key)
                             if not ds:
+                                continue
+                            if owner.setdefault(key, (M, K)) != (M, K):
+                                pooled.append(f"{key[0]} on {key[1]} blocks: {M}x{K} pooled with "
+                                              f"{owner[key][0]}x{owner[key][1]}")
                                 continue
                             us = statistics.median(ds) / 1e3
                             gbps = nbytes / us / 1e3
@@ -151,6 +165,10 @@ def sweep_table(path):
                             k = (dt, M, K, T)
                             if k not in best or us < best[k][0]:
                                 best[k] = (us, R, blocks, gbps)
+    if pooled:
+        print()
+        print("Left out (launches of the same kernel instance and grid by two shapes; the row above "
+              "belongs to the first): " + "; ".join(pooled) + ".")
     print()
     print("Best per shape (kernel-only):")
     print()
