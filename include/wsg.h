@@ -375,7 +375,9 @@ wsg_status wsg_time_stage(wsg_model* m, int32_t stage, int32_t reps, double* us_
  * Cache, "Why it mattered": rows per wave and the two-token variant).
  *   w_dtype WSG_F32: d_W float [M][K], d_X float [T][K];
  *   w_dtype WSG_F16: d_W half [M][K],  d_X half [T][K];
- *   d_Y float [T][M].  1 <= T <= 2; rows_per_wave in {1,2,4,8}, 0 = default.
+ *   d_Y float [T][M].  1 <= T <= 2; rows_per_wave in {1,2,4,8}, 0 = default
+ *   (one row per wave; FP32 rows of K = 3072: one row per two waves, as
+ *   WSG_GEMV_SPLIT2 below).
  *   M >= 1, K >= 1, any sizes; d_W and d_X 16-byte aligned.
  * Asynchronous on hip_stream. */
 wsg_status wsg_gemv(int32_t w_dtype, int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,

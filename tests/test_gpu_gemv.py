@@ -65,6 +65,8 @@ def test_gemv_f32_two_waves_per_row(M, K, T):
     _run_dense(M, K, T, (1,), "f32", seed=14, flags=split | wsg.WSG_GEMV_NONTEMPORAL)
     _run_dense(M, K, T, (1,), "f32", seed=14, grid=3, flags=split)
     _run_dense(M, K, T, (1,), "f32", seed=14, grid=1, flags=split)
+    if K == 3072:   # the default launch shape of FP32 rows of 3072 is this form
+        _run_dense(M, K, T, (0,), "f32", seed=14)
 
 
 @pytest.mark.parametrize("grid,flags", [(1, 0), (7, 1), (256, 0), (512, 1)])

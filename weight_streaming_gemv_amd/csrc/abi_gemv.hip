@@ -28,6 +28,9 @@ extern "C" wsg_status wsg_gemv_ex(int32_t w_dtype, int32_t M, int32_t K, int32_t
   if (w_dtype != WSG_F32 && w_dtype != WSG_F16) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: bad dtype %d", w_dtype);
   if (M < 1 || K < 1) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: M=%d K=%d must be >= 1", M, K);
   if (T < 1 || T > 2) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: T=%d must be 1 or 2", T);
+  // default shape for FP32 rows of 3072: two waves per row (one wave cannot
+  // keep such a row's loads in flight)
+  if (rows_per_wave == 0 && w_dtype == WSG_F32 && K == 3072) flags |= WSG_GEMV_SPLIT2;
   if (!valid_rows(rows_per_wave)) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: rows_per_wave must be 1, 2, 4 or 8");
   if (grid_blocks < 0) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: grid_blocks < 0");
   if (flags & ~(WSG_GEMV_NONTEMPORAL | WSG_GEMV_SPLIT2)) return fail(WSG_ERR_INVALID_ARG, "wsg_gemv: unknown flags 0x%x", flags);
