@@ -371,8 +371,11 @@ __global__ __launch_bounds__(64 * WV) void k_gemv_q4(const uint32_t* __restrict_
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const size_t row = (size_t)min(row0 + r, M - 1);
-      // partial unroll keeps long rows (K = 14336) from using every VGPR
-#pragma unroll 2
+      // Partial unroll keeps long rows (K = 14336) from using every VGPR;
+      // the unroll depth is the number of 16-byte chunks a wave has in
+      // flight.  One row per wave: 4 (cold 4096 x 14336, one row of X:
+      // 9.44 -> 8.78 us against 2, 9.0 with 3; all 7 spill); larger groups 2.
+#pragma unroll(R == 1 ? 4 : 2)
       for (int c = 0; c < NV; ++c) {
         const uint4 w = load_u4<NT>(Wq + row * W8 + c * 256 + lane * 4);
         const float sc = __half2float(S[row * G + c * 32 + (lane >> 1)]);
