@@ -410,8 +410,9 @@ wsg_status wsg_gemv_q4g64(int32_t M, int32_t K, int32_t T, int32_t rows_per_wave
                           float* d_Y, void* hip_stream);
 /* wsg_gemv_q4g64 with an explicit launch shape (grid_blocks as for
  * wsg_gemv_ex; flags: WSG_GEMV_NONTEMPORAL only).  A block is 4 waves, except at K = 14336, where the
- * activations staged per block are 28 KiB per row of X and a block is 16
- * waves (one staged copy serves four times the rows). */
+ * activations staged per block are 28 KiB per row of X and a block is
+ * 16 / rows_per_wave waves, at least 4 (one staged copy serves up to four
+ * times the rows). */
 wsg_status wsg_gemv_q4g64_ex(int32_t M, int32_t K, int32_t T, int32_t rows_per_wave,
                              int32_t grid_blocks, int32_t flags,
                              const uint32_t* d_Wq, const void* d_scales, const void* d_X,

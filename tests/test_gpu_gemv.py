@@ -110,8 +110,8 @@ def test_q4_ragged(M, K, T):
 @pytest.mark.parametrize("M,K", [(1000, 14336), (999, 4096)])
 @pytest.mark.parametrize("T", [1, 2])
 def test_q4_fixed_k_ragged_and_looping(M, K, T):
-    """The fixed-K int4 kernels (16-wave workgroups with a partial last round of
-    activation staging at K = 14336, 4-wave ones at K = 4096) on a ragged row
+    """The fixed-K int4 kernels (16 / R-wave workgroups at K = 14336, some with a
+    partial last round of activation staging, 4-wave ones at K = 4096) on a ragged row
     count: one-shot grids, and grid-stride loops over three workgroups (at
     K = 4096 one row per wave issues each next row before reducing the
     current one; waves past the last row read it and discard it)."""

@@ -551,10 +551,14 @@ void launch_q4(int M, int K, int grid_req, bool nt, const uint32_t* Wq, const __
   WSG_Q4(4096)
 #undef WSG_Q4
   if (K == 14336) {
-    // long rows: 16-wave workgroups, so one LDS copy of the 28 KiB (per row
-    // of X) activations serves four times the waves (cold sweep of
-    // 4096 x 14336: 10.5 -> 9.4 us for one row of X, 15.3 -> 11.0 us for two)
-    constexpr int WV = 16;
+    // long rows: workgroups of 16 / R waves (16 at one row per wave, 8 at
+    // two, 4 beyond), so one LDS copy of the 28 KiB (per row of X)
+    // activations serves up to four times the waves while a 4096-row matrix
+    // still fills 256 workgroups (cold sweep of 4096 x 14336: 16 waves at
+    // R = 1, 10.5 -> 9.4 us for one row of X and 15.3 -> 11.0 us for two;
+    // 8 and 4 waves instead of 16 at R = 2 and 4, 14.7 -> 13.2 and
+    // 25.9 -> 20.9 us)
+    constexpr int WV = R == 1 ? 16 : R == 2 ? 8 : 4;
     const int ngroups = (M + R - 1) / R;
     const int one_shot = (ngroups + WV - 1) / WV;
     const int g16 = grid_req > 0 && grid_req < one_shot ? grid_req : one_shot;

@@ -139,7 +139,7 @@ def sweep_table(path):
                         seen = set()
                         grids = (0, 256, 512) if dt == "q4g64" else ((0, 1280, 2048, 4096) if M > 100000 else (0,))
                         # int4 rows of 14336 run 16-wave workgroups, every other shape 4-wave ones
-                        wv = 16 if dt == "q4g64" and K == 14336 else 4
+                        wv = ({1: 16, 2: 8}.get(R, 4)) if dt == "q4g64" and K == 14336 else 4
                         for G in grids:
                             one = _ceil(M, 2) if R == "1s" else _ceil(_ceil(M, R), wv)
                             blocks = one if G == 0 or G >= one else G
