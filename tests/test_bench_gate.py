@@ -137,3 +137,24 @@ def test_main_publishes_nothing_on_a_failed_check(monkeypatch, capsys):
     monkeypatch.setattr(bench, "_main", failing)
     assert bench.main([]) == 3
     assert capsys.readouterr().out == ""
+
+
+def test_sweep_summary_reads_split_configurations():
+    """The cold sweep's best-configuration table: keys T{T}_R{R}_G{G}, where R = "1s" is an FP32
+    row over two waves; the fastest key per shape and T wins, and its rows per wave, waves per
+    row and grid are read back from the key."""
+    sw = {"f32_1024x3072": {"bytes": 1024 * 3072 * 4,
+                            "T1_R1_G0": {"us": 7.9}, "T1_R2_G0": {"us": 4.5}, "T1_R1s_G0": {"us": 3.9},
+                            "T2_R1_G0": {"us": 4.4}, "T2_R1s_G256": {"us": 4.5},
+                            "ceiling": {"us": 3.3, "gbps": 1024 * 3072 * 4 / 3.3 / 1e3}},
+          "q4g64_4096x4096": {"bytes": 4096 * 2048 + 4096 * 64 * 2,
+                              "T1_R1_G0": {"us": 3.9}, "T1_R2_G512": {"us": 4.4}}}
+    best, _ = bench.sweep_summary(sw)
+    b = best["f32_1024x3072_T1"]
+    assert (b["R"], b["waves_per_row"], b["grid"], b["us"]) == (1, 2, 0, 3.9)
+    assert b["frac_of_stream_ceiling"] == pytest.approx(3.3 / 3.9, abs=1e-4)
+    b = best["f32_1024x3072_T2"]
+    assert (b["R"], b["waves_per_row"], b["grid"], b["us"]) == (1, 1, 0, 4.4)
+    b = best["q4g64_4096x4096_T1"]
+    assert (b["R"], b["waves_per_row"], b["grid"]) == (1, 1, 0) and "frac_of_stream_ceiling" not in b
+    assert "q4g64_4096x4096_T2" not in best
